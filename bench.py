@@ -1,0 +1,183 @@
+#!/usr/bin/env python3
+"""Throughput of the SDM recurrent core (select + gated delta write + sparse
+read) on one MI355X, on the seeded synthetic workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload 1] [--gpus 1]
+
+A step is one sdm_forward over the whole workload (M <- M_0, selection of
+every head-token, forwarding plan, then the token-serial write/read), issued
+as sdm_prepare + sdm_apply so that HIP events on the launch stream time the
+write/read kernel on its own.  Inputs are resident in HBM before timing.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "SDM select+write+read head-tokens/s and achieved HBM GB/s (% peak)"
+
+
+def _log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _traffic(wl, rw_launches_per_step=1):
+    """Counter-measured HBM bytes per launch of the write/read kernel, if a
+    committed summary matches the current kernel source, else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_rw_serial_{wl.name.replace(' ', '_')}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        src = open(os.path.join(ROOT, "sparse_memory_linear_select_amd", "csrc",
+                                "rw_serial.hip"), "rb").read()
+        if rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
+            return None
+        return float(rec["hbm_bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def cpu_baseline(d, wl, seqs):
+    """The float64 oracle on the first `seqs` sequences of the same inputs."""
+    import oracle
+
+    sub = {k: (v[:seqs] if k not in ("M0",) else v) for k, v in d.items() if k != "src"}
+    cores = oracle.default_threads()
+    t = time.perf_counter()
+    oracle.forward(sub, wl.sqrtN, wl.W, wl.R, threads=cores)
+    dt = time.perf_counter() - t
+    ht = seqs * wl.T * wl.H
+    return {"value": ht / dt, "unit": "head-tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{seqs} of {wl.B} sequences of the workload ({ht} head-tokens, all "
+                      f"{wl.d_v} columns), select + init + recurrence, {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=1,
+                    help="synthetic workload index (default 1: the 1.4B-style layer)")
+    ap.add_argument("--cpu-seqs", type=int, default=None,
+                    help="sequences in the CPU-baseline sample (default: all)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the SDM core shards by (sequence, head) chain or by "
+              "column with no exchange on the hot path, so only --gpus 1 is run here",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sdm_inputs as si
+    import sparse_memory_linear_select_amd as sdm
+
+    wl = si.WORKLOADS[args.workload]
+    _log(f"workload {args.workload}: {wl}")
+    t = time.perf_counter()
+    d = si.generate(wl)
+    _log(f"inputs generated in {time.perf_counter() - t:.1f}s")
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(x):
+        import numpy as np
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x).to(dev)
+
+    dd = {k: up(v) for k, v in d.items() if k != "src"}
+    core = sdm.SDM(dd["M0"], wl.W, wl.R)
+    B, T, H = wl.B, wl.T, wl.H
+    y = torch.empty((B, T, H, wl.d_v), dtype=torch.float32, device=dev)
+    M = torch.empty((B, H, wl.N, wl.d_v), dtype=torch.float32, device=dev)
+    dt_code = sdm.BF16 if wl.dtype == "bf16" else sdm.F32
+    ws_n = core.workspace_size(B, T, dt_code, sdm.AUTO)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    L = sdm.lib()
+    stream = torch.cuda.current_stream(dev)
+    sp = sdm._stream(dev)
+    P = sdm._ptr
+
+    def prepare():
+        sdm._check(L.sdm_prepare(core._h, B, T, P(dd["kp"]), P(dd["qp"]), P(dd["alpha"]),
+                                 P(dd["beta"]), dt_code, sdm.AUTO, 0, P(ws), ws_n, P(M), sp))
+
+    def apply():
+        sdm._check(L.sdm_apply(core._h, B, T, P(dd["v"]), dt_code, sdm.AUTO, P(ws), ws_n, P(y),
+                               P(M), sp))
+
+    for _ in range(args.warmup):
+        prepare()
+        apply()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for e in ev:
+        e[0].record(stream)
+        prepare()
+        e[1].record(stream)
+        apply()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    total_ms = ev[0][0].elapsed_time(ev[-1][2])
+    ms_step = total_ms / args.steps
+    rw_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    prep_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    ht = wl.head_tokens
+    row_bytes = ht * (2 * wl.W + wl.R) * wl.d_v * 4  # algorithmic row traffic per launch
+    achieved = row_bytes / (rw_ms * 1e-3) / 1e9
+    traffic = _traffic(wl)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(d, wl, args.cpu_seqs or wl.B)
+
+    out = {
+        "metric": METRIC,
+        "value": ht / (ms_step * 1e-3),
+        "unit": "head-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if wl.dtype == "f32" else "bf16 inputs, f32 state",
+        "data": "synthetic (seeded; recipe in sdm_inputs.py)",
+        "config": {"workload": wl.name, "B": B, "T": T, "H": H, "sqrtN": wl.sqrtN, "N": wl.N,
+                   "d_v": wl.d_v, "W": wl.W, "R": wl.R, "inputs": wl.dtype,
+                   "schedule": "token-serial"},
+        "row_gbs_whole_step": row_bytes / (ms_step * 1e-3) / 1e9,
+        "breakdown_ms": {"prepare (init+select+plan)": prep_ms, "write+read": rw_ms},
+        "wall_s_timed": wall,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

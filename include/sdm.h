@@ -1,0 +1,182 @@
+/*
+ * sdm.h: C ABI of the Sparse Delta Memory (SDM) recurrent core for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The core, per sequence b, head h and token t, in the pages' notation:
+ *
+ *   select  The pre-PKM key k'_t and query q'_t (length 2*sqrtN each) are
+ *           split into halves; slot n = i*sqrtN + j has the outer-sum score
+ *           x_1[i] + x_2[j].  The W slots with the highest scores form the
+ *           write set I^w_t (from k'), the R highest the read set I^r_t
+ *           (from q'), found with the product-key identity
+ *           top_k(s1 (+) s2) = top_k(top_k(s1) (+) top_k(s2))
+ *           [explainer "Sparse Delta Memory：通过稀疏性扩展线性 RNN 的状态容量"
+ *           (papers.ananclaw.com), §3.1 step 1; "Technical Summary: Sparse
+ *           Delta Memory (SDM)" (gist.science), Methodology / Core Mechanism 2].
+ *           Order, ties and weights are readings of this library (the pages
+ *           leave them open): scores are compared as exact real numbers, ties
+ *           go to the lower flat index n, lists are returned in that order,
+ *           and the weights k^(i), q^(i) are the softmax of the selected
+ *           scores.
+ *   write   For i in I^w_t:  m = alpha_t * M[i];  M[i] = m + beta_t * k^(i) *
+ *           (v_t - m); every other row is left as it is
+ *           [explainer §3.1 step 2; Technical Summary, Core Mechanism 3].
+ *   read    y_t = sum over i in I^r_t of q^(i) * M[i], on the state after the
+ *           same token's write [explainer §3.1 step 3; Technical Summary,
+ *           Core Mechanism 4].
+ *   M starts from the shared initial state M_0 of the head [explainer §3.1,
+ *   learned initial state; Technical Summary, Learned Initial State].
+ *
+ * Conventions
+ *   - Every tensor pointer is a DEVICE pointer (HIP global memory) owned by
+ *     the caller; the library never allocates, frees or retains them, except
+ *     that a handle borrows M_0 until sdm_destroy.  All tensors are dense,
+ *     row-major, and must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *     enqueued asynchronously on it; no call synchronises the host.
+ *   - Shapes: B sequences, T tokens, H heads, N = sqrtN^2 slots per head,
+ *     d_v columns per slot.  "ht" below is the head-token index
+ *     (b*T + t)*H + h.
+ *   - Arguments are validated before any HIP call.  On failure the call
+ *     returns a non-zero sdm_status, enqueues nothing, and
+ *     sdm_last_error() describes the reason (thread-local).  No C++
+ *     exception crosses this interface.
+ *   - Inputs must be finite; alpha in (0, 1] and beta in [0, 1] are the
+ *     intended ranges (not checked).
+ *   - Different handles and streams may be used concurrently.  Calls that
+ *     share an output or workspace buffer must be ordered by the caller.
+ *
+ * Limits: 1 <= sqrtN <= 1024, 1 <= W, R <= min(sqrtN, 64), 1 <= d_v, H, B,
+ * 1 <= T, B*T*H < 2^31.
+ */
+#ifndef SDM_H
+#define SDM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sdm_ctx *sdm_handle;
+
+typedef enum {
+    SDM_OK = 0,
+    SDM_ERR_ARG = 1,         /* invalid argument (null, size, alignment) */
+    SDM_ERR_UNSUPPORTED = 2, /* valid but outside the supported limits  */
+    SDM_ERR_WORKSPACE = 3,   /* workspace smaller than sdm_workspace_size */
+    SDM_ERR_HIP = 4          /* a HIP call failed; see sdm_last_error()  */
+} sdm_status;
+
+/* Element type of k', q' and v.  alpha, beta, M_0, y and M are float32. */
+typedef enum { SDM_F32 = 0, SDM_BF16 = 1 } sdm_dtype;
+
+/*
+ * Write/read schedule used by sdm_forward.  Both produce the same result up
+ * to float32 rounding order.
+ *   SERIAL   token-serial per (sequence, head, column slice), rows gathered
+ *            and scattered in HBM with cross-token prefetch.
+ *   TIMEPAR  time-parallel: (slot, t) events sorted per chunk of tokens and
+ *            a per-slot scan of the affine map M <- a*M + c*v.
+ *   AUTO     the library's choice for the shape.
+ */
+typedef enum {
+    SDM_VARIANT_AUTO = 0,
+    SDM_VARIANT_SERIAL = 1,
+    SDM_VARIANT_TIMEPAR = 2
+} sdm_variant;
+
+/* sdm_forward flags */
+#define SDM_FLAG_CONTINUE 1u /* start from the state already in M (no M <- M_0) */
+
+/*
+ * Create a handle for one SDM layer shape.
+ *   M0     device [H][N][d_v] float32, the shared initial state; borrowed:
+ *          it must stay valid and unchanged until sdm_destroy.
+ *   H, sqrtN, d_v, W, R  as above.
+ *   out    receives the handle.
+ * Makes no HIP call.  Errors: SDM_ERR_ARG (null, size), SDM_ERR_UNSUPPORTED
+ * (outside the limits).
+ */
+sdm_status sdm_create(const float *M0, int H, int sqrtN, int d_v, int W, int R,
+                      sdm_handle *out);
+
+/* Release a handle (M_0 is not touched).  NULL is accepted. */
+sdm_status sdm_destroy(sdm_handle h);
+
+/*
+ * Bytes of device workspace sdm_forward needs for B sequences of T tokens
+ * with the given input dtype and variant (a pure function of its
+ * arguments; makes no HIP call).
+ */
+sdm_status sdm_workspace_size(sdm_handle h, int B, int64_t T, sdm_dtype dtype,
+                              sdm_variant variant, size_t *bytes);
+
+/*
+ * Selection only (the first step of the core, standalone).
+ *   kp, qp  device [B][T][H][2*sqrtN], element type `dtype`.
+ *   Iw, kw  device [B][T][H][W]: write slots (int32, canonical order) and
+ *           their softmax weights (float32).
+ *   Ir, qw  device [B][T][H][R]: read slots and weights.
+ * Outputs must not alias inputs.
+ */
+sdm_status sdm_select(sdm_handle h, int B, int64_t T, const void *kp, const void *qp,
+                      sdm_dtype dtype, int32_t *Iw, float *kw, int32_t *Ir, float *qw,
+                      void *stream);
+
+/*
+ * The whole core: select, then the gated delta write and the sparse read for
+ * every token in order.
+ *   kp, qp     device [B][T][H][2*sqrtN], element type `dtype`.
+ *   v          device [B][T][H][d_v], element type `dtype`.
+ *   alpha,beta device [B][T][H] float32, the gates of each head-token.
+ *   workspace  device scratch of ws_bytes >= sdm_workspace_size(...) bytes,
+ *              16-byte aligned; its contents are undefined afterwards.
+ *   y          device [B][T][H][d_v] float32, output.
+ *   M          device [B][H][N][d_v] float32: the final state on return.
+ *              Unless SDM_FLAG_CONTINUE is set it is first overwritten with
+ *              M_0 (so a failed call can simply be retried); with the flag it
+ *              must hold the state to continue from.
+ * Outputs must not alias inputs or each other.
+ */
+sdm_status sdm_forward(sdm_handle h, int B, int64_t T, const void *kp, const void *qp,
+                       const void *v, const float *alpha, const float *beta,
+                       sdm_dtype dtype, sdm_variant variant, unsigned flags,
+                       void *workspace, size_t ws_bytes, float *y, float *M,
+                       void *stream);
+
+/*
+ * The two halves of sdm_forward, for callers that time or pipeline them.
+ * sdm_forward(...) is exactly sdm_prepare(...) followed by sdm_apply(...)
+ * with the same handle, shapes, dtype, variant and workspace.
+ *
+ * sdm_prepare: unless SDM_FLAG_CONTINUE is set, M <- M_0; then the selection
+ *   of every head-token is written into the workspace (with the write
+ *   coefficients alpha*(1 - beta*k) and beta*k, and the forwarding plan the
+ *   token-serial schedule needs).  Arguments as for sdm_forward.
+ * sdm_apply: the gated delta write and sparse read of every token, in order,
+ *   from the prepared workspace: reads v and M, writes y and M.  The
+ *   workspace must hold the result of sdm_prepare for the same call shape
+ *   (stream order is enough; nothing else may write it in between).
+ */
+sdm_status sdm_prepare(sdm_handle h, int B, int64_t T, const void *kp, const void *qp,
+                       const float *alpha, const float *beta, sdm_dtype dtype,
+                       sdm_variant variant, unsigned flags, void *workspace,
+                       size_t ws_bytes, float *M, void *stream);
+
+sdm_status sdm_apply(sdm_handle h, int B, int64_t T, const void *v, sdm_dtype dtype,
+                     sdm_variant variant, void *workspace, size_t ws_bytes, float *y,
+                     float *M, void *stream);
+
+/* Static description of a status code. */
+const char *sdm_status_string(sdm_status s);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char *sdm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDM_H */

@@ -1,0 +1,201 @@
+"""MI355X-native recurrent core of Sparse Delta Memory (SDM).
+
+Thin Python binding of libsdm.so, whose C ABI is declared in include/sdm.h.
+This module only marshals arguments: torch tensors supply device memory and
+the current HIP stream, and every step of the computation (selection, state
+initialisation, forwarding plan, gated delta write, sparse read) runs in the
+library's HIP kernels.  There is no fallback: if libsdm.so is missing or no
+GPU is present, the calls raise.
+
+    core = SDM(M0, W=64, R=64)            # M0: [H, N, d_v] float32 on the GPU
+    Iw, kw, Ir, qw = core.select(kp, qp)  # kp, qp: [B, T, H, 2*sqrtN]
+    y, M = core.forward(kp, qp, v, alpha, beta)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = ["SDM", "SDMError", "lib", "lib_path", "F32", "BF16", "AUTO", "SERIAL", "TIMEPAR",
+           "FLAG_CONTINUE", "EXPORTS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libsdm.so")
+_lib = None
+
+F32, BF16 = 0, 1
+AUTO, SERIAL, TIMEPAR = 0, 1, 2
+FLAG_CONTINUE = 1
+STATUS = {0: "SDM_OK", 1: "SDM_ERR_ARG", 2: "SDM_ERR_UNSUPPORTED", 3: "SDM_ERR_WORKSPACE",
+          4: "SDM_ERR_HIP"}
+
+# every function include/sdm.h declares
+EXPORTS = ("sdm_create", "sdm_destroy", "sdm_workspace_size", "sdm_select", "sdm_forward",
+           "sdm_prepare", "sdm_apply", "sdm_status_string", "sdm_last_error")
+
+
+class SDMError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded libsdm (ctypes), with argument types declared."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise SDMError(-1, f"{_LIB_PATH} is not built; run "
+                               "`python -m sparse_memory_linear_select_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        p, i, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+        L.sdm_create.argtypes = [p, i, i, i, i, i, ctypes.POINTER(p)]
+        L.sdm_destroy.argtypes = [p]
+        L.sdm_workspace_size.argtypes = [p, i, i64, i, i, ctypes.POINTER(sz)]
+        L.sdm_select.argtypes = [p, i, i64, p, p, i, p, p, p, p, p]
+        L.sdm_forward.argtypes = [p, i, i64, p, p, p, p, p, i, i, ctypes.c_uint, p, sz, p, p, p]
+        L.sdm_prepare.argtypes = [p, i, i64, p, p, p, p, i, i, ctypes.c_uint, p, sz, p, p]
+        L.sdm_apply.argtypes = [p, i, i64, p, i, i, p, sz, p, p, p]
+        for f in ("sdm_create", "sdm_destroy", "sdm_workspace_size", "sdm_select", "sdm_forward",
+                  "sdm_prepare", "sdm_apply"):
+            getattr(L, f).restype = ctypes.c_int
+        L.sdm_status_string.argtypes = [i]
+        L.sdm_status_string.restype = ctypes.c_char_p
+        L.sdm_last_error.argtypes = []
+        L.sdm_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise SDMError(status, lib().sdm_last_error().decode())
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev_tensor(t: torch.Tensor, name: str, dtype=None):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise SDMError(1, f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise SDMError(1, f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise SDMError(1, f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _in_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise SDMError(1, f"k', q', v must be float32 or bfloat16, got {t.dtype}")
+
+
+class SDM:
+    """One SDM layer shape bound to its shared initial state M_0 (borrowed)."""
+
+    def __init__(self, M0: torch.Tensor, W: int, R: int):
+        _dev_tensor(M0, "M0", torch.float32)
+        if M0.dim() != 3:
+            raise SDMError(1, "M0 must be [H, N, d_v]")
+        H, N, d_v = M0.shape
+        sqrtN = math.isqrt(N)
+        if sqrtN * sqrtN != N:
+            raise SDMError(1, f"N = {N} is not a perfect square")
+        self.M0, self.H, self.sqrtN, self.N, self.d_v = M0, H, sqrtN, N, d_v
+        self.W, self.R = int(W), int(R)
+        h = ctypes.c_void_p()
+        _check(lib().sdm_create(_ptr(M0), H, sqrtN, d_v, self.W, self.R, ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().sdm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_size(self, B: int, T: int, dtype: int = F32, variant: int = AUTO) -> int:
+        n = ctypes.c_size_t()
+        _check(lib().sdm_workspace_size(self._h, B, T, dtype, variant, ctypes.byref(n)))
+        return n.value
+
+    def _shape_in(self, x: torch.Tensor, last: int, name: str):
+        if x.dim() != 4 or x.shape[2] != self.H or x.shape[3] != last:
+            raise SDMError(1, f"{name} must be [B, T, {self.H}, {last}], got {tuple(x.shape)}")
+        return x.shape[0], x.shape[1]
+
+    def select(self, kp: torch.Tensor, qp: torch.Tensor, out=None):
+        """(Iw, kw, Ir, qw): write/read slots ([B,T,H,W|R] int32) and softmax weights."""
+        _dev_tensor(kp, "kp")
+        _dev_tensor(qp, "qp")
+        B, T = self._shape_in(kp, 2 * self.sqrtN, "kp")
+        if qp.shape != kp.shape or qp.dtype != kp.dtype:
+            raise SDMError(1, "qp must match kp in shape and dtype")
+        dev = kp.device
+        if out is None:
+            Iw = torch.empty((B, T, self.H, self.W), dtype=torch.int32, device=dev)
+            kw = torch.empty((B, T, self.H, self.W), dtype=torch.float32, device=dev)
+            Ir = torch.empty((B, T, self.H, self.R), dtype=torch.int32, device=dev)
+            qw = torch.empty((B, T, self.H, self.R), dtype=torch.float32, device=dev)
+        else:
+            Iw, kw, Ir, qw = out
+        _check(lib().sdm_select(self._h, B, T, _ptr(kp), _ptr(qp), _in_dtype(kp), _ptr(Iw),
+                                _ptr(kw), _ptr(Ir), _ptr(qw), _stream(dev)))
+        return Iw, kw, Ir, qw
+
+    def forward(self, kp, qp, v, alpha, beta, variant: int = AUTO, y=None, M=None,
+                workspace=None, cont: bool = False):
+        """(y, M): outputs [B,T,H,d_v] and final state [B,H,N,d_v] (float32).
+
+        With cont=True, M must hold the state to continue from (no M <- M_0).
+        """
+        for t, n in ((kp, "kp"), (qp, "qp"), (v, "v")):
+            _dev_tensor(t, n)
+        _dev_tensor(alpha, "alpha", torch.float32)
+        _dev_tensor(beta, "beta", torch.float32)
+        B, T = self._shape_in(kp, 2 * self.sqrtN, "kp")
+        if qp.shape != kp.shape or qp.dtype != kp.dtype or v.dtype != kp.dtype:
+            raise SDMError(1, "kp, qp and v must share one dtype (and kp, qp one shape)")
+        if tuple(v.shape) != (B, T, self.H, self.d_v):
+            raise SDMError(1, f"v must be [B, T, H, d_v], got {tuple(v.shape)}")
+        if tuple(alpha.shape) != (B, T, self.H) or tuple(beta.shape) != (B, T, self.H):
+            raise SDMError(1, "alpha and beta must be [B, T, H]")
+        dev = kp.device
+        dt = _in_dtype(kp)
+        if y is None:
+            y = torch.empty((B, T, self.H, self.d_v), dtype=torch.float32, device=dev)
+        if M is None:
+            if cont:
+                raise SDMError(1, "cont=True needs the state M")
+            M = torch.empty((B, self.H, self.N, self.d_v), dtype=torch.float32, device=dev)
+        _dev_tensor(y, "y", torch.float32)
+        _dev_tensor(M, "M", torch.float32)
+        if tuple(M.shape) != (B, self.H, self.N, self.d_v) or tuple(y.shape) != tuple(v.shape):
+            raise SDMError(1, "y or M has the wrong shape")
+        need = self.workspace_size(B, T, dt, variant)
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        _check(lib().sdm_forward(self._h, B, T, _ptr(kp), _ptr(qp), _ptr(v), _ptr(alpha),
+                                 _ptr(beta), dt, variant, FLAG_CONTINUE if cont else 0,
+                                 _ptr(workspace), workspace.numel(), _ptr(y), _ptr(M),
+                                 _stream(dev)))
+        return y, M

@@ -1,0 +1,247 @@
+// C ABI of libsdm: argument validation, workspace layout, stream-ordered
+// launches.  Every check happens before the first HIP call, so invalid
+// arguments never enqueue work.  See include/sdm.h for the contract.
+#include "sdm.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <new>
+#include <string>
+
+#include "sdm_internal.h"
+
+struct sdm_ctx {
+    const float *M0;
+    int H, sqrtN, d_v, W, R;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+sdm_status fail(sdm_status s, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+sdm_status hip_fail(hipError_t e, const char *what)
+{
+    return fail(SDM_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+sdm::Shape shape_of(const sdm_ctx *h, int B, int64_t T)
+{
+    sdm::Shape s;
+    s.B = B;
+    s.T = T;
+    s.H = h->H;
+    s.sqrtN = h->sqrtN;
+    s.d_v = h->d_v;
+    s.W = h->W;
+    s.R = h->R;
+    return s;
+}
+
+sdm_status check_handle_call(const sdm_ctx *h, int B, int64_t T, sdm_dtype dtype)
+{
+    if (!h) return fail(SDM_ERR_ARG, "null handle");
+    if (B < 1) return fail(SDM_ERR_ARG, "B must be >= 1 (got %d)", B);
+    if (T < 1) return fail(SDM_ERR_ARG, "T must be >= 1 (got %lld)", (long long)T);
+    if (dtype != SDM_F32 && dtype != SDM_BF16)
+        return fail(SDM_ERR_ARG, "dtype must be SDM_F32 or SDM_BF16 (got %d)", (int)dtype);
+    const double ht = (double)B * (double)T * (double)h->H;
+    if (ht >= 2147483648.0) return fail(SDM_ERR_UNSUPPORTED, "B*T*H must be < 2^31");
+    return SDM_OK;
+}
+
+// Serial workspace: token records for every (chain, token).
+size_t serial_ws_bytes(const sdm_ctx *h, int B, int64_t T)
+{
+    const sdm::RecLayout L(h->W, h->R);
+    return round_up((size_t)B * h->H * (size_t)T * (size_t)L.dwords() * 4u);
+}
+
+sdm_variant resolve_variant(const sdm_ctx *, sdm_variant v)
+{
+    return v == SDM_VARIANT_AUTO ? SDM_VARIANT_SERIAL : v;
+}
+
+sdm_status check_variant_and_ws(const sdm_ctx *h, int B, int64_t T, sdm_variant variant,
+                                size_t ws_bytes)
+{
+    const sdm_variant var = resolve_variant(h, variant);
+    if (var != SDM_VARIANT_SERIAL && var != SDM_VARIANT_TIMEPAR)
+        return fail(SDM_ERR_ARG, "unknown variant %d", (int)variant);
+    if (var == SDM_VARIANT_TIMEPAR)
+        return fail(SDM_ERR_UNSUPPORTED, "time-parallel variant not built");
+    const size_t need = serial_ws_bytes(h, B, T);
+    if (ws_bytes < need)
+        return fail(SDM_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+    return SDM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *sdm_status_string(sdm_status s)
+{
+    switch (s) {
+        case SDM_OK: return "ok";
+        case SDM_ERR_ARG: return "invalid argument";
+        case SDM_ERR_UNSUPPORTED: return "unsupported shape or option";
+        case SDM_ERR_WORKSPACE: return "workspace too small";
+        case SDM_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *sdm_last_error(void) { return g_err.c_str(); }
+
+sdm_status sdm_create(const float *M0, int H, int sqrtN, int d_v, int W, int R, sdm_handle *out)
+{
+    if (!out) return fail(SDM_ERR_ARG, "null output handle pointer");
+    *out = nullptr;
+    if (!M0) return fail(SDM_ERR_ARG, "null M0");
+    if (!aligned16(M0)) return fail(SDM_ERR_ARG, "M0 must be 16-byte aligned");
+    if (H < 1 || sqrtN < 1 || d_v < 1 || W < 1 || R < 1)
+        return fail(SDM_ERR_ARG, "H, sqrtN, d_v, W, R must be >= 1 (got %d %d %d %d %d)", H,
+                    sqrtN, d_v, W, R);
+    if (W > sqrtN || R > sqrtN)
+        return fail(SDM_ERR_ARG, "W and R must not exceed sqrtN (got W=%d R=%d sqrtN=%d)", W, R,
+                    sqrtN);
+    if (sqrtN > sdm::kMaxSqrtN)
+        return fail(SDM_ERR_UNSUPPORTED, "sqrtN > %d is not supported", sdm::kMaxSqrtN);
+    if (W > sdm::kMaxK || R > sdm::kMaxK)
+        return fail(SDM_ERR_UNSUPPORTED, "W, R > %d are not supported", sdm::kMaxK);
+    sdm_ctx *h = new (std::nothrow) sdm_ctx{M0, H, sqrtN, d_v, W, R};
+    if (!h) return fail(SDM_ERR_ARG, "out of host memory");
+    *out = h;
+    return SDM_OK;
+}
+
+sdm_status sdm_destroy(sdm_handle h)
+{
+    delete h;
+    return SDM_OK;
+}
+
+sdm_status sdm_workspace_size(sdm_handle h, int B, int64_t T, sdm_dtype dtype,
+                              sdm_variant variant, size_t *bytes)
+{
+    if (!bytes) return fail(SDM_ERR_ARG, "null bytes pointer");
+    *bytes = 0;
+    sdm_status st = check_handle_call(h, B, T, dtype);
+    if (st != SDM_OK) return st;
+    const sdm_variant v = resolve_variant(h, variant);
+    if (v == SDM_VARIANT_SERIAL) {
+        *bytes = serial_ws_bytes(h, B, T);
+        return SDM_OK;
+    }
+    if (v == SDM_VARIANT_TIMEPAR) return fail(SDM_ERR_UNSUPPORTED, "time-parallel variant not built");
+    return fail(SDM_ERR_ARG, "unknown variant %d", (int)variant);
+}
+
+sdm_status sdm_select(sdm_handle h, int B, int64_t T, const void *kp, const void *qp,
+                      sdm_dtype dtype, int32_t *Iw, float *kw, int32_t *Ir, float *qw,
+                      void *stream)
+{
+    sdm_status st = check_handle_call(h, B, T, dtype);
+    if (st != SDM_OK) return st;
+    if (!kp || !qp || !Iw || !kw || !Ir || !qw) return fail(SDM_ERR_ARG, "null tensor pointer");
+    if (!aligned16(kp) || !aligned16(qp) || !aligned16(Iw) || !aligned16(kw) || !aligned16(Ir) ||
+        !aligned16(qw))
+        return fail(SDM_ERR_ARG, "tensor pointers must be 16-byte aligned");
+    const sdm::Shape s = shape_of(h, B, T);
+    hipError_t e = sdm::launch_select(s, kp, qp, dtype == SDM_BF16, Iw, kw, Ir, qw, nullptr,
+                                      nullptr, nullptr, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "select launch");
+    return SDM_OK;
+}
+
+sdm_status sdm_prepare(sdm_handle h, int B, int64_t T, const void *kp, const void *qp,
+                       const float *alpha, const float *beta, sdm_dtype dtype,
+                       sdm_variant variant, unsigned flags, void *workspace, size_t ws_bytes,
+                       float *M, void *stream)
+{
+    sdm_status st = check_handle_call(h, B, T, dtype);
+    if (st != SDM_OK) return st;
+    if (!kp || !qp || !alpha || !beta || !M || !workspace)
+        return fail(SDM_ERR_ARG, "null tensor pointer");
+    if (!aligned16(kp) || !aligned16(qp) || !aligned16(alpha) || !aligned16(beta) ||
+        !aligned16(M) || !aligned16(workspace))
+        return fail(SDM_ERR_ARG, "tensor pointers must be 16-byte aligned");
+    if (flags & ~SDM_FLAG_CONTINUE) return fail(SDM_ERR_ARG, "unknown flags 0x%x", flags);
+    st = check_variant_and_ws(h, B, T, variant, ws_bytes);
+    if (st != SDM_OK) return st;
+
+    const sdm::Shape s = shape_of(h, B, T);
+    const hipStream_t hs = (hipStream_t)stream;
+    uint32_t *rec = static_cast<uint32_t *>(workspace);
+    hipError_t e;
+    if (!(flags & SDM_FLAG_CONTINUE)) {
+        e = sdm::launch_init(s, h->M0, M, hs);
+        if (e != hipSuccess) return hip_fail(e, "init launch");
+    }
+    e = sdm::launch_select(s, kp, qp, dtype == SDM_BF16, nullptr, nullptr, nullptr, nullptr, rec,
+                           alpha, beta, hs);
+    if (e != hipSuccess) return hip_fail(e, "select launch");
+    if (s.d_v % 4 == 0) {
+        e = sdm::launch_plan(s, rec, sdm::rw_serial_depth(), hs);
+        if (e != hipSuccess) return hip_fail(e, "plan launch");
+    }
+    return SDM_OK;
+}
+
+sdm_status sdm_apply(sdm_handle h, int B, int64_t T, const void *v, sdm_dtype dtype,
+                     sdm_variant variant, void *workspace, size_t ws_bytes, float *y, float *M,
+                     void *stream)
+{
+    sdm_status st = check_handle_call(h, B, T, dtype);
+    if (st != SDM_OK) return st;
+    if (!v || !y || !M || !workspace) return fail(SDM_ERR_ARG, "null tensor pointer");
+    if (!aligned16(v) || !aligned16(y) || !aligned16(M) || !aligned16(workspace))
+        return fail(SDM_ERR_ARG, "tensor pointers must be 16-byte aligned");
+    st = check_variant_and_ws(h, B, T, variant, ws_bytes);
+    if (st != SDM_OK) return st;
+
+    const sdm::Shape s = shape_of(h, B, T);
+    const hipStream_t hs = (hipStream_t)stream;
+    const uint32_t *rec = static_cast<const uint32_t *>(workspace);
+    const hipError_t e = s.d_v % 4 == 0
+                             ? sdm::launch_rw_serial(s, rec, v, dtype == SDM_BF16, y, M, hs)
+                             : sdm::launch_rw_simple(s, rec, v, dtype == SDM_BF16, y, M, hs);
+    if (e != hipSuccess) return hip_fail(e, "write/read launch");
+    return SDM_OK;
+}
+
+sdm_status sdm_forward(sdm_handle h, int B, int64_t T, const void *kp, const void *qp,
+                       const void *v, const float *alpha, const float *beta, sdm_dtype dtype,
+                       sdm_variant variant, unsigned flags, void *workspace, size_t ws_bytes,
+                       float *y, float *M, void *stream)
+{
+    // validate everything before enqueueing either half
+    sdm_status st = check_handle_call(h, B, T, dtype);
+    if (st != SDM_OK) return st;
+    if (!v || !y) return fail(SDM_ERR_ARG, "null tensor pointer");
+    if (!aligned16(v) || !aligned16(y))
+        return fail(SDM_ERR_ARG, "tensor pointers must be 16-byte aligned");
+    st = sdm_prepare(h, B, T, kp, qp, alpha, beta, dtype, variant, flags, workspace, ws_bytes, M,
+                     stream);
+    if (st != SDM_OK) return st;
+    return sdm_apply(h, B, T, v, dtype, variant, workspace, ws_bytes, y, M, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Internal declarations shared by the HIP sources of libsdm (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sdm {
+
+constexpr int kMaxK = 64;         // largest W or R
+constexpr int kMaxSqrtN = 1024;   // largest sqrtN (N <= 2^20 slots)
+constexpr int kMaxDepth = 8;      // largest cross-token prefetch depth
+
+// A slot word of a token record: the slot index in the low 20 bits; the
+// planner adds a forwarding code above it when an earlier token (at most
+// kMaxDepth-1 tokens back, or the same token for a read) wrote the slot.
+constexpr int kSlotBits = 20;
+constexpr uint32_t kSlotMask = (1u << kSlotBits) - 1u;
+constexpr int kFwdWShift = 20;              // position w' in that token's write list
+constexpr uint32_t kFwdWMask = 63u;
+constexpr int kFwdDShift = 26;              // token distance d = t - t'
+constexpr uint32_t kFwdDMask = 7u;
+constexpr uint32_t kFwdValid = 1u << 29;
+
+// Per (chain, token) record written by select and consumed by the write/read
+// kernels.  A chain is one (sequence b, head h); records of a chain are
+// contiguous in t.  Arrays are padded to multiples of 16 dwords: the serial
+// kernel's 16 lane groups each load ceil(W/16) consecutive entries, so the
+// padding covers every group's load, and every record is 64-byte aligned.
+//   ws[Wp]  write slot words     wa[Wp]  alpha*(1 - beta*k)   wc[Wp]  beta*k
+//   rs[Rp]  read slot words      rq[Rp]  q weights
+struct RecLayout {
+    int Wp, Rp;
+    __host__ __device__ RecLayout(int W, int R) : Wp((W + 15) & ~15), Rp((R + 15) & ~15) {}
+    __host__ __device__ int ws() const { return 0; }
+    __host__ __device__ int wa() const { return Wp; }
+    __host__ __device__ int wc() const { return 2 * Wp; }
+    __host__ __device__ int rs() const { return 3 * Wp; }
+    __host__ __device__ int rq() const { return 3 * Wp + Rp; }
+    __host__ __device__ int dwords() const { return 3 * Wp + 2 * Rp; }
+};
+
+struct Shape {
+    int B;
+    int64_t T;
+    int H, sqrtN, d_v, W, R;
+    int64_t N() const { return (int64_t)sqrtN * sqrtN; }
+    int64_t ht() const { return (int64_t)B * T * H; }
+};
+
+// ---- launchers (each returns the launch error, if any) ----
+
+// Selection.  With rec == nullptr it writes the API layout (Iw, kw, Ir, qw,
+// [B][T][H][K]); otherwise it writes token records (needs alpha, beta).
+hipError_t launch_select(const Shape &s, const void *kp, const void *qp, bool bf16,
+                         int32_t *Iw, float *kw, int32_t *Ir, float *qw,
+                         uint32_t *rec, const float *alpha, const float *beta,
+                         hipStream_t st);
+
+// M[b] <- M0 for every sequence b.
+hipError_t launch_init(const Shape &s, const float *M0, float *M, hipStream_t st);
+
+// Adds forwarding codes (distance < depth) to the slot words of all records.
+hipError_t launch_plan(const Shape &s, uint32_t *rec, int depth, hipStream_t st);
+
+// Token-serial write/read over the records (float4 path, d_v % 4 == 0).
+hipError_t launch_rw_serial(const Shape &s, const uint32_t *rec, const void *v, bool bf16,
+                            float *y, float *M, hipStream_t st);
+int rw_serial_depth();  // prefetch depth the serial kernel is compiled for
+
+// Token-serial write/read, one column per lane, no prefetch (any d_v).
+hipError_t launch_rw_simple(const Shape &s, const uint32_t *rec, const void *v, bool bf16,
+                            float *y, float *M, hipStream_t st);
+
+}  // namespace sdm

@@ -1,0 +1,375 @@
+// Product-key top-K selection for the SDM core on gfx950.
+//
+// Per head-token and per list (k' -> W write slots, q' -> R read slots) one
+// 64-lane wavefront:
+//   stage 1  the two halves x_1 = x[0, sqrtN) and x_2 = x[sqrtN, 2 sqrtN) are
+//            sorted in registers (bitonic network, lane-major layout, 64-bit
+//            keys = order-preserving value bits : inverted index) and their
+//            first K entries kept;
+//   stage 2  candidate pairs (a, b) of per-half ranks with (a+1)(b+1) <= K are
+//            scored with the exact sum x_1 + x_2 (TwoSum pair hi + lo in
+//            float32, compared lexicographically = exact real order) and the
+//            first K in the order (score desc, n = i*sqrtN + j asc) are kept:
+//            each 64-candidate column is sorted across lanes, then columns
+//            are merged pairwise keeping the top 64;
+//   weights  softmax over the K selected scores.
+// The product-key identity (select within each half first, then among sums of
+// survivors) is stated in the explainer "Sparse Delta Memory：通过稀疏性扩展线性
+// RNN 的状态容量", §3.1 step 1, and in "Technical Summary: Sparse Delta Memory
+// (SDM)", Core Mechanism 2.  The pruning to (a+1)(b+1) <= K is exact: a pair
+// of ranks (a, b) is preceded by every pair (a', b') with a' <= a, b' <= b
+// (score at least as large, and on an equal score a smaller flat index), so
+// with (a+1)(b+1) > K at least K pairs come before it.
+#include "sdm_internal.h"
+
+namespace sdm {
+namespace {
+
+constexpr int kTabMax = 320;  // >= number of pruned pairs for K = 64 (280)
+
+__device__ __forceinline__ uint32_t f2ord(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;  // -0 and +0 are the same score
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float ord2f(uint32_t o)
+{
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+__device__ __forceinline__ uint32_t shx(uint32_t v, int m)
+{
+    return (uint32_t)__shfl_xor((int)v, m, 64);
+}
+
+__device__ __forceinline__ uint32_t shl(uint32_t v, int src)
+{
+    return (uint32_t)__shfl((int)v, src, 64);
+}
+
+__device__ __forceinline__ uint64_t shx64(uint64_t v, int m)
+{
+    const uint32_t lo = shx((uint32_t)v, m), hi = shx((uint32_t)(v >> 32), m);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t shl64(uint64_t v, int src)
+{
+    const uint32_t lo = shl((uint32_t)v, src), hi = shl((uint32_t)(v >> 32), src);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Orders LDS traffic between the lanes of one wavefront.
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ void two_sum(float a, float b, float &s, float &e)
+{
+    s = a + b;
+    const float bv = s - a;
+    const float av = s - bv;
+    e = (a - av) + (b - bv);
+}
+
+__device__ __forceinline__ float load_elem(const void *x, bool bf16, int64_t i)
+{
+    if (bf16) return __uint_as_float((uint32_t)((const uint16_t *)x)[i] << 16);
+    return ((const float *)x)[i];
+}
+
+// Sort 64*E keys of each of two halves, descending; element e = lane*E + r.
+template <int E>
+__device__ __forceinline__ void sort_halves_desc(uint64_t (&k1)[E], uint64_t (&k2)[E], int lane)
+{
+    constexpr int n = 64 * E;
+#pragma unroll
+    for (int kk = 2; kk <= n; kk <<= 1) {
+#pragma unroll
+        for (int j = kk >> 1; j > 0; j >>= 1) {
+            if (j < E) {  // partner in the same lane
+#pragma unroll
+                for (int r = 0; r < E; r++) {
+                    if ((r & j) == 0) {
+                        const int e = lane * E + r;
+                        const bool desc = (e & kk) == 0;
+                        uint64_t a = k1[r], b = k1[r | j];
+                        bool sw = desc ? (a < b) : (a > b);
+                        k1[r] = sw ? b : a;
+                        k1[r | j] = sw ? a : b;
+                        a = k2[r];
+                        b = k2[r | j];
+                        sw = desc ? (a < b) : (a > b);
+                        k2[r] = sw ? b : a;
+                        k2[r | j] = sw ? a : b;
+                    }
+                }
+            } else {  // partner in lane ^ (j / E), same register
+                const int lm = j / E;
+#pragma unroll
+                for (int r = 0; r < E; r++) {
+                    const int e = lane * E + r;
+                    const bool keep_max = ((e & j) == 0) == ((e & kk) == 0);
+                    const uint64_t o1 = shx64(k1[r], lm);
+                    const uint64_t o2 = shx64(k2[r], lm);
+                    const uint64_t m1 = k1[r], m2 = k2[r];
+                    k1[r] = keep_max ? (m1 > o1 ? m1 : o1) : (m1 < o1 ? m1 : o1);
+                    k2[r] = keep_max ? (m2 > o2 ? m2 : o2) : (m2 < o2 ? m2 : o2);
+                }
+            }
+        }
+    }
+}
+
+// Does candidate (ka, na) come before (kb, nb)?  Higher exact score first,
+// then lower flat slot index.
+__device__ __forceinline__ bool before(uint64_t ka, uint32_t na, uint64_t kb, uint32_t nb)
+{
+    return ka > kb || (ka == kb && na < nb);
+}
+
+__device__ __forceinline__ void ce_lane(uint64_t &k, uint32_t &n, int m, bool keep_first)
+{
+    const uint64_t ok = shx64(k, m);
+    const uint32_t on = shx(n, m);
+    const bool mine_first = before(k, n, ok, on);
+    if (keep_first != mine_first) {
+        k = ok;
+        n = on;
+    }
+}
+
+// Sort one 64-entry column (one entry per lane) in canonical order.
+__device__ __forceinline__ void col_sort(uint64_t &k, uint32_t &n, int lane)
+{
+#pragma unroll
+    for (int kk = 2; kk <= 64; kk <<= 1) {
+#pragma unroll
+        for (int j = kk >> 1; j > 0; j >>= 1)
+            ce_lane(k, n, j, ((lane & j) == 0) == ((lane & kk) == 0));
+    }
+}
+
+// (ka, na) <- first 64 of two sorted columns, sorted.
+__device__ __forceinline__ void col_merge(uint64_t &ka, uint32_t &na, uint64_t kb, uint32_t nb,
+                                          int lane)
+{
+    const uint64_t rk = shl64(kb, 63 - lane);
+    const uint32_t rn = shl(nb, 63 - lane);
+    if (!before(ka, na, rk, rn)) {
+        ka = rk;
+        na = rn;
+    }
+#pragma unroll
+    for (int j = 32; j > 0; j >>= 1) ce_lane(ka, na, j, (lane & j) == 0);
+}
+
+struct SelArgs {
+    const void *kp, *qp;
+    int bf16;
+    int64_t T;
+    int H, sqrtN, W, R;
+    int64_t n_ht;
+    int32_t *Iw, *Ir;
+    float *kw, *qw;
+    uint32_t *rec;
+    int rec_dwords, Wp, Rp;
+    const float *alpha, *beta;
+};
+
+template <int E>
+__global__ __launch_bounds__(256) void select_kernel(SelArgs a)
+{
+    constexpr int E2 = 5;  // candidate columns: 5*64 >= 280 pairs for K = 64
+    __shared__ uint16_t tab[2][kTabMax];
+    __shared__ int tabn[2];
+    __shared__ float sv[4][2][64];
+    __shared__ uint32_t si[4][2][64];
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+
+    // candidate tables: row a holds K/(a+1) pairs (a, 0..K/(a+1)-1)
+    if (wv == 0) {
+        for (int list = 0; list < 2; list++) {
+            const int K = list ? a.R : a.W;
+            const int len = lane < K ? K / (lane + 1) : 0;
+            int incl = len;  // inclusive prefix sum over lanes
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int t = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += t;
+            }
+            const int off = incl - len;
+            for (int b = 0; b < len; b++) tab[list][off + b] = (uint16_t)((lane << 8) | b);
+            if (lane == 63) tabn[list] = incl;
+        }
+    }
+    __syncthreads();
+
+    const int S = a.sqrtN;
+    const int64_t items = 2 * a.n_ht;
+    for (int64_t it = (int64_t)blockIdx.x * 4 + wv; it < items; it += (int64_t)gridDim.x * 4) {
+        const int list = (int)(it & 1);
+        const int64_t ht = it >> 1;
+        const int K = list ? a.R : a.W;
+        const void *x = list ? a.qp : a.kp;
+        const int64_t base = ht * 2 * S;
+
+        // ---- stage 1: sort each half, keep the first K ----
+        uint64_t k1[E], k2[E];
+#pragma unroll
+        for (int r = 0; r < E; r++) {
+            const int e = lane * E + r;
+            if (e < S) {
+                const uint32_t inv = ~(uint32_t)e;
+                k1[r] = ((uint64_t)f2ord(load_elem(x, a.bf16, base + e)) << 32) | inv;
+                k2[r] = ((uint64_t)f2ord(load_elem(x, a.bf16, base + S + e)) << 32) | inv;
+            } else {
+                k1[r] = 0;  // below every finite score
+                k2[r] = 0;
+            }
+        }
+        sort_halves_desc<E>(k1, k2, lane);
+#pragma unroll
+        for (int r = 0; r < E; r++) {
+            const int e = lane * E + r;
+            if (e < K) {
+                sv[wv][0][e] = ord2f((uint32_t)(k1[r] >> 32));
+                si[wv][0][e] = ~(uint32_t)k1[r];
+                sv[wv][1][e] = ord2f((uint32_t)(k2[r] >> 32));
+                si[wv][1][e] = ~(uint32_t)k2[r];
+            }
+        }
+        wave_sync();
+
+        // ---- stage 2: exact sums of the pruned rank pairs ----
+        const int C = tabn[list];
+        const int e2 = (C + 63) >> 6;
+        uint64_t ck[E2];
+        uint32_t cn[E2];
+#pragma unroll
+        for (int r = 0; r < E2; r++) {
+            const int c = r * 64 + lane;
+            ck[r] = 0;
+            cn[r] = 0xFFFFFFFFu;
+            if (c < C) {
+                const uint32_t ab = tab[list][c];
+                const int ra = (int)(ab >> 8), rb = (int)(ab & 0xFF);
+                float hi, lo;
+                two_sum(sv[wv][0][ra], sv[wv][1][rb], hi, lo);
+                ck[r] = ((uint64_t)f2ord(hi) << 32) | f2ord(lo);
+                cn[r] = si[wv][0][ra] * (uint32_t)S + si[wv][1][rb];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < E2; r++)
+            if (r < e2) col_sort(ck[r], cn[r], lane);
+#pragma unroll
+        for (int s = 1; s < E2; s <<= 1) {
+#pragma unroll
+            for (int r = 0; r + s < E2; r += 2 * s)
+                if (r + s < e2) col_merge(ck[r], cn[r], ck[r + s], cn[r + s], lane);
+        }
+        wave_sync();  // sv/si are rewritten by the next item
+
+        // ---- weights: softmax over the K selected scores ----
+        const uint64_t key = ck[0];
+        const uint32_t n = cn[0];
+        const float hi = ord2f((uint32_t)(key >> 32));
+        const float lo = ord2f((uint32_t)key);
+        const float hi0 = __shfl(hi, 0, 64);
+        const float lo0 = __shfl(lo, 0, 64);
+        const float ex = lane < K ? expf((hi - hi0) + (lo - lo0)) : 0.0f;
+        float z = ex;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o, 64);
+        const float w = ex / z;
+
+        if (a.rec == nullptr) {
+            if (lane < K) {
+                if (list == 0) {
+                    a.Iw[ht * K + lane] = (int32_t)n;
+                    a.kw[ht * K + lane] = w;
+                } else {
+                    a.Ir[ht * K + lane] = (int32_t)n;
+                    a.qw[ht * K + lane] = w;
+                }
+            }
+        } else {
+            // record of chain (b, h) at token t; ht = (b*T + t)*H + h
+            const int64_t bt = ht / a.H;
+            const int h = (int)(ht - bt * a.H);
+            const int64_t b = bt / a.T;
+            const int64_t t = bt - b * a.T;
+            uint32_t *rec = a.rec + (((b * a.H + h) * a.T) + t) * a.rec_dwords;
+            if (list == 0) {
+                if (lane < a.Wp) {
+                    const float al = a.alpha[ht], be = a.beta[ht];
+                    const bool ok = lane < K;
+                    const float c = be * w;
+                    rec[lane] = ok ? n : 0u;
+                    reinterpret_cast<float *>(rec)[a.Wp + lane] = ok ? al * (1.0f - c) : 1.0f;
+                    reinterpret_cast<float *>(rec)[2 * a.Wp + lane] = ok ? c : 0.0f;
+                }
+            } else {
+                if (lane < a.Rp) {
+                    const bool ok = lane < K;
+                    rec[3 * a.Wp + lane] = ok ? n : 0u;
+                    reinterpret_cast<float *>(rec)[3 * a.Wp + a.Rp + lane] = ok ? w : 0.0f;
+                }
+            }
+        }
+    }
+}
+
+template <int E>
+hipError_t launch_e(const SelArgs &args, hipStream_t st)
+{
+    const int64_t items = 2 * args.n_ht;
+    int64_t blocks = (items + 3) / 4;
+    if (blocks > 16384) blocks = 16384;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(select_kernel<E>, dim3((unsigned)blocks), dim3(256), 0, st, args);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_select(const Shape &s, const void *kp, const void *qp, bool bf16,
+                         int32_t *Iw, float *kw, int32_t *Ir, float *qw, uint32_t *rec,
+                         const float *alpha, const float *beta, hipStream_t st)
+{
+    SelArgs a{};
+    a.kp = kp;
+    a.qp = qp;
+    a.bf16 = bf16 ? 1 : 0;
+    a.T = s.T;
+    a.H = s.H;
+    a.sqrtN = s.sqrtN;
+    a.W = s.W;
+    a.R = s.R;
+    a.n_ht = s.ht();
+    a.Iw = Iw;
+    a.kw = kw;
+    a.Ir = Ir;
+    a.qw = qw;
+    a.rec = rec;
+    const RecLayout L(s.W, s.R);
+    a.rec_dwords = L.dwords();
+    a.Wp = L.Wp;
+    a.Rp = L.Rp;
+    a.alpha = alpha;
+    a.beta = beta;
+    if (s.sqrtN <= 64) return launch_e<1>(a, st);
+    if (s.sqrtN <= 128) return launch_e<2>(a, st);
+    if (s.sqrtN <= 256) return launch_e<4>(a, st);
+    if (s.sqrtN <= 512) return launch_e<8>(a, st);
+    return launch_e<16>(a, st);
+}
+
+}  // namespace sdm

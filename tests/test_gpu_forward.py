@@ -1,0 +1,198 @@
+"""GPU parity of sdm_forward (select + write + read) against the float64 oracle,
+plus exact invariants of the recurrence checked on the GPU alone."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sdm_inputs as si
+import sparse_memory_linear_select_amd as sdm
+from gpu_util import (TOL, TOL_LONG, Timer, assert_close, check_selection, gpu_forward, log,
+                      make_core, to_dev, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+def _parity(wl, T=None, c0=0, c1=None, tol=TOL, variant=sdm.AUTO, d=None):
+    log(f"forward: {wl.name} B={wl.B} T={T or wl.T} H={wl.H} S={wl.sqrtN} d_v={wl.d_v} "
+        f"W={wl.W} R={wl.R} {wl.dtype} cols=[{c0},{c1 if c1 is not None else wl.d_v})")
+    if d is None:
+        d = si.generate(wl, T=T)
+    core, dd, y, M = gpu_forward(d, wl.W, wl.R, variant)
+    c1 = wl.d_v if c1 is None else c1
+    ref = oracle.forward(d, wl.sqrtN, wl.W, wl.R, c0=c0, c1=c1)
+    Iw, kw, Ir, qw = [o.cpu().numpy() for o in core.select(dd["kp"], dd["qp"])]
+    check_selection(Iw, kw, ref["Iw"], ref["kw"], "write set")
+    check_selection(Ir, qw, ref["Ir"], ref["qw"], "read set")
+    ey = assert_close(y[..., c0:c1].cpu().numpy(), ref["y"], tol, "y")
+    eM = assert_close(M[..., c0:c1].cpu().numpy(), ref["M"], tol, "M")
+    log(f"  max rel err y {ey:.2e}  M {eM:.2e}")
+    return d, dd, y, M
+
+
+def test_forward_tiny_workload():
+    _parity(si.WORKLOADS[0])
+
+
+SHAPES = [
+    # (B, T, H, sqrtN, d_v, W, R, dtype, reuse)
+    (2, 37, 3, 8, 20, 3, 5, "f32", 0.0),      # ragged column slice, W != R
+    (1, 13, 1, 4, 30, 4, 2, "f32", 0.0),      # d_v % 4 != 0: one-column-per-lane path
+    (1, 1, 1, 1, 4, 1, 1, "f32", 0.0),        # N = 1, single token
+    (2, 200, 2, 16, 48, 16, 16, "f32", 0.0),  # W = R = sqrtN
+    (1, 257, 2, 128, 64, 64, 64, "f32", 0.3),  # the 1.4B-style slot count, key reuse
+    (1, 91, 1, 32, 36, 32, 20, "bf16", 0.5),   # bf16 inputs
+    (3, 50, 1, 9, 8, 9, 9, "f32", 0.0),       # every token writes 9 of 81 slots
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[str(s[:7]) for s in SHAPES])
+def test_forward_shapes(shape):
+    B, T, H, S, D, W, R, dt, reuse = shape
+    wl = si.Workload("shape", B=B, T=T, H=H, sqrtN=S, d_v=D, W=W, R=R, dtype=dt, reuse=reuse,
+                     seed=500 + T)
+    _parity(wl)
+
+
+def test_forward_same_keys_every_token():
+    """Every token writes the same slots and reads them back: each row is
+    rewritten at every step, so every reference goes through the forwarding
+    path (previous token for writes, same token for reads)."""
+    wl = si.Workload("same keys", B=2, T=64, H=2, sqrtN=16, d_v=32, W=8, R=8, dtype="f32",
+                     reuse=0.0, seed=9)
+    d = si.generate(wl)
+    d["kp"][:] = d["kp"][:, :1]
+    d["qp"][:] = d["kp"]
+    _parity(wl, d=d)
+
+
+def test_forward_clustered_keys():
+    """Keys drawn from a few prototypes: slots recur at distances 1..8."""
+    wl = si.Workload("clustered", B=1, T=300, H=2, sqrtN=32, d_v=64, W=32, R=32, dtype="f32",
+                     reuse=0.0, seed=10)
+    d = si.generate(wl)
+    rng = np.random.default_rng(3)
+    proto = d["kp"][0, :5].copy()
+    pick = rng.integers(0, 5, size=wl.T)
+    d["kp"][0] = proto[pick] + 0.05 * rng.standard_normal(d["kp"][0].shape).astype(np.float32)
+    d["qp"][0] = proto[rng.integers(0, 5, size=wl.T)]
+    _parity(wl, d=d)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_forward_full_workload(cfg):
+    """The full workload on the GPU; the oracle computes every token of every
+    chain for a window of 16 columns (columns never interact)."""
+    wl = si.WORKLOADS[cfg]
+    tol = TOL_LONG if cfg == 4 else TOL
+    c0 = {1: 496, 2: 504, 3: 0, 4: 1024}[cfg]
+    with Timer("generate"):
+        d = si.generate(wl)
+    with Timer("gpu + oracle"):
+        _parity(wl, d=d, c0=c0, c1=c0 + 16, tol=tol)
+
+
+# ---------------------------------------------------------------- invariants
+
+def _small(seed, **kw):
+    p = dict(B=2, T=40, H=2, sqrtN=16, d_v=32, W=8, R=8, dtype="f32", reuse=0.0, seed=seed)
+    p.update(kw)
+    wl = si.Workload("inv", **p)
+    return wl, si.generate(wl)
+
+
+def test_unselected_rows_bit_unchanged():
+    wl, d = _small(21)
+    d["kp"][..., :wl.sqrtN] = -8.0
+    d["kp"][..., :2] = 8.0
+    core, dd, y, M = gpu_forward(d, wl.W, wl.R)
+    Iw = core.select(dd["kp"], dd["qp"])[0].cpu().numpy()
+    M = M.cpu().numpy()
+    for b in range(wl.B):
+        for h in range(wl.H):
+            never = np.setdiff1d(np.arange(wl.N), np.unique(Iw[b, :, h]))
+            assert never.size > wl.N // 2
+            np.testing.assert_array_equal(M[b, h, never], d["M0"][h, never])
+
+
+def test_overwrite_gate_sets_row_to_v():
+    """alpha = beta = 1, W = 1 (k = 1): a written row equals v_t bit for bit."""
+    wl, d = _small(22, W=1)
+    d["alpha"][:] = 1.0
+    d["beta"][:] = 1.0
+    core, dd, y, M = gpu_forward(d, 1, wl.R)
+    Iw = core.select(dd["kp"], dd["qp"])[0].cpu().numpy()
+    M = M.cpu().numpy()
+    for b in range(wl.B):
+        for h in range(wl.H):
+            last = {int(Iw[b, t, h, 0]): t for t in range(wl.T)}
+            for s, t in last.items():
+                np.testing.assert_array_equal(M[b, h, s], d["v"][b, t, h])
+
+
+def test_one_hot_read_returns_row():
+    """R = 1 (q = 1): y of the last token is the final row of its read slot."""
+    wl, d = _small(23, R=1)
+    core, dd, y, M = gpu_forward(d, wl.W, 1)
+    Ir = core.select(dd["kp"], dd["qp"])[2].cpu().numpy()
+    y, M = y.cpu().numpy(), M.cpu().numpy()
+    for b in range(wl.B):
+        for h in range(wl.H):
+            np.testing.assert_array_equal(y[b, -1, h], M[b, h, Ir[b, -1, h, 0]])
+
+
+def test_dominant_read_weight():
+    """A score gap above 800 leaves weight 1 on one slot and exactly 0 elsewhere."""
+    wl, d = _small(24, R=4)
+    S = wl.sqrtN
+    d["qp"][:] = 0.0
+    d["qp"][..., 0] = 900.0
+    d["qp"][..., S + 1:] = -900.0
+    core, dd, y, M = gpu_forward(d, wl.W, 4)
+    _, _, Ir, qw = [o.cpu().numpy() for o in core.select(dd["kp"], dd["qp"])]
+    assert (Ir[..., 0] == 0).all() and (qw[..., 0] == 1).all() and (qw[..., 1:] == 0).all()
+    np.testing.assert_array_equal(y[:, -1].cpu().numpy(), M[:, :, 0].cpu().numpy())
+
+
+def test_scaling_by_two_is_exact():
+    wl, d = _small(25, sqrtN=32, d_v=64, W=32, R=32, T=120)
+    _, _, y1, M1 = gpu_forward(d, wl.W, wl.R)
+    d2 = dict(d, M0=d["M0"] * 2, v=d["v"] * 2)
+    _, _, y2, M2 = gpu_forward(d2, wl.W, wl.R)
+    assert torch.equal(y2, 2 * y1) and torch.equal(M2, 2 * M1)
+
+
+def test_runs_are_bitwise_deterministic():
+    wl, d = _small(26, sqrtN=64, d_v=128, W=64, R=64, T=200, B=1)
+    core, dd, y1, M1 = gpu_forward(d, wl.W, wl.R)
+    y2, M2 = core.forward(dd["kp"], dd["qp"], dd["v"], dd["alpha"], dd["beta"])
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(M1, M2)
+
+
+def test_continue_flag_splits_a_sequence():
+    """Two calls (the second continuing from the first's state) give the same
+    outputs, bit for bit, as one call over the whole sequence."""
+    wl, d = _small(27, sqrtN=32, d_v=64, W=16, R=16, T=90)
+    core, dd, y, M = gpu_forward(d, wl.W, wl.R)
+    k = 37
+    part = {n: dd[n][:, :k].contiguous() for n in ("kp", "qp", "v", "alpha", "beta")}
+    rest = {n: dd[n][:, k:].contiguous() for n in ("kp", "qp", "v", "alpha", "beta")}
+    y1, M1 = core.forward(part["kp"], part["qp"], part["v"], part["alpha"], part["beta"])
+    y2, M2 = core.forward(rest["kp"], rest["qp"], rest["v"], rest["alpha"], rest["beta"],
+                          M=M1, cont=True)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([y1, y2], 1), y) and torch.equal(M2, M)
+
+
+def test_forward_rejects_bad_tensors():
+    wl, d = _small(28)
+    dd = upload(d)
+    core = make_core(dd, wl.W, wl.R)
+    with pytest.raises(sdm.SDMError):
+        core.forward(dd["kp"], dd["qp"], dd["v"].to(torch.bfloat16), dd["alpha"], dd["beta"])
+    with pytest.raises(sdm.SDMError):
+        core.forward(dd["kp"][:, :, :1], dd["qp"], dd["v"], dd["alpha"], dd["beta"])
+    with pytest.raises(sdm.SDMError) as e:
+        core.forward(dd["kp"], dd["qp"], dd["v"], dd["alpha"], dd["beta"], variant=sdm.TIMEPAR)
+    assert e.value.status in (1, 2)
