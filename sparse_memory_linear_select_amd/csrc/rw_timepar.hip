@@ -1,0 +1,467 @@
+// Time-parallel write/read schedule of the SDM core.
+//
+// The recurrence of one chain (sequence b, head h) is, per slot, a sequence of
+// affine maps row <- a*row + c*v_t (a = alpha_t(1 - beta_t k), c = beta_t k:
+// the forget gate and delta write of the explainer "Sparse Delta Memory：通过
+// 稀疏性扩展线性 RNN 的状态容量", §3.1 step 2), and a read at token t sees the
+// row after every write at a token <= t (§3.1 step 3).  Slots never interact,
+// so the tokens are cut into epochs of E tokens and, per epoch:
+//
+//   sort     (all epochs at once, before the recurrence) the E*W write events
+//            of the epoch are sorted by slot with a stable LSD radix sort, so
+//            each slot's writes form one segment in time order; every read
+//            gets a link (first write of its slot in the epoch, number of
+//            those at tokens <= its own);
+//   read     each read gathers the row as it was at the epoch start, replays
+//            its linked writes in time order and adds q * row to y_t;
+//   update   each segment loads its row once, applies all its writes in time
+//            order and stores it once.
+//
+// Within an epoch everything is parallel; epochs follow each other in stream
+// order (read of epoch e, update of e, read of e+1, ...).  Each row value is
+// produced by the same float32 operations, in the same order, as in the
+// token-serial schedule, so both schedules give identical M; y uses the same
+// lane mapping and reduction order as the serial kernel with 8 lanes per row.
+#include "sdm_internal.h"
+
+namespace sdm {
+namespace {
+
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr uint32_t kOff = 0x80000000u;
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kLPR = 8;               // lanes (x float4) per row: 128-byte row slices
+constexpr int kRPI = 64 / kLPR;       // row groups per wave
+constexpr int kSortThreads = 1024;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ float4 buf_load4(rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+__device__ __forceinline__ void buf_store4(float4 v, rsrc_t r, uint32_t off)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(
+        __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v), r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ float4 fma4(float a, float4 x, float c, float4 v)
+{
+    return make_float4(fmaf(a, x.x, c * v.x), fmaf(a, x.y, c * v.y), fmaf(a, x.z, c * v.z),
+                       fmaf(a, x.w, c * v.w));
+}
+
+template <bool BF16>
+__device__ __forceinline__ float4 load_v(const void *v, int64_t off)
+{
+    if constexpr (BF16) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(v) + off);
+        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+    } else {
+        return *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(v) + off);
+    }
+}
+
+struct TPArgs {
+    const uint32_t *rec;  // token records (slots, coefficients)
+    TPEntry *sorted;      // [chain][T*W] sorted write events, epoch regions
+    uint64_t *tmpA, *tmpB;  // [chain][T*W] radix ping-pong (key << 32 | event)
+    uint32_t *segs;       // [chain][T*W] segment starts (epoch regions)
+    uint32_t *nseg;       // [chain][nepoch]
+    uint32_t *rlink;      // [chain][T][R] (first << 16) | count
+    const void *v;
+    float *y, *M;
+    int64_t T, N;
+    int H, d_v, W, R, Wp, Rp, rec_dwords;
+    int E, nepoch, passes;
+    int64_t chains;
+};
+
+// ------------------------------------------------------------------ sort
+
+__global__ __launch_bounds__(kSortThreads) void tp_sort_kernel(TPArgs a)
+{
+    __shared__ uint32_t bins[256];
+    __shared__ uint32_t wcnt[kSortThreads / 64][256];
+    __shared__ uint32_t scan_tmp[kSortThreads / 64];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    const int64_t chain = blockIdx.x / a.nepoch;
+    const int ep = (int)(blockIdx.x - chain * a.nepoch);
+    const int64_t t0 = (int64_t)ep * a.E;
+    const int ne = (int)((a.T - t0) < a.E ? (a.T - t0) : a.E);  // tokens in this epoch
+    const int n = ne * a.W;                                      // write events
+    const int64_t base = chain * a.T * a.W + t0 * a.W;          // epoch region
+    const uint32_t *recc = a.rec + (chain * a.T + t0) * a.rec_dwords;
+    const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    for (int p = 0; p < a.passes; p++) {
+        const int shift = 8 * p;
+        const uint64_t *src = (p & 1) ? a.tmpA + base : a.tmpB + base;  // unused when p == 0
+        uint64_t *dst = (p & 1) ? a.tmpB + base : a.tmpA + base;
+        const bool last = p == a.passes - 1;
+        auto item = [&](int j) -> uint64_t {  // (slot << 32) | event j
+            if (p == 0) {
+                const int tl = j / a.W, w = j - tl * a.W;
+                return ((uint64_t)(recc[(int64_t)tl * a.rec_dwords + w] & kSlotMask) << 32) |
+                       (uint32_t)j;
+            }
+            return src[j];
+        };
+        // histogram of this digit
+        if (tid < 256) bins[tid] = 0;
+        __syncthreads();
+        for (int j = tid; j < n; j += kSortThreads)
+            atomicAdd(&bins[(uint32_t)(item(j) >> (32 + shift)) & 255u], 1u);
+        __syncthreads();
+        if (wv == 0) {  // exclusive scan of 256 bins, 4 per lane
+            uint32_t c[4], s = 0;
+            for (int k = 0; k < 4; k++) {
+                c[k] = bins[lane * 4 + k];
+                s += c[k];
+            }
+            uint32_t incl = s;
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t t = (uint32_t)__shfl_up((int)incl, o, 64);
+                if (lane >= o) incl += t;
+            }
+            uint32_t run = incl - s;
+            for (int k = 0; k < 4; k++) {
+                bins[lane * 4 + k] = run;
+                run += c[k];
+            }
+        }
+        __syncthreads();
+        // stable scatter, one tile of kSortThreads events at a time
+        for (int tb = 0; tb < n; tb += kSortThreads) {
+            const int j = tb + tid;
+            const bool valid = j < n;
+            const uint64_t it = valid ? item(j) : 0;
+            const uint32_t dg = (uint32_t)(it >> (32 + shift)) & 255u;
+            for (int k = tid; k < (kSortThreads / 64) * 256; k += kSortThreads)
+                (&wcnt[0][0])[k] = 0;
+            uint64_t peers = __ballot(valid);
+            for (int bit = 0; bit < 8; bit++) {
+                const uint64_t m = __ballot((dg >> bit) & 1u);
+                peers &= ((dg >> bit) & 1u) ? m : ~m;
+            }
+            const uint32_t rank = (uint32_t)__popcll(peers & lanes_below);
+            __syncthreads();
+            if (valid && rank == 0) wcnt[wv][dg] = (uint32_t)__popcll(peers);
+            __syncthreads();
+            if (tid < 256) {  // per digit: offsets of each wave's run, in wave order
+                uint32_t run = bins[tid];
+                for (int w = 0; w < kSortThreads / 64; w++) {
+                    const uint32_t c = wcnt[w][tid];
+                    wcnt[w][tid] = run;
+                    run += c;
+                }
+                bins[tid] = run;
+            }
+            __syncthreads();
+            if (valid) {
+                const uint32_t pos = wcnt[wv][dg] + rank;
+                if (!last) {
+                    dst[pos] = it;
+                } else {  // final order: write the 16-byte entries
+                    const uint32_t ev = (uint32_t)it;
+                    const int tl = (int)(ev / (uint32_t)a.W), w = (int)(ev - tl * a.W);
+                    const float *rf = reinterpret_cast<const float *>(recc + (int64_t)tl * a.rec_dwords);
+                    TPEntry e;
+                    e.slot = (uint32_t)(it >> 32);
+                    e.tw = ((uint32_t)tl << 6) | (uint32_t)w;
+                    e.a = rf[a.Wp + w];
+                    e.c = rf[2 * a.Wp + w];
+                    a.sorted[base + pos] = e;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    __syncthreads();  // the sorted entries of this epoch are complete (workgroup scope)
+
+    // segment starts: positions whose slot differs from the previous one
+    const TPEntry *se = a.sorted + base;
+    uint32_t *segs = a.segs + base;
+    uint32_t nfound = 0;
+    for (int tb = 0; tb < n; tb += kSortThreads) {
+        const int j = tb + tid;
+        const bool head = j < n && (j == 0 || se[j].slot != se[j - 1].slot);
+        const uint64_t hb = __ballot(head);
+        const uint32_t inwave = (uint32_t)__popcll(hb & lanes_below);
+        if (lane == 0) scan_tmp[wv] = (uint32_t)__popcll(hb);
+        __syncthreads();
+        uint32_t before = nfound;
+        for (int w = 0; w < wv; w++) before += scan_tmp[w];
+        if (head) segs[before + inwave] = (uint32_t)j;
+        uint32_t total = 0;
+        for (int w = 0; w < kSortThreads / 64; w++) total += scan_tmp[w];
+        nfound += total;
+        __syncthreads();
+    }
+    if (tid == 0) a.nseg[chain * a.nepoch + ep] = nfound;
+
+    // read links: in-epoch writes of the read slot at tokens <= the read token
+    const int nr = ne * a.R;
+    for (int i = tid; i < nr; i += kSortThreads) {
+        const int tl = i / a.R, r = i - tl * a.R;
+        const uint32_t s = recc[(int64_t)tl * a.rec_dwords + 3 * a.Wp + r] & kSlotMask;
+        int lo = 0, hi = n;  // first entry with slot >= s
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (se[mid].slot < s) lo = mid + 1;
+            else hi = mid;
+        }
+        int l2 = lo, h2 = n;  // first entry past (s, tl)
+        while (l2 < h2) {
+            const int mid = (l2 + h2) >> 1;
+            const TPEntry e = se[mid];
+            if (e.slot == s && (int)(e.tw >> 6) <= tl) l2 = mid + 1;
+            else h2 = mid;
+        }
+        const uint32_t cnt = (uint32_t)(l2 - lo);  // lo may equal n (= 65536) only when cnt == 0
+        a.rlink[(chain * a.T + t0 + tl) * a.R + r] = cnt ? (((uint32_t)lo << 16) | cnt) : 0u;
+    }
+}
+
+// ------------------------------------------------------------------ read
+
+// One wavefront per (chain, token of the epoch, 32-column slice): the 8 row
+// groups take 8 read references at a time, as in the serial kernel.
+template <int NR, bool BF16>
+__global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int64_t units,
+                                                      int nslice)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t unit = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (unit >= units) return;
+    const int slice = (int)(unit % nslice);
+    const int64_t rest = unit / nslice;
+    const int64_t t0 = (int64_t)ep * a.E;
+    const int ne = (int)((a.T - t0) < a.E ? (a.T - t0) : a.E);
+    const int tl = (int)(rest % ne);
+    const int64_t chain = rest / ne;
+    const int64_t t = t0 + tl;
+    const int g = lane / kLPR, q = lane % kLPR;
+    const int col = slice * 4 * kLPR + q * 4;
+    const bool col_ok = col < a.d_v;
+    const int colc = col_ok ? col : 0;
+    const int64_t b = chain / a.H;
+    const int h = (int)(chain - b * a.H);
+    const int64_t hd = (int64_t)a.H * a.d_v;
+    const int64_t vrow0 = (b * a.T * a.H + h) * a.d_v + colc;  // v of token 0 of the chain
+    const rsrc_t Mr = make_rsrc(a.M + chain * a.N * a.d_v, (uint32_t)(a.N * a.d_v * 4));
+    const uint32_t rowb = (uint32_t)a.d_v * 4u;
+    const uint32_t *rc = a.rec + (chain * a.T + t) * a.rec_dwords;
+    const float *rf = reinterpret_cast<const float *>(rc);
+    const TPEntry *se = a.sorted + chain * a.T * a.W + t0 * a.W;
+    const uint32_t *lk = a.rlink + (chain * a.T + t) * a.R;
+
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < NR; i++) {
+        const int r = g * NR + i;
+        const bool ok = col_ok & (r < a.R);
+        const int rr = r < a.R ? r : 0;
+        const uint32_t s = rc[3 * a.Wp + rr] & kSlotMask;
+        const float qv = rf[3 * a.Wp + a.Rp + rr];
+        const uint32_t link = lk[rr];
+        float4 row = buf_load4(Mr, ok ? s * rowb + col * 4u : kOff);
+        const int first = (int)(link >> 16), cnt = (int)(link & 0xFFFFu);
+        for (int k = 0; k < cnt; k++) {
+            const TPEntry e = se[first + k];
+            const float4 vv = load_v<BF16>(a.v, vrow0 + (t0 + (e.tw >> 6)) * hd);
+            row = fma4(e.a, row, e.c, vv);
+        }
+        if (ok) {
+            acc.x = fmaf(qv, row.x, acc.x);
+            acc.y = fmaf(qv, row.y, acc.y);
+            acc.z = fmaf(qv, row.z, acc.z);
+            acc.w = fmaf(qv, row.w, acc.w);
+        }
+    }
+#pragma unroll
+    for (int m = kLPR; m < 64; m <<= 1) {
+        acc.x += __shfl_xor(acc.x, m, 64);
+        acc.y += __shfl_xor(acc.y, m, 64);
+        acc.z += __shfl_xor(acc.z, m, 64);
+        acc.w += __shfl_xor(acc.w, m, 64);
+    }
+    if (g == 0 && col_ok)
+        *reinterpret_cast<float4 *>(a.y + (b * a.T * a.H + t * a.H + h) * a.d_v + col) = acc;
+}
+
+// ------------------------------------------------------------------ update
+
+// One wavefront per (chain, block of 8 segments, 32-column slice); each row
+// group owns one segment: load the row once, apply its writes in time
+// order, store it once.
+template <bool BF16>
+__global__ __launch_bounds__(256) void tp_update_kernel(TPArgs a, int ep, int64_t units,
+                                                        int nslice, int nblk)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t unit = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (unit >= units) return;
+    const int slice = (int)(unit % nslice);
+    const int64_t rest = unit / nslice;
+    const int blk = (int)(rest % nblk);
+    const int64_t chain = rest / nblk;
+    const uint32_t nseg = a.nseg[chain * a.nepoch + ep];
+    if ((uint32_t)blk * kRPI >= nseg) return;
+    const int64_t t0 = (int64_t)ep * a.E;
+    const int ne = (int)((a.T - t0) < a.E ? (a.T - t0) : a.E);
+    const int n = ne * a.W;
+    const int g = lane / kLPR, q = lane % kLPR;
+    const int col = slice * 4 * kLPR + q * 4;
+    const bool col_ok = col < a.d_v;
+    const int colc = col_ok ? col : 0;
+    const int64_t b = chain / a.H;
+    const int h = (int)(chain - b * a.H);
+    const int64_t hd = (int64_t)a.H * a.d_v;
+    const int64_t vrow0 = (b * a.T * a.H + h) * a.d_v + colc;
+    const rsrc_t Mr = make_rsrc(a.M + chain * a.N * a.d_v, (uint32_t)(a.N * a.d_v * 4));
+    const uint32_t rowb = (uint32_t)a.d_v * 4u;
+    const TPEntry *se = a.sorted + chain * a.T * a.W + t0 * a.W;
+    const uint32_t *sg = a.segs + chain * a.T * a.W + t0 * a.W;
+
+    const uint32_t k = (uint32_t)blk * kRPI + g;
+    const bool ok = k < nseg;
+    const uint32_t kk = ok ? k : 0;
+    const int j0 = (int)sg[kk];
+    const int j1 = ok ? (kk + 1 < nseg ? (int)sg[kk + 1] : n) : j0;
+    const uint32_t s = se[j0].slot;
+    const uint32_t off = (ok & col_ok) ? s * rowb + col * 4u : kOff;
+    float4 row = buf_load4(Mr, off);
+    for (int j = j0; j < j1; j++) {
+        const TPEntry e = se[j];
+        const float4 vv = load_v<BF16>(a.v, vrow0 + (t0 + (e.tw >> 6)) * hd);
+        row = fma4(e.a, row, e.c, vv);
+    }
+    buf_store4(row, Mr, off);
+}
+
+}  // namespace
+
+int tp_epoch_len(const Shape &s)
+{
+    // E*W <= 65536 (links hold 16-bit positions), E <= 1024, and E*W/N <= 1
+    // so that a read replays few in-epoch writes on average.
+    int64_t e = 1024;
+    while (e > 1 && (e * s.W > 65536 || e * s.W > s.N())) e >>= 1;
+    if (e > s.T) {
+        e = 1;
+        while (e < s.T) e <<= 1;
+    }
+    return (int)e;
+}
+
+size_t tp_workspace_bytes(const Shape &s)
+{
+    const size_t chains = (size_t)s.B * s.H;
+    const size_t ev = chains * (size_t)s.T * s.W;
+    const int E = tp_epoch_len(s);
+    const size_t nep = (size_t)((s.T + E - 1) / E);
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    return up(ev * sizeof(TPEntry)) + 2 * up(ev * 8) + up(ev * 4) + up(chains * nep * 4) +
+           up(chains * (size_t)s.T * s.R * 4);
+}
+
+static TPArgs tp_args(const Shape &s, const uint32_t *rec, void *ws, const void *v, float *y,
+                      float *M)
+{
+    const RecLayout L(s.W, s.R);
+    TPArgs a{};
+    const size_t chains = (size_t)s.B * s.H;
+    const size_t ev = chains * (size_t)s.T * s.W;
+    a.E = tp_epoch_len(s);
+    a.nepoch = (int)((s.T + a.E - 1) / a.E);
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    char *p = static_cast<char *>(ws);
+    a.sorted = reinterpret_cast<TPEntry *>(p);
+    p += up(ev * sizeof(TPEntry));
+    a.tmpA = reinterpret_cast<uint64_t *>(p);
+    p += up(ev * 8);
+    a.tmpB = reinterpret_cast<uint64_t *>(p);
+    p += up(ev * 8);
+    a.segs = reinterpret_cast<uint32_t *>(p);
+    p += up(ev * 4);
+    a.nseg = reinterpret_cast<uint32_t *>(p);
+    p += up(chains * a.nepoch * 4);
+    a.rlink = reinterpret_cast<uint32_t *>(p);
+    a.rec = rec;
+    a.v = v;
+    a.y = y;
+    a.M = M;
+    a.T = s.T;
+    a.N = s.N();
+    a.H = s.H;
+    a.d_v = s.d_v;
+    a.W = s.W;
+    a.R = s.R;
+    a.Wp = L.Wp;
+    a.Rp = L.Rp;
+    a.rec_dwords = L.dwords();
+    a.chains = (int64_t)chains;
+    int bits = 1;
+    while ((int64_t(1) << bits) < s.N()) bits++;
+    a.passes = (bits + 7) / 8;
+    return a;
+}
+
+bool tp_supported(const Shape &s)
+{
+    return s.d_v % 4 == 0 && (double)s.N() * s.d_v * 4.0 <= 2147483648.0;
+}
+
+hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipStream_t st)
+{
+    TPArgs a = tp_args(s, rec, ws, nullptr, nullptr, nullptr);
+    const int64_t blocks = a.chains * a.nepoch;
+    hipLaunchKernelGGL(tp_sort_kernel, dim3((unsigned)blocks), dim3(kSortThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_tp_apply(const Shape &s, const uint32_t *rec, void *ws, const void *v,
+                           bool bf16, float *y, float *M, hipStream_t st)
+{
+    TPArgs a = tp_args(s, rec, ws, v, y, M);
+    const int nslice = (s.d_v + 4 * kLPR - 1) / (4 * kLPR);
+    const int nr = (s.R + kRPI - 1) / kRPI;
+    for (int ep = 0; ep < a.nepoch; ep++) {
+        const int64_t t0 = (int64_t)ep * a.E;
+        const int ne = (int)((s.T - t0) < a.E ? (s.T - t0) : a.E);
+        const int64_t runits = a.chains * ne * nslice;
+        const dim3 rgrid((unsigned)((runits + 3) / 4));
+#define SDM_TP_READ(NR_)                                                                       \
+    if (nr <= NR_) {                                                                           \
+        if (bf16) hipLaunchKernelGGL((tp_read_kernel<NR_, true>), rgrid, dim3(256), 0, st, a,  \
+                                     ep, runits, nslice);                                      \
+        else hipLaunchKernelGGL((tp_read_kernel<NR_, false>), rgrid, dim3(256), 0, st, a, ep,  \
+                                runits, nslice);                                               \
+    } else
+        SDM_TP_READ(1) SDM_TP_READ(2) SDM_TP_READ(4) SDM_TP_READ(8) { return hipErrorInvalidValue; }
+#undef SDM_TP_READ
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int nblk = (ne * s.W + kRPI - 1) / kRPI;  // bound on segment blocks
+        const int64_t uunits = a.chains * nblk * nslice;
+        const dim3 ugrid((unsigned)((uunits + 3) / 4));
+        if (bf16) hipLaunchKernelGGL(tp_update_kernel<true>, ugrid, dim3(256), 0, st, a, ep, uunits,
+                                     nslice, nblk);
+        else hipLaunchKernelGGL(tp_update_kernel<false>, ugrid, dim3(256), 0, st, a, ep, uunits,
+                                nslice, nblk);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace sdm

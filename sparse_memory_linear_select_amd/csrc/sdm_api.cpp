@@ -66,27 +66,49 @@ sdm_status check_handle_call(const sdm_ctx *h, int B, int64_t T, sdm_dtype dtype
     return SDM_OK;
 }
 
-// Serial workspace: token records for every (chain, token).
-size_t serial_ws_bytes(const sdm_ctx *h, int B, int64_t T)
+// Workspace: token records for every (chain, token); the time-parallel
+// schedule adds its sorted events, segments and read links after them.
+size_t records_bytes(const sdm_ctx *h, int B, int64_t T)
 {
     const sdm::RecLayout L(h->W, h->R);
     return round_up((size_t)B * h->H * (size_t)T * (size_t)L.dwords() * 4u);
 }
 
-sdm_variant resolve_variant(const sdm_ctx *, sdm_variant v)
+sdm_variant resolve_variant(const sdm_ctx *h, int B, int64_t T, sdm_variant v)
 {
-    return v == SDM_VARIANT_AUTO ? SDM_VARIANT_SERIAL : v;
+    if (v != SDM_VARIANT_AUTO) return v;
+    (void)h;
+    (void)B;
+    (void)T;
+    return SDM_VARIANT_SERIAL;
+}
+
+size_t ws_bytes_for(const sdm_ctx *h, int B, int64_t T, sdm_variant var)
+{
+    size_t n = records_bytes(h, B, T);
+    if (var == SDM_VARIANT_TIMEPAR) n += round_up(sdm::tp_workspace_bytes(shape_of(h, B, T)));
+    return n;
+}
+
+sdm_status check_variant(const sdm_ctx *h, int B, int64_t T, sdm_variant variant,
+                         sdm_variant *out)
+{
+    const sdm_variant var = resolve_variant(h, B, T, variant);
+    if (var != SDM_VARIANT_SERIAL && var != SDM_VARIANT_TIMEPAR)
+        return fail(SDM_ERR_ARG, "unknown variant %d", (int)variant);
+    if (var == SDM_VARIANT_TIMEPAR && !sdm::tp_supported(shape_of(h, B, T)))
+        return fail(SDM_ERR_UNSUPPORTED,
+                    "time-parallel schedule needs d_v %% 4 == 0 and N*d_v*4 <= 2^31");
+    *out = var;
+    return SDM_OK;
 }
 
 sdm_status check_variant_and_ws(const sdm_ctx *h, int B, int64_t T, sdm_variant variant,
-                                size_t ws_bytes)
+                                size_t ws_bytes, sdm_variant *out)
 {
-    const sdm_variant var = resolve_variant(h, variant);
-    if (var != SDM_VARIANT_SERIAL && var != SDM_VARIANT_TIMEPAR)
-        return fail(SDM_ERR_ARG, "unknown variant %d", (int)variant);
-    if (var == SDM_VARIANT_TIMEPAR)
-        return fail(SDM_ERR_UNSUPPORTED, "time-parallel variant not built");
-    const size_t need = serial_ws_bytes(h, B, T);
+    sdm_status st = check_variant(h, B, T, variant, out);
+    if (st != SDM_OK) return st;
+    const size_t need = ws_bytes_for(h, B, T, *out);
     if (ws_bytes < need)
         return fail(SDM_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
     return SDM_OK;
@@ -145,13 +167,11 @@ sdm_status sdm_workspace_size(sdm_handle h, int B, int64_t T, sdm_dtype dtype,
     *bytes = 0;
     sdm_status st = check_handle_call(h, B, T, dtype);
     if (st != SDM_OK) return st;
-    const sdm_variant v = resolve_variant(h, variant);
-    if (v == SDM_VARIANT_SERIAL) {
-        *bytes = serial_ws_bytes(h, B, T);
-        return SDM_OK;
-    }
-    if (v == SDM_VARIANT_TIMEPAR) return fail(SDM_ERR_UNSUPPORTED, "time-parallel variant not built");
-    return fail(SDM_ERR_ARG, "unknown variant %d", (int)variant);
+    sdm_variant v;
+    st = check_variant(h, B, T, variant, &v);
+    if (st != SDM_OK) return st;
+    *bytes = ws_bytes_for(h, B, T, v);
+    return SDM_OK;
 }
 
 sdm_status sdm_select(sdm_handle h, int B, int64_t T, const void *kp, const void *qp,
@@ -184,7 +204,8 @@ sdm_status sdm_prepare(sdm_handle h, int B, int64_t T, const void *kp, const voi
         !aligned16(M) || !aligned16(workspace))
         return fail(SDM_ERR_ARG, "tensor pointers must be 16-byte aligned");
     if (flags & ~SDM_FLAG_CONTINUE) return fail(SDM_ERR_ARG, "unknown flags 0x%x", flags);
-    st = check_variant_and_ws(h, B, T, variant, ws_bytes);
+    sdm_variant var;
+    st = check_variant_and_ws(h, B, T, variant, ws_bytes, &var);
     if (st != SDM_OK) return st;
 
     const sdm::Shape s = shape_of(h, B, T);
@@ -198,7 +219,11 @@ sdm_status sdm_prepare(sdm_handle h, int B, int64_t T, const void *kp, const voi
     e = sdm::launch_select(s, kp, qp, dtype == SDM_BF16, nullptr, nullptr, nullptr, nullptr, rec,
                            alpha, beta, hs);
     if (e != hipSuccess) return hip_fail(e, "select launch");
-    if (s.d_v % 4 == 0) {
+    if (var == SDM_VARIANT_TIMEPAR) {
+        char *tp = static_cast<char *>(workspace) + records_bytes(h, B, T);
+        e = sdm::launch_tp_prepare(s, rec, tp, hs);
+        if (e != hipSuccess) return hip_fail(e, "time-parallel sort launch");
+    } else if (sdm::rw_serial_supported(s)) {
         e = sdm::launch_plan(s, rec, sdm::rw_serial_depth(), hs);
         if (e != hipSuccess) return hip_fail(e, "plan launch");
     }
@@ -214,13 +239,20 @@ sdm_status sdm_apply(sdm_handle h, int B, int64_t T, const void *v, sdm_dtype dt
     if (!v || !y || !M || !workspace) return fail(SDM_ERR_ARG, "null tensor pointer");
     if (!aligned16(v) || !aligned16(y) || !aligned16(M) || !aligned16(workspace))
         return fail(SDM_ERR_ARG, "tensor pointers must be 16-byte aligned");
-    st = check_variant_and_ws(h, B, T, variant, ws_bytes);
+    sdm_variant var;
+    st = check_variant_and_ws(h, B, T, variant, ws_bytes, &var);
     if (st != SDM_OK) return st;
 
     const sdm::Shape s = shape_of(h, B, T);
     const hipStream_t hs = (hipStream_t)stream;
     const uint32_t *rec = static_cast<const uint32_t *>(workspace);
-    const hipError_t e = s.d_v % 4 == 0
+    if (var == SDM_VARIANT_TIMEPAR) {
+        char *tp = static_cast<char *>(workspace) + records_bytes(h, B, T);
+        const hipError_t e = sdm::launch_tp_apply(s, rec, tp, v, dtype == SDM_BF16, y, M, hs);
+        if (e != hipSuccess) return hip_fail(e, "time-parallel write/read launch");
+        return SDM_OK;
+    }
+    const hipError_t e = sdm::rw_serial_supported(s)
                              ? sdm::launch_rw_serial(s, rec, v, dtype == SDM_BF16, y, M, hs)
                              : sdm::launch_rw_simple(s, rec, v, dtype == SDM_BF16, y, M, hs);
     if (e != hipSuccess) return hip_fail(e, "write/read launch");

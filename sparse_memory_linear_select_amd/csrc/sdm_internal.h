@@ -24,20 +24,27 @@ constexpr uint32_t kFwdValid = 1u << 29;
 
 // Per (chain, token) record written by select and consumed by the write/read
 // kernels.  A chain is one (sequence b, head h); records of a chain are
-// contiguous in t.  Arrays are padded to multiples of 16 dwords: the serial
-// kernel's 16 lane groups each load ceil(W/16) consecutive entries, so the
-// padding covers every group's load, and every record is 64-byte aligned.
+// contiguous in t.  Every array has kMaxK entries whatever W and R are: the
+// serial kernel's row groups load their references unconditionally (masked
+// entries are ignored), and those loads then always stay inside the record.
 //   ws[Wp]  write slot words     wa[Wp]  alpha*(1 - beta*k)   wc[Wp]  beta*k
 //   rs[Rp]  read slot words      rq[Rp]  q weights
 struct RecLayout {
     int Wp, Rp;
-    __host__ __device__ RecLayout(int W, int R) : Wp((W + 15) & ~15), Rp((R + 15) & ~15) {}
+    __host__ __device__ RecLayout(int, int) : Wp(kMaxK), Rp(kMaxK) {}
     __host__ __device__ int ws() const { return 0; }
     __host__ __device__ int wa() const { return Wp; }
     __host__ __device__ int wc() const { return 2 * Wp; }
     __host__ __device__ int rs() const { return 3 * Wp; }
     __host__ __device__ int rq() const { return 3 * Wp + Rp; }
     __host__ __device__ int dwords() const { return 3 * Wp + 2 * Rp; }
+};
+
+// One write event of an epoch after sorting by slot (time-parallel schedule):
+// slot, token within the epoch << 6 | position w, and the coefficients.
+struct TPEntry {
+    uint32_t slot, tw;
+    float a, c;
 };
 
 struct Shape {
@@ -63,7 +70,9 @@ hipError_t launch_init(const Shape &s, const float *M0, float *M, hipStream_t st
 // Adds forwarding codes (distance < depth) to the slot words of all records.
 hipError_t launch_plan(const Shape &s, uint32_t *rec, int depth, hipStream_t st);
 
-// Token-serial write/read over the records (float4 path, d_v % 4 == 0).
+// Token-serial write/read over the records (float4 path): needs d_v % 4 == 0
+// and one chain's state within 2^31 bytes.
+bool rw_serial_supported(const Shape &s);
 hipError_t launch_rw_serial(const Shape &s, const uint32_t *rec, const void *v, bool bf16,
                             float *y, float *M, hipStream_t st);
 int rw_serial_depth();  // prefetch depth the serial kernel is compiled for
@@ -71,5 +80,13 @@ int rw_serial_depth();  // prefetch depth the serial kernel is compiled for
 // Token-serial write/read, one column per lane, no prefetch (any d_v).
 hipError_t launch_rw_simple(const Shape &s, const uint32_t *rec, const void *v, bool bf16,
                             float *y, float *M, hipStream_t st);
+
+// Time-parallel schedule (epochs of tokens, slot-sorted write events).
+bool tp_supported(const Shape &s);
+int tp_epoch_len(const Shape &s);
+size_t tp_workspace_bytes(const Shape &s);  // beyond the token records
+hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipStream_t st);
+hipError_t launch_tp_apply(const Shape &s, const uint32_t *rec, void *ws, const void *v,
+                           bool bf16, float *y, float *M, hipStream_t st);
 
 }  // namespace sdm

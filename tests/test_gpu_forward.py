@@ -30,8 +30,13 @@ def _parity(wl, T=None, c0=0, c1=None, tol=TOL, variant=sdm.AUTO, d=None):
     return d, dd, y, M
 
 
-def test_forward_tiny_workload():
-    _parity(si.WORKLOADS[0])
+VARIANTS = [sdm.SERIAL, sdm.TIMEPAR]
+VNAMES = ["serial", "timepar"]
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=VNAMES)
+def test_forward_tiny_workload(variant):
+    _parity(si.WORKLOADS[0], variant=variant)
 
 
 SHAPES = [
@@ -46,15 +51,19 @@ SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("variant", VARIANTS, ids=VNAMES)
 @pytest.mark.parametrize("shape", SHAPES, ids=[str(s[:7]) for s in SHAPES])
-def test_forward_shapes(shape):
+def test_forward_shapes(shape, variant):
     B, T, H, S, D, W, R, dt, reuse = shape
+    if variant == sdm.TIMEPAR and D % 4:
+        pytest.skip("the time-parallel schedule needs d_v % 4 == 0 (rejected, tested below)")
     wl = si.Workload("shape", B=B, T=T, H=H, sqrtN=S, d_v=D, W=W, R=R, dtype=dt, reuse=reuse,
                      seed=500 + T)
-    _parity(wl)
+    _parity(wl, variant=variant)
 
 
-def test_forward_same_keys_every_token():
+@pytest.mark.parametrize("variant", VARIANTS, ids=VNAMES)
+def test_forward_same_keys_every_token(variant):
     """Every token writes the same slots and reads them back: each row is
     rewritten at every step, so every reference goes through the forwarding
     path (previous token for writes, same token for reads)."""
@@ -63,10 +72,11 @@ def test_forward_same_keys_every_token():
     d = si.generate(wl)
     d["kp"][:] = d["kp"][:, :1]
     d["qp"][:] = d["kp"]
-    _parity(wl, d=d)
+    _parity(wl, d=d, variant=variant)
 
 
-def test_forward_clustered_keys():
+@pytest.mark.parametrize("variant", VARIANTS, ids=VNAMES)
+def test_forward_clustered_keys(variant):
     """Keys drawn from a few prototypes: slots recur at distances 1..8."""
     wl = si.Workload("clustered", B=1, T=300, H=2, sqrtN=32, d_v=64, W=32, R=32, dtype="f32",
                      reuse=0.0, seed=10)
@@ -76,11 +86,12 @@ def test_forward_clustered_keys():
     pick = rng.integers(0, 5, size=wl.T)
     d["kp"][0] = proto[pick] + 0.05 * rng.standard_normal(d["kp"][0].shape).astype(np.float32)
     d["qp"][0] = proto[rng.integers(0, 5, size=wl.T)]
-    _parity(wl, d=d)
+    _parity(wl, d=d, variant=variant)
 
 
+@pytest.mark.parametrize("variant", VARIANTS, ids=VNAMES)
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
-def test_forward_full_workload(cfg):
+def test_forward_full_workload(cfg, variant):
     """The full workload on the GPU; the oracle computes every token of every
     chain for a window of 16 columns (columns never interact)."""
     wl = si.WORKLOADS[cfg]
@@ -89,7 +100,7 @@ def test_forward_full_workload(cfg):
     with Timer("generate"):
         d = si.generate(wl)
     with Timer("gpu + oracle"):
-        _parity(wl, d=d, c0=c0, c1=c0 + 16, tol=tol)
+        _parity(wl, d=d, c0=c0, c1=c0 + 16, tol=tol, variant=variant)
 
 
 # ---------------------------------------------------------------- invariants
@@ -162,25 +173,28 @@ def test_scaling_by_two_is_exact():
     assert torch.equal(y2, 2 * y1) and torch.equal(M2, 2 * M1)
 
 
-def test_runs_are_bitwise_deterministic():
+@pytest.mark.parametrize("variant", VARIANTS, ids=VNAMES)
+def test_runs_are_bitwise_deterministic(variant):
     wl, d = _small(26, sqrtN=64, d_v=128, W=64, R=64, T=200, B=1)
-    core, dd, y1, M1 = gpu_forward(d, wl.W, wl.R)
-    y2, M2 = core.forward(dd["kp"], dd["qp"], dd["v"], dd["alpha"], dd["beta"])
+    core, dd, y1, M1 = gpu_forward(d, wl.W, wl.R, variant)
+    y2, M2 = core.forward(dd["kp"], dd["qp"], dd["v"], dd["alpha"], dd["beta"], variant=variant)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(M1, M2)
 
 
-def test_continue_flag_splits_a_sequence():
+@pytest.mark.parametrize("variant", VARIANTS, ids=VNAMES)
+def test_continue_flag_splits_a_sequence(variant):
     """Two calls (the second continuing from the first's state) give the same
     outputs, bit for bit, as one call over the whole sequence."""
     wl, d = _small(27, sqrtN=32, d_v=64, W=16, R=16, T=90)
-    core, dd, y, M = gpu_forward(d, wl.W, wl.R)
+    core, dd, y, M = gpu_forward(d, wl.W, wl.R, variant)
     k = 37
     part = {n: dd[n][:, :k].contiguous() for n in ("kp", "qp", "v", "alpha", "beta")}
     rest = {n: dd[n][:, k:].contiguous() for n in ("kp", "qp", "v", "alpha", "beta")}
-    y1, M1 = core.forward(part["kp"], part["qp"], part["v"], part["alpha"], part["beta"])
+    y1, M1 = core.forward(part["kp"], part["qp"], part["v"], part["alpha"], part["beta"],
+                          variant=variant)
     y2, M2 = core.forward(rest["kp"], rest["qp"], rest["v"], rest["alpha"], rest["beta"],
-                          M=M1, cont=True)
+                          M=M1, cont=True, variant=variant)
     torch.cuda.synchronize()
     assert torch.equal(torch.cat([y1, y2], 1), y) and torch.equal(M2, M)
 
@@ -194,5 +208,27 @@ def test_forward_rejects_bad_tensors():
     with pytest.raises(sdm.SDMError):
         core.forward(dd["kp"][:, :, :1], dd["qp"], dd["v"], dd["alpha"], dd["beta"])
     with pytest.raises(sdm.SDMError) as e:
-        core.forward(dd["kp"], dd["qp"], dd["v"], dd["alpha"], dd["beta"], variant=sdm.TIMEPAR)
-    assert e.value.status in (1, 2)
+        core.forward(dd["kp"], dd["qp"], dd["v"], dd["alpha"], dd["beta"], variant=7)
+    assert e.value.status == 1
+    wl2, d2 = _small(29, d_v=30)
+    dd2 = upload(d2)
+    core2 = make_core(dd2, wl2.W, wl2.R)
+    with pytest.raises(sdm.SDMError) as e:
+        core2.forward(dd2["kp"], dd2["qp"], dd2["v"], dd2["alpha"], dd2["beta"],
+                      variant=sdm.TIMEPAR)
+    assert e.value.status == 2
+
+
+@pytest.mark.parametrize("shape", [(2, 300, 2, 32, 64, 32, 32, 0.0), (1, 700, 1, 64, 96, 64, 64, 0.4),
+                                   (4, 129, 2, 16, 32, 16, 8, 0.0)])
+def test_schedules_agree_bitwise_on_state(shape):
+    """Both schedules apply the same float32 operations to every row in the
+    same order, so the final state agrees bit for bit; y agrees to rounding."""
+    B, T, H, S, D, W, R, reuse = shape
+    wl = si.Workload("agree", B=B, T=T, H=H, sqrtN=S, d_v=D, W=W, R=R, dtype="f32",
+                     reuse=reuse, seed=40 + T)
+    d = si.generate(wl)
+    _, _, y1, M1 = gpu_forward(d, W, R, sdm.SERIAL)
+    _, _, y2, M2 = gpu_forward(d, W, R, sdm.TIMEPAR)
+    assert torch.equal(M1, M2)
+    assert torch.allclose(y1, y2, rtol=1e-6, atol=1e-7)
