@@ -71,6 +71,8 @@ def main():
                     help="synthetic workload index (default 1: the 1.4B-style layer)")
     ap.add_argument("--cpu-seqs", type=int, default=None,
                     help="sequences in the CPU-baseline sample (default: all)")
+    ap.add_argument("--variant", choices=["auto", "serial", "timepar"], default="auto",
+                    help="write/read schedule (default: the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -107,7 +109,8 @@ def main():
     y = torch.empty((B, T, H, wl.d_v), dtype=torch.float32, device=dev)
     M = torch.empty((B, H, wl.N, wl.d_v), dtype=torch.float32, device=dev)
     dt_code = sdm.BF16 if wl.dtype == "bf16" else sdm.F32
-    ws_n = core.workspace_size(B, T, dt_code, sdm.AUTO)
+    var = {"auto": sdm.AUTO, "serial": sdm.SERIAL, "timepar": sdm.TIMEPAR}[args.variant]
+    ws_n = core.workspace_size(B, T, dt_code, var)
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
     L = sdm.lib()
     stream = torch.cuda.current_stream(dev)
@@ -116,10 +119,10 @@ def main():
 
     def prepare():
         sdm._check(L.sdm_prepare(core._h, B, T, P(dd["kp"]), P(dd["qp"]), P(dd["alpha"]),
-                                 P(dd["beta"]), dt_code, sdm.AUTO, 0, P(ws), ws_n, P(M), sp))
+                                 P(dd["beta"]), dt_code, var, 0, P(ws), ws_n, P(M), sp))
 
     def apply():
-        sdm._check(L.sdm_apply(core._h, B, T, P(dd["v"]), dt_code, sdm.AUTO, P(ws), ws_n, P(y),
+        sdm._check(L.sdm_apply(core._h, B, T, P(dd["v"]), dt_code, var, P(ws), ws_n, P(y),
                                P(M), sp))
 
     for _ in range(args.warmup):
@@ -167,9 +170,9 @@ def main():
         "data": "synthetic (seeded; recipe in sdm_inputs.py)",
         "config": {"workload": wl.name, "B": B, "T": T, "H": H, "sqrtN": wl.sqrtN, "N": wl.N,
                    "d_v": wl.d_v, "W": wl.W, "R": wl.R, "inputs": wl.dtype,
-                   "schedule": "token-serial"},
+                   "schedule": sdm.variant_name(core, B, T, dt_code, var)},
         "row_gbs_whole_step": row_bytes / (ms_step * 1e-3) / 1e9,
-        "breakdown_ms": {"prepare (init+select+plan)": prep_ms, "write+read": rw_ms},
+        "breakdown_ms": {"prepare (init+select+plan/sort)": prep_ms, "write+read": rw_ms},
         "wall_s_timed": wall,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS,

@@ -74,6 +74,17 @@ def lib():
     return _lib
 
 
+def variant_name(core, B, T, dtype, variant) -> str:
+    """Name of the schedule a call would use ("token-serial" or "time-parallel")."""
+    if variant == SERIAL:
+        return "token-serial"
+    if variant == TIMEPAR:
+        return "time-parallel"
+    n_auto = core.workspace_size(B, T, dtype, AUTO)
+    return "time-parallel" if n_auto == core.workspace_size(B, T, dtype, TIMEPAR) and \
+        n_auto != core.workspace_size(B, T, dtype, SERIAL) else "token-serial"
+
+
 def _check(status: int):
     if status != 0:
         raise SDMError(status, lib().sdm_last_error().decode())
