@@ -14,8 +14,9 @@
 //            those at tokens <= its own);
 //   read     each read gathers the row as it was at the epoch start, replays
 //            its linked writes in time order and adds q * row to y_t;
-//   update   each segment loads its row once, applies all its writes in time
-//            order and stores it once.
+//   update   the first event of each slot's segment loads the row once,
+//            applies all of the segment's writes in time order and stores it
+//            once.
 //
 // Within an epoch everything is parallel; epochs follow each other in stream
 // order (read of epoch e, update of e, read of e+1, ...).  Each row value is
@@ -72,9 +73,7 @@ struct TPArgs {
     const uint32_t *rec;  // token records (slots, coefficients)
     TPEntry *sorted;      // [chain][T*W] sorted write events, epoch regions
     uint64_t *tmpA, *tmpB;  // [chain][T*W] radix ping-pong (key << 32 | event)
-    uint32_t *segs;       // [chain][T*W] segment starts (epoch regions)
-    uint32_t *nseg;       // [chain][nepoch]
-    uint32_t *rlink;      // [chain][T][R] (first << 16) | count
+    uint32_t *rlink;      // [chain][T][kMaxK] (first << 16) | count
     const void *v;
     float *y, *M;
     int64_t T, N;
@@ -89,7 +88,6 @@ __global__ __launch_bounds__(kSortThreads) void tp_sort_kernel(TPArgs a)
 {
     __shared__ uint32_t bins[256];
     __shared__ uint32_t wcnt[kSortThreads / 64][256];
-    __shared__ uint32_t scan_tmp[kSortThreads / 64];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = tid >> 6;
@@ -187,28 +185,8 @@ __global__ __launch_bounds__(kSortThreads) void tp_sort_kernel(TPArgs a)
     }
     __syncthreads();  // the sorted entries of this epoch are complete (workgroup scope)
 
-    // segment starts: positions whose slot differs from the previous one
-    const TPEntry *se = a.sorted + base;
-    uint32_t *segs = a.segs + base;
-    uint32_t nfound = 0;
-    for (int tb = 0; tb < n; tb += kSortThreads) {
-        const int j = tb + tid;
-        const bool head = j < n && (j == 0 || se[j].slot != se[j - 1].slot);
-        const uint64_t hb = __ballot(head);
-        const uint32_t inwave = (uint32_t)__popcll(hb & lanes_below);
-        if (lane == 0) scan_tmp[wv] = (uint32_t)__popcll(hb);
-        __syncthreads();
-        uint32_t before = nfound;
-        for (int w = 0; w < wv; w++) before += scan_tmp[w];
-        if (head) segs[before + inwave] = (uint32_t)j;
-        uint32_t total = 0;
-        for (int w = 0; w < kSortThreads / 64; w++) total += scan_tmp[w];
-        nfound += total;
-        __syncthreads();
-    }
-    if (tid == 0) a.nseg[chain * a.nepoch + ep] = nfound;
-
     // read links: in-epoch writes of the read slot at tokens <= the read token
+    const TPEntry *se = a.sorted + base;
     const int nr = ne * a.R;
     for (int i = tid; i < nr; i += kSortThreads) {
         const int tl = i / a.R, r = i - tl * a.R;
@@ -227,14 +205,37 @@ __global__ __launch_bounds__(kSortThreads) void tp_sort_kernel(TPArgs a)
             else h2 = mid;
         }
         const uint32_t cnt = (uint32_t)(l2 - lo);  // lo may equal n (= 65536) only when cnt == 0
-        a.rlink[(chain * a.T + t0 + tl) * a.R + r] = cnt ? (((uint32_t)lo << 16) | cnt) : 0u;
+        a.rlink[(chain * a.T + t0 + tl) * kMaxK + r] = cnt ? (((uint32_t)lo << 16) | cnt) : 0u;
     }
 }
 
 // ------------------------------------------------------------------ read
 
+template <int K, typename T>
+__device__ __forceinline__ void load_k(const T *p, T (&out)[K])
+{
+    if constexpr (K % 4 == 0 && sizeof(T) == 4) {
+#pragma unroll
+        for (int i = 0; i < K; i += 4) {
+            const uint4 x = *reinterpret_cast<const uint4 *>(p + i);
+            out[i] = __builtin_bit_cast(T, x.x);
+            out[i + 1] = __builtin_bit_cast(T, x.y);
+            out[i + 2] = __builtin_bit_cast(T, x.z);
+            out[i + 3] = __builtin_bit_cast(T, x.w);
+        }
+    } else if constexpr (K == 2 && sizeof(T) == 4) {
+        const uint2 x = *reinterpret_cast<const uint2 *>(p);
+        out[0] = __builtin_bit_cast(T, x.x);
+        out[1] = __builtin_bit_cast(T, x.y);
+    } else {
+#pragma unroll
+        for (int i = 0; i < K; i++) out[i] = p[i];
+    }
+}
+
 // One wavefront per (chain, token of the epoch, 32-column slice): the 8 row
-// groups take 8 read references at a time, as in the serial kernel.
+// groups take 8 read references at a time, as in the serial kernel.  All row
+// gathers are issued before any replay so that they are in flight together.
 template <int NR, bool BF16>
 __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int64_t units,
                                                       int nslice)
@@ -260,32 +261,36 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int64_t 
     const rsrc_t Mr = make_rsrc(a.M + chain * a.N * a.d_v, (uint32_t)(a.N * a.d_v * 4));
     const uint32_t rowb = (uint32_t)a.d_v * 4u;
     const uint32_t *rc = a.rec + (chain * a.T + t) * a.rec_dwords;
-    const float *rf = reinterpret_cast<const float *>(rc);
     const TPEntry *se = a.sorted + chain * a.T * a.W + t0 * a.W;
-    const uint32_t *lk = a.rlink + (chain * a.T + t) * a.R;
 
+    uint32_t sl[NR], lk[NR];
+    float qv[NR];
+    load_k<NR>(rc + 3 * a.Wp + g * NR, sl);
+    load_k<NR>(reinterpret_cast<const float *>(rc) + 3 * a.Wp + a.Rp + g * NR, qv);
+    load_k<NR>(a.rlink + (chain * a.T + t) * kMaxK + g * NR, lk);
+    float4 row[NR];
+#pragma unroll
+    for (int i = 0; i < NR; i++) {
+        const bool ok = col_ok & (g * NR + i < a.R);
+        row[i] = buf_load4(Mr, ok ? (sl[i] & kSlotMask) * rowb + col * 4u : kOff);
+    }
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int i = 0; i < NR; i++) {
-        const int r = g * NR + i;
-        const bool ok = col_ok & (r < a.R);
-        const int rr = r < a.R ? r : 0;
-        const uint32_t s = rc[3 * a.Wp + rr] & kSlotMask;
-        const float qv = rf[3 * a.Wp + a.Rp + rr];
-        const uint32_t link = lk[rr];
-        float4 row = buf_load4(Mr, ok ? s * rowb + col * 4u : kOff);
-        const int first = (int)(link >> 16), cnt = (int)(link & 0xFFFFu);
-        for (int k = 0; k < cnt; k++) {
+        // links exist only for the R real references (the rest were never written)
+        const uint32_t l = (g * NR + i < a.R) ? lk[i] : 0u;
+        const int first = (int)(l >> 16), cnt = (int)(l & 0xFFFFu);
+        float4 rv = row[i];
+        for (int k = 0; k < cnt; k++) {  // writes of this slot earlier in the epoch
             const TPEntry e = se[first + k];
             const float4 vv = load_v<BF16>(a.v, vrow0 + (t0 + (e.tw >> 6)) * hd);
-            row = fma4(e.a, row, e.c, vv);
+            rv = fma4(e.a, rv, e.c, vv);
         }
-        if (ok) {
-            acc.x = fmaf(qv, row.x, acc.x);
-            acc.y = fmaf(qv, row.y, acc.y);
-            acc.z = fmaf(qv, row.z, acc.z);
-            acc.w = fmaf(qv, row.w, acc.w);
-        }
+        // masked references have q = 0 and a zero row
+        acc.x = fmaf(qv[i], rv.x, acc.x);
+        acc.y = fmaf(qv[i], rv.y, acc.y);
+        acc.z = fmaf(qv[i], rv.z, acc.z);
+        acc.w = fmaf(qv[i], rv.w, acc.w);
     }
 #pragma unroll
     for (int m = kLPR; m < 64; m <<= 1) {
@@ -300,10 +305,12 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int64_t 
 
 // ------------------------------------------------------------------ update
 
-// One wavefront per (chain, block of 8 segments, 32-column slice); each row
-// group owns one segment: load the row once, apply its writes in time
-// order, store it once.
-template <bool BF16>
+// One wavefront per (chain, block of 8*SPG sorted write events, 32-column
+// slice); each row group takes SPG consecutive events.  An event whose slot
+// differs from the previous event's starts that slot's segment: its group
+// loads the row once, applies the segment's writes in time order and stores
+// it once.  Loads of the SPG events are issued together.
+template <bool BF16, int SPG>
 __global__ __launch_bounds__(256) void tp_update_kernel(TPArgs a, int ep, int64_t units,
                                                         int nslice, int nblk)
 {
@@ -314,8 +321,6 @@ __global__ __launch_bounds__(256) void tp_update_kernel(TPArgs a, int ep, int64_
     const int64_t rest = unit / nslice;
     const int blk = (int)(rest % nblk);
     const int64_t chain = rest / nblk;
-    const uint32_t nseg = a.nseg[chain * a.nepoch + ep];
-    if ((uint32_t)blk * kRPI >= nseg) return;
     const int64_t t0 = (int64_t)ep * a.E;
     const int ne = (int)((a.T - t0) < a.E ? (a.T - t0) : a.E);
     const int n = ne * a.W;
@@ -330,22 +335,33 @@ __global__ __launch_bounds__(256) void tp_update_kernel(TPArgs a, int ep, int64_
     const rsrc_t Mr = make_rsrc(a.M + chain * a.N * a.d_v, (uint32_t)(a.N * a.d_v * 4));
     const uint32_t rowb = (uint32_t)a.d_v * 4u;
     const TPEntry *se = a.sorted + chain * a.T * a.W + t0 * a.W;
-    const uint32_t *sg = a.segs + chain * a.T * a.W + t0 * a.W;
 
-    const uint32_t k = (uint32_t)blk * kRPI + g;
-    const bool ok = k < nseg;
-    const uint32_t kk = ok ? k : 0;
-    const int j0 = (int)sg[kk];
-    const int j1 = ok ? (kk + 1 < nseg ? (int)sg[kk + 1] : n) : j0;
-    const uint32_t s = se[j0].slot;
-    const uint32_t off = (ok & col_ok) ? s * rowb + col * 4u : kOff;
-    float4 row = buf_load4(Mr, off);
-    for (int j = j0; j < j1; j++) {
-        const TPEntry e = se[j];
-        const float4 vv = load_v<BF16>(a.v, vrow0 + (t0 + (e.tw >> 6)) * hd);
-        row = fma4(e.a, row, e.c, vv);
+    const int j0 = (blk * kRPI + g) * SPG;
+    TPEntry e[SPG];
+#pragma unroll
+    for (int s = 0; s < SPG; s++) e[s] = se[j0 + s < n ? j0 + s : n - 1];
+    const uint32_t prev0 = j0 > 0 && j0 - 1 < n ? se[j0 - 1].slot : 0xFFFFFFFFu;
+    bool head[SPG];
+    float4 row[SPG], vv[SPG];
+#pragma unroll
+    for (int s = 0; s < SPG; s++) {
+        const uint32_t prev = s == 0 ? prev0 : e[s - 1].slot;
+        head[s] = (j0 + s < n) & (e[s].slot != prev);
+        row[s] = buf_load4(Mr, (head[s] & col_ok) ? e[s].slot * rowb + col * 4u : kOff);
+        vv[s] = load_v<BF16>(a.v, vrow0 + (t0 + (e[s].tw >> 6)) * hd);
     }
-    buf_store4(row, Mr, off);
+#pragma unroll
+    for (int s = 0; s < SPG; s++) {
+        float4 r = fma4(e[s].a, row[s], e[s].c, vv[s]);
+        if (head[s]) {
+            for (int j = j0 + s + 1; j < n; j++) {  // the rest of the segment, in time order
+                const TPEntry f = se[j];
+                if (f.slot != e[s].slot) break;
+                r = fma4(f.a, r, f.c, load_v<BF16>(a.v, vrow0 + (t0 + (f.tw >> 6)) * hd));
+            }
+        }
+        buf_store4(r, Mr, (head[s] & col_ok) ? e[s].slot * rowb + col * 4u : kOff);
+    }
 }
 
 }  // namespace
@@ -370,8 +386,8 @@ size_t tp_workspace_bytes(const Shape &s)
     const int E = tp_epoch_len(s);
     const size_t nep = (size_t)((s.T + E - 1) / E);
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    return up(ev * sizeof(TPEntry)) + 2 * up(ev * 8) + up(ev * 4) + up(chains * nep * 4) +
-           up(chains * (size_t)s.T * s.R * 4);
+    (void)nep;
+    return up(ev * sizeof(TPEntry)) + 2 * up(ev * 8) + up(chains * (size_t)s.T * kMaxK * 4);
 }
 
 static TPArgs tp_args(const Shape &s, const uint32_t *rec, void *ws, const void *v, float *y,
@@ -391,10 +407,6 @@ static TPArgs tp_args(const Shape &s, const uint32_t *rec, void *ws, const void 
     p += up(ev * 8);
     a.tmpB = reinterpret_cast<uint64_t *>(p);
     p += up(ev * 8);
-    a.segs = reinterpret_cast<uint32_t *>(p);
-    p += up(ev * 4);
-    a.nseg = reinterpret_cast<uint32_t *>(p);
-    p += up(chains * a.nepoch * 4);
     a.rlink = reinterpret_cast<uint32_t *>(p);
     a.rec = rec;
     a.v = v;
@@ -451,13 +463,14 @@ hipError_t launch_tp_apply(const Shape &s, const uint32_t *rec, void *ws, const 
 #undef SDM_TP_READ
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        const int nblk = (ne * s.W + kRPI - 1) / kRPI;  // bound on segment blocks
+        constexpr int SPG = 4;  // sorted events per row group
+        const int nblk = (ne * s.W + kRPI * SPG - 1) / (kRPI * SPG);
         const int64_t uunits = a.chains * nblk * nslice;
         const dim3 ugrid((unsigned)((uunits + 3) / 4));
-        if (bf16) hipLaunchKernelGGL(tp_update_kernel<true>, ugrid, dim3(256), 0, st, a, ep, uunits,
-                                     nslice, nblk);
-        else hipLaunchKernelGGL(tp_update_kernel<false>, ugrid, dim3(256), 0, st, a, ep, uunits,
-                                nslice, nblk);
+        if (bf16) hipLaunchKernelGGL((tp_update_kernel<true, SPG>), ugrid, dim3(256), 0, st, a, ep,
+                                     uunits, nslice, nblk);
+        else hipLaunchKernelGGL((tp_update_kernel<false, SPG>), ugrid, dim3(256), 0, st, a, ep,
+                                uunits, nslice, nblk);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

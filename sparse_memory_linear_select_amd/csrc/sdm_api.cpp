@@ -75,16 +75,18 @@ size_t records_bytes(const sdm_ctx *h, int B, int64_t T)
 }
 
 // AUTO: the token-serial schedule runs one wavefront per (chain, 32-column
-// slice) and needs at least two of them per compute unit (512) to cover the
-// HBM latency; with fewer chains the time-parallel schedule, whose parallelism
-// does not depend on the chain count, is faster (measured on MI355X: 8 chains
-// of 1024 columns 26 ms vs 43 ms, one chain of 2048 columns 0.43 s vs 1.7 s).
+// slice) and needs about four per compute unit (1024) to cover the HBM
+// latency; with fewer, the time-parallel schedule (whose parallelism does not
+// depend on the chain count, and which also merges repeated writes to a slot
+// within an epoch) is faster.  Measured write+read on MI355X: 32 chains x 512
+// columns 11.2 ms vs 12.2 ms, 8 x 1024 22.0 vs 43.3, 1 x 2048 (2^20 tokens)
+// 339 vs 1676; 32 x 1024 (1024 units) 43.6 vs 41.4.
 sdm_variant resolve_variant(const sdm_ctx *h, int B, int64_t T, sdm_variant v)
 {
     if (v != SDM_VARIANT_AUTO) return v;
     const sdm::Shape s = shape_of(h, B, T);
     const int64_t units = (int64_t)B * h->H * ((h->d_v + 31) / 32);
-    if (units < 512 && sdm::tp_supported(s)) return SDM_VARIANT_TIMEPAR;
+    if (units < 1024 && sdm::tp_supported(s)) return SDM_VARIANT_TIMEPAR;
     return SDM_VARIANT_SERIAL;
 }
 
