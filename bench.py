@@ -5,10 +5,16 @@ read) on one MI355X, on the seeded synthetic workload.
     python bench.py [--steps K] [--warmup W] [--workload 1] [--gpus 1]
 
 A step is one sdm_forward over the whole workload (M <- M_0, selection of
-every head-token, forwarding plan, then the token-serial write/read), issued
-as sdm_prepare + sdm_apply so that HIP events on the launch stream time the
-write/read kernel on its own.  Inputs are resident in HBM before timing.
+every head-token, then the write/read recurrence over all tokens), issued as
+sdm_prepare + sdm_apply so that HIP events on the launch stream time the
+write/read phase on its own.  Inputs are resident in HBM before timing.
 Prints one JSON line.
+
+roofline: HBM-bound; achieved = algorithmic row bytes of the step (per
+head-token (W + R) row reads + W row writes of d_v float32) / the write/read
+phase's duration; traffic = the same phase's HBM bytes from rocprofv3
+FETCH_SIZE / WRITE_SIZE counters, scaled by a copy kernel of known size
+(profiles/), or null when the kernel source changed since.
 """
 from __future__ import annotations
 
@@ -30,19 +36,28 @@ def _log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def _traffic(wl, rw_launches_per_step=1):
-    """Counter-measured HBM bytes per launch of the write/read kernel, if a
-    committed summary matches the current kernel source, else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_rw_serial_{wl.name.replace(' ', '_')}.json")
+SCHEDULES = {  # schedule -> (kernel source, kernels of the write/read phase)
+    "token-serial": ("rw_serial.hip", "rw_serial_kernel (one launch)"),
+    "time-parallel": ("rw_timepar.hip", "tp_read_kernel + tp_update_kernel (one pair per epoch)"),
+}
+
+
+def _traffic(wl, schedule):
+    """Counter-measured HBM bytes of the write/read phase per step, if a
+    committed summary exists for this workload and schedule and the kernel
+    source is unchanged since the counters were taken; else None."""
+    src_name = SCHEDULES[schedule][0]
+    tag = schedule.replace("-", "_") + "__" + wl.name.replace(" ", "_")
+    path = os.path.join(ROOT, "profiles", f"traffic_{tag}.json")
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))
-        src = open(os.path.join(ROOT, "sparse_memory_linear_select_amd", "csrc",
-                                "rw_serial.hip"), "rb").read()
+        src = open(os.path.join(ROOT, "sparse_memory_linear_select_amd", "csrc", src_name),
+                   "rb").read()
         if rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
             return None
-        return float(rec["hbm_bytes_per_launch"])
+        return float(rec["hbm_bytes_per_step"])
     except Exception:
         return None
 
@@ -147,9 +162,10 @@ def main():
     rw_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
     prep_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
     ht = wl.head_tokens
-    row_bytes = ht * (2 * wl.W + wl.R) * wl.d_v * 4  # algorithmic row traffic per launch
+    row_bytes = ht * (2 * wl.W + wl.R) * wl.d_v * 4  # algorithmic row traffic per step
     achieved = row_bytes / (rw_ms * 1e-3) / 1e9
-    traffic = _traffic(wl)
+    schedule = sdm.variant_name(core, B, T, dt_code, var)
+    traffic = _traffic(wl, schedule)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -170,13 +186,16 @@ def main():
         "data": "synthetic (seeded; recipe in sdm_inputs.py)",
         "config": {"workload": wl.name, "B": B, "T": T, "H": H, "sqrtN": wl.sqrtN, "N": wl.N,
                    "d_v": wl.d_v, "W": wl.W, "R": wl.R, "inputs": wl.dtype,
-                   "schedule": sdm.variant_name(core, B, T, dt_code, var)},
+                   "schedule": schedule},
         "row_gbs_whole_step": row_bytes / (ms_step * 1e-3) / 1e9,
         "breakdown_ms": {"prepare (init+select+plan/sort)": prep_ms, "write+read": rw_ms},
         "wall_s_timed": wall,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": traffic},
+                     "traffic": traffic,
+                     "traffic_unit": "HBM bytes per step (write/read phase, counters)",
+                     "kernel": SCHEDULES[schedule][1],
+                     "algorithmic_bytes": row_bytes},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -73,21 +73,31 @@ struct TPArgs {
     const uint32_t *rec;  // token records (slots, coefficients)
     TPEntry *sorted;      // [chain][T*W] sorted write events, epoch regions
     uint64_t *tmpA, *tmpB;  // [chain][T*W] radix ping-pong (key << 32 | event)
+    uint16_t *ckey;       // [chain][T*W] coarse keys of the sorted events (slot >> kshift)
     uint32_t *rlink;      // [chain][T][kMaxK] (first << 16) | count
     const void *v;
     float *y, *M;
     int64_t T, N;
     int H, d_v, W, R, Wp, Rp, rec_dwords;
-    int E, nepoch, passes;
+    int E, nepoch, passes, kshift;
     int64_t chains;
 };
 
 // ------------------------------------------------------------------ sort
 
+constexpr int kDigitBits = 9;                  // radix digit: 512 buckets
+constexpr int kBuckets = 1 << kDigitBits;
+constexpr int kWaves = kSortThreads / 64;
+
+// Stable LSD radix sort of one epoch's write events by slot (one workgroup per
+// (chain, epoch)).  Events are numbered j = token_in_epoch * W + w, so the
+// input order is time order and stability keeps each slot's writes in time
+// order.  The last pass writes the 16-byte entries and a 16-bit coarse key
+// (slot >> kshift) per entry for the link search.
 __global__ __launch_bounds__(kSortThreads) void tp_sort_kernel(TPArgs a)
 {
-    __shared__ uint32_t bins[256];
-    __shared__ uint32_t wcnt[kSortThreads / 64][256];
+    __shared__ uint32_t bins[kBuckets];
+    __shared__ uint32_t wcnt[kWaves][kBuckets];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = tid >> 6;
@@ -101,7 +111,7 @@ __global__ __launch_bounds__(kSortThreads) void tp_sort_kernel(TPArgs a)
     const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
     for (int p = 0; p < a.passes; p++) {
-        const int shift = 8 * p;
+        const int shift = kDigitBits * p;
         const uint64_t *src = (p & 1) ? a.tmpA + base : a.tmpB + base;  // unused when p == 0
         uint64_t *dst = (p & 1) ? a.tmpB + base : a.tmpA + base;
         const bool last = p == a.passes - 1;
@@ -114,25 +124,26 @@ __global__ __launch_bounds__(kSortThreads) void tp_sort_kernel(TPArgs a)
             return src[j];
         };
         // histogram of this digit
-        if (tid < 256) bins[tid] = 0;
+        for (int k = tid; k < kBuckets; k += kSortThreads) bins[k] = 0;
         __syncthreads();
         for (int j = tid; j < n; j += kSortThreads)
-            atomicAdd(&bins[(uint32_t)(item(j) >> (32 + shift)) & 255u], 1u);
+            atomicAdd(&bins[(uint32_t)(item(j) >> (32 + shift)) & (kBuckets - 1)], 1u);
         __syncthreads();
-        if (wv == 0) {  // exclusive scan of 256 bins, 4 per lane
-            uint32_t c[4], s = 0;
-            for (int k = 0; k < 4; k++) {
-                c[k] = bins[lane * 4 + k];
-                s += c[k];
+        if (wv == 0) {  // exclusive scan of the buckets, kBuckets/64 per lane
+            constexpr int PER = kBuckets / 64;
+            uint32_t c[PER], sum = 0;
+            for (int k = 0; k < PER; k++) {
+                c[k] = bins[lane * PER + k];
+                sum += c[k];
             }
-            uint32_t incl = s;
+            uint32_t incl = sum;
             for (int o = 1; o < 64; o <<= 1) {
                 const uint32_t t = (uint32_t)__shfl_up((int)incl, o, 64);
                 if (lane >= o) incl += t;
             }
-            uint32_t run = incl - s;
-            for (int k = 0; k < 4; k++) {
-                bins[lane * 4 + k] = run;
+            uint32_t run = incl - sum;
+            for (int k = 0; k < PER; k++) {
+                bins[lane * PER + k] = run;
                 run += c[k];
             }
         }
@@ -142,11 +153,10 @@ __global__ __launch_bounds__(kSortThreads) void tp_sort_kernel(TPArgs a)
             const int j = tb + tid;
             const bool valid = j < n;
             const uint64_t it = valid ? item(j) : 0;
-            const uint32_t dg = (uint32_t)(it >> (32 + shift)) & 255u;
-            for (int k = tid; k < (kSortThreads / 64) * 256; k += kSortThreads)
-                (&wcnt[0][0])[k] = 0;
-            uint64_t peers = __ballot(valid);
-            for (int bit = 0; bit < 8; bit++) {
+            const uint32_t dg = (uint32_t)(it >> (32 + shift)) & (kBuckets - 1);
+            for (int k = tid; k < kWaves * kBuckets; k += kSortThreads) (&wcnt[0][0])[k] = 0;
+            uint64_t peers = __ballot(valid);  // lanes of this wave with the same digit
+            for (int bit = 0; bit < kDigitBits; bit++) {
                 const uint64_t m = __ballot((dg >> bit) & 1u);
                 peers &= ((dg >> bit) & 1u) ? m : ~m;
             }
@@ -154,21 +164,21 @@ __global__ __launch_bounds__(kSortThreads) void tp_sort_kernel(TPArgs a)
             __syncthreads();
             if (valid && rank == 0) wcnt[wv][dg] = (uint32_t)__popcll(peers);
             __syncthreads();
-            if (tid < 256) {  // per digit: offsets of each wave's run, in wave order
-                uint32_t run = bins[tid];
-                for (int w = 0; w < kSortThreads / 64; w++) {
-                    const uint32_t c = wcnt[w][tid];
-                    wcnt[w][tid] = run;
+            for (int d = tid; d < kBuckets; d += kSortThreads) {  // per digit, in wave order
+                uint32_t run = bins[d];
+                for (int w = 0; w < kWaves; w++) {
+                    const uint32_t c = wcnt[w][d];
+                    wcnt[w][d] = run;
                     run += c;
                 }
-                bins[tid] = run;
+                bins[d] = run;
             }
             __syncthreads();
             if (valid) {
                 const uint32_t pos = wcnt[wv][dg] + rank;
                 if (!last) {
                     dst[pos] = it;
-                } else {  // final order: write the 16-byte entries
+                } else {  // final order: the 16-byte entries and the coarse keys
                     const uint32_t ev = (uint32_t)it;
                     const int tl = (int)(ev / (uint32_t)a.W), w = (int)(ev - tl * a.W);
                     const float *rf = reinterpret_cast<const float *>(recc + (int64_t)tl * a.rec_dwords);
@@ -178,34 +188,56 @@ __global__ __launch_bounds__(kSortThreads) void tp_sort_kernel(TPArgs a)
                     e.a = rf[a.Wp + w];
                     e.c = rf[2 * a.Wp + w];
                     a.sorted[base + pos] = e;
+                    a.ckey[base + pos] = (uint16_t)(e.slot >> a.kshift);
                 }
             }
             __syncthreads();
         }
     }
-    __syncthreads();  // the sorted entries of this epoch are complete (workgroup scope)
+}
 
-    // read links: in-epoch writes of the read slot at tokens <= the read token
+// Read links of one (chain, epoch): for every read, the first of the epoch's
+// writes to its slot and how many of them precede it (token <= its own).  The
+// coarse keys (slot >> kshift) of every stride-th sorted write sit in LDS
+// (at most 64 KiB): a binary search there brackets the slot, a short forward
+// scan of the entries finds the exact range.
+__global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int stride)
+{
+    extern __shared__ uint16_t ck[];
+    const int tid = threadIdx.x;
+    const int64_t chain = blockIdx.x / a.nepoch;
+    const int ep = (int)(blockIdx.x - chain * a.nepoch);
+    const int64_t t0 = (int64_t)ep * a.E;
+    const int ne = (int)((a.T - t0) < a.E ? (a.T - t0) : a.E);
+    const int n = ne * a.W;
+    const int ns = (n + stride - 1) / stride;
+    const int64_t base = chain * a.T * a.W + t0 * a.W;
+    const uint32_t *recc = a.rec + (chain * a.T + t0) * a.rec_dwords;
     const TPEntry *se = a.sorted + base;
+    for (int k = tid; k < ns; k += kSortThreads) ck[k] = a.ckey[base + (int64_t)k * stride];
+    __syncthreads();
     const int nr = ne * a.R;
     for (int i = tid; i < nr; i += kSortThreads) {
         const int tl = i / a.R, r = i - tl * a.R;
         const uint32_t s = recc[(int64_t)tl * a.rec_dwords + 3 * a.Wp + r] & kSlotMask;
-        int lo = 0, hi = n;  // first entry with slot >= s
+        const uint32_t c = s >> a.kshift;
+        int lo = 0, hi = ns;  // first sample with coarse key >= c
         while (lo < hi) {
             const int mid = (lo + hi) >> 1;
-            if (se[mid].slot < s) lo = mid + 1;
+            if (ck[mid] < c) lo = mid + 1;
             else hi = mid;
         }
-        int l2 = lo, h2 = n;  // first entry past (s, tl)
-        while (l2 < h2) {
-            const int mid = (l2 + h2) >> 1;
-            const TPEntry e = se[mid];
-            if (e.slot == s && (int)(e.tw >> 6) <= tl) l2 = mid + 1;
-            else h2 = mid;
+        // the sample before it has a smaller slot, so the slot's first entry follows it
+        int j = lo > 0 ? (lo - 1) * stride + 1 : 0;
+        while (j < n && se[j].slot < s) j++;
+        int l2 = j;  // past the writes of s at tokens <= tl
+        while (l2 < n) {
+            const TPEntry e = se[l2];
+            if (e.slot != s || (int)(e.tw >> 6) > tl) break;
+            l2++;
         }
-        const uint32_t cnt = (uint32_t)(l2 - lo);  // lo may equal n (= 65536) only when cnt == 0
-        a.rlink[(chain * a.T + t0 + tl) * kMaxK + r] = cnt ? (((uint32_t)lo << 16) | cnt) : 0u;
+        const uint32_t cnt = (uint32_t)(l2 - j);  // j may equal n (= 65536) only when cnt == 0
+        a.rlink[(chain * a.T + t0 + tl) * kMaxK + r] = cnt ? (((uint32_t)j << 16) | cnt) : 0u;
     }
 }
 
@@ -337,9 +369,9 @@ __global__ __launch_bounds__(256) void tp_update_kernel(TPArgs a, int ep, int64_
     const TPEntry *se = a.sorted + chain * a.T * a.W + t0 * a.W;
 
     const int j0 = (blk * kRPI + g) * SPG;
-    TPEntry e[SPG];
+    TPEntry e[SPG + 1];  // this group's events and the one after them
 #pragma unroll
-    for (int s = 0; s < SPG; s++) e[s] = se[j0 + s < n ? j0 + s : n - 1];
+    for (int s = 0; s <= SPG; s++) e[s] = se[j0 + s < n ? j0 + s : n - 1];
     const uint32_t prev0 = j0 > 0 && j0 - 1 < n ? se[j0 - 1].slot : 0xFFFFFFFFu;
     bool head[SPG];
     float4 row[SPG], vv[SPG];
@@ -353,8 +385,16 @@ __global__ __launch_bounds__(256) void tp_update_kernel(TPArgs a, int ep, int64_
 #pragma unroll
     for (int s = 0; s < SPG; s++) {
         float4 r = fma4(e[s].a, row[s], e[s].c, vv[s]);
-        if (head[s]) {
-            for (int j = j0 + s + 1; j < n; j++) {  // the rest of the segment, in time order
+        // the rest of the segment, in time order: events of this group from
+        // registers, then (rarely) events past the group from memory
+        bool more = true;
+#pragma unroll
+        for (int s2 = s + 1; s2 < SPG; s2++) {
+            more = more & (j0 + s2 < n) & (e[s2].slot == e[s].slot);
+            if (more) r = fma4(e[s2].a, r, e[s2].c, vv[s2]);
+        }
+        if (head[s] & more & (j0 + SPG < n) & (e[SPG].slot == e[s].slot)) {
+            for (int j = j0 + SPG; j < n; j++) {
                 const TPEntry f = se[j];
                 if (f.slot != e[s].slot) break;
                 r = fma4(f.a, r, f.c, load_v<BF16>(a.v, vrow0 + (t0 + (f.tw >> 6)) * hd));
@@ -366,12 +406,17 @@ __global__ __launch_bounds__(256) void tp_update_kernel(TPArgs a, int ep, int64_
 
 }  // namespace
 
+#ifndef SDM_TP_EPOCH_LOAD
+#define SDM_TP_EPOCH_LOAD 1
+#endif
+
 int tp_epoch_len(const Shape &s)
 {
-    // E*W <= 65536 (links hold 16-bit positions), E <= 1024, and E*W/N <= 1
-    // so that a read replays few in-epoch writes on average.
+    // E*W <= 65536 (links hold 16-bit positions), E <= 1024, and
+    // E*W <= SDM_TP_EPOCH_LOAD * N: longer epochs merge more repeated writes
+    // to a slot, but a read then replays more in-epoch writes.
     int64_t e = 1024;
-    while (e > 1 && (e * s.W > 65536 || e * s.W > s.N())) e >>= 1;
+    while (e > 1 && (e * s.W > 65536 || e * s.W > (int64_t)SDM_TP_EPOCH_LOAD * s.N())) e >>= 1;
     if (e > s.T) {
         e = 1;
         while (e < s.T) e <<= 1;
@@ -387,7 +432,8 @@ size_t tp_workspace_bytes(const Shape &s)
     const size_t nep = (size_t)((s.T + E - 1) / E);
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     (void)nep;
-    return up(ev * sizeof(TPEntry)) + 2 * up(ev * 8) + up(chains * (size_t)s.T * kMaxK * 4);
+    return up(ev * sizeof(TPEntry)) + 2 * up(ev * 8) + up(ev * 2) +
+           up(chains * (size_t)s.T * kMaxK * 4);
 }
 
 static TPArgs tp_args(const Shape &s, const uint32_t *rec, void *ws, const void *v, float *y,
@@ -407,6 +453,8 @@ static TPArgs tp_args(const Shape &s, const uint32_t *rec, void *ws, const void 
     p += up(ev * 8);
     a.tmpB = reinterpret_cast<uint64_t *>(p);
     p += up(ev * 8);
+    a.ckey = reinterpret_cast<uint16_t *>(p);
+    p += up(ev * 2);
     a.rlink = reinterpret_cast<uint32_t *>(p);
     a.rec = rec;
     a.v = v;
@@ -424,7 +472,8 @@ static TPArgs tp_args(const Shape &s, const uint32_t *rec, void *ws, const void 
     a.chains = (int64_t)chains;
     int bits = 1;
     while ((int64_t(1) << bits) < s.N()) bits++;
-    a.passes = (bits + 7) / 8;
+    a.passes = (bits + kDigitBits - 1) / kDigitBits;
+    a.kshift = bits > 16 ? bits - 16 : 0;
     return a;
 }
 
@@ -438,6 +487,14 @@ hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipS
     TPArgs a = tp_args(s, rec, ws, nullptr, nullptr, nullptr);
     const int64_t blocks = a.chains * a.nepoch;
     hipLaunchKernelGGL(tp_sort_kernel, dim3((unsigned)blocks), dim3(kSortThreads), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // sampled coarse keys: at most 32768 of them (64 KiB of LDS)
+    const int64_t nmax = (int64_t)a.E * s.W;
+    const int stride = nmax > 32768 ? (int)((nmax + 32767) / 32768) : 1;
+    const size_t lds = (size_t)((nmax + stride - 1) / stride) * sizeof(uint16_t);
+    hipLaunchKernelGGL(tp_link_kernel, dim3((unsigned)blocks), dim3(kSortThreads), lds, st, a,
+                       stride);
     return hipGetLastError();
 }
 

@@ -74,20 +74,16 @@ size_t records_bytes(const sdm_ctx *h, int B, int64_t T)
     return round_up((size_t)B * h->H * (size_t)T * (size_t)L.dwords() * 4u);
 }
 
-// AUTO: the token-serial schedule runs one wavefront per (chain, 32-column
-// slice) and needs about four per compute unit (1024) to cover the HBM
-// latency; with fewer, the time-parallel schedule (whose parallelism does not
-// depend on the chain count, and which also merges repeated writes to a slot
-// within an epoch) is faster.  Measured write+read on MI355X: 32 chains x 512
-// columns 11.2 ms vs 12.2 ms, 8 x 1024 22.0 vs 43.3, 1 x 2048 (2^20 tokens)
-// 339 vs 1676; 32 x 1024 (1024 units) 43.6 vs 41.4.
+// AUTO: the time-parallel schedule whenever it applies.  Its parallelism does
+// not depend on the number of chains, and it merges repeated writes to a slot
+// within an epoch.  Measured write+read on MI355X (time-parallel vs
+// token-serial): 32 chains x 512 columns 9.6 ms vs 12.2, 8 x 1024 19.5 vs 43.3,
+// 32 x 1024 38.6 vs 41.4, 1 x 2048 (2^20 tokens) 324 vs 1676.  The token-serial
+// schedule remains for d_v % 4 != 0 (one column per lane) and on request.
 sdm_variant resolve_variant(const sdm_ctx *h, int B, int64_t T, sdm_variant v)
 {
     if (v != SDM_VARIANT_AUTO) return v;
-    const sdm::Shape s = shape_of(h, B, T);
-    const int64_t units = (int64_t)B * h->H * ((h->d_v + 31) / 32);
-    if (units < 1024 && sdm::tp_supported(s)) return SDM_VARIANT_TIMEPAR;
-    return SDM_VARIANT_SERIAL;
+    return sdm::tp_supported(shape_of(h, B, T)) ? SDM_VARIANT_TIMEPAR : SDM_VARIANT_SERIAL;
 }
 
 size_t ws_bytes_for(const sdm_ctx *h, int B, int64_t T, sdm_variant var)
