@@ -77,6 +77,54 @@ def cpu_baseline(d, wl, seqs):
                       f"{wl.d_v} columns), select + init + recurrence, {dt:.2f} s wall"}
 
 
+def decode(args, wl):
+    """Decode: B sequences advance by one token per call (T = 1), continuing
+    from the state left by a 256-token prefill.  Reports the step latency."""
+    import numpy as np
+    import torch
+
+    import sdm_inputs as si
+    import sparse_memory_linear_select_amd as sdm
+
+    prefix, steps, warm = 256, args.steps * 20, args.warmup * 5
+    d = si.generate(wl, T=prefix + warm + steps)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    core = sdm.SDM(up(d["M0"]), wl.W, wl.R)
+    names = ("kp", "qp", "v", "alpha", "beta")
+    pre = [up(d[n][:, :prefix]) for n in names]
+    var = {"auto": sdm.AUTO, "serial": sdm.SERIAL, "timepar": sdm.TIMEPAR}[args.variant]
+    _, M = core.forward(*pre, variant=var)
+    toks = [[up(d[n][:, t:t + 1]) for n in names] for t in range(prefix, prefix + warm + steps)]
+    dt_code = sdm.BF16 if wl.dtype == "bf16" else sdm.F32
+    ws = torch.empty(core.workspace_size(wl.B, 1, dt_code, var), dtype=torch.uint8, device=dev)
+    y = torch.empty((wl.B, 1, wl.H, wl.d_v), dtype=torch.float32, device=dev)
+    for t in range(warm):
+        core.forward(*toks[t], variant=var, y=y, M=M, workspace=ws, cont=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(warm, warm + steps):
+        core.forward(*toks[t], variant=var, y=y, M=M, workspace=ws, cont=True)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    print(json.dumps({
+        "metric": "SDM decode step latency (one token for each of B sequences, state continued)",
+        "value": us, "unit": "us/step", "higher_is_better": False, "n_gpus": 1, "steps": steps,
+        "warmup": warm, "head_tokens_per_s": wl.B * wl.H / (us * 1e-6),
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "sqrtN": wl.sqrtN, "d_v": wl.d_v,
+                   "W": wl.W, "R": wl.R, "prefill_tokens": prefix,
+                   "schedule": sdm.variant_name(core, wl.B, 1, dt_code, var)},
+        "data": "synthetic (seeded; recipe in sdm_inputs.py)"}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -89,6 +137,8 @@ def main():
     ap.add_argument("--variant", choices=["auto", "serial", "timepar"], default="auto",
                     help="write/read schedule (default: the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode", action="store_true",
+                    help="measure one-token decode steps (continuing the state) instead")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -104,6 +154,8 @@ def main():
     import sparse_memory_linear_select_amd as sdm
 
     wl = si.WORKLOADS[args.workload]
+    if args.decode:
+        return decode(args, wl)
     _log(f"workload {args.workload}: {wl}")
     t = time.perf_counter()
     d = si.generate(wl)

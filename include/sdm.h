@@ -169,6 +169,19 @@ sdm_status sdm_apply(sdm_handle h, int B, int64_t T, const void *v, sdm_dtype dt
                      sdm_variant variant, void *workspace, size_t ws_bytes, float *y,
                      float *M, void *stream);
 
+/*
+ * Write-slot utilisation (an addressing-collapse monitor; the explainer's
+ * limitations and engineering notes suggest tracking how often each slot is
+ * updated).  Runs the write-set selection of every head-token and adds, for
+ * head h and slot n, the number of head-tokens (b, t) whose write set
+ * contains n:  counts[h][n] += #{(b, t) : n in I^w_(b,t,h)}.
+ *   kp      device [B][T][H][2*sqrtN], element type `dtype`.
+ *   counts  device [H][N] uint32, accumulated into (zero it for a fresh
+ *           count; integer atomics, so the result does not depend on order).
+ */
+sdm_status sdm_write_histogram(sdm_handle h, int B, int64_t T, const void *kp,
+                               sdm_dtype dtype, uint32_t *counts, void *stream);
+
 /* Static description of a status code. */
 const char *sdm_status_string(sdm_status s);
 

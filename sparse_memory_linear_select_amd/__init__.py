@@ -34,7 +34,8 @@ STATUS = {0: "SDM_OK", 1: "SDM_ERR_ARG", 2: "SDM_ERR_UNSUPPORTED", 3: "SDM_ERR_W
 
 # every function include/sdm.h declares
 EXPORTS = ("sdm_create", "sdm_destroy", "sdm_workspace_size", "sdm_select", "sdm_forward",
-           "sdm_prepare", "sdm_apply", "sdm_status_string", "sdm_last_error")
+           "sdm_prepare", "sdm_apply", "sdm_write_histogram", "sdm_status_string",
+           "sdm_last_error")
 
 
 class SDMError(RuntimeError):
@@ -63,8 +64,9 @@ def lib():
         L.sdm_forward.argtypes = [p, i, i64, p, p, p, p, p, i, i, ctypes.c_uint, p, sz, p, p, p]
         L.sdm_prepare.argtypes = [p, i, i64, p, p, p, p, i, i, ctypes.c_uint, p, sz, p, p]
         L.sdm_apply.argtypes = [p, i, i64, p, i, i, p, sz, p, p, p]
+        L.sdm_write_histogram.argtypes = [p, i, i64, p, i, p, p]
         for f in ("sdm_create", "sdm_destroy", "sdm_workspace_size", "sdm_select", "sdm_forward",
-                  "sdm_prepare", "sdm_apply"):
+                  "sdm_prepare", "sdm_apply", "sdm_write_histogram"):
             getattr(L, f).restype = ctypes.c_int
         L.sdm_status_string.argtypes = [i]
         L.sdm_status_string.restype = ctypes.c_char_p
@@ -172,6 +174,20 @@ class SDM:
         _check(lib().sdm_select(self._h, B, T, _ptr(kp), _ptr(qp), _in_dtype(kp), _ptr(Iw),
                                 _ptr(kw), _ptr(Ir), _ptr(qw), _stream(dev)))
         return Iw, kw, Ir, qw
+
+    def write_histogram(self, kp: torch.Tensor, counts: torch.Tensor | None = None):
+        """Per head and slot, how many head-tokens wrote the slot ([H, N] int32 view of
+        uint32 counts).  `counts` (if given) is accumulated into."""
+        _dev_tensor(kp, "kp")
+        B, T = self._shape_in(kp, 2 * self.sqrtN, "kp")
+        if counts is None:
+            counts = torch.zeros((self.H, self.N), dtype=torch.int32, device=kp.device)
+        _dev_tensor(counts, "counts", torch.int32)
+        if tuple(counts.shape) != (self.H, self.N):
+            raise SDMError(1, f"counts must be [H, N] = [{self.H}, {self.N}]")
+        _check(lib().sdm_write_histogram(self._h, B, T, _ptr(kp), _in_dtype(kp), _ptr(counts),
+                                         _stream(kp.device)))
+        return counts
 
     def forward(self, kp, qp, v, alpha, beta, variant: int = AUTO, y=None, M=None,
                 workspace=None, cont: bool = False):

@@ -194,6 +194,22 @@ sdm_status sdm_select(sdm_handle h, int B, int64_t T, const void *kp, const void
     return SDM_OK;
 }
 
+sdm_status sdm_write_histogram(sdm_handle h, int B, int64_t T, const void *kp, sdm_dtype dtype,
+                               uint32_t *counts, void *stream)
+{
+    sdm_status st = check_handle_call(h, B, T, dtype);
+    if (st != SDM_OK) return st;
+    if (!kp || !counts) return fail(SDM_ERR_ARG, "null tensor pointer");
+    if (!aligned16(kp) || !aligned16(counts))
+        return fail(SDM_ERR_ARG, "tensor pointers must be 16-byte aligned");
+    const sdm::Shape s = shape_of(h, B, T);
+    hipError_t e = sdm::launch_select(s, kp, kp, dtype == SDM_BF16, nullptr, nullptr, nullptr,
+                                      nullptr, nullptr, nullptr, nullptr, (hipStream_t)stream,
+                                      counts);
+    if (e != hipSuccess) return hip_fail(e, "histogram launch");
+    return SDM_OK;
+}
+
 sdm_status sdm_prepare(sdm_handle h, int B, int64_t T, const void *kp, const void *qp,
                        const float *alpha, const float *beta, sdm_dtype dtype,
                        sdm_variant variant, unsigned flags, void *workspace, size_t ws_bytes,

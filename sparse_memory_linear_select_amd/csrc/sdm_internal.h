@@ -57,12 +57,13 @@ struct Shape {
 
 // ---- launchers (each returns the launch error, if any) ----
 
-// Selection.  With rec == nullptr it writes the API layout (Iw, kw, Ir, qw,
-// [B][T][H][K]); otherwise it writes token records (needs alpha, beta).
+// Selection.  With hist != nullptr it only counts write slots per head into
+// hist[H][N]; else with rec == nullptr it writes the API layout (Iw, kw, Ir,
+// qw, [B][T][H][K]); otherwise it writes token records (needs alpha, beta).
 hipError_t launch_select(const Shape &s, const void *kp, const void *qp, bool bf16,
                          int32_t *Iw, float *kw, int32_t *Ir, float *qw,
                          uint32_t *rec, const float *alpha, const float *beta,
-                         hipStream_t st);
+                         hipStream_t st, uint32_t *hist = nullptr);
 
 // M[b] <- M0 for every sequence b.
 hipError_t launch_init(const Shape &s, const float *M0, float *M, hipStream_t st);

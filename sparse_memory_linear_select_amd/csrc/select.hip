@@ -180,6 +180,8 @@ struct SelArgs {
     uint32_t *rec;
     int rec_dwords, Wp, Rp;
     const float *alpha, *beta;
+    uint32_t *hist;  // [H][N] write-slot counts (histogram mode: write lists only)
+    int lists;       // 2: write and read lists; 1: write lists only
 };
 
 template <int E>
@@ -212,10 +214,10 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
     __syncthreads();
 
     const int S = a.sqrtN;
-    const int64_t items = 2 * a.n_ht;
+    const int64_t items = a.lists * a.n_ht;
     for (int64_t it = (int64_t)blockIdx.x * 4 + wv; it < items; it += (int64_t)gridDim.x * 4) {
-        const int list = (int)(it & 1);
-        const int64_t ht = it >> 1;
+        const int list = a.lists == 2 ? (int)(it & 1) : 0;
+        const int64_t ht = a.lists == 2 ? it >> 1 : it;
         const int K = list ? a.R : a.W;
         const void *x = list ? a.qp : a.kp;
         const int64_t base = ht * 2 * S;
@@ -290,7 +292,10 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
         for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o, 64);
         const float w = ex / z;
 
-        if (a.rec == nullptr) {
+        if (a.hist != nullptr) {
+            // write-slot utilisation: one count per selected slot of head h
+            if (lane < K) atomicAdd(&a.hist[(int64_t)(ht % a.H) * a.sqrtN * a.sqrtN + n], 1u);
+        } else if (a.rec == nullptr) {
             if (lane < K) {
                 if (list == 0) {
                     a.Iw[ht * K + lane] = (int32_t)n;
@@ -330,7 +335,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
 template <int E>
 hipError_t launch_e(const SelArgs &args, hipStream_t st)
 {
-    const int64_t items = 2 * args.n_ht;
+    const int64_t items = args.lists * args.n_ht;
     int64_t blocks = (items + 3) / 4;
     if (blocks > 16384) blocks = 16384;
     if (blocks < 1) blocks = 1;
@@ -342,7 +347,7 @@ hipError_t launch_e(const SelArgs &args, hipStream_t st)
 
 hipError_t launch_select(const Shape &s, const void *kp, const void *qp, bool bf16,
                          int32_t *Iw, float *kw, int32_t *Ir, float *qw, uint32_t *rec,
-                         const float *alpha, const float *beta, hipStream_t st)
+                         const float *alpha, const float *beta, hipStream_t st, uint32_t *hist)
 {
     SelArgs a{};
     a.kp = kp;
@@ -365,6 +370,8 @@ hipError_t launch_select(const Shape &s, const void *kp, const void *qp, bool bf
     a.Rp = L.Rp;
     a.alpha = alpha;
     a.beta = beta;
+    a.hist = hist;
+    a.lists = hist ? 1 : 2;
     if (s.sqrtN <= 64) return launch_e<1>(a, st);
     if (s.sqrtN <= 128) return launch_e<2>(a, st);
     if (s.sqrtN <= 256) return launch_e<4>(a, st);

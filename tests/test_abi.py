@@ -116,6 +116,38 @@ def test_select_rejects_before_any_device_work():
         L.sdm_destroy(h)
 
 
+def test_histogram_rejects_before_any_device_work():
+    st, h = _create()
+    L = sdm.lib()
+    c = ctypes.c_void_p
+    try:
+        assert L.sdm_write_histogram(h, 1, 4, None, sdm.F32, c(FAKE), None) == 1
+        assert L.sdm_write_histogram(h, 1, 4, c(FAKE), sdm.F32, None, None) == 1
+        assert L.sdm_write_histogram(h, 1, 4, c(FAKE + 4), sdm.F32, c(FAKE), None) == 1
+        assert L.sdm_write_histogram(h, 0, 4, c(FAKE), sdm.F32, c(FAKE), None) == 1
+        assert L.sdm_write_histogram(None, 1, 4, c(FAKE), sdm.F32, c(FAKE), None) == 1
+    finally:
+        L.sdm_destroy(h)
+
+
+def test_prepare_apply_reject_before_any_device_work():
+    st, h = _create()
+    L = sdm.lib()
+    c = ctypes.c_void_p
+    try:
+        ok = [c(FAKE)] * 5
+        # prepare(h, B, T, kp, qp, alpha, beta, dtype, variant, flags, ws, ws_bytes, M, stream)
+        assert L.sdm_prepare(h, 1, 8, *ok[:4], sdm.F32, sdm.AUTO, 0, c(FAKE), 1 << 20, None, None) == 1
+        assert L.sdm_prepare(h, 1, 8, *ok[:4], sdm.F32, sdm.AUTO, 2, c(FAKE), 1 << 20, c(FAKE), None) == 1
+        assert L.sdm_prepare(h, 1, 8, *ok[:4], sdm.F32, sdm.AUTO, 0, c(FAKE), 16, c(FAKE), None) == 3
+        # apply(h, B, T, v, dtype, variant, ws, ws_bytes, y, M, stream)
+        assert L.sdm_apply(h, 1, 8, None, sdm.F32, sdm.AUTO, c(FAKE), 1 << 20, c(FAKE), c(FAKE), None) == 1
+        assert L.sdm_apply(h, 1, 8, c(FAKE), sdm.F32, sdm.AUTO, c(FAKE), 16, c(FAKE), c(FAKE), None) == 3
+        assert L.sdm_apply(h, 1, 8, c(FAKE), sdm.F32, 5, c(FAKE), 1 << 20, c(FAKE), c(FAKE), None) == 1
+    finally:
+        L.sdm_destroy(h)
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(sdm.SDMError):

@@ -232,3 +232,20 @@ def test_schedules_agree_bitwise_on_state(shape):
     _, _, y2, M2 = gpu_forward(d, W, R, sdm.TIMEPAR)
     assert torch.equal(M1, M2)
     assert torch.allclose(y1, y2, rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=VNAMES)
+def test_decode_token_by_token(variant):
+    """Decoding one token per call (continuing from the previous state) gives
+    the same y and M, bit for bit, as one call over the whole sequence."""
+    wl, d = _small(30, sqrtN=16, d_v=32, W=8, R=8, T=12, B=2, H=2)
+    core, dd, y, M = gpu_forward(d, wl.W, wl.R, variant)
+    M1 = torch.empty_like(M)
+    ys = []
+    for t in range(wl.T):
+        step = {n: dd[n][:, t:t + 1].contiguous() for n in ("kp", "qp", "v", "alpha", "beta")}
+        yt, _ = core.forward(step["kp"], step["qp"], step["v"], step["alpha"], step["beta"],
+                             M=M1, cont=t > 0, variant=variant)
+        ys.append(yt)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(ys, 1), y) and torch.equal(M1, M)

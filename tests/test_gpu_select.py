@@ -93,3 +93,24 @@ def test_select_full_workload(cfg):
         assert s.min() >= 0 and s.max() < wl.N and (np.diff(s, axis=-1) > 0).all()
         assert (w > 0).all() and np.abs(w.sum(-1) - 1).max() < 1e-5
         assert (np.diff(w, axis=-1) <= 1e-7).all()
+
+
+@pytest.mark.parametrize("cfg,T", [(0, None), (1, 256), (4, 512)])
+def test_write_histogram(cfg, T):
+    """Write-slot utilisation counts per head equal the oracle's selection
+    counted slot by slot; a second call accumulates."""
+    wl = si.WORKLOADS[cfg]
+    log(f"histogram: {wl.name} T={T or wl.T}")
+    d = si.generate(wl, T=T)
+    M0 = torch.zeros((wl.H, wl.N, 4), dtype=torch.float32, device="cuda")
+    core = sdm.SDM(M0, wl.W, wl.R)
+    kp = to_dev(d["kp"])
+    counts = core.write_histogram(kp)
+    torch.cuda.synchronize()
+    Iw, _ = oracle.select(d["kp"], wl.sqrtN, wl.W)
+    ref = np.stack([np.bincount(Iw[:, :, h].reshape(-1), minlength=wl.N) for h in range(wl.H)])
+    np.testing.assert_array_equal(counts.cpu().numpy(), ref)
+    assert ref.sum() == wl.B * (T or wl.T) * wl.H * wl.W
+    core.write_histogram(kp, counts)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(counts.cpu().numpy(), 2 * ref)
