@@ -190,10 +190,12 @@ class SDM:
         return counts
 
     def forward(self, kp, qp, v, alpha, beta, variant: int = AUTO, y=None, M=None,
-                workspace=None, cont: bool = False):
+                workspace=None, cont: bool = False, staged: bool = False):
         """(y, M): outputs [B,T,H,d_v] and final state [B,H,N,d_v] (float32).
 
         With cont=True, M must hold the state to continue from (no M <- M_0).
+        staged=True issues sdm_prepare + sdm_apply on the current stream
+        instead of sdm_forward (same result, no helper-stream overlap).
         """
         for t, n in ((kp, "kp"), (qp, "qp"), (v, "v")):
             _dev_tensor(t, n)
@@ -221,8 +223,15 @@ class SDM:
         need = self.workspace_size(B, T, dt, variant)
         if workspace is None or workspace.numel() < need:
             workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        flags = FLAG_CONTINUE if cont else 0
+        if staged:
+            _check(lib().sdm_prepare(self._h, B, T, _ptr(kp), _ptr(qp), _ptr(alpha), _ptr(beta),
+                                     dt, variant, flags, _ptr(workspace), workspace.numel(),
+                                     _ptr(M), _stream(dev)))
+            _check(lib().sdm_apply(self._h, B, T, _ptr(v), dt, variant, _ptr(workspace),
+                                   workspace.numel(), _ptr(y), _ptr(M), _stream(dev)))
+            return y, M
         _check(lib().sdm_forward(self._h, B, T, _ptr(kp), _ptr(qp), _ptr(v), _ptr(alpha),
-                                 _ptr(beta), dt, variant, FLAG_CONTINUE if cont else 0,
-                                 _ptr(workspace), workspace.numel(), _ptr(y), _ptr(M),
-                                 _stream(dev)))
+                                 _ptr(beta), dt, variant, flags, _ptr(workspace),
+                                 workspace.numel(), _ptr(y), _ptr(M), _stream(dev)))
         return y, M

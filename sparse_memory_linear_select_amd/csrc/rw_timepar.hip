@@ -7,13 +7,14 @@
 // row after every write at a token <= t (§3.1 step 3).  Slots never interact,
 // so the tokens are cut into epochs of E tokens and, per epoch:
 //
-//   sort     (all epochs at once, before the recurrence) the E*W write events
-//            of the epoch are sorted by slot with a stable LSD radix sort, so
-//            each slot's writes form one segment in time order; every read
-//            gets a link (first write of its slot in the epoch, number of
-//            those at tokens <= its own);
-//   read     each read gathers the row as it was at the epoch start, replays
-//            its linked writes in time order and adds q * row to y_t;
+//   sort     (before the recurrence) the E*W write events of the epoch are
+//            sorted by slot with a stable LSD radix sort, so each slot's
+//            writes form one segment in time order;
+//   plan     every read gets the weight of its slot's epoch-start row and
+//            the (token, weight) pairs of the v rows its in-epoch writes
+//            added (the composed affine map, scaled by the read weight q);
+//   read     y_t = weighted sum of epoch-start rows and v rows, all gathers
+//            independent of each other;
 //   update   the first event of each slot's segment loads the row once,
 //            applies all of the segment's writes in time order and stores it
 //            once.
@@ -21,8 +22,8 @@
 // Within an epoch everything is parallel; epochs follow each other in stream
 // order (read of epoch e, update of e, read of e+1, ...).  Each row value is
 // produced by the same float32 operations, in the same order, as in the
-// token-serial schedule, so both schedules give identical M; y uses the same
-// lane mapping and reduction order as the serial kernel with 8 lanes per row.
+// token-serial schedule, so both schedules give identical M; y agrees to
+// float32 rounding (its terms are grouped differently).
 #include "sdm_internal.h"
 
 namespace sdm {
@@ -74,12 +75,17 @@ struct TPArgs {
     TPEntry *sorted;      // [chain][T*W] sorted write events, epoch regions
     uint64_t *tmpA, *tmpB;  // [chain][T*W] radix ping-pong (key << 32 | event)
     uint16_t *ckey;       // [chain][T*W] coarse keys of the sorted events (slot >> kshift)
-    uint32_t *rlink;      // [chain][T][kMaxK] (first << 16) | count
+    uint32_t *rlink;      // [chain][T][kMaxK] replay links: (first << 16) | count
+    float *rwt;           // [chain][T][kMaxK] weight of each read's epoch-start row
+    uint32_t *npair;      // [chain][T] pairs in use
+    uint2 *pairs;         // [chain][T][P] (token in epoch, weight) of v rows to add
+    int P;                // pair capacity per token
     const void *v;
     float *y, *M;
     int64_t T, N;
     int H, d_v, W, R, Wp, Rp, rec_dwords;
     int E, nepoch, passes, kshift;
+    int ep0, nrun;  // sort/link launches: epochs [ep0, ep0 + nrun)
     int64_t chains;
 };
 
@@ -101,8 +107,8 @@ __global__ __launch_bounds__(kSortThreads) void tp_sort_kernel(TPArgs a)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = tid >> 6;
-    const int64_t chain = blockIdx.x / a.nepoch;
-    const int ep = (int)(blockIdx.x - chain * a.nepoch);
+    const int64_t chain = blockIdx.x / a.nrun;
+    const int ep = a.ep0 + (int)(blockIdx.x - chain * a.nrun);
     const int64_t t0 = (int64_t)ep * a.E;
     const int ne = (int)((a.T - t0) < a.E ? (a.T - t0) : a.E);  // tokens in this epoch
     const int n = ne * a.W;                                      // write events
@@ -196,17 +202,26 @@ __global__ __launch_bounds__(kSortThreads) void tp_sort_kernel(TPArgs a)
     }
 }
 
-// Read links of one (chain, epoch): for every read, the first of the epoch's
-// writes to its slot and how many of them precede it (token <= its own).  The
-// coarse keys (slot >> kshift) of every stride-th sorted write sit in LDS
-// (at most 64 KiB): a binary search there brackets the slot, a short forward
-// scan of the entries finds the exact range.
+// Read plan of one (chain, epoch).  A read of slot s at token t sees the
+// epoch-start row of s after the epoch's writes to s at tokens <= t, i.e.
+// (in time order k = 1..m, row <- a_k row + c_k v_k)
+//     row_t = A row_0 + sum_k C_k v_k,   A = prod_k a_k,  C_k = c_k prod_{l>k} a_l,
+// so q * row_t is a weighted sum of one epoch-start row and m rows of v.  Per
+// token, the read kernel gets the row weights q*A and a list of
+// (token, q*C_k) pairs; reads whose pairs do not fit the token's capacity P
+// keep weight q and a link (first write, count) that the read kernel replays.
+// The sorted writes of s form one segment (time order); the coarse keys
+// (slot >> kshift) of every stride-th sorted write sit in LDS (at most
+// 64 KiB): a binary search there brackets the slot, a short forward scan of
+// the entries finds the exact range.  One wavefront per token: lane r takes
+// read r, a prefix sum over the lanes places the pairs.
 __global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int stride)
 {
     extern __shared__ uint16_t ck[];
     const int tid = threadIdx.x;
-    const int64_t chain = blockIdx.x / a.nepoch;
-    const int ep = (int)(blockIdx.x - chain * a.nepoch);
+    const int lane = tid & 63;
+    const int64_t chain = blockIdx.x / a.nrun;
+    const int ep = a.ep0 + (int)(blockIdx.x - chain * a.nrun);
     const int64_t t0 = (int64_t)ep * a.E;
     const int ne = (int)((a.T - t0) < a.E ? (a.T - t0) : a.E);
     const int n = ne * a.W;
@@ -216,28 +231,62 @@ __global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int str
     const TPEntry *se = a.sorted + base;
     for (int k = tid; k < ns; k += kSortThreads) ck[k] = a.ckey[base + (int64_t)k * stride];
     __syncthreads();
-    const int nr = ne * a.R;
-    for (int i = tid; i < nr; i += kSortThreads) {
-        const int tl = i / a.R, r = i - tl * a.R;
-        const uint32_t s = recc[(int64_t)tl * a.rec_dwords + 3 * a.Wp + r] & kSlotMask;
-        const uint32_t c = s >> a.kshift;
-        int lo = 0, hi = ns;  // first sample with coarse key >= c
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (ck[mid] < c) lo = mid + 1;
-            else hi = mid;
+    for (int tl = tid >> 6; tl < ne; tl += kSortThreads / 64) {  // wave-uniform token
+        const uint32_t *rc = recc + (int64_t)tl * a.rec_dwords;
+        const bool real = lane < a.R;
+        int j = 0, cnt = 0;
+        float q = 0.0f;
+        if (real) {
+            const uint32_t s = rc[3 * a.Wp + lane] & kSlotMask;
+            q = __uint_as_float(rc[3 * a.Wp + a.Rp + lane]);
+            const uint32_t c = s >> a.kshift;
+            int lo = 0, hi = ns;  // first sample with coarse key >= c
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (ck[mid] < c) lo = mid + 1;
+                else hi = mid;
+            }
+            // the sample before it has a smaller slot, so the slot's first entry follows it
+            j = lo > 0 ? (lo - 1) * stride + 1 : 0;
+            while (j < n && se[j].slot < s) j++;
+            int l2 = j;  // past the writes of s at tokens <= tl
+            while (l2 < n) {
+                const TPEntry e = se[l2];
+                if (e.slot != s || (int)(e.tw >> 6) > tl) break;
+                l2++;
+            }
+            cnt = l2 - j;
         }
-        // the sample before it has a smaller slot, so the slot's first entry follows it
-        int j = lo > 0 ? (lo - 1) * stride + 1 : 0;
-        while (j < n && se[j].slot < s) j++;
-        int l2 = j;  // past the writes of s at tokens <= tl
-        while (l2 < n) {
-            const TPEntry e = se[l2];
-            if (e.slot != s || (int)(e.tw >> 6) > tl) break;
-            l2++;
+        // exclusive prefix sum of cnt over the lanes: this read's first pair
+        int incl = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int u = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += u;
         }
-        const uint32_t cnt = (uint32_t)(l2 - j);  // j may equal n (= 65536) only when cnt == 0
-        a.rlink[(chain * a.T + t0 + tl) * kMaxK + r] = cnt ? (((uint32_t)j << 16) | cnt) : 0u;
+        const int off = incl - cnt;
+        const bool fits = off + cnt <= a.P;
+        const int64_t ct = chain * a.T + t0 + tl;
+        uint2 *pp = a.pairs + ct * a.P;
+        float w = q;
+        if (cnt > 0 && fits) {
+            float A = 1.0f;  // product of the a's after the current write
+            for (int k = cnt - 1; k >= 0; k--) {
+                const TPEntry e = se[j + k];
+                pp[off + k] = make_uint2(e.tw >> 6, __float_as_uint(q * (e.c * A)));
+                A *= e.a;
+            }
+            w = q * A;
+        }
+        a.rwt[ct * kMaxK + lane] = w;
+        // j may equal n (= 65536) only when cnt == 0
+        a.rlink[ct * kMaxK + lane] = (cnt > 0 && !fits) ? (((uint32_t)j << 16) | cnt) : 0u;
+        // the reads that fit are a prefix of the lanes: their pairs are [0, npair)
+        const unsigned long long over = __ballot(cnt > 0 && !fits);
+        const int first_over = over ? __builtin_ctzll(over) : 63;
+        const int off_over = __shfl(off, first_over, 64);
+        const int total = __shfl(incl, 63, 64);
+        if (lane == 0) a.npair[ct] = (uint32_t)(over ? off_over : total);
     }
 }
 
@@ -265,9 +314,17 @@ __device__ __forceinline__ void load_k(const T *p, T (&out)[K])
     }
 }
 
-// One wavefront per (chain, token of the epoch, 32-column slice): the 8 row
-// groups take 8 read references at a time, as in the serial kernel.  All row
-// gathers are issued before any replay so that they are in flight together.
+// One wavefront per (chain, token of the epoch, 32-column slice).  With the
+// read plan, y_t = sum_r w_r row_r + sum_j u_j v_(t_j): the 8 row groups take
+// 8 reads at a time (epoch-start rows, as in the serial kernel), then the
+// token's v pairs 8 at a time.  Every load depends only on the plan, so all
+// of them can be in flight together; reads that overflowed the plan replay
+// their writes from the sorted events.
+#ifndef SDM_TP_PAIR_BATCH
+#define SDM_TP_PAIR_BATCH 4
+#endif
+constexpr int kPairBatch = SDM_TP_PAIR_BATCH;  // v pairs per row group in flight
+
 template <int NR, bool BF16>
 __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int64_t units,
                                                       int nslice)
@@ -282,6 +339,7 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int64_t 
     const int tl = (int)(rest % ne);
     const int64_t chain = rest / ne;
     const int64_t t = t0 + tl;
+    const int64_t ct = chain * a.T + t;
     const int g = lane / kLPR, q = lane % kLPR;
     const int col = slice * 4 * kLPR + q * 4;
     const bool col_ok = col < a.d_v;
@@ -292,14 +350,16 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int64_t 
     const int64_t vrow0 = (b * a.T * a.H + h) * a.d_v + colc;  // v of token 0 of the chain
     const rsrc_t Mr = make_rsrc(a.M + chain * a.N * a.d_v, (uint32_t)(a.N * a.d_v * 4));
     const uint32_t rowb = (uint32_t)a.d_v * 4u;
-    const uint32_t *rc = a.rec + (chain * a.T + t) * a.rec_dwords;
+    const uint32_t *rc = a.rec + ct * a.rec_dwords;
     const TPEntry *se = a.sorted + chain * a.T * a.W + t0 * a.W;
+    const uint2 *pp = a.pairs + ct * a.P;
+    const int np = (int)__builtin_amdgcn_readfirstlane(a.npair[ct]);
 
     uint32_t sl[NR], lk[NR];
-    float qv[NR];
+    float wr[NR];
     load_k<NR>(rc + 3 * a.Wp + g * NR, sl);
-    load_k<NR>(reinterpret_cast<const float *>(rc) + 3 * a.Wp + a.Rp + g * NR, qv);
-    load_k<NR>(a.rlink + (chain * a.T + t) * kMaxK + g * NR, lk);
+    load_k<NR>(a.rwt + ct * kMaxK + g * NR, wr);
+    load_k<NR>(a.rlink + ct * kMaxK + g * NR, lk);
     float4 row[NR];
 #pragma unroll
     for (int i = 0; i < NR; i++) {
@@ -309,7 +369,7 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int64_t 
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int i = 0; i < NR; i++) {
-        // links exist only for the R real references (the rest were never written)
+        // links exist only for the R real references; zero unless the plan overflowed
         const uint32_t l = (g * NR + i < a.R) ? lk[i] : 0u;
         const int first = (int)(l >> 16), cnt = (int)(l & 0xFFFFu);
         float4 rv = row[i];
@@ -318,11 +378,30 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int64_t 
             const float4 vv = load_v<BF16>(a.v, vrow0 + (t0 + (e.tw >> 6)) * hd);
             rv = fma4(e.a, rv, e.c, vv);
         }
-        // masked references have q = 0 and a zero row
-        acc.x = fmaf(qv[i], rv.x, acc.x);
-        acc.y = fmaf(qv[i], rv.y, acc.y);
-        acc.z = fmaf(qv[i], rv.z, acc.z);
-        acc.w = fmaf(qv[i], rv.w, acc.w);
+        // masked references have weight 0 and a zero row
+        acc.x = fmaf(wr[i], rv.x, acc.x);
+        acc.y = fmaf(wr[i], rv.y, acc.y);
+        acc.z = fmaf(wr[i], rv.z, acc.z);
+        acc.w = fmaf(wr[i], rv.w, acc.w);
+    }
+    for (int j0 = 0; j0 < np; j0 += kRPI * kPairBatch) {
+        uint2 pr[kPairBatch];
+        float4 vv[kPairBatch];
+#pragma unroll
+        for (int u = 0; u < kPairBatch; u++) {
+            const int j = j0 + u * kRPI + g;
+            pr[u] = j < np ? pp[j] : make_uint2(0u, 0u);  // weight 0 past the end
+        }
+#pragma unroll
+        for (int u = 0; u < kPairBatch; u++) vv[u] = load_v<BF16>(a.v, vrow0 + (t0 + pr[u].x) * hd);
+#pragma unroll
+        for (int u = 0; u < kPairBatch; u++) {
+            const float wgt = __uint_as_float(pr[u].y);
+            acc.x = fmaf(wgt, vv[u].x, acc.x);
+            acc.y = fmaf(wgt, vv[u].y, acc.y);
+            acc.z = fmaf(wgt, vv[u].z, acc.z);
+            acc.w = fmaf(wgt, vv[u].w, acc.w);
+        }
     }
 #pragma unroll
     for (int m = kLPR; m < 64; m <<= 1) {
@@ -406,17 +485,19 @@ __global__ __launch_bounds__(256) void tp_update_kernel(TPArgs a, int ep, int64_
 
 }  // namespace
 
-#ifndef SDM_TP_EPOCH_LOAD
-#define SDM_TP_EPOCH_LOAD 1
+#ifndef SDM_TP_EPOCH_LOG2
+#define SDM_TP_EPOCH_LOG2 0
 #endif
 
 int tp_epoch_len(const Shape &s)
 {
     // E*W <= 65536 (links hold 16-bit positions), E <= 1024, and
-    // E*W <= SDM_TP_EPOCH_LOAD * N: longer epochs merge more repeated writes
-    // to a slot, but a read then replays more in-epoch writes.
+    // E*W <= 2^SDM_TP_EPOCH_LOG2 * N: longer epochs merge more repeated
+    // writes to a slot, but a read then replays more in-epoch writes.
+    const int64_t cap = SDM_TP_EPOCH_LOG2 >= 0 ? s.N() << SDM_TP_EPOCH_LOG2
+                                               : s.N() >> -SDM_TP_EPOCH_LOG2;
     int64_t e = 1024;
-    while (e > 1 && (e * s.W > 65536 || e * s.W > (int64_t)SDM_TP_EPOCH_LOAD * s.N())) e >>= 1;
+    while (e > 1 && (e * s.W > 65536 || e * s.W > cap)) e >>= 1;
     if (e > s.T) {
         e = 1;
         while (e < s.T) e <<= 1;
@@ -424,16 +505,24 @@ int tp_epoch_len(const Shape &s)
     return (int)e;
 }
 
+// v pairs per token: twice the expected number at the end of an epoch
+// (R reads, each slot written about E*W/N times per epoch)
+static int tp_pair_cap(const Shape &s, int E)
+{
+    const int64_t m = ((int64_t)E * s.W + s.N() - 1) / s.N();
+    const int64_t p = 2 * (int64_t)s.R * (m > 1 ? m : 1);
+    return (int)((p + 7) / 8 * 8);
+}
+
 size_t tp_workspace_bytes(const Shape &s)
 {
     const size_t chains = (size_t)s.B * s.H;
     const size_t ev = chains * (size_t)s.T * s.W;
-    const int E = tp_epoch_len(s);
-    const size_t nep = (size_t)((s.T + E - 1) / E);
+    const size_t toks = chains * (size_t)s.T;
+    const int P = tp_pair_cap(s, tp_epoch_len(s));
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    (void)nep;
-    return up(ev * sizeof(TPEntry)) + 2 * up(ev * 8) + up(ev * 2) +
-           up(chains * (size_t)s.T * kMaxK * 4);
+    return up(ev * sizeof(TPEntry)) + 2 * up(ev * 8) + up(ev * 2) + 2 * up(toks * kMaxK * 4) +
+           up(toks * 4) + up(toks * (size_t)P * 8);
 }
 
 static TPArgs tp_args(const Shape &s, const uint32_t *rec, void *ws, const void *v, float *y,
@@ -455,7 +544,15 @@ static TPArgs tp_args(const Shape &s, const uint32_t *rec, void *ws, const void 
     p += up(ev * 8);
     a.ckey = reinterpret_cast<uint16_t *>(p);
     p += up(ev * 2);
+    const size_t toks = chains * (size_t)s.T;
     a.rlink = reinterpret_cast<uint32_t *>(p);
+    p += up(toks * kMaxK * 4);
+    a.rwt = reinterpret_cast<float *>(p);
+    p += up(toks * kMaxK * 4);
+    a.npair = reinterpret_cast<uint32_t *>(p);
+    p += up(toks * 4);
+    a.pairs = reinterpret_cast<uint2 *>(p);
+    a.P = tp_pair_cap(s, a.E);
     a.rec = rec;
     a.v = v;
     a.y = y;
@@ -482,10 +579,15 @@ bool tp_supported(const Shape &s)
     return s.d_v % 4 == 0 && (double)s.N() * s.d_v * 4.0 <= 2147483648.0;
 }
 
-hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipStream_t st)
+hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipStream_t st,
+                             int ep0, int ep1)
 {
     TPArgs a = tp_args(s, rec, ws, nullptr, nullptr, nullptr);
-    const int64_t blocks = a.chains * a.nepoch;
+    if (ep1 < 0 || ep1 > a.nepoch) ep1 = a.nepoch;
+    if (ep0 >= ep1) return hipSuccess;
+    a.ep0 = ep0;
+    a.nrun = ep1 - ep0;
+    const int64_t blocks = a.chains * a.nrun;
     hipLaunchKernelGGL(tp_sort_kernel, dim3((unsigned)blocks), dim3(kSortThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -499,12 +601,13 @@ hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipS
 }
 
 hipError_t launch_tp_apply(const Shape &s, const uint32_t *rec, void *ws, const void *v,
-                           bool bf16, float *y, float *M, hipStream_t st)
+                           bool bf16, float *y, float *M, hipStream_t st, int ep0, int ep1)
 {
     TPArgs a = tp_args(s, rec, ws, v, y, M);
     const int nslice = (s.d_v + 4 * kLPR - 1) / (4 * kLPR);
     const int nr = (s.R + kRPI - 1) / kRPI;
-    for (int ep = 0; ep < a.nepoch; ep++) {
+    if (ep1 < 0 || ep1 > a.nepoch) ep1 = a.nepoch;
+    for (int ep = ep0; ep < ep1; ep++) {
         const int64_t t0 = (int64_t)ep * a.E;
         const int ne = (int)((s.T - t0) < a.E ? (s.T - t0) : a.E);
         const int64_t runits = a.chains * ne * nslice;

@@ -6,14 +6,31 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <new>
 #include <string>
 
 #include "sdm_internal.h"
 
+namespace {
+constexpr int kMaxDevices = 64;
+constexpr int kMaxChunks = 32;  // pipeline stages of a time-parallel forward
+
+// Per-device helper stream of a handle: the time-parallel forward runs the
+// selection and event sort of the next group of epochs there while the
+// caller's stream applies the current one.  Default priority, non-blocking.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr;
+    hipEvent_t ready[kMaxChunks] = {};
+};
+}  // namespace
+
 struct sdm_ctx {
-    const float *M0;
-    int H, sqrtN, d_v, W, R;
+    const float *M0 = nullptr;
+    int H = 0, sqrtN = 0, d_v = 0, W = 0, R = 0;
+    std::mutex mu;  // guards side[] and the enqueue sequence of a pipelined forward
+    SideStream side[kMaxDevices];
 };
 
 namespace {
@@ -117,6 +134,95 @@ sdm_status check_variant_and_ws(const sdm_ctx *h, int B, int64_t T, sdm_variant 
     return SDM_OK;
 }
 
+// The side stream of the current device, created on first use (caller holds
+// h->mu).  Null if it cannot be created.
+SideStream *side_stream(sdm_ctx *h, hipError_t *err)
+{
+    int dev = -1;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    SideStream &ss = h->side[dev];
+    if (ss.s) return &ss;
+    SideStream n;
+    *err = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking);
+    if (*err == hipSuccess) *err = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
+    for (int c = 0; c < kMaxChunks && *err == hipSuccess; c++)
+        *err = hipEventCreateWithFlags(&n.ready[c], hipEventDisableTiming);
+    if (*err != hipSuccess) {
+        for (hipEvent_t e : n.ready)
+            if (e) (void)hipEventDestroy(e);
+        if (n.fork) (void)hipEventDestroy(n.fork);
+        if (n.s) (void)hipStreamDestroy(n.s);
+        return nullptr;
+    }
+    ss = n;
+    return &ss;
+}
+
+// Time-parallel forward as a two-stream pipeline over groups of epochs.  The
+// selection, sort and links of group c (side stream) need only k', q', alpha,
+// beta; the write/read of group c (caller's stream) waits for them, and for
+// the write/read of group c-1 by stream order.  So the selection of later
+// groups (ALU bound) runs under the write/read of earlier ones (HBM bound).
+// Workspace regions of different groups are disjoint.
+sdm_status forward_pipelined(sdm_ctx *h, const sdm::Shape &s, const void *kp, const void *qp,
+                             const void *v, const float *alpha, const float *beta, bool bf16,
+                             unsigned flags, void *workspace, float *y, float *M, hipStream_t hs)
+{
+    std::lock_guard<std::mutex> lock(h->mu);
+    hipError_t e;
+    SideStream *ss = side_stream(h, &e);
+    if (!ss) return hip_fail(e, "helper stream creation");
+    const int E = sdm::tp_epoch_len(s);
+    const int nep = (int)((s.T + E - 1) / E);
+    // group boundaries 0, 1, 2, 4, 8, ... epochs: the first group (the only
+    // exposed selection) is one epoch; later groups are large enough that
+    // their sort and link launches keep many workgroups busy
+    int bound[kMaxChunks + 1];
+    int C = 0;
+    bound[0] = 0;
+    while (bound[C] < nep && C < kMaxChunks) {
+        const int64_t b = bound[C] == 0 ? 1 : 2 * (int64_t)bound[C];
+        C++;
+        bound[C] = (b < nep && C < kMaxChunks) ? (int)b : nep;
+    }
+    uint32_t *rec = static_cast<uint32_t *>(workspace);
+    char *tp = static_cast<char *>(workspace) + records_bytes(h, s.B, s.T);
+
+    // the side stream starts after everything the caller queued before this call
+    e = hipEventRecord(ss->fork, hs);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->fork, 0);
+    if (e != hipSuccess) return hip_fail(e, "stream fork");
+    if (!(flags & SDM_FLAG_CONTINUE)) {
+        e = sdm::launch_init(s, h->M0, M, hs);
+        if (e != hipSuccess) return hip_fail(e, "init launch");
+    }
+    for (int c = 0; c < C; c++) {
+        const int e0 = bound[c], e1 = bound[c + 1];
+        const int64_t t0 = (int64_t)e0 * E;
+        const int64_t t1 = (int64_t)e1 * E < s.T ? (int64_t)e1 * E : s.T;
+        e = sdm::launch_select(s, kp, qp, bf16, nullptr, nullptr, nullptr, nullptr, rec, alpha,
+                               beta, ss->s, nullptr, t0, t1 - t0);
+        if (e != hipSuccess) return hip_fail(e, "select launch");
+        e = sdm::launch_tp_prepare(s, rec, tp, ss->s, e0, e1);
+        if (e != hipSuccess) return hip_fail(e, "time-parallel sort launch");
+        e = hipEventRecord(ss->ready[c], ss->s);
+        if (e != hipSuccess) return hip_fail(e, "event record");
+    }
+    for (int c = 0; c < C; c++) {
+        const int e0 = bound[c], e1 = bound[c + 1];
+        e = hipStreamWaitEvent(hs, ss->ready[c], 0);
+        if (e != hipSuccess) return hip_fail(e, "stream wait");
+        e = sdm::launch_tp_apply(s, rec, tp, v, bf16, y, M, hs, e0, e1);
+        if (e != hipSuccess) return hip_fail(e, "time-parallel write/read launch");
+    }
+    return SDM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -151,14 +257,34 @@ sdm_status sdm_create(const float *M0, int H, int sqrtN, int d_v, int W, int R, 
         return fail(SDM_ERR_UNSUPPORTED, "sqrtN > %d is not supported", sdm::kMaxSqrtN);
     if (W > sdm::kMaxK || R > sdm::kMaxK)
         return fail(SDM_ERR_UNSUPPORTED, "W, R > %d are not supported", sdm::kMaxK);
-    sdm_ctx *h = new (std::nothrow) sdm_ctx{M0, H, sqrtN, d_v, W, R};
+    sdm_ctx *h = new (std::nothrow) sdm_ctx;
     if (!h) return fail(SDM_ERR_ARG, "out of host memory");
+    h->M0 = M0;
+    h->H = H;
+    h->sqrtN = sqrtN;
+    h->d_v = d_v;
+    h->W = W;
+    h->R = R;
     *out = h;
     return SDM_OK;
 }
 
 sdm_status sdm_destroy(sdm_handle h)
 {
+    if (!h) return SDM_OK;
+    int cur = -1;
+    const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+    for (int d = 0; d < kMaxDevices; d++) {
+        SideStream &ss = h->side[d];
+        if (!ss.s) continue;
+        // work still queued on the stream completes before its resources go
+        (void)hipSetDevice(d);
+        for (hipEvent_t &e : ss.ready)
+            if (e) (void)hipEventDestroy(e);
+        if (ss.fork) (void)hipEventDestroy(ss.fork);
+        (void)hipStreamDestroy(ss.s);
+    }
+    if (have_cur) (void)hipSetDevice(cur);
     delete h;
     return SDM_OK;
 }
@@ -289,6 +415,19 @@ sdm_status sdm_forward(sdm_handle h, int B, int64_t T, const void *kp, const voi
     if (!v || !y) return fail(SDM_ERR_ARG, "null tensor pointer");
     if (!aligned16(v) || !aligned16(y))
         return fail(SDM_ERR_ARG, "tensor pointers must be 16-byte aligned");
+    if (!kp || !qp || !alpha || !beta || !M || !workspace)
+        return fail(SDM_ERR_ARG, "null tensor pointer");
+    if (!aligned16(kp) || !aligned16(qp) || !aligned16(alpha) || !aligned16(beta) ||
+        !aligned16(M) || !aligned16(workspace))
+        return fail(SDM_ERR_ARG, "tensor pointers must be 16-byte aligned");
+    if (flags & ~SDM_FLAG_CONTINUE) return fail(SDM_ERR_ARG, "unknown flags 0x%x", flags);
+    sdm_variant var;
+    st = check_variant_and_ws(h, B, T, variant, ws_bytes, &var);
+    if (st != SDM_OK) return st;
+    const sdm::Shape s = shape_of(h, B, T);
+    if (var == SDM_VARIANT_TIMEPAR && s.T > sdm::tp_epoch_len(s))
+        return forward_pipelined(h, s, kp, qp, v, alpha, beta, dtype == SDM_BF16, flags,
+                                 workspace, y, M, (hipStream_t)stream);
     st = sdm_prepare(h, B, T, kp, qp, alpha, beta, dtype, variant, flags, workspace, ws_bytes, M,
                      stream);
     if (st != SDM_OK) return st;

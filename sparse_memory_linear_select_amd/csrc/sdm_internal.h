@@ -63,7 +63,8 @@ struct Shape {
 hipError_t launch_select(const Shape &s, const void *kp, const void *qp, bool bf16,
                          int32_t *Iw, float *kw, int32_t *Ir, float *qw,
                          uint32_t *rec, const float *alpha, const float *beta,
-                         hipStream_t st, uint32_t *hist = nullptr);
+                         hipStream_t st, uint32_t *hist = nullptr, int64_t t0 = 0,
+                         int64_t tn = -1);  // tokens [t0, t0 + tn) of every sequence
 
 // M[b] <- M0 for every sequence b.
 hipError_t launch_init(const Shape &s, const float *M0, float *M, hipStream_t st);
@@ -86,8 +87,11 @@ hipError_t launch_rw_simple(const Shape &s, const uint32_t *rec, const void *v, 
 bool tp_supported(const Shape &s);
 int tp_epoch_len(const Shape &s);
 size_t tp_workspace_bytes(const Shape &s);  // beyond the token records
-hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipStream_t st);
+// Epochs [ep0, ep1) (ep1 < 0: through the last epoch).
+hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipStream_t st,
+                             int ep0 = 0, int ep1 = -1);
 hipError_t launch_tp_apply(const Shape &s, const uint32_t *rec, void *ws, const void *v,
-                           bool bf16, float *y, float *M, hipStream_t st);
+                           bool bf16, float *y, float *M, hipStream_t st, int ep0 = 0,
+                           int ep1 = -1);
 
 }  // namespace sdm

@@ -174,7 +174,8 @@ struct SelArgs {
     int bf16;
     int64_t T;
     int H, sqrtN, W, R;
-    int64_t n_ht;
+    int64_t n_ht;   // head-tokens in the launch: B * tn * H
+    int64_t t0, tn;  // token range [t0, t0 + tn) of every sequence
     int32_t *Iw, *Ir;
     float *kw, *qw;
     uint32_t *rec;
@@ -217,7 +218,12 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
     const int64_t items = a.lists * a.n_ht;
     for (int64_t it = (int64_t)blockIdx.x * 4 + wv; it < items; it += (int64_t)gridDim.x * 4) {
         const int list = a.lists == 2 ? (int)(it & 1) : 0;
-        const int64_t ht = a.lists == 2 ? it >> 1 : it;
+        int64_t ht = a.lists == 2 ? it >> 1 : it;
+        if (a.tn != a.T) {  // position in the token range -> (b*T + t)*H + h
+            const int64_t per_b = a.tn * a.H;
+            const int64_t bb = ht / per_b;
+            ht += bb * (a.T - a.tn) * a.H + a.t0 * a.H;
+        }
         const int K = list ? a.R : a.W;
         const void *x = list ? a.qp : a.kp;
         const int64_t base = ht * 2 * S;
@@ -347,8 +353,10 @@ hipError_t launch_e(const SelArgs &args, hipStream_t st)
 
 hipError_t launch_select(const Shape &s, const void *kp, const void *qp, bool bf16,
                          int32_t *Iw, float *kw, int32_t *Ir, float *qw, uint32_t *rec,
-                         const float *alpha, const float *beta, hipStream_t st, uint32_t *hist)
+                         const float *alpha, const float *beta, hipStream_t st, uint32_t *hist,
+                         int64_t t0, int64_t tn)
 {
+    if (tn < 0) tn = s.T - t0;
     SelArgs a{};
     a.kp = kp;
     a.qp = qp;
@@ -358,7 +366,9 @@ hipError_t launch_select(const Shape &s, const void *kp, const void *qp, bool bf
     a.sqrtN = s.sqrtN;
     a.W = s.W;
     a.R = s.R;
-    a.n_ht = s.ht();
+    a.t0 = t0;
+    a.tn = tn;
+    a.n_ht = (int64_t)s.B * tn * s.H;
     a.Iw = Iw;
     a.kw = kw;
     a.Ir = Ir;

@@ -185,7 +185,7 @@ def test_runs_are_bitwise_deterministic(variant):
 @pytest.mark.parametrize("variant", VARIANTS, ids=VNAMES)
 def test_continue_flag_splits_a_sequence(variant):
     """Two calls (the second continuing from the first's state) give the same
-    outputs, bit for bit, as one call over the whole sequence."""
+    outputs as one call over the whole sequence."""
     wl, d = _small(27, sqrtN=32, d_v=64, W=16, R=16, T=90)
     core, dd, y, M = gpu_forward(d, wl.W, wl.R, variant)
     k = 37
@@ -196,7 +196,18 @@ def test_continue_flag_splits_a_sequence(variant):
     y2, M2 = core.forward(rest["kp"], rest["qp"], rest["v"], rest["alpha"], rest["beta"],
                           M=M1, cont=True, variant=variant)
     torch.cuda.synchronize()
-    assert torch.equal(torch.cat([y1, y2], 1), y) and torch.equal(M2, M)
+    _same_run(torch.cat([y1, y2], 1), M2, y, M, variant)
+
+
+def _same_run(y1, M1, y, M, variant):
+    """M is bit-exact under any split of the tokens.  So is y with the
+    token-serial schedule; the time-parallel read groups its terms by epoch,
+    so where a split moves the epoch boundaries y agrees to float32 rounding."""
+    assert torch.equal(M1, M)
+    if variant == sdm.SERIAL:
+        assert torch.equal(y1, y)
+    else:
+        assert torch.allclose(y1, y, rtol=1e-5, atol=1e-6)
 
 
 def test_forward_rejects_bad_tensors():
@@ -223,7 +234,9 @@ def test_forward_rejects_bad_tensors():
                                    (4, 129, 2, 16, 32, 16, 8, 0.0)])
 def test_schedules_agree_bitwise_on_state(shape):
     """Both schedules apply the same float32 operations to every row in the
-    same order, so the final state agrees bit for bit; y agrees to rounding."""
+    same order, so the final state agrees bit for bit.  y agrees to float32
+    rounding: the time-parallel read sums epoch-start rows and v rows with
+    composed weights instead of replaying each write."""
     B, T, H, S, D, W, R, reuse = shape
     wl = si.Workload("agree", B=B, T=T, H=H, sqrtN=S, d_v=D, W=W, R=R, dtype="f32",
                      reuse=reuse, seed=40 + T)
@@ -231,13 +244,13 @@ def test_schedules_agree_bitwise_on_state(shape):
     _, _, y1, M1 = gpu_forward(d, W, R, sdm.SERIAL)
     _, _, y2, M2 = gpu_forward(d, W, R, sdm.TIMEPAR)
     assert torch.equal(M1, M2)
-    assert torch.allclose(y1, y2, rtol=1e-6, atol=1e-7)
+    assert torch.allclose(y1, y2, rtol=1e-5, atol=1e-6)
 
 
 @pytest.mark.parametrize("variant", VARIANTS, ids=VNAMES)
 def test_decode_token_by_token(variant):
     """Decoding one token per call (continuing from the previous state) gives
-    the same y and M, bit for bit, as one call over the whole sequence."""
+    the same y and M as one call over the whole sequence."""
     wl, d = _small(30, sqrtN=16, d_v=32, W=8, R=8, T=12, B=2, H=2)
     core, dd, y, M = gpu_forward(d, wl.W, wl.R, variant)
     M1 = torch.empty_like(M)
@@ -248,4 +261,36 @@ def test_decode_token_by_token(variant):
                              M=M1, cont=t > 0, variant=variant)
         ys.append(yt)
     torch.cuda.synchronize()
-    assert torch.equal(torch.cat(ys, 1), y) and torch.equal(M1, M)
+    _same_run(torch.cat(ys, 1), M1, y, M, variant)
+
+
+@pytest.mark.parametrize("shape", [(2, 1285, 2, 16, 32, 8, 8, "f32"),
+                                   (1, 700, 3, 32, 64, 32, 32, "bf16")],
+                         ids=["41-epochs", "22-epochs-bf16"])
+def test_pipelined_forward_matches_staged(shape):
+    """With the time-parallel schedule, sdm_forward runs the selection and
+    sort of later epoch groups on a helper stream under the write/read of
+    earlier ones (groups of 1, 1, 2, 4, ... epochs; 41 epochs end with a
+    partial group).  It must
+    match the oracle and give, bit for bit, what sdm_prepare + sdm_apply give
+    on one stream: from M_0, continuing from a state, and on a side stream."""
+    B, T, H, S, D, W, R, dt = shape
+    wl = si.Workload("pipeline", B=B, T=T, H=H, sqrtN=S, d_v=D, W=W, R=R, dtype=dt, reuse=0.2,
+                     seed=60 + T)
+    d, dd, y, M = _parity(wl, variant=sdm.TIMEPAR)
+    core = make_core(dd, W, R)
+    args = [dd[n] for n in ("kp", "qp", "v", "alpha", "beta")]
+    y2, M2 = core.forward(*args, variant=sdm.TIMEPAR, staged=True)
+    y3, M3 = core.forward(*args, variant=sdm.TIMEPAR, M=M.clone(), cont=True)
+    y4, M4 = core.forward(*args, variant=sdm.TIMEPAR, M=M.clone(), cont=True, staged=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2) and torch.equal(M, M2)
+    assert torch.equal(y3, y4) and torch.equal(M3, M4)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        y5, M5 = core.forward(*args, variant=sdm.TIMEPAR)
+        s5 = (y5.sum(), M5.sum())  # consumed on the same stream right away
+    side.synchronize()
+    assert torch.equal(y5, y) and torch.equal(M5, M)
+    assert s5[0].item() == y.sum().item() and s5[1].item() == M.sum().item()
