@@ -9,9 +9,11 @@
 //   stage 2  candidate pairs (a, b) of per-half ranks with (a+1)(b+1) <= K are
 //            scored with the exact sum x_1 + x_2 (TwoSum pair hi + lo in
 //            float32, compared lexicographically = exact real order) and the
-//            first K in the order (score desc, n = i*sqrtN + j asc) are kept:
-//            each 64-candidate column is sorted across lanes, then columns
-//            are merged pairwise keeping the top 64;
+//            first K in the order (score desc, n = i*sqrtN + j asc) are kept.
+//            The pairs are laid out in five 64-lane columns so that two
+//            arrive sorted and one bitonic (runs along a row or down a
+//            column of ranks are already in order); the other two are sorted
+//            across lanes, and columns are merged pairwise keeping the top 64;
 //   weights  softmax over the K selected scores.
 // The product-key identity (select within each half first, then among sums of
 // survivors) is stated in the explainer "Sparse Delta Memory：通过稀疏性扩展线性
@@ -169,6 +171,56 @@ __device__ __forceinline__ void col_merge(uint64_t &ka, uint32_t &na, uint64_t k
     for (int j = 32; j > 0; j >>= 1) ce_lane(ka, na, j, (lane & j) == 0);
 }
 
+// Sort one 64-entry bitonic column (falling, then rising) in canonical order.
+__device__ __forceinline__ void col_bitonic(uint64_t &k, uint32_t &n, int lane)
+{
+#pragma unroll
+    for (int j = 32; j > 0; j >>= 1) ce_lane(k, n, j, (lane & j) == 0);
+}
+
+// Pair of per-half ranks (a << 8 | b) held by `lane` in candidate column `col`
+// for a list of K, or kNoPair.  The pruned pairs (a+1)(b+1) <= K split into
+// hooks h = min(a, b): row part (h, b >= h) and column part (a > h, h), each
+// already in canonical order (scores fall along a row and down a column,
+// ties keep the lower index first).  Columns:
+//   0  (0, b), b < K                               sorted
+//   1  (a, 0), 1 <= a < K                          sorted
+//   2  hook 1: row part from lane 0 up, column
+//      part from lane 63 down                      bitonic
+//   3, 4  hooks h >= 2, concatenated               unsorted
+constexpr uint16_t kNoPair = 0xFFFF;
+
+__device__ __forceinline__ uint16_t hook_pair(int K, int col, int lane)
+{
+    if (col == 0) return lane < K ? (uint16_t)lane : kNoPair;
+    if (col == 1) return lane + 1 < K ? (uint16_t)((lane + 1) << 8) : kNoPair;
+    if (col == 2) {
+        const int end = K / 2;  // hook 1 spans ranks 1 .. end-1
+        if (lane + 1 < end) return (uint16_t)((1 << 8) | (lane + 1));
+        const int a = 2 + (63 - lane);
+        if (lane > 63 - (end - 2) && a < end) return (uint16_t)((a << 8) | 1);
+        return kNoPair;
+    }
+    int idx = (col - 3) * 64 + lane;
+    for (int h = 2; (h + 1) * (h + 1) <= K; h++) {
+        const int end = K / (h + 1);
+        const int nr = end - h, nc = end - h - 1;
+        if (idx < nr) return (uint16_t)((h << 8) | (h + idx));
+        idx -= nr;
+        if (idx < nc) return (uint16_t)(((h + 1 + idx) << 8) | h);
+        idx -= nc;
+    }
+    return kNoPair;
+}
+
+// Number of pruned pairs with both ranks >= 2 (columns 3 and 4).
+__device__ __forceinline__ int hook_rest(int K)
+{
+    int n = 0;
+    for (int h = 2; (h + 1) * (h + 1) <= K; h++) n += 2 * (K / (h + 1) - h) - 1;
+    return n;
+}
+
 struct SelArgs {
     const void *kp, *qp;
     int bf16;
@@ -196,20 +248,13 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
 
-    // candidate tables: row a holds K/(a+1) pairs (a, 0..K/(a+1)-1)
+    // candidate columns of both lists
     if (wv == 0) {
         for (int list = 0; list < 2; list++) {
             const int K = list ? a.R : a.W;
-            const int len = lane < K ? K / (lane + 1) : 0;
-            int incl = len;  // inclusive prefix sum over lanes
 #pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int t = __shfl_up(incl, o, 64);
-                if (lane >= o) incl += t;
-            }
-            const int off = incl - len;
-            for (int b = 0; b < len; b++) tab[list][off + b] = (uint16_t)((lane << 8) | b);
-            if (lane == 63) tabn[list] = incl;
+            for (int c = 0; c < E2; c++) tab[list][c * 64 + lane] = hook_pair(K, c, lane);
+            if (lane == 0) tabn[list] = hook_rest(K);
         }
     }
     __syncthreads();
@@ -256,17 +301,15 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
         wave_sync();
 
         // ---- stage 2: exact sums of the pruned rank pairs ----
-        const int C = tabn[list];
-        const int e2 = (C + 63) >> 6;
+        const int rest = tabn[list];
         uint64_t ck[E2];
         uint32_t cn[E2];
 #pragma unroll
         for (int r = 0; r < E2; r++) {
-            const int c = r * 64 + lane;
-            ck[r] = 0;
+            ck[r] = 0;  // empty: after every real candidate
             cn[r] = 0xFFFFFFFFu;
-            if (c < C) {
-                const uint32_t ab = tab[list][c];
+            const uint32_t ab = tab[list][r * 64 + lane];
+            if (ab != kNoPair) {
                 const int ra = (int)(ab >> 8), rb = (int)(ab & 0xFF);
                 float hi, lo;
                 two_sum(sv[wv][0][ra], sv[wv][1][rb], hi, lo);
@@ -274,14 +317,19 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
                 cn[r] = si[wv][0][ra] * (uint32_t)S + si[wv][1][rb];
             }
         }
-#pragma unroll
-        for (int r = 0; r < E2; r++)
-            if (r < e2) col_sort(ck[r], cn[r], lane);
-#pragma unroll
-        for (int s = 1; s < E2; s <<= 1) {
-#pragma unroll
-            for (int r = 0; r + s < E2; r += 2 * s)
-                if (r + s < e2) col_merge(ck[r], cn[r], ck[r + s], cn[r + s], lane);
+        // columns 0, 1 sorted; 2 bitonic; 3, 4 unsorted (K-uniform branches)
+        if (K >= 2) col_merge(ck[0], cn[0], ck[1], cn[1], lane);
+        if (K >= 4) {
+            col_bitonic(ck[2], cn[2], lane);
+            col_merge(ck[0], cn[0], ck[2], cn[2], lane);
+        }
+        if (rest > 0) {
+            col_sort(ck[3], cn[3], lane);
+            if (rest > 64) {
+                col_sort(ck[4], cn[4], lane);
+                col_merge(ck[3], cn[3], ck[4], cn[4], lane);
+            }
+            col_merge(ck[0], cn[0], ck[3], cn[3], lane);
         }
         wave_sync();  // sv/si are rewritten by the next item
 
