@@ -63,6 +63,26 @@ def _traffic(wl, schedule):
         return None
 
 
+def d2d_copy_gbs(dev, nbytes=1 << 30, reps=5):
+    """Device-to-device copy rate (read + write bytes / time) of a 1 GiB
+    buffer: the practical streaming ceiling of this GPU's HBM."""
+    import torch
+
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(d, wl, seqs):
     """The float64 oracle on the first `seqs` sequences of the same inputs."""
     import oracle
@@ -237,6 +257,8 @@ def main():
     schedule = sdm.variant_name(core, B, T, dt_code, var)
     traffic = _traffic(wl, schedule)
 
+    copy_gbs = d2d_copy_gbs(dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(d, wl, args.cpu_seqs or wl.B)
@@ -268,7 +290,9 @@ def main():
                      "kernel": SCHEDULES[schedule][1],
                      "timing": "write/read kernels bracketed by HIP events on their stream in "
                                "a second pass of K steps issued as sdm_prepare + sdm_apply",
-                     "algorithmic_bytes": row_bytes},
+                     "algorithmic_bytes": row_bytes,
+                     "d2d_copy_gbs": copy_gbs,
+                     "frac_of_copy": achieved / copy_gbs},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

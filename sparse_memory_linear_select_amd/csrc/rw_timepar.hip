@@ -35,6 +35,10 @@ constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kLPR = 8;               // lanes (x float4) per row: 128-byte row slices
 constexpr int kRPI = 64 / kLPR;       // row groups per wave
 constexpr int kSortThreads = 1024;
+constexpr int kMaxEpoch = 4096;            // tokens per epoch
+constexpr int kMaxEpochEvents = 1 << 18;   // write events per (chain, epoch)
+constexpr int kCntBits = 13;               // replay link: count < 2^13, position < 2^19
+static_assert(kMaxEpoch < (1 << kCntBits), "a slot is written at most once per token");
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
@@ -75,7 +79,7 @@ struct TPArgs {
     TPEntry *sorted;      // [chain][T*W] sorted write events, epoch regions
     uint64_t *tmpA, *tmpB;  // [chain][T*W] radix ping-pong (key << 32 | event)
     uint16_t *ckey;       // [chain][T*W] coarse keys of the sorted events (slot >> kshift)
-    uint32_t *rlink;      // [chain][T][kMaxK] replay links: (first << 16) | count
+    uint32_t *rlink;      // [chain][T][kMaxK] replay links: (first << kCntBits) | count
     float *rwt;           // [chain][T][kMaxK] weight of each read's epoch-start row
     uint32_t *npair;      // [chain][T] pairs in use
     uint2 *pairs;         // [chain][T][P] (token in epoch, weight) of v rows to add
@@ -279,8 +283,8 @@ __global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int str
             w = q * A;
         }
         a.rwt[ct * kMaxK + lane] = w;
-        // j may equal n (= 65536) only when cnt == 0
-        a.rlink[ct * kMaxK + lane] = (cnt > 0 && !fits) ? (((uint32_t)j << 16) | cnt) : 0u;
+        // j < n <= kMaxEpochEvents when cnt > 0
+        a.rlink[ct * kMaxK + lane] = (cnt > 0 && !fits) ? (((uint32_t)j << kCntBits) | cnt) : 0u;
         // the reads that fit are a prefix of the lanes: their pairs are [0, npair)
         const unsigned long long over = __ballot(cnt > 0 && !fits);
         const int first_over = over ? __builtin_ctzll(over) : 63;
@@ -371,7 +375,7 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int64_t 
     for (int i = 0; i < NR; i++) {
         // links exist only for the R real references; zero unless the plan overflowed
         const uint32_t l = (g * NR + i < a.R) ? lk[i] : 0u;
-        const int first = (int)(l >> 16), cnt = (int)(l & 0xFFFFu);
+        const int first = (int)(l >> kCntBits), cnt = (int)(l & ((1u << kCntBits) - 1u));
         float4 rv = row[i];
         for (int k = 0; k < cnt; k++) {  // writes of this slot earlier in the epoch
             const TPEntry e = se[first + k];
@@ -491,13 +495,14 @@ __global__ __launch_bounds__(256) void tp_update_kernel(TPArgs a, int ep, int64_
 
 int tp_epoch_len(const Shape &s)
 {
-    // E*W <= 65536 (links hold 16-bit positions), E <= 1024, and
-    // E*W <= 2^SDM_TP_EPOCH_LOG2 * N: longer epochs merge more repeated
-    // writes to a slot, but a read then replays more in-epoch writes.
+    // E <= kMaxEpoch and E*W <= kMaxEpochEvents (replay links pack an event
+    // position and a count into 32 bits), and E*W <= 2^SDM_TP_EPOCH_LOG2 * N:
+    // longer epochs merge more repeated writes to a slot, but every read
+    // then carries more v pairs from in-epoch writes.
     const int64_t cap = SDM_TP_EPOCH_LOG2 >= 0 ? s.N() << SDM_TP_EPOCH_LOG2
                                                : s.N() >> -SDM_TP_EPOCH_LOG2;
-    int64_t e = 1024;
-    while (e > 1 && (e * s.W > 65536 || e * s.W > cap)) e >>= 1;
+    int64_t e = kMaxEpoch;
+    while (e > 1 && (e * s.W > kMaxEpochEvents || e * s.W > cap)) e >>= 1;
     if (e > s.T) {
         e = 1;
         while (e < s.T) e <<= 1;

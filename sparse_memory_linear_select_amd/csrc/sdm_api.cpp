@@ -14,7 +14,8 @@
 
 namespace {
 constexpr int kMaxDevices = 64;
-constexpr int kMaxChunks = 32;  // pipeline stages of a time-parallel forward
+constexpr int kMaxChunks = 32;       // pipeline stages of a time-parallel forward
+constexpr int kMinSortBlocks = 64;   // workgroups per sort launch in the pipeline
 
 // Per-device helper stream of a handle: the time-parallel forward runs the
 // selection and event sort of the next group of epochs there while the
@@ -163,6 +164,21 @@ SideStream *side_stream(sdm_ctx *h, hipError_t *err)
     return &ss;
 }
 
+// Whether the pipelined forward gets at least four groups of epochs (see
+// forward_pipelined); otherwise the single-stream path is used.  Measured on
+// MI355X, the overlap saves about 3.6% of a step with 16 epochs of 32 chains
+// (groups of 2, 2, 4, 8 epochs) and nothing with fewer groups: the selection
+// running beside the write/read slows it by nearly what it hides.
+bool pipeline_pays(const sdm::Shape &s)
+{
+    const int64_t E = sdm::tp_epoch_len(s);
+    const int64_t nep = (s.T + E - 1) / E;
+    const int64_t chains = (int64_t)s.B * s.H;
+    int64_t g = 1;
+    while (g < nep && chains * g < kMinSortBlocks) g <<= 1;
+    return 8 * g <= nep;
+}
+
 // Time-parallel forward as a two-stream pipeline over groups of epochs.  The
 // selection, sort and links of group c (side stream) need only k', q', alpha,
 // beta; the write/read of group c (caller's stream) waits for them, and for
@@ -179,14 +195,18 @@ sdm_status forward_pipelined(sdm_ctx *h, const sdm::Shape &s, const void *kp, co
     if (!ss) return hip_fail(e, "helper stream creation");
     const int E = sdm::tp_epoch_len(s);
     const int nep = (int)((s.T + E - 1) / E);
-    // group boundaries 0, 1, 2, 4, 8, ... epochs: the first group (the only
-    // exposed selection) is one epoch; later groups are large enough that
-    // their sort and link launches keep many workgroups busy
+    // group boundaries 0, g, 2g, 4g, ... epochs: the first group (the only
+    // exposed selection) is short; g keeps at least kMinSortBlocks workgroups
+    // in each sort and link launch (one per chain and epoch), so that their
+    // latency stays below the write/read of the previous group
+    const int64_t chains = (int64_t)s.B * s.H;
+    int g = 1;
+    while (g < nep && chains * g < kMinSortBlocks) g <<= 1;
     int bound[kMaxChunks + 1];
     int C = 0;
     bound[0] = 0;
     while (bound[C] < nep && C < kMaxChunks) {
-        const int64_t b = bound[C] == 0 ? 1 : 2 * (int64_t)bound[C];
+        const int64_t b = bound[C] == 0 ? g : 2 * (int64_t)bound[C];
         C++;
         bound[C] = (b < nep && C < kMaxChunks) ? (int)b : nep;
     }
@@ -425,7 +445,7 @@ sdm_status sdm_forward(sdm_handle h, int B, int64_t T, const void *kp, const voi
     st = check_variant_and_ws(h, B, T, variant, ws_bytes, &var);
     if (st != SDM_OK) return st;
     const sdm::Shape s = shape_of(h, B, T);
-    if (var == SDM_VARIANT_TIMEPAR && s.T > sdm::tp_epoch_len(s))
+    if (var == SDM_VARIANT_TIMEPAR && pipeline_pays(s))
         return forward_pipelined(h, s, kp, qp, v, alpha, beta, dtype == SDM_BF16, flags,
                                  workspace, y, M, (hipStream_t)stream);
     st = sdm_prepare(h, B, T, kp, qp, alpha, beta, dtype, variant, flags, workspace, ws_bytes, M,
