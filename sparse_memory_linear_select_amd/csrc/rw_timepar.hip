@@ -38,6 +38,7 @@ constexpr int kSortThreads = 1024;
 constexpr int kMaxEpoch = 4096;            // tokens per epoch
 constexpr int kMaxEpochEvents = 1 << 18;   // write events per (chain, epoch)
 constexpr int kCntBits = 13;               // replay link: count < 2^13, position < 2^19
+constexpr uint32_t kReplayFlag = 1u << 31;  // in npair: the token has replay links
 static_assert(kMaxEpoch < (1 << kCntBits), "a slot is written at most once per token");
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
@@ -81,7 +82,7 @@ struct TPArgs {
     uint16_t *ckey;       // [chain][T*W] coarse keys of the sorted events (slot >> kshift)
     uint32_t *rlink;      // [chain][T][kMaxK] replay links: (first << kCntBits) | count
     float *rwt;           // [chain][T][kMaxK] weight of each read's epoch-start row
-    uint32_t *npair;      // [chain][T] pairs in use
+    uint32_t *npair;      // [chain][T] pairs in use (| kReplayFlag: some read replays)
     uint2 *pairs;         // [chain][T][P] (token in epoch, weight) of v rows to add
     int P;                // pair capacity per token
     const void *v;
@@ -290,7 +291,8 @@ __global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int str
         const int first_over = over ? __builtin_ctzll(over) : 63;
         const int off_over = __shfl(off, first_over, 64);
         const int total = __shfl(incl, 63, 64);
-        if (lane == 0) a.npair[ct] = (uint32_t)(over ? off_over : total);
+        // bit 31: some read of this token replays its writes
+        if (lane == 0) a.npair[ct] = over ? ((uint32_t)off_over | kReplayFlag) : (uint32_t)total;
     }
 }
 
@@ -357,36 +359,41 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int64_t 
     const uint32_t *rc = a.rec + ct * a.rec_dwords;
     const TPEntry *se = a.sorted + chain * a.T * a.W + t0 * a.W;
     const uint2 *pp = a.pairs + ct * a.P;
-    const int np = (int)__builtin_amdgcn_readfirstlane(a.npair[ct]);
+    const uint32_t npw = __builtin_amdgcn_readfirstlane(a.npair[ct]);
+    const int np = (int)(npw & ~kReplayFlag);
 
-    uint32_t sl[NR], lk[NR];
+    uint32_t sl[NR];
     float wr[NR];
     load_k<NR>(rc + 3 * a.Wp + g * NR, sl);
     load_k<NR>(a.rwt + ct * kMaxK + g * NR, wr);
-    load_k<NR>(a.rlink + ct * kMaxK + g * NR, lk);
     float4 row[NR];
 #pragma unroll
     for (int i = 0; i < NR; i++) {
         const bool ok = col_ok & (g * NR + i < a.R);
         row[i] = buf_load4(Mr, ok ? (sl[i] & kSlotMask) * rowb + col * 4u : kOff);
     }
+    if (npw & kReplayFlag) {  // rare: reads whose pairs did not fit replay their writes
+        const uint32_t *lkp = a.rlink + ct * kMaxK + g * NR;
+#pragma unroll
+        for (int i = 0; i < NR; i++) {
+            // links exist only for the R real references; zero unless the plan overflowed
+            const uint32_t l = (g * NR + i < a.R) ? lkp[i] : 0u;
+            const int first = (int)(l >> kCntBits), cnt = (int)(l & ((1u << kCntBits) - 1u));
+            for (int k = 0; k < cnt; k++) {  // writes of this slot earlier in the epoch
+                const TPEntry e = se[first + k];
+                const float4 vv = load_v<BF16>(a.v, vrow0 + (t0 + (e.tw >> 6)) * hd);
+                row[i] = fma4(e.a, row[i], e.c, vv);
+            }
+        }
+    }
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int i = 0; i < NR; i++) {
-        // links exist only for the R real references; zero unless the plan overflowed
-        const uint32_t l = (g * NR + i < a.R) ? lk[i] : 0u;
-        const int first = (int)(l >> kCntBits), cnt = (int)(l & ((1u << kCntBits) - 1u));
-        float4 rv = row[i];
-        for (int k = 0; k < cnt; k++) {  // writes of this slot earlier in the epoch
-            const TPEntry e = se[first + k];
-            const float4 vv = load_v<BF16>(a.v, vrow0 + (t0 + (e.tw >> 6)) * hd);
-            rv = fma4(e.a, rv, e.c, vv);
-        }
         // masked references have weight 0 and a zero row
-        acc.x = fmaf(wr[i], rv.x, acc.x);
-        acc.y = fmaf(wr[i], rv.y, acc.y);
-        acc.z = fmaf(wr[i], rv.z, acc.z);
-        acc.w = fmaf(wr[i], rv.w, acc.w);
+        acc.x = fmaf(wr[i], row[i].x, acc.x);
+        acc.y = fmaf(wr[i], row[i].y, acc.y);
+        acc.z = fmaf(wr[i], row[i].z, acc.z);
+        acc.w = fmaf(wr[i], row[i].w, acc.w);
     }
     for (int j0 = 0; j0 < np; j0 += kRPI * kPairBatch) {
         uint2 pr[kPairBatch];
