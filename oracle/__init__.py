@@ -57,8 +57,10 @@ def _load():
             lib.sdm_oracle_recurrence.argtypes = [
                 ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                 ctypes.c_int, ctypes.c_int, p, p, p, p, p, ctypes.c_int, p, p, p,
-                ctypes.c_int, ctypes.c_int, p, p, ctypes.c_int]
+                ctypes.c_int, ctypes.c_int, ctypes.c_int, p, p, ctypes.c_int]
             lib.sdm_oracle_recurrence.restype = ctypes.c_int
+            lib.sdm_oracle_round_bf16.argtypes = [p, p, ctypes.c_int64]
+            lib.sdm_oracle_round_bf16.restype = None
             _lib = lib
     return _lib
 
@@ -107,9 +109,20 @@ def select(x: np.ndarray, sqrtN: int, K: int, threads: int | None = None,
     return (idx, w, hi, lo) if scores else (idx, w)
 
 
+def round_bf16(x) -> np.ndarray:
+    """Nearest bfloat16 values (ties to even) of float64 x, as float64."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    _load().sdm_oracle_round_bf16(_ptr(x), _ptr(out), x.size)
+    return out
+
+
 def recurrence(Iw, kw, Ir, qw, v, alpha, beta, M0, sqrtN: int, c0: int = 0,
-               c1: int | None = None, threads: int | None = None):
-    """Token-serial write/read from a given selection; columns [c0, c1)."""
+               c1: int | None = None, threads: int | None = None, state: str = "f32"):
+    """Token-serial write/read from a given selection; columns [c0, c1).
+    state="bf16" holds the state in bfloat16 (rounded at init and after
+    every write)."""
+    assert state in ("f32", "bf16")
     B, T, H, W = Iw.shape
     R = Ir.shape[-1]
     d_v = v.shape[-1]
@@ -126,18 +139,18 @@ def recurrence(Iw, kw, Ir, qw, v, alpha, beta, M0, sqrtN: int, c0: int = 0,
     M = np.empty((B, H, N, nc), dtype=np.float64)
     rc = _load().sdm_oracle_recurrence(
         B, T, H, sqrtN, d_v, W, R, _ptr(Iw), _ptr(kw), _ptr(Ir), _ptr(qw), _ptr(v),
-        _dtype_code(v), _ptr(alpha), _ptr(beta), _ptr(M0), c0, c1, _ptr(y), _ptr(M),
-        threads or default_threads())
+        _dtype_code(v), _ptr(alpha), _ptr(beta), _ptr(M0), 1 if state == "bf16" else 0, c0, c1,
+        _ptr(y), _ptr(M), threads or default_threads())
     if rc != 0:
         raise ValueError(f"sdm_oracle_recurrence failed ({rc})")
     return y, M
 
 
 def forward(inp: dict, sqrtN: int, W: int, R: int, c0: int = 0, c1: int | None = None,
-            threads: int | None = None) -> dict:
+            threads: int | None = None, state: str = "f32") -> dict:
     """Selection plus recurrence on the inputs of `sdm_inputs.generate`."""
     Iw, kw = select(inp["kp"], sqrtN, W, threads)
     Ir, qw = select(inp["qp"], sqrtN, R, threads)
     y, M = recurrence(Iw, kw, Ir, qw, inp["v"], inp["alpha"], inp["beta"], inp["M0"],
-                      sqrtN, c0, c1, threads)
+                      sqrtN, c0, c1, threads, state)
     return dict(Iw=Iw, kw=kw, Ir=Ir, qw=qw, y=y, M=M)

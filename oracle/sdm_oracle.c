@@ -30,6 +30,14 @@
  *     order, of q^(i) * M[i], taken after the same token's write.
  *  Every sequence starts from the shared initial state M_0 [explainer §3.1,
  *  learned initial state paragraph; Technical Summary, Learned Initial State].
+ *  6. Reduced-precision state (optional).  The engineering notes of the
+ *     explainer suggest storing the state in a narrower type to fit larger
+ *     N; the pages fix no rule.  Reading adopted: the state is held in
+ *     bfloat16 -- M_0 is rounded to bfloat16 at the start, every write
+ *     computes the new row from the stored values and rounds it to
+ *     bfloat16, and reads use the stored values.  Rounding is to nearest,
+ *     ties to even, at bfloat16 precision (8 significant bits, the exponent
+ *     range of float32, subnormal spacing 2^-133).
  *
  * Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off -fPIC -shared.
  * (-ffp-contract=off keeps every product and sum separately rounded, so the
@@ -181,17 +189,39 @@ int sdm_oracle_topk_rows(int64_t nrows, int sqrtN, int K, const void *x, int dty
  * requested column window [c0, c1): init from M_0, then for every token the
  * gated delta write of the W selected rows followed by the sparse read.
  */
+/* Nearest bfloat16 value of x, ties to even: x is rounded to a multiple of
+   the bfloat16 spacing at its magnitude, 2^(e-8) for |x| in [2^(e-1), 2^e),
+   never finer than the subnormal spacing 2^-133.  nearbyint rounds half to
+   even in the default rounding mode. */
+static double round_bf16(double x)
+{
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    (void)frexp(x, &e);
+    int q = e - 8;
+    if (q < -133) q = -133;
+    return ldexp(nearbyint(ldexp(x, -q)), q);
+}
+
+/* Element-wise round_bf16 (exported for the tests). */
+void sdm_oracle_round_bf16(const double *x, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = round_bf16(x[i]);
+}
+
 static void run_chain(int64_t T, int H, int64_t N, int d_v, int W, int R, int b, int h,
                       const int32_t *Iw, const double *kw, const int32_t *Ir,
                       const double *qw, const void *v, int v_dtype, const float *alpha,
-                      const float *beta, const float *M0, int c0, int c1, int ca, int cb,
-                      double *y, double *M)
+                      const float *beta, const float *M0, int state_bf16, int c0, int c1,
+                      int ca, int cb, double *y, double *M)
 {
     const int nc = c1 - c0;
     double *Mc = M + ((int64_t)b * H + h) * N * nc; /* this chain's [N][nc] */
     for (int64_t n = 0; n < N; n++)
-        for (int c = ca; c < cb; c++)
-            Mc[n * nc + (c - c0)] = (double)M0[((int64_t)h * N + n) * d_v + c];
+        for (int c = ca; c < cb; c++) {
+            const double m0 = (double)M0[((int64_t)h * N + n) * d_v + c];
+            Mc[n * nc + (c - c0)] = state_bf16 ? round_bf16(m0) : m0;
+        }
 
     for (int64_t t = 0; t < T; t++) {
         const int64_t ht = ((int64_t)b * T + t) * H + h; /* head-token index */
@@ -206,6 +236,7 @@ static void run_chain(int64_t T, int H, int64_t N, int d_v, int W, int R, int b,
                 double *row = &Mc[s * nc + (c - c0)];
                 const double m = a_t * (*row);     /* forget gate */
                 *row = m + b_t * k * (vt - m);     /* delta + input gate */
+                if (state_bf16) *row = round_bf16(*row);
             }
         }
         /* read: on the state after this token's write */
@@ -225,6 +256,7 @@ static void run_chain(int64_t T, int H, int64_t N, int d_v, int W, int R, int b,
  *   Iw,kw [B][T][H][W], Ir,qw [B][T][H][R]   selection (from the oracle)
  *   v [B][T][H][d_v] (float32 or bf16 bits), alpha,beta [B][T][H] float32
  *   M0 [H][N][d_v] float32
+ *   state_bf16: 0 = float64 state, 1 = state held in bfloat16 (item 6 above)
  * Only the columns [c0, c1) of y and M are produced (columns of the state
  * never interact):  y [B][T][H][c1-c0], M [B][H][N][c1-c0], both float64.
  * Returns 0, or -1 on bad arguments.
@@ -232,8 +264,8 @@ static void run_chain(int64_t T, int H, int64_t N, int d_v, int W, int R, int b,
 int sdm_oracle_recurrence(int B, int64_t T, int H, int sqrtN, int d_v, int W, int R,
                           const int32_t *Iw, const double *kw, const int32_t *Ir,
                           const double *qw, const void *v, int v_dtype, const float *alpha,
-                          const float *beta, const float *M0, int c0, int c1, double *y,
-                          double *M, int nthreads)
+                          const float *beta, const float *M0, int state_bf16, int c0, int c1,
+                          double *y, double *M, int nthreads)
 {
     if (B < 1 || T < 0 || H < 1 || sqrtN < 1 || d_v < 1 || W < 1 || R < 1) return -1;
     if (W > sqrtN || R > sqrtN || c0 < 0 || c1 > d_v || c0 >= c1) return -1;
@@ -253,7 +285,7 @@ int sdm_oracle_recurrence(int B, int64_t T, int H, int sqrtN, int d_v, int W, in
         const int ca = c0 + blk * CB;
         const int cb = ca + CB < c1 ? ca + CB : c1;
         run_chain(T, H, N, d_v, W, R, b, h, Iw, kw, Ir, qw, v, v_dtype, alpha, beta, M0,
-                  c0, c1, ca, cb, y, M);
+                  state_bf16, c0, c1, ca, cb, y, M);
     }
     return 0;
 }

@@ -283,3 +283,86 @@ def test_state_size_equation(cfg, d_model):
     assert dqk % (2 * wl.H) == 0
     assert wl.sqrtN == dqk // (2 * wl.H) and wl.d_v == dv // wl.H
     assert dqk * dqk * dv // (4 * wl.H * wl.H) == wl.H * wl.N * wl.d_v
+
+
+# ------------------------------------------------------ bfloat16 state (reading)
+
+def test_round_bf16_matches_torch_conversion():
+    """The oracle's bfloat16 rounding (nearest, ties to even) agrees with
+    torch's float32 -> bfloat16 conversion on float32 inputs: random values
+    over many binades, exact halfway cases with even and odd neighbours,
+    subnormals and signed zeros."""
+    import torch
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal(20000) * np.exp2(rng.integers(-40, 40, 20000))).astype(np.float32)
+    bits = rng.integers(0, 2**31 - 1, 4000, dtype=np.int64).astype(np.uint32)
+    ties = ((bits & 0xFFFF0000) | 0x8000).view(np.float32)              # exactly halfway
+    sub = (rng.integers(1, 2**23, 2000, dtype=np.int64).astype(np.uint32)).view(np.float32)
+    special = np.array([0.0, -0.0, 1.0, -1.0, 1.00390625, 3.0078125, 0.1, 65504.0], np.float32)
+    for arr in (x, ties[np.isfinite(ties)], sub, -sub, special):
+        want = torch.from_numpy(arr.copy()).to(torch.bfloat16).to(torch.float64).numpy()
+        got = oracle.round_bf16(arr.astype(np.float64))
+        np.testing.assert_array_equal(got, want)
+
+
+def test_golden_recurrence_bf16_state(golden):
+    (c,) = golden("recurrence_bf16_state.txt")
+    S, D, T = int(c["sqrtN"][0]), int(c["d_v"][0]), int(c["T"][0])
+    inp = dict(
+        kp=np.array(c["kp"], np.float32).reshape(1, T, 1, 2 * S),
+        qp=np.array(c["qp"], np.float32).reshape(1, T, 1, 2 * S),
+        v=np.array(c["v"], np.float32).reshape(1, T, 1, D),
+        alpha=np.array(c["alpha"], np.float32).reshape(1, T, 1),
+        beta=np.array(c["beta"], np.float32).reshape(1, T, 1),
+        M0=np.array(c["M0"], np.float32).reshape(1, S * S, D))
+    o = oracle.forward(inp, S, 1, 1, state="bf16")
+    np.testing.assert_array_equal(o["y"].reshape(-1), c["y"])
+    np.testing.assert_array_equal(o["M"].reshape(-1), c["M"])
+    # the float64 state keeps the low bits the bfloat16 state drops
+    o64 = oracle.forward(inp, S, 1, 1)
+    assert o64["y"].reshape(-1)[0] != c["y"][0]
+
+
+def test_bf16_state_unwritten_rows_are_rounded_m0():
+    wl, d = _tiny(seed=31, S=8)
+    d["kp"][..., :wl.sqrtN] = -8.0
+    d["kp"][..., :2] = 8.0
+    o = oracle.forward(d, wl.sqrtN, wl.W, wl.R, state="bf16")
+    for b in range(wl.B):
+        for h in range(wl.H):
+            never = np.setdiff1d(np.arange(wl.N), np.unique(o["Iw"][b, :, h]))
+            assert never.size > 0
+            np.testing.assert_array_equal(o["M"][b, h, never],
+                                          oracle.round_bf16(d["M0"][h, never].astype(np.float64)))
+
+
+def test_bf16_state_overwrite_gate():
+    """alpha = beta = 1 with W = 1 (weight 1): the written row becomes
+    bfloat16(v_t) exactly."""
+    wl, d = _tiny(seed=32, W=1, R=1)
+    d["alpha"][:] = 1.0
+    d["beta"][:] = 1.0
+    o = oracle.forward(d, wl.sqrtN, 1, 1, state="bf16")
+    for b in range(wl.B):
+        for h in range(wl.H):
+            last = {}
+            for t in range(wl.T):
+                last[int(o["Iw"][b, t, h, 0])] = t
+            for s, t in last.items():
+                np.testing.assert_array_equal(
+                    o["M"][b, h, s], oracle.round_bf16(d["v"][b, t, h].astype(np.float64)))
+
+
+def test_bf16_state_error_bound():
+    """Each stored value carries at most half a bfloat16 spacing (2^-9
+    relative) of fresh rounding, and writes are contractions, so the
+    bfloat16-state result stays within (writes + 1) * 2^-8 * max|M| of the
+    float64-state result (a loose bound: 2^-8 covers the rounding of M_0)."""
+    wl, d = _tiny(seed=33, T=40, S=6, W=3, R=3)
+    o16 = oracle.forward(d, wl.sqrtN, wl.W, wl.R, state="bf16")
+    o64 = oracle.forward(d, wl.sqrtN, wl.W, wl.R)
+    scale = max(np.abs(o64["M"]).max(), np.abs(d["v"]).max())
+    writes = wl.T  # at most one write per token per slot
+    assert np.abs(o16["M"] - o64["M"]).max() <= (writes + 1) * 2.0**-8 * scale
+    assert np.abs(o16["y"] - o64["y"]).max() <= (writes + 1) * 2.0**-8 * scale
+    assert np.abs(o16["M"] - o64["M"]).max() > 0  # the rounding is really applied
