@@ -43,12 +43,14 @@ SCHEDULES = {  # schedule -> (kernel source, kernels of the write/read phase)
 }
 
 
-def _traffic(wl, schedule):
+def _traffic(wl, schedule, state="f32"):
     """Counter-measured HBM bytes of the write/read phase per step, if a
-    committed summary exists for this workload and schedule and the kernel
-    source is unchanged since the counters were taken; else None."""
+    committed summary exists for this workload, schedule and state type and
+    the kernel source is unchanged since the counters were taken; else None."""
     src_name = SCHEDULES[schedule][0]
     tag = schedule.replace("-", "_") + "__" + wl.name.replace(" ", "_")
+    if state != "f32":
+        tag += f"__{state}_state"
     path = os.path.join(ROOT, "profiles", f"traffic_{tag}.json")
     if not os.path.exists(path):
         return None
@@ -83,14 +85,14 @@ def d2d_copy_gbs(dev, nbytes=1 << 30, reps=5):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(d, wl, seqs):
+def cpu_baseline(d, wl, seqs, state="f32"):
     """The float64 oracle on the first `seqs` sequences of the same inputs."""
     import oracle
 
     sub = {k: (v[:seqs] if k not in ("M0",) else v) for k, v in d.items() if k != "src"}
     cores = oracle.default_threads()
     t = time.perf_counter()
-    oracle.forward(sub, wl.sqrtN, wl.W, wl.R, threads=cores)
+    oracle.forward(sub, wl.sqrtN, wl.W, wl.R, threads=cores, state=state)
     dt = time.perf_counter() - t
     ht = seqs * wl.T * wl.H
     return {"value": ht / dt, "unit": "head-tokens/s", "cores": cores, "kind": "oracle",
@@ -157,6 +159,8 @@ def main():
                     help="sequences in the CPU-baseline sample (default: all)")
     ap.add_argument("--variant", choices=["auto", "serial", "timepar"], default="auto",
                     help="write/read schedule (default: the library's choice)")
+    ap.add_argument("--state", choices=["f32", "bf16"], default="f32",
+                    help="element type of the state M (bf16: reduced-precision state)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode", action="store_true",
                     help="measure one-token decode steps (continuing the state) instead")
@@ -192,10 +196,12 @@ def main():
         return torch.from_numpy(x).to(dev)
 
     dd = {k: up(v) for k, v in d.items() if k != "src"}
-    core = sdm.SDM(dd["M0"], wl.W, wl.R)
+    state = torch.bfloat16 if args.state == "bf16" else torch.float32
+    esz = 2 if args.state == "bf16" else 4  # bytes per state element
+    core = sdm.SDM(dd["M0"], wl.W, wl.R, state=state)
     B, T, H = wl.B, wl.T, wl.H
     y = torch.empty((B, T, H, wl.d_v), dtype=torch.float32, device=dev)
-    M = torch.empty((B, H, wl.N, wl.d_v), dtype=torch.float32, device=dev)
+    M = torch.empty((B, H, wl.N, wl.d_v), dtype=state, device=dev)
     dt_code = sdm.BF16 if wl.dtype == "bf16" else sdm.F32
     var = {"auto": sdm.AUTO, "serial": sdm.SERIAL, "timepar": sdm.TIMEPAR}[args.variant]
     ws_n = core.workspace_size(B, T, dt_code, var)
@@ -252,16 +258,16 @@ def main():
     rw_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
     prep_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
     ht = wl.head_tokens
-    row_bytes = ht * (2 * wl.W + wl.R) * wl.d_v * 4  # algorithmic row traffic per step
+    row_bytes = ht * (2 * wl.W + wl.R) * wl.d_v * esz  # algorithmic row traffic per step
     achieved = row_bytes / (rw_ms * 1e-3) / 1e9
     schedule = sdm.variant_name(core, B, T, dt_code, var)
-    traffic = _traffic(wl, schedule)
+    traffic = _traffic(wl, schedule, args.state)
 
     copy_gbs = d2d_copy_gbs(dev)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(d, wl, args.cpu_seqs or wl.B)
+        cpu = cpu_baseline(d, wl, args.cpu_seqs or wl.B, args.state)
 
     out = {
         "metric": METRIC,
@@ -274,11 +280,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if wl.dtype == "f32" else "bf16 inputs, f32 state",
+        "dtype": {("f32", "f32"): "f32", ("bf16", "f32"): "bf16 inputs, f32 state",
+                  ("f32", "bf16"): "f32 compute, bf16 state",
+                  ("bf16", "bf16"): "bf16 inputs, f32 compute, bf16 state"}[(wl.dtype, args.state)],
         "data": "synthetic (seeded; recipe in sdm_inputs.py)",
         "config": {"workload": wl.name, "B": B, "T": T, "H": H, "sqrtN": wl.sqrtN, "N": wl.N,
                    "d_v": wl.d_v, "W": wl.W, "R": wl.R, "inputs": wl.dtype,
-                   "schedule": schedule},
+                   "state": args.state, "schedule": schedule},
         "row_gbs_whole_step": row_bytes / (ms_step * 1e-3) / 1e9,
         "breakdown_ms": {"staged step (prepare + apply, one stream)": staged_ms,
                          "prepare (init+select+plan/sort)": prep_ms, "write+read": rw_ms},

@@ -103,6 +103,27 @@ sdm_status sdm_create(const float *M0, int H, int sqrtN, int d_v, int W, int R,
                       sdm_handle *out);
 
 /*
+ * As sdm_create, with the element type of the state M that the calls below
+ * read and write:
+ *   SDM_F32   float32 (what sdm_create gives);
+ *   SDM_BF16  bfloat16, a reduced-precision state (the explainer "Sparse
+ *             Delta Memory：通过稀疏性扩展线性 RNN 的状态容量" suggests a narrower
+ *             state type to fit larger N in its engineering notes; the pages
+ *             fix no rounding rule).  M_0 stays float32 and is rounded to
+ *             bfloat16 (nearest, ties to even) when M is initialised; every
+ *             write computes a*row + c*v in float32 from the stored row and
+ *             stores it rounded the same way; reads use the stored rows and
+ *             accumulate y in float32.  Halves the row traffic.  Needs the
+ *             time-parallel schedule (d_v % 4 == 0): SDM_VARIANT_SERIAL
+ *             returns SDM_ERR_UNSUPPORTED.  Reads that see a write of the
+ *             same epoch use the unrounded composition of those writes (one
+ *             bfloat16 rounding of the row, at most, differs).
+ * Errors as sdm_create, plus SDM_ERR_ARG for another state_dtype.
+ */
+sdm_status sdm_create_ex(const float *M0, int H, int sqrtN, int d_v, int W, int R,
+                         sdm_dtype state_dtype, sdm_handle *out);
+
+/*
  * Release a handle (M_0 is not touched) and the helper streams sdm_forward
  * created for it; work already queued on them still completes.  NULL is
  * accepted.
@@ -138,7 +159,8 @@ sdm_status sdm_select(sdm_handle h, int B, int64_t T, const void *kp, const void
  *   workspace  device scratch of ws_bytes >= sdm_workspace_size(...) bytes,
  *              16-byte aligned; its contents are undefined afterwards.
  *   y          device [B][T][H][d_v] float32, output.
- *   M          device [B][H][N][d_v] float32: the final state on return.
+ *   M          device [B][H][N][d_v], float32 or bfloat16 as the handle's
+ *              state type (sdm_create_ex): the final state on return.
  *              Unless SDM_FLAG_CONTINUE is set it is first overwritten with
  *              M_0 (so a failed call can simply be retried); with the flag it
  *              must hold the state to continue from.
@@ -158,7 +180,7 @@ sdm_status sdm_select(sdm_handle h, int B, int64_t T, const void *kp, const void
 sdm_status sdm_forward(sdm_handle h, int B, int64_t T, const void *kp, const void *qp,
                        const void *v, const float *alpha, const float *beta,
                        sdm_dtype dtype, sdm_variant variant, unsigned flags,
-                       void *workspace, size_t ws_bytes, float *y, float *M,
+                       void *workspace, size_t ws_bytes, float *y, void *M,
                        void *stream);
 
 /*
@@ -180,11 +202,11 @@ sdm_status sdm_forward(sdm_handle h, int B, int64_t T, const void *kp, const voi
 sdm_status sdm_prepare(sdm_handle h, int B, int64_t T, const void *kp, const void *qp,
                        const float *alpha, const float *beta, sdm_dtype dtype,
                        sdm_variant variant, unsigned flags, void *workspace,
-                       size_t ws_bytes, float *M, void *stream);
+                       size_t ws_bytes, void *M, void *stream);
 
 sdm_status sdm_apply(sdm_handle h, int B, int64_t T, const void *v, sdm_dtype dtype,
                      sdm_variant variant, void *workspace, size_t ws_bytes, float *y,
-                     float *M, void *stream);
+                     void *M, void *stream);
 
 /*
  * Write-slot utilisation (an addressing-collapse monitor; the explainer's

@@ -33,7 +33,7 @@ STATUS = {0: "SDM_OK", 1: "SDM_ERR_ARG", 2: "SDM_ERR_UNSUPPORTED", 3: "SDM_ERR_W
           4: "SDM_ERR_HIP"}
 
 # every function include/sdm.h declares
-EXPORTS = ("sdm_create", "sdm_destroy", "sdm_workspace_size", "sdm_select", "sdm_forward",
+EXPORTS = ("sdm_create", "sdm_create_ex", "sdm_destroy", "sdm_workspace_size", "sdm_select", "sdm_forward",
            "sdm_prepare", "sdm_apply", "sdm_write_histogram", "sdm_status_string",
            "sdm_last_error")
 
@@ -58,6 +58,7 @@ def lib():
         L = ctypes.CDLL(_LIB_PATH)
         p, i, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
         L.sdm_create.argtypes = [p, i, i, i, i, i, ctypes.POINTER(p)]
+        L.sdm_create_ex.argtypes = [p, i, i, i, i, i, i, ctypes.POINTER(p)]
         L.sdm_destroy.argtypes = [p]
         L.sdm_workspace_size.argtypes = [p, i, i64, i, i, ctypes.POINTER(sz)]
         L.sdm_select.argtypes = [p, i, i64, p, p, i, p, p, p, p, p]
@@ -65,7 +66,7 @@ def lib():
         L.sdm_prepare.argtypes = [p, i, i64, p, p, p, p, i, i, ctypes.c_uint, p, sz, p, p]
         L.sdm_apply.argtypes = [p, i, i64, p, i, i, p, sz, p, p, p]
         L.sdm_write_histogram.argtypes = [p, i, i64, p, i, p, p]
-        for f in ("sdm_create", "sdm_destroy", "sdm_workspace_size", "sdm_select", "sdm_forward",
+        for f in ("sdm_create", "sdm_create_ex", "sdm_destroy", "sdm_workspace_size", "sdm_select", "sdm_forward",
                   "sdm_prepare", "sdm_apply", "sdm_write_histogram"):
             getattr(L, f).restype = ctypes.c_int
         L.sdm_status_string.argtypes = [i]
@@ -80,7 +81,7 @@ def variant_name(core, B, T, dtype, variant) -> str:
     """Name of the schedule a call would use ("token-serial" or "time-parallel")."""
     if variant == SERIAL:
         return "token-serial"
-    if variant == TIMEPAR:
+    if variant == TIMEPAR or core.state == torch.bfloat16:
         return "time-parallel"
     n_auto = core.workspace_size(B, T, dtype, AUTO)
     return "time-parallel" if n_auto == core.workspace_size(B, T, dtype, TIMEPAR) and \
@@ -119,20 +120,27 @@ def _in_dtype(t: torch.Tensor) -> int:
 
 
 class SDM:
-    """One SDM layer shape bound to its shared initial state M_0 (borrowed)."""
+    """One SDM layer shape bound to its shared initial state M_0 (borrowed).
 
-    def __init__(self, M0: torch.Tensor, W: int, R: int):
+    state: element type of the state M (torch.float32, or torch.bfloat16 for
+    the reduced-precision state, which needs the time-parallel schedule).
+    """
+
+    def __init__(self, M0: torch.Tensor, W: int, R: int, state: torch.dtype = torch.float32):
         _dev_tensor(M0, "M0", torch.float32)
         if M0.dim() != 3:
             raise SDMError(1, "M0 must be [H, N, d_v]")
+        if state not in (torch.float32, torch.bfloat16):
+            raise SDMError(1, f"state must be torch.float32 or torch.bfloat16, got {state}")
         H, N, d_v = M0.shape
         sqrtN = math.isqrt(N)
         if sqrtN * sqrtN != N:
             raise SDMError(1, f"N = {N} is not a perfect square")
         self.M0, self.H, self.sqrtN, self.N, self.d_v = M0, H, sqrtN, N, d_v
-        self.W, self.R = int(W), int(R)
+        self.W, self.R, self.state = int(W), int(R), state
         h = ctypes.c_void_p()
-        _check(lib().sdm_create(_ptr(M0), H, sqrtN, d_v, self.W, self.R, ctypes.byref(h)))
+        _check(lib().sdm_create_ex(_ptr(M0), H, sqrtN, d_v, self.W, self.R,
+                                   BF16 if state == torch.bfloat16 else F32, ctypes.byref(h)))
         self._h = h
 
     def close(self):
@@ -215,9 +223,9 @@ class SDM:
         if M is None:
             if cont:
                 raise SDMError(1, "cont=True needs the state M")
-            M = torch.empty((B, self.H, self.N, self.d_v), dtype=torch.float32, device=dev)
+            M = torch.empty((B, self.H, self.N, self.d_v), dtype=self.state, device=dev)
         _dev_tensor(y, "y", torch.float32)
-        _dev_tensor(M, "M", torch.float32)
+        _dev_tensor(M, "M", self.state)
         if tuple(M.shape) != (B, self.H, self.N, self.d_v) or tuple(y.shape) != tuple(v.shape):
             raise SDMError(1, "y or M has the wrong shape")
         need = self.workspace_size(B, T, dt, variant)

@@ -2,7 +2,8 @@
 // (explainer "Sparse Delta Memory：通过稀疏性扩展线性 RNN 的状态容量", §3.1,
 // learned initial state; "Technical Summary: Sparse Delta Memory (SDM)",
 // Learned Initial State).  Streaming copy: each float4 of M_0 is read once
-// and written B times.
+// and written B times.  A bfloat16 state receives M_0 rounded to nearest,
+// ties to even.
 #include "sdm_internal.h"
 
 namespace sdm {
@@ -36,14 +37,43 @@ __global__ __launch_bounds__(256) void init_kernel_scalar(const float *__restric
     }
 }
 
+__device__ __forceinline__ uint32_t bf16_bits(float f)  // nearest, ties to even (finite f)
+{
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// bfloat16 state: n is a multiple of 4 (d_v % 4 == 0), so every 4 values of
+// a sequence's slab are 8-byte aligned.
+__global__ __launch_bounds__(256) void init_kernel_bf16(const float *__restrict__ M0,
+                                                        uint2 *__restrict__ M, int64_t n, int B)
+{
+    const int64_t n4 = n >> 2;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const float4 *src = reinterpret_cast<const float4 *>(M0);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        const float4 x = src[i];
+        const uint2 u = make_uint2(bf16_bits(x.x) | (bf16_bits(x.y) << 16),
+                                   bf16_bits(x.z) | (bf16_bits(x.w) << 16));
+        for (int b = 0; b < B; b++) M[(int64_t)b * n4 + i] = u;
+    }
+}
+
 }  // namespace
 
-hipError_t launch_init(const Shape &s, const float *M0, float *M, hipStream_t st)
+hipError_t launch_init(const Shape &s, const float *M0, void *Mv, bool state_bf16, hipStream_t st)
 {
-    const int64_t n = (int64_t)s.H * s.N() * s.d_v;  // floats per sequence
+    const int64_t n = (int64_t)s.H * s.N() * s.d_v;  // values per sequence
     int64_t blocks = (n / 4 + 255) / 256;
     if (blocks > 8192) blocks = 8192;
     if (blocks < 1) blocks = 1;
+    if (state_bf16) {
+        if (n & 3) return hipErrorInvalidValue;  // callers check d_v % 4 == 0
+        hipLaunchKernelGGL(init_kernel_bf16, dim3((unsigned)blocks), dim3(256), 0, st, M0,
+                           static_cast<uint2 *>(Mv), n, s.B);
+        return hipGetLastError();
+    }
+    float *M = static_cast<float *>(Mv);
     if ((n & 3) == 0)
         hipLaunchKernelGGL(init_kernel, dim3((unsigned)blocks), dim3(256), 0, st, M0, M, n, s.B);
     else

@@ -32,8 +32,6 @@ namespace {
 using rsrc_t = __amdgpu_buffer_rsrc_t;
 constexpr uint32_t kOff = 0x80000000u;
 constexpr int kRsrcWord3 = 0x00020000;
-constexpr int kLPR = 8;               // lanes (x float4) per row: 128-byte row slices
-constexpr int kRPI = 64 / kLPR;       // row groups per wave
 constexpr int kSortThreads = 1024;
 constexpr int kMaxEpoch = 4096;            // tokens per epoch
 constexpr int kMaxEpochEvents = 1 << 18;   // write events per (chain, epoch)
@@ -63,6 +61,66 @@ __device__ __forceinline__ float4 fma4(float a, float4 x, float c, float4 v)
                        fmaf(a, x.w, c * v.w));
 }
 
+// Nearest bfloat16 (ties to even) of a finite float, as its 16 bits.
+__device__ __forceinline__ uint32_t bf16_bits(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Row storage of the state.  Every lane holds 4 columns of a row; a row
+// slice is the 128 bytes that LPR lanes cover (the fabric's request size).
+//   float32 state: 8 lanes x 16 bytes;
+//   bfloat16 state: 16 lanes x 8 bytes, widened exactly on load, rounded to
+//   nearest-even after every write (the value the state holds).
+template <bool SB>
+struct StateRow;
+
+template <>
+struct StateRow<false> {
+    static constexpr int kLPR = 8;
+    static constexpr uint32_t kElem = 4;
+    using Raw = float4;
+    static __device__ __forceinline__ Raw load_raw(rsrc_t r, uint32_t off) { return buf_load4(r, off); }
+    static __device__ __forceinline__ float4 widen(Raw x) { return x; }
+    static __device__ __forceinline__ float4 load(rsrc_t r, uint32_t off) { return buf_load4(r, off); }
+    static __device__ __forceinline__ void store(float4 v, rsrc_t r, uint32_t off)
+    {
+        buf_store4(v, r, off);
+    }
+    static __device__ __forceinline__ float4 round(float4 v) { return v; }
+};
+
+template <>
+struct StateRow<true> {
+    static constexpr int kLPR = 16;
+    static constexpr uint32_t kElem = 2;
+    using Raw = uint2;  // 4 bfloat16 values
+    static __device__ __forceinline__ Raw load_raw(rsrc_t r, uint32_t off)
+    {
+        const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+        return make_uint2(u[0], u[1]);
+    }
+    static __device__ __forceinline__ float4 widen(Raw u)
+    {
+        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+    }
+    static __device__ __forceinline__ float4 load(rsrc_t r, uint32_t off) { return widen(load_raw(r, off)); }
+    static __device__ __forceinline__ void store(float4 v, rsrc_t r, uint32_t off)
+    {
+        __attribute__((ext_vector_type(2))) unsigned u;
+        u[0] = bf16_bits(v.x) | (bf16_bits(v.y) << 16);
+        u[1] = bf16_bits(v.z) | (bf16_bits(v.w) << 16);
+        __builtin_amdgcn_raw_buffer_store_b64(u, r, (int)off, 0, 0);
+    }
+    static __device__ __forceinline__ float4 round(float4 v)
+    {
+        return make_float4(__uint_as_float(bf16_bits(v.x) << 16), __uint_as_float(bf16_bits(v.y) << 16),
+                           __uint_as_float(bf16_bits(v.z) << 16), __uint_as_float(bf16_bits(v.w) << 16));
+    }
+};
+
 template <bool BF16>
 __device__ __forceinline__ float4 load_v(const void *v, int64_t off)
 {
@@ -86,7 +144,8 @@ struct TPArgs {
     uint2 *pairs;         // [chain][T][P] (token in epoch, weight) of v rows to add
     int P;                // pair capacity per token
     const void *v;
-    float *y, *M;
+    float *y;
+    void *M;  // float32 or bfloat16 state
     int64_t T, N;
     int H, d_v, W, R, Wp, Rp, rec_dwords;
     int E, nepoch, passes, kshift;
@@ -331,10 +390,12 @@ __device__ __forceinline__ void load_k(const T *p, T (&out)[K])
 #endif
 constexpr int kPairBatch = SDM_TP_PAIR_BATCH;  // v pairs per row group in flight
 
-template <int NR, bool BF16>
+template <int NR, bool BF16, bool SB>
 __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int64_t units,
                                                       int nslice)
 {
+    using S = StateRow<SB>;
+    constexpr int kLPR = S::kLPR, kRPI = 64 / kLPR;
     const int lane = threadIdx.x & 63;
     const int64_t unit = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (unit >= units) return;
@@ -354,8 +415,9 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int64_t 
     const int h = (int)(chain - b * a.H);
     const int64_t hd = (int64_t)a.H * a.d_v;
     const int64_t vrow0 = (b * a.T * a.H + h) * a.d_v + colc;  // v of token 0 of the chain
-    const rsrc_t Mr = make_rsrc(a.M + chain * a.N * a.d_v, (uint32_t)(a.N * a.d_v * 4));
-    const uint32_t rowb = (uint32_t)a.d_v * 4u;
+    const rsrc_t Mr = make_rsrc(static_cast<char *>(a.M) + chain * a.N * a.d_v * S::kElem,
+                                (uint32_t)(a.N * a.d_v * S::kElem));
+    const uint32_t rowb = (uint32_t)a.d_v * S::kElem;
     const uint32_t *rc = a.rec + ct * a.rec_dwords;
     const TPEntry *se = a.sorted + chain * a.T * a.W + t0 * a.W;
     const uint2 *pp = a.pairs + ct * a.P;
@@ -366,34 +428,33 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int64_t 
     float wr[NR];
     load_k<NR>(rc + 3 * a.Wp + g * NR, sl);
     load_k<NR>(a.rwt + ct * kMaxK + g * NR, wr);
-    float4 row[NR];
+    typename S::Raw row[NR];
 #pragma unroll
     for (int i = 0; i < NR; i++) {
         const bool ok = col_ok & (g * NR + i < a.R);
-        row[i] = buf_load4(Mr, ok ? (sl[i] & kSlotMask) * rowb + col * 4u : kOff);
+        row[i] = S::load_raw(Mr, ok ? (sl[i] & kSlotMask) * rowb + col * S::kElem : kOff);
     }
-    if (npw & kReplayFlag) {  // rare: reads whose pairs did not fit replay their writes
-        const uint32_t *lkp = a.rlink + ct * kMaxK + g * NR;
+    const bool replay = npw & kReplayFlag;  // rare: reads whose pairs did not fit
+    const uint32_t *lkp = a.rlink + ct * kMaxK + g * NR;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int i = 0; i < NR; i++) {
+    for (int i = 0; i < NR; i++) {
+        float4 rv = S::widen(row[i]);
+        if (replay) {
             // links exist only for the R real references; zero unless the plan overflowed
             const uint32_t l = (g * NR + i < a.R) ? lkp[i] : 0u;
             const int first = (int)(l >> kCntBits), cnt = (int)(l & ((1u << kCntBits) - 1u));
             for (int k = 0; k < cnt; k++) {  // writes of this slot earlier in the epoch
                 const TPEntry e = se[first + k];
                 const float4 vv = load_v<BF16>(a.v, vrow0 + (t0 + (e.tw >> 6)) * hd);
-                row[i] = fma4(e.a, row[i], e.c, vv);
+                rv = S::round(fma4(e.a, rv, e.c, vv));
             }
         }
-    }
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int i = 0; i < NR; i++) {
         // masked references have weight 0 and a zero row
-        acc.x = fmaf(wr[i], row[i].x, acc.x);
-        acc.y = fmaf(wr[i], row[i].y, acc.y);
-        acc.z = fmaf(wr[i], row[i].z, acc.z);
-        acc.w = fmaf(wr[i], row[i].w, acc.w);
+        acc.x = fmaf(wr[i], rv.x, acc.x);
+        acc.y = fmaf(wr[i], rv.y, acc.y);
+        acc.z = fmaf(wr[i], rv.z, acc.z);
+        acc.w = fmaf(wr[i], rv.w, acc.w);
     }
     for (int j0 = 0; j0 < np; j0 += kRPI * kPairBatch) {
         uint2 pr[kPairBatch];
@@ -432,10 +493,12 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int64_t 
 // differs from the previous event's starts that slot's segment: its group
 // loads the row once, applies the segment's writes in time order and stores
 // it once.  Loads of the SPG events are issued together.
-template <bool BF16, int SPG>
+template <bool BF16, int SPG, bool SB>
 __global__ __launch_bounds__(256) void tp_update_kernel(TPArgs a, int ep, int64_t units,
                                                         int nslice, int nblk)
 {
+    using S = StateRow<SB>;
+    constexpr int kLPR = S::kLPR, kRPI = 64 / kLPR;
     const int lane = threadIdx.x & 63;
     const int64_t unit = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (unit >= units) return;
@@ -454,8 +517,9 @@ __global__ __launch_bounds__(256) void tp_update_kernel(TPArgs a, int ep, int64_
     const int h = (int)(chain - b * a.H);
     const int64_t hd = (int64_t)a.H * a.d_v;
     const int64_t vrow0 = (b * a.T * a.H + h) * a.d_v + colc;
-    const rsrc_t Mr = make_rsrc(a.M + chain * a.N * a.d_v, (uint32_t)(a.N * a.d_v * 4));
-    const uint32_t rowb = (uint32_t)a.d_v * 4u;
+    const rsrc_t Mr = make_rsrc(static_cast<char *>(a.M) + chain * a.N * a.d_v * S::kElem,
+                                (uint32_t)(a.N * a.d_v * S::kElem));
+    const uint32_t rowb = (uint32_t)a.d_v * S::kElem;
     const TPEntry *se = a.sorted + chain * a.T * a.W + t0 * a.W;
 
     const int j0 = (blk * kRPI + g) * SPG;
@@ -469,28 +533,28 @@ __global__ __launch_bounds__(256) void tp_update_kernel(TPArgs a, int ep, int64_
     for (int s = 0; s < SPG; s++) {
         const uint32_t prev = s == 0 ? prev0 : e[s - 1].slot;
         head[s] = (j0 + s < n) & (e[s].slot != prev);
-        row[s] = buf_load4(Mr, (head[s] & col_ok) ? e[s].slot * rowb + col * 4u : kOff);
+        row[s] = S::load(Mr, (head[s] & col_ok) ? e[s].slot * rowb + col * S::kElem : kOff);
         vv[s] = load_v<BF16>(a.v, vrow0 + (t0 + (e[s].tw >> 6)) * hd);
     }
 #pragma unroll
     for (int s = 0; s < SPG; s++) {
-        float4 r = fma4(e[s].a, row[s], e[s].c, vv[s]);
+        float4 r = S::round(fma4(e[s].a, row[s], e[s].c, vv[s]));
         // the rest of the segment, in time order: events of this group from
         // registers, then (rarely) events past the group from memory
         bool more = true;
 #pragma unroll
         for (int s2 = s + 1; s2 < SPG; s2++) {
             more = more & (j0 + s2 < n) & (e[s2].slot == e[s].slot);
-            if (more) r = fma4(e[s2].a, r, e[s2].c, vv[s2]);
+            if (more) r = S::round(fma4(e[s2].a, r, e[s2].c, vv[s2]));
         }
         if (head[s] & more & (j0 + SPG < n) & (e[SPG].slot == e[s].slot)) {
             for (int j = j0 + SPG; j < n; j++) {
                 const TPEntry f = se[j];
                 if (f.slot != e[s].slot) break;
-                r = fma4(f.a, r, f.c, load_v<BF16>(a.v, vrow0 + (t0 + (f.tw >> 6)) * hd));
+                r = S::round(fma4(f.a, r, f.c, load_v<BF16>(a.v, vrow0 + (t0 + (f.tw >> 6)) * hd)));
             }
         }
-        buf_store4(r, Mr, (head[s] & col_ok) ? e[s].slot * rowb + col * 4u : kOff);
+        S::store(r, Mr, (head[s] & col_ok) ? e[s].slot * rowb + col * S::kElem : kOff);
     }
 }
 
@@ -538,7 +602,7 @@ size_t tp_workspace_bytes(const Shape &s)
 }
 
 static TPArgs tp_args(const Shape &s, const uint32_t *rec, void *ws, const void *v, float *y,
-                      float *M)
+                      void *M)
 {
     const RecLayout L(s.W, s.R);
     TPArgs a{};
@@ -588,6 +652,8 @@ static TPArgs tp_args(const Shape &s, const uint32_t *rec, void *ws, const void 
 
 bool tp_supported(const Shape &s)
 {
+    // 32-bit buffer offsets within one chain's float32 state (a bfloat16
+    // state takes half of that)
     return s.d_v % 4 == 0 && (double)s.N() * s.d_v * 4.0 <= 2147483648.0;
 }
 
@@ -612,26 +678,28 @@ hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipS
     return hipGetLastError();
 }
 
-hipError_t launch_tp_apply(const Shape &s, const uint32_t *rec, void *ws, const void *v,
-                           bool bf16, float *y, float *M, hipStream_t st, int ep0, int ep1)
+template <bool SB>
+static hipError_t tp_apply_state(const Shape &s, TPArgs a, bool bf16, hipStream_t st, int ep0,
+                                 int ep1)
 {
-    TPArgs a = tp_args(s, rec, ws, v, y, M);
+    constexpr int kLPR = StateRow<SB>::kLPR, kRPI = 64 / kLPR;
     const int nslice = (s.d_v + 4 * kLPR - 1) / (4 * kLPR);
     const int nr = (s.R + kRPI - 1) / kRPI;
-    if (ep1 < 0 || ep1 > a.nepoch) ep1 = a.nepoch;
     for (int ep = ep0; ep < ep1; ep++) {
         const int64_t t0 = (int64_t)ep * a.E;
         const int ne = (int)((s.T - t0) < a.E ? (s.T - t0) : a.E);
         const int64_t runits = a.chains * ne * nslice;
         const dim3 rgrid((unsigned)((runits + 3) / 4));
-#define SDM_TP_READ(NR_)                                                                       \
-    if (nr <= NR_) {                                                                           \
-        if (bf16) hipLaunchKernelGGL((tp_read_kernel<NR_, true>), rgrid, dim3(256), 0, st, a,  \
-                                     ep, runits, nslice);                                      \
-        else hipLaunchKernelGGL((tp_read_kernel<NR_, false>), rgrid, dim3(256), 0, st, a, ep,  \
-                                runits, nslice);                                               \
+#define SDM_TP_READ(NR_)                                                                          \
+    if (nr <= NR_) {                                                                              \
+        if (bf16) hipLaunchKernelGGL((tp_read_kernel<NR_, true, SB>), rgrid, dim3(256), 0, st, a, \
+                                     ep, runits, nslice);                                         \
+        else hipLaunchKernelGGL((tp_read_kernel<NR_, false, SB>), rgrid, dim3(256), 0, st, a, ep, \
+                                runits, nslice);                                                  \
     } else
-        SDM_TP_READ(1) SDM_TP_READ(2) SDM_TP_READ(4) SDM_TP_READ(8) { return hipErrorInvalidValue; }
+        SDM_TP_READ(1) SDM_TP_READ(2) SDM_TP_READ(4) SDM_TP_READ(8) SDM_TP_READ(16) {
+            return hipErrorInvalidValue;
+        }
 #undef SDM_TP_READ
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -639,14 +707,26 @@ hipError_t launch_tp_apply(const Shape &s, const uint32_t *rec, void *ws, const 
         const int nblk = (ne * s.W + kRPI * SPG - 1) / (kRPI * SPG);
         const int64_t uunits = a.chains * nblk * nslice;
         const dim3 ugrid((unsigned)((uunits + 3) / 4));
-        if (bf16) hipLaunchKernelGGL((tp_update_kernel<true, SPG>), ugrid, dim3(256), 0, st, a, ep,
-                                     uunits, nslice, nblk);
-        else hipLaunchKernelGGL((tp_update_kernel<false, SPG>), ugrid, dim3(256), 0, st, a, ep,
-                                uunits, nslice, nblk);
+        if (bf16)
+            hipLaunchKernelGGL((tp_update_kernel<true, SPG, SB>), ugrid, dim3(256), 0, st, a, ep,
+                               uunits, nslice, nblk);
+        else
+            hipLaunchKernelGGL((tp_update_kernel<false, SPG, SB>), ugrid, dim3(256), 0, st, a, ep,
+                               uunits, nslice, nblk);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_tp_apply(const Shape &s, const uint32_t *rec, void *ws, const void *v,
+                           bool bf16, float *y, void *M, bool state_bf16, hipStream_t st, int ep0,
+                           int ep1)
+{
+    TPArgs a = tp_args(s, rec, ws, v, y, M);
+    if (ep1 < 0 || ep1 > a.nepoch) ep1 = a.nepoch;
+    return state_bf16 ? tp_apply_state<true>(s, a, bf16, st, ep0, ep1)
+                      : tp_apply_state<false>(s, a, bf16, st, ep0, ep1);
 }
 
 }  // namespace sdm

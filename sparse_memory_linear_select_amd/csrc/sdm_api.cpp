@@ -30,6 +30,7 @@ struct SideStream {
 struct sdm_ctx {
     const float *M0 = nullptr;
     int H = 0, sqrtN = 0, d_v = 0, W = 0, R = 0;
+    bool state_bf16 = false;  // M holds bfloat16 values
     std::mutex mu;  // guards side[] and the enqueue sequence of a pipelined forward
     SideStream side[kMaxDevices];
 };
@@ -117,6 +118,9 @@ sdm_status check_variant(const sdm_ctx *h, int B, int64_t T, sdm_variant variant
     const sdm_variant var = resolve_variant(h, B, T, variant);
     if (var != SDM_VARIANT_SERIAL && var != SDM_VARIANT_TIMEPAR)
         return fail(SDM_ERR_ARG, "unknown variant %d", (int)variant);
+    if (h->state_bf16 && var == SDM_VARIANT_SERIAL)
+        return fail(SDM_ERR_UNSUPPORTED,
+                    "a bfloat16 state needs the time-parallel schedule (d_v %% 4 == 0)");
     if (var == SDM_VARIANT_TIMEPAR && !sdm::tp_supported(shape_of(h, B, T)))
         return fail(SDM_ERR_UNSUPPORTED,
                     "time-parallel schedule needs d_v %% 4 == 0 and N*d_v*4 <= 2^31");
@@ -187,7 +191,7 @@ bool pipeline_pays(const sdm::Shape &s)
 // Workspace regions of different groups are disjoint.
 sdm_status forward_pipelined(sdm_ctx *h, const sdm::Shape &s, const void *kp, const void *qp,
                              const void *v, const float *alpha, const float *beta, bool bf16,
-                             unsigned flags, void *workspace, float *y, float *M, hipStream_t hs)
+                             unsigned flags, void *workspace, float *y, void *M, hipStream_t hs)
 {
     std::lock_guard<std::mutex> lock(h->mu);
     hipError_t e;
@@ -218,7 +222,7 @@ sdm_status forward_pipelined(sdm_ctx *h, const sdm::Shape &s, const void *kp, co
     if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->fork, 0);
     if (e != hipSuccess) return hip_fail(e, "stream fork");
     if (!(flags & SDM_FLAG_CONTINUE)) {
-        e = sdm::launch_init(s, h->M0, M, hs);
+        e = sdm::launch_init(s, h->M0, M, h->state_bf16, hs);
         if (e != hipSuccess) return hip_fail(e, "init launch");
     }
     for (int c = 0; c < C; c++) {
@@ -237,7 +241,7 @@ sdm_status forward_pipelined(sdm_ctx *h, const sdm::Shape &s, const void *kp, co
         const int e0 = bound[c], e1 = bound[c + 1];
         e = hipStreamWaitEvent(hs, ss->ready[c], 0);
         if (e != hipSuccess) return hip_fail(e, "stream wait");
-        e = sdm::launch_tp_apply(s, rec, tp, v, bf16, y, M, hs, e0, e1);
+        e = sdm::launch_tp_apply(s, rec, tp, v, bf16, y, M, h->state_bf16, hs, e0, e1);
         if (e != hipSuccess) return hip_fail(e, "time-parallel write/read launch");
     }
     return SDM_OK;
@@ -261,7 +265,8 @@ const char *sdm_status_string(sdm_status s)
 
 const char *sdm_last_error(void) { return g_err.c_str(); }
 
-sdm_status sdm_create(const float *M0, int H, int sqrtN, int d_v, int W, int R, sdm_handle *out)
+sdm_status sdm_create_ex(const float *M0, int H, int sqrtN, int d_v, int W, int R,
+                         sdm_dtype state_dtype, sdm_handle *out)
 {
     if (!out) return fail(SDM_ERR_ARG, "null output handle pointer");
     *out = nullptr;
@@ -277,6 +282,9 @@ sdm_status sdm_create(const float *M0, int H, int sqrtN, int d_v, int W, int R, 
         return fail(SDM_ERR_UNSUPPORTED, "sqrtN > %d is not supported", sdm::kMaxSqrtN);
     if (W > sdm::kMaxK || R > sdm::kMaxK)
         return fail(SDM_ERR_UNSUPPORTED, "W, R > %d are not supported", sdm::kMaxK);
+    if (state_dtype != SDM_F32 && state_dtype != SDM_BF16)
+        return fail(SDM_ERR_ARG, "state dtype must be SDM_F32 or SDM_BF16 (got %d)",
+                    (int)state_dtype);
     sdm_ctx *h = new (std::nothrow) sdm_ctx;
     if (!h) return fail(SDM_ERR_ARG, "out of host memory");
     h->M0 = M0;
@@ -285,18 +293,25 @@ sdm_status sdm_create(const float *M0, int H, int sqrtN, int d_v, int W, int R, 
     h->d_v = d_v;
     h->W = W;
     h->R = R;
+    h->state_bf16 = state_dtype == SDM_BF16;
     *out = h;
     return SDM_OK;
+}
+
+sdm_status sdm_create(const float *M0, int H, int sqrtN, int d_v, int W, int R, sdm_handle *out)
+{
+    return sdm_create_ex(M0, H, sqrtN, d_v, W, R, SDM_F32, out);
 }
 
 sdm_status sdm_destroy(sdm_handle h)
 {
     if (!h) return SDM_OK;
     int cur = -1;
-    const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+    bool have_cur = false;  // HIP is touched only if a helper stream exists
     for (int d = 0; d < kMaxDevices; d++) {
         SideStream &ss = h->side[d];
         if (!ss.s) continue;
+        if (!have_cur) have_cur = hipGetDevice(&cur) == hipSuccess;
         // work still queued on the stream completes before its resources go
         (void)hipSetDevice(d);
         for (hipEvent_t &e : ss.ready)
@@ -359,7 +374,7 @@ sdm_status sdm_write_histogram(sdm_handle h, int B, int64_t T, const void *kp, s
 sdm_status sdm_prepare(sdm_handle h, int B, int64_t T, const void *kp, const void *qp,
                        const float *alpha, const float *beta, sdm_dtype dtype,
                        sdm_variant variant, unsigned flags, void *workspace, size_t ws_bytes,
-                       float *M, void *stream)
+                       void *M, void *stream)
 {
     sdm_status st = check_handle_call(h, B, T, dtype);
     if (st != SDM_OK) return st;
@@ -378,7 +393,7 @@ sdm_status sdm_prepare(sdm_handle h, int B, int64_t T, const void *kp, const voi
     uint32_t *rec = static_cast<uint32_t *>(workspace);
     hipError_t e;
     if (!(flags & SDM_FLAG_CONTINUE)) {
-        e = sdm::launch_init(s, h->M0, M, hs);
+        e = sdm::launch_init(s, h->M0, M, h->state_bf16, hs);
         if (e != hipSuccess) return hip_fail(e, "init launch");
     }
     e = sdm::launch_select(s, kp, qp, dtype == SDM_BF16, nullptr, nullptr, nullptr, nullptr, rec,
@@ -396,7 +411,7 @@ sdm_status sdm_prepare(sdm_handle h, int B, int64_t T, const void *kp, const voi
 }
 
 sdm_status sdm_apply(sdm_handle h, int B, int64_t T, const void *v, sdm_dtype dtype,
-                     sdm_variant variant, void *workspace, size_t ws_bytes, float *y, float *M,
+                     sdm_variant variant, void *workspace, size_t ws_bytes, float *y, void *M,
                      void *stream)
 {
     sdm_status st = check_handle_call(h, B, T, dtype);
@@ -413,13 +428,15 @@ sdm_status sdm_apply(sdm_handle h, int B, int64_t T, const void *v, sdm_dtype dt
     const uint32_t *rec = static_cast<const uint32_t *>(workspace);
     if (var == SDM_VARIANT_TIMEPAR) {
         char *tp = static_cast<char *>(workspace) + records_bytes(h, B, T);
-        const hipError_t e = sdm::launch_tp_apply(s, rec, tp, v, dtype == SDM_BF16, y, M, hs);
+        const hipError_t e =
+            sdm::launch_tp_apply(s, rec, tp, v, dtype == SDM_BF16, y, M, h->state_bf16, hs);
         if (e != hipSuccess) return hip_fail(e, "time-parallel write/read launch");
         return SDM_OK;
     }
+    float *Mf = static_cast<float *>(M);  // the serial schedule keeps a float32 state
     const hipError_t e = sdm::rw_serial_supported(s)
-                             ? sdm::launch_rw_serial(s, rec, v, dtype == SDM_BF16, y, M, hs)
-                             : sdm::launch_rw_simple(s, rec, v, dtype == SDM_BF16, y, M, hs);
+                             ? sdm::launch_rw_serial(s, rec, v, dtype == SDM_BF16, y, Mf, hs)
+                             : sdm::launch_rw_simple(s, rec, v, dtype == SDM_BF16, y, Mf, hs);
     if (e != hipSuccess) return hip_fail(e, "write/read launch");
     return SDM_OK;
 }
@@ -427,7 +444,7 @@ sdm_status sdm_apply(sdm_handle h, int B, int64_t T, const void *v, sdm_dtype dt
 sdm_status sdm_forward(sdm_handle h, int B, int64_t T, const void *kp, const void *qp,
                        const void *v, const float *alpha, const float *beta, sdm_dtype dtype,
                        sdm_variant variant, unsigned flags, void *workspace, size_t ws_bytes,
-                       float *y, float *M, void *stream)
+                       float *y, void *M, void *stream)
 {
     // validate everything before enqueueing either half
     sdm_status st = check_handle_call(h, B, T, dtype);

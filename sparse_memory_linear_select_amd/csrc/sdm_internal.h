@@ -67,7 +67,7 @@ hipError_t launch_select(const Shape &s, const void *kp, const void *qp, bool bf
                          int64_t tn = -1);  // tokens [t0, t0 + tn) of every sequence
 
 // M[b] <- M0 for every sequence b.
-hipError_t launch_init(const Shape &s, const float *M0, float *M, hipStream_t st);
+hipError_t launch_init(const Shape &s, const float *M0, void *M, bool state_bf16, hipStream_t st);
 
 // Adds forwarding codes (distance < depth) to the slot words of all records.
 hipError_t launch_plan(const Shape &s, uint32_t *rec, int depth, hipStream_t st);
@@ -91,7 +91,7 @@ size_t tp_workspace_bytes(const Shape &s);  // beyond the token records
 hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipStream_t st,
                              int ep0 = 0, int ep1 = -1);
 hipError_t launch_tp_apply(const Shape &s, const uint32_t *rec, void *ws, const void *v,
-                           bool bf16, float *y, float *M, hipStream_t st, int ep0 = 0,
-                           int ep1 = -1);
+                           bool bf16, float *y, void *M, bool state_bf16, hipStream_t st,
+                           int ep0 = 0, int ep1 = -1);
 
 }  // namespace sdm

@@ -152,3 +152,29 @@ def test_python_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(sdm.SDMError):
         sdm.SDM(torch.zeros(1, 16, 4), 2, 2)
+
+
+def test_bf16_state_handle():
+    """sdm_create_ex takes the state type; a bfloat16 state needs the
+    time-parallel schedule, which the checks report without a GPU."""
+    L = sdm.lib()
+    h = ctypes.c_void_p()
+    assert L.sdm_create_ex(ctypes.c_void_p(FAKE), 2, 16, 32, 4, 4, 7, ctypes.byref(h)) == 1
+    assert h.value is None
+    assert L.sdm_create_ex(ctypes.c_void_p(FAKE), 2, 16, 32, 4, 4, sdm.BF16, ctypes.byref(h)) == 0
+    n = ctypes.c_size_t()
+    try:
+        assert L.sdm_workspace_size(h, 2, 100, sdm.F32, sdm.TIMEPAR, ctypes.byref(n)) == 0
+        ntp = n.value
+        assert L.sdm_workspace_size(h, 2, 100, sdm.F32, sdm.AUTO, ctypes.byref(n)) == 0
+        assert n.value == ntp  # AUTO picks the time-parallel schedule
+        assert L.sdm_workspace_size(h, 2, 100, sdm.F32, sdm.SERIAL, ctypes.byref(n)) == 2
+        assert b"bfloat16" in L.sdm_last_error()
+    finally:
+        L.sdm_destroy(h)
+    # d_v % 4 != 0: no schedule can hold a bfloat16 state
+    assert L.sdm_create_ex(ctypes.c_void_p(FAKE), 1, 16, 30, 4, 4, sdm.BF16, ctypes.byref(h)) == 0
+    try:
+        assert L.sdm_workspace_size(h, 1, 10, sdm.F32, sdm.AUTO, ctypes.byref(n)) == 2
+    finally:
+        L.sdm_destroy(h)
