@@ -357,6 +357,28 @@ __global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int str
 
 // ------------------------------------------------------------------ read
 
+// Value of x in lane (lane & ~(LPR - 1)) | i, i.e. lane i of this lane's
+// group of LPR lanes (LPR = 8 or 16): ds_swizzle in bit mode acts within 32
+// lanes as lane' = (lane & and_mask) | or_mask.
+// (i is a constant once the callers' loops are unrolled, so the switch folds
+// to one instruction; the swizzle pattern must be an immediate.)
+template <int LPR>
+__device__ __forceinline__ uint32_t group_bcast(uint32_t x, int i)
+{
+    static_assert(LPR == 8 || LPR == 16, "row groups of 8 or 16 lanes");
+    constexpr int kAnd = 0x1F & ~(LPR - 1);
+    const int v = (int)x;
+    switch (i) {
+#define SDM_SWZ(I) \
+    case I: return (uint32_t)__builtin_amdgcn_ds_swizzle(v, kAnd | ((I) << 5));
+        SDM_SWZ(0) SDM_SWZ(1) SDM_SWZ(2) SDM_SWZ(3) SDM_SWZ(4) SDM_SWZ(5) SDM_SWZ(6) SDM_SWZ(7)
+        SDM_SWZ(8) SDM_SWZ(9) SDM_SWZ(10) SDM_SWZ(11) SDM_SWZ(12) SDM_SWZ(13) SDM_SWZ(14)
+        SDM_SWZ(15)
+#undef SDM_SWZ
+    }
+    return 0u;
+}
+
 template <int K, typename T>
 __device__ __forceinline__ void load_k(const T *p, T (&out)[K])
 {
@@ -424,23 +446,40 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int64_t 
     const uint32_t npw = __builtin_amdgcn_readfirstlane(a.npair[ct]);
     const int np = (int)(npw & ~kReplayFlag);
 
-    uint32_t sl[NR];
-    float wr[NR];
-    load_k<NR>(rc + 3 * a.Wp + g * NR, sl);
-    load_k<NR>(a.rwt + ct * kMaxK + g * NR, wr);
-    typename S::Raw row[NR];
-#pragma unroll
-    for (int i = 0; i < NR; i++) {
-        const bool ok = col_ok & (g * NR + i < a.R);
-        row[i] = S::load_raw(Mr, ok ? (sl[i] & kSlotMask) * rowb + col * S::kElem : kOff);
-    }
-    const bool replay = npw & kReplayFlag;  // rare: reads whose pairs did not fit
-    const uint32_t *lkp = a.rlink + ct * kMaxK + g * NR;
+    // lane q of row group g holds the slot word and weight of reference
+    // g*NR + q (q < NR); the group reads them back with in-group broadcasts
+    const bool mine = (q < NR) & (g * NR + q < a.R);
+    const uint32_t sl_mine = mine ? rc[3 * a.Wp + g * NR + q] : 0u;
+    const float wr_mine = mine ? a.rwt[ct * kMaxK + g * NR + q] : 0.0f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (!(npw & kReplayFlag)) {
+        // every row gather at once, then the weighted sum
+        typename S::Raw row[NR];
 #pragma unroll
-    for (int i = 0; i < NR; i++) {
-        float4 rv = S::widen(row[i]);
-        if (replay) {
+        for (int i = 0; i < NR; i++) {
+            const uint32_t sl = group_bcast<kLPR>(sl_mine, i);
+            const bool ok = col_ok & (g * NR + i < a.R);
+            row[i] = S::load_raw(Mr, ok ? (sl & kSlotMask) * rowb + col * S::kElem : kOff);
+        }
+#pragma unroll
+        for (int i = 0; i < NR; i++) {
+            // masked references have weight 0 and a zero row
+            const float4 rv = S::widen(row[i]);
+            const float wr = __uint_as_float(group_bcast<kLPR>(__float_as_uint(wr_mine), i));
+            acc.x = fmaf(wr, rv.x, acc.x);
+            acc.y = fmaf(wr, rv.y, acc.y);
+            acc.z = fmaf(wr, rv.z, acc.z);
+            acc.w = fmaf(wr, rv.w, acc.w);
+        }
+    } else {
+        // rare: some reads of this token replay the writes their pairs could
+        // not hold; one reference at a time
+        const uint32_t *lkp = a.rlink + ct * kMaxK + g * NR;
+#pragma unroll 1
+        for (int i = 0; i < NR; i++) {
+            const uint32_t sl = group_bcast<kLPR>(sl_mine, i);
+            const bool ok = col_ok & (g * NR + i < a.R);
+            float4 rv = S::load(Mr, ok ? (sl & kSlotMask) * rowb + col * S::kElem : kOff);
             // links exist only for the R real references; zero unless the plan overflowed
             const uint32_t l = (g * NR + i < a.R) ? lkp[i] : 0u;
             const int first = (int)(l >> kCntBits), cnt = (int)(l & ((1u << kCntBits) - 1u));
@@ -449,12 +488,12 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int64_t 
                 const float4 vv = load_v<BF16>(a.v, vrow0 + (t0 + (e.tw >> 6)) * hd);
                 rv = S::round(fma4(e.a, rv, e.c, vv));
             }
+            const float wr = __uint_as_float(group_bcast<kLPR>(__float_as_uint(wr_mine), i));
+            acc.x = fmaf(wr, rv.x, acc.x);
+            acc.y = fmaf(wr, rv.y, acc.y);
+            acc.z = fmaf(wr, rv.z, acc.z);
+            acc.w = fmaf(wr, rv.w, acc.w);
         }
-        // masked references have weight 0 and a zero row
-        acc.x = fmaf(wr[i], rv.x, acc.x);
-        acc.y = fmaf(wr[i], rv.y, acc.y);
-        acc.z = fmaf(wr[i], rv.z, acc.z);
-        acc.w = fmaf(wr[i], rv.w, acc.w);
     }
     for (int j0 = 0; j0 < np; j0 += kRPI * kPairBatch) {
         uint2 pr[kPairBatch];
@@ -703,7 +742,10 @@ static hipError_t tp_apply_state(const Shape &s, TPArgs a, bool bf16, hipStream_
 #undef SDM_TP_READ
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        constexpr int SPG = 4;  // sorted events per row group
+#ifndef SDM_TP_SPG_BF16
+#define SDM_TP_SPG_BF16 4
+#endif
+        constexpr int SPG = SB ? SDM_TP_SPG_BF16 : 4;  // sorted events per row group
         const int nblk = (ne * s.W + kRPI * SPG - 1) / (kRPI * SPG);
         const int64_t uunits = a.chains * nblk * nslice;
         const dim3 ugrid((unsigned)((uunits + 3) / 4));
