@@ -59,6 +59,11 @@ def _load():
                 ctypes.c_int, ctypes.c_int, p, p, p, p, p, ctypes.c_int, p, p, p,
                 ctypes.c_int, ctypes.c_int, ctypes.c_int, p, p, ctypes.c_int]
             lib.sdm_oracle_recurrence.restype = ctypes.c_int
+            lib.sdm_oracle_backward.argtypes = [
+                ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                ctypes.c_int, ctypes.c_int, p, p, p, p, p, ctypes.c_int, p, p, p, p, p,
+                p, p, p, p, p, p, ctypes.c_int]
+            lib.sdm_oracle_backward.restype = ctypes.c_int
             lib.sdm_oracle_round_bf16.argtypes = [p, p, ctypes.c_int64]
             lib.sdm_oracle_round_bf16.restype = None
             _lib = lib
@@ -154,3 +159,33 @@ def forward(inp: dict, sqrtN: int, W: int, R: int, c0: int = 0, c1: int | None =
     y, M = recurrence(Iw, kw, Ir, qw, inp["v"], inp["alpha"], inp["beta"], inp["M0"],
                       sqrtN, c0, c1, threads, state)
     return dict(Iw=Iw, kw=kw, Ir=Ir, qw=qw, y=y, M=M)
+
+
+def backward(inp: dict, sqrtN: int, W: int, R: int, dy, dMT=None,
+             threads: int | None = None) -> dict:
+    """Gradients of the core (float64 state, selections held fixed) for the
+    upstream gradients dy [B,T,H,d_v] and dMT [B,H,N,d_v] (None: zero).
+    Returns dkp, dqp [B,T,H,2 sqrtN], dv [B,T,H,d_v], dalpha, dbeta [B,T,H]
+    and dM0 [H,N,d_v], all float64."""
+    Iw, kw = select(inp["kp"], sqrtN, W, threads)
+    Ir, qw = select(inp["qp"], sqrtN, R, threads)
+    v, alpha, beta, M0 = (np.ascontiguousarray(inp[k]) for k in ("v", "alpha", "beta", "M0"))
+    B, T, H, d_v = v.shape
+    N = sqrtN * sqrtN
+    dy = np.ascontiguousarray(dy, dtype=np.float64)
+    assert dy.shape == (B, T, H, d_v)
+    if dMT is not None:
+        dMT = np.ascontiguousarray(dMT, dtype=np.float64)
+        assert dMT.shape == (B, H, N, d_v)
+    out = dict(dkp=np.empty((B, T, H, 2 * sqrtN)), dqp=np.empty((B, T, H, 2 * sqrtN)),
+               dv=np.empty((B, T, H, d_v)), dalpha=np.empty((B, T, H)),
+               dbeta=np.empty((B, T, H)), dM0=np.empty((H, N, d_v)))
+    rc = _load().sdm_oracle_backward(
+        B, T, H, sqrtN, d_v, W, R, _ptr(Iw), _ptr(kw), _ptr(Ir), _ptr(qw), _ptr(v),
+        _dtype_code(v), _ptr(alpha), _ptr(beta), _ptr(M0), _ptr(dy),
+        _ptr(dMT) if dMT is not None else None, _ptr(out["dkp"]), _ptr(out["dqp"]),
+        _ptr(out["dv"]), _ptr(out["dalpha"]), _ptr(out["dbeta"]), _ptr(out["dM0"]),
+        threads or default_threads())
+    if rc != 0:
+        raise ValueError(f"sdm_oracle_backward failed ({rc})")
+    return out

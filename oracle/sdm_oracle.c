@@ -30,6 +30,24 @@
  *     order, of q^(i) * M[i], taken after the same token's write.
  *  Every sequence starts from the shared initial state M_0 [explainer §3.1,
  *  learned initial state paragraph; Technical Summary, Learned Initial State].
+ *  7. Backward (reverse mode, float64 state) with the selected index sets
+ *     held fixed -- they are piecewise constant in k' and q', so the
+ *     gradient reaches k' and q' only through the softmax weights.  The
+ *     explainer's training discussion (memory-efficient backward, learned
+ *     initial state M_0) needs these gradients; the pages print no formulas,
+ *     so they are derived here from steps 3-5 by the chain rule.  Per token,
+ *     in reverse order, with G the gradient of the loss with respect to the
+ *     state after the token:
+ *       read:  dq_r = <dy_t, M[r]>,  G[r] += q_r dy_t
+ *       write: with m = alpha M_old, new = m + beta k (v - m):
+ *              dk     = <G[i], beta (v - m)>
+ *              dalpha += <G[i], M_old> (1 - beta k)
+ *              dbeta  += <G[i], k (v - m)>
+ *              dv     += beta k G[i]
+ *              G[i]    = alpha (1 - beta k) G[i],  M[i] = M_old
+ *       weights: dscore_j = w_j (dw_j - sum_l w_l dw_l) (softmax), and a
+ *              slot n = i sqrtN + j passes dscore to x[i] and x[sqrtN + j].
+ *     After token 0, dM_0[h] = sum over sequences b of G.
  *  6. Reduced-precision state (optional).  The engineering notes of the
  *     explainer suggest storing the state in a narrower type to fit larger
  *     N; the pages fix no rule.  Reading adopted: the state is held in
@@ -288,4 +306,158 @@ int sdm_oracle_recurrence(int B, int64_t T, int H, int sqrtN, int d_v, int W, in
                   state_bf16, c0, c1, ca, cb, y, M);
     }
     return 0;
+}
+
+/*
+ * Backward of one chain (b, h): recomputes the forward with a tape of the
+ * rows each write replaced, then runs the tokens in reverse.  Gf receives
+ * the gradient with respect to this chain's initial state.
+ */
+static int backward_chain(int64_t T, int H, int64_t N, int d_v, int W, int R, int sqrtN, int b,
+                          int h, const int32_t *Iw, const double *kw, const int32_t *Ir,
+                          const double *qw, const void *v, int v_dtype, const float *alpha,
+                          const float *beta, const float *M0, const double *dy, const double *dMT,
+                          double *dkp, double *dqp, double *dv, double *dalpha, double *dbeta,
+                          double *Gf)
+{
+    double *M = malloc(sizeof(double) * (size_t)(N * d_v));
+    double *tape = malloc(sizeof(double) * (size_t)(T * W) * (size_t)d_v);
+    double *dwk = malloc(sizeof(double) * (size_t)(W > R ? W : R));
+    if (!M || !tape || !dwk) {
+        free(M);
+        free(tape);
+        free(dwk);
+        return -2;
+    }
+    double *G = Gf;
+    const int64_t S = 2 * (int64_t)sqrtN;
+    for (int64_t x = 0; x < N * d_v; x++) M[x] = (double)M0[(int64_t)h * N * d_v + x];
+    /* forward, recording the old row of every write */
+    for (int64_t t = 0; t < T; t++) {
+        const int64_t ht = ((int64_t)b * T + t) * H + h;
+        const double a_t = (double)alpha[ht], b_t = (double)beta[ht];
+        for (int w = 0; w < W; w++) {
+            const int64_t sl = Iw[ht * W + w];
+            const double k = kw[ht * W + w];
+            double *row = M + sl * d_v;
+            double *old = tape + (t * W + w) * d_v;
+            for (int c = 0; c < d_v; c++) {
+                old[c] = row[c];
+                const double m = a_t * row[c];
+                row[c] = m + b_t * k * (load_value(v, v_dtype, ht * d_v + c) - m);
+            }
+        }
+    }
+    /* reverse */
+    const int64_t chain_off = ((int64_t)b * H + h) * N * d_v;
+    for (int64_t x = 0; x < N * d_v; x++) G[x] = dMT ? dMT[chain_off + x] : 0.0;
+    for (int64_t t = T - 1; t >= 0; t--) {
+        const int64_t ht = ((int64_t)b * T + t) * H + h;
+        const double a_t = (double)alpha[ht], b_t = (double)beta[ht];
+        const double *dyt = dy + ht * d_v;
+        double *dkp_t = dkp + ht * S, *dqp_t = dqp + ht * S;
+        for (int64_t x = 0; x < S; x++) dkp_t[x] = dqp_t[x] = 0.0;
+        /* read: on the state after this token's writes */
+        double sw = 0.0;
+        for (int r = 0; r < R; r++) {
+            const int64_t sl = Ir[ht * R + r];
+            const double q = qw[ht * R + r];
+            double dq = 0.0;
+            for (int c = 0; c < d_v; c++) dq += dyt[c] * M[sl * d_v + c];
+            for (int c = 0; c < d_v; c++) G[sl * d_v + c] += q * dyt[c];
+            dwk[r] = dq;
+            sw += q * dq;
+        }
+        for (int r = 0; r < R; r++) {
+            const double q = qw[ht * R + r];
+            const double ds = q * (dwk[r] - sw);
+            const int64_t n = Ir[ht * R + r];
+            dqp_t[n / sqrtN] += ds;
+            dqp_t[sqrtN + n % sqrtN] += ds;
+        }
+        /* writes (distinct slots: order is irrelevant) */
+        double da = 0.0, db = 0.0;
+        for (int c = 0; c < d_v; c++) dv[ht * d_v + c] = 0.0;
+        sw = 0.0;
+        for (int w = 0; w < W; w++) {
+            const int64_t sl = Iw[ht * W + w];
+            const double k = kw[ht * W + w];
+            const double *old = tape + (t * W + w) * d_v;
+            double *g = G + sl * d_v;
+            double dk = 0.0;
+            for (int c = 0; c < d_v; c++) {
+                const double vt = load_value(v, v_dtype, ht * d_v + c);
+                const double m = a_t * old[c];
+                dk += g[c] * b_t * (vt - m);
+                da += g[c] * old[c] * (1.0 - b_t * k);
+                db += g[c] * k * (vt - m);
+                dv[ht * d_v + c] += b_t * k * g[c];
+                g[c] *= a_t * (1.0 - b_t * k);
+                M[sl * d_v + c] = old[c];
+            }
+            dwk[w] = dk;
+            sw += k * dk;
+        }
+        dalpha[ht] = da;
+        dbeta[ht] = db;
+        for (int w = 0; w < W; w++) {
+            const double k = kw[ht * W + w];
+            const double ds = k * (dwk[w] - sw);
+            const int64_t n = Iw[ht * W + w];
+            dkp_t[n / sqrtN] += ds;
+            dkp_t[sqrtN + n % sqrtN] += ds;
+        }
+    }
+    free(M);
+    free(tape);
+    free(dwk);
+    return 0;
+}
+
+/*
+ * Gradients of the token-serial core (float64 state) from a given selection.
+ *   dy [B][T][H][d_v], dMT [B][H][N][d_v] (NULL: zero) upstream gradients
+ *   out: dkp, dqp [B][T][H][2*sqrtN], dv [B][T][H][d_v], dalpha, dbeta
+ *   [B][T][H], dM0 [H][N][d_v]  (all float64, every column)
+ * Returns 0, -1 on bad arguments, -2 when out of host memory.
+ */
+int sdm_oracle_backward(int B, int64_t T, int H, int sqrtN, int d_v, int W, int R,
+                        const int32_t *Iw, const double *kw, const int32_t *Ir, const double *qw,
+                        const void *v, int v_dtype, const float *alpha, const float *beta,
+                        const float *M0, const double *dy, const double *dMT, double *dkp,
+                        double *dqp, double *dv, double *dalpha, double *dbeta, double *dM0,
+                        int nthreads)
+{
+    if (B < 1 || T < 1 || H < 1 || sqrtN < 1 || d_v < 1 || W < 1 || R < 1) return -1;
+    if (W > sqrtN || R > sqrtN) return -1;
+    if (!Iw || !kw || !Ir || !qw || !v || !alpha || !beta || !M0 || !dy) return -1;
+    if (!dkp || !dqp || !dv || !dalpha || !dbeta || !dM0) return -1;
+    if (v_dtype != ORACLE_F32 && v_dtype != ORACLE_BF16) return -1;
+    if (nthreads < 1) nthreads = 1;
+    const int64_t N = (int64_t)sqrtN * sqrtN;
+    const int64_t chains = (int64_t)B * H;
+    double *Gall = malloc(sizeof(double) * (size_t)(chains * N) * (size_t)d_v);
+    if (!Gall) return -2;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int64_t ch = 0; ch < chains; ch++) {
+        const int b = (int)(ch / H), h = (int)(ch % H);
+        if (backward_chain(T, H, N, d_v, W, R, sqrtN, b, h, Iw, kw, Ir, qw, v, v_dtype, alpha,
+                           beta, M0, dy, dMT, dkp, dqp, dv, dalpha, dbeta,
+                           Gall + ch * N * d_v) != 0) {
+#pragma omp atomic write
+            bad = 1;
+        }
+    }
+    if (!bad) {
+        /* dM_0[h] = sum over b of the chains' initial-state gradients, b in order */
+        for (int h = 0; h < H; h++)
+            for (int64_t x = 0; x < N * d_v; x++) {
+                double acc = 0.0;
+                for (int b = 0; b < B; b++) acc += Gall[((int64_t)b * H + h) * N * d_v + x];
+                dM0[(int64_t)h * N * d_v + x] = acc;
+            }
+    }
+    free(Gall);
+    return bad ? -2 : 0;
 }

@@ -366,3 +366,85 @@ def test_bf16_state_error_bound():
     assert np.abs(o16["M"] - o64["M"]).max() <= (writes + 1) * 2.0**-8 * scale
     assert np.abs(o16["y"] - o64["y"]).max() <= (writes + 1) * 2.0**-8 * scale
     assert np.abs(o16["M"] - o64["M"]).max() > 0  # the rounding is really applied
+
+
+# ------------------------------------------------------------------ backward
+
+def _loss(inp, S, W, R, Ry, RM):
+    o = oracle.forward(inp, S, W, R)
+    return float((o["y"] * Ry).sum() + (o["M"] * RM).sum()), o
+
+
+@pytest.mark.parametrize("case", [
+    dict(B=1, T=6, H=1, S=4, D=3, W=2, R=2, dtype="f32", seed=51),
+    dict(B=2, T=9, H=2, S=5, D=4, W=3, R=2, dtype="f32", seed=52),
+    dict(B=1, T=12, H=1, S=3, D=5, W=3, R=3, dtype="f32", seed=53),  # every slot rewritten often
+    dict(B=2, T=7, H=1, S=4, D=4, W=2, R=3, dtype="bf16", seed=54),
+])
+def test_backward_matches_finite_differences(case):
+    """Every gradient of the oracle's backward (with the selections held
+    fixed) against central differences of the forward, for the loss
+    L = sum(y * Ry) + sum(M_T * RM) with random Ry, RM."""
+    c = dict(case)
+    wl = si.Workload("fd", B=c["B"], T=c["T"], H=c["H"], sqrtN=c["S"], d_v=c["D"], W=c["W"],
+                     R=c["R"], dtype=c["dtype"], reuse=0.2, seed=c["seed"])
+    d = si.generate(wl)
+    # gates away from 0 and 1 so that +-h stays a valid gate; M_0 of order 1
+    d["alpha"][:] = np.clip(d["alpha"], 0.2, 0.95)
+    d["beta"][:] = np.clip(d["beta"], 0.05, 0.95)
+    d["M0"][:] = (d["M0"] * 40).astype(np.float32)
+    rng = np.random.default_rng(c["seed"])
+    Ry = rng.standard_normal((wl.B, wl.T, wl.H, wl.d_v))
+    RM = rng.standard_normal((wl.B, wl.H, wl.N, wl.d_v))
+    L0, o0 = _loss(d, wl.sqrtN, wl.W, wl.R, Ry, RM)
+    g = oracle.backward(d, wl.sqrtN, wl.W, wl.R, Ry, RM)
+    names = {"kp": "dkp", "qp": "dqp", "v": "dv", "alpha": "dalpha", "beta": "dbeta",
+             "M0": "dM0"}
+    checked = 0
+    for name, gname in names.items():
+        x = d[name]
+        flat = x.reshape(-1)
+        for idx in rng.choice(flat.size, size=min(12, flat.size), replace=False):
+            if x.dtype == np.uint16:  # bf16 inputs: step to the neighbouring bf16 values
+                old = flat[idx]
+                bf = lambda bits: float(np.array([int(bits) << 16], np.uint32).view(np.float32)[0])
+                if bf(old) == 0.0 or (int(old) & 0x7FFF) in (0, 0x7FFF):
+                    continue  # stay away from zero and the top of the range
+                flat[idx] = old + 1; xp = bf(flat[idx]); Lp, op = _loss(d, wl.sqrtN, wl.W, wl.R, Ry, RM)
+                flat[idx] = old - 1; xm = bf(flat[idx]); Lm, om = _loss(d, wl.sqrtN, wl.W, wl.R, Ry, RM)
+                flat[idx] = old
+            else:
+                old = flat[idx]
+                h = np.float32(2.0 ** -9 * max(1.0, abs(float(old))))
+                flat[idx] = old + h; xp = float(flat[idx]); Lp, op = _loss(d, wl.sqrtN, wl.W, wl.R, Ry, RM)
+                flat[idx] = old - h; xm = float(flat[idx]); Lm, om = _loss(d, wl.sqrtN, wl.W, wl.R, Ry, RM)
+                flat[idx] = old
+            if name in ("kp", "qp"):  # the selection must not move
+                if not all((op[k] == o0[k]).all() and (om[k] == o0[k]).all() for k in ("Iw", "Ir")):
+                    continue
+            fd = (Lp - Lm) / (xp - xm)
+            an = float(g[gname].reshape(-1)[idx])
+            assert abs(fd - an) <= 2e-3 * (1.0 + abs(an)), (name, idx, fd, an)
+            checked += 1
+    assert checked >= 40
+
+
+def test_backward_linear_pieces_are_exact():
+    """Closed forms the backward must reproduce: with dMT only (dy = 0), the
+    gradient reaching M_0 through never-written rows is dMT itself, summed
+    over sequences; and beta = 0 makes v, beta-free paths vanish: dv = 0."""
+    wl, d = _tiny(seed=55, S=8)
+    d["kp"][..., :wl.sqrtN] = -8.0
+    d["kp"][..., :2] = 8.0
+    rng = np.random.default_rng(55)
+    RM = rng.standard_normal((wl.B, wl.H, wl.N, wl.d_v))
+    o = oracle.forward(d, wl.sqrtN, wl.W, wl.R)
+    g = oracle.backward(d, wl.sqrtN, wl.W, wl.R, np.zeros((wl.B, wl.T, wl.H, wl.d_v)), RM)
+    for h in range(wl.H):
+        never = np.setdiff1d(np.arange(wl.N), np.unique(o["Iw"][:, :, h]))
+        assert never.size > 0
+        np.testing.assert_allclose(g["dM0"][h, never], RM[:, h, never].sum(0), rtol=1e-15)
+    d2 = dict(d)
+    d2["beta"] = np.zeros_like(d["beta"])
+    g2 = oracle.backward(d2, wl.sqrtN, wl.W, wl.R, rng.standard_normal((wl.B, wl.T, wl.H, wl.d_v)), RM)
+    assert (g2["dv"] == 0).all()
