@@ -148,6 +148,56 @@ def decode(args, wl):
         "data": "synthetic (seeded; recipe in sdm_inputs.py)"}), flush=True)
 
 
+def backward(args, wl):
+    """Backward of the core over the whole workload: dL/dy random, dL/dM_T
+    random; one step = one sdm_backward call (it recomputes the forward)."""
+    import numpy as np
+    import torch
+
+    import sdm_inputs as si
+    import sparse_memory_linear_select_amd as sdm
+
+    d = si.generate(wl)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x).to(dev)
+
+    dd = {k: up(v) for k, v in d.items() if k != "src"}
+    core = sdm.SDM(dd["M0"], wl.W, wl.R)
+    args_ = [dd[n] for n in ("kp", "qp", "v", "alpha", "beta")]
+    g = torch.Generator(device=dev).manual_seed(0)
+    dy = torch.randn((wl.B, wl.T, wl.H, wl.d_v), device=dev, generator=g)
+    dMT = torch.randn((wl.B, wl.H, wl.N, wl.d_v), device=dev, generator=g)
+    dt_code = sdm.BF16 if wl.dtype == "bf16" else sdm.F32
+    import ctypes
+    nb = ctypes.c_size_t()
+    sdm._check(sdm.lib().sdm_backward_workspace_size(core._h, wl.B, wl.T, dt_code,
+                                                     ctypes.byref(nb)))
+    ws = torch.empty(nb.value, dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        core.backward(*args_, dy, dMT=dMT, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        core.backward(*args_, dy, dMT=dMT, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    print(json.dumps({
+        "metric": "SDM backward head-tokens/s (forward recompute + reverse, selections fixed)",
+        "value": wl.head_tokens / (ms * 1e-3), "unit": "head-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "workspace_gb": nb.value / 1e9,
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": wl.H, "sqrtN": wl.sqrtN,
+                   "d_v": wl.d_v, "W": wl.W, "R": wl.R, "inputs": wl.dtype},
+        "data": "synthetic (seeded; recipe in sdm_inputs.py)"}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,6 +214,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode", action="store_true",
                     help="measure one-token decode steps (continuing the state) instead")
+    ap.add_argument("--backward", action="store_true",
+                    help="measure the backward (sdm_backward: forward recompute + reverse) instead")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -181,6 +233,8 @@ def main():
     wl = si.WORKLOADS[args.workload]
     if args.decode:
         return decode(args, wl)
+    if args.backward:
+        return backward(args, wl)
     _log(f"workload {args.workload}: {wl}")
     t = time.perf_counter()
     d = si.generate(wl)

@@ -221,6 +221,43 @@ sdm_status sdm_apply(sdm_handle h, int B, int64_t T, const void *v, sdm_dtype dt
 sdm_status sdm_write_histogram(sdm_handle h, int B, int64_t T, const void *kp,
                                sdm_dtype dtype, uint32_t *counts, void *stream);
 
+/*
+ * Backward of the core: gradients of a loss L(y, M_T) given dL/dy and
+ * dL/dM_T, with the selected slot sets held fixed (they are piecewise
+ * constant in k', q'; the gradient reaches k' and q' through the softmax
+ * weights).  The explainer "Sparse Delta Memory：通过稀疏性扩展线性 RNN 的状态容量"
+ * (§3.1; its training discussion needs a memory-efficient backward and the
+ * gradient of the learned initial state) fixes the forward; the derivatives
+ * follow from it by the chain rule.
+ *
+ * The call recomputes the forward (selection, then the writes, recording
+ * the row every write replaces) and runs the tokens in reverse on the
+ * time-parallel schedule; it needs a float32 state (sdm_create) and
+ * d_v % 4 == 0 (else SDM_ERR_UNSUPPORTED).
+ *   kp, qp, v, alpha, beta, dtype   the forward's inputs (as sdm_forward)
+ *   Minit      device [B][H][N][d_v] float32: the state the forward started
+ *              from (as with SDM_FLAG_CONTINUE), or NULL for M_0
+ *   dy         device [B][T][H][d_v] float32, dL/dy
+ *   dMT        device [B][H][N][d_v] float32, dL/dM_T, or NULL for zero
+ *   workspace  >= sdm_backward_workspace_size(...) bytes, 16-byte aligned.
+ *              It holds the tape: B*H*T*W*d_v*4 bytes and more.
+ * Outputs (device, float32, overwritten):
+ *   dkp, dqp   [B][T][H][2*sqrtN]   dL/dk', dL/dq'
+ *   dv         [B][T][H][d_v]       dL/dv
+ *   dalpha, dbeta [B][T][H]
+ *   dMinit     [B][H][N][d_v]       dL/d(initial state of each sequence)
+ *   dM0        [H][N][d_v]          sum over b of dMinit, or NULL to skip
+ * Results are deterministic (fixed reduction orders).
+ */
+sdm_status sdm_backward_workspace_size(sdm_handle h, int B, int64_t T, sdm_dtype dtype,
+                                       size_t *bytes);
+
+sdm_status sdm_backward(sdm_handle h, int B, int64_t T, const void *kp, const void *qp,
+                        const void *v, const float *alpha, const float *beta, sdm_dtype dtype,
+                        const float *Minit, const float *dy, const float *dMT, void *workspace,
+                        size_t ws_bytes, float *dkp, float *dqp, float *dv, float *dalpha,
+                        float *dbeta, float *dMinit, float *dM0, void *stream);
+
 /* Static description of a status code. */
 const char *sdm_status_string(sdm_status s);
 

@@ -33,7 +33,8 @@ STATUS = {0: "SDM_OK", 1: "SDM_ERR_ARG", 2: "SDM_ERR_UNSUPPORTED", 3: "SDM_ERR_W
           4: "SDM_ERR_HIP"}
 
 # every function include/sdm.h declares
-EXPORTS = ("sdm_create", "sdm_create_ex", "sdm_destroy", "sdm_workspace_size", "sdm_select", "sdm_forward",
+EXPORTS = ("sdm_backward", "sdm_backward_workspace_size", "sdm_create", "sdm_create_ex",
+           "sdm_destroy", "sdm_workspace_size", "sdm_select", "sdm_forward",
            "sdm_prepare", "sdm_apply", "sdm_write_histogram", "sdm_status_string",
            "sdm_last_error")
 
@@ -66,7 +67,11 @@ def lib():
         L.sdm_prepare.argtypes = [p, i, i64, p, p, p, p, i, i, ctypes.c_uint, p, sz, p, p]
         L.sdm_apply.argtypes = [p, i, i64, p, i, i, p, sz, p, p, p]
         L.sdm_write_histogram.argtypes = [p, i, i64, p, i, p, p]
-        for f in ("sdm_create", "sdm_create_ex", "sdm_destroy", "sdm_workspace_size", "sdm_select", "sdm_forward",
+        L.sdm_backward_workspace_size.argtypes = [p, i, i64, i, ctypes.POINTER(sz)]
+        L.sdm_backward.argtypes = [p, i, i64, p, p, p, p, p, i, p, p, p, p, sz, p, p, p, p, p,
+                                   p, p, p]
+        for f in ("sdm_backward", "sdm_backward_workspace_size", "sdm_create", "sdm_create_ex",
+                  "sdm_destroy", "sdm_workspace_size", "sdm_select", "sdm_forward",
                   "sdm_prepare", "sdm_apply", "sdm_write_histogram"):
             getattr(L, f).restype = ctypes.c_int
         L.sdm_status_string.argtypes = [i]
@@ -196,6 +201,52 @@ class SDM:
         _check(lib().sdm_write_histogram(self._h, B, T, _ptr(kp), _in_dtype(kp), _ptr(counts),
                                          _stream(kp.device)))
         return counts
+
+    def backward(self, kp, qp, v, alpha, beta, dy, dMT=None, Minit=None, workspace=None,
+                  dM0: bool = True) -> dict:
+        """Gradients of the core for upstream gradients dy [B,T,H,d_v] (and dMT
+        [B,H,N,d_v], None = zero), with the selections held fixed.  Minit is the
+        state the forward started from (None: M_0).  Returns float32 dkp, dqp
+        [B,T,H,2 sqrtN], dv [B,T,H,d_v], dalpha, dbeta [B,T,H], dMinit
+        [B,H,N,d_v] and (dM0=True) dM0 [H,N,d_v]."""
+        for t, nm in ((kp, "kp"), (qp, "qp"), (v, "v")):
+            _dev_tensor(t, nm)
+        _dev_tensor(alpha, "alpha", torch.float32)
+        _dev_tensor(beta, "beta", torch.float32)
+        _dev_tensor(dy, "dy", torch.float32)
+        B, T = self._shape_in(kp, 2 * self.sqrtN, "kp")
+        if qp.shape != kp.shape or qp.dtype != kp.dtype or v.dtype != kp.dtype:
+            raise SDMError(1, "kp, qp and v must share one dtype (and kp, qp one shape)")
+        if tuple(v.shape) != (B, T, self.H, self.d_v) or tuple(dy.shape) != tuple(v.shape):
+            raise SDMError(1, "v and dy must be [B, T, H, d_v]")
+        if tuple(alpha.shape) != (B, T, self.H) or tuple(beta.shape) != (B, T, self.H):
+            raise SDMError(1, "alpha and beta must be [B, T, H]")
+        sshape = (B, self.H, self.N, self.d_v)
+        for t, nm in ((dMT, "dMT"), (Minit, "Minit")):
+            if t is not None:
+                _dev_tensor(t, nm, torch.float32)
+                if tuple(t.shape) != sshape:
+                    raise SDMError(1, f"{nm} must be [B, H, N, d_v]")
+        dev = kp.device
+        dt = _in_dtype(kp)
+        n = ctypes.c_size_t()
+        _check(lib().sdm_backward_workspace_size(self._h, B, T, dt, ctypes.byref(n)))
+        if workspace is None or workspace.numel() < n.value:
+            workspace = torch.empty(max(n.value, 16), dtype=torch.uint8, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        out = dict(dkp=torch.empty((B, T, self.H, 2 * self.sqrtN), **f32),
+                   dqp=torch.empty((B, T, self.H, 2 * self.sqrtN), **f32),
+                   dv=torch.empty((B, T, self.H, self.d_v), **f32),
+                   dalpha=torch.empty((B, T, self.H), **f32), dbeta=torch.empty((B, T, self.H), **f32),
+                   dMinit=torch.empty(sshape, **f32))
+        if dM0:
+            out["dM0"] = torch.empty((self.H, self.N, self.d_v), **f32)
+        _check(lib().sdm_backward(
+            self._h, B, T, _ptr(kp), _ptr(qp), _ptr(v), _ptr(alpha), _ptr(beta), dt, _ptr(Minit),
+            _ptr(dy), _ptr(dMT), _ptr(workspace), workspace.numel(), _ptr(out["dkp"]),
+            _ptr(out["dqp"]), _ptr(out["dv"]), _ptr(out["dalpha"]), _ptr(out["dbeta"]),
+            _ptr(out["dMinit"]), _ptr(out.get("dM0")), _stream(dev)))
+        return out
 
     def forward(self, kp, qp, v, alpha, beta, variant: int = AUTO, y=None, M=None,
                 workspace=None, cont: bool = False, staged: bool = False):

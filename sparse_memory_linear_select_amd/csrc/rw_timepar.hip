@@ -24,114 +24,17 @@
 // produced by the same float32 operations, in the same order, as in the
 // token-serial schedule, so both schedules give identical M; y agrees to
 // float32 rounding (its terms are grouped differently).
-#include "sdm_internal.h"
+#include "tp_device.h"
 
 namespace sdm {
 namespace {
 
-using rsrc_t = __amdgpu_buffer_rsrc_t;
-constexpr uint32_t kOff = 0x80000000u;
-constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kSortThreads = 1024;
 constexpr int kMaxEpoch = 4096;            // tokens per epoch
 constexpr int kMaxEpochEvents = 1 << 18;   // write events per (chain, epoch)
 constexpr int kCntBits = 13;               // replay link: count < 2^13, position < 2^19
 constexpr uint32_t kReplayFlag = 1u << 31;  // in npair: the token has replay links
 static_assert(kMaxEpoch < (1 << kCntBits), "a slot is written at most once per token");
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
-}
-
-__device__ __forceinline__ float4 buf_load4(rsrc_t r, uint32_t off)
-{
-    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
-}
-
-__device__ __forceinline__ void buf_store4(float4 v, rsrc_t r, uint32_t off)
-{
-    __builtin_amdgcn_raw_buffer_store_b128(
-        __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v), r, (int)off, 0, 0);
-}
-
-__device__ __forceinline__ float4 fma4(float a, float4 x, float c, float4 v)
-{
-    return make_float4(fmaf(a, x.x, c * v.x), fmaf(a, x.y, c * v.y), fmaf(a, x.z, c * v.z),
-                       fmaf(a, x.w, c * v.w));
-}
-
-// Nearest bfloat16 (ties to even) of a finite float, as its 16 bits.
-__device__ __forceinline__ uint32_t bf16_bits(float f)
-{
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-// Row storage of the state.  Every lane holds 4 columns of a row; a row
-// slice is the 128 bytes that LPR lanes cover (the fabric's request size).
-//   float32 state: 8 lanes x 16 bytes;
-//   bfloat16 state: 16 lanes x 8 bytes, widened exactly on load, rounded to
-//   nearest-even after every write (the value the state holds).
-template <bool SB>
-struct StateRow;
-
-template <>
-struct StateRow<false> {
-    static constexpr int kLPR = 8;
-    static constexpr uint32_t kElem = 4;
-    using Raw = float4;
-    static __device__ __forceinline__ Raw load_raw(rsrc_t r, uint32_t off) { return buf_load4(r, off); }
-    static __device__ __forceinline__ float4 widen(Raw x) { return x; }
-    static __device__ __forceinline__ float4 load(rsrc_t r, uint32_t off) { return buf_load4(r, off); }
-    static __device__ __forceinline__ void store(float4 v, rsrc_t r, uint32_t off)
-    {
-        buf_store4(v, r, off);
-    }
-    static __device__ __forceinline__ float4 round(float4 v) { return v; }
-};
-
-template <>
-struct StateRow<true> {
-    static constexpr int kLPR = 16;
-    static constexpr uint32_t kElem = 2;
-    using Raw = uint2;  // 4 bfloat16 values
-    static __device__ __forceinline__ Raw load_raw(rsrc_t r, uint32_t off)
-    {
-        const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
-        return make_uint2(u[0], u[1]);
-    }
-    static __device__ __forceinline__ float4 widen(Raw u)
-    {
-        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
-                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
-    }
-    static __device__ __forceinline__ float4 load(rsrc_t r, uint32_t off) { return widen(load_raw(r, off)); }
-    static __device__ __forceinline__ void store(float4 v, rsrc_t r, uint32_t off)
-    {
-        __attribute__((ext_vector_type(2))) unsigned u;
-        u[0] = bf16_bits(v.x) | (bf16_bits(v.y) << 16);
-        u[1] = bf16_bits(v.z) | (bf16_bits(v.w) << 16);
-        __builtin_amdgcn_raw_buffer_store_b64(u, r, (int)off, 0, 0);
-    }
-    static __device__ __forceinline__ float4 round(float4 v)
-    {
-        return make_float4(__uint_as_float(bf16_bits(v.x) << 16), __uint_as_float(bf16_bits(v.y) << 16),
-                           __uint_as_float(bf16_bits(v.z) << 16), __uint_as_float(bf16_bits(v.w) << 16));
-    }
-};
-
-template <bool BF16>
-__device__ __forceinline__ float4 load_v(const void *v, int64_t off)
-{
-    if constexpr (BF16) {
-        const uint2 u = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(v) + off);
-        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
-                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
-    } else {
-        return *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(v) + off);
-    }
-}
 
 struct TPArgs {
     const uint32_t *rec;  // token records (slots, coefficients)
@@ -151,6 +54,15 @@ struct TPArgs {
     int E, nepoch, passes, kshift;
     int ep0, nrun;  // sort/link launches: epochs [ep0, ep0 + nrun)
     int64_t chains;
+    float *tape;    // backward's forward pass: [chain][T][W][d_v] row each write replaced
+};
+
+// Where a sort writes: the forward sorts the W write events of each token;
+// the backward sorts them together with the R read events (W + R per token).
+struct SortIO {
+    TPEntry *out;           // [chain][T * per_token] sorted entries, epoch regions
+    uint64_t *tmpA, *tmpB;  // radix ping-pong, same layout
+    uint16_t *ckey;         // coarse keys (forward only)
 };
 
 // ------------------------------------------------------------------ sort
@@ -164,8 +76,10 @@ constexpr int kWaves = kSortThreads / 64;
 // input order is time order and stability keeps each slot's writes in time
 // order.  The last pass writes the 16-byte entries and a 16-bit coarse key
 // (slot >> kshift) per entry for the link search.
-__global__ __launch_bounds__(kSortThreads) void tp_sort_kernel(TPArgs a)
+template <bool MERGED>
+__global__ __launch_bounds__(kSortThreads) void tp_sort_kernel(TPArgs a, SortIO io)
 {
+    const int ept = MERGED ? a.W + a.R : a.W;  // events per token
     __shared__ uint32_t bins[kBuckets];
     __shared__ uint32_t wcnt[kWaves][kBuckets];
     const int tid = threadIdx.x;
@@ -175,20 +89,21 @@ __global__ __launch_bounds__(kSortThreads) void tp_sort_kernel(TPArgs a)
     const int ep = a.ep0 + (int)(blockIdx.x - chain * a.nrun);
     const int64_t t0 = (int64_t)ep * a.E;
     const int ne = (int)((a.T - t0) < a.E ? (a.T - t0) : a.E);  // tokens in this epoch
-    const int n = ne * a.W;                                      // write events
-    const int64_t base = chain * a.T * a.W + t0 * a.W;          // epoch region
+    const int n = ne * ept;                                      // events
+    const int64_t base = chain * a.T * ept + t0 * ept;          // epoch region
     const uint32_t *recc = a.rec + (chain * a.T + t0) * a.rec_dwords;
     const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
     for (int p = 0; p < a.passes; p++) {
         const int shift = kDigitBits * p;
-        const uint64_t *src = (p & 1) ? a.tmpA + base : a.tmpB + base;  // unused when p == 0
-        uint64_t *dst = (p & 1) ? a.tmpB + base : a.tmpA + base;
+        const uint64_t *src = (p & 1) ? io.tmpA + base : io.tmpB + base;  // unused when p == 0
+        uint64_t *dst = (p & 1) ? io.tmpB + base : io.tmpA + base;
         const bool last = p == a.passes - 1;
         auto item = [&](int j) -> uint64_t {  // (slot << 32) | event j
             if (p == 0) {
-                const int tl = j / a.W, w = j - tl * a.W;
-                return ((uint64_t)(recc[(int64_t)tl * a.rec_dwords + w] & kSlotMask) << 32) |
+                const int tl = j / ept, k = j - tl * ept;  // k >= W: read k - W
+                const int col = (MERGED && k >= a.W) ? 3 * a.Wp + (k - a.W) : k;
+                return ((uint64_t)(recc[(int64_t)tl * a.rec_dwords + col] & kSlotMask) << 32) |
                        (uint32_t)j;
             }
             return src[j];
@@ -250,15 +165,25 @@ __global__ __launch_bounds__(kSortThreads) void tp_sort_kernel(TPArgs a)
                     dst[pos] = it;
                 } else {  // final order: the 16-byte entries and the coarse keys
                     const uint32_t ev = (uint32_t)it;
-                    const int tl = (int)(ev / (uint32_t)a.W), w = (int)(ev - tl * a.W);
+                    const int tl = (int)(ev / (uint32_t)ept), k = (int)(ev - tl * ept);
                     const float *rf = reinterpret_cast<const float *>(recc + (int64_t)tl * a.rec_dwords);
                     TPEntry e;
                     e.slot = (uint32_t)(it >> 32);
-                    e.tw = ((uint32_t)tl << 6) | (uint32_t)w;
-                    e.a = rf[a.Wp + w];
-                    e.c = rf[2 * a.Wp + w];
-                    a.sorted[base + pos] = e;
-                    a.ckey[base + pos] = (uint16_t)(e.slot >> a.kshift);
+                    if (!MERGED) {  // write w = k: (token << 6) | w, a, c
+                        e.tw = ((uint32_t)tl << 6) | (uint32_t)k;
+                        e.a = rf[a.Wp + k];
+                        e.c = rf[2 * a.Wp + k];
+                    } else if (k < a.W) {  // write: (token << 7) | w, a, c
+                        e.tw = ((uint32_t)tl << 7) | (uint32_t)k;
+                        e.a = rf[a.Wp + k];
+                        e.c = rf[2 * a.Wp + k];
+                    } else {  // read r: (token << 7) | 64 | r, q, 0
+                        e.tw = ((uint32_t)tl << 7) | 64u | (uint32_t)(k - a.W);
+                        e.a = rf[3 * a.Wp + a.Rp + (k - a.W)];
+                        e.c = 0.0f;
+                    }
+                    io.out[base + pos] = e;
+                    if (!MERGED) io.ckey[base + pos] = (uint16_t)(e.slot >> a.kshift);
                 }
             }
             __syncthreads();
@@ -356,50 +281,6 @@ __global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int str
 }
 
 // ------------------------------------------------------------------ read
-
-// Value of x in lane (lane & ~(LPR - 1)) | i, i.e. lane i of this lane's
-// group of LPR lanes (LPR = 8 or 16): ds_swizzle in bit mode acts within 32
-// lanes as lane' = (lane & and_mask) | or_mask.
-// (i is a constant once the callers' loops are unrolled, so the switch folds
-// to one instruction; the swizzle pattern must be an immediate.)
-template <int LPR>
-__device__ __forceinline__ uint32_t group_bcast(uint32_t x, int i)
-{
-    static_assert(LPR == 8 || LPR == 16, "row groups of 8 or 16 lanes");
-    constexpr int kAnd = 0x1F & ~(LPR - 1);
-    const int v = (int)x;
-    switch (i) {
-#define SDM_SWZ(I) \
-    case I: return (uint32_t)__builtin_amdgcn_ds_swizzle(v, kAnd | ((I) << 5));
-        SDM_SWZ(0) SDM_SWZ(1) SDM_SWZ(2) SDM_SWZ(3) SDM_SWZ(4) SDM_SWZ(5) SDM_SWZ(6) SDM_SWZ(7)
-        SDM_SWZ(8) SDM_SWZ(9) SDM_SWZ(10) SDM_SWZ(11) SDM_SWZ(12) SDM_SWZ(13) SDM_SWZ(14)
-        SDM_SWZ(15)
-#undef SDM_SWZ
-    }
-    return 0u;
-}
-
-template <int K, typename T>
-__device__ __forceinline__ void load_k(const T *p, T (&out)[K])
-{
-    if constexpr (K % 4 == 0 && sizeof(T) == 4) {
-#pragma unroll
-        for (int i = 0; i < K; i += 4) {
-            const uint4 x = *reinterpret_cast<const uint4 *>(p + i);
-            out[i] = __builtin_bit_cast(T, x.x);
-            out[i + 1] = __builtin_bit_cast(T, x.y);
-            out[i + 2] = __builtin_bit_cast(T, x.z);
-            out[i + 3] = __builtin_bit_cast(T, x.w);
-        }
-    } else if constexpr (K == 2 && sizeof(T) == 4) {
-        const uint2 x = *reinterpret_cast<const uint2 *>(p);
-        out[0] = __builtin_bit_cast(T, x.x);
-        out[1] = __builtin_bit_cast(T, x.y);
-    } else {
-#pragma unroll
-        for (int i = 0; i < K; i++) out[i] = p[i];
-    }
-}
 
 // One wavefront per (chain, token of the epoch, 32-column slice).  With the
 // read plan, y_t = sum_r w_r row_r + sum_j u_j v_(t_j): the 8 row groups take
@@ -532,10 +413,11 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int64_t 
 // differs from the previous event's starts that slot's segment: its group
 // loads the row once, applies the segment's writes in time order and stores
 // it once.  Loads of the SPG events are issued together.
-template <bool BF16, int SPG, bool SB>
+template <bool BF16, int SPG, bool SB, bool TAPE = false>
 __global__ __launch_bounds__(256) void tp_update_kernel(TPArgs a, int ep, int64_t units,
                                                         int nslice, int nblk)
 {
+    static_assert(!(TAPE && SB), "the tape holds float32 rows");
     using S = StateRow<SB>;
     constexpr int kLPR = S::kLPR, kRPI = 64 / kLPR;
     const int lane = threadIdx.x & 63;
@@ -560,6 +442,13 @@ __global__ __launch_bounds__(256) void tp_update_kernel(TPArgs a, int ep, int64_
                                 (uint32_t)(a.N * a.d_v * S::kElem));
     const uint32_t rowb = (uint32_t)a.d_v * S::kElem;
     const TPEntry *se = a.sorted + chain * a.T * a.W + t0 * a.W;
+    // TAPE: the row each write replaced, at [chain][token][w][column]
+    float *tape_c = TAPE ? a.tape + (chain * a.T + t0) * a.W * a.d_v + colc : nullptr;
+    auto tape_put = [&](const TPEntry &ev, float4 x, bool on) {
+        if (TAPE && on)
+            *reinterpret_cast<float4 *>(tape_c + ((int64_t)(ev.tw >> 6) * a.W + (ev.tw & 63u)) *
+                                                     a.d_v) = x;
+    };
 
     const int j0 = (blk * kRPI + g) * SPG;
     TPEntry e[SPG + 1];  // this group's events and the one after them
@@ -577,6 +466,7 @@ __global__ __launch_bounds__(256) void tp_update_kernel(TPArgs a, int ep, int64_
     }
 #pragma unroll
     for (int s = 0; s < SPG; s++) {
+        tape_put(e[s], row[s], head[s] & col_ok);
         float4 r = S::round(fma4(e[s].a, row[s], e[s].c, vv[s]));
         // the rest of the segment, in time order: events of this group from
         // registers, then (rarely) events past the group from memory
@@ -584,12 +474,14 @@ __global__ __launch_bounds__(256) void tp_update_kernel(TPArgs a, int ep, int64_
 #pragma unroll
         for (int s2 = s + 1; s2 < SPG; s2++) {
             more = more & (j0 + s2 < n) & (e[s2].slot == e[s].slot);
+            tape_put(e[s2], r, head[s] & more & col_ok);
             if (more) r = S::round(fma4(e[s2].a, r, e[s2].c, vv[s2]));
         }
         if (head[s] & more & (j0 + SPG < n) & (e[SPG].slot == e[s].slot)) {
             for (int j = j0 + SPG; j < n; j++) {
                 const TPEntry f = se[j];
                 if (f.slot != e[s].slot) break;
+                tape_put(f, r, col_ok);
                 r = S::round(fma4(f.a, r, f.c, load_v<BF16>(a.v, vrow0 + (t0 + (f.tw >> 6)) * hd)));
             }
         }
@@ -697,7 +589,7 @@ bool tp_supported(const Shape &s)
 }
 
 hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipStream_t st,
-                             int ep0, int ep1)
+                             int ep0, int ep1, bool link)
 {
     TPArgs a = tp_args(s, rec, ws, nullptr, nullptr, nullptr);
     if (ep1 < 0 || ep1 > a.nepoch) ep1 = a.nepoch;
@@ -705,9 +597,11 @@ hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipS
     a.ep0 = ep0;
     a.nrun = ep1 - ep0;
     const int64_t blocks = a.chains * a.nrun;
-    hipLaunchKernelGGL(tp_sort_kernel, dim3((unsigned)blocks), dim3(kSortThreads), 0, st, a);
+    const SortIO io{a.sorted, a.tmpA, a.tmpB, a.ckey};
+    hipLaunchKernelGGL(tp_sort_kernel<false>, dim3((unsigned)blocks), dim3(kSortThreads), 0, st, a,
+                       io);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || !link) return e;
     // sampled coarse keys: at most 32768 of them (64 KiB of LDS)
     const int64_t nmax = (int64_t)a.E * s.W;
     const int stride = nmax > 32768 ? (int)((nmax + 32767) / 32768) : 1;
@@ -759,6 +653,43 @@ static hipError_t tp_apply_state(const Shape &s, TPArgs a, bool bf16, hipStream_
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_tp_forward_tape(const Shape &s, const uint32_t *rec, void *ws, const void *v,
+                                  bool bf16, float *M, float *tape, hipStream_t st)
+{
+    TPArgs a = tp_args(s, rec, ws, v, nullptr, M);
+    a.tape = tape;
+    constexpr int kLPR = StateRow<false>::kLPR, kRPI = 64 / kLPR, SPG = 4;
+    const int nslice = (s.d_v + 4 * kLPR - 1) / (4 * kLPR);
+    for (int ep = 0; ep < a.nepoch; ep++) {
+        const int64_t t0 = (int64_t)ep * a.E;
+        const int ne = (int)((s.T - t0) < a.E ? (s.T - t0) : a.E);
+        const int nblk = (ne * s.W + kRPI * SPG - 1) / (kRPI * SPG);
+        const int64_t uunits = a.chains * nblk * nslice;
+        const dim3 ugrid((unsigned)((uunits + 3) / 4));
+        if (bf16)
+            hipLaunchKernelGGL((tp_update_kernel<true, SPG, false, true>), ugrid, dim3(256), 0, st, a,
+                               ep, uunits, nslice, nblk);
+        else
+            hipLaunchKernelGGL((tp_update_kernel<false, SPG, false, true>), ugrid, dim3(256), 0, st,
+                               a, ep, uunits, nslice, nblk);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_tp_sort_merged(const Shape &s, const uint32_t *rec, void *ws, TPEntry *out,
+                                 uint64_t *tmpA, uint64_t *tmpB, hipStream_t st)
+{
+    TPArgs a = tp_args(s, rec, ws, nullptr, nullptr, nullptr);
+    a.ep0 = 0;
+    a.nrun = a.nepoch;
+    const SortIO io{out, tmpA, tmpB, nullptr};
+    hipLaunchKernelGGL(tp_sort_kernel<true>, dim3((unsigned)(a.chains * a.nrun)),
+                       dim3(kSortThreads), 0, st, a, io);
+    return hipGetLastError();
 }
 
 hipError_t launch_tp_apply(const Shape &s, const uint32_t *rec, void *ws, const void *v,

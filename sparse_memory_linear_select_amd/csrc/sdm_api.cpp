@@ -247,6 +247,24 @@ sdm_status forward_pipelined(sdm_ctx *h, const sdm::Shape &s, const void *kp, co
     return SDM_OK;
 }
 
+size_t bwd_ws_bytes(const sdm_ctx *h, int B, int64_t T)
+{
+    const sdm::Shape s = shape_of(h, B, T);
+    return records_bytes(h, B, T) + round_up(sdm::tp_workspace_bytes(s)) +
+           round_up(sdm::tp_backward_workspace_bytes(s));
+}
+
+sdm_status check_backward(const sdm_ctx *h, int B, int64_t T)
+{
+    if (h->state_bf16)
+        return fail(SDM_ERR_UNSUPPORTED, "the backward needs a float32 state");
+    if (!sdm::tp_supported(shape_of(h, B, T)))
+        return fail(SDM_ERR_UNSUPPORTED,
+                    "the backward runs on the time-parallel schedule: d_v %% 4 == 0 and "
+                    "N*d_v*4 <= 2^31");
+    return SDM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -469,6 +487,60 @@ sdm_status sdm_forward(sdm_handle h, int B, int64_t T, const void *kp, const voi
                      stream);
     if (st != SDM_OK) return st;
     return sdm_apply(h, B, T, v, dtype, variant, workspace, ws_bytes, y, M, stream);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+sdm_status sdm_backward_workspace_size(sdm_handle h, int B, int64_t T, sdm_dtype dtype,
+                                       size_t *bytes)
+{
+    if (!bytes) return fail(SDM_ERR_ARG, "null bytes pointer");
+    *bytes = 0;
+    sdm_status st = check_handle_call(h, B, T, dtype);
+    if (st != SDM_OK) return st;
+    st = check_backward(h, B, T);
+    if (st != SDM_OK) return st;
+    *bytes = bwd_ws_bytes(h, B, T);
+    return SDM_OK;
+}
+
+sdm_status sdm_backward(sdm_handle h, int B, int64_t T, const void *kp, const void *qp,
+                        const void *v, const float *alpha, const float *beta, sdm_dtype dtype,
+                        const float *Minit, const float *dy, const float *dMT, void *workspace,
+                        size_t ws_bytes, float *dkp, float *dqp, float *dv, float *dalpha,
+                        float *dbeta, float *dMinit, float *dM0, void *stream)
+{
+    sdm_status st = check_handle_call(h, B, T, dtype);
+    if (st != SDM_OK) return st;
+    if (!kp || !qp || !v || !alpha || !beta || !dy || !workspace || !dkp || !dqp || !dv ||
+        !dalpha || !dbeta || !dMinit)
+        return fail(SDM_ERR_ARG, "null tensor pointer");
+    const void *ptrs[] = {kp, qp, v, alpha, beta, dy, workspace, dkp, dqp, dv, dalpha, dbeta,
+                          dMinit};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return fail(SDM_ERR_ARG, "tensor pointers must be 16-byte aligned");
+    if ((Minit && !aligned16(Minit)) || (dMT && !aligned16(dMT)) || (dM0 && !aligned16(dM0)))
+        return fail(SDM_ERR_ARG, "tensor pointers must be 16-byte aligned");
+    st = check_backward(h, B, T);
+    if (st != SDM_OK) return st;
+    const size_t need = bwd_ws_bytes(h, B, T);
+    if (ws_bytes < need)
+        return fail(SDM_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+
+    const sdm::Shape s = shape_of(h, B, T);
+    const hipStream_t hs = (hipStream_t)stream;
+    uint32_t *rec = static_cast<uint32_t *>(workspace);
+    char *fwd = static_cast<char *>(workspace) + records_bytes(h, B, T);
+    char *bwd = fwd + round_up(sdm::tp_workspace_bytes(s));
+    hipError_t e = sdm::launch_select(s, kp, qp, dtype == SDM_BF16, nullptr, nullptr, nullptr,
+                                      nullptr, rec, alpha, beta, hs);
+    if (e != hipSuccess) return hip_fail(e, "select launch");
+    e = sdm::launch_tp_backward(s, rec, fwd, bwd, v, dtype == SDM_BF16, h->M0, Minit, dy, dMT,
+                                alpha, beta, dkp, dqp, dv, dalpha, dbeta, dMinit, dM0, hs);
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+    return SDM_OK;
 }
 
 }  // extern "C"

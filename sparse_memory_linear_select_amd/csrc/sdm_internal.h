@@ -28,7 +28,8 @@ constexpr uint32_t kFwdValid = 1u << 29;
 // serial kernel's row groups load their references unconditionally (masked
 // entries are ignored), and those loads then always stay inside the record.
 //   ws[Wp]  write slot words     wa[Wp]  alpha*(1 - beta*k)   wc[Wp]  beta*k
-//   rs[Rp]  read slot words      rq[Rp]  q weights
+//   rs[Rp]  read slot words      rq[Rp]  q weights            wk[Wp]  k weights
+// (wk is read by the backward only.)
 struct RecLayout {
     int Wp, Rp;
     __host__ __device__ RecLayout(int, int) : Wp(kMaxK), Rp(kMaxK) {}
@@ -37,7 +38,8 @@ struct RecLayout {
     __host__ __device__ int wc() const { return 2 * Wp; }
     __host__ __device__ int rs() const { return 3 * Wp; }
     __host__ __device__ int rq() const { return 3 * Wp + Rp; }
-    __host__ __device__ int dwords() const { return 3 * Wp + 2 * Rp; }
+    __host__ __device__ int wk() const { return 3 * Wp + 2 * Rp; }
+    __host__ __device__ int dwords() const { return 4 * Wp + 2 * Rp; }
 };
 
 // One write event of an epoch after sorting by slot (time-parallel schedule):
@@ -89,9 +91,23 @@ int tp_epoch_len(const Shape &s);
 size_t tp_workspace_bytes(const Shape &s);  // beyond the token records
 // Epochs [ep0, ep1) (ep1 < 0: through the last epoch).
 hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipStream_t st,
-                             int ep0 = 0, int ep1 = -1);
+                             int ep0 = 0, int ep1 = -1, bool link = true);
 hipError_t launch_tp_apply(const Shape &s, const uint32_t *rec, void *ws, const void *v,
                            bool bf16, float *y, void *M, bool state_bf16, hipStream_t st,
                            int ep0 = 0, int ep1 = -1);
+
+// Backward (float32 state): a forward write pass that records, per write
+// event, the row it replaced ([chain][T][W][d_v]); the write and read events
+// of every epoch sorted together by slot; the reverse pass.
+hipError_t launch_tp_forward_tape(const Shape &s, const uint32_t *rec, void *ws, const void *v,
+                                  bool bf16, float *M, float *tape, hipStream_t st);
+hipError_t launch_tp_sort_merged(const Shape &s, const uint32_t *rec, void *ws, TPEntry *out,
+                                 uint64_t *tmpA, uint64_t *tmpB, hipStream_t st);
+size_t tp_backward_workspace_bytes(const Shape &s);  // beyond the forward's workspace
+hipError_t launch_tp_backward(const Shape &s, const uint32_t *rec, void *fwd_ws, void *bwd_ws,
+                              const void *v, bool bf16, const float *M0, const float *Minit,
+                              const float *dy, const float *dMT, const float *alpha,
+                              const float *beta, float *dkp, float *dqp, float *dv, float *dalpha,
+                              float *dbeta, float *dMinit, float *dM0, hipStream_t st);
 
 }  // namespace sdm

@@ -374,6 +374,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
                     rec[lane] = ok ? n : 0u;
                     reinterpret_cast<float *>(rec)[a.Wp + lane] = ok ? al * (1.0f - c) : 1.0f;
                     reinterpret_cast<float *>(rec)[2 * a.Wp + lane] = ok ? c : 0.0f;
+                    reinterpret_cast<float *>(rec)[3 * a.Wp + 2 * a.Rp + lane] = ok ? w : 0.0f;
                 }
             } else {
                 if (lane < a.Rp) {

@@ -59,8 +59,8 @@ def test_create_destroy_and_workspace_size():
     assert st == 0 and h.value
     n = ctypes.c_size_t()
     assert L.sdm_workspace_size(h, 2, 100, sdm.F32, sdm.AUTO, ctypes.byref(n)) == 0
-    # one record per (chain, token): 3*64 + 2*64 dwords
-    assert n.value >= 2 * 2 * 100 * (3 * 64 + 2 * 64) * 4
+    # one record per (chain, token): 4*64 + 2*64 dwords
+    assert n.value >= 2 * 2 * 100 * (4 * 64 + 2 * 64) * 4
     assert L.sdm_workspace_size(h, 0, 100, sdm.F32, sdm.AUTO, ctypes.byref(n)) == 1
     assert L.sdm_workspace_size(h, 2, 0, sdm.F32, sdm.AUTO, ctypes.byref(n)) == 1
     assert L.sdm_workspace_size(h, 2, 10, 7, sdm.AUTO, ctypes.byref(n)) == 1
