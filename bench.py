@@ -138,10 +138,24 @@ def decode(args, wl):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
+    # the same steps captured once in a HIP graph and replayed (no per-launch
+    # host overhead): what a serving loop that replays captured steps pays
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for t in range(warm, warm + steps):
+            core.forward(*toks[t], variant=var, y=y, M=M, workspace=ws, cont=True)
+    g.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us_graph = e0.elapsed_time(e1) * 1e3 / steps
     print(json.dumps({
         "metric": "SDM decode step latency (one token for each of B sequences, state continued)",
         "value": us, "unit": "us/step", "higher_is_better": False, "n_gpus": 1, "steps": steps,
         "warmup": warm, "head_tokens_per_s": wl.B * wl.H / (us * 1e-6),
+        "graph_replay_us_per_step": us_graph,
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "sqrtN": wl.sqrtN, "d_v": wl.d_v,
                    "W": wl.W, "R": wl.R, "prefill_tokens": prefix,
                    "schedule": sdm.variant_name(core, wl.B, 1, dt_code, var)},
