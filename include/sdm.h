@@ -80,6 +80,9 @@ typedef enum { SDM_F32 = 0, SDM_BF16 = 1 } sdm_dtype;
  *   TIMEPAR  time-parallel: (slot, t) events sorted per chunk of tokens and
  *            a per-slot scan of the affine map M <- a*M + c*v.
  *   AUTO     the library's choice for the shape.
+ * With one token per sequence (T == 1: a decode step) there is no order
+ * across tokens to schedule, and TIMEPAR runs a single kernel instead of the
+ * sort and scan: the token's writes, then its reads of the updated rows.
  */
 typedef enum {
     SDM_VARIANT_AUTO = 0,

@@ -22,7 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsdm.so")
 
-SOURCES = ["select.hip", "init.hip", "plan.hip", "rw_serial.hip", "rw_timepar.hip", "backward.hip",
+SOURCES = ["select.hip", "init.hip", "plan.hip", "rw_serial.hip", "rw_timepar.hip", "decode.hip",
+           "backward.hip",
            "sdm_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "hipcc")

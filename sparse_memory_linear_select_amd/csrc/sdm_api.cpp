@@ -418,9 +418,11 @@ sdm_status sdm_prepare(sdm_handle h, int B, int64_t T, const void *kp, const voi
                            alpha, beta, hs);
     if (e != hipSuccess) return hip_fail(e, "select launch");
     if (var == SDM_VARIANT_TIMEPAR) {
-        char *tp = static_cast<char *>(workspace) + records_bytes(h, B, T);
-        e = sdm::launch_tp_prepare(s, rec, tp, hs);
-        if (e != hipSuccess) return hip_fail(e, "time-parallel sort launch");
+        if (!sdm::decode_supported(s)) {  // one token: nothing to sort (see sdm_apply)
+            char *tp = static_cast<char *>(workspace) + records_bytes(h, B, T);
+            e = sdm::launch_tp_prepare(s, rec, tp, hs);
+            if (e != hipSuccess) return hip_fail(e, "time-parallel sort launch");
+        }
     } else if (sdm::rw_serial_supported(s)) {
         e = sdm::launch_plan(s, rec, sdm::rw_serial_depth(), hs);
         if (e != hipSuccess) return hip_fail(e, "plan launch");
@@ -444,6 +446,13 @@ sdm_status sdm_apply(sdm_handle h, int B, int64_t T, const void *v, sdm_dtype dt
     const sdm::Shape s = shape_of(h, B, T);
     const hipStream_t hs = (hipStream_t)stream;
     const uint32_t *rec = static_cast<const uint32_t *>(workspace);
+    if (var == SDM_VARIANT_TIMEPAR && sdm::decode_supported(s)) {
+        // one token per sequence: its writes, then its reads, in one kernel
+        const hipError_t e =
+            sdm::launch_rw_decode(s, rec, v, dtype == SDM_BF16, y, M, h->state_bf16, hs);
+        if (e != hipSuccess) return hip_fail(e, "one-token write/read launch");
+        return SDM_OK;
+    }
     if (var == SDM_VARIANT_TIMEPAR) {
         char *tp = static_cast<char *>(workspace) + records_bytes(h, B, T);
         const hipError_t e =

@@ -96,6 +96,12 @@ hipError_t launch_tp_apply(const Shape &s, const uint32_t *rec, void *ws, const 
                            bool bf16, float *y, void *M, bool state_bf16, hipStream_t st,
                            int ep0 = 0, int ep1 = -1);
 
+// One-token step (T == 1): the token's writes, then its reads, in one kernel
+// (d_v % 4 == 0 and one chain's state within 2^31 bytes).
+bool decode_supported(const Shape &s);
+hipError_t launch_rw_decode(const Shape &s, const uint32_t *rec, const void *v, bool bf16,
+                            float *y, void *M, bool state_bf16, hipStream_t st);
+
 // Backward (float32 state): a forward write pass that records, per write
 // event, the row it replaced ([chain][T][W][d_v]); the write and read events
 // of every epoch sorted together by slot; the reverse pass.
