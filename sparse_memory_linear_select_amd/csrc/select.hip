@@ -15,6 +15,9 @@
 //            column of ranks are already in order); the other two are sorted
 //            across lanes, and columns are merged pairwise keeping the top 64;
 //   weights  softmax over the K selected scores.
+// The compare-exchange steps form each list's dependent chain; for sqrtN <=
+// 256 their lane exchanges use DPP and the gfx950 permlane swaps (a few
+// cycles) rather than the LDS crossbar.
 // The product-key identity (select within each half first, then among sums of
 // survivors) is stated in the explainer "Sparse Delta Memory：通过稀疏性扩展线性
 // RNN 的状态容量", §3.1 step 1, and in "Technical Summary: Sparse Delta Memory
@@ -63,6 +66,78 @@ __device__ __forceinline__ uint64_t shl64(uint64_t v, int src)
     return ((uint64_t)hi << 32) | lo;
 }
 
+// Lane exchanges inside the compare-exchange networks.  These form the
+// dependent chain of a selection, so they avoid the LDS crossbar
+// (ds_bpermute) where a lane pattern allows:
+//   m = 1, 2   one DPP quad permutation;
+//   m = 4, 8   two DPP moves within the 16-lane row (xor 3 then the half-row
+//              mirror, xor 7; the half-row mirror then the row mirror, xor 15);
+//   m = 16, 32 the gfx950 permlane swaps, which give every lane both values
+//              of its pair {l, l ^ m}: (lower lane's, upper lane's).
+// m is a constant once the callers' loops are unrolled; the DPP controls must
+// be immediates, hence the switch.
+__device__ __forceinline__ uint32_t dpp_xor(uint32_t x, int m)
+{
+    switch (m) {
+    case 1: return __builtin_amdgcn_update_dpp(0u, x, 0xB1, 0xF, 0xF, false);
+    case 2: return __builtin_amdgcn_update_dpp(0u, x, 0x4E, 0xF, 0xF, false);
+    case 4:
+        return __builtin_amdgcn_update_dpp(0u, __builtin_amdgcn_update_dpp(0u, x, 0x1B, 0xF, 0xF, false),
+                                           0x141, 0xF, 0xF, false);
+    default:
+        return __builtin_amdgcn_update_dpp(0u, __builtin_amdgcn_update_dpp(0u, x, 0x141, 0xF, 0xF, false),
+                                           0x140, 0xF, 0xF, false);
+    }
+}
+
+__device__ __forceinline__ void pair_vals(uint32_t x, int m, uint32_t &lo, uint32_t &hi)
+{
+    if (m == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        lo = r[0];
+        hi = r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        lo = r[0];
+        hi = r[1];
+    }
+}
+
+__device__ __forceinline__ uint64_t dpp_xor64(uint64_t v, int m)
+{
+    return ((uint64_t)dpp_xor((uint32_t)(v >> 32), m) << 32) | dpp_xor((uint32_t)v, m);
+}
+
+__device__ __forceinline__ void pair_vals64(uint64_t v, int m, uint64_t &lo, uint64_t &hi)
+{
+    uint32_t l0, h0, l1, h1;
+    pair_vals((uint32_t)v, m, l0, h0);
+    pair_vals((uint32_t)(v >> 32), m, l1, h1);
+    lo = ((uint64_t)l1 << 32) | l0;
+    hi = ((uint64_t)h1 << 32) | h0;
+}
+
+// This lane's key after a compare-exchange with lane ^ m: the larger key of
+// the pair if keep_max, else the smaller (one compare; equal keys: either).
+// DPP = false: every exchange through ds_bpermute (the large-E kernels, whose
+// networks are too long for the compiler to unroll and fold the lane
+// patterns into immediates).
+template <bool DPP>
+__device__ __forceinline__ uint64_t xchg_max(uint64_t k, int m, bool keep_max)
+{
+    if (!DPP) {
+        const uint64_t o = shx64(k, m);
+        return ((o > k) == keep_max) ? o : k;
+    }
+    if (m >= 16) {
+        uint64_t lo, hi;
+        pair_vals64(k, m, lo, hi);
+        return ((lo > hi) == keep_max) ? lo : hi;
+    }
+    const uint64_t o = dpp_xor64(k, m);
+    return ((o > k) == keep_max) ? o : k;
+}
+
 // Orders LDS traffic between the lanes of one wavefront.
 __device__ __forceinline__ void wave_sync()
 {
@@ -86,7 +161,7 @@ __device__ __forceinline__ float load_elem(const void *x, bool bf16, int64_t i)
 }
 
 // Sort 64*E keys of each of two halves, descending; element e = lane*E + r.
-template <int E>
+template <int E, bool DPP>
 __device__ __forceinline__ void sort_halves_desc(uint64_t (&k1)[E], uint64_t (&k2)[E], int lane)
 {
     constexpr int n = 64 * E;
@@ -98,15 +173,17 @@ __device__ __forceinline__ void sort_halves_desc(uint64_t (&k1)[E], uint64_t (&k
 #pragma unroll
                 for (int r = 0; r < E; r++) {
                     if ((r & j) == 0) {
+                        // one compare per exchange: swap when the pair is out
+                        // of the step's direction (equal keys: either way)
                         const int e = lane * E + r;
                         const bool desc = (e & kk) == 0;
                         uint64_t a = k1[r], b = k1[r | j];
-                        bool sw = desc ? (a < b) : (a > b);
+                        bool sw = (a < b) == desc;
                         k1[r] = sw ? b : a;
                         k1[r | j] = sw ? a : b;
                         a = k2[r];
                         b = k2[r | j];
-                        sw = desc ? (a < b) : (a > b);
+                        sw = (a < b) == desc;
                         k2[r] = sw ? b : a;
                         k2[r | j] = sw ? a : b;
                     }
@@ -117,11 +194,8 @@ __device__ __forceinline__ void sort_halves_desc(uint64_t (&k1)[E], uint64_t (&k
                 for (int r = 0; r < E; r++) {
                     const int e = lane * E + r;
                     const bool keep_max = ((e & j) == 0) == ((e & kk) == 0);
-                    const uint64_t o1 = shx64(k1[r], lm);
-                    const uint64_t o2 = shx64(k2[r], lm);
-                    const uint64_t m1 = k1[r], m2 = k2[r];
-                    k1[r] = keep_max ? (m1 > o1 ? m1 : o1) : (m1 < o1 ? m1 : o1);
-                    k2[r] = keep_max ? (m2 > o2 ? m2 : o2) : (m2 < o2 ? m2 : o2);
+                    k1[r] = xchg_max<DPP>(k1[r], lm, keep_max);
+                    k2[r] = xchg_max<DPP>(k2[r], lm, keep_max);
                 }
             }
         }
@@ -135,10 +209,32 @@ __device__ __forceinline__ bool before(uint64_t ka, uint32_t na, uint64_t kb, ui
     return ka > kb || (ka == kb && na < nb);
 }
 
+// Compare-exchange of (k, n) with lane ^ m: this lane keeps the entry of the
+// pair that comes first if keep_first, else the other one.
+template <bool DPP>
 __device__ __forceinline__ void ce_lane(uint64_t &k, uint32_t &n, int m, bool keep_first)
 {
-    const uint64_t ok = shx64(k, m);
-    const uint32_t on = shx(n, m);
+    if (!DPP) {
+        const uint64_t ok = shx64(k, m);
+        const uint32_t on = shx(n, m);
+        if (keep_first != before(k, n, ok, on)) {
+            k = ok;
+            n = on;
+        }
+        return;
+    }
+    if (m >= 16) {
+        uint64_t lk, uk;
+        uint32_t ln, un;
+        pair_vals64(k, m, lk, uk);
+        pair_vals(n, m, ln, un);
+        const bool take_lo = before(lk, ln, uk, un) == keep_first;
+        k = take_lo ? lk : uk;
+        n = take_lo ? ln : un;
+        return;
+    }
+    const uint64_t ok = dpp_xor64(k, m);
+    const uint32_t on = dpp_xor(n, m);
     const bool mine_first = before(k, n, ok, on);
     if (keep_first != mine_first) {
         k = ok;
@@ -147,17 +243,19 @@ __device__ __forceinline__ void ce_lane(uint64_t &k, uint32_t &n, int m, bool ke
 }
 
 // Sort one 64-entry column (one entry per lane) in canonical order.
+template <bool DPP>
 __device__ __forceinline__ void col_sort(uint64_t &k, uint32_t &n, int lane)
 {
 #pragma unroll
     for (int kk = 2; kk <= 64; kk <<= 1) {
 #pragma unroll
         for (int j = kk >> 1; j > 0; j >>= 1)
-            ce_lane(k, n, j, ((lane & j) == 0) == ((lane & kk) == 0));
+            ce_lane<DPP>(k, n, j, ((lane & j) == 0) == ((lane & kk) == 0));
     }
 }
 
 // (ka, na) <- first 64 of two sorted columns, sorted.
+template <bool DPP>
 __device__ __forceinline__ void col_merge(uint64_t &ka, uint32_t &na, uint64_t kb, uint32_t nb,
                                           int lane)
 {
@@ -168,14 +266,15 @@ __device__ __forceinline__ void col_merge(uint64_t &ka, uint32_t &na, uint64_t k
         na = rn;
     }
 #pragma unroll
-    for (int j = 32; j > 0; j >>= 1) ce_lane(ka, na, j, (lane & j) == 0);
+    for (int j = 32; j > 0; j >>= 1) ce_lane<DPP>(ka, na, j, (lane & j) == 0);
 }
 
 // Sort one 64-entry bitonic column (falling, then rising) in canonical order.
+template <bool DPP>
 __device__ __forceinline__ void col_bitonic(uint64_t &k, uint32_t &n, int lane)
 {
 #pragma unroll
-    for (int j = 32; j > 0; j >>= 1) ce_lane(k, n, j, (lane & j) == 0);
+    for (int j = 32; j > 0; j >>= 1) ce_lane<DPP>(k, n, j, (lane & j) == 0);
 }
 
 // Pair of per-half ranks (a << 8 | b) held by `lane` in candidate column `col`
@@ -241,6 +340,7 @@ template <int E>
 __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
 {
     constexpr int E2 = 5;  // candidate columns: 5*64 >= 280 pairs for K = 64
+    constexpr bool kDpp = E <= 4;  // lane exchanges by DPP / permlane (see xchg_max)
     __shared__ uint16_t tab[2][kTabMax];
     __shared__ int tabn[2];
     __shared__ float sv[4][2][64];
@@ -287,7 +387,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
                 k2[r] = 0;
             }
         }
-        sort_halves_desc<E>(k1, k2, lane);
+        sort_halves_desc<E, kDpp>(k1, k2, lane);
 #pragma unroll
         for (int r = 0; r < E; r++) {
             const int e = lane * E + r;
@@ -318,10 +418,10 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
             }
         }
         // columns 0, 1 sorted; 2 bitonic; 3, 4 unsorted (K-uniform branches)
-        if (K >= 2) col_merge(ck[0], cn[0], ck[1], cn[1], lane);
+        if (K >= 2) col_merge<kDpp>(ck[0], cn[0], ck[1], cn[1], lane);
         if (K >= 4) {
-            col_bitonic(ck[2], cn[2], lane);
-            col_merge(ck[0], cn[0], ck[2], cn[2], lane);
+            col_bitonic<kDpp>(ck[2], cn[2], lane);
+            col_merge<kDpp>(ck[0], cn[0], ck[2], cn[2], lane);
         }
         if (rest > 0) {
             // Columns 0-2 now hold the first 64 of hooks 0 and 1, sorted.  A
@@ -359,8 +459,8 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
                     sk = ((uint64_t)xh[lane] << 32) | xl[lane];
                     sn = xn[lane];
                 }
-                col_sort(sk, sn, lane);
-                col_merge(ck[0], cn[0], sk, sn, lane);
+                col_sort<kDpp>(sk, sn, lane);
+                col_merge<kDpp>(ck[0], cn[0], sk, sn, lane);
             }
         }
         wave_sync();  // sv/si are rewritten by the next item
