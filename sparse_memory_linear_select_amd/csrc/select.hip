@@ -346,7 +346,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
     __shared__ float sv[4][2][64];
     __shared__ uint32_t si[4][2][64];
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
     // candidate columns of both lists
     if (wv == 0) {
@@ -360,18 +360,21 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
     __syncthreads();
 
     const int S = a.sqrtN;
-    const int64_t items = a.lists * a.n_ht;
-    for (int64_t it = (int64_t)blockIdx.x * 4 + wv; it < items; it += (int64_t)gridDim.x * 4) {
-        const int list = a.lists == 2 ? (int)(it & 1) : 0;
-        int64_t ht = a.lists == 2 ? it >> 1 : it;
-        if (a.tn != a.T) {  // position in the token range -> (b*T + t)*H + h
-            const int64_t per_b = a.tn * a.H;
-            const int64_t bb = ht / per_b;
-            ht += bb * (a.T - a.tn) * a.H + a.t0 * a.H;
+    // head-token arithmetic in 32 bits (B*T*H < 2^31) on wave-uniform values,
+    // so that it runs on the scalar unit
+    const uint32_t T32 = (uint32_t)a.T, H32 = (uint32_t)a.H;
+    const uint32_t tn32 = (uint32_t)a.tn, t032 = (uint32_t)a.t0;
+    const uint32_t items = (uint32_t)(a.lists * a.n_ht);
+    for (uint32_t it = blockIdx.x * 4u + (uint32_t)wv; it < items; it += gridDim.x * 4u) {
+        const int list = a.lists == 2 ? (int)(it & 1u) : 0;
+        uint32_t ht = a.lists == 2 ? it >> 1 : it;
+        if (tn32 != T32) {  // position in the token range -> (b*T + t)*H + h
+            const uint32_t bb = ht / (tn32 * H32);
+            ht += bb * (T32 - tn32) * H32 + t032 * H32;
         }
         const int K = list ? a.R : a.W;
         const void *x = list ? a.qp : a.kp;
-        const int64_t base = ht * 2 * S;
+        const int64_t base = (int64_t)ht * 2 * S;
 
         // ---- stage 1: sort each half, keep the first K ----
         uint64_t k1[E], k2[E];
@@ -480,24 +483,25 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
 
         if (a.hist != nullptr) {
             // write-slot utilisation: one count per selected slot of head h
-            if (lane < K) atomicAdd(&a.hist[(int64_t)(ht % a.H) * a.sqrtN * a.sqrtN + n], 1u);
+            if (lane < K) atomicAdd(&a.hist[(int64_t)(ht % H32) * a.sqrtN * a.sqrtN + n], 1u);
         } else if (a.rec == nullptr) {
             if (lane < K) {
+                const int64_t o = (int64_t)ht * K + lane;
                 if (list == 0) {
-                    a.Iw[ht * K + lane] = (int32_t)n;
-                    a.kw[ht * K + lane] = w;
+                    a.Iw[o] = (int32_t)n;
+                    a.kw[o] = w;
                 } else {
-                    a.Ir[ht * K + lane] = (int32_t)n;
-                    a.qw[ht * K + lane] = w;
+                    a.Ir[o] = (int32_t)n;
+                    a.qw[o] = w;
                 }
             }
         } else {
             // record of chain (b, h) at token t; ht = (b*T + t)*H + h
-            const int64_t bt = ht / a.H;
-            const int h = (int)(ht - bt * a.H);
-            const int64_t b = bt / a.T;
-            const int64_t t = bt - b * a.T;
-            uint32_t *rec = a.rec + (((b * a.H + h) * a.T) + t) * a.rec_dwords;
+            const uint32_t bt = ht / H32;
+            const uint32_t h = ht - bt * H32;
+            const uint32_t b = bt / T32;
+            const uint32_t t = bt - b * T32;
+            uint32_t *rec = a.rec + (((int64_t)(b * H32 + h) * T32) + t) * a.rec_dwords;
             if (list == 0) {
                 if (lane < a.Wp) {
                     const float al = a.alpha[ht], be = a.beta[ht];
