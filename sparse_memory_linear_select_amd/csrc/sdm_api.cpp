@@ -139,24 +139,35 @@ sdm_status check_variant_and_ws(const sdm_ctx *h, int B, int64_t T, sdm_variant 
     return SDM_OK;
 }
 
-// The side stream of the current device, created on first use (caller holds
-// h->mu).  Null if it cannot be created.
-SideStream *side_stream(sdm_ctx *h, hipError_t *err)
+// The side stream of the device that `hs` belongs to (the current device
+// for the null stream), created on first use (caller holds h->mu).  Null if
+// it cannot be created.
+SideStream *side_stream(sdm_ctx *h, hipStream_t hs, hipError_t *err)
 {
-    int dev = -1;
-    *err = hipGetDevice(&dev);
+    int cur = -1, dev = -1;
+    *err = hipGetDevice(&cur);
     if (*err != hipSuccess) return nullptr;
+    dev = cur;
+    if (hs) {
+        *err = hipStreamGetDevice(hs, &dev);
+        if (*err != hipSuccess) return nullptr;
+    }
     if (dev < 0 || dev >= kMaxDevices) {
         *err = hipErrorInvalidDevice;
         return nullptr;
     }
     SideStream &ss = h->side[dev];
     if (ss.s) return &ss;
+    if (dev != cur) {  // streams and events are created on the current device
+        *err = hipSetDevice(dev);
+        if (*err != hipSuccess) return nullptr;
+    }
     SideStream n;
     *err = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking);
     if (*err == hipSuccess) *err = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
     for (int c = 0; c < kMaxChunks && *err == hipSuccess; c++)
         *err = hipEventCreateWithFlags(&n.ready[c], hipEventDisableTiming);
+    if (dev != cur) (void)hipSetDevice(cur);
     if (*err != hipSuccess) {
         for (hipEvent_t e : n.ready)
             if (e) (void)hipEventDestroy(e);
@@ -195,7 +206,7 @@ sdm_status forward_pipelined(sdm_ctx *h, const sdm::Shape &s, const void *kp, co
 {
     std::lock_guard<std::mutex> lock(h->mu);
     hipError_t e;
-    SideStream *ss = side_stream(h, &e);
+    SideStream *ss = side_stream(h, hs, &e);
     if (!ss) return hip_fail(e, "helper stream creation");
     const int E = sdm::tp_epoch_len(s);
     const int nep = (int)((s.T + E - 1) / E);

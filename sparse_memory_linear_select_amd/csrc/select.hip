@@ -364,10 +364,10 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
     // so that it runs on the scalar unit
     const uint32_t T32 = (uint32_t)a.T, H32 = (uint32_t)a.H;
     const uint32_t tn32 = (uint32_t)a.tn, t032 = (uint32_t)a.t0;
-    const uint32_t items = (uint32_t)(a.lists * a.n_ht);
-    for (uint32_t it = blockIdx.x * 4u + (uint32_t)wv; it < items; it += gridDim.x * 4u) {
+    const uint64_t items = (uint64_t)a.lists * (uint64_t)a.n_ht;  // < 2^32, but it + stride may not be
+    for (uint64_t it = blockIdx.x * 4u + (uint32_t)wv; it < items; it += gridDim.x * 4u) {
         const int list = a.lists == 2 ? (int)(it & 1u) : 0;
-        uint32_t ht = a.lists == 2 ? it >> 1 : it;
+        uint32_t ht = (uint32_t)(a.lists == 2 ? it >> 1 : it);
         if (tn32 != T32) {  // position in the token range -> (b*T + t)*H + h
             const uint32_t bb = ht / (tn32 * H32);
             ht += bb * (T32 - tn32) * H32 + t032 * H32;
