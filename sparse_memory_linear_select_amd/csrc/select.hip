@@ -15,9 +15,9 @@
 //            column of ranks are already in order); the other two are sorted
 //            across lanes, and columns are merged pairwise keeping the top 64;
 //   weights  softmax over the K selected scores.
-// The compare-exchange steps form each list's dependent chain; for sqrtN <=
-// 256 their lane exchanges use DPP and the gfx950 permlane swaps (a few
-// cycles) rather than the LDS crossbar.
+// The compare-exchange steps form each list's dependent chain; their lane
+// exchanges use DPP and the gfx950 permlane swaps (a few cycles) rather than
+// the LDS crossbar.
 // The product-key identity (select within each half first, then among sums of
 // survivors) is stated in the explainer "Sparse Delta Memory：通过稀疏性扩展线性
 // RNN 的状态容量", §3.1 step 1, and in "Technical Summary: Sparse Delta Memory
@@ -44,20 +44,9 @@ __device__ __forceinline__ float ord2f(uint32_t o)
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-__device__ __forceinline__ uint32_t shx(uint32_t v, int m)
-{
-    return (uint32_t)__shfl_xor((int)v, m, 64);
-}
-
 __device__ __forceinline__ uint32_t shl(uint32_t v, int src)
 {
     return (uint32_t)__shfl((int)v, src, 64);
-}
-
-__device__ __forceinline__ uint64_t shx64(uint64_t v, int m)
-{
-    const uint32_t lo = shx((uint32_t)v, m), hi = shx((uint32_t)(v >> 32), m);
-    return ((uint64_t)hi << 32) | lo;
 }
 
 __device__ __forceinline__ uint64_t shl64(uint64_t v, int src)
@@ -68,25 +57,25 @@ __device__ __forceinline__ uint64_t shl64(uint64_t v, int src)
 
 // Lane exchanges inside the compare-exchange networks.  These form the
 // dependent chain of a selection, so they avoid the LDS crossbar
-// (ds_bpermute) where a lane pattern allows:
+// (ds_bpermute):
 //   m = 1, 2   one DPP quad permutation;
-//   m = 4, 8   two DPP moves within the 16-lane row (xor 3 then the half-row
-//              mirror, xor 7; the half-row mirror then the row mirror, xor 15);
+//   m = 4      row_shl:4 into banks 0 and 2 (lanes with bit 2 clear), then
+//              row_shr:4 into banks 1 and 3 (bank = 4 lanes of a 16-lane row);
+//   m = 8      row_ror:8 (a rotation by half of the 16-lane row);
 //   m = 16, 32 the gfx950 permlane swaps, which give every lane both values
 //              of its pair {l, l ^ m}: (lower lane's, upper lane's).
-// m is a constant once the callers' loops are unrolled; the DPP controls must
-// be immediates, hence the switch.
+// m is a compile-time constant at every call (the networks are instantiated
+// step by step); the DPP controls must be immediates, hence the switch.
 __device__ __forceinline__ uint32_t dpp_xor(uint32_t x, int m)
 {
     switch (m) {
     case 1: return __builtin_amdgcn_update_dpp(0u, x, 0xB1, 0xF, 0xF, false);
     case 2: return __builtin_amdgcn_update_dpp(0u, x, 0x4E, 0xF, 0xF, false);
-    case 4:
-        return __builtin_amdgcn_update_dpp(0u, __builtin_amdgcn_update_dpp(0u, x, 0x1B, 0xF, 0xF, false),
-                                           0x141, 0xF, 0xF, false);
-    default:
-        return __builtin_amdgcn_update_dpp(0u, __builtin_amdgcn_update_dpp(0u, x, 0x141, 0xF, 0xF, false),
-                                           0x140, 0xF, 0xF, false);
+    case 4: {
+        const uint32_t y = __builtin_amdgcn_update_dpp(x, x, 0x104, 0xF, 0x5, false);
+        return __builtin_amdgcn_update_dpp(y, x, 0x114, 0xF, 0xA, false);
+    }
+    default: return __builtin_amdgcn_update_dpp(0u, x, 0x128, 0xF, 0xF, false);
     }
 }
 
@@ -119,16 +108,8 @@ __device__ __forceinline__ void pair_vals64(uint64_t v, int m, uint64_t &lo, uin
 
 // This lane's key after a compare-exchange with lane ^ m: the larger key of
 // the pair if keep_max, else the smaller (one compare; equal keys: either).
-// DPP = false: every exchange through ds_bpermute (the large-E kernels, whose
-// networks are too long for the compiler to unroll and fold the lane
-// patterns into immediates).
-template <bool DPP>
 __device__ __forceinline__ uint64_t xchg_max(uint64_t k, int m, bool keep_max)
 {
-    if (!DPP) {
-        const uint64_t o = shx64(k, m);
-        return ((o > k) == keep_max) ? o : k;
-    }
     if (m >= 16) {
         uint64_t lo, hi;
         pair_vals64(k, m, lo, hi);
@@ -160,46 +141,61 @@ __device__ __forceinline__ float load_elem(const void *x, bool bf16, int64_t i)
     return ((const float *)x)[i];
 }
 
-// Sort 64*E keys of each of two halves, descending; element e = lane*E + r.
-template <int E, bool DPP>
-__device__ __forceinline__ void sort_halves_desc(uint64_t (&k1)[E], uint64_t (&k2)[E], int lane)
+// Step (KK, J) of the bitonic network over both halves (descending); the
+// steps are instantiated one by one so that every lane pattern is a
+// compile-time constant (the DPP controls must be immediates).
+template <int E, int KK, int J>
+__device__ __forceinline__ void sort_step(uint64_t (&k1)[E], uint64_t (&k2)[E], int lane)
 {
-    constexpr int n = 64 * E;
+    if constexpr (J < E) {  // partner in the same lane
 #pragma unroll
-    for (int kk = 2; kk <= n; kk <<= 1) {
-#pragma unroll
-        for (int j = kk >> 1; j > 0; j >>= 1) {
-            if (j < E) {  // partner in the same lane
-#pragma unroll
-                for (int r = 0; r < E; r++) {
-                    if ((r & j) == 0) {
-                        // one compare per exchange: swap when the pair is out
-                        // of the step's direction (equal keys: either way)
-                        const int e = lane * E + r;
-                        const bool desc = (e & kk) == 0;
-                        uint64_t a = k1[r], b = k1[r | j];
-                        bool sw = (a < b) == desc;
-                        k1[r] = sw ? b : a;
-                        k1[r | j] = sw ? a : b;
-                        a = k2[r];
-                        b = k2[r | j];
-                        sw = (a < b) == desc;
-                        k2[r] = sw ? b : a;
-                        k2[r | j] = sw ? a : b;
-                    }
-                }
-            } else {  // partner in lane ^ (j / E), same register
-                const int lm = j / E;
-#pragma unroll
-                for (int r = 0; r < E; r++) {
-                    const int e = lane * E + r;
-                    const bool keep_max = ((e & j) == 0) == ((e & kk) == 0);
-                    k1[r] = xchg_max<DPP>(k1[r], lm, keep_max);
-                    k2[r] = xchg_max<DPP>(k2[r], lm, keep_max);
-                }
+        for (int r = 0; r < E; r++) {
+            if ((r & J) == 0) {
+                // one compare per exchange: swap when the pair is out of the
+                // step's direction (equal keys: either way)
+                const int e = lane * E + r;
+                const bool desc = (e & KK) == 0;
+                uint64_t a = k1[r], b = k1[r | J];
+                bool sw = (a < b) == desc;
+                k1[r] = sw ? b : a;
+                k1[r | J] = sw ? a : b;
+                a = k2[r];
+                b = k2[r | J];
+                sw = (a < b) == desc;
+                k2[r] = sw ? b : a;
+                k2[r | J] = sw ? a : b;
             }
         }
+    } else {  // partner in lane ^ (J / E), same register
+#pragma unroll
+        for (int r = 0; r < E; r++) {
+            const int e = lane * E + r;
+            const bool keep_max = ((e & J) == 0) == ((e & KK) == 0);
+            k1[r] = xchg_max(k1[r], J / E, keep_max);
+            k2[r] = xchg_max(k2[r], J / E, keep_max);
+        }
     }
+}
+
+template <int E, int KK, int J>
+__device__ __forceinline__ void sort_steps(uint64_t (&k1)[E], uint64_t (&k2)[E], int lane)
+{
+    sort_step<E, KK, J>(k1, k2, lane);
+    if constexpr (J > 1) sort_steps<E, KK, J / 2>(k1, k2, lane);
+}
+
+template <int E, int KK>
+__device__ __forceinline__ void sort_stages(uint64_t (&k1)[E], uint64_t (&k2)[E], int lane)
+{
+    sort_steps<E, KK, KK / 2>(k1, k2, lane);
+    if constexpr (KK < 64 * E) sort_stages<E, 2 * KK>(k1, k2, lane);
+}
+
+// Sort 64*E keys of each of two halves, descending; element e = lane*E + r.
+template <int E>
+__device__ __forceinline__ void sort_halves_desc(uint64_t (&k1)[E], uint64_t (&k2)[E], int lane)
+{
+    sort_stages<E, 2>(k1, k2, lane);
 }
 
 // Does candidate (ka, na) come before (kb, nb)?  Higher exact score first,
@@ -211,18 +207,8 @@ __device__ __forceinline__ bool before(uint64_t ka, uint32_t na, uint64_t kb, ui
 
 // Compare-exchange of (k, n) with lane ^ m: this lane keeps the entry of the
 // pair that comes first if keep_first, else the other one.
-template <bool DPP>
 __device__ __forceinline__ void ce_lane(uint64_t &k, uint32_t &n, int m, bool keep_first)
 {
-    if (!DPP) {
-        const uint64_t ok = shx64(k, m);
-        const uint32_t on = shx(n, m);
-        if (keep_first != before(k, n, ok, on)) {
-            k = ok;
-            n = on;
-        }
-        return;
-    }
     if (m >= 16) {
         uint64_t lk, uk;
         uint32_t ln, un;
@@ -243,19 +229,34 @@ __device__ __forceinline__ void ce_lane(uint64_t &k, uint32_t &n, int m, bool ke
 }
 
 // Sort one 64-entry column (one entry per lane) in canonical order.
-template <bool DPP>
+template <int KK, int J>
+__device__ __forceinline__ void col_sort_steps(uint64_t &k, uint32_t &n, int lane)
+{
+    ce_lane(k, n, J, ((lane & J) == 0) == ((lane & KK) == 0));
+    if constexpr (J > 1) col_sort_steps<KK, J / 2>(k, n, lane);
+}
+
+template <int KK>
+__device__ __forceinline__ void col_sort_stages(uint64_t &k, uint32_t &n, int lane)
+{
+    col_sort_steps<KK, KK / 2>(k, n, lane);
+    if constexpr (KK < 64) col_sort_stages<2 * KK>(k, n, lane);
+}
+
+// Bitonic clean-up of one 64-entry column: steps 32, 16, ..., 1.
+template <int J>
+__device__ __forceinline__ void col_clean(uint64_t &k, uint32_t &n, int lane)
+{
+    ce_lane(k, n, J, (lane & J) == 0);
+    if constexpr (J > 1) col_clean<J / 2>(k, n, lane);
+}
+
 __device__ __forceinline__ void col_sort(uint64_t &k, uint32_t &n, int lane)
 {
-#pragma unroll
-    for (int kk = 2; kk <= 64; kk <<= 1) {
-#pragma unroll
-        for (int j = kk >> 1; j > 0; j >>= 1)
-            ce_lane<DPP>(k, n, j, ((lane & j) == 0) == ((lane & kk) == 0));
-    }
+    col_sort_stages<2>(k, n, lane);
 }
 
 // (ka, na) <- first 64 of two sorted columns, sorted.
-template <bool DPP>
 __device__ __forceinline__ void col_merge(uint64_t &ka, uint32_t &na, uint64_t kb, uint32_t nb,
                                           int lane)
 {
@@ -265,16 +266,13 @@ __device__ __forceinline__ void col_merge(uint64_t &ka, uint32_t &na, uint64_t k
         ka = rk;
         na = rn;
     }
-#pragma unroll
-    for (int j = 32; j > 0; j >>= 1) ce_lane<DPP>(ka, na, j, (lane & j) == 0);
+    col_clean<32>(ka, na, lane);
 }
 
 // Sort one 64-entry bitonic column (falling, then rising) in canonical order.
-template <bool DPP>
 __device__ __forceinline__ void col_bitonic(uint64_t &k, uint32_t &n, int lane)
 {
-#pragma unroll
-    for (int j = 32; j > 0; j >>= 1) ce_lane<DPP>(k, n, j, (lane & j) == 0);
+    col_clean<32>(k, n, lane);
 }
 
 // Pair of per-half ranks (a << 8 | b) held by `lane` in candidate column `col`
@@ -340,7 +338,6 @@ template <int E>
 __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
 {
     constexpr int E2 = 5;  // candidate columns: 5*64 >= 280 pairs for K = 64
-    constexpr bool kDpp = E <= 4;  // lane exchanges by DPP / permlane (see xchg_max)
     __shared__ uint16_t tab[2][kTabMax];
     __shared__ int tabn[2];
     __shared__ float sv[4][2][64];
@@ -390,7 +387,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
                 k2[r] = 0;
             }
         }
-        sort_halves_desc<E, kDpp>(k1, k2, lane);
+        sort_halves_desc<E>(k1, k2, lane);
 #pragma unroll
         for (int r = 0; r < E; r++) {
             const int e = lane * E + r;
@@ -421,10 +418,10 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
             }
         }
         // columns 0, 1 sorted; 2 bitonic; 3, 4 unsorted (K-uniform branches)
-        if (K >= 2) col_merge<kDpp>(ck[0], cn[0], ck[1], cn[1], lane);
+        if (K >= 2) col_merge(ck[0], cn[0], ck[1], cn[1], lane);
         if (K >= 4) {
-            col_bitonic<kDpp>(ck[2], cn[2], lane);
-            col_merge<kDpp>(ck[0], cn[0], ck[2], cn[2], lane);
+            col_bitonic(ck[2], cn[2], lane);
+            col_merge(ck[0], cn[0], ck[2], cn[2], lane);
         }
         if (rest > 0) {
             // Columns 0-2 now hold the first 64 of hooks 0 and 1, sorted.  A
@@ -462,8 +459,8 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
                     sk = ((uint64_t)xh[lane] << 32) | xl[lane];
                     sn = xn[lane];
                 }
-                col_sort<kDpp>(sk, sn, lane);
-                col_merge<kDpp>(ck[0], cn[0], sk, sn, lane);
+                col_sort(sk, sn, lane);
+                col_merge(ck[0], cn[0], sk, sn, lane);
             }
         }
         wave_sync();  // sv/si are rewritten by the next item
