@@ -287,7 +287,7 @@ __device__ __forceinline__ void col_bitonic(uint64_t &k, uint32_t &n, int lane)
 //   3, 4  hooks h >= 2, concatenated               unsorted
 constexpr uint16_t kNoPair = 0xFFFF;
 
-__device__ __forceinline__ uint16_t hook_pair(int K, int col, int lane)
+__host__ __device__ inline uint16_t hook_pair(int K, int col, int lane)
 {
     if (col == 0) return lane < K ? (uint16_t)lane : kNoPair;
     if (col == 1) return lane + 1 < K ? (uint16_t)((lane + 1) << 8) : kNoPair;
@@ -311,7 +311,7 @@ __device__ __forceinline__ uint16_t hook_pair(int K, int col, int lane)
 }
 
 // Number of pruned pairs with both ranks >= 2 (columns 3 and 4).
-__device__ __forceinline__ int hook_rest(int K)
+__host__ __device__ inline int hook_rest(int K)
 {
     int n = 0;
     for (int h = 2; (h + 1) * (h + 1) <= K; h++) n += 2 * (K / (h + 1) - h) - 1;
@@ -332,29 +332,20 @@ struct SelArgs {
     const float *alpha, *beta;
     uint32_t *hist;  // [H][N] write-slot counts (histogram mode: write lists only)
     int lists;       // 2: write and read lists; 1: write lists only
+    // candidate columns of both lists (pairs a << 8 | b, laid out by hooks),
+    // computed on the host: lane l of column c reads entry c*64 + l
+    uint16_t tab[2][kTabMax];
+    int tabn[2];  // pairs with both ranks >= 2 (columns 3 and 4)
 };
 
 template <int E>
 __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
 {
     constexpr int E2 = 5;  // candidate columns: 5*64 >= 280 pairs for K = 64
-    __shared__ uint16_t tab[2][kTabMax];
-    __shared__ int tabn[2];
     __shared__ float sv[4][2][64];
     __shared__ uint32_t si[4][2][64];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-
-    // candidate columns of both lists
-    if (wv == 0) {
-        for (int list = 0; list < 2; list++) {
-            const int K = list ? a.R : a.W;
-#pragma unroll
-            for (int c = 0; c < E2; c++) tab[list][c * 64 + lane] = hook_pair(K, c, lane);
-            if (lane == 0) tabn[list] = hook_rest(K);
-        }
-    }
-    __syncthreads();
 
     const int S = a.sqrtN;
     // head-token arithmetic in 32 bits (B*T*H < 2^31) on wave-uniform values,
@@ -362,15 +353,21 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
     const uint32_t T32 = (uint32_t)a.T, H32 = (uint32_t)a.H;
     const uint32_t tn32 = (uint32_t)a.tn, t032 = (uint32_t)a.t0;
     const uint64_t items = (uint64_t)a.lists * (uint64_t)a.n_ht;  // < 2^32, but it + stride may not be
+    // items alternate between the lists and the stride is even, so a wave
+    // keeps one list: its candidate columns stay in registers
+    const int list = a.lists == 2 ? (wv & 1) : 0;
+    const int K = list ? a.R : a.W;
+    const void *x = list ? a.qp : a.kp;
+    const int rest = a.tabn[list];
+    uint16_t tabv[E2];
+#pragma unroll
+    for (int r = 0; r < E2; r++) tabv[r] = a.tab[list][r * 64 + lane];
     for (uint64_t it = blockIdx.x * 4u + (uint32_t)wv; it < items; it += gridDim.x * 4u) {
-        const int list = a.lists == 2 ? (int)(it & 1u) : 0;
         uint32_t ht = (uint32_t)(a.lists == 2 ? it >> 1 : it);
         if (tn32 != T32) {  // position in the token range -> (b*T + t)*H + h
             const uint32_t bb = ht / (tn32 * H32);
             ht += bb * (T32 - tn32) * H32 + t032 * H32;
         }
-        const int K = list ? a.R : a.W;
-        const void *x = list ? a.qp : a.kp;
         const int64_t base = (int64_t)ht * 2 * S;
 
         // ---- stage 1: sort each half, keep the first K ----
@@ -401,14 +398,13 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
         wave_sync();
 
         // ---- stage 2: exact sums of the pruned rank pairs ----
-        const int rest = tabn[list];
         uint64_t ck[E2];
         uint32_t cn[E2];
 #pragma unroll
         for (int r = 0; r < E2; r++) {
             ck[r] = 0;  // empty: after every real candidate
             cn[r] = 0xFFFFFFFFu;
-            const uint32_t ab = tab[list][r * 64 + lane];
+            const uint32_t ab = tabv[r];
             if (ab != kNoPair) {
                 const int ra = (int)(ab >> 8), rb = (int)(ab & 0xFF);
                 float hi, lo;
@@ -564,6 +560,11 @@ hipError_t launch_select(const Shape &s, const void *kp, const void *qp, bool bf
     a.beta = beta;
     a.hist = hist;
     a.lists = hist ? 1 : 2;
+    for (int list = 0; list < 2; list++) {
+        const int K = list ? s.R : s.W;
+        for (int i = 0; i < kTabMax; i++) a.tab[list][i] = hook_pair(K, i / 64, i % 64);
+        a.tabn[list] = hook_rest(K);
+    }
     if (s.sqrtN <= 64) return launch_e<1>(a, st);
     if (s.sqrtN <= 128) return launch_e<2>(a, st);
     if (s.sqrtN <= 256) return launch_e<4>(a, st);
