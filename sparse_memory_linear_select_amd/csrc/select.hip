@@ -369,6 +369,12 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
             ht += bb * (T32 - tn32) * H32 + t032 * H32;
         }
         const int64_t base = (int64_t)ht * 2 * S;
+        // the gates of a write list, fetched now so their latency overlaps the selection
+        float al = 0.0f, be = 0.0f;
+        if (a.rec != nullptr && list == 0) {
+            al = a.alpha[ht];
+            be = a.beta[ht];
+        }
 
         // ---- stage 1: sort each half, keep the first K ----
         uint64_t k1[E], k2[E];
@@ -497,7 +503,6 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
             uint32_t *rec = a.rec + (((int64_t)(b * H32 + h) * T32) + t) * a.rec_dwords;
             if (list == 0) {
                 if (lane < a.Wp) {
-                    const float al = a.alpha[ht], be = a.beta[ht];
                     const bool ok = lane < K;
                     const float c = be * w;
                     rec[lane] = ok ? n : 0u;
