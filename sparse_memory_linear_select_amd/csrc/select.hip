@@ -27,6 +27,9 @@
 // with (a+1)(b+1) > K at least K pairs come before it.
 #include "sdm_internal.h"
 
+#include <array>
+#include <cstring>
+
 namespace sdm {
 namespace {
 
@@ -521,6 +524,26 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
     }
 }
 
+// The candidate columns of every list length K, built once per process (a
+// thread-safe static) rather than on every launch.
+struct HookTable {
+    uint16_t pair[kTabMax];
+    int rest;
+};
+
+const HookTable &hook_table(int K)
+{
+    static const std::array<HookTable, kMaxK + 1> tables = [] {
+        std::array<HookTable, kMaxK + 1> t{};
+        for (int k = 1; k <= kMaxK; k++) {
+            for (int i = 0; i < kTabMax; i++) t[k].pair[i] = hook_pair(k, i / 64, i % 64);
+            t[k].rest = hook_rest(k);
+        }
+        return t;
+    }();
+    return tables[K];
+}
+
 template <int E>
 hipError_t launch_e(const SelArgs &args, hipStream_t st)
 {
@@ -566,9 +589,9 @@ hipError_t launch_select(const Shape &s, const void *kp, const void *qp, bool bf
     a.hist = hist;
     a.lists = hist ? 1 : 2;
     for (int list = 0; list < 2; list++) {
-        const int K = list ? s.R : s.W;
-        for (int i = 0; i < kTabMax; i++) a.tab[list][i] = hook_pair(K, i / 64, i % 64);
-        a.tabn[list] = hook_rest(K);
+        const HookTable &t = hook_table(list ? s.R : s.W);
+        memcpy(a.tab[list], t.pair, sizeof t.pair);
+        a.tabn[list] = t.rest;
     }
     if (s.sqrtN <= 64) return launch_e<1>(a, st);
     if (s.sqrtN <= 128) return launch_e<2>(a, st);
