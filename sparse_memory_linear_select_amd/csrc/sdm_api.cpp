@@ -181,9 +181,10 @@ SideStream *side_stream(sdm_ctx *h, hipStream_t hs, hipError_t *err)
 
 // Whether the pipelined forward gets at least four groups of epochs (see
 // forward_pipelined); otherwise the single-stream path is used.  Measured on
-// MI355X, the overlap saves about 3.6% of a step with 16 epochs of 32 chains
-// (groups of 2, 2, 4, 8 epochs) and nothing with fewer groups: the selection
-// running beside the write/read slows it by nearly what it hides.
+// MI355X, the overlap saves about 1% of a step with 16 epochs of 32 chains
+// (groups of 2, 2, 4, 8 epochs) and loses with fewer or smaller groups: the
+// selection and sort running beside the write/read slow it by nearly what
+// they hide.
 bool pipeline_pays(const sdm::Shape &s)
 {
     const int64_t E = sdm::tp_epoch_len(s);
