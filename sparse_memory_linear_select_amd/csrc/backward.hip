@@ -15,8 +15,10 @@
 //   softmax weights -> scores -> the halves of k' (q'): for slot
 //          n = i*sqrtN + j, x[i] and x[sqrtN + j] receive w (dw - <w, dw>).
 //
-// Schedule.  A forward pass (write updates only) records, per write event,
-// the row it replaced (the tape).  The write and read events of each
+// Schedule.  A forward pass (write updates only) records, per slot written
+// in an epoch, its epoch-start row at the slot's first write of the epoch
+// (the tape; the rows the later writes replace are recomputed from it in the
+// reverse pass with the same operations).  The write and read events of each
 // (chain, epoch) are sorted together by slot (time order within a slot,
 // writes before reads at one token).  Epochs are then processed in reverse;
 // per slot segment one row group walks the segment forward (rows seen by the
@@ -37,7 +39,7 @@ constexpr int kDots = 3 * kMaxK;  // per (chain, token): da[64], dc[64], dq[64]
 struct BwdArgs {
     const uint32_t *rec;     // token records
     const TPEntry *ms;       // [chain][T*(W+R)] merged sorted events, epoch regions
-    const float *tape;       // [chain][T][W][d_v] rows replaced by writes
+    float *tape;             // [chain][T][W][d_v] epoch-start rows at first writes (see the segment kernel)
     const void *v;
     const float *dy;         // [B][T][H][d_v]
     float *Mw;               // [chain][N][d_v] state: end of the current epoch -> its start
@@ -109,9 +111,9 @@ __global__ __launch_bounds__(1024) void bwd_segstart_kernel(BwdArgs a, int nep, 
 // their rows -- v (write) or dy (read), and the tape row (write) -- are
 // loaded in one batch; longer segments continue from memory.  Per segment:
 // the epoch-start row (first write's tape entry, or the state when nothing
-// writes the slot), a forward walk (the row each read sees -> dq), a reverse
-// walk (the adjoint -> da, dc, dv contributions), then the slot's adjoint and
-// epoch-start state are stored.
+// writes the slot), a forward walk (the row each read sees -> dq, and the
+// row each write replaces), a reverse walk (the adjoint -> da, dc, dv
+// contributions), then the slot's adjoint and epoch-start state are stored.
 #ifndef SDM_BWD_CACHE
 #define SDM_BWD_CACHE 4
 #endif
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(256) void bwd_segment_kernel(BwdArgs a, int ep, int
     const int64_t row0_off = (b * a.T * a.H + h) * a.d_v + colc;  // v, dy of token 0
     const TPEntry *se = a.ms + chain * a.T * ept + t0 * ept;
     const int *st = starts + chain * a.T * ept + t0 * ept;
-    const float *tape_c = a.tape + (chain * a.T + t0) * a.W * a.d_v + colc;
+    float *tape_c = a.tape + (chain * a.T + t0) * a.W * a.d_v + colc;
     float *part = a.part + chain * (int64_t)nsg * a.E * ept * 2 + (int64_t)sg * a.E * ept * 2;
     const rsrc_t Mr = make_rsrc(a.Mw + chain * a.N * a.d_v, (uint32_t)(a.N * a.d_v * 4));
     const rsrc_t Gr = make_rsrc(a.G + chain * a.N * a.d_v, (uint32_t)(a.N * a.d_v * 4));
@@ -184,30 +186,22 @@ __global__ __launch_bounds__(256) void bwd_segment_kernel(BwdArgs a, int ep, int
 #pragma unroll
         for (int c = 0; c < kCache; c++)
             if (c < lc) e[c] = se[p0 + c];
-#pragma unroll
-        for (int c = 0; c < kCache; c++) {
-            xv[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-            tp[c] = xv[c];
-            if (c < lc) {
-                xv[c] = event_row(e[c]);
-                if (is_write(e[c])) tp[c] = tape_row(e[c]);
-            }
-        }
-        const uint32_t roff = col_ok ? slot * (uint32_t)a.d_v * 4u + col * 4u : kOff;
-        float4 gv = buf_load4(Gr, roff);
-        // epoch-start row
+        // the segment's first write: its tape entry is the epoch-start row
         int firstw = -1;
 #pragma unroll
         for (int c = kCache - 1; c >= 0; c--)
             if (c < lc && is_write(e[c])) firstw = c;
-        float4 row0;
-        bool written = firstw >= 0;
-        if (firstw >= 0) {
-            row0 = tp[0];
+        float4 row0 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-            for (int c = 1; c < kCache; c++)
-                if (c == firstw) row0 = tp[c];
-        } else {
+        for (int c = 0; c < kCache; c++) {
+            xv[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (c < lc) xv[c] = event_row(e[c]);
+            if (c == firstw) row0 = tape_row(e[c]);
+        }
+        const uint32_t roff = col_ok ? slot * (uint32_t)a.d_v * 4u + col * 4u : kOff;
+        float4 gv = buf_load4(Gr, roff);
+        bool written = firstw >= 0;
+        if (firstw < 0) {
             int pw = -1;
             for (int p = p0 + lc; p < p1; p++)
                 if (is_write(se[p])) {
@@ -218,22 +212,36 @@ __global__ __launch_bounds__(256) void bwd_segment_kernel(BwdArgs a, int ep, int
             row0 = written ? tape_row(se[pw]) : buf_load4(Mr, roff);
         }
 
-        // forward walk: the row each read sees
+        // forward walk: the row each read sees, and the row each write
+        // replaces (recomputed with the forward's own operations, so equal
+        // to it bit for bit): in registers for the cached events, in the
+        // write's tape entry for the rest
         float4 cur = row0;
-        auto fwd_event = [&](const TPEntry &x, float4 val, int p) {
+#pragma unroll
+        for (int c = 0; c < kCache; c++) {
+            tp[c] = cur;
+            if (c < lc) {
+                if (is_write(e[c])) {
+                    cur = fma4(e[c].a, cur, e[c].c, xv[c]);
+                } else {
+                    const float dq = wave_sum(col_ok ? dot4(xv[c], cur) : 0.0f);
+                    if (lane == 0) part[(int64_t)(p0 + c) * 2] = dq;
+                }
+            }
+        }
+        for (int p = p0 + lc; p < p1; p++) {
+            const TPEntry x = se[p];
+            const float4 val = event_row(x);
             if (is_write(x)) {
+                if (col_ok)
+                    *reinterpret_cast<float4 *>(tape_c +
+                                                ((int64_t)(x.tw >> 7) * a.W + (x.tw & 63u)) *
+                                                    a.d_v) = cur;
                 cur = fma4(x.a, cur, x.c, val);
             } else {
                 const float dq = wave_sum(col_ok ? dot4(val, cur) : 0.0f);
                 if (lane == 0) part[(int64_t)p * 2] = dq;
             }
-        };
-#pragma unroll
-        for (int c = 0; c < kCache; c++)
-            if (c < lc) fwd_event(e[c], xv[c], p0 + c);
-        for (int p = p0 + lc; p < p1; p++) {
-            const TPEntry x = se[p];
-            fwd_event(x, event_row(x), p);
         }
 
         // reverse walk: the adjoint of the row

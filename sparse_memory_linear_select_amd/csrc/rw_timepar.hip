@@ -442,7 +442,9 @@ __global__ __launch_bounds__(256) void tp_update_kernel(TPArgs a, int ep, int64_
                                 (uint32_t)(a.N * a.d_v * S::kElem));
     const uint32_t rowb = (uint32_t)a.d_v * S::kElem;
     const TPEntry *se = a.sorted + chain * a.T * a.W + t0 * a.W;
-    // TAPE: the row each write replaced, at [chain][token][w][column]
+    // TAPE: the epoch-start row of each written slot, stored at the slot of
+    // its first write in the epoch ([chain][token][w][column]); the backward
+    // recomputes the rows the later writes of the epoch replaced
     float *tape_c = TAPE ? a.tape + (chain * a.T + t0) * a.W * a.d_v + colc : nullptr;
     auto tape_put = [&](const TPEntry &ev, float4 x, bool on) {
         if (TAPE && on)
@@ -474,14 +476,12 @@ __global__ __launch_bounds__(256) void tp_update_kernel(TPArgs a, int ep, int64_
 #pragma unroll
         for (int s2 = s + 1; s2 < SPG; s2++) {
             more = more & (j0 + s2 < n) & (e[s2].slot == e[s].slot);
-            tape_put(e[s2], r, head[s] & more & col_ok);
             if (more) r = S::round(fma4(e[s2].a, r, e[s2].c, vv[s2]));
         }
         if (head[s] & more & (j0 + SPG < n) & (e[SPG].slot == e[s].slot)) {
             for (int j = j0 + SPG; j < n; j++) {
                 const TPEntry f = se[j];
                 if (f.slot != e[s].slot) break;
-                tape_put(f, r, col_ok);
                 r = S::round(fma4(f.a, r, f.c, load_v<BF16>(a.v, vrow0 + (t0 + (f.tw >> 6)) * hd)));
             }
         }

@@ -48,6 +48,8 @@ SHAPES = [
     (1, 257, 2, 128, 64, 64, 64, "f32", 0.3),  # the 1.4B-style slot count, key reuse
     (1, 91, 1, 32, 36, 32, 20, "bf16", 0.5),   # bf16 inputs
     (3, 50, 1, 9, 8, 9, 9, "f32", 0.0),       # every token writes 9 of 81 slots
+    (1, 300, 1, 1024, 8, 64, 64, "f32", 0.2),  # the largest sqrtN (2^20 slots), W = R = 64
+    (2, 600, 1, 512, 16, 64, 32, "bf16", 0.2),  # sqrtN = 512 with bf16 inputs, W != R
 ]
 
 
