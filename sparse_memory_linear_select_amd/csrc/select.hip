@@ -12,8 +12,10 @@
 //            first K in the order (score desc, n = i*sqrtN + j asc) are kept.
 //            The pairs are laid out in five 64-lane columns so that two
 //            arrive sorted and one bitonic (runs along a row or down a
-//            column of ranks are already in order); the other two are sorted
-//            across lanes, and columns are merged pairwise keeping the top 64;
+//            column of ranks are already in order); those three are merged
+//            keeping the top 64, the pairs of the other two that do not come
+//            before its K-th entry are dropped, and the survivors are
+//            compacted into one column, sorted and merged in;
 //   weights  softmax over the K selected scores.
 // The compare-exchange steps form each list's dependent chain; their lane
 // exchanges use DPP and the gfx950 permlane swaps (a few cycles) rather than
