@@ -409,13 +409,17 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int64_t 
 // ------------------------------------------------------------------ update
 
 // One wavefront per (chain, block of 8*SPG sorted write events, 32-column
-// slice); each row group takes SPG consecutive events.  An event whose slot
+// slice); each row group takes SPG consecutive events.  With `rev` the
+// chains are taken last to first: the read kernel before it (or the previous
+// update) ends on the last chains, whose rows may still sit in the
+// memory-side cache (measured: 8.18 -> 8.04 ms write/read per 1.4B-style
+// step).  An event whose slot
 // differs from the previous event's starts that slot's segment: its group
 // loads the row once, applies the segment's writes in time order and stores
 // it once.  Loads of the SPG events are issued together.
 template <bool BF16, int SPG, bool SB, bool TAPE = false>
 __global__ __launch_bounds__(256) void tp_update_kernel(TPArgs a, int ep, int64_t units,
-                                                        int nslice, int nblk)
+                                                        int nslice, int nblk, bool rev)
 {
     static_assert(!(TAPE && SB), "the tape holds float32 rows");
     using S = StateRow<SB>;
@@ -426,7 +430,7 @@ __global__ __launch_bounds__(256) void tp_update_kernel(TPArgs a, int ep, int64_
     const int slice = (int)(unit % nslice);
     const int64_t rest = unit / nslice;
     const int blk = (int)(rest % nblk);
-    const int64_t chain = rest / nblk;
+    const int64_t chain = rev ? a.chains - 1 - rest / nblk : rest / nblk;
     const int64_t t0 = (int64_t)ep * a.E;
     const int ne = (int)((a.T - t0) < a.E ? (a.T - t0) : a.E);
     const int n = ne * a.W;
@@ -645,10 +649,10 @@ static hipError_t tp_apply_state(const Shape &s, TPArgs a, bool bf16, hipStream_
         const dim3 ugrid((unsigned)((uunits + 3) / 4));
         if (bf16)
             hipLaunchKernelGGL((tp_update_kernel<true, SPG, SB>), ugrid, dim3(256), 0, st, a, ep,
-                               uunits, nslice, nblk);
+                               uunits, nslice, nblk, true);
         else
             hipLaunchKernelGGL((tp_update_kernel<false, SPG, SB>), ugrid, dim3(256), 0, st, a, ep,
-                               uunits, nslice, nblk);
+                               uunits, nslice, nblk, true);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -668,12 +672,13 @@ hipError_t launch_tp_forward_tape(const Shape &s, const uint32_t *rec, void *ws,
         const int nblk = (ne * s.W + kRPI * SPG - 1) / (kRPI * SPG);
         const int64_t uunits = a.chains * nblk * nslice;
         const dim3 ugrid((unsigned)((uunits + 3) / 4));
+        const bool rev = ep & 1;  // each launch starts on the chains the previous one ended on
         if (bf16)
             hipLaunchKernelGGL((tp_update_kernel<true, SPG, false, true>), ugrid, dim3(256), 0, st, a,
-                               ep, uunits, nslice, nblk);
+                               ep, uunits, nslice, nblk, rev);
         else
             hipLaunchKernelGGL((tp_update_kernel<false, SPG, false, true>), ugrid, dim3(256), 0, st,
-                               a, ep, uunits, nslice, nblk);
+                               a, ep, uunits, nslice, nblk, rev);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
