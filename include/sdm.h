@@ -169,11 +169,12 @@ sdm_status sdm_select(sdm_handle h, int B, int64_t T, const void *kp, const void
  *              must hold the state to continue from.
  * Outputs must not alias inputs or each other.
  *
- * With the time-parallel schedule and more than one epoch of tokens, the call
- * splits the tokens into up to 32 groups of epochs and issues the selection
- * and event sort of each group on a helper stream that the handle owns (one
- * per device, default priority, created by the first such call on that
- * device): it starts after the work queued on `stream` before the call, and
+ * With the time-parallel schedule, a float32 state and enough epochs of
+ * tokens to form at least four groups (where the overlap measured faster),
+ * the call splits the tokens into up to 32 groups of epochs and issues the
+ * selection and event sort of each group on a helper stream that the handle
+ * owns (one per device, default priority, created by the first such call on
+ * that device): it starts after the work queued on `stream` before the call, and
  * `stream` waits for each group before its write/read.  Everything the call
  * enqueues is therefore ordered before later work on `stream`, as for a
  * single-stream call.  Calls on one handle from several host threads are

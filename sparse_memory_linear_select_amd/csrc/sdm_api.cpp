@@ -180,13 +180,15 @@ SideStream *side_stream(sdm_ctx *h, hipStream_t hs, hipError_t *err)
 }
 
 // Whether the pipelined forward gets at least four groups of epochs (see
-// forward_pipelined); otherwise the single-stream path is used.  Measured on
-// MI355X, the overlap saves about 1% of a step with 16 epochs of 32 chains
-// (groups of 2, 2, 4, 8 epochs) and loses with fewer or smaller groups: the
-// selection and sort running beside the write/read slow it by nearly what
-// they hide.
-bool pipeline_pays(const sdm::Shape &s)
+// forward_pipelined) and a float32 state; otherwise the single-stream path is
+// used.  Measured on MI355X, the overlap saves under 1% of a step with 16
+// epochs of 32 chains (groups of 2, 2, 4, 8 epochs) and loses with fewer or
+// smaller groups, or with a bfloat16 state (7.07 vs 6.95 ms at the 1.4B-style
+// layer, whose write/read is shorter): the selection and sort running beside
+// the write/read slow it by nearly what they hide.
+bool pipeline_pays(const sdm_ctx *h, const sdm::Shape &s)
 {
+    if (h->state_bf16) return false;
     const int64_t E = sdm::tp_epoch_len(s);
     const int64_t nep = (s.T + E - 1) / E;
     const int64_t chains = (int64_t)s.B * s.H;
@@ -501,7 +503,7 @@ sdm_status sdm_forward(sdm_handle h, int B, int64_t T, const void *kp, const voi
     st = check_variant_and_ws(h, B, T, variant, ws_bytes, &var);
     if (st != SDM_OK) return st;
     const sdm::Shape s = shape_of(h, B, T);
-    if (var == SDM_VARIANT_TIMEPAR && pipeline_pays(s))
+    if (var == SDM_VARIANT_TIMEPAR && pipeline_pays(h, s))
         return forward_pipelined(h, s, kp, qp, v, alpha, beta, dtype == SDM_BF16, flags,
                                  workspace, y, M, (hipStream_t)stream);
     st = sdm_prepare(h, B, T, kp, qp, alpha, beta, dtype, variant, flags, workspace, ws_bytes, M,

@@ -110,9 +110,10 @@ def test_bf16_state_scaling_by_two_is_exact():
     assert torch.equal(y2, 2 * y1) and torch.equal(M2, 2 * M1)
 
 
-def test_bf16_state_deterministic_pipelined_and_continued():
-    """Bitwise run-to-run determinism; the pipelined forward equals prepare +
-    apply bit for bit; a continuation split gives the same state bit for bit."""
+def test_bf16_state_deterministic_staged_and_continued():
+    """Bitwise run-to-run determinism; sdm_forward (which runs on one stream
+    with a bfloat16 state) equals prepare + apply bit for bit; a continuation
+    split gives the same state bit for bit."""
     wl = si.Workload("bf16 pipe", B=4, T=1189, H=4, sqrtN=16, d_v=32, W=8, R=8, dtype="f32",
                      reuse=0.2, seed=44)
     d = si.generate(wl)
