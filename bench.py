@@ -298,8 +298,7 @@ def main():
         apply()
     torch.cuda.synchronize()
 
-    # timed region: K whole steps (sdm_forward; with the time-parallel
-    # schedule its selection and sort overlap the write/read on a helper stream)
+    # timed region: K whole steps (sdm_forward)
     t0_ev, t1_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()

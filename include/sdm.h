@@ -127,8 +127,7 @@ sdm_status sdm_create_ex(const float *M0, int H, int sqrtN, int d_v, int W, int 
                          sdm_dtype state_dtype, sdm_handle *out);
 
 /*
- * Release a handle (M_0 is not touched) and the helper streams sdm_forward
- * created for it; work already queued on them still completes.  NULL is
+ * Release a handle (M_0 is not touched).  Makes no HIP call.  NULL is
  * accepted.
  */
 sdm_status sdm_destroy(sdm_handle h);
@@ -168,18 +167,8 @@ sdm_status sdm_select(sdm_handle h, int B, int64_t T, const void *kp, const void
  *              M_0 (so a failed call can simply be retried); with the flag it
  *              must hold the state to continue from.
  * Outputs must not alias inputs or each other.
- *
- * With the time-parallel schedule, a float32 state and enough epochs of
- * tokens to form at least four groups (where the overlap measured faster),
- * the call splits the tokens into up to 32 groups of epochs and issues the
- * selection and event sort of each group on a helper stream that the handle
- * owns (one per device, default priority, created by the first such call on
- * that device): it starts after the work queued on `stream` before the call, and
- * `stream` waits for each group before its write/read.  Everything the call
- * enqueues is therefore ordered before later work on `stream`, as for a
- * single-stream call.  Calls on one handle from several host threads are
- * serialised while they enqueue.  HIP errors from creating the helper stream
- * return SDM_ERR_HIP.
+ * Everything runs on `stream`, in order: sdm_prepare(...) then
+ * sdm_apply(...) with the same arguments.
  */
 sdm_status sdm_forward(sdm_handle h, int B, int64_t T, const void *kp, const void *qp,
                        const void *v, const float *alpha, const float *beta,
@@ -189,10 +178,8 @@ sdm_status sdm_forward(sdm_handle h, int B, int64_t T, const void *kp, const voi
 
 /*
  * The two halves of sdm_forward, for callers that time or pipeline them.
- * sdm_forward(...) computes exactly what sdm_prepare(...) followed by
- * sdm_apply(...) with the same handle, shapes, dtype, variant and workspace
- * computes (bit for bit); the pair runs on `stream` alone, without the
- * overlap sdm_forward arranges.
+ * sdm_forward(...) is sdm_prepare(...) followed by sdm_apply(...) with the
+ * same handle, shapes, dtype, variant and workspace.
  *
  * sdm_prepare: unless SDM_FLAG_CONTINUE is set, M <- M_0; then the selection
  *   of every head-token is written into the workspace (with the write

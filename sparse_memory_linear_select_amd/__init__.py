@@ -253,8 +253,8 @@ class SDM:
         """(y, M): outputs [B,T,H,d_v] and final state [B,H,N,d_v] (float32).
 
         With cont=True, M must hold the state to continue from (no M <- M_0).
-        staged=True issues sdm_prepare + sdm_apply on the current stream
-        instead of sdm_forward (same result, no helper-stream overlap).
+        staged=True issues sdm_prepare + sdm_apply instead of sdm_forward
+        (the same work on the same stream).
         """
         for t, n in ((kp, "kp"), (qp, "qp"), (v, "v")):
             _dev_tensor(t, n)

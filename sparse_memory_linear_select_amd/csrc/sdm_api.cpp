@@ -6,33 +6,15 @@
 #include <stdarg.h>
 #include <stdio.h>
 
-#include <mutex>
 #include <new>
 #include <string>
 
 #include "sdm_internal.h"
 
-namespace {
-constexpr int kMaxDevices = 64;
-constexpr int kMaxChunks = 32;       // pipeline stages of a time-parallel forward
-constexpr int kMinSortBlocks = 64;   // workgroups per sort launch in the pipeline
-
-// Per-device helper stream of a handle: the time-parallel forward runs the
-// selection and event sort of the next group of epochs there while the
-// caller's stream applies the current one.  Default priority, non-blocking.
-struct SideStream {
-    hipStream_t s = nullptr;
-    hipEvent_t fork = nullptr;
-    hipEvent_t ready[kMaxChunks] = {};
-};
-}  // namespace
-
 struct sdm_ctx {
     const float *M0 = nullptr;
     int H = 0, sqrtN = 0, d_v = 0, W = 0, R = 0;
     bool state_bf16 = false;  // M holds bfloat16 values
-    std::mutex mu;  // guards side[] and the enqueue sequence of a pipelined forward
-    SideStream side[kMaxDevices];
 };
 
 namespace {
@@ -139,128 +121,6 @@ sdm_status check_variant_and_ws(const sdm_ctx *h, int B, int64_t T, sdm_variant 
     return SDM_OK;
 }
 
-// The side stream of the device that `hs` belongs to (the current device
-// for the null stream), created on first use (caller holds h->mu).  Null if
-// it cannot be created.
-SideStream *side_stream(sdm_ctx *h, hipStream_t hs, hipError_t *err)
-{
-    int cur = -1, dev = -1;
-    *err = hipGetDevice(&cur);
-    if (*err != hipSuccess) return nullptr;
-    dev = cur;
-    if (hs) {
-        *err = hipStreamGetDevice(hs, &dev);
-        if (*err != hipSuccess) return nullptr;
-    }
-    if (dev < 0 || dev >= kMaxDevices) {
-        *err = hipErrorInvalidDevice;
-        return nullptr;
-    }
-    SideStream &ss = h->side[dev];
-    if (ss.s) return &ss;
-    if (dev != cur) {  // streams and events are created on the current device
-        *err = hipSetDevice(dev);
-        if (*err != hipSuccess) return nullptr;
-    }
-    SideStream n;
-    *err = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking);
-    if (*err == hipSuccess) *err = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
-    for (int c = 0; c < kMaxChunks && *err == hipSuccess; c++)
-        *err = hipEventCreateWithFlags(&n.ready[c], hipEventDisableTiming);
-    if (dev != cur) (void)hipSetDevice(cur);
-    if (*err != hipSuccess) {
-        for (hipEvent_t e : n.ready)
-            if (e) (void)hipEventDestroy(e);
-        if (n.fork) (void)hipEventDestroy(n.fork);
-        if (n.s) (void)hipStreamDestroy(n.s);
-        return nullptr;
-    }
-    ss = n;
-    return &ss;
-}
-
-// Whether the pipelined forward gets at least four groups of epochs (see
-// forward_pipelined) and a float32 state; otherwise the single-stream path is
-// used.  Measured on MI355X, the overlap saves under 1% of a step with 16
-// epochs of 32 chains (groups of 2, 2, 4, 8 epochs) and loses with fewer or
-// smaller groups, or with a bfloat16 state (7.07 vs 6.95 ms at the 1.4B-style
-// layer, whose write/read is shorter): the selection and sort running beside
-// the write/read slow it by nearly what they hide.
-bool pipeline_pays(const sdm_ctx *h, const sdm::Shape &s)
-{
-    if (h->state_bf16) return false;
-    const int64_t E = sdm::tp_epoch_len(s);
-    const int64_t nep = (s.T + E - 1) / E;
-    const int64_t chains = (int64_t)s.B * s.H;
-    int64_t g = 1;
-    while (g < nep && chains * g < kMinSortBlocks) g <<= 1;
-    return 8 * g <= nep;
-}
-
-// Time-parallel forward as a two-stream pipeline over groups of epochs.  The
-// selection, sort and links of group c (side stream) need only k', q', alpha,
-// beta; the write/read of group c (caller's stream) waits for them, and for
-// the write/read of group c-1 by stream order.  So the selection of later
-// groups (ALU bound) runs under the write/read of earlier ones (HBM bound).
-// Workspace regions of different groups are disjoint.
-sdm_status forward_pipelined(sdm_ctx *h, const sdm::Shape &s, const void *kp, const void *qp,
-                             const void *v, const float *alpha, const float *beta, bool bf16,
-                             unsigned flags, void *workspace, float *y, void *M, hipStream_t hs)
-{
-    std::lock_guard<std::mutex> lock(h->mu);
-    hipError_t e;
-    SideStream *ss = side_stream(h, hs, &e);
-    if (!ss) return hip_fail(e, "helper stream creation");
-    const int E = sdm::tp_epoch_len(s);
-    const int nep = (int)((s.T + E - 1) / E);
-    // group boundaries 0, g, 2g, 4g, ... epochs: the first group (the only
-    // exposed selection) is short; g keeps at least kMinSortBlocks workgroups
-    // in each sort and link launch (one per chain and epoch), so that their
-    // latency stays below the write/read of the previous group
-    const int64_t chains = (int64_t)s.B * s.H;
-    int g = 1;
-    while (g < nep && chains * g < kMinSortBlocks) g <<= 1;
-    int bound[kMaxChunks + 1];
-    int C = 0;
-    bound[0] = 0;
-    while (bound[C] < nep && C < kMaxChunks) {
-        const int64_t b = bound[C] == 0 ? g : 2 * (int64_t)bound[C];
-        C++;
-        bound[C] = (b < nep && C < kMaxChunks) ? (int)b : nep;
-    }
-    uint32_t *rec = static_cast<uint32_t *>(workspace);
-    char *tp = static_cast<char *>(workspace) + records_bytes(h, s.B, s.T);
-
-    // the side stream starts after everything the caller queued before this call
-    e = hipEventRecord(ss->fork, hs);
-    if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->fork, 0);
-    if (e != hipSuccess) return hip_fail(e, "stream fork");
-    if (!(flags & SDM_FLAG_CONTINUE)) {
-        e = sdm::launch_init(s, h->M0, M, h->state_bf16, hs);
-        if (e != hipSuccess) return hip_fail(e, "init launch");
-    }
-    for (int c = 0; c < C; c++) {
-        const int e0 = bound[c], e1 = bound[c + 1];
-        const int64_t t0 = (int64_t)e0 * E;
-        const int64_t t1 = (int64_t)e1 * E < s.T ? (int64_t)e1 * E : s.T;
-        e = sdm::launch_select(s, kp, qp, bf16, nullptr, nullptr, nullptr, nullptr, rec, alpha,
-                               beta, ss->s, nullptr, t0, t1 - t0);
-        if (e != hipSuccess) return hip_fail(e, "select launch");
-        e = sdm::launch_tp_prepare(s, rec, tp, ss->s, e0, e1);
-        if (e != hipSuccess) return hip_fail(e, "time-parallel sort launch");
-        e = hipEventRecord(ss->ready[c], ss->s);
-        if (e != hipSuccess) return hip_fail(e, "event record");
-    }
-    for (int c = 0; c < C; c++) {
-        const int e0 = bound[c], e1 = bound[c + 1];
-        e = hipStreamWaitEvent(hs, ss->ready[c], 0);
-        if (e != hipSuccess) return hip_fail(e, "stream wait");
-        e = sdm::launch_tp_apply(s, rec, tp, v, bf16, y, M, h->state_bf16, hs, e0, e1);
-        if (e != hipSuccess) return hip_fail(e, "time-parallel write/read launch");
-    }
-    return SDM_OK;
-}
-
 size_t bwd_ws_bytes(const sdm_ctx *h, int B, int64_t T)
 {
     const sdm::Shape s = shape_of(h, B, T);
@@ -337,21 +197,6 @@ sdm_status sdm_create(const float *M0, int H, int sqrtN, int d_v, int W, int R, 
 
 sdm_status sdm_destroy(sdm_handle h)
 {
-    if (!h) return SDM_OK;
-    int cur = -1;
-    bool have_cur = false;  // HIP is touched only if a helper stream exists
-    for (int d = 0; d < kMaxDevices; d++) {
-        SideStream &ss = h->side[d];
-        if (!ss.s) continue;
-        if (!have_cur) have_cur = hipGetDevice(&cur) == hipSuccess;
-        // work still queued on the stream completes before its resources go
-        (void)hipSetDevice(d);
-        for (hipEvent_t &e : ss.ready)
-            if (e) (void)hipEventDestroy(e);
-        if (ss.fork) (void)hipEventDestroy(ss.fork);
-        (void)hipStreamDestroy(ss.s);
-    }
-    if (have_cur) (void)hipSetDevice(cur);
     delete h;
     return SDM_OK;
 }
@@ -502,10 +347,6 @@ sdm_status sdm_forward(sdm_handle h, int B, int64_t T, const void *kp, const voi
     sdm_variant var;
     st = check_variant_and_ws(h, B, T, variant, ws_bytes, &var);
     if (st != SDM_OK) return st;
-    const sdm::Shape s = shape_of(h, B, T);
-    if (var == SDM_VARIANT_TIMEPAR && pipeline_pays(h, s))
-        return forward_pipelined(h, s, kp, qp, v, alpha, beta, dtype == SDM_BF16, flags,
-                                 workspace, y, M, (hipStream_t)stream);
     st = sdm_prepare(h, B, T, kp, qp, alpha, beta, dtype, variant, flags, workspace, ws_bytes, M,
                      stream);
     if (st != SDM_OK) return st;

@@ -269,15 +269,13 @@ def test_decode_token_by_token(variant):
 @pytest.mark.parametrize("shape", [(4, 1189, 4, 16, 32, 8, 8, "f32"),
                                    (2, 1100, 8, 32, 64, 32, 32, "bf16")],
                          ids=["38-epochs", "35-epochs-bf16"])
-def test_pipelined_forward_matches_staged(shape):
-    """With the time-parallel schedule and enough epochs, sdm_forward runs the
-    selection and sort of later epoch groups on a helper stream under the
-    write/read of earlier ones (16 chains: groups of 4, 4, 8, 16, ... epochs;
-    38 epochs end with a partial group).  It must match the oracle and give,
-    bit for bit, what sdm_prepare + sdm_apply give on one stream: from M_0,
-    continuing from a state, and on a side stream."""
+def test_forward_matches_staged_many_epochs(shape):
+    """Many epochs of the time-parallel schedule (the last one partial): the
+    forward matches the oracle and gives, bit for bit, what sdm_prepare +
+    sdm_apply give: from M_0, continuing from a state, and issued on a
+    non-default torch stream whose results are consumed on that stream."""
     B, T, H, S, D, W, R, dt = shape
-    wl = si.Workload("pipeline", B=B, T=T, H=H, sqrtN=S, d_v=D, W=W, R=R, dtype=dt, reuse=0.2,
+    wl = si.Workload("epochs", B=B, T=T, H=H, sqrtN=S, d_v=D, W=W, R=R, dtype=dt, reuse=0.2,
                      seed=60 + T)
     d, dd, y, M = _parity(wl, variant=sdm.TIMEPAR)
     core = make_core(dd, W, R)

@@ -1,5 +1,5 @@
-"""HIP graph capture of the forward: the pipelined time-parallel forward
-(helper stream forked and joined with events) and a one-token decode step
+"""HIP graph capture of the forward: many epochs of the time-parallel
+schedule, a short sequence, and a one-token decode step
 replay bit for bit like eager calls.  Replays are separated by eager work
 and synchronisations, and every replay is checked."""
 import numpy as np
@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("shape", [(4, 1189, 4, 16, 32, 8, 8), (2, 300, 2, 32, 64, 16, 16)],
-                         ids=["pipelined", "single-stream"])
+                         ids=["many-epochs", "few-epochs"])
 @pytest.mark.parametrize("variant", [sdm.TIMEPAR, sdm.SERIAL], ids=["timepar", "serial"])
 def test_forward_graph_replays(shape, variant):
     B, T, H, S, D, W, R = shape
