@@ -118,7 +118,7 @@ __global__ __launch_bounds__(1024) void bwd_segstart_kernel(BwdArgs a, int nep, 
 #define SDM_BWD_CACHE 4
 #endif
 constexpr int kCache = SDM_BWD_CACHE;
-constexpr int kSegsPerWave = 8;
+constexpr int kSegsPerWave = 4;  // measured 4 / 8 / 16: 32.3 / 32.7 / 33.4 ms per 1.4B-style step
 constexpr int kColsPerWave = 256;
 
 __device__ __forceinline__ float wave_sum(float x)
