@@ -78,8 +78,8 @@ size_t records_bytes(const sdm_ctx *h, int B, int64_t T)
 // AUTO: the time-parallel schedule whenever it applies.  Its parallelism does
 // not depend on the number of chains, and it merges repeated writes to a slot
 // within an epoch.  Measured write+read on MI355X (time-parallel vs
-// token-serial): 32 chains x 512 columns 9.6 ms vs 12.2, 8 x 1024 19.5 vs 43.3,
-// 32 x 1024 38.6 vs 41.4, 1 x 2048 (2^20 tokens) 324 vs 1676.  The token-serial
+// token-serial): 32 chains x 512 columns 7.8 ms vs 12.2, 8 x 1024 15.9 vs 43.3,
+// 32 x 1024 31.8 vs 41.4, 1 x 2048 (2^20 tokens) 269 vs 1676.  The token-serial
 // schedule remains for d_v % 4 != 0 (one column per lane) and on request.
 sdm_variant resolve_variant(const sdm_ctx *h, int B, int64_t T, sdm_variant v)
 {
