@@ -37,12 +37,6 @@ __global__ __launch_bounds__(256) void init_kernel_scalar(const float *__restric
     }
 }
 
-__device__ __forceinline__ uint32_t bf16_bits(float f)  // nearest, ties to even (finite f)
-{
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 // bfloat16 state: n is a multiple of 4 (d_v % 4 == 0), so every 4 values of
 // a sequence's slab are 8-byte aligned.
 __global__ __launch_bounds__(256) void init_kernel_bf16(const float *__restrict__ M0,

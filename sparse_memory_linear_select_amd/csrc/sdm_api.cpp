@@ -269,12 +269,17 @@ sdm_status sdm_prepare(sdm_handle h, int B, int64_t T, const void *kp, const voi
     const hipStream_t hs = (hipStream_t)stream;
     uint32_t *rec = static_cast<uint32_t *>(workspace);
     hipError_t e;
-    if (!(flags & SDM_FLAG_CONTINUE)) {
+    // M <- M_0, inside the selection launch where its items cover M_0 (the
+    // copy then runs under the selection's arithmetic), else on its own
+    const bool init = !(flags & SDM_FLAG_CONTINUE);
+    const bool fused_init = init && sdm::select_can_init(s);
+    if (init && !fused_init) {
         e = sdm::launch_init(s, h->M0, M, h->state_bf16, hs);
         if (e != hipSuccess) return hip_fail(e, "init launch");
     }
+    const sdm::SelInit si{h->M0, M, h->state_bf16};
     e = sdm::launch_select(s, kp, qp, dtype == SDM_BF16, nullptr, nullptr, nullptr, nullptr, rec,
-                           alpha, beta, hs);
+                           alpha, beta, hs, nullptr, 0, -1, fused_init ? &si : nullptr);
     if (e != hipSuccess) return hip_fail(e, "select launch");
     if (var == SDM_VARIANT_TIMEPAR) {
         if (!sdm::decode_supported(s)) {  // one token: nothing to sort (see sdm_apply)

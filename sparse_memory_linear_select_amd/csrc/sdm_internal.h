@@ -49,6 +49,13 @@ struct TPEntry {
     float a, c;
 };
 
+// Nearest bfloat16 (ties to even) of a finite float, as its 16 bits.
+__device__ __forceinline__ uint32_t bf16_bits(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 struct Shape {
     int B;
     int64_t T;
@@ -59,6 +66,19 @@ struct Shape {
 
 // ---- launchers (each returns the launch error, if any) ----
 
+// State initialisation M[b] <- M_0 (every sequence b) carried out by the
+// selection launch: each item (head-token and list) copies one 1 KB piece of
+// M_0, loaded when the item starts and stored B times when it ends, so the
+// copy runs under the selection's arithmetic.  Possible when the items cover
+// M_0 that way (select_can_init); M is float32, or bfloat16 (rounded to
+// nearest, ties to even).
+struct SelInit {
+    const float *M0;
+    void *M;
+    bool state_bf16;
+};
+bool select_can_init(const Shape &s);
+
 // Selection.  With hist != nullptr it only counts write slots per head into
 // hist[H][N]; else with rec == nullptr it writes the API layout (Iw, kw, Ir,
 // qw, [B][T][H][K]); otherwise it writes token records (needs alpha, beta).
@@ -66,7 +86,8 @@ hipError_t launch_select(const Shape &s, const void *kp, const void *qp, bool bf
                          int32_t *Iw, float *kw, int32_t *Ir, float *qw,
                          uint32_t *rec, const float *alpha, const float *beta,
                          hipStream_t st, uint32_t *hist = nullptr, int64_t t0 = 0,
-                         int64_t tn = -1);  // tokens [t0, t0 + tn) of every sequence
+                         int64_t tn = -1,  // tokens [t0, t0 + tn) of every sequence
+                         const SelInit *init = nullptr);
 
 // M[b] <- M0 for every sequence b.
 hipError_t launch_init(const Shape &s, const float *M0, void *M, bool state_bf16, hipStream_t st);

@@ -337,13 +337,19 @@ struct SelArgs {
     const float *alpha, *beta;
     uint32_t *hist;  // [H][N] write-slot counts (histogram mode: write lists only)
     int lists;       // 2: write and read lists; 1: write lists only
+    // state initialisation (SelInit): item i copies float4s [64 i, 64 i + 64)
+    // of M0 to every sequence's slab of M (n4 float4s per slab)
+    const float4 *M0;
+    void *M;
+    int64_t n4;
+    int Bseq, init_bf16;
     // candidate columns of both lists (pairs a << 8 | b, laid out by hooks),
     // computed on the host: lane l of column c reads entry c*64 + l
     uint16_t tab[2][kTabMax];
     int tabn[2];  // pairs with both ranks >= 2 (columns 3 and 4)
 };
 
-template <int E>
+template <int E, bool INIT>
 __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
 {
     constexpr int E2 = 5;  // candidate columns: 5*64 >= 280 pairs for K = 64
@@ -380,6 +386,10 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
             al = a.alpha[ht];
             be = a.beta[ht];
         }
+        // this item's piece of M0, stored once the stage-1 sort is done
+        const int64_t jm = (int64_t)it * 64 + lane;
+        const bool init = INIT && jm < a.n4;
+        const float4 m0 = init ? a.M0[jm] : make_float4(0.f, 0.f, 0.f, 0.f);
 
         // ---- stage 1: sort each half, keep the first K ----
         uint64_t k1[E], k2[E];
@@ -396,6 +406,15 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
             }
         }
         sort_halves_desc<E>(k1, k2, lane);
+        if (init) {  // the piece of M0 has arrived during the sort
+            if (a.init_bf16) {
+                const uint2 u = make_uint2(bf16_bits(m0.x) | (bf16_bits(m0.y) << 16),
+                                           bf16_bits(m0.z) | (bf16_bits(m0.w) << 16));
+                for (int b = 0; b < a.Bseq; b++) reinterpret_cast<uint2 *>(a.M)[b * a.n4 + jm] = u;
+            } else {
+                for (int b = 0; b < a.Bseq; b++) reinterpret_cast<float4 *>(a.M)[b * a.n4 + jm] = m0;
+            }
+        }
 #pragma unroll
         for (int r = 0; r < E; r++) {
             const int e = lane * E + r;
@@ -553,16 +572,29 @@ hipError_t launch_e(const SelArgs &args, hipStream_t st)
     int64_t blocks = (items + 3) / 4;
     if (blocks > 16384) blocks = 16384;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(select_kernel<E>, dim3((unsigned)blocks), dim3(256), 0, st, args);
+    // the copy of M0 is a separate instantiation: its registers would lower
+    // the occupancy of every other selection
+    if (args.M0)
+        hipLaunchKernelGGL((select_kernel<E, true>), dim3((unsigned)blocks), dim3(256), 0, st, args);
+    else
+        hipLaunchKernelGGL((select_kernel<E, false>), dim3((unsigned)blocks), dim3(256), 0, st, args);
     return hipGetLastError();
 }
 
 }  // namespace
 
+// Item i of a full selection (both lists, all tokens) copies float4s
+// [64 i, 64 i + 64) of M0: the items must cover the n/4 float4s of a slab.
+bool select_can_init(const Shape &s)
+{
+    const int64_t n = (int64_t)s.H * s.N() * s.d_v;
+    return n % 4 == 0 && 2 * s.ht() * 64 >= n / 4;
+}
+
 hipError_t launch_select(const Shape &s, const void *kp, const void *qp, bool bf16,
                          int32_t *Iw, float *kw, int32_t *Ir, float *qw, uint32_t *rec,
                          const float *alpha, const float *beta, hipStream_t st, uint32_t *hist,
-                         int64_t t0, int64_t tn)
+                         int64_t t0, int64_t tn, const SelInit *init)
 {
     if (tn < 0) tn = s.T - t0;
     SelArgs a{};
@@ -590,6 +622,15 @@ hipError_t launch_select(const Shape &s, const void *kp, const void *qp, bool bf
     a.beta = beta;
     a.hist = hist;
     a.lists = hist ? 1 : 2;
+    if (init) {
+        // only for a full selection whose items cover M0 (select_can_init)
+        if (hist || tn != s.T || !select_can_init(s)) return hipErrorInvalidValue;
+        a.M0 = reinterpret_cast<const float4 *>(init->M0);
+        a.M = init->M;
+        a.n4 = (int64_t)s.H * s.N() * s.d_v / 4;
+        a.Bseq = s.B;
+        a.init_bf16 = init->state_bf16 ? 1 : 0;
+    }
     for (int list = 0; list < 2; list++) {
         const HookTable &t = hook_table(list ? s.R : s.W);
         memcpy(a.tab[list], t.pair, sizeof t.pair);

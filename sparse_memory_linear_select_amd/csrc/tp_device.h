@@ -14,7 +14,6 @@ using rsrc_t = __amdgpu_buffer_rsrc_t;
 constexpr uint32_t kOff = 0x80000000u;
 constexpr int kRsrcWord3 = 0x00020000;
 
-
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
@@ -35,13 +34,6 @@ __device__ __forceinline__ float4 fma4(float a, float4 x, float c, float4 v)
 {
     return make_float4(fmaf(a, x.x, c * v.x), fmaf(a, x.y, c * v.y), fmaf(a, x.z, c * v.z),
                        fmaf(a, x.w, c * v.w));
-}
-
-// Nearest bfloat16 (ties to even) of a finite float, as its 16 bits.
-__device__ __forceinline__ uint32_t bf16_bits(float f)
-{
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
 // Row storage of the state.  Every lane holds 4 columns of a row; a row
