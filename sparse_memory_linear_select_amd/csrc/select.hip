@@ -585,10 +585,13 @@ hipError_t launch_e(const SelArgs &args, hipStream_t st)
 
 // Item i of a full selection (both lists, all tokens) copies float4s
 // [64 i, 64 i + 64) of M0: the items must cover the n/4 float4s of a slab.
+// Only up to sqrtN = 256: the copy's registers cost the wider instantiations
+// a wave per SIMD (at sqrtN = 512 the selection then took 24.1 ms instead of
+// 23.1 + 0.4 for the separate copy).
 bool select_can_init(const Shape &s)
 {
     const int64_t n = (int64_t)s.H * s.N() * s.d_v;
-    return n % 4 == 0 && 2 * s.ht() * 64 >= n / 4;
+    return s.sqrtN <= 256 && n % 4 == 0 && 2 * s.ht() * 64 >= n / 4;
 }
 
 hipError_t launch_select(const Shape &s, const void *kp, const void *qp, bool bf16,
