@@ -350,7 +350,7 @@ struct SelArgs {
 };
 
 template <int E, bool INIT>
-__global__ __launch_bounds__(256) void select_kernel(SelArgs a)
+__device__ __forceinline__ void select_body(SelArgs a)
 {
     constexpr int E2 = 5;  // candidate columns: 5*64 >= 280 pairs for K = 64
     __shared__ float sv[4][2][64];
@@ -545,6 +545,21 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a)
     }
 }
 
+template <int E>
+__global__ __launch_bounds__(256) void select_kernel(SelArgs a)
+{
+    select_body<E, false>(a);
+}
+
+// The variant that also copies M0 is held to the occupancy of the plain one
+// (five wavefronts per SIMD), which its extra registers would otherwise lower;
+// it fits without spilling up to sqrtN = 128 (E <= 2).
+template <int E>
+__global__ __launch_bounds__(256, 5) void select_init_kernel(SelArgs a)
+{
+    select_body<E, true>(a);
+}
+
 // The candidate columns of every list length K, built once per process (a
 // thread-safe static) rather than on every launch.
 struct HookTable {
@@ -574,10 +589,16 @@ hipError_t launch_e(const SelArgs &args, hipStream_t st)
     if (blocks < 1) blocks = 1;
     // the copy of M0 is a separate instantiation: its registers would lower
     // the occupancy of every other selection
-    if (args.M0)
-        hipLaunchKernelGGL((select_kernel<E, true>), dim3((unsigned)blocks), dim3(256), 0, st, args);
-    else
-        hipLaunchKernelGGL((select_kernel<E, false>), dim3((unsigned)blocks), dim3(256), 0, st, args);
+    if constexpr (E <= 2) {
+        if (args.M0) {
+            hipLaunchKernelGGL(select_init_kernel<E>, dim3((unsigned)blocks), dim3(256), 0, st,
+                               args);
+            return hipGetLastError();
+        }
+    } else if (args.M0) {
+        return hipErrorInvalidValue;  // select_can_init rules this out
+    }
+    hipLaunchKernelGGL(select_kernel<E>, dim3((unsigned)blocks), dim3(256), 0, st, args);
     return hipGetLastError();
 }
 
@@ -585,13 +606,13 @@ hipError_t launch_e(const SelArgs &args, hipStream_t st)
 
 // Item i of a full selection (both lists, all tokens) copies float4s
 // [64 i, 64 i + 64) of M0: the items must cover the n/4 float4s of a slab.
-// Only up to sqrtN = 256: the copy's registers cost the wider instantiations
-// a wave per SIMD (at sqrtN = 512 the selection then took 24.1 ms instead of
-// 23.1 + 0.4 for the separate copy).
+// Only up to sqrtN = 128: wider instantiations cannot hold the copy's
+// registers at the same occupancy (at sqrtN = 512 the selection took 24.1 ms
+// instead of 23.1 + 0.4 for the separate copy).
 bool select_can_init(const Shape &s)
 {
     const int64_t n = (int64_t)s.H * s.N() * s.d_v;
-    return s.sqrtN <= 256 && n % 4 == 0 && 2 * s.ht() * 64 >= n / 4;
+    return s.sqrtN <= 128 && n % 4 == 0 && 2 * s.ht() * 64 >= n / 4;
 }
 
 hipError_t launch_select(const Shape &s, const void *kp, const void *qp, bool bf16,
