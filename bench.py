@@ -95,7 +95,16 @@ def cpu_baseline(d, wl, seqs, state="f32"):
     oracle.forward(sub, wl.sqrtN, wl.W, wl.R, threads=cores, state=state)
     dt = time.perf_counter() - t
     ht = seqs * wl.T * wl.H
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": ht / dt, "unit": "head-tokens/s", "cores": cores, "kind": "oracle",
+            "cpu": model,
             "sample": f"{seqs} of {wl.B} sequences of the workload ({ht} head-tokens, all "
                       f"{wl.d_v} columns), select + init + recurrence, {dt:.2f} s wall"}
 

@@ -61,5 +61,5 @@ def test_cpu_baseline_on_a_sample():
     d = si.generate(wl)
     out = bench.cpu_baseline(d, wl, 1)
     assert out["kind"] == "oracle" and out["unit"] == "head-tokens/s"
-    assert out["value"] > 0 and out["cores"] >= 1
+    assert out["value"] > 0 and out["cores"] >= 1 and out["cpu"]
     assert f"{wl.T * wl.H} head-tokens" in out["sample"]
