@@ -416,10 +416,17 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int64_t 
 // step).  An event whose slot
 // differs from the previous event's starts that slot's segment: its group
 // loads the row once, applies the segment's writes in time order and stores
-// it once.  Loads of the SPG events are issued together.
+// it once.  Loads of the SPG events are issued together.  Lane q of a row
+// group holds event q of the group's SPG and the group reads the fields with
+// in-group broadcasts, so the events do not take registers in every lane:
+// 93 VGPRs instead of 125 for a float32 state (five waves per SIMD instead
+// of four; write/read 7.81 -> 7.50 ms per 1.4B-style step).  A bfloat16
+// state is held to six waves per SIMD, where the compiler then fits seven
+// (5.23 -> 5.07 ms).
 template <bool BF16, int SPG, bool SB, bool TAPE = false>
-__global__ __launch_bounds__(256) void tp_update_kernel(TPArgs a, int ep, int64_t units,
-                                                        int nslice, int nblk, bool rev)
+__global__ __launch_bounds__(256, SB ? 6 : 1) void tp_update_kernel(TPArgs a, int ep,
+                                                                    int64_t units, int nslice,
+                                                                    int nblk, bool rev)
 {
     static_assert(!(TAPE && SB), "the tape holds float32 rows");
     using S = StateRow<SB>;
@@ -456,40 +463,59 @@ __global__ __launch_bounds__(256) void tp_update_kernel(TPArgs a, int ep, int64_
                                                      a.d_v) = x;
     };
 
+    static_assert(SPG <= kLPR, "one event per lane of a row group");
     const int j0 = (blk * kRPI + g) * SPG;
-    TPEntry e[SPG + 1];  // this group's events and the one after them
-#pragma unroll
-    for (int s = 0; s <= SPG; s++) e[s] = se[j0 + s < n ? j0 + s : n - 1];
+    // lane q < SPG of a row group holds event j0 + q; the group reads the
+    // fields back with in-group broadcasts when it needs them
+    const TPEntry me = se[(q < SPG && j0 + q < n) ? j0 + q : n - 1];
+    const uint32_t next = j0 + SPG < n ? se[j0 + SPG].slot : 0xFFFFFFFFu;
     const uint32_t prev0 = j0 > 0 && j0 - 1 < n ? se[j0 - 1].slot : 0xFFFFFFFFu;
-    bool head[SPG];
+    // bit s of `same`: event s continues the segment of event s - 1 (bit
+    // SPG: the event after the group continues the last one's); events are
+    // sorted by slot, so a segment is a run of set bits
+    uint32_t same = 0u, prev = prev0;
     float4 row[SPG], vv[SPG];
 #pragma unroll
     for (int s = 0; s < SPG; s++) {
-        const uint32_t prev = s == 0 ? prev0 : e[s - 1].slot;
-        head[s] = (j0 + s < n) & (e[s].slot != prev);
-        row[s] = S::load(Mr, (head[s] & col_ok) ? e[s].slot * rowb + col * S::kElem : kOff);
-        vv[s] = load_v<BF16>(a.v, vrow0 + (t0 + (e[s].tw >> 6)) * hd);
+        const uint32_t sl = group_bcast<kLPR>(me.slot, s);
+        const bool in = j0 + s < n;
+        same |= (uint32_t)(in & (sl == prev)) << s;
+        const bool head = in & (sl != prev);
+        row[s] = S::load(Mr, (head & col_ok) ? sl * rowb + col * S::kElem : kOff);
+        const uint32_t tw = group_bcast<kLPR>(me.tw, s);
+        vv[s] = load_v<BF16>(a.v, vrow0 + (t0 + (tw >> 6)) * hd);
+        prev = sl;
     }
+    same |= (uint32_t)((j0 + SPG < n) & (next == prev)) << SPG;
 #pragma unroll
     for (int s = 0; s < SPG; s++) {
-        tape_put(e[s], row[s], head[s] & col_ok);
-        float4 r = S::round(fma4(e[s].a, row[s], e[s].c, vv[s]));
+        const bool head = (j0 + s < n) & !((same >> s) & 1u);
+        if (TAPE) {
+            TPEntry ev;
+            ev.tw = group_bcast<kLPR>(me.tw, s);
+            tape_put(ev, row[s], head & col_ok);
+        }
+        float4 r = S::round(fma4(__uint_as_float(group_bcast<kLPR>(__float_as_uint(me.a), s)), row[s],
+                                 __uint_as_float(group_bcast<kLPR>(__float_as_uint(me.c), s)), vv[s]));
         // the rest of the segment, in time order: events of this group from
         // registers, then (rarely) events past the group from memory
         bool more = true;
 #pragma unroll
         for (int s2 = s + 1; s2 < SPG; s2++) {
-            more = more & (j0 + s2 < n) & (e[s2].slot == e[s].slot);
-            if (more) r = S::round(fma4(e[s2].a, r, e[s2].c, vv[s2]));
+            more = more & ((same >> s2) & 1u);
+            if (more)
+                r = S::round(fma4(__uint_as_float(group_bcast<kLPR>(__float_as_uint(me.a), s2)), r,
+                                  __uint_as_float(group_bcast<kLPR>(__float_as_uint(me.c), s2)), vv[s2]));
         }
-        if (head[s] & more & (j0 + SPG < n) & (e[SPG].slot == e[s].slot)) {
+        const uint32_t sl = group_bcast<kLPR>(me.slot, s);
+        if (head & more & ((same >> SPG) & 1u)) {
             for (int j = j0 + SPG; j < n; j++) {
                 const TPEntry f = se[j];
-                if (f.slot != e[s].slot) break;
+                if (f.slot != sl) break;
                 r = S::round(fma4(f.a, r, f.c, load_v<BF16>(a.v, vrow0 + (t0 + (f.tw >> 6)) * hd)));
             }
         }
-        S::store(r, Mr, (head[s] & col_ok) ? e[s].slot * rowb + col * S::kElem : kOff);
+        S::store(r, Mr, (head & col_ok) ? sl * rowb + col * S::kElem : kOff);
     }
 }
 
@@ -640,13 +666,10 @@ static hipError_t tp_apply_state(const Shape &s, TPArgs a, bool bf16, hipStream_
 #undef SDM_TP_READ
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-#ifndef SDM_TP_SPG_BF16
-#define SDM_TP_SPG_BF16 4
-#endif
-        // sorted events per row group (measured: 8 for a float32 state, e.g.
-        // 8.05 -> 7.81 ms write/read at the 1.4B-style layer; 4 for a
-        // bfloat16 state, whose rows are half as wide)
-        constexpr int SPG = SB ? SDM_TP_SPG_BF16 : 8;
+        // sorted events per row group (measured at the 1.4B-style layer,
+        // write/read: 8 rather than 4, 8.05 -> 7.81 ms, for a float32 state
+        // and 5.53 -> 5.23 ms for a bfloat16 state; 16 is slower for both)
+        constexpr int SPG = 8;
         const int nblk = (ne * s.W + kRPI * SPG - 1) / (kRPI * SPG);
         const int64_t uunits = a.chains * nblk * nslice;
         const dim3 ugrid((unsigned)((uunits + 3) / 4));
