@@ -408,21 +408,27 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int64_t 
 
 // ------------------------------------------------------------------ update
 
-// One wavefront per (chain, block of 8*SPG sorted write events, 32-column
-// slice); each row group takes SPG consecutive events.  With `rev` the
+// One wavefront per (chain, block of kRPI*SPG sorted write events, 128-byte
+// row slice); each row group takes SPG consecutive events.  With `rev` the
 // chains are taken last to first: the read kernel before it (or the previous
 // update) ends on the last chains, whose rows may still sit in the
 // memory-side cache (measured: 8.18 -> 8.04 ms write/read per 1.4B-style
-// step).  An event whose slot
-// differs from the previous event's starts that slot's segment: its group
-// loads the row once, applies the segment's writes in time order and stores
-// it once.  Loads of the SPG events are issued together.  Lane q of a row
-// group holds event q of the group's SPG and the group reads the fields with
-// in-group broadcasts, so the events do not take registers in every lane:
-// 93 VGPRs instead of 125 for a float32 state (five waves per SIMD instead
-// of four; write/read 7.81 -> 7.50 ms per 1.4B-style step).  A bfloat16
-// state is held to six waves per SIMD, where the compiler then fits seven
-// (5.23 -> 5.07 ms).
+// step).  An event whose slot differs from the previous event's starts that
+// slot's segment: its group loads the row once, applies the segment's writes
+// in time order and stores it once.  Loads of the SPG events are issued
+// together.
+//
+// Lane q of a row group holds event q of the group and the group reads the
+// fields with in-group broadcasts, so the events do not take registers in
+// every lane (93 VGPRs instead of 125 for a float32 state: five waves per
+// SIMD instead of four; write/read 7.81 -> 7.50 ms per 1.4B-style step).
+// The group's last segment may go on past the group.  Its next events are
+// the next row group's, whose lanes hold their fields and v slices: the
+// group takes them from there with cross-lane reads and goes to memory only
+// in the wave's last group or for a segment longer than the next group
+// (write/read 7.50 -> 7.19 ms; doing the tail inside the per-event loop,
+// from memory, forced full waits for every outstanding load).  A bfloat16
+// state is held to six waves per SIMD.
 template <bool BF16, int SPG, bool SB, bool TAPE = false>
 __global__ __launch_bounds__(256, SB ? 6 : 1) void tp_update_kernel(TPArgs a, int ep,
                                                                     int64_t units, int nslice,
@@ -487,6 +493,11 @@ __global__ __launch_bounds__(256, SB ? 6 : 1) void tp_update_kernel(TPArgs a, in
         prev = sl;
     }
     same |= (uint32_t)((j0 + SPG < n) & (next == prev)) << SPG;
+    // the group's last segment, when it goes on past the group: finished
+    // from memory after the group's other rows are stored
+    float4 rt = make_float4(0.f, 0.f, 0.f, 0.f);
+    uint32_t slt = 0u;
+    bool tail = false;
 #pragma unroll
     for (int s = 0; s < SPG; s++) {
         const bool head = (j0 + s < n) & !((same >> s) & 1u);
@@ -497,8 +508,7 @@ __global__ __launch_bounds__(256, SB ? 6 : 1) void tp_update_kernel(TPArgs a, in
         }
         float4 r = S::round(fma4(__uint_as_float(group_bcast<kLPR>(__float_as_uint(me.a), s)), row[s],
                                  __uint_as_float(group_bcast<kLPR>(__float_as_uint(me.c), s)), vv[s]));
-        // the rest of the segment, in time order: events of this group from
-        // registers, then (rarely) events past the group from memory
+        // the rest of the segment within the group, in time order
         bool more = true;
 #pragma unroll
         for (int s2 = s + 1; s2 < SPG; s2++) {
@@ -508,14 +518,47 @@ __global__ __launch_bounds__(256, SB ? 6 : 1) void tp_update_kernel(TPArgs a, in
                                   __uint_as_float(group_bcast<kLPR>(__float_as_uint(me.c), s2)), vv[s2]));
         }
         const uint32_t sl = group_bcast<kLPR>(me.slot, s);
-        if (head & more & ((same >> SPG) & 1u)) {
-            for (int j = j0 + SPG; j < n; j++) {
-                const TPEntry f = se[j];
-                if (f.slot != sl) break;
-                r = S::round(fma4(f.a, r, f.c, load_v<BF16>(a.v, vrow0 + (t0 + (f.tw >> 6)) * hd)));
-            }
+        const bool cont = head & more & ((same >> SPG) & 1u);
+        if (cont) {
+            rt = r;
+            slt = sl;
         }
-        S::store(r, Mr, (head & col_ok) ? sl * rowb + col * S::kElem : kOff);
+        tail |= cont;
+        S::store(r, Mr, (head & !cont & col_ok) ? sl * rowb + col * S::kElem : kOff);
+    }
+    // The events just past the group are the next row group's (same wave,
+    // same columns, kLPR lanes up): its lanes hold their fields, v rows and
+    // which of them continue the segment (leading bits of its `same`).
+    int jm = j0 + SPG;  // first event still to apply from memory
+    if (__builtin_amdgcn_ballot_w64(tail) != 0ull) {
+        const bool inw = g < kRPI - 1;
+        const int up = (lane + kLPR) & 63;
+        const uint32_t same_nx = (uint32_t)__builtin_amdgcn_ds_bpermute(up * 4, (int)same);
+        bool go = tail & inw;
+#pragma unroll
+        for (int s2 = 0; s2 < SPG; s2++) {
+            go = go & ((same_nx >> s2) & 1u);
+            if (__builtin_amdgcn_ballot_w64(go) == 0ull) break;
+            const int src = ((g + 1) * kLPR + s2) & 63;
+            const float a2 = __int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(me.a)));
+            const float c2 = __int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(me.c)));
+            float4 v2;
+            v2.x = __int_as_float(__builtin_amdgcn_ds_bpermute(up * 4, __float_as_int(vv[s2].x)));
+            v2.y = __int_as_float(__builtin_amdgcn_ds_bpermute(up * 4, __float_as_int(vv[s2].y)));
+            v2.z = __int_as_float(__builtin_amdgcn_ds_bpermute(up * 4, __float_as_int(vv[s2].z)));
+            v2.w = __int_as_float(__builtin_amdgcn_ds_bpermute(up * 4, __float_as_int(vv[s2].w)));
+            if (go) rt = S::round(fma4(a2, rt, c2, v2));
+        }
+        // the last group of the wave, or a segment that outlasts the next group too
+        if (inw) jm = go ? j0 + 2 * SPG : n;
+    }
+    if (tail) {
+        for (int j = jm; j < n; j++) {
+            const TPEntry f = se[j];
+            if (f.slot != slt) break;
+            rt = S::round(fma4(f.a, rt, f.c, load_v<BF16>(a.v, vrow0 + (t0 + (f.tw >> 6)) * hd)));
+        }
+        S::store(rt, Mr, col_ok ? slt * rowb + col * S::kElem : kOff);
     }
 }
 
