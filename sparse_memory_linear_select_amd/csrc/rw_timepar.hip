@@ -65,6 +65,20 @@ struct SortIO {
     uint16_t *ckey;         // coarse keys (forward only)
 };
 
+// Grid of a launch over every chain: x covers one chain's waves (four to a
+// workgroup), y and z the chains (y at most 65535), so the kernels split
+// their wave index with 32-bit arithmetic.
+static dim3 chain_grid(int64_t chains, int64_t waves_per_chain)
+{
+    const unsigned gy = (unsigned)(chains < 65535 ? chains : 65535);
+    return dim3((unsigned)((waves_per_chain + 3) / 4), gy, (unsigned)((chains + gy - 1) / gy));
+}
+
+__device__ __forceinline__ int64_t grid_chain()
+{
+    return (int64_t)blockIdx.y + (int64_t)blockIdx.z * gridDim.y;
+}
+
 // ------------------------------------------------------------------ sort
 
 constexpr int kDigitBits = 9;                  // radix digit: 512 buckets
@@ -294,27 +308,26 @@ __global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int str
 constexpr int kPairBatch = SDM_TP_PAIR_BATCH;  // v pairs per row group in flight
 
 template <int NR, bool BF16, bool SB>
-__global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int64_t units,
-                                                      int nslice)
+__global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int nslice)
 {
     using S = StateRow<SB>;
     constexpr int kLPR = S::kLPR, kRPI = 64 / kLPR;
     const int lane = threadIdx.x & 63;
-    const int64_t unit = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (unit >= units) return;
-    const int slice = (int)(unit % nslice);
-    const int64_t rest = unit / nslice;
+    const int64_t chain = grid_chain();
     const int64_t t0 = (int64_t)ep * a.E;
     const int ne = (int)((a.T - t0) < a.E ? (a.T - t0) : a.E);
-    const int tl = (int)(rest % ne);
-    const int64_t chain = rest / ne;
+    const uint32_t u = blockIdx.x * 4u + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (chain >= a.chains || u >= (uint32_t)(ne * nslice)) return;
+    const int slice = (int)(u % (uint32_t)nslice);
+    const int tl = (int)(u / (uint32_t)nslice);
     const int64_t t = t0 + tl;
     const int64_t ct = chain * a.T + t;
     const int g = lane / kLPR, q = lane % kLPR;
     const int col = slice * 4 * kLPR + q * 4;
     const bool col_ok = col < a.d_v;
     const int colc = col_ok ? col : 0;
-    const int64_t b = chain / a.H;
+    // chains < 2^32 (the grid's y and z), so 32-bit division
+    const int64_t b = (uint32_t)chain / (uint32_t)a.H;
     const int h = (int)(chain - b * a.H);
     const int64_t hd = (int64_t)a.H * a.d_v;
     const int64_t vrow0 = (b * a.T * a.H + h) * a.d_v + colc;  // v of token 0 of the chain
@@ -430,20 +443,19 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int64_t 
 // from memory, forced full waits for every outstanding load).  A bfloat16
 // state is held to six waves per SIMD.
 template <bool BF16, int SPG, bool SB, bool TAPE = false>
-__global__ __launch_bounds__(256, SB ? 6 : 1) void tp_update_kernel(TPArgs a, int ep,
-                                                                    int64_t units, int nslice,
+__global__ __launch_bounds__(256, SB ? 6 : 1) void tp_update_kernel(TPArgs a, int ep, int nslice,
                                                                     int nblk, bool rev)
 {
     static_assert(!(TAPE && SB), "the tape holds float32 rows");
     using S = StateRow<SB>;
     constexpr int kLPR = S::kLPR, kRPI = 64 / kLPR;
     const int lane = threadIdx.x & 63;
-    const int64_t unit = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (unit >= units) return;
-    const int slice = (int)(unit % nslice);
-    const int64_t rest = unit / nslice;
-    const int blk = (int)(rest % nblk);
-    const int64_t chain = rev ? a.chains - 1 - rest / nblk : rest / nblk;
+    const int64_t cg = grid_chain();
+    const uint32_t u = blockIdx.x * 4u + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (cg >= a.chains || u >= (uint32_t)(nblk * nslice)) return;
+    const int slice = (int)(u % (uint32_t)nslice);
+    const int blk = (int)(u / (uint32_t)nslice);
+    const int64_t chain = rev ? a.chains - 1 - cg : cg;
     const int64_t t0 = (int64_t)ep * a.E;
     const int ne = (int)((a.T - t0) < a.E ? (a.T - t0) : a.E);
     const int n = ne * a.W;
@@ -451,7 +463,8 @@ __global__ __launch_bounds__(256, SB ? 6 : 1) void tp_update_kernel(TPArgs a, in
     const int col = slice * 4 * kLPR + q * 4;
     const bool col_ok = col < a.d_v;
     const int colc = col_ok ? col : 0;
-    const int64_t b = chain / a.H;
+    // chains < 2^32 (the grid's y and z), so 32-bit division
+    const int64_t b = (uint32_t)chain / (uint32_t)a.H;
     const int h = (int)(chain - b * a.H);
     const int64_t hd = (int64_t)a.H * a.d_v;
     const int64_t vrow0 = (b * a.T * a.H + h) * a.d_v + colc;
@@ -694,14 +707,13 @@ static hipError_t tp_apply_state(const Shape &s, TPArgs a, bool bf16, hipStream_
     for (int ep = ep0; ep < ep1; ep++) {
         const int64_t t0 = (int64_t)ep * a.E;
         const int ne = (int)((s.T - t0) < a.E ? (s.T - t0) : a.E);
-        const int64_t runits = a.chains * ne * nslice;
-        const dim3 rgrid((unsigned)((runits + 3) / 4));
+        const dim3 rgrid = chain_grid(a.chains, (int64_t)ne * nslice);
 #define SDM_TP_READ(NR_)                                                                          \
     if (nr <= NR_) {                                                                              \
         if (bf16) hipLaunchKernelGGL((tp_read_kernel<NR_, true, SB>), rgrid, dim3(256), 0, st, a, \
-                                     ep, runits, nslice);                                         \
+                                     ep, nslice);                                                 \
         else hipLaunchKernelGGL((tp_read_kernel<NR_, false, SB>), rgrid, dim3(256), 0, st, a, ep, \
-                                runits, nslice);                                                  \
+                                nslice);                                                          \
     } else
         SDM_TP_READ(1) SDM_TP_READ(2) SDM_TP_READ(4) SDM_TP_READ(8) SDM_TP_READ(16) {
             return hipErrorInvalidValue;
@@ -714,14 +726,13 @@ static hipError_t tp_apply_state(const Shape &s, TPArgs a, bool bf16, hipStream_
         // and 5.53 -> 5.23 ms for a bfloat16 state; 16 is slower for both)
         constexpr int SPG = 8;
         const int nblk = (ne * s.W + kRPI * SPG - 1) / (kRPI * SPG);
-        const int64_t uunits = a.chains * nblk * nslice;
-        const dim3 ugrid((unsigned)((uunits + 3) / 4));
+        const dim3 ugrid = chain_grid(a.chains, (int64_t)nblk * nslice);
         if (bf16)
             hipLaunchKernelGGL((tp_update_kernel<true, SPG, SB>), ugrid, dim3(256), 0, st, a, ep,
-                               uunits, nslice, nblk, true);
+                               nslice, nblk, true);
         else
             hipLaunchKernelGGL((tp_update_kernel<false, SPG, SB>), ugrid, dim3(256), 0, st, a, ep,
-                               uunits, nslice, nblk, true);
+                               nslice, nblk, true);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -741,15 +752,14 @@ hipError_t launch_tp_forward_tape(const Shape &s, const uint32_t *rec, void *ws,
         const int64_t t0 = (int64_t)ep * a.E;
         const int ne = (int)((s.T - t0) < a.E ? (s.T - t0) : a.E);
         const int nblk = (ne * s.W + kRPI * SPG - 1) / (kRPI * SPG);
-        const int64_t uunits = a.chains * nblk * nslice;
-        const dim3 ugrid((unsigned)((uunits + 3) / 4));
+        const dim3 ugrid = chain_grid(a.chains, (int64_t)nblk * nslice);
         const bool rev = ep & 1;  // each launch starts on the chains the previous one ended on
         if (bf16)
             hipLaunchKernelGGL((tp_update_kernel<true, SPG, false, true>), ugrid, dim3(256), 0, st, a,
-                               ep, uunits, nslice, nblk, rev);
+                               ep, nslice, nblk, rev);
         else
             hipLaunchKernelGGL((tp_update_kernel<false, SPG, false, true>), ugrid, dim3(256), 0, st,
-                               a, ep, uunits, nslice, nblk, rev);
+                               a, ep, nslice, nblk, rev);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
