@@ -134,12 +134,11 @@ __global__ __launch_bounds__(256) void bwd_segment_kernel(BwdArgs a, int ep, int
                                                           const int *nsegs)
 {
     const int lane = threadIdx.x & 63;
-    const int64_t unit = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int sg = (int)(unit % nsg);
-    const int64_t rest = unit / nsg;
-    const int wb = (int)(rest % nwb);
-    const int64_t chain = rest / nwb;
-    if (chain >= a.chains) return;
+    const uint32_t u = blockIdx.x * 4u + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int sg = (int)(u % (uint32_t)nsg);
+    const int wb = (int)(u / (uint32_t)nsg);
+    const int64_t chain = grid_chain();
+    if (chain >= a.chains || wb >= nwb) return;
     const int ept = a.W + a.R;
     const int64_t t0 = (int64_t)ep * a.E;
     const int ne = (int)((a.T - t0) < a.E ? (a.T - t0) : a.E);
@@ -151,7 +150,7 @@ __global__ __launch_bounds__(256) void bwd_segment_kernel(BwdArgs a, int ep, int
     const int col = sg * kColsPerWave + lane * 4;
     const bool col_ok = col < a.d_v;
     const int colc = col_ok ? col : 0;
-    const int64_t b = chain / a.H;
+    const int64_t b = (uint32_t)chain / (uint32_t)a.H;  // chains < 2^32 (grid y and z)
     const int h = (int)(chain - b * a.H);
     const int64_t hd = (int64_t)a.H * a.d_v;
     const int64_t row0_off = (b * a.T * a.H + h) * a.d_v + colc;  // v, dy of token 0
@@ -284,17 +283,16 @@ __global__ __launch_bounds__(256) void bwd_segment_kernel(BwdArgs a, int ep, int
 
 // dv_t = sum over w of dvbuf[t][w] (w in order per row group, then a fixed
 // butterfly across groups).  One wavefront per (chain, token, column slice).
-__global__ __launch_bounds__(256) void bwd_dv_kernel(BwdArgs a, int ep, int64_t units, float *dv)
+__global__ __launch_bounds__(256) void bwd_dv_kernel(BwdArgs a, int ep, float *dv)
 {
     const int lane = threadIdx.x & 63;
-    const int64_t unit = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (unit >= units) return;
-    const int slice = (int)(unit % a.nslice);
-    const int64_t rest = unit / a.nslice;
+    const uint32_t u = blockIdx.x * 4u + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int slice = (int)(u % (uint32_t)a.nslice);
+    const int tl = (int)(u / (uint32_t)a.nslice);
     const int64_t t0 = (int64_t)ep * a.E;
     const int ne = (int)((a.T - t0) < a.E ? (a.T - t0) : a.E);
-    const int tl = (int)(rest % ne);
-    const int64_t chain = rest / ne;
+    const int64_t chain = grid_chain();
+    if (chain >= a.chains || tl >= ne) return;
     const int g = lane / kLPR, q = lane % kLPR;
     const int col = slice * 4 * kLPR + q * 4;
     const bool col_ok = col < a.d_v;
@@ -315,7 +313,7 @@ __global__ __launch_bounds__(256) void bwd_dv_kernel(BwdArgs a, int ep, int64_t 
         acc.z += __shfl_xor(acc.z, m, 64);
         acc.w += __shfl_xor(acc.w, m, 64);
     }
-    const int64_t b = chain / a.H;
+    const int64_t b = (uint32_t)chain / (uint32_t)a.H;  // chains < 2^32 (grid y and z)
     const int h = (int)(chain - b * a.H);
     if (g == 0 && col_ok)
         *reinterpret_cast<float4 *>(dv + ((b * a.T + t0 + tl) * a.H + h) * a.d_v + col) = acc;
@@ -571,8 +569,7 @@ hipError_t launch_tp_backward(const Shape &s, const uint32_t *rec, void *fwd_ws,
         const int64_t t0 = (int64_t)ep * E;
         const int ne = (int)((s.T - t0) < E ? (s.T - t0) : E);
         const int nwb = (int)((ne * ept + kSegsPerWave - 1) / kSegsPerWave);  // segments <= events
-        const int64_t units = (int64_t)chains * nwb * nsg;
-        const dim3 grid((unsigned)((units + 3) / 4));
+        const dim3 grid = chain_grid(chains, (int64_t)nwb * nsg);
         if (bf16)
             hipLaunchKernelGGL(bwd_segment_kernel<true>, grid, dim3(256), 0, st, a, ep, nep, nwb, nsg,
                                starts, nsegs);
@@ -580,9 +577,8 @@ hipError_t launch_tp_backward(const Shape &s, const uint32_t *rec, void *fwd_ws,
             hipLaunchKernelGGL(bwd_segment_kernel<false>, grid, dim3(256), 0, st, a, ep, nep, nwb, nsg,
                                starts, nsegs);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        const int64_t dunits = (int64_t)chains * ne * nslice;
-        hipLaunchKernelGGL(bwd_dv_kernel, dim3((unsigned)((dunits + 3) / 4)), dim3(256), 0, st, a, ep,
-                           dunits, dv);
+        hipLaunchKernelGGL(bwd_dv_kernel, chain_grid(chains, (int64_t)ne * nslice), dim3(256), 0, st,
+                           a, ep, dv);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const int64_t nev = (int64_t)chains * ne * ept;
         hipLaunchKernelGGL(bwd_dots_kernel, dim3((unsigned)((nev + 255) / 256)), dim3(256), 0, st, a, ep,

@@ -65,20 +65,6 @@ struct SortIO {
     uint16_t *ckey;         // coarse keys (forward only)
 };
 
-// Grid of a launch over every chain: x covers one chain's waves (four to a
-// workgroup), y and z the chains (y at most 65535), so the kernels split
-// their wave index with 32-bit arithmetic.
-static dim3 chain_grid(int64_t chains, int64_t waves_per_chain)
-{
-    const unsigned gy = (unsigned)(chains < 65535 ? chains : 65535);
-    return dim3((unsigned)((waves_per_chain + 3) / 4), gy, (unsigned)((chains + gy - 1) / gy));
-}
-
-__device__ __forceinline__ int64_t grid_chain()
-{
-    return (int64_t)blockIdx.y + (int64_t)blockIdx.z * gridDim.y;
-}
-
 // ------------------------------------------------------------------ sort
 
 constexpr int kDigitBits = 9;                  // radix digit: 512 buckets

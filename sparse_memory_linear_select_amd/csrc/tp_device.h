@@ -1,7 +1,8 @@
 // Device helpers shared by the time-parallel forward and backward kernels:
 // raw buffer loads/stores (out-of-range offsets load zero and drop stores),
 // the affine row update, v loads, the float32/bfloat16 state row access and
-// in-group lane broadcasts.  Included by one translation unit each, so the
+// in-group lane broadcasts, and the chain grid of per-chain launches.
+// Included by one translation unit each, so the
 // definitions stay internal to it.
 #pragma once
 
@@ -143,6 +144,20 @@ __device__ __forceinline__ void load_k(const T *p, T (&out)[K])
 #pragma unroll
         for (int i = 0; i < K; i++) out[i] = p[i];
     }
+}
+
+// Grid of a launch over every chain: x covers one chain's waves (four to a
+// workgroup), y and z the chains (y at most 65535), so the kernels split
+// their wave index with 32-bit arithmetic.
+static dim3 chain_grid(int64_t chains, int64_t waves_per_chain)
+{
+    const unsigned gy = (unsigned)(chains < 65535 ? chains : 65535);
+    return dim3((unsigned)((waves_per_chain + 3) / 4), gy, (unsigned)((chains + gy - 1) / gy));
+}
+
+__device__ __forceinline__ int64_t grid_chain()
+{
+    return (int64_t)blockIdx.y + (int64_t)blockIdx.z * gridDim.y;
 }
 
 }  // namespace
