@@ -552,10 +552,18 @@ __global__ __launch_bounds__(256, SB ? 6 : 1) void tp_update_kernel(TPArgs a, in
         if (inw) jm = go ? j0 + 2 * SPG : n;
     }
     if (tail) {
-        for (int j = jm; j < n; j++) {
-            const TPEntry f = se[j];
-            if (f.slot != slt) break;
-            rt = S::round(fma4(f.a, rt, f.c, load_v<BF16>(a.v, vrow0 + (t0 + (f.tw >> 6)) * hd)));
+        // two events per round trip: both entries load together, then both
+        // v slices, so a one-event tail also learns where it ends
+        for (int j = jm; j < n; j += 2) {
+            const TPEntry f0 = se[j];
+            const TPEntry f1 = se[j + 1 < n ? j + 1 : j];
+            if (f0.slot != slt) break;
+            const bool c1 = (j + 1 < n) & (f1.slot == slt);
+            const float4 v0 = load_v<BF16>(a.v, vrow0 + (t0 + (f0.tw >> 6)) * hd);
+            const float4 v1 = load_v<BF16>(a.v, vrow0 + (t0 + ((c1 ? f1 : f0).tw >> 6)) * hd);
+            rt = S::round(fma4(f0.a, rt, f0.c, v0));
+            if (!c1) break;
+            rt = S::round(fma4(f1.a, rt, f1.c, v1));
         }
         S::store(rt, Mr, col_ok ? slt * rowb + col * S::kElem : kOff);
     }
