@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kSortThreads) void tp_sort_kernel(TPArgs a, SortIO 
 // 64 KiB): a binary search there brackets the slot, a short forward scan of
 // the entries finds the exact range.  One wavefront per token: lane r takes
 // read r, a prefix sum over the lanes places the pairs.
-__global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int stride)
+__global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int stride, int exact)
 {
     extern __shared__ uint16_t ck[];
     const int tid = threadIdx.x;
@@ -218,7 +218,13 @@ __global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int str
     const int64_t base = chain * a.T * a.W + t0 * a.W;
     const uint32_t *recc = a.rec + (chain * a.T + t0) * a.rec_dwords;
     const TPEntry *se = a.sorted + base;
-    for (int k = tid; k < ns; k += kSortThreads) ck[k] = a.ckey[base + (int64_t)k * stride];
+    // exact (every write sampled, keys = slots): the token of every sorted
+    // write sits in LDS as well, and the searches never touch memory
+    uint16_t *tk = ck + ns;
+    for (int k = tid; k < ns; k += kSortThreads) {
+        ck[k] = a.ckey[base + (int64_t)k * stride];
+        if (exact) tk[k] = (uint16_t)(se[k].tw >> 6);
+    }
     __syncthreads();
     for (int tl = tid >> 6; tl < ne; tl += kSortThreads / 64) {  // wave-uniform token
         const uint32_t *rc = recc + (int64_t)tl * a.rec_dwords;
@@ -235,14 +241,21 @@ __global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int str
                 if (ck[mid] < c) lo = mid + 1;
                 else hi = mid;
             }
-            // the sample before it has a smaller slot, so the slot's first entry follows it
-            j = lo > 0 ? (lo - 1) * stride + 1 : 0;
-            while (j < n && se[j].slot < s) j++;
-            int l2 = j;  // past the writes of s at tokens <= tl
-            while (l2 < n) {
-                const TPEntry e = se[l2];
-                if (e.slot != s || (int)(e.tw >> 6) > tl) break;
-                l2++;
+            int l2;  // past the writes of s at tokens <= tl
+            if (exact) {
+                j = lo;
+                l2 = j;
+                while (l2 < n && ck[l2] == s && (int)tk[l2] <= tl) l2++;
+            } else {
+                // the sample before it has a smaller slot, so the slot's first entry follows it
+                j = lo > 0 ? (lo - 1) * stride + 1 : 0;
+                while (j < n && se[j].slot < s) j++;
+                l2 = j;
+                while (l2 < n) {
+                    const TPEntry e = se[l2];
+                    if (e.slot != s || (int)(e.tw >> 6) > tl) break;
+                    l2++;
+                }
             }
             cnt = l2 - j;
         }
@@ -685,9 +698,12 @@ hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipS
     // sampled coarse keys: at most 32768 of them (64 KiB of LDS)
     const int64_t nmax = (int64_t)a.E * s.W;
     const int stride = nmax > 32768 ? (int)((nmax + 32767) / 32768) : 1;
-    const size_t lds = (size_t)((nmax + stride - 1) / stride) * sizeof(uint16_t);
+    // with every write sampled and keys equal to slots, also the tokens (at
+    // most 64 KiB in all)
+    const int exact = stride == 1 && a.kshift == 0 && nmax <= 16384;
+    const size_t lds = (size_t)((nmax + stride - 1) / stride) * sizeof(uint16_t) * (exact ? 2 : 1);
     hipLaunchKernelGGL(tp_link_kernel, dim3((unsigned)blocks), dim3(kSortThreads), lds, st, a,
-                       stride);
+                       stride, exact);
     return hipGetLastError();
 }
 
