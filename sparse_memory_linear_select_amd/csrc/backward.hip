@@ -174,9 +174,12 @@ __global__ __launch_bounds__(256) void bwd_segment_kernel(BwdArgs a, int ep, int
             tape_c + ((int64_t)(x.tw >> 7) * a.W + (x.tw & 63u)) * a.d_v);
     };
 
+    // the wave's segment starts (and the end of its last segment), one per
+    // lane, loaded together
+    const int stl = (lane <= kSegsPerWave && k0 + lane < nseg) ? st[k0 + lane] : n;
     for (int k = k0; k < k1; k++) {
-        const int p0 = st[k];
-        const int p1 = k + 1 < nseg ? st[k + 1] : n;
+        const int p0 = __builtin_amdgcn_readlane(stl, k - k0);
+        const int p1 = __builtin_amdgcn_readlane(stl, k - k0 + 1);
         const int len = p1 - p0;
         const int lc = len < kCache ? len : kCache;
         const uint32_t slot = se[p0].slot;
