@@ -247,13 +247,20 @@ __global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int str
                 l2 = j;
                 while (l2 < n && ck[l2] == s && (int)tk[l2] <= tl) l2++;
             } else {
-                // the sample before it has a smaller slot, so the slot's first entry follows it
+                // the sample before it has a smaller slot, so the slot's first
+                // entry follows it; both scans look at two entries per round trip
                 j = lo > 0 ? (lo - 1) * stride + 1 : 0;
-                while (j < n && se[j].slot < s) j++;
+                while (j < n) {
+                    const uint32_t s0 = se[j].slot, s1 = se[j + 1 < n ? j + 1 : j].slot;
+                    if (s0 >= s) break;
+                    if (++j >= n || s1 >= s) break;
+                    j++;
+                }
                 l2 = j;
                 while (l2 < n) {
-                    const TPEntry e = se[l2];
-                    if (e.slot != s || (int)(e.tw >> 6) > tl) break;
+                    const TPEntry e0 = se[l2], e1 = se[l2 + 1 < n ? l2 + 1 : l2];
+                    if (e0.slot != s || (int)(e0.tw >> 6) > tl) break;
+                    if (++l2 >= n || e1.slot != s || (int)(e1.tw >> 6) > tl) break;
                     l2++;
                 }
             }
