@@ -118,9 +118,10 @@ sdm_status sdm_create(const float *M0, int H, int sqrtN, int d_v, int W, int R,
  *             stores it rounded the same way; reads use the stored rows and
  *             accumulate y in float32.  Halves the row traffic.  Needs the
  *             time-parallel schedule (d_v % 4 == 0): SDM_VARIANT_SERIAL
- *             returns SDM_ERR_UNSUPPORTED.  Reads that see a write of the
- *             same epoch use the unrounded composition of those writes (one
- *             bfloat16 rounding of the row, at most, differs).
+ *             returns SDM_ERR_UNSUPPORTED.  Every read sees the row as the
+ *             state holds it after the writes at tokens <= its own, rounded
+ *             after each of them, so y does not depend on how the tokens are
+ *             split into calls.
  * Errors as sdm_create, plus SDM_ERR_ARG for another state_dtype.
  */
 sdm_status sdm_create_ex(const float *M0, int H, int sqrtN, int d_v, int W, int R,

@@ -114,10 +114,7 @@ __global__ __launch_bounds__(1024) void bwd_segstart_kernel(BwdArgs a, int nep, 
 // writes the slot), a forward walk (the row each read sees -> dq, and the
 // row each write replaces), a reverse walk (the adjoint -> da, dc, dv
 // contributions), then the slot's adjoint and epoch-start state are stored.
-#ifndef SDM_BWD_CACHE
-#define SDM_BWD_CACHE 4
-#endif
-constexpr int kCache = SDM_BWD_CACHE;
+constexpr int kCache = 4;  // events of a segment loaded in the first batch
 constexpr int kSegsPerWave = 4;  // measured 4 / 8 / 16: 32.3 / 32.7 / 33.4 ms per 1.4B-style step
 constexpr int kColsPerWave = 256;
 

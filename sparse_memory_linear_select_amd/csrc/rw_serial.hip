@@ -19,64 +19,20 @@
 //
 // rw_simple_kernel is the plain version (one column per lane, no prefetch),
 // used when d_v is not a multiple of 4.
-#include "sdm_internal.h"
-
-#ifndef SDM_RW_DEPTH
-#define SDM_RW_DEPTH 2
-#endif
+#include "tp_device.h"
 
 namespace sdm {
 namespace {
 
-constexpr int kDepth = SDM_RW_DEPTH;  // cross-token prefetch depth
+// Cross-token prefetch depth: the rows of token t+P are gathered while token
+// t is processed.
+constexpr int kDepth = 2;
 
 __device__ __forceinline__ void wave_sync()
 {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-template <int K, typename T>
-__device__ __forceinline__ void load_k(const T *p, T (&out)[K])
-{
-    if constexpr (K == 4 && sizeof(T) == 4) {
-        const uint4 x = *reinterpret_cast<const uint4 *>(p);
-        out[0] = __builtin_bit_cast(T, x.x);
-        out[1] = __builtin_bit_cast(T, x.y);
-        out[2] = __builtin_bit_cast(T, x.z);
-        out[3] = __builtin_bit_cast(T, x.w);
-    } else if constexpr (K == 8 && sizeof(T) == 4) {
-        const uint4 x = *reinterpret_cast<const uint4 *>(p);
-        const uint4 z = *reinterpret_cast<const uint4 *>(p + 4);
-        out[0] = __builtin_bit_cast(T, x.x);
-        out[1] = __builtin_bit_cast(T, x.y);
-        out[2] = __builtin_bit_cast(T, x.z);
-        out[3] = __builtin_bit_cast(T, x.w);
-        out[4] = __builtin_bit_cast(T, z.x);
-        out[5] = __builtin_bit_cast(T, z.y);
-        out[6] = __builtin_bit_cast(T, z.z);
-        out[7] = __builtin_bit_cast(T, z.w);
-    } else if constexpr (K == 2 && sizeof(T) == 4) {
-        const uint2 x = *reinterpret_cast<const uint2 *>(p);
-        out[0] = __builtin_bit_cast(T, x.x);
-        out[1] = __builtin_bit_cast(T, x.y);
-    } else {
-#pragma unroll
-        for (int i = 0; i < K; i++) out[i] = p[i];
-    }
-}
-
-template <bool BF16>
-__device__ __forceinline__ float4 load_v4(const void *v, int64_t off)
-{
-    if constexpr (BF16) {
-        const uint2 u = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(v) + off);
-        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
-                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
-    } else {
-        return *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(v) + off);
-    }
 }
 
 struct RWArgs {
@@ -87,31 +43,6 @@ struct RWArgs {
     int H, d_v, W, R, Wp, Rp, rec_dwords;
     int64_t nslice, units, per_xcd;
 };
-
-using rsrc_t = __amdgpu_buffer_rsrc_t;
-constexpr uint32_t kOff = 0x80000000u;  // out-of-range buffer offset: loads give 0, stores drop
-constexpr int kRsrcWord3 = 0x00020000;  // gfx9 raw buffer descriptor flags
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
-}
-
-__device__ __forceinline__ float4 buf_load4(rsrc_t r, uint32_t off)
-{
-    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
-}
-
-__device__ __forceinline__ void buf_store4(float4 v, rsrc_t r, uint32_t off)
-{
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v), r, (int)off, 0, 0);
-}
-
-__device__ __forceinline__ float4 fma4(float a, float4 x, float c, float4 v)
-{
-    return make_float4(fmaf(a, x.x, c * v.x), fmaf(a, x.y, c * v.y), fmaf(a, x.z, c * v.z),
-                       fmaf(a, x.w, c * v.w));
-}
 
 // One wavefront = one unit (chain, slice of 4*LPR columns): LPR lanes x float4
 // cover one row of the slice, 64/LPR row groups take that many references at
@@ -143,8 +74,7 @@ __global__ __launch_bounds__(256) void rw_serial_kernel(RWArgs a)
     const rsrc_t Mr = make_rsrc(a.M + chain * a.N * a.d_v, (uint32_t)(a.N * a.d_v * 4));
     const uint32_t *recc = a.rec + chain * T * a.rec_dwords;
     const int64_t hd = (int64_t)a.H * a.d_v;  // stride of one token in v and y
-    const float *vf = reinterpret_cast<const float *>(a.v) + (b * T * a.H + h) * a.d_v + colc;
-    const uint16_t *vh = reinterpret_cast<const uint16_t *>(a.v) + (b * T * a.H + h) * a.d_v + colc;
+    const int64_t vrow0 = (b * T * a.H + h) * a.d_v + colc;  // v of token 0 of the chain
     float *ybase = a.y + (b * T * a.H + h) * a.d_v;
     bool okw[NW], okr[NR];
 #pragma unroll
@@ -176,13 +106,7 @@ __global__ __launch_bounds__(256) void rw_serial_kernel(RWArgs a)
 #pragma unroll
         for (int i = 0; i < NR; i++)
             orr[i] = buf_load4(Mr, (okr[i] & !fwd(ir[i])) ? (ir[i] & kSlotMask) * rowb + col * 4u : kOff);
-        if constexpr (BF16) {
-            const uint2 u = *reinterpret_cast<const uint2 *>(vh + tc * hd);
-            ov = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
-                             __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
-        } else {
-            ov = *reinterpret_cast<const float4 *>(vf + tc * hd);
-        }
+        ov = load_v<BF16>(a.v, vrow0 + tc * hd);
         const float *r = reinterpret_cast<const float *>(recc + tc * a.rec_dwords);
         load_k<NW>(r + a.Wp + g * NW, oa);
         load_k<NW>(r + 2 * a.Wp + g * NW, oc);

@@ -204,7 +204,15 @@ __global__ __launch_bounds__(kSortThreads) void tp_sort_kernel(TPArgs a, SortIO 
 // 64 KiB): a binary search there brackets the slot, a short forward scan of
 // the entries finds the exact range.  One wavefront per token: lane r takes
 // read r, a prefix sum over the lanes places the pairs.
-__global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int stride, int exact)
+//
+// With `stored` (a bfloat16 state) a read must see the row as the state
+// holds it, rounded after every write, which no composed weight can give.
+// There every read keeps weight q, a read that sees in-epoch writes gets the
+// link (first write, count) to replay them, and the token's pair area holds,
+// per read, the first of those writes: token, a, c at [r], [R + r], [2R + r]
+// (3R dwords <= the 2P dwords of the area, as P >= 2R).
+__global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int stride, int exact,
+                                                               int stored)
 {
     extern __shared__ uint16_t ck[];
     const int tid = threadIdx.x;
@@ -266,6 +274,21 @@ __global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int str
             }
             cnt = l2 - j;
         }
+        const int64_t ct = chain * a.T + t0 + tl;
+        if (stored) {  // wave-uniform
+            a.rwt[ct * kMaxK + lane] = q;
+            // j < n <= kMaxEpochEvents and cnt <= E < 2^kCntBits
+            a.rlink[ct * kMaxK + lane] = cnt > 0 ? (((uint32_t)j << kCntBits) | cnt) : 0u;
+            if (cnt > 0) {
+                uint32_t *fw = reinterpret_cast<uint32_t *>(a.pairs + ct * a.P);
+                const TPEntry e = se[j];
+                fw[lane] = e.tw >> 6;
+                fw[a.R + lane] = __float_as_uint(e.a);
+                fw[2 * a.R + lane] = __float_as_uint(e.c);
+            }
+            if (lane == 0) a.npair[ct] = 0u;
+            continue;
+        }
         // exclusive prefix sum of cnt over the lanes: this read's first pair
         int incl = cnt;
 #pragma unroll
@@ -275,7 +298,6 @@ __global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int str
         }
         const int off = incl - cnt;
         const bool fits = off + cnt <= a.P;
-        const int64_t ct = chain * a.T + t0 + tl;
         uint2 *pp = a.pairs + ct * a.P;
         float w = q;
         if (cnt > 0 && fits) {
@@ -302,21 +324,18 @@ __global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int str
 
 // ------------------------------------------------------------------ read
 
-// One wavefront per (chain, token of the epoch, 32-column slice).  With the
-// read plan, y_t = sum_r w_r row_r + sum_j u_j v_(t_j): the 8 row groups take
-// 8 reads at a time (epoch-start rows, as in the serial kernel), then the
-// token's v pairs 8 at a time.  Every load depends only on the plan, so all
-// of them can be in flight together; reads that overflowed the plan replay
-// their writes from the sorted events.
-#ifndef SDM_TP_PAIR_BATCH
-#define SDM_TP_PAIR_BATCH 4
-#endif
-constexpr int kPairBatch = SDM_TP_PAIR_BATCH;  // v pairs per row group in flight
+// Float32 state.  One wavefront per (chain, token of the epoch, 128-byte row
+// slice).  With the read plan, y_t = sum_r w_r row_r + sum_j u_j v_(t_j): the
+// 8 row groups take their NR reads at once (epoch-start rows), then the
+// token's v pairs kPairBatch per group at a time.  Every load depends only on
+// the plan, so all of them can be in flight together; reads that overflowed
+// the plan replay their writes from the sorted events.
+constexpr int kPairBatch = 4;  // v pairs per row group in flight
 
-template <int NR, bool BF16, bool SB>
+template <int NR, bool BF16>
 __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int nslice)
 {
-    using S = StateRow<SB>;
+    using S = StateRow<false>;  // float32 state (a bfloat16 state: tp_read_bf16_kernel)
     constexpr int kLPR = S::kLPR, kRPI = 64 / kLPR;
     const int lane = threadIdx.x & 63;
     const int64_t chain = grid_chain();
@@ -413,6 +432,110 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int nsli
             acc.z = fmaf(wgt, vv[u].z, acc.z);
             acc.w = fmaf(wgt, vv[u].w, acc.w);
         }
+    }
+#pragma unroll
+    for (int m = kLPR; m < 64; m <<= 1) {
+        acc.x += __shfl_xor(acc.x, m, 64);
+        acc.y += __shfl_xor(acc.y, m, 64);
+        acc.z += __shfl_xor(acc.z, m, 64);
+        acc.w += __shfl_xor(acc.w, m, 64);
+    }
+    if (g == 0 && col_ok)
+        *reinterpret_cast<float4 *>(a.y + (b * a.T * a.H + t * a.H + h) * a.d_v + col) = acc;
+}
+
+// Read with a bfloat16 state.  The state holds every written row rounded
+// to bfloat16, so a read of a slot written earlier in the epoch (at a token
+// <= its own) must see the row after each of those writes, rounded: it
+// replays them on the epoch-start row with the update kernel's own
+// operations, S::round(a*row + c*v) in time order.  One wavefront per
+// (chain, token of the epoch, 128-byte row slice), 16 lanes per row group,
+// group g taking reads g*NR .. g*NR + NR-1; lane q of the group holds read
+// g*NR + q: slot word, weight q, link (first write, count) and the first
+// write's token, a and c from the plan.  The row gathers and the first
+// writes' v gathers depend only on the plan and are all issued before any
+// arithmetic; a read with two or more in-epoch writes takes the rest from the
+// sorted events (about one read in eleven at the 1.4B-style layer).
+template <int NR, bool BF16>
+__global__ __launch_bounds__(256) void tp_read_bf16_kernel(TPArgs a, int ep, int nslice)
+{
+    using S = StateRow<true>;
+    constexpr int kLPR = S::kLPR;
+    const int lane = threadIdx.x & 63;
+    const int64_t chain = grid_chain();
+    const int64_t t0 = (int64_t)ep * a.E;
+    const int ne = (int)((a.T - t0) < a.E ? (a.T - t0) : a.E);
+    const uint32_t u = blockIdx.x * 4u + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (chain >= a.chains || u >= (uint32_t)(ne * nslice)) return;
+    const int slice = (int)(u % (uint32_t)nslice);
+    const int tl = (int)(u / (uint32_t)nslice);
+    const int64_t t = t0 + tl;
+    const int64_t ct = chain * a.T + t;
+    const int g = lane / kLPR, q = lane % kLPR;
+    const int col = slice * 4 * kLPR + q * 4;
+    const bool col_ok = col < a.d_v;
+    const int colc = col_ok ? col : 0;
+    // chains < 2^32 (the grid's y and z), so 32-bit division
+    const int64_t b = (uint32_t)chain / (uint32_t)a.H;
+    const int h = (int)(chain - b * a.H);
+    const int64_t hd = (int64_t)a.H * a.d_v;
+    const int64_t vrow0 = (b * a.T * a.H + h) * a.d_v + colc;  // v of token 0 of the chain
+    const rsrc_t Mr = make_rsrc(static_cast<char *>(a.M) + chain * a.N * a.d_v * S::kElem,
+                                (uint32_t)(a.N * a.d_v * S::kElem));
+    const uint32_t rowb = (uint32_t)a.d_v * S::kElem;
+    const uint32_t *rc = a.rec + ct * a.rec_dwords;
+    const TPEntry *se = a.sorted + chain * a.T * a.W + t0 * a.W;
+    const uint32_t *fw = reinterpret_cast<const uint32_t *>(a.pairs + ct * a.P);
+
+    const int r = g * NR + q;
+    const bool mine = (q < NR) & (r < a.R);
+    const uint32_t sl_mine = mine ? rc[3 * a.Wp + r] : 0u;
+    const float wr_mine = mine ? a.rwt[ct * kMaxK + r] : 0.0f;
+    const uint32_t lk_mine = mine ? a.rlink[ct * kMaxK + r] : 0u;
+    uint32_t t1_mine = 0u, a1_mine = 0u, c1_mine = 0u;
+    if (lk_mine != 0u) {
+        t1_mine = fw[r];
+        a1_mine = fw[a.R + r];
+        c1_mine = fw[2 * a.R + r];
+    }
+    typename S::Raw row[NR];
+#pragma unroll
+    for (int i = 0; i < NR; i++) {
+        const uint32_t sl = group_bcast<kLPR>(sl_mine, i);
+        const bool ok = col_ok & (g * NR + i < a.R);
+        row[i] = S::load_raw(Mr, ok ? (sl & kSlotMask) * rowb + col * S::kElem : kOff);
+    }
+    // v of each read's first in-epoch write (the group shares the read, so
+    // the condition is uniform within the group)
+    float4 v1[NR];
+#pragma unroll
+    for (int i = 0; i < NR; i++) {
+        const uint32_t lk = group_bcast<kLPR>(lk_mine, i);
+        const uint32_t t1 = group_bcast<kLPR>(t1_mine, i);
+        v1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (lk != 0u) v1[i] = load_v<BF16>(a.v, vrow0 + (t0 + t1) * hd);
+    }
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < NR; i++) {
+        const uint32_t lk = group_bcast<kLPR>(lk_mine, i);
+        const float a1 = __uint_as_float(group_bcast<kLPR>(a1_mine, i));
+        const float c1 = __uint_as_float(group_bcast<kLPR>(c1_mine, i));
+        const float wr = __uint_as_float(group_bcast<kLPR>(__float_as_uint(wr_mine), i));
+        float4 rv = S::widen(row[i]);
+        if (lk != 0u) {
+            rv = S::round(fma4(a1, rv, c1, v1[i]));
+            const int first = (int)(lk >> kCntBits), cnt = (int)(lk & ((1u << kCntBits) - 1u));
+            for (int k = 1; k < cnt; k++) {  // further writes of this slot earlier in the epoch
+                const TPEntry e = se[first + k];
+                const float4 vv = load_v<BF16>(a.v, vrow0 + (t0 + (e.tw >> 6)) * hd);
+                rv = S::round(fma4(e.a, rv, e.c, vv));
+            }
+        }
+        acc.x = fmaf(wr, rv.x, acc.x);
+        acc.y = fmaf(wr, rv.y, acc.y);
+        acc.z = fmaf(wr, rv.z, acc.z);
+        acc.w = fmaf(wr, rv.w, acc.w);
     }
 #pragma unroll
     for (int m = kLPR; m < 64; m <<= 1) {
@@ -591,18 +714,14 @@ __global__ __launch_bounds__(256, SB ? 6 : 1) void tp_update_kernel(TPArgs a, in
 
 }  // namespace
 
-#ifndef SDM_TP_EPOCH_LOG2
-#define SDM_TP_EPOCH_LOG2 0
-#endif
-
 int tp_epoch_len(const Shape &s)
 {
     // E <= kMaxEpoch and E*W <= kMaxEpochEvents (replay links pack an event
-    // position and a count into 32 bits), and E*W <= 2^SDM_TP_EPOCH_LOG2 * N:
-    // longer epochs merge more repeated writes to a slot, but every read
-    // then carries more v pairs from in-epoch writes.
-    const int64_t cap = SDM_TP_EPOCH_LOG2 >= 0 ? s.N() << SDM_TP_EPOCH_LOG2
-                                               : s.N() >> -SDM_TP_EPOCH_LOG2;
+    // position and a count into 32 bits), and E*W <= N: longer epochs merge
+    // more repeated writes to a slot, but every read then carries more v
+    // pairs from in-epoch writes (write/read at the 1.4B-style layer with
+    // E*W = N/2, N, 2N: 9.13, 8.25, 8.67 ms).
+    const int64_t cap = s.N();
     int64_t e = kMaxEpoch;
     while (e > 1 && (e * s.W > kMaxEpochEvents || e * s.W > cap)) e >>= 1;
     if (e > s.T) {
@@ -689,7 +808,7 @@ bool tp_supported(const Shape &s)
 }
 
 hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipStream_t st,
-                             int ep0, int ep1, bool link)
+                             int ep0, int ep1, bool link, bool state_bf16)
 {
     TPArgs a = tp_args(s, rec, ws, nullptr, nullptr, nullptr);
     if (ep1 < 0 || ep1 > a.nepoch) ep1 = a.nepoch;
@@ -710,7 +829,7 @@ hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipS
     const int exact = stride == 1 && a.kshift == 0 && nmax <= 16384;
     const size_t lds = (size_t)((nmax + stride - 1) / stride) * sizeof(uint16_t) * (exact ? 2 : 1);
     hipLaunchKernelGGL(tp_link_kernel, dim3((unsigned)blocks), dim3(kSortThreads), lds, st, a,
-                       stride, exact);
+                       stride, exact, state_bf16 ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -725,17 +844,31 @@ static hipError_t tp_apply_state(const Shape &s, TPArgs a, bool bf16, hipStream_
         const int64_t t0 = (int64_t)ep * a.E;
         const int ne = (int)((s.T - t0) < a.E ? (s.T - t0) : a.E);
         const dim3 rgrid = chain_grid(a.chains, (int64_t)ne * nslice);
+        if constexpr (SB) {  // stored-value reads (rows rounded after every write)
 #define SDM_TP_READ(NR_)                                                                          \
     if (nr <= NR_) {                                                                              \
-        if (bf16) hipLaunchKernelGGL((tp_read_kernel<NR_, true, SB>), rgrid, dim3(256), 0, st, a, \
-                                     ep, nslice);                                                 \
-        else hipLaunchKernelGGL((tp_read_kernel<NR_, false, SB>), rgrid, dim3(256), 0, st, a, ep, \
+        if (bf16) hipLaunchKernelGGL((tp_read_bf16_kernel<NR_, true>), rgrid, dim3(256), 0, st,   \
+                                     a, ep, nslice);                                              \
+        else hipLaunchKernelGGL((tp_read_bf16_kernel<NR_, false>), rgrid, dim3(256), 0, st, a,    \
+                                ep, nslice);                                                      \
+    } else
+            SDM_TP_READ(1) SDM_TP_READ(2) SDM_TP_READ(4) SDM_TP_READ(8) SDM_TP_READ(16) {
+                return hipErrorInvalidValue;
+            }
+#undef SDM_TP_READ
+        } else {
+#define SDM_TP_READ(NR_)                                                                          \
+    if (nr <= NR_) {                                                                              \
+        if (bf16) hipLaunchKernelGGL((tp_read_kernel<NR_, true>), rgrid, dim3(256), 0, st, a, ep, \
+                                     nslice);                                                     \
+        else hipLaunchKernelGGL((tp_read_kernel<NR_, false>), rgrid, dim3(256), 0, st, a, ep,     \
                                 nslice);                                                          \
     } else
-        SDM_TP_READ(1) SDM_TP_READ(2) SDM_TP_READ(4) SDM_TP_READ(8) SDM_TP_READ(16) {
-            return hipErrorInvalidValue;
-        }
+            SDM_TP_READ(1) SDM_TP_READ(2) SDM_TP_READ(4) SDM_TP_READ(8) SDM_TP_READ(16) {
+                return hipErrorInvalidValue;
+            }
 #undef SDM_TP_READ
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         // sorted events per row group (measured at the 1.4B-style layer,

@@ -284,7 +284,7 @@ sdm_status sdm_prepare(sdm_handle h, int B, int64_t T, const void *kp, const voi
     if (var == SDM_VARIANT_TIMEPAR) {
         if (!sdm::decode_supported(s)) {  // one token: nothing to sort (see sdm_apply)
             char *tp = static_cast<char *>(workspace) + records_bytes(h, B, T);
-            e = sdm::launch_tp_prepare(s, rec, tp, hs);
+            e = sdm::launch_tp_prepare(s, rec, tp, hs, 0, -1, true, h->state_bf16);
             if (e != hipSuccess) return hip_fail(e, "time-parallel sort launch");
         }
     } else if (sdm::rw_serial_supported(s)) {

@@ -110,9 +110,12 @@ hipError_t launch_rw_simple(const Shape &s, const uint32_t *rec, const void *v, 
 bool tp_supported(const Shape &s);
 int tp_epoch_len(const Shape &s);
 size_t tp_workspace_bytes(const Shape &s);  // beyond the token records
-// Epochs [ep0, ep1) (ep1 < 0: through the last epoch).
+// Epochs [ep0, ep1) (ep1 < 0: through the last epoch).  With state_bf16
+// the read plan is the one of stored-value reads (rows rounded after every
+// write): weights q and links to each read's in-epoch writes.
 hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipStream_t st,
-                             int ep0 = 0, int ep1 = -1, bool link = true);
+                             int ep0 = 0, int ep1 = -1, bool link = true,
+                             bool state_bf16 = false);
 hipError_t launch_tp_apply(const Shape &s, const uint32_t *rec, void *ws, const void *v,
                            bool bf16, float *y, void *M, bool state_bf16, hipStream_t st,
                            int ep0 = 0, int ep1 = -1);
