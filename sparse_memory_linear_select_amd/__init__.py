@@ -70,9 +70,7 @@ def lib():
         L.sdm_backward_workspace_size.argtypes = [p, i, i64, i, ctypes.POINTER(sz)]
         L.sdm_backward.argtypes = [p, i, i64, p, p, p, p, p, i, p, p, p, p, sz, p, p, p, p, p,
                                    p, p, p]
-        for f in ("sdm_backward", "sdm_backward_workspace_size", "sdm_create", "sdm_create_ex",
-                  "sdm_destroy", "sdm_workspace_size", "sdm_select", "sdm_forward",
-                  "sdm_prepare", "sdm_apply", "sdm_write_histogram"):
+        for f in EXPORTS[:-2]:
             getattr(L, f).restype = ctypes.c_int
         L.sdm_status_string.argtypes = [i]
         L.sdm_status_string.restype = ctypes.c_char_p
@@ -114,6 +112,34 @@ def _dev_tensor(t: torch.Tensor, name: str, dtype=None):
     if dtype is not None and t.dtype != dtype:
         raise SDMError(1, f"{name} must be {dtype}, got {t.dtype}")
     return t
+
+
+def _same_device(t: torch.Tensor, ref: torch.Tensor, name: str):
+    if t.device != ref.device:
+        raise SDMError(1, f"{name} is on {t.device}, the inputs on {ref.device}")
+    return t
+
+
+def _out_tensor(t, name: str, shape: tuple, dtype, ref: torch.Tensor):
+    """A caller-supplied output: a contiguous GPU tensor of exactly this shape
+    and dtype on the inputs' device (the kernels write through its pointer)."""
+    _dev_tensor(t, name, dtype)
+    _same_device(t, ref, name)
+    if tuple(t.shape) != tuple(shape):
+        raise SDMError(1, f"{name} must be {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _workspace(ws, need: int, ref: torch.Tensor):
+    """The caller's workspace (a contiguous uint8 GPU tensor on the inputs'
+    device with at least `need` bytes), or a new one."""
+    if ws is None:
+        return torch.empty(max(need, 16), dtype=torch.uint8, device=ref.device)
+    _dev_tensor(ws, "workspace", torch.uint8)
+    _same_device(ws, ref, "workspace")
+    if ws.numel() < need:
+        raise SDMError(3, f"workspace has {ws.numel()} bytes, needs {need}")
+    return ws
 
 
 def _in_dtype(t: torch.Tensor) -> int:
@@ -177,13 +203,19 @@ class SDM:
         if qp.shape != kp.shape or qp.dtype != kp.dtype:
             raise SDMError(1, "qp must match kp in shape and dtype")
         dev = kp.device
+        _same_device(qp, kp, "qp")
+        shp_w, shp_r = (B, T, self.H, self.W), (B, T, self.H, self.R)
         if out is None:
-            Iw = torch.empty((B, T, self.H, self.W), dtype=torch.int32, device=dev)
-            kw = torch.empty((B, T, self.H, self.W), dtype=torch.float32, device=dev)
-            Ir = torch.empty((B, T, self.H, self.R), dtype=torch.int32, device=dev)
-            qw = torch.empty((B, T, self.H, self.R), dtype=torch.float32, device=dev)
+            Iw = torch.empty(shp_w, dtype=torch.int32, device=dev)
+            kw = torch.empty(shp_w, dtype=torch.float32, device=dev)
+            Ir = torch.empty(shp_r, dtype=torch.int32, device=dev)
+            qw = torch.empty(shp_r, dtype=torch.float32, device=dev)
         else:
             Iw, kw, Ir, qw = out
+            _out_tensor(Iw, "Iw", shp_w, torch.int32, kp)
+            _out_tensor(kw, "kw", shp_w, torch.float32, kp)
+            _out_tensor(Ir, "Ir", shp_r, torch.int32, kp)
+            _out_tensor(qw, "qw", shp_r, torch.float32, kp)
         _check(lib().sdm_select(self._h, B, T, _ptr(kp), _ptr(qp), _in_dtype(kp), _ptr(Iw),
                                 _ptr(kw), _ptr(Ir), _ptr(qw), _stream(dev)))
         return Iw, kw, Ir, qw
@@ -195,9 +227,7 @@ class SDM:
         B, T = self._shape_in(kp, 2 * self.sqrtN, "kp")
         if counts is None:
             counts = torch.zeros((self.H, self.N), dtype=torch.int32, device=kp.device)
-        _dev_tensor(counts, "counts", torch.int32)
-        if tuple(counts.shape) != (self.H, self.N):
-            raise SDMError(1, f"counts must be [H, N] = [{self.H}, {self.N}]")
+        _out_tensor(counts, "counts", (self.H, self.N), torch.int32, kp)
         _check(lib().sdm_write_histogram(self._h, B, T, _ptr(kp), _in_dtype(kp), _ptr(counts),
                                          _stream(kp.device)))
         return counts
@@ -222,17 +252,17 @@ class SDM:
         if tuple(alpha.shape) != (B, T, self.H) or tuple(beta.shape) != (B, T, self.H):
             raise SDMError(1, "alpha and beta must be [B, T, H]")
         sshape = (B, self.H, self.N, self.d_v)
+        for t, nm in ((qp, "qp"), (v, "v"), (alpha, "alpha"), (beta, "beta"), (dy, "dy"),
+                      (self.M0, "M0")):
+            _same_device(t, kp, nm)
         for t, nm in ((dMT, "dMT"), (Minit, "Minit")):
             if t is not None:
-                _dev_tensor(t, nm, torch.float32)
-                if tuple(t.shape) != sshape:
-                    raise SDMError(1, f"{nm} must be [B, H, N, d_v]")
+                _out_tensor(t, nm, sshape, torch.float32, kp)
         dev = kp.device
         dt = _in_dtype(kp)
         n = ctypes.c_size_t()
         _check(lib().sdm_backward_workspace_size(self._h, B, T, dt, ctypes.byref(n)))
-        if workspace is None or workspace.numel() < n.value:
-            workspace = torch.empty(max(n.value, 16), dtype=torch.uint8, device=dev)
+        workspace = _workspace(workspace, n.value, kp)
         f32 = dict(dtype=torch.float32, device=dev)
         out = dict(dkp=torch.empty((B, T, self.H, 2 * self.sqrtN), **f32),
                    dqp=torch.empty((B, T, self.H, 2 * self.sqrtN), **f32),
@@ -248,14 +278,8 @@ class SDM:
             _ptr(out["dMinit"]), _ptr(out.get("dM0")), _stream(dev)))
         return out
 
-    def forward(self, kp, qp, v, alpha, beta, variant: int = AUTO, y=None, M=None,
-                workspace=None, cont: bool = False, staged: bool = False):
-        """(y, M): outputs [B,T,H,d_v] and final state [B,H,N,d_v] (float32).
-
-        With cont=True, M must hold the state to continue from (no M <- M_0).
-        staged=True issues sdm_prepare + sdm_apply instead of sdm_forward
-        (the same work on the same stream).
-        """
+    def _forward_args(self, kp, qp, v, alpha, beta, y, M, cont):
+        """Validated (B, T, input dtype code, y, M) of a forward call."""
         for t, n in ((kp, "kp"), (qp, "qp"), (v, "v")):
             _dev_tensor(t, n)
         _dev_tensor(alpha, "alpha", torch.float32)
@@ -267,21 +291,30 @@ class SDM:
             raise SDMError(1, f"v must be [B, T, H, d_v], got {tuple(v.shape)}")
         if tuple(alpha.shape) != (B, T, self.H) or tuple(beta.shape) != (B, T, self.H):
             raise SDMError(1, "alpha and beta must be [B, T, H]")
+        for t, n in ((qp, "qp"), (v, "v"), (alpha, "alpha"), (beta, "beta"), (self.M0, "M0")):
+            _same_device(t, kp, n)
         dev = kp.device
-        dt = _in_dtype(kp)
         if y is None:
             y = torch.empty((B, T, self.H, self.d_v), dtype=torch.float32, device=dev)
         if M is None:
             if cont:
                 raise SDMError(1, "cont=True needs the state M")
             M = torch.empty((B, self.H, self.N, self.d_v), dtype=self.state, device=dev)
-        _dev_tensor(y, "y", torch.float32)
-        _dev_tensor(M, "M", self.state)
-        if tuple(M.shape) != (B, self.H, self.N, self.d_v) or tuple(y.shape) != tuple(v.shape):
-            raise SDMError(1, "y or M has the wrong shape")
-        need = self.workspace_size(B, T, dt, variant)
-        if workspace is None or workspace.numel() < need:
-            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        _out_tensor(y, "y", (B, T, self.H, self.d_v), torch.float32, kp)
+        _out_tensor(M, "M", (B, self.H, self.N, self.d_v), self.state, kp)
+        return B, T, _in_dtype(kp), y, M
+
+    def forward(self, kp, qp, v, alpha, beta, variant: int = AUTO, y=None, M=None,
+                workspace=None, cont: bool = False, staged: bool = False):
+        """(y, M): outputs [B,T,H,d_v] and final state [B,H,N,d_v] (float32).
+
+        With cont=True, M must hold the state to continue from (no M <- M_0).
+        staged=True issues sdm_prepare + sdm_apply instead of sdm_forward
+        (the same work on the same stream).
+        """
+        B, T, dt, y, M = self._forward_args(kp, qp, v, alpha, beta, y, M, cont)
+        dev = kp.device
+        workspace = _workspace(workspace, self.workspace_size(B, T, dt, variant), kp)
         flags = FLAG_CONTINUE if cont else 0
         if staged:
             _check(lib().sdm_prepare(self._h, B, T, _ptr(kp), _ptr(qp), _ptr(alpha), _ptr(beta),

@@ -223,6 +223,29 @@ def test_forward_rejects_bad_tensors():
     with pytest.raises(sdm.SDMError) as e:
         core.forward(dd["kp"], dd["qp"], dd["v"], dd["alpha"], dd["beta"], variant=7)
     assert e.value.status == 1
+    args = [dd[n] for n in ("kp", "qp", "v", "alpha", "beta")]
+    B, T = wl.B, wl.T
+    y_ok = torch.empty((B, T, wl.H, wl.d_v), device="cuda")
+    M_ok = torch.empty((B, wl.H, wl.N, wl.d_v), device="cuda")
+    need = core.workspace_size(B, T)
+    # caller-supplied outputs and workspace are checked on the host: wrong
+    # device, dtype, shape or size raise before anything is enqueued
+    bad_out = [dict(y=y_ok.cpu()), dict(y=y_ok[:, :-1]), dict(M=M_ok.cpu()), dict(M=M_ok[:1]),
+               dict(M=M_ok.to(torch.bfloat16)),
+               dict(workspace=torch.empty(need, dtype=torch.uint8)),
+               dict(workspace=torch.empty(need // 4 + 1, dtype=torch.float32, device="cuda")),
+               dict(workspace=torch.empty(need - 1, dtype=torch.uint8, device="cuda"))]
+    for kw in bad_out:
+        kw = {**dict(y=y_ok, M=M_ok), **kw}
+        with pytest.raises(sdm.SDMError):
+            core.forward(*args, **kw)
+    Iw, kw_, Ir, qw = core.select(dd["kp"], dd["qp"])
+    for bad in ((Iw.cpu(), kw_, Ir, qw), (Iw, kw_[:, :1], Ir, qw), (Iw, kw_, Ir.float(), qw),
+                (Iw, kw_, Ir, qw.transpose(0, 1))):
+        with pytest.raises(sdm.SDMError):
+            core.select(dd["kp"], dd["qp"], out=bad)
+    with pytest.raises(sdm.SDMError):
+        core.write_histogram(dd["kp"], torch.zeros((wl.H, wl.N), dtype=torch.int32))
     wl2, d2 = _small(29, d_v=30)
     dd2 = upload(d2)
     core2 = make_core(dd2, wl2.W, wl2.R)
