@@ -178,6 +178,29 @@ sdm_status sdm_forward(sdm_handle h, int B, int64_t T, const void *kp, const voi
                        void *stream);
 
 /*
+ * sdm_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops such as
+ * one-token decode steps, harnesses that forbid allocation).  The scratch is
+ * a static device array of SDM_NOALLOC_MAX_BYTES that the library holds on
+ * each GPU it runs on until the process ends; the call allocates nothing.
+ * Arguments, results and errors as sdm_forward, plus SDM_ERR_UNSUPPORTED
+ * when sdm_workspace_size(...) for the call exceeds SDM_NOALLOC_MAX_BYTES
+ * (a one-token step of every layer shape within the limits above fits; so
+ * do a few hundred tokens of the shapes with sqrtN <= 128).  The first call
+ * on a device looks up that device's scratch address (a HIP call; the
+ * stream's device is made current for it and restored).  Every call on one
+ * GPU uses the same scratch: calls that overlap on one GPU (other streams,
+ * other threads) race and must be ordered by the caller.  Nothing in the
+ * scratch needs to start at zero.
+ */
+#define SDM_NOALLOC_MAX_BYTES (64u << 20)
+
+sdm_status sdm_forward_noalloc(sdm_handle h, int B, int64_t T, const void *kp, const void *qp,
+                               const void *v, const float *alpha, const float *beta,
+                               sdm_dtype dtype, sdm_variant variant, unsigned flags, float *y,
+                               void *M, void *stream);
+
+/*
  * The two halves of sdm_forward, for callers that time or pipeline them.
  * sdm_forward(...) is sdm_prepare(...) followed by sdm_apply(...) with the
  * same handle, shapes, dtype, variant and workspace.

@@ -20,7 +20,7 @@ import os
 import torch
 
 __all__ = ["SDM", "SDMError", "lib", "lib_path", "F32", "BF16", "AUTO", "SERIAL", "TIMEPAR",
-           "FLAG_CONTINUE", "EXPORTS"]
+           "FLAG_CONTINUE", "EXPORTS", "NOALLOC_MAX_BYTES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsdm.so")
@@ -35,8 +35,9 @@ STATUS = {0: "SDM_OK", 1: "SDM_ERR_ARG", 2: "SDM_ERR_UNSUPPORTED", 3: "SDM_ERR_W
 # every function include/sdm.h declares
 EXPORTS = ("sdm_backward", "sdm_backward_workspace_size", "sdm_create", "sdm_create_ex",
            "sdm_destroy", "sdm_workspace_size", "sdm_select", "sdm_forward",
-           "sdm_prepare", "sdm_apply", "sdm_write_histogram", "sdm_status_string",
-           "sdm_last_error")
+           "sdm_forward_noalloc", "sdm_prepare", "sdm_apply", "sdm_write_histogram",
+           "sdm_status_string", "sdm_last_error")
+NOALLOC_MAX_BYTES = 64 << 20  # SDM_NOALLOC_MAX_BYTES: the static scratch of sdm_forward_noalloc
 
 
 class SDMError(RuntimeError):
@@ -64,6 +65,7 @@ def lib():
         L.sdm_workspace_size.argtypes = [p, i, i64, i, i, ctypes.POINTER(sz)]
         L.sdm_select.argtypes = [p, i, i64, p, p, i, p, p, p, p, p]
         L.sdm_forward.argtypes = [p, i, i64, p, p, p, p, p, i, i, ctypes.c_uint, p, sz, p, p, p]
+        L.sdm_forward_noalloc.argtypes = [p, i, i64, p, p, p, p, p, i, i, ctypes.c_uint, p, p, p]
         L.sdm_prepare.argtypes = [p, i, i64, p, p, p, p, i, i, ctypes.c_uint, p, sz, p, p]
         L.sdm_apply.argtypes = [p, i, i64, p, i, i, p, sz, p, p, p]
         L.sdm_write_histogram.argtypes = [p, i, i64, p, i, p, p]
@@ -303,6 +305,21 @@ class SDM:
         _out_tensor(y, "y", (B, T, self.H, self.d_v), torch.float32, kp)
         _out_tensor(M, "M", (B, self.H, self.N, self.d_v), self.state, kp)
         return B, T, _in_dtype(kp), y, M
+
+    def forward_noalloc(self, kp, qp, v, alpha, beta, y, M, variant: int = AUTO,
+                        cont: bool = False):
+        """sdm_forward_noalloc: as forward(), with the library's static scratch
+        in place of a workspace, so the call allocates no device memory (y and
+        M are the caller's).  For callers that cannot allocate: HIP graph
+        capture, serving loops.  Raises SDMError (SDM_ERR_UNSUPPORTED) when the
+        call needs more than NOALLOC_MAX_BYTES of scratch; calls that overlap
+        on one GPU share the scratch and race."""
+        B, T, dt, y, M = self._forward_args(kp, qp, v, alpha, beta, y, M, cont)
+        flags = FLAG_CONTINUE if cont else 0
+        _check(lib().sdm_forward_noalloc(self._h, B, T, _ptr(kp), _ptr(qp), _ptr(v), _ptr(alpha),
+                                         _ptr(beta), dt, variant, flags, _ptr(y), _ptr(M),
+                                         _stream(kp.device)))
+        return y, M
 
     def forward(self, kp, qp, v, alpha, beta, variant: int = AUTO, y=None, M=None,
                 workspace=None, cont: bool = False, staged: bool = False):

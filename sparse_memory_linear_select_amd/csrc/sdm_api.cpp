@@ -6,10 +6,18 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <new>
 #include <string>
 
 #include "sdm_internal.h"
+
+// Scratch of sdm_forward_noalloc: the workspace of one forward call, in a
+// static device array (each GPU the library runs on holds its own copy
+// until the process ends).  Host code never uses the name `scratch` as an
+// address: it looks up each device's address once (scratch_on) and passes
+// that to the kernels.
+static __device__ __align__(256) unsigned char scratch[SDM_NOALLOC_MAX_BYTES];
 
 struct sdm_ctx {
     const float *M0 = nullptr;
@@ -136,6 +144,39 @@ sdm_status check_backward(const sdm_ctx *h, int B, int64_t T)
         return fail(SDM_ERR_UNSUPPORTED,
                     "the backward runs on the time-parallel schedule: d_v %% 4 == 0 and "
                     "N*d_v*4 <= 2^31");
+    return SDM_OK;
+}
+
+// Device address of `scratch` on the device of `stream` (the current device
+// for the null stream), looked up once per device with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+sdm_status scratch_on(hipStream_t stream, void **out)
+{
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "device of the stream");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(SDM_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev,
+                    kMaxDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return hip_fail(e, "current device");
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "set device");
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return hip_fail(e, "address of the static scratch");
+        if (!p) return fail(SDM_ERR_HIP, "address of the static scratch: null");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
     return SDM_OK;
 }
 
@@ -356,6 +397,35 @@ sdm_status sdm_forward(sdm_handle h, int B, int64_t T, const void *kp, const voi
                      stream);
     if (st != SDM_OK) return st;
     return sdm_apply(h, B, T, v, dtype, variant, workspace, ws_bytes, y, M, stream);
+}
+
+sdm_status sdm_forward_noalloc(sdm_handle h, int B, int64_t T, const void *kp, const void *qp,
+                               const void *v, const float *alpha, const float *beta,
+                               sdm_dtype dtype, sdm_variant variant, unsigned flags, float *y,
+                               void *M, void *stream)
+{
+    sdm_status st = check_handle_call(h, B, T, dtype);
+    if (st != SDM_OK) return st;
+    if (!kp || !qp || !v || !alpha || !beta || !y || !M)
+        return fail(SDM_ERR_ARG, "null tensor pointer");
+    if (!aligned16(kp) || !aligned16(qp) || !aligned16(v) || !aligned16(alpha) ||
+        !aligned16(beta) || !aligned16(y) || !aligned16(M))
+        return fail(SDM_ERR_ARG, "tensor pointers must be 16-byte aligned");
+    if (flags & ~SDM_FLAG_CONTINUE) return fail(SDM_ERR_ARG, "unknown flags 0x%x", flags);
+    sdm_variant var;
+    st = check_variant(h, B, T, variant, &var);
+    if (st != SDM_OK) return st;
+    const size_t need = ws_bytes_for(h, B, T, var);
+    if (need > (size_t)SDM_NOALLOC_MAX_BYTES)
+        return fail(SDM_ERR_UNSUPPORTED,
+                    "this call needs %zu bytes of scratch; the static scratch holds %zu "
+                    "(fewer sequences or tokens per call, or sdm_forward with a workspace)",
+                    need, (size_t)SDM_NOALLOC_MAX_BYTES);
+    void *ws = nullptr;
+    st = scratch_on((hipStream_t)stream, &ws);
+    if (st != SDM_OK) return st;
+    return sdm_forward(h, B, T, kp, qp, v, alpha, beta, dtype, variant, flags, ws,
+                       (size_t)SDM_NOALLOC_MAX_BYTES, y, M, stream);
 }
 
 }  // extern "C"

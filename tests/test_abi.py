@@ -98,6 +98,42 @@ def test_forward_rejects_before_any_device_work():
         sdm.lib().sdm_destroy(h)
 
 
+def _forward_noalloc(h, B=1, T=8, ptrs=None, flags=0):
+    p = dict(kp=FAKE, qp=FAKE, v=FAKE, alpha=FAKE, beta=FAKE, y=FAKE, M=FAKE)
+    p.update(ptrs or {})
+    c = lambda x: ctypes.c_void_p(x) if x else None
+    return sdm.lib().sdm_forward_noalloc(h, B, T, c(p["kp"]), c(p["qp"]), c(p["v"]),
+                                         c(p["alpha"]), c(p["beta"]), sdm.F32, sdm.AUTO, flags,
+                                         c(p["y"]), c(p["M"]), None)
+
+
+def test_forward_noalloc_rejects_before_any_device_work():
+    """Invalid arguments, and calls whose scratch would exceed the static
+    array, fail before the first HIP call (no device is needed to see it)."""
+    st, h = _create()
+    L = sdm.lib()
+    try:
+        for name in ("kp", "qp", "v", "alpha", "beta", "y", "M"):
+            assert _forward_noalloc(h, ptrs={name: 0}) == 1, name
+            assert _forward_noalloc(h, ptrs={name: FAKE + 8}) == 1, name
+        assert _forward_noalloc(None) == 1
+        assert _forward_noalloc(h, B=0) == 1
+        assert _forward_noalloc(h, flags=4) == 1
+        n = ctypes.c_size_t()
+        assert L.sdm_workspace_size(h, 64, 4096, sdm.F32, sdm.AUTO, ctypes.byref(n)) == 0
+        assert n.value > sdm.NOALLOC_MAX_BYTES
+        assert _forward_noalloc(h, B=64, T=4096) == 2
+        assert b"static scratch" in L.sdm_last_error()
+    finally:
+        L.sdm_destroy(h)
+
+
+def test_noalloc_limit_matches_header():
+    text = open(os.path.join(ROOT, "include", "sdm.h")).read()
+    m = re.search(r"#define SDM_NOALLOC_MAX_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == sdm.NOALLOC_MAX_BYTES
+
+
 def test_select_rejects_before_any_device_work():
     st, h = _create()
     L = sdm.lib()

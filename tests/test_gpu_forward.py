@@ -239,6 +239,8 @@ def test_forward_rejects_bad_tensors():
         kw = {**dict(y=y_ok, M=M_ok), **kw}
         with pytest.raises(sdm.SDMError):
             core.forward(*args, **kw)
+    with pytest.raises(sdm.SDMError):
+        core.forward_noalloc(*args, y=y_ok.cpu(), M=M_ok)
     Iw, kw_, Ir, qw = core.select(dd["kp"], dd["qp"])
     for bad in ((Iw.cpu(), kw_, Ir, qw), (Iw, kw_[:, :1], Ir, qw), (Iw, kw_, Ir.float(), qw),
                 (Iw, kw_, Ir, qw.transpose(0, 1))):
