@@ -196,11 +196,8 @@ def backward(args, wl):
     dy = torch.randn((wl.B, wl.T, wl.H, wl.d_v), device=dev, generator=g)
     dMT = torch.randn((wl.B, wl.H, wl.N, wl.d_v), device=dev, generator=g)
     dt_code = sdm.BF16 if wl.dtype == "bf16" else sdm.F32
-    import ctypes
-    nb = ctypes.c_size_t()
-    sdm._check(sdm.lib().sdm_backward_workspace_size(core._h, wl.B, wl.T, dt_code,
-                                                     ctypes.byref(nb)))
-    ws = torch.empty(nb.value, dtype=torch.uint8, device=dev)
+    nb = core.backward_workspace_size(wl.B, wl.T, dt_code, args.backward_chunks)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
     for _ in range(args.warmup):
         core.backward(*args_, dy, dMT=dMT, workspace=ws)
     torch.cuda.synchronize()
@@ -215,7 +212,8 @@ def backward(args, wl):
         "metric": "SDM backward head-tokens/s (forward recompute + reverse, selections fixed)",
         "value": wl.head_tokens / (ms * 1e-3), "unit": "head-tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
-        "workspace_gb": nb.value / 1e9,
+        "workspace_gb": nb / 1e9,
+        "chunks": args.backward_chunks or "least memory",
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": wl.H, "sqrtN": wl.sqrtN,
                    "d_v": wl.d_v, "W": wl.W, "R": wl.R, "inputs": wl.dtype},
         "data": "synthetic (seeded; recipe in sdm_inputs.py)"}), flush=True)
@@ -239,6 +237,9 @@ def main():
                     help="measure one-token decode steps (continuing the state) instead")
     ap.add_argument("--backward", action="store_true",
                     help="measure the backward (sdm_backward: forward recompute + reverse) instead")
+    ap.add_argument("--backward-chunks", type=int, default=0,
+                    help="backward workspace sized for this many chunks of epochs (0: the least "
+                         "memory; 1: the whole sequence at once)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -246,16 +246,24 @@ sdm_status sdm_write_histogram(sdm_handle h, int B, int64_t T, const void *kp,
  * follow from it by the chain rule.
  *
  * The call recomputes the forward (selection, then the writes, recording
- * the row every write replaces) and runs the tokens in reverse on the
- * time-parallel schedule; it needs a float32 state (sdm_create) and
- * d_v % 4 == 0 (else SDM_ERR_UNSUPPORTED).
+ * the epoch-start row of every slot an epoch writes) and runs the tokens in
+ * reverse on the time-parallel schedule; it needs a float32 state
+ * (sdm_create) and d_v % 4 == 0 (else SDM_ERR_UNSUPPORTED).  Memory stays
+ * bounded for long sequences: the tokens are taken in chunks of whole epochs,
+ * the recorded rows cover one chunk, and the state at each chunk start is
+ * kept (a first forward pass computes those states, then each chunk's
+ * forward runs again from its start state and is reversed).  The call uses
+ * the fewest chunks that ws_bytes allows; every chunk count gives the same
+ * gradients bit for bit.
  *   kp, qp, v, alpha, beta, dtype   the forward's inputs (as sdm_forward)
  *   Minit      device [B][H][N][d_v] float32: the state the forward started
  *              from (as with SDM_FLAG_CONTINUE), or NULL for M_0
  *   dy         device [B][T][H][d_v] float32, dL/dy
  *   dMT        device [B][H][N][d_v] float32, dL/dM_T, or NULL for zero
- *   workspace  >= sdm_backward_workspace_size(...) bytes, 16-byte aligned.
- *              It holds the tape: B*H*T*W*d_v*4 bytes and more.
+ *   workspace  >= sdm_backward_workspace_size(...) bytes, 16-byte aligned:
+ *              the least memory the call can run in.  A larger workspace
+ *              (sdm_backward_workspace_size_ex with fewer chunks) saves
+ *              forward recomputation.
  * Outputs (device, float32, overwritten):
  *   dkp, dqp   [B][T][H][2*sqrtN]   dL/dk', dL/dq'
  *   dv         [B][T][H][d_v]       dL/dv
@@ -266,6 +274,17 @@ sdm_status sdm_write_histogram(sdm_handle h, int B, int64_t T, const void *kp,
  */
 sdm_status sdm_backward_workspace_size(sdm_handle h, int B, int64_t T, sdm_dtype dtype,
                                        size_t *bytes);
+
+/*
+ * Workspace for the backward run in `chunks` chunks of whole epochs (1: the
+ * whole sequence in one chunk, the fastest; 0: the count that needs the least
+ * memory, which is what sdm_backward_workspace_size reports).  Counts beyond
+ * the number of epochs act as that number.  A pure function of its
+ * arguments; no HIP call.  Errors as sdm_backward_workspace_size, plus
+ * SDM_ERR_ARG for chunks < 0.
+ */
+sdm_status sdm_backward_workspace_size_ex(sdm_handle h, int B, int64_t T, sdm_dtype dtype,
+                                          int chunks, size_t *bytes);
 
 sdm_status sdm_backward(sdm_handle h, int B, int64_t T, const void *kp, const void *qp,
                         const void *v, const float *alpha, const float *beta, sdm_dtype dtype,

@@ -33,7 +33,8 @@ STATUS = {0: "SDM_OK", 1: "SDM_ERR_ARG", 2: "SDM_ERR_UNSUPPORTED", 3: "SDM_ERR_W
           4: "SDM_ERR_HIP"}
 
 # every function include/sdm.h declares
-EXPORTS = ("sdm_backward", "sdm_backward_workspace_size", "sdm_create", "sdm_create_ex",
+EXPORTS = ("sdm_backward", "sdm_backward_workspace_size", "sdm_backward_workspace_size_ex",
+           "sdm_create", "sdm_create_ex",
            "sdm_destroy", "sdm_workspace_size", "sdm_select", "sdm_forward",
            "sdm_forward_noalloc", "sdm_prepare", "sdm_apply", "sdm_write_histogram",
            "sdm_status_string", "sdm_last_error")
@@ -70,6 +71,7 @@ def lib():
         L.sdm_apply.argtypes = [p, i, i64, p, i, i, p, sz, p, p, p]
         L.sdm_write_histogram.argtypes = [p, i, i64, p, i, p, p]
         L.sdm_backward_workspace_size.argtypes = [p, i, i64, i, ctypes.POINTER(sz)]
+        L.sdm_backward_workspace_size_ex.argtypes = [p, i, i64, i, i, ctypes.POINTER(sz)]
         L.sdm_backward.argtypes = [p, i, i64, p, p, p, p, p, i, p, p, p, p, sz, p, p, p, p, p,
                                    p, p, p]
         for f in EXPORTS[:-2]:
@@ -234,12 +236,21 @@ class SDM:
                                          _stream(kp.device)))
         return counts
 
+    def backward_workspace_size(self, B: int, T: int, dtype: int = F32, chunks: int = 0) -> int:
+        """Bytes of workspace for sdm_backward run in `chunks` chunks of epochs
+        (0: the least memory; 1: the whole sequence at once, the fastest)."""
+        n = ctypes.c_size_t()
+        _check(lib().sdm_backward_workspace_size_ex(self._h, B, T, dtype, chunks,
+                                                    ctypes.byref(n)))
+        return n.value
+
     def backward(self, kp, qp, v, alpha, beta, dy, dMT=None, Minit=None, workspace=None,
-                  dM0: bool = True) -> dict:
+                  dM0: bool = True, chunks: int = 0) -> dict:
         """Gradients of the core for upstream gradients dy [B,T,H,d_v] (and dMT
         [B,H,N,d_v], None = zero), with the selections held fixed.  Minit is the
-        state the forward started from (None: M_0).  Returns float32 dkp, dqp
-        [B,T,H,2 sqrtN], dv [B,T,H,d_v], dalpha, dbeta [B,T,H], dMinit
+        state the forward started from (None: M_0).  Without a workspace, one
+        for `chunks` chunks is allocated (0: the least memory).  Returns float32
+        dkp, dqp [B,T,H,2 sqrtN], dv [B,T,H,d_v], dalpha, dbeta [B,T,H], dMinit
         [B,H,N,d_v] and (dM0=True) dM0 [H,N,d_v]."""
         for t, nm in ((kp, "kp"), (qp, "qp"), (v, "v")):
             _dev_tensor(t, nm)
@@ -262,9 +273,10 @@ class SDM:
                 _out_tensor(t, nm, sshape, torch.float32, kp)
         dev = kp.device
         dt = _in_dtype(kp)
-        n = ctypes.c_size_t()
-        _check(lib().sdm_backward_workspace_size(self._h, B, T, dt, ctypes.byref(n)))
-        workspace = _workspace(workspace, n.value, kp)
+        need = self.backward_workspace_size(B, T, dt, 0)
+        if workspace is None:
+            need = self.backward_workspace_size(B, T, dt, chunks)
+        workspace = _workspace(workspace, need, kp)
         f32 = dict(dtype=torch.float32, device=dev)
         out = dict(dkp=torch.empty((B, T, self.H, 2 * self.sqrtN), **f32),
                    dqp=torch.empty((B, T, self.H, 2 * self.sqrtN), **f32),

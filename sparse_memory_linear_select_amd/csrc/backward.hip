@@ -18,7 +18,13 @@
 // Schedule.  A forward pass (write updates only) records, per slot written
 // in an epoch, its epoch-start row at the slot's first write of the epoch
 // (the tape; the rows the later writes replace are recomputed from it in the
-// reverse pass with the same operations).  The write and read events of each
+// reverse pass with the same operations).  The tape covers one chunk of
+// epochs at a time, so memory does not grow with T: a first forward pass
+// keeps the state at the start of every chunk (checkpoints), then, from the
+// last chunk to the first, each chunk's forward runs again from its
+// checkpoint with the tape and is reversed at once.  Every chunk count gives
+// the same gradients bit for bit (the recomputed forward applies the same
+// operations in the same order).  The write and read events of each
 // (chain, epoch) are sorted together by slot (time order within a slot,
 // writes before reads at one token).  Epochs are then processed in reverse;
 // per slot segment one row group walks the segment forward (rows seen by the
@@ -39,7 +45,8 @@ constexpr int kDots = 3 * kMaxK;  // per (chain, token): da[64], dc[64], dq[64]
 struct BwdArgs {
     const uint32_t *rec;     // token records
     const TPEntry *ms;       // [chain][T*(W+R)] merged sorted events, epoch regions
-    float *tape;             // [chain][T][W][d_v] epoch-start rows at first writes (see the segment kernel)
+    float *tape;             // [chain][tapeT][W][d_v] epoch-start rows at first writes (see the segment kernel)
+    int64_t tapeT, tape_t0;  // tokens per chain in the tape (one chunk), token of its first entry
     const void *v;
     const float *dy;         // [B][T][H][d_v]
     float *Mw;               // [chain][N][d_v] state: end of the current epoch -> its start
@@ -153,7 +160,7 @@ __global__ __launch_bounds__(256) void bwd_segment_kernel(BwdArgs a, int ep, int
     const int64_t row0_off = (b * a.T * a.H + h) * a.d_v + colc;  // v, dy of token 0
     const TPEntry *se = a.ms + chain * a.T * ept + t0 * ept;
     const int *st = starts + chain * a.T * ept + t0 * ept;
-    float *tape_c = a.tape + (chain * a.T + t0) * a.W * a.d_v + colc;
+    float *tape_c = a.tape + (chain * a.tapeT + (t0 - a.tape_t0)) * a.W * a.d_v + colc;
     float *part = a.part + chain * (int64_t)nsg * a.E * ept * 2 + (int64_t)sg * a.E * ept * 2;
     const rsrc_t Mr = make_rsrc(a.Mw + chain * a.N * a.d_v, (uint32_t)(a.N * a.d_v * 4));
     const rsrc_t Gr = make_rsrc(a.G + chain * a.N * a.d_v, (uint32_t)(a.N * a.d_v * 4));
@@ -465,59 +472,110 @@ dim3 grid_for(int64_t n, int64_t cap = 16384)
 
 }  // namespace
 
-size_t tp_backward_workspace_bytes(const Shape &s)
+namespace {
+
+// Layout of the backward's workspace for a given chunk count.
+struct BwdLayout {
+    int E, nep, chunks, per;  // epoch length, epochs, chunks, epochs per chunk
+    size_t ms, mt, tape, state, dvbuf, part, dots, total;  // bytes of each region
+};
+
+BwdLayout bwd_layout(const Shape &s, int chunks)
 {
+    BwdLayout L{};
     const size_t chains = (size_t)s.B * s.H;
-    const int E = tp_epoch_len(s);
+    L.E = tp_epoch_len(s);
+    L.nep = (int)((s.T + L.E - 1) / L.E);
+    if (chunks < 1 || chunks > L.nep) chunks = L.nep;
+    L.per = (L.nep + chunks - 1) / chunks;
+    L.chunks = (L.nep + L.per - 1) / L.per;
     const size_t ept = (size_t)s.W + s.R;
     const int nsg = (s.d_v + kColsPerWave - 1) / kColsPerWave;
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    return up(chains * s.T * ept * sizeof(TPEntry)) + 2 * up(chains * s.T * ept * 8) +  // merged
-           up(chains * s.T * (size_t)s.W * s.d_v * 4) +                              // tape
-           up(chains * (size_t)s.N() * s.d_v * 4) +                                  // Mw
-           up(chains * (size_t)E * s.W * s.d_v * 4) +                                // dvbuf
-           up(chains * (size_t)E * ept * nsg * 2 * 4) +                              // part
-           up(chains * s.T * (size_t)kDots * 4);                                     // dots
+    const int64_t tape_tokens = (int64_t)L.per * L.E < s.T ? (int64_t)L.per * L.E : s.T;
+    L.ms = up(chains * s.T * ept * sizeof(TPEntry));
+    L.mt = up(chains * s.T * ept * 8);
+    L.tape = up(chains * (size_t)tape_tokens * s.W * s.d_v * 4);
+    L.state = up(chains * (size_t)s.N() * s.d_v * 4);
+    L.dvbuf = up(chains * (size_t)L.E * s.W * s.d_v * 4);
+    L.part = up(chains * (size_t)L.E * ept * nsg * 2 * 4);
+    L.dots = up(chains * s.T * (size_t)kDots * 4);
+    // merged events, 2 radix buffers, the tape, one state per chunk (the
+    // first chunk's start and a checkpoint per later chunk), dv, dots
+    L.total = L.ms + 2 * L.mt + L.tape + (size_t)L.chunks * L.state + L.dvbuf + L.part + L.dots;
+    return L;
 }
 
-hipError_t launch_tp_backward(const Shape &s, const uint32_t *rec, void *fwd_ws, void *bwd_ws,
-                              const void *v, bool bf16, const float *M0, const float *Minit,
-                              const float *dy, const float *dMT, const float *alpha,
-                              const float *beta, float *dkp, float *dqp, float *dv, float *dalpha,
-                              float *dbeta, float *dMinit, float *dM0, hipStream_t st)
+}  // namespace
+
+int tp_backward_epochs(const Shape &s)
+{
+    const int E = tp_epoch_len(s);
+    return (int)((s.T + E - 1) / E);
+}
+
+int tp_backward_min_chunks(const Shape &s)
+{
+    // fewest chunks among those that need the least memory
+    const int nep = tp_backward_epochs(s);
+    int best = 1;
+    size_t least = bwd_layout(s, 1).total;
+    for (int c = 2; c <= nep; c++) {
+        const BwdLayout L = bwd_layout(s, c);
+        if (L.chunks == c && L.total < least) {
+            least = L.total;
+            best = c;
+        }
+    }
+    return best;
+}
+
+size_t tp_backward_workspace_bytes(const Shape &s, int chunks)
+{
+    return bwd_layout(s, chunks < 1 ? tp_backward_min_chunks(s) : chunks).total;
+}
+
+hipError_t launch_tp_backward(const Shape &s, int chunks, const uint32_t *rec, void *fwd_ws,
+                              void *bwd_ws, const void *v, bool bf16, const float *M0,
+                              const float *Minit, const float *dy, const float *dMT,
+                              const float *alpha, const float *beta, float *dkp, float *dqp,
+                              float *dv, float *dalpha, float *dbeta, float *dMinit, float *dM0,
+                              hipStream_t st)
 {
     const size_t chains = (size_t)s.B * s.H;
-    const int E = tp_epoch_len(s);
-    const int nep = (int)((s.T + E - 1) / E);
+    const BwdLayout L = bwd_layout(s, chunks);
+    const int E = L.E, nep = L.nep;
     const size_t ept = (size_t)s.W + s.R;
     const int nslice = (s.d_v + 4 * kLPR - 1) / (4 * kLPR);
     const int nsg = (s.d_v + kColsPerWave - 1) / kColsPerWave;
-    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     char *p = static_cast<char *>(bwd_ws);
     TPEntry *ms = reinterpret_cast<TPEntry *>(p);
-    p += up(chains * s.T * ept * sizeof(TPEntry));
+    p += L.ms;
     uint64_t *mtA = reinterpret_cast<uint64_t *>(p);
-    p += up(chains * s.T * ept * 8);
+    p += L.mt;
     uint64_t *mtB = reinterpret_cast<uint64_t *>(p);
-    p += up(chains * s.T * ept * 8);
+    p += L.mt;
     float *tape = reinterpret_cast<float *>(p);
-    p += up(chains * s.T * (size_t)s.W * s.d_v * 4);
-    float *Mw = reinterpret_cast<float *>(p);
-    p += up(chains * (size_t)s.N() * s.d_v * 4);
+    p += L.tape;
+    float *states = reinterpret_cast<float *>(p);  // chunk c starts from states + c * nstate
+    p += (size_t)L.chunks * L.state;
     float *dvbuf = reinterpret_cast<float *>(p);
-    p += up(chains * (size_t)E * s.W * s.d_v * 4);
+    p += L.dvbuf;
     float *part = reinterpret_cast<float *>(p);
-    p += up(chains * (size_t)E * ept * nsg * 2 * 4);
+    p += L.part;
     float *dots = reinterpret_cast<float *>(p);
 
     const int64_t nstate = (int64_t)chains * s.N() * s.d_v;
+    const size_t sstride = L.state / sizeof(float);
+    auto chunk_state = [&](int c) { return states + (size_t)c * sstride; };
     hipError_t e;
     // the state the forward starts from, and the adjoint of the final state
     if (Minit) {
-        hipLaunchKernelGGL(bwd_copy_kernel, grid_for(nstate), dim3(256), 0, st, Minit, Mw, nstate);
+        hipLaunchKernelGGL(bwd_copy_kernel, grid_for(nstate), dim3(256), 0, st, Minit,
+                           chunk_state(0), nstate);
         e = hipGetLastError();
     } else {
-        e = launch_init(s, M0, Mw, false, st);
+        e = launch_init(s, M0, chunk_state(0), false, st);
     }
     if (e != hipSuccess) return e;
     if (dMT)
@@ -526,11 +584,18 @@ hipError_t launch_tp_backward(const Shape &s, const uint32_t *rec, void *fwd_ws,
         hipLaunchKernelGGL(bwd_fill_kernel, grid_for(nstate), dim3(256), 0, st, dMinit, nstate, 0.f);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
-    // forward write pass with the tape, then the merged event sort
+    // write events sorted per epoch, then the checkpoints: chunk c + 1 starts
+    // from chunk c's start advanced over chunk c's epochs
     e = launch_tp_prepare(s, rec, fwd_ws, st, 0, -1, false);
     if (e != hipSuccess) return e;
-    e = launch_tp_forward_tape(s, rec, fwd_ws, v, bf16, Mw, tape, st);
-    if (e != hipSuccess) return e;
+    for (int c = 0; c + 1 < L.chunks; c++) {
+        hipLaunchKernelGGL(bwd_copy_kernel, grid_for(nstate), dim3(256), 0, st, chunk_state(c),
+                           chunk_state(c + 1), nstate);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        e = launch_tp_forward_tape(s, rec, fwd_ws, v, bf16, chunk_state(c + 1), nullptr, 0, 0,
+                                   c * L.per, (c + 1) * L.per, st);
+        if (e != hipSuccess) return e;
+    }
     e = launch_tp_sort_merged(s, rec, fwd_ws, ms, mtA, mtB, st);
     if (e != hipSuccess) return e;
 
@@ -538,9 +603,9 @@ hipError_t launch_tp_backward(const Shape &s, const uint32_t *rec, void *fwd_ws,
     a.rec = rec;
     a.ms = ms;
     a.tape = tape;
+    a.tapeT = (int64_t)L.per * E < s.T ? (int64_t)L.per * E : s.T;
     a.v = v;
     a.dy = dy;
-    a.Mw = Mw;
     a.G = dMinit;
     a.dvbuf = dvbuf;
     a.part = part;
@@ -551,10 +616,10 @@ hipError_t launch_tp_backward(const Shape &s, const uint32_t *rec, void *fwd_ws,
     a.d_v = s.d_v;
     a.W = s.W;
     a.R = s.R;
-    const RecLayout L(s.W, s.R);
-    a.Wp = L.Wp;
-    a.Rp = L.Rp;
-    a.rec_dwords = L.dwords();
+    const RecLayout RL(s.W, s.R);
+    a.Wp = RL.Wp;
+    a.Rp = RL.Rp;
+    a.rec_dwords = RL.dwords();
     a.E = E;
     a.nslice = nslice;
     a.sqrtN = s.sqrtN;
@@ -565,25 +630,36 @@ hipError_t launch_tp_backward(const Shape &s, const uint32_t *rec, void *fwd_ws,
     hipLaunchKernelGGL(bwd_segstart_kernel, dim3((unsigned)(chains * nep)), dim3(1024), 0, st, a,
                        nep, starts, nsegs);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    for (int ep = nep - 1; ep >= 0; ep--) {
-        const int64_t t0 = (int64_t)ep * E;
-        const int ne = (int)((s.T - t0) < E ? (s.T - t0) : E);
-        const int nwb = (int)((ne * ept + kSegsPerWave - 1) / kSegsPerWave);  // segments <= events
-        const dim3 grid = chain_grid(chains, (int64_t)nwb * nsg);
-        if (bf16)
-            hipLaunchKernelGGL(bwd_segment_kernel<true>, grid, dim3(256), 0, st, a, ep, nep, nwb, nsg,
-                               starts, nsegs);
-        else
-            hipLaunchKernelGGL(bwd_segment_kernel<false>, grid, dim3(256), 0, st, a, ep, nep, nwb, nsg,
-                               starts, nsegs);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(bwd_dv_kernel, chain_grid(chains, (int64_t)ne * nslice), dim3(256), 0, st,
-                           a, ep, dv);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        const int64_t nev = (int64_t)chains * ne * ept;
-        hipLaunchKernelGGL(bwd_dots_kernel, dim3((unsigned)((nev + 255) / 256)), dim3(256), 0, st, a, ep,
-                           nsg);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+    for (int c = L.chunks - 1; c >= 0; c--) {
+        const int ep0 = c * L.per, ep1 = (c + 1) * L.per < nep ? (c + 1) * L.per : nep;
+        // the chunk's forward again, from its start, recording the tape; its
+        // state buffer then holds the chunk's end state, which the reverse
+        // walks back epoch by epoch
+        a.Mw = chunk_state(c);
+        a.tape_t0 = (int64_t)ep0 * E;
+        e = launch_tp_forward_tape(s, rec, fwd_ws, v, bf16, a.Mw, tape, a.tapeT, a.tape_t0, ep0,
+                                   ep1, st);
+        if (e != hipSuccess) return e;
+        for (int ep = ep1 - 1; ep >= ep0; ep--) {
+            const int64_t t0 = (int64_t)ep * E;
+            const int ne = (int)((s.T - t0) < E ? (s.T - t0) : E);
+            const int nwb = (int)((ne * ept + kSegsPerWave - 1) / kSegsPerWave);  // segments <= events
+            const dim3 grid = chain_grid(chains, (int64_t)nwb * nsg);
+            if (bf16)
+                hipLaunchKernelGGL(bwd_segment_kernel<true>, grid, dim3(256), 0, st, a, ep, nep, nwb,
+                                   nsg, starts, nsegs);
+            else
+                hipLaunchKernelGGL(bwd_segment_kernel<false>, grid, dim3(256), 0, st, a, ep, nep, nwb,
+                                   nsg, starts, nsegs);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            hipLaunchKernelGGL(bwd_dv_kernel, chain_grid(chains, (int64_t)ne * nslice), dim3(256), 0,
+                               st, a, ep, dv);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            const int64_t nev = (int64_t)chains * ne * ept;
+            hipLaunchKernelGGL(bwd_dots_kernel, dim3((unsigned)((nev + 255) / 256)), dim3(256), 0, st,
+                               a, ep, nsg);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
     }
     const int64_t n_ht = s.ht();
     int64_t blocks = (2 * n_ht + 3) / 4;

@@ -54,7 +54,8 @@ struct TPArgs {
     int E, nepoch, passes, kshift;
     int ep0, nrun;  // sort/link launches: epochs [ep0, ep0 + nrun)
     int64_t chains;
-    float *tape;    // backward's forward pass: [chain][T][W][d_v] row each write replaced
+    float *tape;    // backward's forward pass: [chain][tapeT][W][d_v] epoch-start rows
+    int64_t tapeT, tape_t0;  // tokens per chain in the tape, token of its first entry
 };
 
 // Where a sort writes: the forward sorts the W write events of each token;
@@ -604,7 +605,8 @@ __global__ __launch_bounds__(256, SB ? 6 : 1) void tp_update_kernel(TPArgs a, in
     // TAPE: the epoch-start row of each written slot, stored at the slot of
     // its first write in the epoch ([chain][token][w][column]); the backward
     // recomputes the rows the later writes of the epoch replaced
-    float *tape_c = TAPE ? a.tape + (chain * a.T + t0) * a.W * a.d_v + colc : nullptr;
+    float *tape_c =
+        TAPE ? a.tape + (chain * a.tapeT + (t0 - a.tape_t0)) * a.W * a.d_v + colc : nullptr;
     auto tape_put = [&](const TPEntry &ev, float4 x, bool on) {
         if (TAPE && on)
             *reinterpret_cast<float4 *>(tape_c + ((int64_t)(ev.tw >> 6) * a.W + (ev.tw & 63u)) *
@@ -890,26 +892,39 @@ static hipError_t tp_apply_state(const Shape &s, TPArgs a, bool bf16, hipStream_
 }
 
 hipError_t launch_tp_forward_tape(const Shape &s, const uint32_t *rec, void *ws, const void *v,
-                                  bool bf16, float *M, float *tape, hipStream_t st)
+                                  bool bf16, float *M, float *tape, int64_t tapeT,
+                                  int64_t tape_t0, int ep0, int ep1, hipStream_t st)
 {
     TPArgs a = tp_args(s, rec, ws, v, nullptr, M);
     a.tape = tape;
+    a.tapeT = tapeT;
+    a.tape_t0 = tape_t0;
+    if (ep1 < 0 || ep1 > a.nepoch) ep1 = a.nepoch;
     // 8 events per row group, as in the forward (backward step 32.43 -> 32.11 ms
     // against 4 at the 1.4B-style layer)
     constexpr int kLPR = StateRow<false>::kLPR, kRPI = 64 / kLPR, SPG = 8;
     const int nslice = (s.d_v + 4 * kLPR - 1) / (4 * kLPR);
-    for (int ep = 0; ep < a.nepoch; ep++) {
+    for (int ep = ep0; ep < ep1; ep++) {
         const int64_t t0 = (int64_t)ep * a.E;
         const int ne = (int)((s.T - t0) < a.E ? (s.T - t0) : a.E);
         const int nblk = (ne * s.W + kRPI * SPG - 1) / (kRPI * SPG);
         const dim3 ugrid = chain_grid(a.chains, (int64_t)nblk * nslice);
         const bool rev = ep & 1;  // each launch starts on the chains the previous one ended on
-        if (bf16)
-            hipLaunchKernelGGL((tp_update_kernel<true, SPG, false, true>), ugrid, dim3(256), 0, st, a,
-                               ep, nslice, nblk, rev);
-        else
-            hipLaunchKernelGGL((tp_update_kernel<false, SPG, false, true>), ugrid, dim3(256), 0, st,
-                               a, ep, nslice, nblk, rev);
+        if (tape) {
+            if (bf16)
+                hipLaunchKernelGGL((tp_update_kernel<true, SPG, false, true>), ugrid, dim3(256), 0,
+                                   st, a, ep, nslice, nblk, rev);
+            else
+                hipLaunchKernelGGL((tp_update_kernel<false, SPG, false, true>), ugrid, dim3(256), 0,
+                                   st, a, ep, nslice, nblk, rev);
+        } else {  // state only (the checkpoint pass)
+            if (bf16)
+                hipLaunchKernelGGL((tp_update_kernel<true, SPG, false>), ugrid, dim3(256), 0, st, a,
+                                   ep, nslice, nblk, rev);
+            else
+                hipLaunchKernelGGL((tp_update_kernel<false, SPG, false>), ugrid, dim3(256), 0, st, a,
+                                   ep, nslice, nblk, rev);
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

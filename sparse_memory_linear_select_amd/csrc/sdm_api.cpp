@@ -129,11 +129,24 @@ sdm_status check_variant_and_ws(const sdm_ctx *h, int B, int64_t T, sdm_variant 
     return SDM_OK;
 }
 
-size_t bwd_ws_bytes(const sdm_ctx *h, int B, int64_t T)
+// Backward workspace with the sequence run in `chunks` chunks (0: the count
+// that needs the least memory).
+size_t bwd_ws_bytes(const sdm_ctx *h, int B, int64_t T, int chunks)
 {
     const sdm::Shape s = shape_of(h, B, T);
     return records_bytes(h, B, T) + round_up(sdm::tp_workspace_bytes(s)) +
-           round_up(sdm::tp_backward_workspace_bytes(s));
+           round_up(sdm::tp_backward_workspace_bytes(s, chunks));
+}
+
+// The fewest chunks whose workspace fits in ws_bytes (0 if none does).
+int bwd_chunks_for(const sdm_ctx *h, int B, int64_t T, size_t ws_bytes)
+{
+    const sdm::Shape s = shape_of(h, B, T);
+    const int nep = sdm::tp_backward_epochs(s);
+    const int cmin = sdm::tp_backward_min_chunks(s);
+    for (int c = 1; c <= nep; c++)
+        if (bwd_ws_bytes(h, B, T, c) <= ws_bytes) return c;
+    return bwd_ws_bytes(h, B, T, cmin) <= ws_bytes ? cmin : 0;
 }
 
 sdm_status check_backward(const sdm_ctx *h, int B, int64_t T)
@@ -432,8 +445,8 @@ sdm_status sdm_forward_noalloc(sdm_handle h, int B, int64_t T, const void *kp, c
 
 extern "C" {
 
-sdm_status sdm_backward_workspace_size(sdm_handle h, int B, int64_t T, sdm_dtype dtype,
-                                       size_t *bytes)
+sdm_status sdm_backward_workspace_size_ex(sdm_handle h, int B, int64_t T, sdm_dtype dtype,
+                                          int chunks, size_t *bytes)
 {
     if (!bytes) return fail(SDM_ERR_ARG, "null bytes pointer");
     *bytes = 0;
@@ -441,8 +454,15 @@ sdm_status sdm_backward_workspace_size(sdm_handle h, int B, int64_t T, sdm_dtype
     if (st != SDM_OK) return st;
     st = check_backward(h, B, T);
     if (st != SDM_OK) return st;
-    *bytes = bwd_ws_bytes(h, B, T);
+    if (chunks < 0) return fail(SDM_ERR_ARG, "chunks must be >= 0 (got %d)", chunks);
+    *bytes = bwd_ws_bytes(h, B, T, chunks);
     return SDM_OK;
+}
+
+sdm_status sdm_backward_workspace_size(sdm_handle h, int B, int64_t T, sdm_dtype dtype,
+                                       size_t *bytes)
+{
+    return sdm_backward_workspace_size_ex(h, B, T, dtype, 0, bytes);
 }
 
 sdm_status sdm_backward(sdm_handle h, int B, int64_t T, const void *kp, const void *qp,
@@ -464,9 +484,10 @@ sdm_status sdm_backward(sdm_handle h, int B, int64_t T, const void *kp, const vo
         return fail(SDM_ERR_ARG, "tensor pointers must be 16-byte aligned");
     st = check_backward(h, B, T);
     if (st != SDM_OK) return st;
-    const size_t need = bwd_ws_bytes(h, B, T);
-    if (ws_bytes < need)
-        return fail(SDM_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+    const int chunks = bwd_chunks_for(h, B, T, ws_bytes);
+    if (chunks == 0)
+        return fail(SDM_ERR_WORKSPACE, "workspace has %zu bytes, needs at least %zu", ws_bytes,
+                    bwd_ws_bytes(h, B, T, 0));
 
     const sdm::Shape s = shape_of(h, B, T);
     const hipStream_t hs = (hipStream_t)stream;
@@ -476,8 +497,8 @@ sdm_status sdm_backward(sdm_handle h, int B, int64_t T, const void *kp, const vo
     hipError_t e = sdm::launch_select(s, kp, qp, dtype == SDM_BF16, nullptr, nullptr, nullptr,
                                       nullptr, rec, alpha, beta, hs);
     if (e != hipSuccess) return hip_fail(e, "select launch");
-    e = sdm::launch_tp_backward(s, rec, fwd, bwd, v, dtype == SDM_BF16, h->M0, Minit, dy, dMT,
-                                alpha, beta, dkp, dqp, dv, dalpha, dbeta, dMinit, dM0, hs);
+    e = sdm::launch_tp_backward(s, chunks, rec, fwd, bwd, v, dtype == SDM_BF16, h->M0, Minit, dy,
+                                dMT, alpha, beta, dkp, dqp, dv, dalpha, dbeta, dMinit, dM0, hs);
     if (e != hipSuccess) return hip_fail(e, "backward launch");
     return SDM_OK;
 }

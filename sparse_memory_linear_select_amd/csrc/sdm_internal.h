@@ -126,18 +126,27 @@ bool decode_supported(const Shape &s);
 hipError_t launch_rw_decode(const Shape &s, const uint32_t *rec, const void *v, bool bf16,
                             float *y, void *M, bool state_bf16, hipStream_t st);
 
-// Backward (float32 state): a forward write pass that records, per write
-// event, the row it replaced ([chain][T][W][d_v]); the write and read events
-// of every epoch sorted together by slot; the reverse pass.
+// Backward (float32 state): a forward write pass over epochs [ep0, ep1) that
+// records each written slot's epoch-start row in the tape ([chain][tapeT][W]
+// [d_v], token t at entry t - tape_t0), or, with tape == nullptr, only
+// advances the state; the write and read events of every epoch sorted
+// together by slot; the reverse pass.
 hipError_t launch_tp_forward_tape(const Shape &s, const uint32_t *rec, void *ws, const void *v,
-                                  bool bf16, float *M, float *tape, hipStream_t st);
+                                  bool bf16, float *M, float *tape, int64_t tapeT,
+                                  int64_t tape_t0, int ep0, int ep1, hipStream_t st);
 hipError_t launch_tp_sort_merged(const Shape &s, const uint32_t *rec, void *ws, TPEntry *out,
                                  uint64_t *tmpA, uint64_t *tmpB, hipStream_t st);
-size_t tp_backward_workspace_bytes(const Shape &s);  // beyond the forward's workspace
-hipError_t launch_tp_backward(const Shape &s, const uint32_t *rec, void *fwd_ws, void *bwd_ws,
-                              const void *v, bool bf16, const float *M0, const float *Minit,
-                              const float *dy, const float *dMT, const float *alpha,
-                              const float *beta, float *dkp, float *dqp, float *dv, float *dalpha,
-                              float *dbeta, float *dMinit, float *dM0, hipStream_t st);
+// The backward runs the sequence in `chunks` chunks of whole epochs (1 ..
+// number of epochs; 0: the count that needs the least memory): the tape
+// holds one chunk, and the state at every chunk start is kept.
+int tp_backward_epochs(const Shape &s);
+int tp_backward_min_chunks(const Shape &s);
+size_t tp_backward_workspace_bytes(const Shape &s, int chunks);  // beyond the forward's workspace
+hipError_t launch_tp_backward(const Shape &s, int chunks, const uint32_t *rec, void *fwd_ws,
+                              void *bwd_ws, const void *v, bool bf16, const float *M0,
+                              const float *Minit, const float *dy, const float *dMT,
+                              const float *alpha, const float *beta, float *dkp, float *dqp,
+                              float *dv, float *dalpha, float *dbeta, float *dMinit, float *dM0,
+                              hipStream_t st);
 
 }  // namespace sdm

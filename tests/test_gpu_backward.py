@@ -145,6 +145,98 @@ def test_backward_full_workload():
         _compare(g, ref)
 
 
+def _dy_dMT(wl, seed):
+    rng = np.random.default_rng(seed)
+    dy = rng.standard_normal((wl.B, wl.T, wl.H, wl.d_v)).astype(np.float32)
+    dMT = rng.standard_normal((wl.B, wl.H, wl.N, wl.d_v)).astype(np.float32)
+    return dy, dMT
+
+
+def test_backward_chunk_counts_agree_bitwise():
+    """The backward takes the tokens in chunks of whole epochs (the tape holds
+    one chunk; each chunk's forward runs again from its start state).  The
+    least-memory workspace (several chunks) and the whole-sequence workspace
+    (one chunk) give the same gradients bit for bit, and both match the
+    oracle."""
+    wl = si.Workload("bwd chunks", B=2, T=1200, H=2, sqrtN=16, d_v=32, W=8, R=8, dtype="f32",
+                     reuse=0.2, seed=81)
+    d = si.generate(wl)
+    dd = upload(d)
+    core = make_core(dd, wl.W, wl.R)
+    n_min = core.backward_workspace_size(wl.B, wl.T, sdm.F32, 0)
+    n_one = core.backward_workspace_size(wl.B, wl.T, sdm.F32, 1)
+    log(f"backward workspace: least {n_min} B, one chunk {n_one} B")
+    assert n_min < n_one
+    dy, dMT = _dy_dMT(wl, 12)
+    args = [dd[n] for n in ("kp", "qp", "v", "alpha", "beta")]
+    dyg, dMTg = torch.from_numpy(dy).cuda(), torch.from_numpy(dMT).cuda()
+    g_min = core.backward(*args, dyg, dMT=dMTg, chunks=0)
+    g_one = core.backward(*args, dyg, dMT=dMTg, chunks=1)
+    torch.cuda.synchronize()
+    for n in g_min:
+        assert torch.equal(g_min[n], g_one[n]), n
+    ref = oracle.backward(d, wl.sqrtN, wl.W, wl.R, dy.astype(np.float64), dMT.astype(np.float64))
+    ref["dMinit"] = None
+    _compare(g_min, ref)
+
+
+def test_backward_8b_style_shape_in_chunks():
+    """The 8B-style layer's head shape (sqrtN = 256, d_v = 1024, W = R = 64;
+    epochs of 1024 tokens, whose reads take the sampled link search in the
+    forward) over 4 epochs, in the least memory (two chunks), against the
+    oracle."""
+    wl = si.Workload("bwd 8B-style", B=1, T=4096, H=2, sqrtN=256, d_v=1024, W=64, R=64,
+                     dtype="f32", reuse=0.1, seed=82)
+    log(f"backward: B={wl.B} T={wl.T} H={wl.H} S={wl.sqrtN} d_v={wl.d_v} W={wl.W} R={wl.R}")
+    with Timer("generate"):
+        d = si.generate(wl)
+    with Timer("gpu + oracle backward"):
+        core, dd, args, g, dy, dMT, ref = _grads(wl, d, seed=13)
+        assert core.backward_workspace_size(wl.B, wl.T, sdm.F32, 0) < \
+            core.backward_workspace_size(wl.B, wl.T, sdm.F32, 1)
+        _compare(g, ref)
+
+
+def test_backward_long_context_shape_chained_calls():
+    """The long-context head shape (sqrtN = 512, d_v = 2048, W = R = 64, bf16
+    inputs, key reuse) run as three calls that continue the state (the
+    chunking a caller does across calls): forwards to get each call's start
+    state, then the backwards in reverse, each fed the next one's dMinit as
+    dMT.  The concatenated gradients match the oracle's backward of the whole
+    sequence."""
+    wl = si.Workload("bwd long", B=1, T=600, H=1, sqrtN=512, d_v=2048, W=64, R=64,
+                     dtype="bf16", reuse=0.1, seed=83)
+    log(f"backward: B={wl.B} T={wl.T} H={wl.H} S={wl.sqrtN} d_v={wl.d_v} bf16, 3 calls")
+    d = si.generate(wl)
+    dd = upload(d)
+    core = make_core(dd, wl.W, wl.R)
+    dy, dMT = _dy_dMT(wl, 14)
+    dyg, dMTg = torch.from_numpy(dy).cuda(), torch.from_numpy(dMT).cuda()
+    args = [dd[n] for n in ("kp", "qp", "v", "alpha", "beta")]
+    cuts = [0, 200, 400, 600]
+    part = lambda x, i: x[:, cuts[i]:cuts[i + 1]].contiguous()
+    starts = [None]
+    M = None
+    for i in range(2):  # start states of calls 1 and 2
+        _, M = core.forward(*[part(a, i) for a in args], M=None if M is None else M.clone(),
+                            cont=M is not None)
+        starts.append(M.clone())
+    grads = [None] * 3
+    upstream = dMTg
+    for i in (2, 1, 0):
+        grads[i] = core.backward(*[part(a, i) for a in args], part(dyg, i), dMT=upstream,
+                                 Minit=starts[i])
+        upstream = grads[i]["dMinit"]
+    torch.cuda.synchronize()
+    got = {n: torch.cat([grads[i][n] for i in range(3)], 1) for n in
+           ("dkp", "dqp", "dv", "dalpha", "dbeta")}
+    got["dM0"] = grads[0]["dMinit"][0]
+    with Timer("oracle backward"):
+        ref = oracle.backward(d, wl.sqrtN, wl.W, wl.R, dy.astype(np.float64),
+                              dMT.astype(np.float64))
+    _compare(got, ref, names=("dkp", "dqp", "dv", "dalpha", "dbeta", "dM0"))
+
+
 def test_backward_rejects_bf16_state():
     wl = si.Workload("bwd5", B=1, T=8, H=1, sqrtN=8, d_v=8, W=4, R=4, dtype="f32", reuse=0.0,
                      seed=80)
