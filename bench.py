@@ -85,28 +85,43 @@ def d2d_copy_gbs(dev, nbytes=1 << 30, reps=5):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(d, wl, seqs, state="f32"):
-    """The float64 oracle on the first `seqs` sequences of the same inputs."""
-    import oracle
-
-    sub = {k: (v[:seqs] if k not in ("M0",) else v) for k, v in d.items() if k != "src"}
-    cores = oracle.default_threads()
-    t = time.perf_counter()
-    oracle.forward(sub, wl.sqrtN, wl.W, wl.R, threads=cores, state=state)
-    dt = time.perf_counter() - t
-    ht = seqs * wl.T * wl.H
-    model = "unknown"
+def _cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
             if line.startswith("model name"):
-                model = line.split(":", 1)[1].strip()
-                break
+                return line.split(":", 1)[1].strip()
     except OSError:
         pass
+    return "unknown"
+
+
+def cpu_baseline(d, wl, seqs, T=None, state="f32", threads=None, runs=5):
+    """The float64 oracle on a bounded sample of the same inputs (the first
+    `seqs` sequences, their first T tokens): select + init + recurrence,
+    median wall time of `runs` runs on `threads` host threads (all by
+    default)."""
+    import statistics
+
+    import numpy as np
+
+    import oracle
+
+    T = wl.T if T is None else min(T, wl.T)
+    sub = {k: (np.ascontiguousarray(v[:seqs, :T]) if k != "M0" else v) for k, v in d.items()
+           if k != "src"}
+    cores = threads or oracle.default_threads()
+    times = []
+    for _ in range(runs):
+        t = time.perf_counter()
+        oracle.forward(sub, wl.sqrtN, wl.W, wl.R, threads=cores, state=state)
+        times.append(time.perf_counter() - t)
+    dt = statistics.median(times)
+    ht = seqs * T * wl.H
     return {"value": ht / dt, "unit": "head-tokens/s", "cores": cores, "kind": "oracle",
-            "cpu": model,
-            "sample": f"{seqs} of {wl.B} sequences of the workload ({ht} head-tokens, all "
-                      f"{wl.d_v} columns), select + init + recurrence, {dt:.2f} s wall"}
+            "cpu": _cpu_model(), "runs": runs,
+            "sample": f"{wl.name}: {seqs} of {wl.B} sequences x {T} of {wl.T} tokens x {wl.H} "
+                      f"heads ({ht} head-tokens, all {wl.d_v} columns), select + init + "
+                      f"recurrence, median of {runs} runs: {dt:.3f} s"}
 
 
 def decode(args, wl):
@@ -219,6 +234,233 @@ def backward(args, wl):
         "data": "synthetic (seeded; recipe in sdm_inputs.py)"}), flush=True)
 
 
+def _short_kernel(name: str) -> str:
+    """`tp_read_kernel<16, false>` from a demangled rocprofv3 kernel name."""
+    import re
+
+    name = re.sub(r"^void ", "", name.strip())
+    name = re.sub(r"\(anonymous namespace\)::|sdm::", "", name)
+    depth, out = 0, []
+    for ch in name:  # drop the argument list, keep template arguments
+        if ch == "(" and depth == 0:
+            break
+        depth += ch == "<"
+        depth -= ch == ">"
+        out.append(ch)
+    return "".join(out).strip()
+
+
+def counters_summary(args, wl):
+    """Summarise rocprofv3 `--pmc` runs of this script (CSV output, one
+    directory per run): per kernel, the number of dispatches and the mean of
+    every counter per dispatch, as a markdown table on stdout.  When the runs
+    hold FETCH_SIZE and WRITE_SIZE, also write the workload's counted HBM
+    traffic of the write/read phase (profiles/traffic_*.json, the `traffic`
+    of the JSON line): both counters are scaled by what they read for the
+    1 GiB device copy this script makes (d2d_copy_gbs), summed over the
+    write/read kernels and divided by the number of steps in the run."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    vals = defaultdict(list)  # (kernel, counter) -> values per dispatch
+    for d in args.counters_summary:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            sys.exit(f"no *counter_collection.csv under {d}")
+        for f in files:
+            for row in csv.DictReader(open(f)):
+                vals[(_short_kernel(row["Kernel_Name"]), row["Counter_Name"])].append(
+                    float(row["Counter_Value"]))
+    kernels = sorted({k for k, _ in vals})
+    counters = sorted({c for _, c in vals})
+    print("| kernel | dispatches | " + " | ".join(counters) + " |")
+    print("|---|---|" + "---|" * len(counters))
+    for k in kernels:
+        n = max(len(vals.get((k, c), [])) for c in counters)
+        cells = []
+        for c in counters:
+            v = vals.get((k, c))
+            cells.append(f"{sum(v) / len(v):.6g}" if v else "")
+        print(f"| `{k}` | {n} | " + " | ".join(cells) + " |")
+    if not {"FETCH_SIZE", "WRITE_SIZE"} <= set(counters):
+        return
+    copy = [k for k in kernels if "copyBuffer" in k]
+    if not copy:
+        sys.exit("no device-copy dispatch to calibrate FETCH_SIZE / WRITE_SIZE with")
+    mean = lambda k, c: sum(vals[(k, c)]) / len(vals[(k, c)])
+    fscale = 1048576.0 / mean(copy[0], "FETCH_SIZE")  # KiB per 1 GiB copy
+    wscale = 1048576.0 / mean(copy[0], "WRITE_SIZE")
+    schedule = "time-parallel" if args.variant in ("auto", "timepar") else "token-serial"
+    if schedule == "time-parallel":
+        rw = [k for k in kernels if k.startswith(("tp_read", "tp_update"))]
+        E = _epoch_len(wl)
+        steps = sum(len(vals[(k, "FETCH_SIZE")]) for k in rw if k.startswith("tp_read")) / (
+            -(-wl.T // E))
+    else:
+        rw = [k for k in kernels if k.startswith("rw_serial_kernel")]
+        steps = sum(len(vals[(k, "FETCH_SIZE")]) for k in rw)
+    fetch = sum(sum(vals[(k, "FETCH_SIZE")]) for k in rw) * 1024 * fscale / steps
+    write = sum(sum(vals[(k, "WRITE_SIZE")]) for k in rw) * 1024 * wscale / steps
+    src_name = SCHEDULES[schedule][0]
+    src = open(os.path.join(ROOT, "sparse_memory_linear_select_amd", "csrc", src_name), "rb").read()
+    tag = schedule.replace("-", "_") + "__" + wl.name.replace(" ", "_")
+    if args.state != "f32":
+        tag += f"__{args.state}_state"
+    rec = {"schedule": schedule, "workload": wl.name, "kernels": rw,
+           "hbm_bytes_per_step": fetch + write, "fetch_bytes": fetch, "write_bytes": write,
+           "fetch_scale": fscale, "write_scale": wscale, "steps_in_run": steps,
+           "source_sha256": hashlib.sha256(src).hexdigest()}
+    path = os.path.join(ROOT, "profiles", f"traffic_{tag}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(f"\nFETCH_SIZE scale {fscale:.4f}, WRITE_SIZE scale {wscale:.4f} (1 GiB device copy); "
+          f"write/read phase {fetch / 1e9:.2f} GB read + {write / 1e9:.2f} GB written = "
+          f"{(fetch + write) / 1e9:.2f} GB per step over {steps:g} steps -> {path}")
+
+
+def _epoch_len(wl):
+    """Tokens per epoch of the time-parallel schedule (the library's rule:
+    the largest power of two <= 4096 with E*W <= N and E*W <= 2^18, and no
+    longer than the next power of two >= T)."""
+    e = 4096
+    while e > 1 and (e * wl.W > (1 << 18) or e * wl.W > wl.N):
+        e //= 2
+    if e > wl.T:
+        e = 1
+        while e < wl.T:
+            e *= 2
+    return e
+
+
+def _upload(d, dev):
+    import numpy as np
+    import torch
+
+    def up(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(
+                torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    return {k: up(v) for k, v in d.items() if k != "src"}
+
+
+def measure_forward(wl, d, dev, state, variant, steps, warmup):
+    """Times `steps` whole forward steps (sdm_forward) after `warmup`, then
+    the same number issued as sdm_prepare + sdm_apply with HIP events on the
+    launch stream around each half.  Returns the figures of one workload."""
+    import statistics
+
+    import torch
+
+    import sparse_memory_linear_select_amd as sdm
+
+    dd = _upload(d, dev)
+    st = torch.bfloat16 if state == "bf16" else torch.float32
+    esz = 2 if state == "bf16" else 4  # bytes per state element
+    core = sdm.SDM(dd["M0"], wl.W, wl.R, state=st)
+    B, T, H = wl.B, wl.T, wl.H
+    y = torch.empty((B, T, H, wl.d_v), dtype=torch.float32, device=dev)
+    M = torch.empty((B, H, wl.N, wl.d_v), dtype=st, device=dev)
+    dt_code = sdm.BF16 if wl.dtype == "bf16" else sdm.F32
+    ws_n = core.workspace_size(B, T, dt_code, variant)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    L = sdm.lib()
+    stream = torch.cuda.current_stream(dev)
+    sp = sdm._stream(dev)
+    P = sdm._ptr
+
+    def forward():
+        sdm._check(L.sdm_forward(core._h, B, T, P(dd["kp"]), P(dd["qp"]), P(dd["v"]),
+                                 P(dd["alpha"]), P(dd["beta"]), dt_code, variant, 0, P(ws), ws_n,
+                                 P(y), P(M), sp))
+
+    def prepare():
+        sdm._check(L.sdm_prepare(core._h, B, T, P(dd["kp"]), P(dd["qp"]), P(dd["alpha"]),
+                                 P(dd["beta"]), dt_code, variant, 0, P(ws), ws_n, P(M), sp))
+
+    def apply():
+        sdm._check(L.sdm_apply(core._h, B, T, P(dd["v"]), dt_code, variant, P(ws), ws_n, P(y),
+                               P(M), sp))
+
+    for _ in range(warmup):
+        forward()
+        prepare()
+        apply()
+    torch.cuda.synchronize()
+
+    # timed region: `steps` whole steps (sdm_forward), an event after each
+    ev_step = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev_step[0].record(stream)
+    for i in range(steps):
+        forward()
+        ev_step[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = ev_step[0].elapsed_time(ev_step[-1]) / steps
+    per_step = [ev_step[i].elapsed_time(ev_step[i + 1]) for i in range(steps)]
+
+    # second pass: each step as sdm_prepare + sdm_apply on one stream, HIP
+    # events bracketing the write/read kernels alone (roofline)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in ev:
+        e[0].record(stream)
+        prepare()
+        e[1].record(stream)
+        apply()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    rw = [e[1].elapsed_time(e[2]) for e in ev]
+    prep = [e[0].elapsed_time(e[1]) for e in ev]
+    staged_ms = ev[0][0].elapsed_time(ev[-1][2]) / steps
+    rw_ms = sum(rw) / steps
+    ht = wl.head_tokens
+    row_bytes = ht * (2 * wl.W + wl.R) * wl.d_v * esz  # algorithmic row traffic per step
+    schedule = sdm.variant_name(core, B, T, dt_code, variant)
+    traffic = _traffic(wl, schedule, state)
+    out = {
+        "ms_per_step": ms_step, "ms_per_step_median": statistics.median(per_step),
+        "head_tokens_per_s": ht / (ms_step * 1e-3),
+        "staged_ms_per_step": staged_ms, "prepare_ms": sum(prep) / steps,
+        "write_read_ms": rw_ms, "write_read_ms_median": statistics.median(rw),
+        "schedule": schedule, "row_bytes": row_bytes, "wall_s_timed": wall,
+        "effective_gbs": row_bytes / (rw_ms * 1e-3) / 1e9,
+        "traffic": traffic,
+        "hbm_gbs_counted": None if traffic is None else traffic / (rw_ms * 1e-3) / 1e9,
+        "row_gbs_whole_step": row_bytes / (ms_step * 1e-3) / 1e9,
+    }
+    del dd, y, M, ws, core
+    torch.cuda.empty_cache()
+    return out
+
+
+def _workload_record(wl, m, cpu):
+    """One workload's figures for the `workloads` object of the JSON line."""
+    return {
+        "config": {"B": wl.B, "T": wl.T, "H": wl.H, "sqrtN": wl.sqrtN, "d_v": wl.d_v, "W": wl.W,
+                   "R": wl.R, "inputs": wl.dtype, "key_reuse": wl.reuse},
+        "schedule": m["schedule"],
+        "head_tokens_per_s": m["head_tokens_per_s"], "ms_per_step": m["ms_per_step"],
+        "ms_per_step_median": m["ms_per_step_median"], "prepare_ms": m["prepare_ms"],
+        "write_read_ms": m["write_read_ms"], "algorithmic_row_bytes": m["row_bytes"],
+        "effective_gbs": m["effective_gbs"], "frac": m["effective_gbs"] / PEAK_HBM_GBS,
+        "traffic": m["traffic"], "hbm_gbs_counted": m["hbm_gbs_counted"],
+        "frac_counted": (None if m["hbm_gbs_counted"] is None
+                         else m["hbm_gbs_counted"] / PEAK_HBM_GBS),
+        "frac_whole_step": m["row_gbs_whole_step"] / PEAK_HBM_GBS,
+        "cpu_baseline": cpu,
+    }
+
+
+# bounded oracle samples per workload: (sequences, tokens, runs)
+CPU_SAMPLES = {0: (1, None, 5), 1: (2, None, 5), 2: (1, 4096, 3), 3: (1, 4096, 3),
+               4: (1, 16384, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -226,13 +468,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=1,
                     help="synthetic workload index (default 1: the 1.4B-style layer)")
-    ap.add_argument("--cpu-seqs", type=int, default=None,
-                    help="sequences in the CPU-baseline sample (default: all)")
     ap.add_argument("--variant", choices=["auto", "serial", "timepar"], default="auto",
                     help="write/read schedule (default: the library's choice)")
     ap.add_argument("--state", choices=["f32", "bf16"], default="f32",
                     help="element type of the state M (bf16: reduced-precision state)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="measure the headline workload only (no `workloads` object)")
     ap.add_argument("--decode", action="store_true",
                     help="measure one-token decode steps (continuing the state) instead")
     ap.add_argument("--backward", action="store_true",
@@ -240,6 +482,9 @@ def main():
     ap.add_argument("--backward-chunks", type=int, default=0,
                     help="backward workspace sized for this many chunks of epochs (0: the least "
                          "memory; 1: the whole sequence at once)")
+    ap.add_argument("--counters-summary", nargs="+", metavar="DIR",
+                    help="summarise rocprofv3 CSV output directories instead of running "
+                         "(see counters_summary)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -249,9 +494,13 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    import sdm_inputs as si
+
+    if args.counters_summary:
+        return counters_summary(args, si.WORKLOADS[args.workload])
+
     import torch
 
-    import sdm_inputs as si
     import sparse_memory_linear_select_amd as sdm
 
     wl = si.WORKLOADS[args.workload]
@@ -259,101 +508,56 @@ def main():
         return decode(args, wl)
     if args.backward:
         return backward(args, wl)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    var = {"auto": sdm.AUTO, "serial": sdm.SERIAL, "timepar": sdm.TIMEPAR}[args.variant]
+
     _log(f"workload {args.workload}: {wl}")
     t = time.perf_counter()
     d = si.generate(wl)
     _log(f"inputs generated in {time.perf_counter() - t:.1f}s")
-
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    def up(x):
-        import numpy as np
-        if x.dtype == np.uint16:
-            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(x).to(dev)
-
-    dd = {k: up(v) for k, v in d.items() if k != "src"}
-    state = torch.bfloat16 if args.state == "bf16" else torch.float32
-    esz = 2 if args.state == "bf16" else 4  # bytes per state element
-    core = sdm.SDM(dd["M0"], wl.W, wl.R, state=state)
-    B, T, H = wl.B, wl.T, wl.H
-    y = torch.empty((B, T, H, wl.d_v), dtype=torch.float32, device=dev)
-    M = torch.empty((B, H, wl.N, wl.d_v), dtype=state, device=dev)
-    dt_code = sdm.BF16 if wl.dtype == "bf16" else sdm.F32
-    var = {"auto": sdm.AUTO, "serial": sdm.SERIAL, "timepar": sdm.TIMEPAR}[args.variant]
-    ws_n = core.workspace_size(B, T, dt_code, var)
-    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
-    L = sdm.lib()
-    stream = torch.cuda.current_stream(dev)
-    sp = sdm._stream(dev)
-    P = sdm._ptr
-
-    def forward():
-        sdm._check(L.sdm_forward(core._h, B, T, P(dd["kp"]), P(dd["qp"]), P(dd["v"]),
-                                 P(dd["alpha"]), P(dd["beta"]), dt_code, var, 0, P(ws), ws_n,
-                                 P(y), P(M), sp))
-
-    def prepare():
-        sdm._check(L.sdm_prepare(core._h, B, T, P(dd["kp"]), P(dd["qp"]), P(dd["alpha"]),
-                                 P(dd["beta"]), dt_code, var, 0, P(ws), ws_n, P(M), sp))
-
-    def apply():
-        sdm._check(L.sdm_apply(core._h, B, T, P(dd["v"]), dt_code, var, P(ws), ws_n, P(y),
-                               P(M), sp))
-
-    for _ in range(args.warmup):
-        forward()
-        prepare()
-        apply()
-    torch.cuda.synchronize()
-
-    # timed region: K whole steps (sdm_forward)
-    t0_ev, t1_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t0_ev.record(stream)
-    for _ in range(args.steps):
-        forward()
-    t1_ev.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = t0_ev.elapsed_time(t1_ev) / args.steps
-
-    # second pass, K steps issued as sdm_prepare + sdm_apply on one stream, so
-    # that HIP events bracket the write/read kernels alone (roofline)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for e in ev:
-        e[0].record(stream)
-        prepare()
-        e[1].record(stream)
-        apply()
-        e[2].record(stream)
-    torch.cuda.synchronize()
-    staged_ms = ev[0][0].elapsed_time(ev[-1][2]) / args.steps
-    rw_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
-    prep_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    ht = wl.head_tokens
-    row_bytes = ht * (2 * wl.W + wl.R) * wl.d_v * esz  # algorithmic row traffic per step
-    achieved = row_bytes / (rw_ms * 1e-3) / 1e9
-    schedule = sdm.variant_name(core, B, T, dt_code, var)
-    traffic = _traffic(wl, schedule, args.state)
-
+    m = measure_forward(wl, d, dev, args.state, var, args.steps, args.warmup)
+    _log(f"headline: {m['ms_per_step']:.3f} ms/step, write/read {m['write_read_ms']:.3f} ms")
     copy_gbs = d2d_copy_gbs(dev)
 
-    cpu = None
+    cpu = cpu1 = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(d, wl, args.cpu_seqs or wl.B, args.state)
+        seqs, T, runs = CPU_SAMPLES.get(args.workload, (1, 1024, 3))
+        cpu = cpu_baseline(d, wl, seqs, T, args.state, runs=runs)
+        # one host core: the tiny workload whole, and a slice of this one
+        cpu1 = {"tiny": cpu_baseline(si.generate(si.WORKLOADS[0]), si.WORKLOADS[0], 1,
+                                     state=args.state, threads=1, runs=5)}
+        if args.workload != 0:
+            cpu1[wl.name] = cpu_baseline(d, wl, 1, min(wl.T, 1024), args.state, threads=1, runs=3)
+    del d
+
+    workloads = {}
+    if not args.no_workloads and args.variant == "auto" and args.state == "f32":
+        for c in (1, 2, 3, 4):
+            if c == args.workload:
+                continue
+            w = si.WORKLOADS[c]
+            _log(f"workload {c}: {w}")
+            t = time.perf_counter()
+            dw = si.generate(w)
+            _log(f"  inputs generated in {time.perf_counter() - t:.1f}s")
+            mw = measure_forward(w, dw, dev, "f32", sdm.AUTO, min(args.steps, 5), 1)
+            _log(f"  {mw['ms_per_step']:.3f} ms/step, write/read {mw['write_read_ms']:.3f} ms")
+            cw = None
+            if not args.no_cpu_baseline:
+                seqs, T, runs = CPU_SAMPLES[c]
+                cw = cpu_baseline(dw, w, seqs, T, "f32", runs=runs)
+            del dw
+            workloads[w.name] = _workload_record(w, mw, cw)
 
     out = {
         "metric": METRIC,
-        "value": ht / (ms_step * 1e-3),
+        "value": m["head_tokens_per_s"],
         "unit": "head-tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -361,24 +565,36 @@ def main():
                   ("f32", "bf16"): "f32 compute, bf16 state",
                   ("bf16", "bf16"): "bf16 inputs, f32 compute, bf16 state"}[(wl.dtype, args.state)],
         "data": "synthetic (seeded; recipe in sdm_inputs.py)",
-        "config": {"workload": wl.name, "B": B, "T": T, "H": H, "sqrtN": wl.sqrtN, "N": wl.N,
-                   "d_v": wl.d_v, "W": wl.W, "R": wl.R, "inputs": wl.dtype,
-                   "state": args.state, "schedule": schedule},
-        "row_gbs_whole_step": row_bytes / (ms_step * 1e-3) / 1e9,
-        "breakdown_ms": {"staged step (prepare + apply, one stream)": staged_ms,
-                         "prepare (init+select+plan/sort)": prep_ms, "write+read": rw_ms},
-        "wall_s_timed": wall,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": traffic,
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": wl.H, "sqrtN": wl.sqrtN,
+                   "N": wl.N, "d_v": wl.d_v, "W": wl.W, "R": wl.R, "inputs": wl.dtype,
+                   "state": args.state, "schedule": m["schedule"]},
+        "ms_per_step_median": m["ms_per_step_median"],
+        "row_gbs_whole_step": m["row_gbs_whole_step"],
+        "breakdown_ms": {"staged step (prepare + apply, one stream)": m["staged_ms_per_step"],
+                         "prepare (init+select+sort+plan)": m["prepare_ms"],
+                         "write+read": m["write_read_ms"],
+                         "write+read median": m["write_read_ms_median"]},
+        "wall_s_timed": m["wall_s_timed"],
+        "roofline": {"bound": "hbm", "achieved": m["effective_gbs"], "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": m["effective_gbs"] / PEAK_HBM_GBS,
+                     "traffic": m["traffic"],
                      "traffic_unit": "HBM bytes per step (write/read phase, counters)",
-                     "kernel": SCHEDULES[schedule][1],
+                     "kernel": SCHEDULES[m["schedule"]][1],
                      "timing": "write/read kernels bracketed by HIP events on their stream in "
                                "a second pass of K steps issued as sdm_prepare + sdm_apply",
-                     "algorithmic_bytes": row_bytes,
+                     "achieved_is": "effective: algorithmic row bytes ((2W+R) d_v per "
+                                    "head-token) / write-read time; repeated writes to a slot "
+                                    "within an epoch merge, so HBM moves fewer bytes",
+                     "algorithmic_bytes": m["row_bytes"],
+                     "hbm_gbs_counted": m["hbm_gbs_counted"],
+                     "frac_counted": (None if m["hbm_gbs_counted"] is None
+                                      else m["hbm_gbs_counted"] / PEAK_HBM_GBS),
+                     "frac_whole_step": m["row_gbs_whole_step"] / PEAK_HBM_GBS,
                      "d2d_copy_gbs": copy_gbs,
-                     "frac_of_copy": achieved / copy_gbs},
+                     "frac_of_copy": m["effective_gbs"] / copy_gbs},
         "cpu_baseline": cpu,
+        "cpu_baseline_1core": cpu1,
+        "workloads": workloads or None,
     }
     print(json.dumps(out), flush=True)
 

@@ -63,3 +63,60 @@ def test_cpu_baseline_on_a_sample():
     assert out["kind"] == "oracle" and out["unit"] == "head-tokens/s"
     assert out["value"] > 0 and out["cores"] >= 1 and out["cpu"]
     assert f"{wl.T * wl.H} head-tokens" in out["sample"]
+
+
+def test_cpu_baseline_token_slice_and_one_core():
+    wl = si.WORKLOADS[0]
+    d = si.generate(wl)
+    out = bench.cpu_baseline(d, wl, 1, T=16, threads=1, runs=3)
+    assert out["cores"] == 1 and out["runs"] == 3
+    assert f"{16 * wl.H} head-tokens" in out["sample"]
+
+
+def test_epoch_length_rule():
+    # tokens per epoch of the time-parallel schedule on the five workloads
+    assert [bench._epoch_len(si.WORKLOADS[c]) for c in range(5)] == [64, 256, 1024, 1024, 4096]
+
+
+def test_counters_summary_calibrates_with_the_device_copy(tmp_path, monkeypatch, capsys):
+    """Counted traffic = (FETCH_SIZE * f + WRITE_SIZE * w) KiB over the
+    write/read kernels per step, where f and w make the 1 GiB device copy
+    read and write 1 GiB."""
+    import argparse
+    import csv
+    import shutil
+
+    fake = tmp_path / "repo"
+    (fake / "profiles").mkdir(parents=True)
+    (fake / "sparse_memory_linear_select_amd" / "csrc").mkdir(parents=True)
+    shutil.copy(os.path.join(ROOT, "sparse_memory_linear_select_amd", "csrc", "rw_timepar.hip"),
+                fake / "sparse_memory_linear_select_amd" / "csrc" / "rw_timepar.hip")
+    monkeypatch.setattr(bench, "ROOT", str(fake))
+    wl = si.WORKLOADS[1]  # 16 epochs per step
+    rows = []
+    for cnt, per_read, per_upd, copy in (("FETCH_SIZE", 100.0, 50.0, 524288.0),
+                                         ("WRITE_SIZE", 1.0, 80.0, 1048576.0)):
+        for i in range(32):  # two steps
+            rows.append(("void sdm::(anonymous namespace)::tp_read_kernel<8, false>(x)", cnt, per_read))
+            rows.append(("void sdm::(anonymous namespace)::tp_update_kernel<false, 8, false, false>(x)",
+                         cnt, per_upd))
+        rows.append(("__amd_rocclr_copyBuffer", cnt, copy))
+        rows.append(("void sdm::(anonymous namespace)::tp_sort_kernel<false>(x)", cnt, 1e6))
+    for i, (cnt, sub) in enumerate((("FETCH_SIZE", "f"), ("WRITE_SIZE", "w"))):
+        dd = tmp_path / sub / "host" / "123"
+        dd.mkdir(parents=True)
+        with open(dd / "run_counter_collection.csv", "w", newline="") as f:
+            wr = csv.writer(f)
+            wr.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+            for j, (k, c, v) in enumerate(r for r in rows if r[1] == cnt):
+                wr.writerow([j, k, c, v])
+    args = argparse.Namespace(counters_summary=[str(tmp_path / "f"), str(tmp_path / "w")],
+                              variant="auto", state="f32")
+    bench.counters_summary(args, wl)
+    rec = json.load(open(fake / "profiles" / "traffic_time_parallel__1.4B-style_layer.json"))
+    assert rec["steps_in_run"] == 2
+    assert rec["fetch_scale"] == pytest.approx(2.0) and rec["write_scale"] == pytest.approx(1.0)
+    assert rec["fetch_bytes"] == pytest.approx(16 * (100 + 50) * 1024 * 2.0)
+    assert rec["write_bytes"] == pytest.approx(16 * (1 + 80) * 1024 * 1.0)
+    assert bench._traffic(wl, "time-parallel") == pytest.approx(rec["hbm_bytes_per_step"])
+    assert "tp_sort_kernel<false>" in capsys.readouterr().out
