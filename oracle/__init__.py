@@ -57,7 +57,7 @@ def _load():
             lib.sdm_oracle_recurrence.argtypes = [
                 ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                 ctypes.c_int, ctypes.c_int, p, p, p, p, p, ctypes.c_int, p, p, p,
-                ctypes.c_int, ctypes.c_int, ctypes.c_int, p, p, ctypes.c_int]
+                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, p, p, ctypes.c_int]
             lib.sdm_oracle_recurrence.restype = ctypes.c_int
             lib.sdm_oracle_backward.argtypes = [
                 ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -66,6 +66,8 @@ def _load():
             lib.sdm_oracle_backward.restype = ctypes.c_int
             lib.sdm_oracle_round_bf16.argtypes = [p, p, ctypes.c_int64]
             lib.sdm_oracle_round_bf16.restype = None
+            lib.sdm_oracle_round_fp8.argtypes = [p, p, ctypes.c_int64, ctypes.c_int]
+            lib.sdm_oracle_round_fp8.restype = None
             _lib = lib
     return _lib
 
@@ -122,12 +124,25 @@ def round_bf16(x) -> np.ndarray:
     return out
 
 
+def round_fp8(x, scale_log2: int = 0) -> np.ndarray:
+    """Nearest values of the E4M3 format scaled by 2^scale_log2 (ties to even,
+    saturated at +-448 * 2^scale_log2), as float64."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    _load().sdm_oracle_round_fp8(_ptr(x), _ptr(out), x.size, int(scale_log2))
+    return out
+
+
+STATE_MODES = {"f32": 0, "bf16": 1, "fp8": 2}
+
+
 def recurrence(Iw, kw, Ir, qw, v, alpha, beta, M0, sqrtN: int, c0: int = 0,
-               c1: int | None = None, threads: int | None = None, state: str = "f32"):
+               c1: int | None = None, threads: int | None = None, state: str = "f32",
+               scale_log2: int = 0):
     """Token-serial write/read from a given selection; columns [c0, c1).
-    state="bf16" holds the state in bfloat16 (rounded at init and after
-    every write)."""
-    assert state in ("f32", "bf16")
+    state="bf16" holds the state in bfloat16, state="fp8" in E4M3 scaled by
+    2^scale_log2 (rounded at init and after every write)."""
+    assert state in STATE_MODES
     B, T, H, W = Iw.shape
     R = Ir.shape[-1]
     d_v = v.shape[-1]
@@ -144,20 +159,20 @@ def recurrence(Iw, kw, Ir, qw, v, alpha, beta, M0, sqrtN: int, c0: int = 0,
     M = np.empty((B, H, N, nc), dtype=np.float64)
     rc = _load().sdm_oracle_recurrence(
         B, T, H, sqrtN, d_v, W, R, _ptr(Iw), _ptr(kw), _ptr(Ir), _ptr(qw), _ptr(v),
-        _dtype_code(v), _ptr(alpha), _ptr(beta), _ptr(M0), 1 if state == "bf16" else 0, c0, c1,
-        _ptr(y), _ptr(M), threads or default_threads())
+        _dtype_code(v), _ptr(alpha), _ptr(beta), _ptr(M0), STATE_MODES[state], int(scale_log2),
+        c0, c1, _ptr(y), _ptr(M), threads or default_threads())
     if rc != 0:
         raise ValueError(f"sdm_oracle_recurrence failed ({rc})")
     return y, M
 
 
 def forward(inp: dict, sqrtN: int, W: int, R: int, c0: int = 0, c1: int | None = None,
-            threads: int | None = None, state: str = "f32") -> dict:
+            threads: int | None = None, state: str = "f32", scale_log2: int = 0) -> dict:
     """Selection plus recurrence on the inputs of `sdm_inputs.generate`."""
     Iw, kw = select(inp["kp"], sqrtN, W, threads)
     Ir, qw = select(inp["qp"], sqrtN, R, threads)
     y, M = recurrence(Iw, kw, Ir, qw, inp["v"], inp["alpha"], inp["beta"], inp["M0"],
-                      sqrtN, c0, c1, threads, state)
+                      sqrtN, c0, c1, threads, state, scale_log2)
     return dict(Iw=Iw, kw=kw, Ir=Ir, qw=qw, y=y, M=M)
 
 

@@ -56,6 +56,12 @@
  *     bfloat16, and reads use the stored values.  Rounding is to nearest,
  *     ties to even, at bfloat16 precision (8 significant bits, the exponent
  *     range of float32, subnormal spacing 2^-133).
+ *     The same notes name 8-bit states to fit N ~ 10^7 on one card; the
+ *     reading adopted for that: the OCP FP8 E4M3 format (4 exponent bits,
+ *     bias 7, 3 mantissa bits, largest magnitude 448, no infinities) with a
+ *     power-of-two scale 2^s given per layer -- a stored code c means the
+ *     value c * 2^s -- rounded to nearest, ties to even, and saturated at
+ *     +-448 * 2^s; M_0, writes and reads follow the bfloat16 rule above.
  *
  * Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off -fPIC -shared.
  * (-ffp-contract=off keeps every product and sum separately rounded, so the
@@ -227,18 +233,52 @@ void sdm_oracle_round_bf16(const double *x, double *out, int64_t n)
     for (int64_t i = 0; i < n; i++) out[i] = round_bf16(x[i]);
 }
 
+/* Nearest value of the scaled E4M3 format (item 6): a = x * 2^-s is rounded
+   to a multiple of the E4M3 spacing at its magnitude, 2^(e-4) for |a| in
+   [2^(e-1), 2^e) (3 mantissa bits), never finer than the subnormal spacing
+   2^-9; ties to even; magnitudes above 448 saturate to 448.  The result is
+   scaled back by 2^s (both scalings are exact). */
+static double round_fp8(double x, int s)
+{
+    if (x == 0.0 || !isfinite(x)) return x;
+    const double a = ldexp(x, -s);
+    int e;
+    (void)frexp(a, &e);
+    int q = e - 4;
+    if (q < -9) q = -9;
+    double r = ldexp(nearbyint(ldexp(a, -q)), q);
+    if (r > 448.0) r = 448.0;
+    if (r < -448.0) r = -448.0;
+    return ldexp(r, s);
+}
+
+/* Element-wise round_fp8 with scale 2^s (exported for the tests). */
+void sdm_oracle_round_fp8(const double *x, double *out, int64_t n, int s)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = round_fp8(x[i], s);
+}
+
+/* The value the state holds for x: itself (mode 0), bfloat16 (mode 1) or
+   scaled E4M3 (mode 2, scale 2^s). */
+static double store_value(double x, int state_mode, int s)
+{
+    if (state_mode == 1) return round_bf16(x);
+    if (state_mode == 2) return round_fp8(x, s);
+    return x;
+}
+
 static void run_chain(int64_t T, int H, int64_t N, int d_v, int W, int R, int b, int h,
                       const int32_t *Iw, const double *kw, const int32_t *Ir,
                       const double *qw, const void *v, int v_dtype, const float *alpha,
-                      const float *beta, const float *M0, int state_bf16, int c0, int c1,
-                      int ca, int cb, double *y, double *M)
+                      const float *beta, const float *M0, int state_mode, int scale_log2,
+                      int c0, int c1, int ca, int cb, double *y, double *M)
 {
     const int nc = c1 - c0;
     double *Mc = M + ((int64_t)b * H + h) * N * nc; /* this chain's [N][nc] */
     for (int64_t n = 0; n < N; n++)
         for (int c = ca; c < cb; c++) {
             const double m0 = (double)M0[((int64_t)h * N + n) * d_v + c];
-            Mc[n * nc + (c - c0)] = state_bf16 ? round_bf16(m0) : m0;
+            Mc[n * nc + (c - c0)] = store_value(m0, state_mode, scale_log2);
         }
 
     for (int64_t t = 0; t < T; t++) {
@@ -254,7 +294,7 @@ static void run_chain(int64_t T, int H, int64_t N, int d_v, int W, int R, int b,
                 double *row = &Mc[s * nc + (c - c0)];
                 const double m = a_t * (*row);     /* forget gate */
                 *row = m + b_t * k * (vt - m);     /* delta + input gate */
-                if (state_bf16) *row = round_bf16(*row);
+                *row = store_value(*row, state_mode, scale_log2);
             }
         }
         /* read: on the state after this token's write */
@@ -274,7 +314,8 @@ static void run_chain(int64_t T, int H, int64_t N, int d_v, int W, int R, int b,
  *   Iw,kw [B][T][H][W], Ir,qw [B][T][H][R]   selection (from the oracle)
  *   v [B][T][H][d_v] (float32 or bf16 bits), alpha,beta [B][T][H] float32
  *   M0 [H][N][d_v] float32
- *   state_bf16: 0 = float64 state, 1 = state held in bfloat16 (item 6 above)
+ *   state_mode: 0 = float64 state, 1 = state held in bfloat16, 2 = state held
+ *   in E4M3 with scale 2^scale_log2 (item 6 above)
  * Only the columns [c0, c1) of y and M are produced (columns of the state
  * never interact):  y [B][T][H][c1-c0], M [B][H][N][c1-c0], both float64.
  * Returns 0, or -1 on bad arguments.
@@ -282,13 +323,14 @@ static void run_chain(int64_t T, int H, int64_t N, int d_v, int W, int R, int b,
 int sdm_oracle_recurrence(int B, int64_t T, int H, int sqrtN, int d_v, int W, int R,
                           const int32_t *Iw, const double *kw, const int32_t *Ir,
                           const double *qw, const void *v, int v_dtype, const float *alpha,
-                          const float *beta, const float *M0, int state_bf16, int c0, int c1,
-                          double *y, double *M, int nthreads)
+                          const float *beta, const float *M0, int state_mode, int scale_log2,
+                          int c0, int c1, double *y, double *M, int nthreads)
 {
     if (B < 1 || T < 0 || H < 1 || sqrtN < 1 || d_v < 1 || W < 1 || R < 1) return -1;
     if (W > sqrtN || R > sqrtN || c0 < 0 || c1 > d_v || c0 >= c1) return -1;
     if (!Iw || !kw || !Ir || !qw || !v || !alpha || !beta || !M0 || !y || !M) return -1;
     if (v_dtype != ORACLE_F32 && v_dtype != ORACLE_BF16) return -1;
+    if (state_mode < 0 || state_mode > 2 || scale_log2 < -100 || scale_log2 > 100) return -1;
     if (nthreads < 1) nthreads = 1;
     const int64_t N = (int64_t)sqrtN * sqrtN;
     /* independent units: (chain, block of columns); CB columns per unit */
@@ -303,7 +345,7 @@ int sdm_oracle_recurrence(int B, int64_t T, int H, int sqrtN, int d_v, int W, in
         const int ca = c0 + blk * CB;
         const int cb = ca + CB < c1 ? ca + CB : c1;
         run_chain(T, H, N, d_v, W, R, b, h, Iw, kw, Ir, qw, v, v_dtype, alpha, beta, M0,
-                  state_bf16, c0, c1, ca, cb, y, M);
+                  state_mode, scale_log2, c0, c1, ca, cb, y, M);
     }
     return 0;
 }

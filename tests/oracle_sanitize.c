@@ -17,8 +17,9 @@ void sdm_oracle_round_bf16(const double *x, double *out, int64_t n);
 int sdm_oracle_recurrence(int B, int64_t T, int H, int sqrtN, int d_v, int W, int R,
                           const int32_t *Iw, const double *kw, const int32_t *Ir,
                           const double *qw, const void *v, int v_dtype, const float *alpha,
-                          const float *beta, const float *M0, int state_bf16, int c0, int c1,
-                          double *y, double *M, int nthreads);
+                          const float *beta, const float *M0, int state_mode, int scale_log2,
+                          int c0, int c1, double *y, double *M, int nthreads);
+void sdm_oracle_round_fp8(const double *x, double *out, int64_t n, int s);
 int sdm_oracle_backward(int B, int64_t T, int H, int sqrtN, int d_v, int W, int R,
                         const int32_t *Iw, const double *kw, const int32_t *Ir, const double *qw,
                         const void *v, int v_dtype, const float *alpha, const float *beta,
@@ -103,16 +104,17 @@ int main(void)
         const void *vv = dt ? (const void *)vb : (const void *)v;
         CHECK(sdm_oracle_topk_rows(ht, S, W, k, dt, Iw, kw, hi, lo, threads));
         CHECK(sdm_oracle_topk_rows(ht, S, R, q, dt, Ir, qw, NULL, NULL, threads));
-        for (int sb = 0; sb < 2; sb++) { /* float64 state, bfloat16 state */
+        for (int sb = 0; sb < 3; sb++) { /* float64, bfloat16 and scaled E4M3 state */
             CHECK(sdm_oracle_recurrence(B, T, H, S, D, W, R, Iw, kw, Ir, qw, vv, dt, alpha, beta,
-                                        M0, sb, 0, D, y, M, threads));
+                                        M0, sb, sb == 2 ? -4 : 0, 0, D, y, M, threads));
             CHECK(sdm_oracle_recurrence(B, T, H, S, D, W, R, Iw, kw, Ir, qw, vv, dt, alpha, beta,
-                                        M0, sb, 3, 7, y, M, threads)); /* column window */
+                                        M0, sb, sb == 2 ? 3 : 0, 3, 7, y, M, threads)); /* window */
         }
         CHECK(sdm_oracle_backward(B, T, H, S, D, W, R, Iw, kw, Ir, qw, vv, dt, alpha, beta, M0, dy,
                                   dt ? NULL : dMT, dkp, dqp, dv, da, db, dM0, threads));
     }
     sdm_oracle_round_bf16(y, dv, ht * D);
+    sdm_oracle_round_fp8(y, dv, ht * D, -5);
     /* the full ordering of a tiny key (K = sqrtN) and the smallest shape */
     CHECK(sdm_oracle_topk_rows(4, S, S, kp, 0, Iw, kw, hi, lo, 1));
     CHECK(sdm_oracle_topk_rows(1, 1, 1, kp, 0, Iw, kw, NULL, NULL, 1));

@@ -368,6 +368,111 @@ def test_bf16_state_error_bound():
     assert np.abs(o16["M"] - o64["M"]).max() > 0  # the rounding is really applied
 
 
+# ------------------------------------------------- scaled E4M3 state (reading)
+
+def _e4m3_values():
+    """Every finite non-negative value of the E4M3 format, ascending (from
+    torch's decoding of the 256 codes)."""
+    import torch
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    v = codes.to(torch.float64).numpy()
+    return np.unique(v[np.isfinite(v) & (v >= 0)])
+
+
+@pytest.mark.parametrize("s", [0, -4, 5])
+def test_round_fp8_matches_torch_conversion(s):
+    """The oracle's E4M3 rounding of x at scale 2^s (nearest, ties to even)
+    agrees with torch's float32 -> float8_e4m3fn conversion of x * 2^-s,
+    scaled back, wherever torch stays finite (|x * 2^-s| <= 464): random
+    values over the whole range, every value halfway between two
+    neighbours, the subnormals, signed zeros."""
+    import torch
+    rng = np.random.default_rng(11 + s)
+    a = (rng.standard_normal(30000) * np.exp2(rng.integers(-14, 9, 30000))).astype(np.float32)
+    vals = _e4m3_values()
+    mids = ((vals[1:] + vals[:-1]) / 2).astype(np.float32)
+    assert np.array_equal(mids.astype(np.float64), (vals[1:] + vals[:-1]) / 2)  # exact
+    sub = np.arange(0, 9, dtype=np.float32) * np.float32(2.0**-9)
+    special = np.array([0.0, -0.0, 448.0, 464.0, -464.0, 0.1, 1.0625, 1.1875], np.float32)
+    for arr in (a, mids, -mids, sub, special):
+        arr = arr[np.abs(arr) <= 464]
+        want = torch.from_numpy(arr.copy()).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+        got = oracle.round_fp8(arr.astype(np.float64) * 2.0**s, s) * 2.0**-s
+        np.testing.assert_array_equal(got, want)
+    # ties go to the neighbour with an even last mantissa bit: both ways occur
+    up = oracle.round_fp8(mids.astype(np.float64), 0) > mids
+    assert up.any() and (~up).any()
+
+
+def test_round_fp8_saturates():
+    """Beyond the largest magnitude the reading saturates (a state must stay
+    finite); torch's conversion gives NaN there."""
+    x = np.array([464.0001, 480.0, 500.0, 1e6, 1e30])
+    for s in (0, -4, 3):
+        np.testing.assert_array_equal(oracle.round_fp8(x * 2.0**s, s), 448.0 * 2.0**s)
+        np.testing.assert_array_equal(oracle.round_fp8(-x * 2.0**s, s), -448.0 * 2.0**s)
+
+
+def test_golden_recurrence_fp8_state(golden):
+    (c,) = golden("recurrence_fp8_state.txt")
+    S, D, T = int(c["sqrtN"][0]), int(c["d_v"][0]), int(c["T"][0])
+    sc = int(c["scale_log2"][0])
+    inp = dict(
+        kp=np.array(c["kp"], np.float32).reshape(1, T, 1, 2 * S),
+        qp=np.array(c["qp"], np.float32).reshape(1, T, 1, 2 * S),
+        v=np.array(c["v"], np.float32).reshape(1, T, 1, D),
+        alpha=np.array(c["alpha"], np.float32).reshape(1, T, 1),
+        beta=np.array(c["beta"], np.float32).reshape(1, T, 1),
+        M0=np.array(c["M0"], np.float32).reshape(1, S * S, D))
+    o = oracle.forward(inp, S, 1, 1, state="fp8", scale_log2=sc)
+    np.testing.assert_array_equal(o["y"].reshape(-1), c["y"])
+    np.testing.assert_array_equal(o["M"].reshape(-1), c["M"])
+    # another scale gives other values (the scale really applies)
+    o2 = oracle.forward(inp, S, 1, 1, state="fp8", scale_log2=0)
+    assert not np.array_equal(o2["y"], o["y"])
+
+
+def test_fp8_state_unwritten_rows_and_overwrite_gate():
+    """Rows never written hold M_0 rounded to the scaled format; with
+    alpha = beta = 1 and W = 1 a written row becomes round(v_t)."""
+    wl, d = _tiny(seed=34, S=8)
+    d["kp"][..., :wl.sqrtN] = -8.0
+    d["kp"][..., :2] = 8.0
+    o = oracle.forward(d, wl.sqrtN, wl.W, wl.R, state="fp8", scale_log2=-5)
+    for b in range(wl.B):
+        for h in range(wl.H):
+            never = np.setdiff1d(np.arange(wl.N), np.unique(o["Iw"][b, :, h]))
+            assert never.size > 0
+            np.testing.assert_array_equal(
+                o["M"][b, h, never], oracle.round_fp8(d["M0"][h, never].astype(np.float64), -5))
+    wl, d = _tiny(seed=35, W=1, R=1)
+    d["alpha"][:] = 1.0
+    d["beta"][:] = 1.0
+    o = oracle.forward(d, wl.sqrtN, 1, 1, state="fp8", scale_log2=-3)
+    for b in range(wl.B):
+        for h in range(wl.H):
+            last = {int(o["Iw"][b, t, h, 0]): t for t in range(wl.T)}
+            for sl, t in last.items():
+                np.testing.assert_array_equal(
+                    o["M"][b, h, sl], oracle.round_fp8(d["v"][b, t, h].astype(np.float64), -3))
+
+
+def test_fp8_state_error_bound():
+    """Each stored value carries at most half an E4M3 spacing (2^-4 relative
+    in the normal range, 2^-10 * 2^s absolute below it) of fresh rounding,
+    and writes are contractions, so the state stays within (writes + 1) *
+    (2^-4 * max|M| + 2^(s-10)) of the float64 state."""
+    wl, d = _tiny(seed=36, T=40, S=6, W=3, R=3)
+    s = -4
+    o8 = oracle.forward(d, wl.sqrtN, wl.W, wl.R, state="fp8", scale_log2=s)
+    o64 = oracle.forward(d, wl.sqrtN, wl.W, wl.R)
+    scale = max(np.abs(o64["M"]).max(), np.abs(d["v"]).max())
+    bound = (wl.T + 1) * (2.0**-4 * scale + 2.0**(s - 10))
+    assert np.abs(o8["M"] - o64["M"]).max() <= bound
+    assert np.abs(o8["y"] - o64["y"]).max() <= bound
+    assert np.abs(o8["M"] - o64["M"]).max() > 0
+
+
 # ------------------------------------------------------------------ backward
 
 def _loss(inp, S, W, R, Ry, RM):
