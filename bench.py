@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+FP8_SCALE_LOG2 = -4  # E4M3 state: codes of M * 2^4 (magnitudes up to 28)
 METRIC = "SDM select+write+read head-tokens/s and achieved HBM GB/s (% peak)"
 
 
@@ -113,7 +114,8 @@ def cpu_baseline(d, wl, seqs, T=None, state="f32", threads=None, runs=5):
     times = []
     for _ in range(runs):
         t = time.perf_counter()
-        oracle.forward(sub, wl.sqrtN, wl.W, wl.R, threads=cores, state=state)
+        oracle.forward(sub, wl.sqrtN, wl.W, wl.R, threads=cores, state=state,
+                       scale_log2=FP8_SCALE_LOG2)
         times.append(time.perf_counter() - t)
     dt = statistics.median(times)
     ht = seqs * T * wl.H
@@ -357,9 +359,9 @@ def measure_forward(wl, d, dev, state, variant, steps, warmup):
     import sparse_memory_linear_select_amd as sdm
 
     dd = _upload(d, dev)
-    st = torch.bfloat16 if state == "bf16" else torch.float32
-    esz = 2 if state == "bf16" else 4  # bytes per state element
-    core = sdm.SDM(dd["M0"], wl.W, wl.R, state=st)
+    st = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[state]
+    esz = {"f32": 4, "bf16": 2, "fp8": 1}[state]  # bytes per state element
+    core = sdm.SDM(dd["M0"], wl.W, wl.R, state=st, state_scale_log2=FP8_SCALE_LOG2)
     B, T, H = wl.B, wl.T, wl.H
     y = torch.empty((B, T, H, wl.d_v), dtype=torch.float32, device=dev)
     M = torch.empty((B, H, wl.N, wl.d_v), dtype=st, device=dev)
@@ -470,8 +472,9 @@ def main():
                     help="synthetic workload index (default 1: the 1.4B-style layer)")
     ap.add_argument("--variant", choices=["auto", "serial", "timepar"], default="auto",
                     help="write/read schedule (default: the library's choice)")
-    ap.add_argument("--state", choices=["f32", "bf16"], default="f32",
-                    help="element type of the state M (bf16: reduced-precision state)")
+    ap.add_argument("--state", choices=["f32", "bf16", "fp8"], default="f32",
+                    help="element type of the state M (bf16, or fp8: E4M3 codes scaled by "
+                         f"2^{FP8_SCALE_LOG2})")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-workloads", action="store_true",
                     help="measure the headline workload only (no `workloads` object)")
@@ -563,7 +566,10 @@ def main():
         "vs_baseline": None,
         "dtype": {("f32", "f32"): "f32", ("bf16", "f32"): "bf16 inputs, f32 state",
                   ("f32", "bf16"): "f32 compute, bf16 state",
-                  ("bf16", "bf16"): "bf16 inputs, f32 compute, bf16 state"}[(wl.dtype, args.state)],
+                  ("bf16", "bf16"): "bf16 inputs, f32 compute, bf16 state",
+                  ("f32", "fp8"): "f32 compute, fp8 (E4M3) state",
+                  ("bf16", "fp8"): "bf16 inputs, f32 compute, fp8 (E4M3) state"}[
+                      (wl.dtype, args.state)],
         "data": "synthetic (seeded; recipe in sdm_inputs.py)",
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": wl.H, "sqrtN": wl.sqrtN,
                    "N": wl.N, "d_v": wl.d_v, "W": wl.W, "R": wl.R, "inputs": wl.dtype,

@@ -69,8 +69,9 @@ typedef enum {
     SDM_ERR_HIP = 4          /* a HIP call failed; see sdm_last_error()  */
 } sdm_status;
 
-/* Element type of k', q' and v.  alpha, beta, M_0, y and M are float32. */
-typedef enum { SDM_F32 = 0, SDM_BF16 = 1 } sdm_dtype;
+/* Element type of k', q' and v (SDM_F32 or SDM_BF16), and of the state M
+ * (sdm_create_ex, sdm_create_fp8).  alpha, beta, M_0 and y are float32. */
+typedef enum { SDM_F32 = 0, SDM_BF16 = 1, SDM_FP8_E4M3 = 2 } sdm_dtype;
 
 /*
  * Write/read schedule used by sdm_forward.  Both produce the same result up
@@ -122,10 +123,32 @@ sdm_status sdm_create(const float *M0, int H, int sqrtN, int d_v, int W, int R,
  *             state holds it after the writes at tokens <= its own, rounded
  *             after each of them, so y does not depend on how the tokens are
  *             split into calls.
- * Errors as sdm_create, plus SDM_ERR_ARG for another state_dtype.
+ * Errors as sdm_create, plus SDM_ERR_ARG for another state_dtype
+ * (SDM_FP8_E4M3 included: it takes a scale, see sdm_create_fp8).
  */
 sdm_status sdm_create_ex(const float *M0, int H, int sqrtN, int d_v, int W, int R,
                          sdm_dtype state_dtype, sdm_handle *out);
+
+/*
+ * As sdm_create, with an 8-bit state: M holds OCP FP8 E4M3 codes (sign, 4
+ * exponent bits with bias 7, 3 mantissa bits, largest magnitude 448, no
+ * infinities) of the state scaled by 2^-scale_log2, i.e. a code c stands for
+ * the value c * 2^scale_log2.  The explainer "Sparse Delta Memory：通过稀疏性
+ * 扩展线性 RNN 的状态容量" names 8-bit states to fit N ~ 10^7 slots on one card
+ * (engineering notes); the pages fix no format or scale, so this is a
+ * reading: one power-of-two scale per layer (so scaling is exact), values
+ * rounded to the nearest code, ties to even, magnitudes beyond 448 *
+ * 2^scale_log2 saturated.  M_0 stays float32 and is rounded that way when M
+ * is initialised; every write computes a*row + c*v in float32 from the
+ * stored row and stores it rounded; reads use the stored rows and
+ * accumulate y in float32.  A quarter of the float32 row traffic.  Needs the
+ * time-parallel schedule (d_v % 4 == 0); no backward.  Choose the scale so
+ * that the state's magnitudes stay below 448 * 2^scale_log2 (e.g. -4 for
+ * values up to 28 with spacing 2^-11 near 2^-5).
+ * Errors as sdm_create, plus SDM_ERR_ARG for scale_log2 outside [-64, 64].
+ */
+sdm_status sdm_create_fp8(const float *M0, int H, int sqrtN, int d_v, int W, int R,
+                          int scale_log2, sdm_handle *out);
 
 /*
  * Release a handle (M_0 is not touched).  Makes no HIP call.  NULL is
@@ -162,8 +185,9 @@ sdm_status sdm_select(sdm_handle h, int B, int64_t T, const void *kp, const void
  *   workspace  device scratch of ws_bytes >= sdm_workspace_size(...) bytes,
  *              16-byte aligned; its contents are undefined afterwards.
  *   y          device [B][T][H][d_v] float32, output.
- *   M          device [B][H][N][d_v], float32 or bfloat16 as the handle's
- *              state type (sdm_create_ex): the final state on return.
+ *   M          device [B][H][N][d_v], float32, bfloat16 or E4M3 codes as the
+ *              handle's state type (sdm_create_ex, sdm_create_fp8): the
+ *              final state on return.
  *              Unless SDM_FLAG_CONTINUE is set it is first overwritten with
  *              M_0 (so a failed call can simply be retried); with the flag it
  *              must hold the state to continue from.

@@ -19,14 +19,14 @@ import os
 
 import torch
 
-__all__ = ["SDM", "SDMError", "lib", "lib_path", "F32", "BF16", "AUTO", "SERIAL", "TIMEPAR",
+__all__ = ["SDM", "SDMError", "lib", "lib_path", "F32", "BF16", "FP8_E4M3", "AUTO", "SERIAL", "TIMEPAR",
            "FLAG_CONTINUE", "EXPORTS", "NOALLOC_MAX_BYTES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsdm.so")
 _lib = None
 
-F32, BF16 = 0, 1
+F32, BF16, FP8_E4M3 = 0, 1, 2
 AUTO, SERIAL, TIMEPAR = 0, 1, 2
 FLAG_CONTINUE = 1
 STATUS = {0: "SDM_OK", 1: "SDM_ERR_ARG", 2: "SDM_ERR_UNSUPPORTED", 3: "SDM_ERR_WORKSPACE",
@@ -34,7 +34,7 @@ STATUS = {0: "SDM_OK", 1: "SDM_ERR_ARG", 2: "SDM_ERR_UNSUPPORTED", 3: "SDM_ERR_W
 
 # every function include/sdm.h declares
 EXPORTS = ("sdm_backward", "sdm_backward_workspace_size", "sdm_backward_workspace_size_ex",
-           "sdm_create", "sdm_create_ex",
+           "sdm_create", "sdm_create_ex", "sdm_create_fp8",
            "sdm_destroy", "sdm_workspace_size", "sdm_select", "sdm_forward",
            "sdm_forward_noalloc", "sdm_prepare", "sdm_apply", "sdm_write_histogram",
            "sdm_status_string", "sdm_last_error")
@@ -62,6 +62,7 @@ def lib():
         p, i, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
         L.sdm_create.argtypes = [p, i, i, i, i, i, ctypes.POINTER(p)]
         L.sdm_create_ex.argtypes = [p, i, i, i, i, i, i, ctypes.POINTER(p)]
+        L.sdm_create_fp8.argtypes = [p, i, i, i, i, i, i, ctypes.POINTER(p)]
         L.sdm_destroy.argtypes = [p]
         L.sdm_workspace_size.argtypes = [p, i, i64, i, i, ctypes.POINTER(sz)]
         L.sdm_select.argtypes = [p, i, i64, p, p, i, p, p, p, p, p]
@@ -88,7 +89,7 @@ def variant_name(core, B, T, dtype, variant) -> str:
     """Name of the schedule a call would use ("token-serial" or "time-parallel")."""
     if variant == SERIAL:
         return "token-serial"
-    if variant == TIMEPAR or core.state == torch.bfloat16:
+    if variant == TIMEPAR or core.state != torch.float32:
         return "time-parallel"
     n_auto = core.workspace_size(B, T, dtype, AUTO)
     return "time-parallel" if n_auto == core.workspace_size(B, T, dtype, TIMEPAR) and \
@@ -157,26 +158,41 @@ def _in_dtype(t: torch.Tensor) -> int:
 class SDM:
     """One SDM layer shape bound to its shared initial state M_0 (borrowed).
 
-    state: element type of the state M (torch.float32, or torch.bfloat16 for
-    the reduced-precision state, which needs the time-parallel schedule).
+    state: element type of the state M: torch.float32; torch.bfloat16; or
+    torch.float8_e4m3fn, whose codes stand for their value times
+    2^state_scale_log2 (M.float() * 2**state_scale_log2 gives the state).
+    The narrower states need the time-parallel schedule.
     """
 
-    def __init__(self, M0: torch.Tensor, W: int, R: int, state: torch.dtype = torch.float32):
+    def __init__(self, M0: torch.Tensor, W: int, R: int, state: torch.dtype = torch.float32,
+                 state_scale_log2: int = 0):
         _dev_tensor(M0, "M0", torch.float32)
         if M0.dim() != 3:
             raise SDMError(1, "M0 must be [H, N, d_v]")
-        if state not in (torch.float32, torch.bfloat16):
-            raise SDMError(1, f"state must be torch.float32 or torch.bfloat16, got {state}")
+        if state not in (torch.float32, torch.bfloat16, torch.float8_e4m3fn):
+            raise SDMError(1, "state must be torch.float32, torch.bfloat16 or "
+                              f"torch.float8_e4m3fn, got {state}")
         H, N, d_v = M0.shape
         sqrtN = math.isqrt(N)
         if sqrtN * sqrtN != N:
             raise SDMError(1, f"N = {N} is not a perfect square")
         self.M0, self.H, self.sqrtN, self.N, self.d_v = M0, H, sqrtN, N, d_v
         self.W, self.R, self.state = int(W), int(R), state
+        self.state_scale_log2 = int(state_scale_log2) if state == torch.float8_e4m3fn else 0
         h = ctypes.c_void_p()
-        _check(lib().sdm_create_ex(_ptr(M0), H, sqrtN, d_v, self.W, self.R,
-                                   BF16 if state == torch.bfloat16 else F32, ctypes.byref(h)))
+        if state == torch.float8_e4m3fn:
+            _check(lib().sdm_create_fp8(_ptr(M0), H, sqrtN, d_v, self.W, self.R,
+                                        self.state_scale_log2, ctypes.byref(h)))
+        else:
+            _check(lib().sdm_create_ex(_ptr(M0), H, sqrtN, d_v, self.W, self.R,
+                                       BF16 if state == torch.bfloat16 else F32, ctypes.byref(h)))
         self._h = h
+
+    def state_values(self, M: torch.Tensor) -> torch.Tensor:
+        """The float32 values a state tensor M of this layer holds."""
+        if self.state == torch.float8_e4m3fn:
+            return M.float() * (2.0 ** self.state_scale_log2)
+        return M.float()
 
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value:

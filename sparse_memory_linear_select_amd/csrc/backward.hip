@@ -38,7 +38,7 @@
 namespace sdm {
 namespace {
 
-constexpr int kLPR = StateRow<false>::kLPR;  // 8 lanes x float4 per 128-byte row slice
+constexpr int kLPR = StateRow<kStateF32>::kLPR;  // 8 lanes x float4 per 128-byte row slice
 constexpr int kRPI = 64 / kLPR;
 constexpr int kDots = 3 * kMaxK;  // per (chain, token): da[64], dc[64], dq[64]
 
@@ -575,7 +575,7 @@ hipError_t launch_tp_backward(const Shape &s, int chunks, const uint32_t *rec, v
                            chunk_state(0), nstate);
         e = hipGetLastError();
     } else {
-        e = launch_init(s, M0, chunk_state(0), false, st);
+        e = launch_init(s, M0, chunk_state(0), StateFmt{}, st);
     }
     if (e != hipSuccess) return e;
     if (dMT)

@@ -15,17 +15,28 @@ struct DecArgs {
     const uint32_t *rec;  // records [chain] (one token)
     const void *v;        // [B][1][H][d_v]
     float *y;             // [B][1][H][d_v]
-    void *M;              // [chain][N][d_v] float32 or bfloat16
+    void *M;              // [chain][N][d_v] float32, bfloat16 or E4M3
+    float ssc, sisc;      // E4M3 state: 2^s, 2^-s
     int64_t N;
     int H, d_v, W, R, Wp, Rp, rec_dwords;
     int64_t chains;
 };
 
-template <bool BF16, bool SB, int NK>
+// Lanes per row slice: the state's 128-byte slice, except for an E4M3 state,
+// whose 128 bytes take 32 lanes; there 16 lanes (64 bytes) keep 4 row groups
+// and at most 16 references per group in registers.
+template <int ST>
+constexpr int dec_lpr()
+{
+    return ST == kStateFP8 ? 16 : StateRow<ST>::kLPR;
+}
+
+template <bool BF16, int ST, int NK>
 __global__ __launch_bounds__(64) void rw_decode_kernel(DecArgs a, int nslice)
 {
-    using S = StateRow<SB>;
-    constexpr int kLPR = S::kLPR, kRPI = 64 / kLPR;
+    using S = StateRow<ST>;
+    const S st(a.ssc, a.sisc);
+    constexpr int kLPR = dec_lpr<ST>(), kRPI = 64 / kLPR;
     const int lane = threadIdx.x;
     const int64_t unit = blockIdx.x;
     const int slice = (int)(unit % nslice);
@@ -68,9 +79,9 @@ __global__ __launch_bounds__(64) void rw_decode_kernel(DecArgs a, int nslice)
     // writes (rows are distinct within a token)
     typename S::Raw old[NK];
 #pragma unroll
-    for (int i = 0; i < NK; i++) old[i] = S::load_raw(Mr, wslot[i]);
+    for (int i = 0; i < NK; i++) old[i] = st.load_raw(Mr, wslot[i]);
 #pragma unroll
-    for (int i = 0; i < NK; i++) S::store(S::round(fma4(wa[i], S::widen(old[i]), wc[i], vv)), Mr, wslot[i]);
+    for (int i = 0; i < NK; i++) st.store(st.round(fma4(wa[i], st.widen(old[i]), wc[i], vv)), Mr, wslot[i]);
     // the reads below are ordered after the stores at workgroup scope: the
     // workgroup is this one wavefront, whose vector memory operations all go
     // through one CU's L1 (no L2 write-back or invalidation is needed)
@@ -80,11 +91,11 @@ __global__ __launch_bounds__(64) void rw_decode_kernel(DecArgs a, int nslice)
     // reads of the updated state
     typename S::Raw row[NK];
 #pragma unroll
-    for (int i = 0; i < NK; i++) row[i] = S::load_raw(Mr, rslot[i]);
+    for (int i = 0; i < NK; i++) row[i] = st.load_raw(Mr, rslot[i]);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int i = 0; i < NK; i++) {
-        const float4 x = S::widen(row[i]);
+        const float4 x = st.widen(row[i]);
         acc.x = fmaf(rq[i], x.x, acc.x);
         acc.y = fmaf(rq[i], x.y, acc.y);
         acc.z = fmaf(rq[i], x.z, acc.z);
@@ -100,10 +111,10 @@ __global__ __launch_bounds__(64) void rw_decode_kernel(DecArgs a, int nslice)
     if (g == 0 && col_ok) *reinterpret_cast<float4 *>(a.y + chain * a.d_v + col) = acc;
 }
 
-template <bool SB>
+template <int ST>
 hipError_t launch_state(const Shape &s, const DecArgs &a, bool bf16, hipStream_t st)
 {
-    constexpr int kLPR = StateRow<SB>::kLPR, kRPI = 64 / kLPR;
+    constexpr int kLPR = dec_lpr<ST>(), kRPI = 64 / kLPR;
     const int nslice = (s.d_v + 4 * kLPR - 1) / (4 * kLPR);
     // one wavefront per workgroup: few units, spread over as many CUs as possible
     const dim3 grid((unsigned)(a.chains * nslice));
@@ -111,9 +122,9 @@ hipError_t launch_state(const Shape &s, const DecArgs &a, bool bf16, hipStream_t
     const int nk = (K + kRPI - 1) / kRPI;
 #define SDM_DEC(NK_)                                                                              \
     if (nk <= NK_) {                                                                              \
-        if (bf16) hipLaunchKernelGGL((rw_decode_kernel<true, SB, NK_>), grid, dim3(64), 0, st, a, \
+        if (bf16) hipLaunchKernelGGL((rw_decode_kernel<true, ST, NK_>), grid, dim3(64), 0, st, a, \
                                      nslice);                                                     \
-        else hipLaunchKernelGGL((rw_decode_kernel<false, SB, NK_>), grid, dim3(64), 0, st, a,     \
+        else hipLaunchKernelGGL((rw_decode_kernel<false, ST, NK_>), grid, dim3(64), 0, st, a,     \
                                 nslice);                                                          \
         return hipGetLastError();                                                                 \
     }
@@ -130,7 +141,7 @@ bool decode_supported(const Shape &s)
 }
 
 hipError_t launch_rw_decode(const Shape &s, const uint32_t *rec, const void *v, bool bf16,
-                            float *y, void *M, bool state_bf16, hipStream_t st)
+                            float *y, void *M, StateFmt fmt, hipStream_t st)
 {
     DecArgs a{};
     const RecLayout L(s.W, s.R);
@@ -147,7 +158,13 @@ hipError_t launch_rw_decode(const Shape &s, const uint32_t *rec, const void *v, 
     a.Rp = L.Rp;
     a.rec_dwords = L.dwords();
     a.chains = (int64_t)s.B * s.H;
-    return state_bf16 ? launch_state<true>(s, a, bf16, st) : launch_state<false>(s, a, bf16, st);
+    a.ssc = ldexpf(1.0f, fmt.scale_log2);
+    a.sisc = ldexpf(1.0f, -fmt.scale_log2);
+    switch (fmt.type) {
+        case kStateBF16: return launch_state<kStateBF16>(s, a, bf16, st);
+        case kStateFP8: return launch_state<kStateFP8>(s, a, bf16, st);
+        default: return launch_state<kStateF32>(s, a, bf16, st);
+    }
 }
 
 }  // namespace sdm

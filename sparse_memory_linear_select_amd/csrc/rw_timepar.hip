@@ -54,6 +54,7 @@ struct TPArgs {
     int E, nepoch, passes, kshift;
     int ep0, nrun;  // sort/link launches: epochs [ep0, ep0 + nrun)
     int64_t chains;
+    float ssc, sisc;  // E4M3 state: 2^s and 2^-s (the scale of the stored codes)
     float *tape;    // backward's forward pass: [chain][tapeT][W][d_v] epoch-start rows
     int64_t tapeT, tape_t0;  // tokens per chain in the tape, token of its first entry
 };
@@ -206,12 +207,13 @@ __global__ __launch_bounds__(kSortThreads) void tp_sort_kernel(TPArgs a, SortIO 
 // the entries finds the exact range.  One wavefront per token: lane r takes
 // read r, a prefix sum over the lanes places the pairs.
 //
-// With `stored` (a bfloat16 state) a read must see the row as the state
-// holds it, rounded after every write, which no composed weight can give.
-// There every read keeps weight q, a read that sees in-epoch writes gets the
-// link (first write, count) to replay them, and the token's pair area holds,
-// per read, the first of those writes: token, a, c at [r], [R + r], [2R + r]
-// (3R dwords <= the 2P dwords of the area, as P >= 2R).
+// With `stored` (a bfloat16 or E4M3 state) a read must see the row as the
+// state holds it, rounded after every write, which no composed weight can
+// give.  There every read keeps weight q, a read that sees in-epoch writes
+// gets the link (first write, count) to replay them, and the token's pair
+// area holds, per read, the first two of those writes: token, a, c of the
+// first at [r], [R + r], [2R + r], of the second at [3R + r], [4R + r],
+// [5R + r] (6R dwords <= the 2P dwords of the area, as P >= 3R).
 __global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int stride, int exact,
                                                                int stored)
 {
@@ -286,6 +288,12 @@ __global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int str
                 fw[lane] = e.tw >> 6;
                 fw[a.R + lane] = __float_as_uint(e.a);
                 fw[2 * a.R + lane] = __float_as_uint(e.c);
+                if (cnt > 1) {
+                    const TPEntry e2 = se[j + 1];
+                    fw[3 * a.R + lane] = e2.tw >> 6;
+                    fw[4 * a.R + lane] = __float_as_uint(e2.a);
+                    fw[5 * a.R + lane] = __float_as_uint(e2.c);
+                }
             }
             if (lane == 0) a.npair[ct] = 0u;
             continue;
@@ -336,7 +344,8 @@ constexpr int kPairBatch = 4;  // v pairs per row group in flight
 template <int NR, bool BF16>
 __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int nslice)
 {
-    using S = StateRow<false>;  // float32 state (a bfloat16 state: tp_read_bf16_kernel)
+    using S = StateRow<kStateF32>;  // float32 state (narrower states: tp_read_stored_kernel)
+    const S st(0.f, 0.f);
     constexpr int kLPR = S::kLPR, kRPI = 64 / kLPR;
     const int lane = threadIdx.x & 63;
     const int64_t chain = grid_chain();
@@ -379,12 +388,12 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int nsli
         for (int i = 0; i < NR; i++) {
             const uint32_t sl = group_bcast<kLPR>(sl_mine, i);
             const bool ok = col_ok & (g * NR + i < a.R);
-            row[i] = S::load_raw(Mr, ok ? (sl & kSlotMask) * rowb + col * S::kElem : kOff);
+            row[i] = st.load_raw(Mr, ok ? (sl & kSlotMask) * rowb + col * S::kElem : kOff);
         }
 #pragma unroll
         for (int i = 0; i < NR; i++) {
             // masked references have weight 0 and a zero row
-            const float4 rv = S::widen(row[i]);
+            const float4 rv = st.widen(row[i]);
             const float wr = __uint_as_float(group_bcast<kLPR>(__float_as_uint(wr_mine), i));
             acc.x = fmaf(wr, rv.x, acc.x);
             acc.y = fmaf(wr, rv.y, acc.y);
@@ -399,14 +408,14 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int nsli
         for (int i = 0; i < NR; i++) {
             const uint32_t sl = group_bcast<kLPR>(sl_mine, i);
             const bool ok = col_ok & (g * NR + i < a.R);
-            float4 rv = S::load(Mr, ok ? (sl & kSlotMask) * rowb + col * S::kElem : kOff);
+            float4 rv = st.load(Mr, ok ? (sl & kSlotMask) * rowb + col * S::kElem : kOff);
             // links exist only for the R real references; zero unless the plan overflowed
             const uint32_t l = (g * NR + i < a.R) ? lkp[i] : 0u;
             const int first = (int)(l >> kCntBits), cnt = (int)(l & ((1u << kCntBits) - 1u));
             for (int k = 0; k < cnt; k++) {  // writes of this slot earlier in the epoch
                 const TPEntry e = se[first + k];
                 const float4 vv = load_v<BF16>(a.v, vrow0 + (t0 + (e.tw >> 6)) * hd);
-                rv = S::round(fma4(e.a, rv, e.c, vv));
+                rv = st.round(fma4(e.a, rv, e.c, vv));
             }
             const float wr = __uint_as_float(group_bcast<kLPR>(__float_as_uint(wr_mine), i));
             acc.x = fmaf(wr, rv.x, acc.x);
@@ -445,23 +454,33 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int nsli
         *reinterpret_cast<float4 *>(a.y + (b * a.T * a.H + t * a.H + h) * a.d_v + col) = acc;
 }
 
-// Read with a bfloat16 state.  The state holds every written row rounded
-// to bfloat16, so a read of a slot written earlier in the epoch (at a token
-// <= its own) must see the row after each of those writes, rounded: it
-// replays them on the epoch-start row with the update kernel's own
-// operations, S::round(a*row + c*v) in time order.  One wavefront per
-// (chain, token of the epoch, 128-byte row slice), 16 lanes per row group,
-// group g taking reads g*NR .. g*NR + NR-1; lane q of the group holds read
-// g*NR + q: slot word, weight q, link (first write, count) and the first
-// write's token, a and c from the plan.  The row gathers and the first
-// writes' v gathers depend only on the plan and are all issued before any
-// arithmetic; a read with two or more in-epoch writes takes the rest from the
-// sorted events (about one read in eleven at the 1.4B-style layer).
-template <int NR, bool BF16>
-__global__ __launch_bounds__(256) void tp_read_bf16_kernel(TPArgs a, int ep, int nslice)
+// Read with a bfloat16 or E4M3 state.  The state holds every written row
+// rounded, so a read of a slot written earlier in the epoch (at a token <=
+// its own) must see the row after each of those writes, rounded: it replays
+// them on the epoch-start row with the update kernel's own operations,
+// st.round(a*row + c*v) in time order.
+//
+// One wavefront per (chain, token of the epoch, 128-byte row slice); row
+// group g (kLPR lanes) takes reads g*NR .. g*NR + NR-1, and lane q of the
+// group holds the plan of read g*NR + q: slot word, weight q, link (first
+// write, count) and the first two writes' token, a and c.  The epoch-start
+// rows of the reads that see no in-epoch write are gathered at once.  The
+// others are taken kD at a time per group (lowest index first): their rows
+// and the v slices of their first two writes depend only on the plan and
+// are gathered together; a third or later write comes from the sorted
+// events, one round trip for all kD reads per write.  Each replayed row
+// (exactly a stored value) goes back into the group's row registers, so y
+// sums the R rows in read order whichever reads saw in-epoch writes: y does
+// not depend on where epochs start.
+constexpr int kReplayBatch = 4;  // replayed reads per row group in flight
+
+template <int NR, bool BF16, int ST>
+__global__ __launch_bounds__(256) void tp_read_stored_kernel(TPArgs a, int ep, int nslice)
 {
-    using S = StateRow<true>;
-    constexpr int kLPR = S::kLPR;
+    using S = StateRow<ST>;
+    constexpr int kLPR = S::kLPR, kD = kReplayBatch;
+    static_assert(NR <= kLPR, "one read per lane of a row group");
+    const S st(a.ssc, a.sisc);
     const int lane = threadIdx.x & 63;
     const int64_t chain = grid_chain();
     const int64_t t0 = (int64_t)ep * a.E;
@@ -493,46 +512,104 @@ __global__ __launch_bounds__(256) void tp_read_bf16_kernel(TPArgs a, int ep, int
     const uint32_t sl_mine = mine ? rc[3 * a.Wp + r] : 0u;
     const float wr_mine = mine ? a.rwt[ct * kMaxK + r] : 0.0f;
     const uint32_t lk_mine = mine ? a.rlink[ct * kMaxK + r] : 0u;
-    uint32_t t1_mine = 0u, a1_mine = 0u, c1_mine = 0u;
-    if (lk_mine != 0u) {
-        t1_mine = fw[r];
-        a1_mine = fw[a.R + r];
-        c1_mine = fw[2 * a.R + r];
+    const int cnt_mine = (int)(lk_mine & ((1u << kCntBits) - 1u));
+    uint32_t w1[3] = {0u, 0u, 0u}, w2[3] = {0u, 0u, 0u};  // (token, a, c) of writes 1, 2
+    if (cnt_mine > 0) {
+        w1[0] = fw[r];
+        w1[1] = fw[a.R + r];
+        w1[2] = fw[2 * a.R + r];
     }
+    if (cnt_mine > 1) {
+        w2[0] = fw[3 * a.R + r];
+        w2[1] = fw[4 * a.R + r];
+        w2[2] = fw[5 * a.R + r];
+    }
+
+    // epoch-start rows of the reads without in-epoch writes
     typename S::Raw row[NR];
 #pragma unroll
     for (int i = 0; i < NR; i++) {
         const uint32_t sl = group_bcast<kLPR>(sl_mine, i);
-        const bool ok = col_ok & (g * NR + i < a.R);
-        row[i] = S::load_raw(Mr, ok ? (sl & kSlotMask) * rowb + col * S::kElem : kOff);
-    }
-    // v of each read's first in-epoch write (the group shares the read, so
-    // the condition is uniform within the group)
-    float4 v1[NR];
-#pragma unroll
-    for (int i = 0; i < NR; i++) {
         const uint32_t lk = group_bcast<kLPR>(lk_mine, i);
-        const uint32_t t1 = group_bcast<kLPR>(t1_mine, i);
-        v1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (lk != 0u) v1[i] = load_v<BF16>(a.v, vrow0 + (t0 + t1) * hd);
+        const bool ok = col_ok & (g * NR + i < a.R) & (lk == 0u);
+        row[i] = st.load_raw(Mr, ok ? (sl & kSlotMask) * rowb + col * S::kElem : kOff);
+    }
+
+    // the group's reads with in-epoch writes (bit i: read g*NR + i)
+    const uint64_t dirty = __ballot(lk_mine != 0u);
+    uint32_t dm = (uint32_t)(dirty >> (g * kLPR)) & (uint32_t)((1ull << NR) - 1ull);
+    while (__ballot(dm != 0u) != 0ull) {  // wave-uniform
+        int id[kD];
+        bool has[kD];
+#pragma unroll
+        for (int d = 0; d < kD; d++) {
+            has[d] = dm != 0u;
+            id[d] = has[d] ? __builtin_ctz(dm) : 0;
+            dm &= dm - 1u;
+        }
+        typename S::Raw drow[kD];
+        float4 v1[kD], v2[kD];
+        float a1[kD], c1[kD], a2[kD], c2[kD];
+        int first[kD], cnt[kD];
+#pragma unroll
+        for (int d = 0; d < kD; d++) {
+            const int src = g * kLPR + id[d];  // the lane holding the read's plan
+            const uint32_t sl = lane_read(sl_mine, src);
+            const uint32_t lk = lane_read(lk_mine, src);
+            const uint32_t t1 = lane_read(w1[0], src), t2 = lane_read(w2[0], src);
+            a1[d] = __uint_as_float(lane_read(w1[1], src));
+            c1[d] = __uint_as_float(lane_read(w1[2], src));
+            a2[d] = __uint_as_float(lane_read(w2[1], src));
+            c2[d] = __uint_as_float(lane_read(w2[2], src));
+            first[d] = (int)(lk >> kCntBits);
+            cnt[d] = has[d] ? (int)(lk & ((1u << kCntBits) - 1u)) : 0;
+            drow[d] = st.load_raw(Mr, (has[d] & col_ok) ? (sl & kSlotMask) * rowb + col * S::kElem
+                                                          : kOff);
+            v1[d] = make_float4(0.f, 0.f, 0.f, 0.f);
+            v2[d] = v1[d];
+            if (cnt[d] > 0) v1[d] = load_v<BF16>(a.v, vrow0 + (t0 + t1) * hd);
+            if (cnt[d] > 1) v2[d] = load_v<BF16>(a.v, vrow0 + (t0 + t2) * hd);
+        }
+        float4 rv[kD];
+#pragma unroll
+        for (int d = 0; d < kD; d++) {
+            rv[d] = st.round(fma4(a1[d], st.widen(drow[d]), c1[d], v1[d]));
+            if (cnt[d] > 1) rv[d] = st.round(fma4(a2[d], rv[d], c2[d], v2[d]));
+        }
+        // third and later in-epoch writes (rare)
+        for (int k = 2;; k++) {
+            bool more = false;
+#pragma unroll
+            for (int d = 0; d < kD; d++) more |= k < cnt[d];
+            if (__ballot(more) == 0ull) break;
+            TPEntry e[kD];
+            float4 vk[kD];
+#pragma unroll
+            for (int d = 0; d < kD; d++)
+                if (k < cnt[d]) e[d] = se[first[d] + k];
+#pragma unroll
+            for (int d = 0; d < kD; d++)
+                if (k < cnt[d]) vk[d] = load_v<BF16>(a.v, vrow0 + (t0 + (e[d].tw >> 6)) * hd);
+#pragma unroll
+            for (int d = 0; d < kD; d++)
+                if (k < cnt[d]) rv[d] = st.round(fma4(e[d].a, rv[d], e[d].c, vk[d]));
+        }
+        // back into the read's row register (each value is exactly a stored one)
+#pragma unroll
+        for (int d = 0; d < kD; d++) {
+            if (!has[d]) continue;
+            const typename S::Raw p = st.pack(rv[d]);
+#pragma unroll
+            for (int i = 0; i < NR; i++)
+                if (id[d] == i) row[i] = p;
+        }
     }
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int i = 0; i < NR; i++) {
-        const uint32_t lk = group_bcast<kLPR>(lk_mine, i);
-        const float a1 = __uint_as_float(group_bcast<kLPR>(a1_mine, i));
-        const float c1 = __uint_as_float(group_bcast<kLPR>(c1_mine, i));
+        // masked references have weight 0 and a zero row
+        const float4 rv = st.widen(row[i]);
         const float wr = __uint_as_float(group_bcast<kLPR>(__float_as_uint(wr_mine), i));
-        float4 rv = S::widen(row[i]);
-        if (lk != 0u) {
-            rv = S::round(fma4(a1, rv, c1, v1[i]));
-            const int first = (int)(lk >> kCntBits), cnt = (int)(lk & ((1u << kCntBits) - 1u));
-            for (int k = 1; k < cnt; k++) {  // further writes of this slot earlier in the epoch
-                const TPEntry e = se[first + k];
-                const float4 vv = load_v<BF16>(a.v, vrow0 + (t0 + (e.tw >> 6)) * hd);
-                rv = S::round(fma4(e.a, rv, e.c, vv));
-            }
-        }
         acc.x = fmaf(wr, rv.x, acc.x);
         acc.y = fmaf(wr, rv.y, acc.y);
         acc.z = fmaf(wr, rv.z, acc.z);
@@ -571,13 +648,16 @@ __global__ __launch_bounds__(256) void tp_read_bf16_kernel(TPArgs a, int ep, int
 // in the wave's last group or for a segment longer than the next group
 // (write/read 7.50 -> 7.19 ms; doing the tail inside the per-event loop,
 // from memory, forced full waits for every outstanding load).  A bfloat16
-// state is held to six waves per SIMD.
-template <bool BF16, int SPG, bool SB, bool TAPE = false>
-__global__ __launch_bounds__(256, SB ? 6 : 1) void tp_update_kernel(TPArgs a, int ep, int nslice,
-                                                                    int nblk, bool rev)
+// state is held to six waves per SIMD, an E4M3 state (whose codes take more
+// registers to encode) to five.
+template <bool BF16, int SPG, int ST, bool TAPE = false>
+__global__ __launch_bounds__(256, ST == kStateBF16 ? 6 : (ST == kStateFP8 ? 5 : 1)) void tp_update_kernel(TPArgs a, int ep,
+                                                                                 int nslice,
+                                                                                 int nblk, bool rev)
 {
-    static_assert(!(TAPE && SB), "the tape holds float32 rows");
-    using S = StateRow<SB>;
+    static_assert(!(TAPE && ST != kStateF32), "the tape holds float32 rows");
+    using S = StateRow<ST>;
+    const S st(a.ssc, a.sisc);
     constexpr int kLPR = S::kLPR, kRPI = 64 / kLPR;
     const int lane = threadIdx.x & 63;
     const int64_t cg = grid_chain();
@@ -631,7 +711,7 @@ __global__ __launch_bounds__(256, SB ? 6 : 1) void tp_update_kernel(TPArgs a, in
         const bool in = j0 + s < n;
         same |= (uint32_t)(in & (sl == prev)) << s;
         const bool head = in & (sl != prev);
-        row[s] = S::load(Mr, (head & col_ok) ? sl * rowb + col * S::kElem : kOff);
+        row[s] = st.load(Mr, (head & col_ok) ? sl * rowb + col * S::kElem : kOff);
         const uint32_t tw = group_bcast<kLPR>(me.tw, s);
         vv[s] = load_v<BF16>(a.v, vrow0 + (t0 + (tw >> 6)) * hd);
         prev = sl;
@@ -650,7 +730,7 @@ __global__ __launch_bounds__(256, SB ? 6 : 1) void tp_update_kernel(TPArgs a, in
             ev.tw = group_bcast<kLPR>(me.tw, s);
             tape_put(ev, row[s], head & col_ok);
         }
-        float4 r = S::round(fma4(__uint_as_float(group_bcast<kLPR>(__float_as_uint(me.a), s)), row[s],
+        float4 r = st.round(fma4(__uint_as_float(group_bcast<kLPR>(__float_as_uint(me.a), s)), row[s],
                                  __uint_as_float(group_bcast<kLPR>(__float_as_uint(me.c), s)), vv[s]));
         // the rest of the segment within the group, in time order
         bool more = true;
@@ -658,7 +738,7 @@ __global__ __launch_bounds__(256, SB ? 6 : 1) void tp_update_kernel(TPArgs a, in
         for (int s2 = s + 1; s2 < SPG; s2++) {
             more = more & ((same >> s2) & 1u);
             if (more)
-                r = S::round(fma4(__uint_as_float(group_bcast<kLPR>(__float_as_uint(me.a), s2)), r,
+                r = st.round(fma4(__uint_as_float(group_bcast<kLPR>(__float_as_uint(me.a), s2)), r,
                                   __uint_as_float(group_bcast<kLPR>(__float_as_uint(me.c), s2)), vv[s2]));
         }
         const uint32_t sl = group_bcast<kLPR>(me.slot, s);
@@ -668,7 +748,7 @@ __global__ __launch_bounds__(256, SB ? 6 : 1) void tp_update_kernel(TPArgs a, in
             slt = sl;
         }
         tail |= cont;
-        S::store(r, Mr, (head & !cont & col_ok) ? sl * rowb + col * S::kElem : kOff);
+        st.store(r, Mr, (head & !cont & col_ok) ? sl * rowb + col * S::kElem : kOff);
     }
     // The events just past the group are the next row group's (same wave,
     // same columns, kLPR lanes up): its lanes hold their fields, v rows and
@@ -691,7 +771,7 @@ __global__ __launch_bounds__(256, SB ? 6 : 1) void tp_update_kernel(TPArgs a, in
             v2.y = __int_as_float(__builtin_amdgcn_ds_bpermute(up * 4, __float_as_int(vv[s2].y)));
             v2.z = __int_as_float(__builtin_amdgcn_ds_bpermute(up * 4, __float_as_int(vv[s2].z)));
             v2.w = __int_as_float(__builtin_amdgcn_ds_bpermute(up * 4, __float_as_int(vv[s2].w)));
-            if (go) rt = S::round(fma4(a2, rt, c2, v2));
+            if (go) rt = st.round(fma4(a2, rt, c2, v2));
         }
         // the last group of the wave, or a segment that outlasts the next group too
         if (inw) jm = go ? j0 + 2 * SPG : n;
@@ -706,11 +786,11 @@ __global__ __launch_bounds__(256, SB ? 6 : 1) void tp_update_kernel(TPArgs a, in
             const bool c1 = (j + 1 < n) & (f1.slot == slt);
             const float4 v0 = load_v<BF16>(a.v, vrow0 + (t0 + (f0.tw >> 6)) * hd);
             const float4 v1 = load_v<BF16>(a.v, vrow0 + (t0 + ((c1 ? f1 : f0).tw >> 6)) * hd);
-            rt = S::round(fma4(f0.a, rt, f0.c, v0));
+            rt = st.round(fma4(f0.a, rt, f0.c, v0));
             if (!c1) break;
-            rt = S::round(fma4(f1.a, rt, f1.c, v1));
+            rt = st.round(fma4(f1.a, rt, f1.c, v1));
         }
-        S::store(rt, Mr, col_ok ? slt * rowb + col * S::kElem : kOff);
+        st.store(rt, Mr, col_ok ? slt * rowb + col * S::kElem : kOff);
     }
 }
 
@@ -734,11 +814,13 @@ int tp_epoch_len(const Shape &s)
 }
 
 // v pairs per token: twice the expected number at the end of an epoch
-// (R reads, each slot written about E*W/N times per epoch)
+// (R reads, each slot written about E*W/N times per epoch), and at least
+// 3R, which the stored-value plan needs (two writes per read, 3 dwords each)
 static int tp_pair_cap(const Shape &s, int E)
 {
     const int64_t m = ((int64_t)E * s.W + s.N() - 1) / s.N();
-    const int64_t p = 2 * (int64_t)s.R * (m > 1 ? m : 1);
+    int64_t p = 2 * (int64_t)s.R * (m > 1 ? m : 1);
+    if (p < 3 * (int64_t)s.R) p = 3 * (int64_t)s.R;
     return (int)((p + 7) / 8 * 8);
 }
 
@@ -810,7 +892,7 @@ bool tp_supported(const Shape &s)
 }
 
 hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipStream_t st,
-                             int ep0, int ep1, bool link, bool state_bf16)
+                             int ep0, int ep1, bool link, bool stored)
 {
     TPArgs a = tp_args(s, rec, ws, nullptr, nullptr, nullptr);
     if (ep1 < 0 || ep1 > a.nepoch) ep1 = a.nepoch;
@@ -831,31 +913,35 @@ hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipS
     const int exact = stride == 1 && a.kshift == 0 && nmax <= 16384;
     const size_t lds = (size_t)((nmax + stride - 1) / stride) * sizeof(uint16_t) * (exact ? 2 : 1);
     hipLaunchKernelGGL(tp_link_kernel, dim3((unsigned)blocks), dim3(kSortThreads), lds, st, a,
-                       stride, exact, state_bf16 ? 1 : 0);
+                       stride, exact, stored ? 1 : 0);
     return hipGetLastError();
 }
 
-template <bool SB>
+template <int ST>
 static hipError_t tp_apply_state(const Shape &s, TPArgs a, bool bf16, hipStream_t st, int ep0,
                                  int ep1)
 {
-    constexpr int kLPR = StateRow<SB>::kLPR, kRPI = 64 / kLPR;
+    constexpr int kLPR = StateRow<ST>::kLPR, kRPI = 64 / kLPR;
     const int nslice = (s.d_v + 4 * kLPR - 1) / (4 * kLPR);
     const int nr = (s.R + kRPI - 1) / kRPI;
     for (int ep = ep0; ep < ep1; ep++) {
         const int64_t t0 = (int64_t)ep * a.E;
         const int ne = (int)((s.T - t0) < a.E ? (s.T - t0) : a.E);
         const dim3 rgrid = chain_grid(a.chains, (int64_t)ne * nslice);
-        if constexpr (SB) {  // stored-value reads (rows rounded after every write)
+        if constexpr (ST != kStateF32) {  // stored-value reads (rows rounded after every write)
 #define SDM_TP_READ(NR_)                                                                          \
     if (nr <= NR_) {                                                                              \
-        if (bf16) hipLaunchKernelGGL((tp_read_bf16_kernel<NR_, true>), rgrid, dim3(256), 0, st,   \
-                                     a, ep, nslice);                                              \
-        else hipLaunchKernelGGL((tp_read_bf16_kernel<NR_, false>), rgrid, dim3(256), 0, st, a,    \
-                                ep, nslice);                                                      \
+        if (bf16) hipLaunchKernelGGL((tp_read_stored_kernel<NR_, true, ST>), rgrid, dim3(256), 0, \
+                                     st, a, ep, nslice);                                          \
+        else hipLaunchKernelGGL((tp_read_stored_kernel<NR_, false, ST>), rgrid, dim3(256), 0, st, \
+                                a, ep, nslice);                                                   \
     } else
             SDM_TP_READ(1) SDM_TP_READ(2) SDM_TP_READ(4) SDM_TP_READ(8) SDM_TP_READ(16) {
-                return hipErrorInvalidValue;
+                if constexpr (kLPR >= 32) {
+                    SDM_TP_READ(32) { return hipErrorInvalidValue; }
+                } else {
+                    return hipErrorInvalidValue;
+                }
             }
 #undef SDM_TP_READ
         } else {
@@ -880,10 +966,10 @@ static hipError_t tp_apply_state(const Shape &s, TPArgs a, bool bf16, hipStream_
         const int nblk = (ne * s.W + kRPI * SPG - 1) / (kRPI * SPG);
         const dim3 ugrid = chain_grid(a.chains, (int64_t)nblk * nslice);
         if (bf16)
-            hipLaunchKernelGGL((tp_update_kernel<true, SPG, SB>), ugrid, dim3(256), 0, st, a, ep,
+            hipLaunchKernelGGL((tp_update_kernel<true, SPG, ST>), ugrid, dim3(256), 0, st, a, ep,
                                nslice, nblk, true);
         else
-            hipLaunchKernelGGL((tp_update_kernel<false, SPG, SB>), ugrid, dim3(256), 0, st, a, ep,
+            hipLaunchKernelGGL((tp_update_kernel<false, SPG, ST>), ugrid, dim3(256), 0, st, a, ep,
                                nslice, nblk, true);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -902,7 +988,7 @@ hipError_t launch_tp_forward_tape(const Shape &s, const uint32_t *rec, void *ws,
     if (ep1 < 0 || ep1 > a.nepoch) ep1 = a.nepoch;
     // 8 events per row group, as in the forward (backward step 32.43 -> 32.11 ms
     // against 4 at the 1.4B-style layer)
-    constexpr int kLPR = StateRow<false>::kLPR, kRPI = 64 / kLPR, SPG = 8;
+    constexpr int kLPR = StateRow<kStateF32>::kLPR, kRPI = 64 / kLPR, SPG = 8;
     const int nslice = (s.d_v + 4 * kLPR - 1) / (4 * kLPR);
     for (int ep = ep0; ep < ep1; ep++) {
         const int64_t t0 = (int64_t)ep * a.E;
@@ -912,18 +998,18 @@ hipError_t launch_tp_forward_tape(const Shape &s, const uint32_t *rec, void *ws,
         const bool rev = ep & 1;  // each launch starts on the chains the previous one ended on
         if (tape) {
             if (bf16)
-                hipLaunchKernelGGL((tp_update_kernel<true, SPG, false, true>), ugrid, dim3(256), 0,
-                                   st, a, ep, nslice, nblk, rev);
+                hipLaunchKernelGGL((tp_update_kernel<true, SPG, kStateF32, true>), ugrid, dim3(256),
+                                   0, st, a, ep, nslice, nblk, rev);
             else
-                hipLaunchKernelGGL((tp_update_kernel<false, SPG, false, true>), ugrid, dim3(256), 0,
-                                   st, a, ep, nslice, nblk, rev);
+                hipLaunchKernelGGL((tp_update_kernel<false, SPG, kStateF32, true>), ugrid, dim3(256),
+                                   0, st, a, ep, nslice, nblk, rev);
         } else {  // state only (the checkpoint pass)
             if (bf16)
-                hipLaunchKernelGGL((tp_update_kernel<true, SPG, false>), ugrid, dim3(256), 0, st, a,
-                                   ep, nslice, nblk, rev);
+                hipLaunchKernelGGL((tp_update_kernel<true, SPG, kStateF32>), ugrid, dim3(256), 0, st,
+                                   a, ep, nslice, nblk, rev);
             else
-                hipLaunchKernelGGL((tp_update_kernel<false, SPG, false>), ugrid, dim3(256), 0, st, a,
-                                   ep, nslice, nblk, rev);
+                hipLaunchKernelGGL((tp_update_kernel<false, SPG, kStateF32>), ugrid, dim3(256), 0, st,
+                                   a, ep, nslice, nblk, rev);
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -944,13 +1030,18 @@ hipError_t launch_tp_sort_merged(const Shape &s, const uint32_t *rec, void *ws, 
 }
 
 hipError_t launch_tp_apply(const Shape &s, const uint32_t *rec, void *ws, const void *v,
-                           bool bf16, float *y, void *M, bool state_bf16, hipStream_t st, int ep0,
+                           bool bf16, float *y, void *M, StateFmt fmt, hipStream_t st, int ep0,
                            int ep1)
 {
     TPArgs a = tp_args(s, rec, ws, v, y, M);
+    a.ssc = ldexpf(1.0f, fmt.scale_log2);
+    a.sisc = ldexpf(1.0f, -fmt.scale_log2);
     if (ep1 < 0 || ep1 > a.nepoch) ep1 = a.nepoch;
-    return state_bf16 ? tp_apply_state<true>(s, a, bf16, st, ep0, ep1)
-                      : tp_apply_state<false>(s, a, bf16, st, ep0, ep1);
+    switch (fmt.type) {
+        case kStateBF16: return tp_apply_state<kStateBF16>(s, a, bf16, st, ep0, ep1);
+        case kStateFP8: return tp_apply_state<kStateFP8>(s, a, bf16, st, ep0, ep1);
+        default: return tp_apply_state<kStateF32>(s, a, bf16, st, ep0, ep1);
+    }
 }
 
 }  // namespace sdm

@@ -22,7 +22,7 @@ static __device__ __align__(256) unsigned char scratch[SDM_NOALLOC_MAX_BYTES];
 struct sdm_ctx {
     const float *M0 = nullptr;
     int H = 0, sqrtN = 0, d_v = 0, W = 0, R = 0;
-    bool state_bf16 = false;  // M holds bfloat16 values
+    sdm::StateFmt state;  // element type of M (and the E4M3 scale)
 };
 
 namespace {
@@ -108,9 +108,9 @@ sdm_status check_variant(const sdm_ctx *h, int B, int64_t T, sdm_variant variant
     const sdm_variant var = resolve_variant(h, B, T, variant);
     if (var != SDM_VARIANT_SERIAL && var != SDM_VARIANT_TIMEPAR)
         return fail(SDM_ERR_ARG, "unknown variant %d", (int)variant);
-    if (h->state_bf16 && var == SDM_VARIANT_SERIAL)
+    if (h->state.type != sdm::kStateF32 && var == SDM_VARIANT_SERIAL)
         return fail(SDM_ERR_UNSUPPORTED,
-                    "a bfloat16 state needs the time-parallel schedule (d_v %% 4 == 0)");
+                    "a bfloat16 or E4M3 state needs the time-parallel schedule (d_v %% 4 == 0)");
     if (var == SDM_VARIANT_TIMEPAR && !sdm::tp_supported(shape_of(h, B, T)))
         return fail(SDM_ERR_UNSUPPORTED,
                     "time-parallel schedule needs d_v %% 4 == 0 and N*d_v*4 <= 2^31");
@@ -151,7 +151,7 @@ int bwd_chunks_for(const sdm_ctx *h, int B, int64_t T, size_t ws_bytes)
 
 sdm_status check_backward(const sdm_ctx *h, int B, int64_t T)
 {
-    if (h->state_bf16)
+    if (h->state.type != sdm::kStateF32)
         return fail(SDM_ERR_UNSUPPORTED, "the backward needs a float32 state");
     if (!sdm::tp_supported(shape_of(h, B, T)))
         return fail(SDM_ERR_UNSUPPORTED,
@@ -228,6 +228,8 @@ sdm_status sdm_create_ex(const float *M0, int H, int sqrtN, int d_v, int W, int 
         return fail(SDM_ERR_UNSUPPORTED, "sqrtN > %d is not supported", sdm::kMaxSqrtN);
     if (W > sdm::kMaxK || R > sdm::kMaxK)
         return fail(SDM_ERR_UNSUPPORTED, "W, R > %d are not supported", sdm::kMaxK);
+    if (state_dtype == SDM_FP8_E4M3)
+        return fail(SDM_ERR_ARG, "an E4M3 state takes a scale: create it with sdm_create_fp8");
     if (state_dtype != SDM_F32 && state_dtype != SDM_BF16)
         return fail(SDM_ERR_ARG, "state dtype must be SDM_F32 or SDM_BF16 (got %d)",
                     (int)state_dtype);
@@ -239,7 +241,7 @@ sdm_status sdm_create_ex(const float *M0, int H, int sqrtN, int d_v, int W, int 
     h->d_v = d_v;
     h->W = W;
     h->R = R;
-    h->state_bf16 = state_dtype == SDM_BF16;
+    h->state.type = state_dtype == SDM_BF16 ? sdm::kStateBF16 : sdm::kStateF32;
     *out = h;
     return SDM_OK;
 }
@@ -247,6 +249,19 @@ sdm_status sdm_create_ex(const float *M0, int H, int sqrtN, int d_v, int W, int 
 sdm_status sdm_create(const float *M0, int H, int sqrtN, int d_v, int W, int R, sdm_handle *out)
 {
     return sdm_create_ex(M0, H, sqrtN, d_v, W, R, SDM_F32, out);
+}
+
+sdm_status sdm_create_fp8(const float *M0, int H, int sqrtN, int d_v, int W, int R,
+                          int scale_log2, sdm_handle *out)
+{
+    if (out) *out = nullptr;
+    if (scale_log2 < -64 || scale_log2 > 64)
+        return fail(SDM_ERR_ARG, "scale_log2 must be in [-64, 64] (got %d)", scale_log2);
+    sdm_status st = sdm_create_ex(M0, H, sqrtN, d_v, W, R, SDM_F32, out);
+    if (st != SDM_OK) return st;
+    (*out)->state.type = sdm::kStateFP8;
+    (*out)->state.scale_log2 = scale_log2;
+    return SDM_OK;
 }
 
 sdm_status sdm_destroy(sdm_handle h)
@@ -326,19 +341,21 @@ sdm_status sdm_prepare(sdm_handle h, int B, int64_t T, const void *kp, const voi
     // M <- M_0, inside the selection launch where its items cover M_0 (the
     // copy then runs under the selection's arithmetic), else on its own
     const bool init = !(flags & SDM_FLAG_CONTINUE);
-    const bool fused_init = init && sdm::select_can_init(s);
+    const bool fused_init =
+        init && h->state.type != sdm::kStateFP8 && sdm::select_can_init(s);
     if (init && !fused_init) {
-        e = sdm::launch_init(s, h->M0, M, h->state_bf16, hs);
+        e = sdm::launch_init(s, h->M0, M, h->state, hs);
         if (e != hipSuccess) return hip_fail(e, "init launch");
     }
-    const sdm::SelInit si{h->M0, M, h->state_bf16};
+    const sdm::SelInit si{h->M0, M, h->state.type == sdm::kStateBF16};
     e = sdm::launch_select(s, kp, qp, dtype == SDM_BF16, nullptr, nullptr, nullptr, nullptr, rec,
                            alpha, beta, hs, nullptr, 0, -1, fused_init ? &si : nullptr);
     if (e != hipSuccess) return hip_fail(e, "select launch");
     if (var == SDM_VARIANT_TIMEPAR) {
         if (!sdm::decode_supported(s)) {  // one token: nothing to sort (see sdm_apply)
             char *tp = static_cast<char *>(workspace) + records_bytes(h, B, T);
-            e = sdm::launch_tp_prepare(s, rec, tp, hs, 0, -1, true, h->state_bf16);
+            e = sdm::launch_tp_prepare(s, rec, tp, hs, 0, -1, true,
+                                       h->state.type != sdm::kStateF32);
             if (e != hipSuccess) return hip_fail(e, "time-parallel sort launch");
         }
     } else if (sdm::rw_serial_supported(s)) {
@@ -367,14 +384,14 @@ sdm_status sdm_apply(sdm_handle h, int B, int64_t T, const void *v, sdm_dtype dt
     if (var == SDM_VARIANT_TIMEPAR && sdm::decode_supported(s)) {
         // one token per sequence: its writes, then its reads, in one kernel
         const hipError_t e =
-            sdm::launch_rw_decode(s, rec, v, dtype == SDM_BF16, y, M, h->state_bf16, hs);
+            sdm::launch_rw_decode(s, rec, v, dtype == SDM_BF16, y, M, h->state, hs);
         if (e != hipSuccess) return hip_fail(e, "one-token write/read launch");
         return SDM_OK;
     }
     if (var == SDM_VARIANT_TIMEPAR) {
         char *tp = static_cast<char *>(workspace) + records_bytes(h, B, T);
         const hipError_t e =
-            sdm::launch_tp_apply(s, rec, tp, v, dtype == SDM_BF16, y, M, h->state_bf16, hs);
+            sdm::launch_tp_apply(s, rec, tp, v, dtype == SDM_BF16, y, M, h->state, hs);
         if (e != hipSuccess) return hip_fail(e, "time-parallel write/read launch");
         return SDM_OK;
     }

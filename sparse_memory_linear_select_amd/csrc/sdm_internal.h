@@ -49,11 +49,50 @@ struct TPEntry {
     float a, c;
 };
 
+// Element type of the state M.  float32; bfloat16; or 8-bit OCP FP8 E4M3
+// codes scaled by a power of two 2^s (a code c holds the value c * 2^s).
+enum StateType : int { kStateF32 = 0, kStateBF16 = 1, kStateFP8 = 2 };
+struct StateFmt {
+    int type = kStateF32;
+    int scale_log2 = 0;  // s (E4M3 state only)
+};
+
 // Nearest bfloat16 (ties to even) of a finite float, as its 16 bits.
 __device__ __forceinline__ uint32_t bf16_bits(float f)
 {
     const uint32_t u = __float_as_uint(f);
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Nearest E4M3 code of a finite float a (sign, 4 exponent bits with bias 7,
+// 3 mantissa bits; normal values (1 + m/8) 2^(e-7), subnormals m 2^-9):
+// rounded to nearest, ties to even, magnitudes from 448 up saturated to 448
+// (the format has no infinities).
+__device__ __forceinline__ uint32_t e4m3_code(float a)
+{
+    const uint32_t u = __float_as_uint(a);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t m = u & 0x7FFFFFFFu;
+    uint32_t c;
+    if (m >= 0x43E00000u) {  // |a| >= 448
+        c = 0x7Eu;
+    } else if (m >= 0x3C800000u) {  // |a| >= 2^-6: keep 3 of float32's 23 mantissa bits
+        const uint32_t r = m + 0x7FFFFu + ((m >> 20) & 1u);  // a carry moves the exponent up
+        c = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);      // exponent bias 127 -> 7
+        c = c > 0x7Eu ? 0x7Eu : c;
+    } else {  // a multiple of 2^-9; 8 * 2^-9 is the smallest normal, code 0x08
+        c = (uint32_t)__builtin_rintf(__uint_as_float(m) * 512.0f);
+    }
+    return sign | c;
+}
+
+// Value of an E4M3 code (exact in float32).
+__device__ __forceinline__ float e4m3_value(uint32_t c)
+{
+    const uint32_t sign = (c & 0x80u) << 24;
+    const uint32_t em = c & 0x7Fu;
+    if (em >= 8u) return __uint_as_float(sign | ((em + 960u) << 20));  // exponent + 120
+    return __uint_as_float(sign | __float_as_uint((float)em * 0.001953125f));
 }
 
 struct Shape {
@@ -75,7 +114,7 @@ struct Shape {
 struct SelInit {
     const float *M0;
     void *M;
-    bool state_bf16;
+    bool state_bf16;  // else float32 (the selection does not carry an E4M3 copy)
 };
 bool select_can_init(const Shape &s);
 
@@ -89,8 +128,8 @@ hipError_t launch_select(const Shape &s, const void *kp, const void *qp, bool bf
                          int64_t tn = -1,  // tokens [t0, t0 + tn) of every sequence
                          const SelInit *init = nullptr);
 
-// M[b] <- M0 for every sequence b.
-hipError_t launch_init(const Shape &s, const float *M0, void *M, bool state_bf16, hipStream_t st);
+// M[b] <- M0 for every sequence b, in the state's element type.
+hipError_t launch_init(const Shape &s, const float *M0, void *M, StateFmt fmt, hipStream_t st);
 
 // Adds forwarding codes (distance < depth) to the slot words of all records.
 hipError_t launch_plan(const Shape &s, uint32_t *rec, int depth, hipStream_t st);
@@ -110,21 +149,21 @@ hipError_t launch_rw_simple(const Shape &s, const uint32_t *rec, const void *v, 
 bool tp_supported(const Shape &s);
 int tp_epoch_len(const Shape &s);
 size_t tp_workspace_bytes(const Shape &s);  // beyond the token records
-// Epochs [ep0, ep1) (ep1 < 0: through the last epoch).  With state_bf16
-// the read plan is the one of stored-value reads (rows rounded after every
-// write): weights q and links to each read's in-epoch writes.
+// Epochs [ep0, ep1) (ep1 < 0: through the last epoch).  With `stored` (a
+// bfloat16 or E4M3 state) the read plan is the one of stored-value reads
+// (rows rounded after every write): weights q and each read's in-epoch
+// writes.
 hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipStream_t st,
-                             int ep0 = 0, int ep1 = -1, bool link = true,
-                             bool state_bf16 = false);
+                             int ep0 = 0, int ep1 = -1, bool link = true, bool stored = false);
 hipError_t launch_tp_apply(const Shape &s, const uint32_t *rec, void *ws, const void *v,
-                           bool bf16, float *y, void *M, bool state_bf16, hipStream_t st,
+                           bool bf16, float *y, void *M, StateFmt fmt, hipStream_t st,
                            int ep0 = 0, int ep1 = -1);
 
 // One-token step (T == 1): the token's writes, then its reads, in one kernel
 // (d_v % 4 == 0 and one chain's state within 2^31 bytes).
 bool decode_supported(const Shape &s);
 hipError_t launch_rw_decode(const Shape &s, const uint32_t *rec, const void *v, bool bf16,
-                            float *y, void *M, bool state_bf16, hipStream_t st);
+                            float *y, void *M, StateFmt fmt, hipStream_t st);
 
 // Backward (float32 state): a forward write pass over epochs [ep0, ep1) that
 // records each written slot's epoch-start row in the tape ([chain][tapeT][W]

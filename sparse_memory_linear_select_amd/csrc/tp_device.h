@@ -38,56 +38,100 @@ __device__ __forceinline__ float4 fma4(float a, float4 x, float c, float4 v)
 }
 
 // Row storage of the state.  Every lane holds 4 columns of a row; a row
-// slice is the 128 bytes that LPR lanes cover (the fabric's request size).
+// slice is the 128 bytes that kLPR lanes cover (the fabric's request size).
 //   float32 state: 8 lanes x 16 bytes;
 //   bfloat16 state: 16 lanes x 8 bytes, widened exactly on load, rounded to
-//   nearest-even after every write (the value the state holds).
-template <bool SB>
+//   nearest-even after every write (the value the state holds);
+//   E4M3 state: 32 lanes x 4 bytes, codes of the values scaled by 2^-s,
+//   decoded exactly and scaled by 2^s on load, encoded (nearest-even,
+//   saturating) after every write.
+// An object carries the scale (sc = 2^s, isc = 2^-s; unused by the other
+// types): `const S st(sc, isc);` then st.load(...), st.store(...).
+template <int ST>
 struct StateRow;
 
 template <>
-struct StateRow<false> {
+struct StateRow<kStateF32> {
     static constexpr int kLPR = 8;
     static constexpr uint32_t kElem = 4;
     using Raw = float4;
-    static __device__ __forceinline__ Raw load_raw(rsrc_t r, uint32_t off) { return buf_load4(r, off); }
-    static __device__ __forceinline__ float4 widen(Raw x) { return x; }
-    static __device__ __forceinline__ float4 load(rsrc_t r, uint32_t off) { return buf_load4(r, off); }
-    static __device__ __forceinline__ void store(float4 v, rsrc_t r, uint32_t off)
+    __device__ StateRow(float, float) {}
+    __device__ __forceinline__ Raw load_raw(rsrc_t r, uint32_t off) const { return buf_load4(r, off); }
+    __device__ __forceinline__ float4 widen(Raw x) const { return x; }
+    __device__ __forceinline__ float4 load(rsrc_t r, uint32_t off) const { return buf_load4(r, off); }
+    __device__ __forceinline__ void store(float4 v, rsrc_t r, uint32_t off) const
     {
         buf_store4(v, r, off);
     }
-    static __device__ __forceinline__ float4 round(float4 v) { return v; }
+    __device__ __forceinline__ float4 round(float4 v) const { return v; }
+    __device__ __forceinline__ Raw pack(float4 v) const { return v; }
 };
 
 template <>
-struct StateRow<true> {
+struct StateRow<kStateBF16> {
     static constexpr int kLPR = 16;
     static constexpr uint32_t kElem = 2;
     using Raw = uint2;  // 4 bfloat16 values
-    static __device__ __forceinline__ Raw load_raw(rsrc_t r, uint32_t off)
+    __device__ StateRow(float, float) {}
+    __device__ __forceinline__ Raw load_raw(rsrc_t r, uint32_t off) const
     {
         const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
         return make_uint2(u[0], u[1]);
     }
-    static __device__ __forceinline__ float4 widen(Raw u)
+    __device__ __forceinline__ float4 widen(Raw u) const
     {
         return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
                            __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
     }
-    static __device__ __forceinline__ float4 load(rsrc_t r, uint32_t off) { return widen(load_raw(r, off)); }
-    static __device__ __forceinline__ void store(float4 v, rsrc_t r, uint32_t off)
+    __device__ __forceinline__ float4 load(rsrc_t r, uint32_t off) const { return widen(load_raw(r, off)); }
+    // the 4 values rounded to bfloat16, packed
+    __device__ __forceinline__ Raw pack(float4 v) const
     {
+        return make_uint2(bf16_bits(v.x) | (bf16_bits(v.y) << 16),
+                          bf16_bits(v.z) | (bf16_bits(v.w) << 16));
+    }
+    __device__ __forceinline__ void store(float4 v, rsrc_t r, uint32_t off) const
+    {
+        const uint2 p = pack(v);
         __attribute__((ext_vector_type(2))) unsigned u;
-        u[0] = bf16_bits(v.x) | (bf16_bits(v.y) << 16);
-        u[1] = bf16_bits(v.z) | (bf16_bits(v.w) << 16);
+        u[0] = p.x;
+        u[1] = p.y;
         __builtin_amdgcn_raw_buffer_store_b64(u, r, (int)off, 0, 0);
     }
-    static __device__ __forceinline__ float4 round(float4 v)
+    __device__ __forceinline__ float4 round(float4 v) const
     {
         return make_float4(__uint_as_float(bf16_bits(v.x) << 16), __uint_as_float(bf16_bits(v.y) << 16),
                            __uint_as_float(bf16_bits(v.z) << 16), __uint_as_float(bf16_bits(v.w) << 16));
     }
+};
+
+template <>
+struct StateRow<kStateFP8> {
+    static constexpr int kLPR = 32;
+    static constexpr uint32_t kElem = 1;
+    using Raw = uint32_t;  // 4 E4M3 codes, column k in byte k
+    float sc, isc;
+    __device__ StateRow(float sc_, float isc_) : sc(sc_), isc(isc_) {}
+    __device__ __forceinline__ Raw load_raw(rsrc_t r, uint32_t off) const
+    {
+        return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+    }
+    __device__ __forceinline__ float4 widen(Raw u) const
+    {
+        return make_float4(e4m3_value(u & 0xFFu) * sc, e4m3_value((u >> 8) & 0xFFu) * sc,
+                           e4m3_value((u >> 16) & 0xFFu) * sc, e4m3_value(u >> 24) * sc);
+    }
+    __device__ __forceinline__ float4 load(rsrc_t r, uint32_t off) const { return widen(load_raw(r, off)); }
+    __device__ __forceinline__ Raw pack(float4 v) const
+    {
+        return e4m3_code(v.x * isc) | (e4m3_code(v.y * isc) << 8) | (e4m3_code(v.z * isc) << 16) |
+               (e4m3_code(v.w * isc) << 24);
+    }
+    __device__ __forceinline__ void store(float4 v, rsrc_t r, uint32_t off) const
+    {
+        __builtin_amdgcn_raw_buffer_store_b32(pack(v), r, (int)off, 0, 0);
+    }
+    __device__ __forceinline__ float4 round(float4 v) const { return widen(pack(v)); }
 };
 
 template <bool BF16>
@@ -110,7 +154,7 @@ __device__ __forceinline__ float4 load_v(const void *v, int64_t off)
 template <int LPR>
 __device__ __forceinline__ uint32_t group_bcast(uint32_t x, int i)
 {
-    static_assert(LPR == 8 || LPR == 16, "row groups of 8 or 16 lanes");
+    static_assert(LPR == 8 || LPR == 16 || LPR == 32, "row groups of 8, 16 or 32 lanes");
     constexpr int kAnd = 0x1F & ~(LPR - 1);
     const int v = (int)x;
     switch (i) {
@@ -118,10 +162,18 @@ __device__ __forceinline__ uint32_t group_bcast(uint32_t x, int i)
     case I: return (uint32_t)__builtin_amdgcn_ds_swizzle(v, kAnd | ((I) << 5));
         SDM_SWZ(0) SDM_SWZ(1) SDM_SWZ(2) SDM_SWZ(3) SDM_SWZ(4) SDM_SWZ(5) SDM_SWZ(6) SDM_SWZ(7)
         SDM_SWZ(8) SDM_SWZ(9) SDM_SWZ(10) SDM_SWZ(11) SDM_SWZ(12) SDM_SWZ(13) SDM_SWZ(14)
-        SDM_SWZ(15)
+        SDM_SWZ(15) SDM_SWZ(16) SDM_SWZ(17) SDM_SWZ(18) SDM_SWZ(19) SDM_SWZ(20) SDM_SWZ(21)
+        SDM_SWZ(22) SDM_SWZ(23) SDM_SWZ(24) SDM_SWZ(25) SDM_SWZ(26) SDM_SWZ(27) SDM_SWZ(28)
+        SDM_SWZ(29) SDM_SWZ(30) SDM_SWZ(31)
 #undef SDM_SWZ
     }
     return 0u;
+}
+
+// Value of x in lane `src` (any lane of the wave; src is a per-lane value).
+__device__ __forceinline__ uint32_t lane_read(uint32_t x, int src)
+{
+    return (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)x);
 }
 
 template <int K, typename T>

@@ -22,6 +22,9 @@ WTOL = 1e-5      # absolute bound on the softmax weights (diagnostic)
 # Everywhere else both hold the same bits, which the bfloat16 tests check
 # through the fraction of elements within TOL.
 TOL_BF16 = 2.0 ** -7
+# E4M3 state: the same outer bound at 2^-2, two E4M3 spacings (3 mantissa
+# bits) at |ref| ~ 1, for the same reason.
+TOL_FP8 = 2.0 ** -2
 
 
 def log(*a):
@@ -39,13 +42,17 @@ def upload(d: dict) -> dict:
     return {k: to_dev(v) for k, v in d.items() if k != "src"}
 
 
-def make_core(dd: dict, W: int, R: int, state=torch.float32) -> sdm.SDM:
-    return sdm.SDM(dd["M0"], W, R, state=state)
+FP8_SCALE_LOG2 = -4  # E4M3 state scale used by the tests: codes of M * 2^4
 
 
-def gpu_forward(d: dict, W: int, R: int, variant=sdm.AUTO, state=torch.float32):
+def make_core(dd: dict, W: int, R: int, state=torch.float32, scale_log2=FP8_SCALE_LOG2) -> sdm.SDM:
+    return sdm.SDM(dd["M0"], W, R, state=state, state_scale_log2=scale_log2)
+
+
+def gpu_forward(d: dict, W: int, R: int, variant=sdm.AUTO, state=torch.float32,
+                scale_log2=FP8_SCALE_LOG2):
     dd = upload(d)
-    core = make_core(dd, W, R, state)
+    core = make_core(dd, W, R, state, scale_log2)
     y, M = core.forward(dd["kp"], dd["qp"], dd["v"], dd["alpha"], dd["beta"], variant=variant)
     torch.cuda.synchronize()
     return core, dd, y, M
@@ -83,9 +90,10 @@ class Timer:
         log(f"  [{self.name}: {time.time() - self.t:.1f}s]")
 
 
-def check_bf16_state(y, M, ref_y, ref_M, what=""):
-    """GPU (bfloat16 state) vs the oracle's bfloat16-state mode.  Outer bound:
-    every element of y and M within TOL_BF16 * (1 + |ref|).  Inner bounds,
+def check_bf16_state(y, M, ref_y, ref_M, what="", outer=TOL_BF16):
+    """GPU (bfloat16 or E4M3 state; M as values) vs the oracle's mode for the
+    same state.  Outer bound: every element of y and M within
+    outer * (1 + |ref|) (TOL_BF16, or TOL_FP8 for E4M3).  Inner bounds,
     which only reads of the stored, rounded rows meet: >= 99.99% of y within
     TOL * (1 + |ref|) and >= 99.9% of M equal to the oracle's bits (reading
     the unrounded composition of a slot's writes instead misses a rounding by
@@ -97,8 +105,8 @@ def check_bf16_state(y, M, ref_y, ref_M, what=""):
     fy = float((np.abs(yg - ref_y) <= TOL * (1.0 + np.abs(ref_y))).mean()) if yg.size else 1.0
     same = float((Mg == ref_M).mean()) if Mg.size else 1.0
     log(f"  {what}y within {TOL:.0e}: {fy:.6f}; M equal to the oracle's bits: {same:.6f}")
-    ey = assert_close(yg, ref_y, TOL_BF16, "y")
-    eM = assert_close(Mg, ref_M, TOL_BF16, "M")
+    ey = assert_close(yg, ref_y, outer, "y")
+    eM = assert_close(Mg, ref_M, outer, "M")
     log(f"  {what}max rel err y {ey:.2e}  M {eM:.2e}")
     assert fy >= 0.9999, f"y: only {fy:.6f} of the elements within {TOL:.0e} * (1 + |ref|)"
     assert same >= 0.999, f"M: only {same:.6f} of the elements equal the oracle's"

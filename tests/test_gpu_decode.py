@@ -8,7 +8,8 @@ import torch
 import oracle
 import sdm_inputs as si
 import sparse_memory_linear_select_amd as sdm
-from gpu_util import TOL, assert_close, check_bf16_state, log, make_core, upload
+from gpu_util import (FP8_SCALE_LOG2, TOL, TOL_BF16, TOL_FP8, assert_close, check_bf16_state, log,
+                      make_core, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -51,6 +52,9 @@ SHAPES = [
     (2, 2, 32, 64, 32, 32, "f32", "bf16", 6, 5),   # bfloat16 state
     (1, 1, 16, 100, 16, 4, "bf16", "bf16", 2, 4),  # bfloat16 state, ragged 64-column slice
     (2, 1, 64, 128, 64, 64, "f32", "bf16", 3, 3),  # bfloat16 state, W = R = 64 (16 rows per group)
+    (2, 2, 32, 64, 32, 32, "f32", "fp8", 6, 5),    # E4M3 state
+    (1, 1, 16, 100, 16, 4, "bf16", "fp8", 2, 4),   # E4M3 state, ragged 64-column slice
+    (2, 1, 64, 160, 64, 64, "f32", "fp8", 3, 3),   # E4M3 state, W = R = 64, 3 slices
 ]
 
 
@@ -64,11 +68,12 @@ def test_decode_matches_oracle(shape):
         f"prefill={prefill} steps={steps}")
     d = si.generate(wl)
     dd = upload(d)
-    state = torch.bfloat16 if st == "bf16" else torch.float32
-    _, y, M = _decode_run(d, dd, W, R, prefill, state)
-    ref = oracle.forward(d, S, W, R, state=st)
-    if st == "bf16":
-        check_bf16_state(y.double().cpu().numpy(), M.double().cpu().numpy(), ref["y"], ref["M"])
+    state = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[st]
+    core, y, M = _decode_run(d, dd, W, R, prefill, state)
+    ref = oracle.forward(d, S, W, R, state=st, scale_log2=FP8_SCALE_LOG2)
+    if st != "f32":
+        check_bf16_state(y.double().cpu().numpy(), core.state_values(M).double().cpu().numpy(),
+                         ref["y"], ref["M"], outer=TOL_FP8 if st == "fp8" else TOL_BF16)
         return
     ey = assert_close(y.cpu().numpy(), ref["y"], TOL, "y")
     eM = assert_close(M.float().cpu().numpy(), ref["M"], TOL, "M")
