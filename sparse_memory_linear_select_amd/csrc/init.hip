@@ -64,8 +64,7 @@ __global__ __launch_bounds__(256) void init_kernel_fp8(const float *__restrict__
     const float4 *src = reinterpret_cast<const float4 *>(M0);
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
         const float4 x = src[i];
-        const uint32_t u = e4m3_code(x.x * isc) | (e4m3_code(x.y * isc) << 8) |
-                           (e4m3_code(x.z * isc) << 16) | (e4m3_code(x.w * isc) << 24);
+        const uint32_t u = e4m3_pack4(x.x * isc, x.y * isc, x.z * isc, x.w * isc);
         for (int b = 0; b < B; b++) M[(int64_t)b * n4 + i] = u;
     }
 }

@@ -460,160 +460,139 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int nsli
 // them on the epoch-start row with the update kernel's own operations,
 // st.round(a*row + c*v) in time order.
 //
-// One wavefront per (chain, token of the epoch, 128-byte row slice); row
-// group g (kLPR lanes) takes reads g*NR .. g*NR + NR-1, and lane q of the
-// group holds the plan of read g*NR + q: slot word, weight q, link (first
-// write, count) and the first two writes' token, a and c.  The epoch-start
-// rows of the reads that see no in-epoch write are gathered at once.  The
-// others are taken kD at a time per group (lowest index first): their rows
-// and the v slices of their first two writes depend only on the plan and
-// are gathered together; a third or later write comes from the sorted
-// events, one round trip for all kD reads per write.  Each replayed row
-// (exactly a stored value) goes back into the group's row registers, so y
-// sums the R rows in read order whichever reads saw in-epoch writes: y does
-// not depend on where epochs start.
-constexpr int kReplayBatch = 4;  // replayed reads per row group in flight
+// The R reads of a (chain, token of the epoch, 128-byte row slice) unit are
+// split over kWPU wavefronts (a power of two dividing 4, so a unit's waves
+// share a workgroup), 8 reads per row group: lane q < 8 of a group holds
+// read q's plan -- slot word, weight q, link (first write, count) and the
+// first two in-epoch writes' token, a and c.  Every gather that depends only
+// on the plan -- the epoch-start rows and the v slices of the first two
+// writes -- is issued at once; a third or later write comes from the sorted
+// events, one round trip for all of the wave's reads per write.  Each wave
+// sums its reads in read order, and the unit's first wave adds the partial
+// sums of the others in wave order (LDS), so y sums the R rows in one fixed
+// order whichever reads saw in-epoch writes: it does not depend on where
+// epochs start.
+constexpr int kStoredNR = 8;  // reads per row group
 
-template <int NR, bool BF16, int ST>
+template <int ST>
+constexpr int stored_waves_per_unit(int R)
+{
+    const int per_wave = kStoredNR * (64 / StateRow<ST>::kLPR);
+    const int w = (R + per_wave - 1) / per_wave;
+    return w <= 1 ? 1 : (w <= 2 ? 2 : 4);
+}
+
+template <bool BF16, int ST, int WPU>
 __global__ __launch_bounds__(256) void tp_read_stored_kernel(TPArgs a, int ep, int nslice)
 {
     using S = StateRow<ST>;
-    constexpr int kLPR = S::kLPR, kD = kReplayBatch;
-    static_assert(NR <= kLPR, "one read per lane of a row group");
+    constexpr int kLPR = S::kLPR, kRPI = 64 / kLPR, NR = kStoredNR;
+    static_assert(NR <= kLPR && 4 % WPU == 0, "one read per lane; a unit's waves in a workgroup");
+    __shared__ float4 part[4][kLPR];  // partial sums of the waves (column quads of the slice)
     const S st(a.ssc, a.sisc);
     const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t chain = grid_chain();
     const int64_t t0 = (int64_t)ep * a.E;
     const int ne = (int)((a.T - t0) < a.E ? (a.T - t0) : a.E);
-    const uint32_t u = blockIdx.x * 4u + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (chain >= a.chains || u >= (uint32_t)(ne * nslice)) return;
+    const uint32_t wid = blockIdx.x * 4u + (uint32_t)wv;  // wave of this chain
+    const uint32_t u = wid / WPU;                          // its unit
+    const int w = (int)(wid % WPU);                        // its part of the unit's reads
+    const bool active = chain < a.chains && u < (uint32_t)(ne * nslice);  // wave-uniform
     const int slice = (int)(u % (uint32_t)nslice);
-    const int tl = (int)(u / (uint32_t)nslice);
+    const int tl = active ? (int)(u / (uint32_t)nslice) : 0;
     const int64_t t = t0 + tl;
-    const int64_t ct = chain * a.T + t;
+    const int64_t ct = (active ? chain : 0) * a.T + t;
     const int g = lane / kLPR, q = lane % kLPR;
     const int col = slice * 4 * kLPR + q * 4;
-    const bool col_ok = col < a.d_v;
+    const bool col_ok = active & (col < a.d_v);
     const int colc = col_ok ? col : 0;
     // chains < 2^32 (the grid's y and z), so 32-bit division
     const int64_t b = (uint32_t)chain / (uint32_t)a.H;
     const int h = (int)(chain - b * a.H);
     const int64_t hd = (int64_t)a.H * a.d_v;
     const int64_t vrow0 = (b * a.T * a.H + h) * a.d_v + colc;  // v of token 0 of the chain
-    const rsrc_t Mr = make_rsrc(static_cast<char *>(a.M) + chain * a.N * a.d_v * S::kElem,
+    const rsrc_t Mr = make_rsrc(static_cast<char *>(a.M) + (active ? chain : 0) * a.N * a.d_v * S::kElem,
                                 (uint32_t)(a.N * a.d_v * S::kElem));
     const uint32_t rowb = (uint32_t)a.d_v * S::kElem;
     const uint32_t *rc = a.rec + ct * a.rec_dwords;
-    const TPEntry *se = a.sorted + chain * a.T * a.W + t0 * a.W;
+    const TPEntry *se = a.sorted + (active ? chain : 0) * a.T * a.W + t0 * a.W;
     const uint32_t *fw = reinterpret_cast<const uint32_t *>(a.pairs + ct * a.P);
 
-    const int r = g * NR + q;
-    const bool mine = (q < NR) & (r < a.R);
+    // this lane's read (lane q < NR of group g): w*kRPI*NR + g*NR + q
+    const int r0 = (w * kRPI + g) * NR;
+    const int r = r0 + q;
+    const bool mine = active & (q < NR) & (r < a.R);
     const uint32_t sl_mine = mine ? rc[3 * a.Wp + r] : 0u;
     const float wr_mine = mine ? a.rwt[ct * kMaxK + r] : 0.0f;
     const uint32_t lk_mine = mine ? a.rlink[ct * kMaxK + r] : 0u;
-    const int cnt_mine = (int)(lk_mine & ((1u << kCntBits) - 1u));
-    uint32_t w1[3] = {0u, 0u, 0u}, w2[3] = {0u, 0u, 0u};  // (token, a, c) of writes 1, 2
-    if (cnt_mine > 0) {
-        w1[0] = fw[r];
-        w1[1] = fw[a.R + r];
-        w1[2] = fw[2 * a.R + r];
-    }
-    if (cnt_mine > 1) {
-        w2[0] = fw[3 * a.R + r];
-        w2[1] = fw[4 * a.R + r];
-        w2[2] = fw[5 * a.R + r];
-    }
+    // the first two writes' fields: loaded with the rest of the plan (the
+    // token's pair area is always there; the fields are used only where the
+    // link count says the writes exist)
+    const int rr = mine ? r : 0;
+    const uint32_t t1m = fw[rr], a1m = fw[a.R + rr], c1m = fw[2 * a.R + rr];
+    const uint32_t t2m = fw[3 * a.R + rr], a2m = fw[4 * a.R + rr], c2m = fw[5 * a.R + rr];
 
-    // epoch-start rows of the reads without in-epoch writes
+    // every gather the plan decides: rows, and v of the first two writes
     typename S::Raw row[NR];
+    float4 v1[NR], v2[NR];
 #pragma unroll
     for (int i = 0; i < NR; i++) {
         const uint32_t sl = group_bcast<kLPR>(sl_mine, i);
-        const uint32_t lk = group_bcast<kLPR>(lk_mine, i);
-        const bool ok = col_ok & (g * NR + i < a.R) & (lk == 0u);
+        const bool ok = col_ok & (r0 + i < a.R);
         row[i] = st.load_raw(Mr, ok ? (sl & kSlotMask) * rowb + col * S::kElem : kOff);
     }
-
-    // the group's reads with in-epoch writes (bit i: read g*NR + i)
-    const uint64_t dirty = __ballot(lk_mine != 0u);
-    uint32_t dm = (uint32_t)(dirty >> (g * kLPR)) & (uint32_t)((1ull << NR) - 1ull);
-    while (__ballot(dm != 0u) != 0ull) {  // wave-uniform
-        int id[kD];
-        bool has[kD];
 #pragma unroll
-        for (int d = 0; d < kD; d++) {
-            has[d] = dm != 0u;
-            id[d] = has[d] ? __builtin_ctz(dm) : 0;
-            dm &= dm - 1u;
-        }
-        typename S::Raw drow[kD];
-        float4 v1[kD], v2[kD];
-        float a1[kD], c1[kD], a2[kD], c2[kD];
-        int first[kD], cnt[kD];
+    for (int i = 0; i < NR; i++) {
+        const int cnt = (int)(group_bcast<kLPR>(lk_mine, i) & ((1u << kCntBits) - 1u));
+        const uint32_t t1 = group_bcast<kLPR>(t1m, i), t2 = group_bcast<kLPR>(t2m, i);
+        v1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        v2[i] = v1[i];
+        if (cnt > 0) v1[i] = load_v<BF16>(a.v, vrow0 + (t0 + t1) * hd);
+        if (cnt > 1) v2[i] = load_v<BF16>(a.v, vrow0 + (t0 + t2) * hd);
+    }
+    float4 rv[NR];
+    int cnt[NR], first[NR];
 #pragma unroll
-        for (int d = 0; d < kD; d++) {
-            const int src = g * kLPR + id[d];  // the lane holding the read's plan
-            const uint32_t sl = lane_read(sl_mine, src);
-            const uint32_t lk = lane_read(lk_mine, src);
-            const uint32_t t1 = lane_read(w1[0], src), t2 = lane_read(w2[0], src);
-            a1[d] = __uint_as_float(lane_read(w1[1], src));
-            c1[d] = __uint_as_float(lane_read(w1[2], src));
-            a2[d] = __uint_as_float(lane_read(w2[1], src));
-            c2[d] = __uint_as_float(lane_read(w2[2], src));
-            first[d] = (int)(lk >> kCntBits);
-            cnt[d] = has[d] ? (int)(lk & ((1u << kCntBits) - 1u)) : 0;
-            drow[d] = st.load_raw(Mr, (has[d] & col_ok) ? (sl & kSlotMask) * rowb + col * S::kElem
-                                                          : kOff);
-            v1[d] = make_float4(0.f, 0.f, 0.f, 0.f);
-            v2[d] = v1[d];
-            if (cnt[d] > 0) v1[d] = load_v<BF16>(a.v, vrow0 + (t0 + t1) * hd);
-            if (cnt[d] > 1) v2[d] = load_v<BF16>(a.v, vrow0 + (t0 + t2) * hd);
-        }
-        float4 rv[kD];
+    for (int i = 0; i < NR; i++) {
+        const uint32_t lk = group_bcast<kLPR>(lk_mine, i);
+        cnt[i] = (int)(lk & ((1u << kCntBits) - 1u));
+        first[i] = (int)(lk >> kCntBits);
+        rv[i] = st.widen(row[i]);
+        if (cnt[i] > 0)
+            rv[i] = st.round(fma4(__uint_as_float(group_bcast<kLPR>(a1m, i)), rv[i],
+                                  __uint_as_float(group_bcast<kLPR>(c1m, i)), v1[i]));
+        if (cnt[i] > 1)
+            rv[i] = st.round(fma4(__uint_as_float(group_bcast<kLPR>(a2m, i)), rv[i],
+                                  __uint_as_float(group_bcast<kLPR>(c2m, i)), v2[i]));
+    }
+    // third and later in-epoch writes (rare): one round trip per write level
+    for (int k = 2;; k++) {
+        bool more = false;
 #pragma unroll
-        for (int d = 0; d < kD; d++) {
-            rv[d] = st.round(fma4(a1[d], st.widen(drow[d]), c1[d], v1[d]));
-            if (cnt[d] > 1) rv[d] = st.round(fma4(a2[d], rv[d], c2[d], v2[d]));
-        }
-        // third and later in-epoch writes (rare)
-        for (int k = 2;; k++) {
-            bool more = false;
+        for (int i = 0; i < NR; i++) more |= k < cnt[i];
+        if (__ballot(more) == 0ull) break;
+        TPEntry e[NR];
 #pragma unroll
-            for (int d = 0; d < kD; d++) more |= k < cnt[d];
-            if (__ballot(more) == 0ull) break;
-            TPEntry e[kD];
-            float4 vk[kD];
+        for (int i = 0; i < NR; i++)
+            if (k < cnt[i]) e[i] = se[first[i] + k];
 #pragma unroll
-            for (int d = 0; d < kD; d++)
-                if (k < cnt[d]) e[d] = se[first[d] + k];
-#pragma unroll
-            for (int d = 0; d < kD; d++)
-                if (k < cnt[d]) vk[d] = load_v<BF16>(a.v, vrow0 + (t0 + (e[d].tw >> 6)) * hd);
-#pragma unroll
-            for (int d = 0; d < kD; d++)
-                if (k < cnt[d]) rv[d] = st.round(fma4(e[d].a, rv[d], e[d].c, vk[d]));
-        }
-        // back into the read's row register (each value is exactly a stored one)
-#pragma unroll
-        for (int d = 0; d < kD; d++) {
-            if (!has[d]) continue;
-            const typename S::Raw p = st.pack(rv[d]);
-#pragma unroll
-            for (int i = 0; i < NR; i++)
-                if (id[d] == i) row[i] = p;
+        for (int i = 0; i < NR; i++) {
+            if (k < cnt[i]) {
+                const float4 vk = load_v<BF16>(a.v, vrow0 + (t0 + (e[i].tw >> 6)) * hd);
+                rv[i] = st.round(fma4(e[i].a, rv[i], e[i].c, vk));
+            }
         }
     }
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int i = 0; i < NR; i++) {
         // masked references have weight 0 and a zero row
-        const float4 rv = st.widen(row[i]);
         const float wr = __uint_as_float(group_bcast<kLPR>(__float_as_uint(wr_mine), i));
-        acc.x = fmaf(wr, rv.x, acc.x);
-        acc.y = fmaf(wr, rv.y, acc.y);
-        acc.z = fmaf(wr, rv.z, acc.z);
-        acc.w = fmaf(wr, rv.w, acc.w);
+        acc.x = fmaf(wr, rv[i].x, acc.x);
+        acc.y = fmaf(wr, rv[i].y, acc.y);
+        acc.z = fmaf(wr, rv[i].z, acc.z);
+        acc.w = fmaf(wr, rv[i].w, acc.w);
     }
 #pragma unroll
     for (int m = kLPR; m < 64; m <<= 1) {
@@ -621,6 +600,19 @@ __global__ __launch_bounds__(256) void tp_read_stored_kernel(TPArgs a, int ep, i
         acc.y += __shfl_xor(acc.y, m, 64);
         acc.z += __shfl_xor(acc.z, m, 64);
         acc.w += __shfl_xor(acc.w, m, 64);
+    }
+    if constexpr (WPU > 1) {
+        if (g == 0) part[wv][q] = acc;
+        __syncthreads();
+        if (w != 0) return;
+#pragma unroll
+        for (int k = 1; k < WPU; k++) {
+            const float4 p = part[wv + k][q];
+            acc.x += p.x;
+            acc.y += p.y;
+            acc.z += p.z;
+            acc.w += p.w;
+        }
     }
     if (g == 0 && col_ok)
         *reinterpret_cast<float4 *>(a.y + (b * a.T * a.H + t * a.H + h) * a.d_v + col) = acc;
@@ -648,10 +640,9 @@ __global__ __launch_bounds__(256) void tp_read_stored_kernel(TPArgs a, int ep, i
 // in the wave's last group or for a segment longer than the next group
 // (write/read 7.50 -> 7.19 ms; doing the tail inside the per-event loop,
 // from memory, forced full waits for every outstanding load).  A bfloat16
-// state is held to six waves per SIMD, an E4M3 state (whose codes take more
-// registers to encode) to five.
+// or E4M3 state is held to six waves per SIMD.
 template <bool BF16, int SPG, int ST, bool TAPE = false>
-__global__ __launch_bounds__(256, ST == kStateBF16 ? 6 : (ST == kStateFP8 ? 5 : 1)) void tp_update_kernel(TPArgs a, int ep,
+__global__ __launch_bounds__(256, ST != kStateF32 ? 6 : 1) void tp_update_kernel(TPArgs a, int ep,
                                                                                  int nslice,
                                                                                  int nblk, bool rev)
 {
@@ -929,20 +920,16 @@ static hipError_t tp_apply_state(const Shape &s, TPArgs a, bool bf16, hipStream_
         const int ne = (int)((s.T - t0) < a.E ? (s.T - t0) : a.E);
         const dim3 rgrid = chain_grid(a.chains, (int64_t)ne * nslice);
         if constexpr (ST != kStateF32) {  // stored-value reads (rows rounded after every write)
-#define SDM_TP_READ(NR_)                                                                          \
-    if (nr <= NR_) {                                                                              \
-        if (bf16) hipLaunchKernelGGL((tp_read_stored_kernel<NR_, true, ST>), rgrid, dim3(256), 0, \
+            const int wpu = stored_waves_per_unit<ST>(s.R);
+            const dim3 sgrid = chain_grid(a.chains, (int64_t)ne * nslice * wpu);
+#define SDM_TP_READ(W_)                                                                           \
+    if (wpu == W_) {                                                                              \
+        if (bf16) hipLaunchKernelGGL((tp_read_stored_kernel<true, ST, W_>), sgrid, dim3(256), 0,  \
                                      st, a, ep, nslice);                                          \
-        else hipLaunchKernelGGL((tp_read_stored_kernel<NR_, false, ST>), rgrid, dim3(256), 0, st, \
+        else hipLaunchKernelGGL((tp_read_stored_kernel<false, ST, W_>), sgrid, dim3(256), 0, st,  \
                                 a, ep, nslice);                                                   \
     } else
-            SDM_TP_READ(1) SDM_TP_READ(2) SDM_TP_READ(4) SDM_TP_READ(8) SDM_TP_READ(16) {
-                if constexpr (kLPR >= 32) {
-                    SDM_TP_READ(32) { return hipErrorInvalidValue; }
-                } else {
-                    return hipErrorInvalidValue;
-                }
-            }
+            SDM_TP_READ(1) SDM_TP_READ(2) SDM_TP_READ(4) { return hipErrorInvalidValue; }
 #undef SDM_TP_READ
         } else {
 #define SDM_TP_READ(NR_)                                                                          \

@@ -64,35 +64,37 @@ __device__ __forceinline__ uint32_t bf16_bits(float f)
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Nearest E4M3 code of a finite float a (sign, 4 exponent bits with bias 7,
-// 3 mantissa bits; normal values (1 + m/8) 2^(e-7), subnormals m 2^-9):
-// rounded to nearest, ties to even, magnitudes from 448 up saturated to 448
-// (the format has no infinities).
-__device__ __forceinline__ uint32_t e4m3_code(float a)
+// E4M3 codes (OCP FP8: sign, 4 exponent bits with bias 7, 3 mantissa bits;
+// normal values (1 + m/8) 2^(e-7), subnormals m 2^-9; largest magnitude 448,
+// no infinities).  The rule: the nearest code, ties to even, magnitudes
+// beyond 448 saturated to 448.  gfx950's conversion instructions use this
+// format and round to nearest even, subnormals included (checked against a
+// bit-level implementation of the rule over every float32 of magnitude <=
+// 448), so the saturation is a clamp before them.
+__device__ __forceinline__ float e4m3_clamp(float a)
 {
-    const uint32_t u = __float_as_uint(a);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t m = u & 0x7FFFFFFFu;
-    uint32_t c;
-    if (m >= 0x43E00000u) {  // |a| >= 448
-        c = 0x7Eu;
-    } else if (m >= 0x3C800000u) {  // |a| >= 2^-6: keep 3 of float32's 23 mantissa bits
-        const uint32_t r = m + 0x7FFFFu + ((m >> 20) & 1u);  // a carry moves the exponent up
-        c = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);      // exponent bias 127 -> 7
-        c = c > 0x7Eu ? 0x7Eu : c;
-    } else {  // a multiple of 2^-9; 8 * 2^-9 is the smallest normal, code 0x08
-        c = (uint32_t)__builtin_rintf(__uint_as_float(m) * 512.0f);
-    }
-    return sign | c;
+    return __builtin_fminf(__builtin_fmaxf(a, -448.0f), 448.0f);
 }
 
-// Value of an E4M3 code (exact in float32).
-__device__ __forceinline__ float e4m3_value(uint32_t c)
+// Codes of a and b in bytes 0 and 1 (HIGH = false) or 2 and 3 (HIGH = true)
+// of `old`, the other two bytes kept.
+template <bool HIGH>
+__device__ __forceinline__ uint32_t e4m3_pack2(float a, float b, uint32_t old)
 {
-    const uint32_t sign = (c & 0x80u) << 24;
-    const uint32_t em = c & 0x7Fu;
-    if (em >= 8u) return __uint_as_float(sign | ((em + 960u) << 20));  // exponent + 120
-    return __uint_as_float(sign | __float_as_uint((float)em * 0.001953125f));
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), (int)old, HIGH);
+}
+
+// Codes of the 4 values, column k in byte k.
+__device__ __forceinline__ uint32_t e4m3_pack4(float x, float y, float z, float w)
+{
+    return e4m3_pack2<true>(z, w, e4m3_pack2<false>(x, y, 0u));
+}
+
+// Value of byte k (0..3) of a word of E4M3 codes (exact in float32).
+template <int K>
+__device__ __forceinline__ float e4m3_value(uint32_t w)
+{
+    return __builtin_amdgcn_cvt_f32_fp8((int)w, K);
 }
 
 struct Shape {

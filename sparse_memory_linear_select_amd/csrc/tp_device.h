@@ -118,14 +118,13 @@ struct StateRow<kStateFP8> {
     }
     __device__ __forceinline__ float4 widen(Raw u) const
     {
-        return make_float4(e4m3_value(u & 0xFFu) * sc, e4m3_value((u >> 8) & 0xFFu) * sc,
-                           e4m3_value((u >> 16) & 0xFFu) * sc, e4m3_value(u >> 24) * sc);
+        return make_float4(e4m3_value<0>(u) * sc, e4m3_value<1>(u) * sc, e4m3_value<2>(u) * sc,
+                           e4m3_value<3>(u) * sc);
     }
     __device__ __forceinline__ float4 load(rsrc_t r, uint32_t off) const { return widen(load_raw(r, off)); }
     __device__ __forceinline__ Raw pack(float4 v) const
     {
-        return e4m3_code(v.x * isc) | (e4m3_code(v.y * isc) << 8) | (e4m3_code(v.z * isc) << 16) |
-               (e4m3_code(v.w * isc) << 24);
+        return e4m3_pack4(v.x * isc, v.y * isc, v.z * isc, v.w * isc);
     }
     __device__ __forceinline__ void store(float4 v, rsrc_t r, uint32_t off) const
     {

@@ -75,13 +75,28 @@ def _codes(x: torch.Tensor, s: int) -> torch.Tensor:
     return (x.float() * 2.0 ** -s).to(F8).view(torch.uint8)
 
 
+def _e4m3_grid():
+    """Every finite E4M3 value, every point halfway between neighbours, and
+    random magnitudes over all binades up to 448, with both signs (float32)."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(F8).float().numpy()
+    vals = np.unique(codes[np.isfinite(codes) & (codes >= 0)]).astype(np.float64)
+    mids = (vals[1:] + vals[:-1]) / 2
+    rng = np.random.default_rng(3)
+    rnd = np.exp2(rng.uniform(-12, np.log2(448.0), 4096))
+    g = np.concatenate([vals, mids, rnd]).astype(np.float32)
+    return np.concatenate([g, -g])
+
+
 def test_fp8_state_init_and_unselected_rows():
     """Rows never written hold the codes of M_0 * 2^-s, bit for bit as
-    torch converts them (nearest, ties to even)."""
+    torch converts them (nearest, ties to even), for M_0 covering every
+    E4M3 value, every halfway point and the subnormals."""
     wl, d = _small(51)
     d["kp"][..., :wl.sqrtN] = -8.0
     d["kp"][..., :2] = 8.0
     s = FP8_SCALE_LOG2
+    grid = _e4m3_grid() * np.float32(2.0 ** s)
+    d["M0"] = np.resize(grid, d["M0"].size).reshape(d["M0"].shape).astype(np.float32)
     core, dd, y, M = gpu_forward(d, wl.W, wl.R, sdm.AUTO, F8, s)
     Iw = core.select(dd["kp"], dd["qp"])[0].cpu().numpy()
     want = _codes(dd["M0"], s)
