@@ -339,7 +339,8 @@ __global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int str
 // token's v pairs kPairBatch per group at a time.  Every load depends only on
 // the plan, so all of them can be in flight together; reads that overflowed
 // the plan replay their writes from the sorted events.
-constexpr int kPairBatch = 4;  // v pairs per row group in flight
+constexpr int kPairBatch = 4;   // v pairs per row group in flight, after the first ones
+constexpr int kFirstPairs = 2;  // v pairs per row group loaded with the plan
 
 template <int NR, bool BF16>
 __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int nslice)
@@ -372,14 +373,32 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int nsli
     const uint32_t *rc = a.rec + ct * a.rec_dwords;
     const TPEntry *se = a.sorted + chain * a.T * a.W + t0 * a.W;
     const uint2 *pp = a.pairs + ct * a.P;
-    const uint32_t npw = __builtin_amdgcn_readfirstlane(a.npair[ct]);
-    const int np = (int)(npw & ~kReplayFlag);
 
-    // lane q of row group g holds the slot word and weight of reference
-    // g*NR + q (q < NR); the group reads them back with in-group broadcasts
+    // The plan: the pair count, the token's first pairs (the pair area is
+    // always there; entries past the count are masked below) and, in lane q
+    // of row group g, the slot word and weight of reference g*NR + q (q < NR;
+    // the group reads them back with in-group broadcasts).  None of these
+    // loads depends on another, so they take one round trip; the row and v
+    // gathers then depend only on them and take one more.
+    const uint32_t npw_v = a.npair[ct];
+    uint2 pr0[kFirstPairs];
+#pragma unroll
+    for (int u = 0; u < kFirstPairs; u++) {
+        const int j = u * kRPI + g;
+        pr0[u] = j < a.P ? pp[j] : make_uint2(0u, 0u);
+    }
     const bool mine = (q < NR) & (g * NR + q < a.R);
     const uint32_t sl_mine = mine ? rc[3 * a.Wp + g * NR + q] : 0u;
     const float wr_mine = mine ? a.rwt[ct * kMaxK + g * NR + q] : 0.0f;
+    const uint32_t npw = __builtin_amdgcn_readfirstlane(npw_v);
+    const int np = (int)(npw & ~kReplayFlag);
+    // v rows of the first pairs (a pair past the count: weight 0, token 0)
+    float4 vv0[kFirstPairs];
+#pragma unroll
+    for (int u = 0; u < kFirstPairs; u++) {
+        if (u * kRPI + g >= np) pr0[u] = make_uint2(0u, 0u);
+        vv0[u] = load_v<BF16>(a.v, vrow0 + (t0 + pr0[u].x) * hd);
+    }
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (!(npw & kReplayFlag)) {
         // every row gather at once, then the weighted sum
@@ -424,7 +443,16 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int nsli
             acc.w = fmaf(wr, rv.w, acc.w);
         }
     }
-    for (int j0 = 0; j0 < np; j0 += kRPI * kPairBatch) {
+#pragma unroll
+    for (int u = 0; u < kFirstPairs; u++) {
+        const float wgt = __uint_as_float(pr0[u].y);
+        acc.x = fmaf(wgt, vv0[u].x, acc.x);
+        acc.y = fmaf(wgt, vv0[u].y, acc.y);
+        acc.z = fmaf(wgt, vv0[u].z, acc.z);
+        acc.w = fmaf(wgt, vv0[u].w, acc.w);
+    }
+    // the rest of the pairs (tokens with many in-epoch writes before them)
+    for (int j0 = kRPI * kFirstPairs; j0 < np; j0 += kRPI * kPairBatch) {
         uint2 pr[kPairBatch];
         float4 vv[kPairBatch];
 #pragma unroll
@@ -461,10 +489,10 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int nsli
 // st.round(a*row + c*v) in time order.
 //
 // The R reads of a (chain, token of the epoch, 128-byte row slice) unit are
-// split over kWPU wavefronts (a power of two dividing 4, so a unit's waves
-// share a workgroup), 8 reads per row group: lane q < 8 of a group holds
-// read q's plan -- slot word, weight q, link (first write, count) and the
-// first two in-epoch writes' token, a and c.  Every gather that depends only
+// split over WPU wavefronts (a power of two; a unit's waves share a
+// workgroup), kStoredNR reads per row group: lane q < kStoredNR of a group
+// holds read q's plan -- slot word, weight q, link (first write, count) and
+// the first two in-epoch writes' token, a and c.  Every gather that depends only
 // on the plan -- the epoch-start rows and the v slices of the first two
 // writes -- is issued at once; a third or later write comes from the sorted
 // events, one round trip for all of the wave's reads per write.  Each wave
@@ -472,30 +500,40 @@ __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int nsli
 // sums of the others in wave order (LDS), so y sums the R rows in one fixed
 // order whichever reads saw in-epoch writes: it does not depend on where
 // epochs start.
-constexpr int kStoredNR = 8;  // reads per row group
+// Reads per row group, and whether the second write's v is gathered with
+// the rows.  Measured at the 1.4B-style layer with a bfloat16 state
+// (write/read): 4 reads with the second write 5.67 ms (62 VGPRs, eight waves
+// per SIMD), 4 without it 5.97, 8 with it 6.00 (115 VGPRs, four waves), 8
+// without it 6.04.
+constexpr int kStoredNR = 4;
+constexpr bool kSecondWithPlan = true;
 
+// Waves per (chain, token, slice) unit: enough for R reads, a power of two.
 template <int ST>
 constexpr int stored_waves_per_unit(int R)
 {
     const int per_wave = kStoredNR * (64 / StateRow<ST>::kLPR);
     const int w = (R + per_wave - 1) / per_wave;
-    return w <= 1 ? 1 : (w <= 2 ? 2 : 4);
+    return w <= 1 ? 1 : (w <= 2 ? 2 : (w <= 4 ? 4 : 8));
 }
+static_assert(kStoredNR * 2 * 8 >= kMaxK, "8 waves of 2 row groups hold every read");
 
 template <bool BF16, int ST, int WPU>
-__global__ __launch_bounds__(256) void tp_read_stored_kernel(TPArgs a, int ep, int nslice)
+__global__ __launch_bounds__(64 * (WPU > 4 ? WPU : 4)) void tp_read_stored_kernel(TPArgs a, int ep,
+                                                                                  int nslice)
 {
     using S = StateRow<ST>;
     constexpr int kLPR = S::kLPR, kRPI = 64 / kLPR, NR = kStoredNR;
-    static_assert(NR <= kLPR && 4 % WPU == 0, "one read per lane; a unit's waves in a workgroup");
-    __shared__ float4 part[4][kLPR];  // partial sums of the waves (column quads of the slice)
+    constexpr int kWG = WPU > 4 ? WPU : 4;  // waves per workgroup
+    static_assert(NR <= kLPR && kWG % WPU == 0, "one read per lane; a unit's waves in a workgroup");
+    __shared__ float4 part[kWG][kLPR];  // partial sums of the waves (column quads of the slice)
     const S st(a.ssc, a.sisc);
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t chain = grid_chain();
     const int64_t t0 = (int64_t)ep * a.E;
     const int ne = (int)((a.T - t0) < a.E ? (a.T - t0) : a.E);
-    const uint32_t wid = blockIdx.x * 4u + (uint32_t)wv;  // wave of this chain
+    const uint32_t wid = blockIdx.x * (uint32_t)kWG + (uint32_t)wv;  // wave of this chain
     const uint32_t u = wid / WPU;                          // its unit
     const int w = (int)(wid % WPU);                        // its part of the unit's reads
     const bool active = chain < a.chains && u < (uint32_t)(ne * nslice);  // wave-uniform
@@ -549,7 +587,7 @@ __global__ __launch_bounds__(256) void tp_read_stored_kernel(TPArgs a, int ep, i
         v1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
         v2[i] = v1[i];
         if (cnt > 0) v1[i] = load_v<BF16>(a.v, vrow0 + (t0 + t1) * hd);
-        if (cnt > 1) v2[i] = load_v<BF16>(a.v, vrow0 + (t0 + t2) * hd);
+        if (kSecondWithPlan && cnt > 1) v2[i] = load_v<BF16>(a.v, vrow0 + (t0 + t2) * hd);
     }
     float4 rv[NR];
     int cnt[NR], first[NR];
@@ -562,9 +600,26 @@ __global__ __launch_bounds__(256) void tp_read_stored_kernel(TPArgs a, int ep, i
         if (cnt[i] > 0)
             rv[i] = st.round(fma4(__uint_as_float(group_bcast<kLPR>(a1m, i)), rv[i],
                                   __uint_as_float(group_bcast<kLPR>(c1m, i)), v1[i]));
-        if (cnt[i] > 1)
+        if (kSecondWithPlan && cnt[i] > 1)
             rv[i] = st.round(fma4(__uint_as_float(group_bcast<kLPR>(a2m, i)), rv[i],
                                   __uint_as_float(group_bcast<kLPR>(c2m, i)), v2[i]));
+    }
+    if constexpr (!kSecondWithPlan) {  // second writes: one more round trip
+        bool more = false;
+#pragma unroll
+        for (int i = 0; i < NR; i++) more |= cnt[i] > 1;
+        if (__ballot(more) != 0ull) {
+#pragma unroll
+            for (int i = 0; i < NR; i++) {
+                const uint32_t t2 = group_bcast<kLPR>(t2m, i);
+                if (cnt[i] > 1) v2[i] = load_v<BF16>(a.v, vrow0 + (t0 + t2) * hd);
+            }
+#pragma unroll
+            for (int i = 0; i < NR; i++)
+                if (cnt[i] > 1)
+                    rv[i] = st.round(fma4(__uint_as_float(group_bcast<kLPR>(a2m, i)), rv[i],
+                                          __uint_as_float(group_bcast<kLPR>(c2m, i)), v2[i]));
+        }
     }
     // third and later in-epoch writes (rare): one round trip per write level
     for (int k = 2;; k++) {
@@ -921,15 +976,20 @@ static hipError_t tp_apply_state(const Shape &s, TPArgs a, bool bf16, hipStream_
         const dim3 rgrid = chain_grid(a.chains, (int64_t)ne * nslice);
         if constexpr (ST != kStateF32) {  // stored-value reads (rows rounded after every write)
             const int wpu = stored_waves_per_unit<ST>(s.R);
-            const dim3 sgrid = chain_grid(a.chains, (int64_t)ne * nslice * wpu);
+            const int wg = wpu > 4 ? wpu : 4;  // waves per workgroup
+            const int64_t waves = (int64_t)ne * nslice * wpu;
+            dim3 sgrid = chain_grid(a.chains, waves);
+            sgrid.x = (unsigned)((waves + wg - 1) / wg);
 #define SDM_TP_READ(W_)                                                                           \
     if (wpu == W_) {                                                                              \
-        if (bf16) hipLaunchKernelGGL((tp_read_stored_kernel<true, ST, W_>), sgrid, dim3(256), 0,  \
-                                     st, a, ep, nslice);                                          \
-        else hipLaunchKernelGGL((tp_read_stored_kernel<false, ST, W_>), sgrid, dim3(256), 0, st,  \
-                                a, ep, nslice);                                                   \
+        if (bf16) hipLaunchKernelGGL((tp_read_stored_kernel<true, ST, W_>), sgrid, dim3(64 * wg), \
+                                     0, st, a, ep, nslice);                                       \
+        else hipLaunchKernelGGL((tp_read_stored_kernel<false, ST, W_>), sgrid, dim3(64 * wg), 0,  \
+                                st, a, ep, nslice);                                               \
     } else
-            SDM_TP_READ(1) SDM_TP_READ(2) SDM_TP_READ(4) { return hipErrorInvalidValue; }
+            SDM_TP_READ(1) SDM_TP_READ(2) SDM_TP_READ(4) SDM_TP_READ(8) {
+                return hipErrorInvalidValue;
+            }
 #undef SDM_TP_READ
         } else {
 #define SDM_TP_READ(NR_)                                                                          \
