@@ -95,9 +95,13 @@ typedef enum {
 #define SDM_FLAG_CONTINUE 1u /* start from the state already in M (no M <- M_0) */
 
 /*
- * Create a handle for one SDM layer shape.
- *   M0     device [H][N][d_v] float32, the shared initial state; borrowed:
- *          it must stay valid and unchanged until sdm_destroy.
+ * Create a handle for one SDM layer shape: H heads, each with N = sqrtN^2
+ * slots of d_v columns, W write slots and R read slots per token
+ * [explainer "Sparse Delta Memory：通过稀疏性扩展线性 RNN 的状态容量", §3.1 and
+ * §3.3 Eq. (6); "Technical Summary: Sparse Delta Memory (SDM)", Methodology].
+ *   M0     device [H][N][d_v] float32, the shared initial state (explainer
+ *          §3.1, learned initial state); borrowed: it must stay valid and
+ *          unchanged until sdm_destroy.
  *   H, sqrtN, d_v, W, R  as above.
  *   out    receives the handle.
  * Makes no HIP call.  Errors: SDM_ERR_ARG (null, size), SDM_ERR_UNSUPPORTED
@@ -165,7 +169,10 @@ sdm_status sdm_workspace_size(sdm_handle h, int B, int64_t T, sdm_dtype dtype,
                               sdm_variant variant, size_t *bytes);
 
 /*
- * Selection only (the first step of the core, standalone).
+ * Selection only (the first step of the core, standalone): the top-W slots of
+ * k' and the top-R slots of q' under the outer-sum scores, by the
+ * product-key identity, with softmax weights [explainer §3.1 step 1;
+ * Technical Summary, Core Mechanism 2].
  *   kp, qp  device [B][T][H][2*sqrtN], element type `dtype`.
  *   Iw, kw  device [B][T][H][W]: write slots (int32, canonical order) and
  *           their softmax weights (float32).
@@ -178,7 +185,8 @@ sdm_status sdm_select(sdm_handle h, int B, int64_t T, const void *kp, const void
 
 /*
  * The whole core: select, then the gated delta write and the sparse read for
- * every token in order.
+ * every token in order [explainer §3.1 steps 1-3; Technical Summary, Core
+ * Mechanism 2-4].
  *   kp, qp     device [B][T][H][2*sqrtN], element type `dtype`.
  *   v          device [B][T][H][d_v], element type `dtype`.
  *   alpha,beta device [B][T][H] float32, the gates of each head-token.

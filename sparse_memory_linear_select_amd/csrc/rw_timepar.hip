@@ -13,8 +13,11 @@
 //   plan     every read gets the weight of its slot's epoch-start row and
 //            the (token, weight) pairs of the v rows its in-epoch writes
 //            added (the composed affine map, scaled by the read weight q);
+//            with a bfloat16 or E4M3 state, whose rows are rounded after
+//            every write, a read instead gets its in-epoch writes themselves;
 //   read     y_t = weighted sum of epoch-start rows and v rows, all gathers
-//            independent of each other;
+//            independent of each other (narrower states: the epoch-start row
+//            with the read's in-epoch writes replayed, rounded as stored);
 //   update   the first event of each slot's segment loads the row once,
 //            applies all of the segment's writes in time order and stores it
 //            once.
@@ -22,8 +25,8 @@
 // Within an epoch everything is parallel; epochs follow each other in stream
 // order (read of epoch e, update of e, read of e+1, ...).  Each row value is
 // produced by the same float32 operations, in the same order, as in the
-// token-serial schedule, so both schedules give identical M; y agrees to
-// float32 rounding (its terms are grouped differently).
+// token-serial schedule, so both schedules give identical M; with a float32
+// state y agrees to float32 rounding (its terms are grouped differently).
 #include "tp_device.h"
 
 namespace sdm {
