@@ -355,7 +355,8 @@ class SDM:
 
         With cont=True, M must hold the state to continue from (no M <- M_0).
         staged=True issues sdm_prepare + sdm_apply instead of sdm_forward
-        (the same work on the same stream).
+        (the same results on the same stream; for one token per sequence
+        sdm_forward runs the whole step as one launch).
         """
         B, T, dt, y, M = self._forward_args(kp, qp, v, alpha, beta, y, M, cont)
         dev = kp.device

@@ -6,6 +6,7 @@
 // stores the written rows, then gathers the read rows (a read of a slot written by the same
 // token finds the new row) and sums them into y.  Only the wavefront that
 // wrote a row slice reads it back, so no other ordering is needed.
+#include "select_device.h"
 #include "tp_device.h"
 
 namespace sdm {
@@ -133,7 +134,337 @@ hipError_t launch_state(const Shape &s, const DecArgs &a, bool bf16, hipStream_t
     return hipErrorInvalidValue;
 }
 
+// The whole step in one launch.  A workgroup of four wavefronts serves one
+// chain (b, h) and a range of its row slices.  It first selects the chain's
+// slots itself, with the selection kernel's steps (so the same slots and
+// weights): wavefront (list, half) sorts one half of k' (list 0) or q'
+// (list 1); of each list's two wavefronts one merges the pairs of hooks 0
+// and 1 while the other sorts those of hooks >= 2, and the first merges the
+// two and takes the softmax; the write coefficients a = alpha(1 - beta k),
+// c = beta k go to LDS with the slots.  Wavefronts 0 and 1 then take a row
+// slice each, as the two-launch kernel does, but gather the written and the
+// read rows at once; while the gathers are in flight every wavefront looks
+// for reads whose slot the token also writes, and such a read takes the new
+// row from the LDS copy of the rows its wavefront just wrote (the stored
+// values), so no gather waits on the stores.  Every workgroup of a chain
+// repeats the selection: for one token the chip has far more compute units
+// than lists, and the repeat costs no time, while records in memory and a
+// second launch would.
+struct DecFArgs {
+    const void *kp, *qp, *v;
+    const float *alpha, *beta;
+    float *y;
+    void *M;
+    float ssc, sisc;  // E4M3 state: 2^s, 2^-s
+    int64_t N;
+    int sqrtN, d_v, W, R, bf16;
+    int nslice, groups, spw;  // row slices per chain; workgroups per chain; slices per wavefront
+    uint16_t tab[2][kTabMax];
+    int tabn[2];
+};
+
+template <int E, int ST>
+__global__ __launch_bounds__(256) void rw_decode_fused_kernel(DecFArgs a)
+{
+    using S = StateRow<ST>;
+    using Raw = typename S::Raw;
+    const S st(a.ssc, a.sisc);
+    constexpr int kLPR = dec_lpr<ST>(), kRPI = 64 / kLPR, NK = kMaxK / kRPI;
+    __shared__ float sv[2][2][64];
+    __shared__ uint32_t si[2][2][64];
+    __shared__ uint32_t yh[2][64], yl[2][64], yn[2][64];  // sorted pairs of hooks >= 2
+    __shared__ __align__(16) uint32_t wsl_s[kMaxK];
+    __shared__ uint32_t rsl_s[kMaxK];
+    __shared__ float wa_s[kMaxK], wc_s[kMaxK], rq_s[kMaxK];
+    __shared__ int rmatch_s[kMaxK];
+    __shared__ Raw wrow[2][kMaxK][kLPR];  // rows wavefronts 0 and 1 wrote, as stored
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int list = wv >> 1, half = wv & 1;
+    // one token: the chain b*H + h is also the head-token's index
+    const uint32_t chain = blockIdx.x / (uint32_t)a.groups;
+    const int grp = (int)(blockIdx.x - chain * (uint32_t)a.groups);
+    const int Sq = a.sqrtN;
+    const int K = list ? a.R : a.W;
+    const int rest = a.tabn[list];
+
+    float al = 0.0f, be = 0.0f;
+    if (wv == 0) {
+        al = a.alpha[chain];
+        be = a.beta[chain];
+    }
+    // this wavefront's candidate columns: 0-2 (half 0) or 3, 4 (half 1)
+    uint16_t tabv[3];
+#pragma unroll
+    for (int r = 0; r < 3; r++) {
+        const int c = half ? 3 + r : r;
+        tabv[r] = c < 5 ? a.tab[list][c * 64 + lane] : kNoPair;
+    }
+
+    // ---- selection, stage 1: this wavefront's half, sorted; first K kept ----
+    {
+        const void *x = list ? a.qp : a.kp;
+        const int64_t base = (int64_t)chain * 2 * Sq + half * Sq;
+        uint64_t kk[1][E];
+#pragma unroll
+        for (int r = 0; r < E; r++) {
+            const int e = lane * E + r;
+            kk[0][r] = e < Sq ? ((uint64_t)f2ord(load_elem(x, a.bf16, base + e)) << 32) |
+                                    ~(uint32_t)e
+                              : 0;  // below every finite score
+        }
+        sort_desc<1, E>(kk, lane);
+#pragma unroll
+        for (int r = 0; r < E; r++) {
+            const int e = lane * E + r;
+            if (e < K) {
+                sv[list][half][e] = ord2f((uint32_t)(kk[0][r] >> 32));
+                si[list][half][e] = ~(uint32_t)kk[0][r];
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- stage 2 (see select_pairs: the same candidates, split over the
+    // list's two wavefronts; every candidate is kept until the last merge) ----
+    uint64_t key = 0;
+    uint32_t n = 0xFFFFFFFFu;
+    {
+        const float *v1 = sv[list][0], *v2 = sv[list][1];
+        const uint32_t *i1 = si[list][0], *i2 = si[list][1];
+        if (half == 0) {
+            // hook 0: columns 0 and 1 arrive sorted; hook 1: column 2 bitonic
+            uint64_t ck[3];
+            uint32_t cn[3];
+#pragma unroll
+            for (int r = 0; r < 3; r++) pair_entry(v1, v2, i1, i2, tabv[r], Sq, ck[r], cn[r]);
+            if (K >= 2) col_merge(ck[0], cn[0], ck[1], cn[1], lane);
+            if (K >= 4) {
+                col_bitonic(ck[2], cn[2], lane);
+                col_merge(ck[0], cn[0], ck[2], cn[2], lane);
+            }
+            key = ck[0];
+            n = cn[0];
+        } else if (rest > 0) {
+            // hooks >= 2: columns 3 and 4, unsorted
+            uint64_t ck[2];
+            uint32_t cn[2];
+#pragma unroll
+            for (int r = 0; r < 2; r++) pair_entry(v1, v2, i1, i2, tabv[r], Sq, ck[r], cn[r]);
+            col_sort(ck[0], cn[0], lane);
+            if (rest > 64) {
+                col_sort(ck[1], cn[1], lane);
+                col_merge(ck[0], cn[0], ck[1], cn[1], lane);
+            }
+            yh[list][lane] = (uint32_t)(ck[0] >> 32);
+            yl[list][lane] = (uint32_t)ck[0];
+            yn[list][lane] = cn[0];
+        }
+    }
+    __syncthreads();
+    if (half == 0) {
+        if (rest > 0) {
+            const int r = 63 - lane;
+            col_merge_rev(key, n, ((uint64_t)yh[list][r] << 32) | yl[list][r], yn[list][r], lane);
+        }
+        const float w = select_weight(key, K, lane);
+        if (lane < K) {
+            if (list == 0) {
+                const float c = be * w;
+                wsl_s[lane] = n;
+                wa_s[lane] = al * (1.0f - c);
+                wc_s[lane] = c;
+            } else {
+                rsl_s[lane] = n;
+                rq_s[lane] = w;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- writes and reads: wavefronts 0 and 1 take row slices ----
+    const int g = lane / kLPR, q = lane % kLPR;
+    const rsrc_t Mr = make_rsrc(static_cast<char *>(a.M) + (int64_t)chain * a.N * a.d_v * S::kElem,
+                                (uint32_t)(a.N * a.d_v * S::kElem));
+    const uint32_t rowb = (uint32_t)a.d_v * S::kElem;
+    // row group g takes writes and reads g, g + kRPI, ...
+    uint32_t wsl[NK], rsl[NK];
+    float wa[NK], wc[NK], rq[NK];
+    // (entries past W or R hold stale LDS: their gathers and stores are masked,
+    // and a read weight past R is zeroed)
+#pragma unroll
+    for (int i = 0; i < NK; i++) {
+        const int k = g + i * kRPI;
+        wsl[i] = wsl_s[k];
+        wa[i] = wa_s[k];
+        wc[i] = wc_s[k];
+        rsl[i] = rsl_s[k];
+        const float w = rq_s[k];
+        rq[i] = k < a.R ? w : 0.0f;
+    }
+    // gathers of one slice: the written rows and every read row
+    Raw old[NK], row[NK];
+    float4 vv = make_float4(0.f, 0.f, 0.f, 0.f);
+    int slice = grp * a.spw * 2 + wv;
+    bool have = wv < 2 && slice < a.nslice;
+    auto gather = [&](int sl) {
+        const int col = sl * 4 * kLPR + q * 4;
+        const bool col_ok = col < a.d_v;
+        const int64_t vy = (int64_t)chain * a.d_v + (col_ok ? col : 0);
+        vv = a.bf16 ? load_v<true>(a.v, vy) : load_v<false>(a.v, vy);
+#pragma unroll
+        for (int i = 0; i < NK; i++) {
+            const int k = g + i * kRPI;
+            old[i] = st.load_raw(Mr, (col_ok & (k < a.W)) ? wsl[i] * rowb + col * S::kElem : kOff);
+        }
+#pragma unroll
+        for (int i = 0; i < NK; i++) {
+            const int k = g + i * kRPI;
+            row[i] = st.load_raw(Mr, (col_ok & (k < a.R)) ? rsl[i] * rowb + col * S::kElem : kOff);
+        }
+    };
+    if (have) gather(slice);
+
+    // ---- meanwhile: the write of each read's slot by this token, if any
+    // (slots within a list are distinct); four lanes per read, 16 writes each ----
+    {
+        const int i = wv * 16 + (lane >> 2);
+        const int j0 = (lane & 3) * 16;
+        int m = -1;
+        if (i < a.R) {
+            const uint32_t sl = rsl_s[i];
+            const uint4 *w4 = reinterpret_cast<const uint4 *>(wsl_s + j0);
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const uint4 ws = w4[u];
+                const int j = j0 + 4 * u;
+                if (j < a.W && ws.x == sl) m = j;
+                if (j + 1 < a.W && ws.y == sl) m = j + 1;
+                if (j + 2 < a.W && ws.z == sl) m = j + 2;
+                if (j + 3 < a.W && ws.w == sl) m = j + 3;
+            }
+        }
+        m = max(m, __shfl_xor(m, 1, 64));
+        m = max(m, __shfl_xor(m, 2, 64));
+        if ((lane & 3) == 0 && i < a.R) rmatch_s[i] = m;
+    }
+    __syncthreads();
+    if (wv >= 2) return;
+    int rm[NK];
+#pragma unroll
+    for (int i = 0; i < NK; i++) {
+        const int k = g + i * kRPI;
+        rm[i] = k < a.R ? rmatch_s[k] : -1;
+    }
+
+    for (int u = 0; have;) {
+        const int col = slice * 4 * kLPR + q * 4;
+        const bool col_ok = col < a.d_v;
+        wave_sync();  // the previous slice's reads of wrow are done
+#pragma unroll
+        for (int i = 0; i < NK; i++) {
+            const int k = g + i * kRPI;
+            const float4 nw = st.round(fma4(wa[i], st.widen(old[i]), wc[i], vv));
+            st.store(nw, Mr, (col_ok & (k < a.W)) ? wsl[i] * rowb + col * S::kElem : kOff);
+            if (k < a.W) wrow[wv][k][q] = st.pack(nw);
+        }
+        wave_sync();
+#pragma unroll
+        for (int i = 0; i < NK; i++)
+            if (rm[i] >= 0) row[i] = wrow[wv][rm[i]][q];
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int i = 0; i < NK; i++) {
+            const float4 x = st.widen(row[i]);
+            acc.x = fmaf(rq[i], x.x, acc.x);
+            acc.y = fmaf(rq[i], x.y, acc.y);
+            acc.z = fmaf(rq[i], x.z, acc.z);
+            acc.w = fmaf(rq[i], x.w, acc.w);
+        }
+#pragma unroll
+        for (int m = kLPR; m < 64; m <<= 1) {
+            acc.x = xor_add(acc.x, m);
+            acc.y = xor_add(acc.y, m);
+            acc.z = xor_add(acc.z, m);
+            acc.w = xor_add(acc.w, m);
+        }
+        if (g == 0 && col_ok)
+            *reinterpret_cast<float4 *>(a.y + (int64_t)chain * a.d_v + col) = acc;
+        if (++u >= a.spw) break;
+        slice = (grp * a.spw + u) * 2 + wv;
+        have = slice < a.nslice;
+        if (have) gather(slice);
+    }
+}
+
+template <int ST>
+hipError_t launch_fused_state(const Shape &s, DecFArgs &a, hipStream_t st)
+{
+    constexpr int kLPR = dec_lpr<ST>();
+    a.nslice = (s.d_v + 4 * kLPR - 1) / (4 * kLPR);
+    const int64_t chains = (int64_t)s.B * s.H;
+    // two slices per workgroup (one per row wavefront), unless that makes
+    // more than 1024 workgroups (each repeats its chain's selection)
+    int spw = 1;
+    while (chains * ((a.nslice + 2 * spw - 1) / (2 * spw)) > 1024 && 2 * spw < a.nslice) spw *= 2;
+    a.spw = spw;
+    a.groups = (a.nslice + 2 * spw - 1) / (2 * spw);
+    const int64_t blocks = chains * a.groups;
+    if (blocks >= (int64_t)1 << 31) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)blocks);
+#define SDM_DECF(E_)                                                                            case E_:                                                                                        hipLaunchKernelGGL((rw_decode_fused_kernel<E_, ST>), grid, dim3(256), 0, st, a);           return hipGetLastError();
+    switch ((s.sqrtN + 63) / 64) {
+        SDM_DECF(1)
+        SDM_DECF(2)
+    case 3:
+        SDM_DECF(4)
+    case 5:
+    case 6:
+    case 7:
+        SDM_DECF(8)
+    default: return hipErrorInvalidValue;
+    }
+#undef SDM_DECF
+}
+
 }  // namespace
+
+bool decode_fused_supported(const Shape &s)
+{
+    return decode_supported(s) && s.sqrtN <= 512;
+}
+
+hipError_t launch_decode_fused(const Shape &s, const void *kp, const void *qp, const void *v,
+                               bool bf16, const float *alpha, const float *beta, float *y,
+                               void *M, StateFmt fmt, hipStream_t st)
+{
+    if (!decode_fused_supported(s)) return hipErrorInvalidValue;
+    DecFArgs a{};
+    a.kp = kp;
+    a.qp = qp;
+    a.v = v;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.y = y;
+    a.M = M;
+    a.ssc = ldexpf(1.0f, fmt.scale_log2);
+    a.sisc = ldexpf(1.0f, -fmt.scale_log2);
+    a.N = s.N();
+    a.sqrtN = s.sqrtN;
+    a.d_v = s.d_v;
+    a.W = s.W;
+    a.R = s.R;
+    a.bf16 = bf16 ? 1 : 0;
+    for (int list = 0; list < 2; list++) {
+        const uint16_t *t = hook_columns(list ? s.R : s.W, &a.tabn[list]);
+        for (int i = 0; i < kTabMax; i++) a.tab[list][i] = t[i];
+    }
+    switch (fmt.type) {
+        case kStateBF16: return launch_fused_state<kStateBF16>(s, a, st);
+        case kStateFP8: return launch_fused_state<kStateFP8>(s, a, st);
+        default: return launch_fused_state<kStateF32>(s, a, st);
+    }
+}
 
 bool decode_supported(const Shape &s)
 {

@@ -423,6 +423,21 @@ sdm_status sdm_forward(sdm_handle h, int B, int64_t T, const void *kp, const voi
     sdm_variant var;
     st = check_variant_and_ws(h, B, T, variant, ws_bytes, &var);
     if (st != SDM_OK) return st;
+    const sdm::Shape s = shape_of(h, B, T);
+    if (var == SDM_VARIANT_TIMEPAR && sdm::decode_fused_supported(s)) {
+        // one token per sequence: selection, writes and reads in one launch
+        // (the workspace is not used)
+        const hipStream_t hs = (hipStream_t)stream;
+        hipError_t e;
+        if (!(flags & SDM_FLAG_CONTINUE)) {
+            e = sdm::launch_init(s, h->M0, M, h->state, hs);
+            if (e != hipSuccess) return hip_fail(e, "init launch");
+        }
+        e = sdm::launch_decode_fused(s, kp, qp, v, dtype == SDM_BF16, alpha, beta, y, M, h->state,
+                                     hs);
+        if (e != hipSuccess) return hip_fail(e, "one-token step launch");
+        return SDM_OK;
+    }
     st = sdm_prepare(h, B, T, kp, qp, alpha, beta, dtype, variant, flags, workspace, ws_bytes, M,
                      stream);
     if (st != SDM_OK) return st;

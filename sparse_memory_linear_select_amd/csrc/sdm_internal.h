@@ -166,6 +166,17 @@ hipError_t launch_tp_apply(const Shape &s, const uint32_t *rec, void *ws, const 
 bool decode_supported(const Shape &s);
 hipError_t launch_rw_decode(const Shape &s, const uint32_t *rec, const void *v, bool bf16,
                             float *y, void *M, StateFmt fmt, hipStream_t st);
+// The whole one-token step in one launch: each workgroup selects its
+// chain's write and read slots itself (no token records) and then writes and
+// reads a range of row slices.  Results bit-identical to launch_select +
+// launch_rw_decode.  For decode_supported shapes with sqrtN <= 512.
+bool decode_fused_supported(const Shape &s);
+hipError_t launch_decode_fused(const Shape &s, const void *kp, const void *qp, const void *v,
+                               bool bf16, const float *alpha, const float *beta, float *y,
+                               void *M, StateFmt fmt, hipStream_t st);
+// Candidate columns of stage 2 for lists of K slots (kTabMax entries, pairs
+// a << 8 | b) and the number of pairs with both ranks >= 2.
+const uint16_t *hook_columns(int K, int *rest);
 
 // Backward (float32 state): a forward write pass over epochs [ep0, ep1) that
 // records each written slot's epoch-start row in the tape ([chain][tapeT][W]

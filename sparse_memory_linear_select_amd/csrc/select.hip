@@ -27,301 +27,13 @@
 // of ranks (a, b) is preceded by every pair (a', b') with a' <= a, b' <= b
 // (score at least as large, and on an equal score a smaller flat index), so
 // with (a+1)(b+1) > K at least K pairs come before it.
-#include "sdm_internal.h"
+#include "select_device.h"
 
 #include <array>
 #include <cstring>
 
 namespace sdm {
 namespace {
-
-constexpr int kTabMax = 320;  // >= number of pruned pairs for K = 64 (280)
-
-__device__ __forceinline__ uint32_t f2ord(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    if (u == 0x80000000u) u = 0u;  // -0 and +0 are the same score
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float ord2f(uint32_t o)
-{
-    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
-}
-
-__device__ __forceinline__ uint32_t shl(uint32_t v, int src)
-{
-    return (uint32_t)__shfl((int)v, src, 64);
-}
-
-__device__ __forceinline__ uint64_t shl64(uint64_t v, int src)
-{
-    const uint32_t lo = shl((uint32_t)v, src), hi = shl((uint32_t)(v >> 32), src);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-// Lane exchanges inside the compare-exchange networks.  These form the
-// dependent chain of a selection, so they avoid the LDS crossbar
-// (ds_bpermute):
-//   m = 1, 2   one DPP quad permutation;
-//   m = 4      row_shl:4 into banks 0 and 2 (lanes with bit 2 clear), then
-//              row_shr:4 into banks 1 and 3 (bank = 4 lanes of a 16-lane row);
-//   m = 8      row_ror:8 (a rotation by half of the 16-lane row);
-//   m = 16, 32 the gfx950 permlane swaps, which give every lane both values
-//              of its pair {l, l ^ m}: (lower lane's, upper lane's).
-// m is a compile-time constant at every call (the networks are instantiated
-// step by step); the DPP controls must be immediates, hence the switch.
-__device__ __forceinline__ uint32_t dpp_xor(uint32_t x, int m)
-{
-    switch (m) {
-    case 1: return __builtin_amdgcn_update_dpp(0u, x, 0xB1, 0xF, 0xF, false);
-    case 2: return __builtin_amdgcn_update_dpp(0u, x, 0x4E, 0xF, 0xF, false);
-    case 4: {
-        const uint32_t y = __builtin_amdgcn_update_dpp(x, x, 0x104, 0xF, 0x5, false);
-        return __builtin_amdgcn_update_dpp(y, x, 0x114, 0xF, 0xA, false);
-    }
-    default: return __builtin_amdgcn_update_dpp(0u, x, 0x128, 0xF, 0xF, false);
-    }
-}
-
-__device__ __forceinline__ void pair_vals(uint32_t x, int m, uint32_t &lo, uint32_t &hi)
-{
-    if (m == 16) {
-        const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-        lo = r[0];
-        hi = r[1];
-    } else {
-        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-        lo = r[0];
-        hi = r[1];
-    }
-}
-
-__device__ __forceinline__ uint64_t dpp_xor64(uint64_t v, int m)
-{
-    return ((uint64_t)dpp_xor((uint32_t)(v >> 32), m) << 32) | dpp_xor((uint32_t)v, m);
-}
-
-__device__ __forceinline__ void pair_vals64(uint64_t v, int m, uint64_t &lo, uint64_t &hi)
-{
-    uint32_t l0, h0, l1, h1;
-    pair_vals((uint32_t)v, m, l0, h0);
-    pair_vals((uint32_t)(v >> 32), m, l1, h1);
-    lo = ((uint64_t)l1 << 32) | l0;
-    hi = ((uint64_t)h1 << 32) | h0;
-}
-
-// This lane's key after a compare-exchange with lane ^ m: the larger key of
-// the pair if keep_max, else the smaller (one compare; equal keys: either).
-__device__ __forceinline__ uint64_t xchg_max(uint64_t k, int m, bool keep_max)
-{
-    if (m >= 16) {
-        uint64_t lo, hi;
-        pair_vals64(k, m, lo, hi);
-        return ((lo > hi) == keep_max) ? lo : hi;
-    }
-    const uint64_t o = dpp_xor64(k, m);
-    return ((o > k) == keep_max) ? o : k;
-}
-
-// Orders LDS traffic between the lanes of one wavefront.
-__device__ __forceinline__ void wave_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__device__ __forceinline__ void two_sum(float a, float b, float &s, float &e)
-{
-    s = a + b;
-    const float bv = s - a;
-    const float av = s - bv;
-    e = (a - av) + (b - bv);
-}
-
-__device__ __forceinline__ float load_elem(const void *x, bool bf16, int64_t i)
-{
-    if (bf16) return __uint_as_float((uint32_t)((const uint16_t *)x)[i] << 16);
-    return ((const float *)x)[i];
-}
-
-// Step (KK, J) of the bitonic network over both halves (descending); the
-// steps are instantiated one by one so that every lane pattern is a
-// compile-time constant (the DPP controls must be immediates).
-template <int E, int KK, int J>
-__device__ __forceinline__ void sort_step(uint64_t (&k1)[E], uint64_t (&k2)[E], int lane)
-{
-    if constexpr (J < E) {  // partner in the same lane
-#pragma unroll
-        for (int r = 0; r < E; r++) {
-            if ((r & J) == 0) {
-                // one compare per exchange: swap when the pair is out of the
-                // step's direction (equal keys: either way)
-                const int e = lane * E + r;
-                const bool desc = (e & KK) == 0;
-                uint64_t a = k1[r], b = k1[r | J];
-                bool sw = (a < b) == desc;
-                k1[r] = sw ? b : a;
-                k1[r | J] = sw ? a : b;
-                a = k2[r];
-                b = k2[r | J];
-                sw = (a < b) == desc;
-                k2[r] = sw ? b : a;
-                k2[r | J] = sw ? a : b;
-            }
-        }
-    } else {  // partner in lane ^ (J / E), same register
-#pragma unroll
-        for (int r = 0; r < E; r++) {
-            const int e = lane * E + r;
-            const bool keep_max = ((e & J) == 0) == ((e & KK) == 0);
-            k1[r] = xchg_max(k1[r], J / E, keep_max);
-            k2[r] = xchg_max(k2[r], J / E, keep_max);
-        }
-    }
-}
-
-template <int E, int KK, int J>
-__device__ __forceinline__ void sort_steps(uint64_t (&k1)[E], uint64_t (&k2)[E], int lane)
-{
-    sort_step<E, KK, J>(k1, k2, lane);
-    if constexpr (J > 1) sort_steps<E, KK, J / 2>(k1, k2, lane);
-}
-
-template <int E, int KK>
-__device__ __forceinline__ void sort_stages(uint64_t (&k1)[E], uint64_t (&k2)[E], int lane)
-{
-    sort_steps<E, KK, KK / 2>(k1, k2, lane);
-    if constexpr (KK < 64 * E) sort_stages<E, 2 * KK>(k1, k2, lane);
-}
-
-// Sort 64*E keys of each of two halves, descending; element e = lane*E + r.
-template <int E>
-__device__ __forceinline__ void sort_halves_desc(uint64_t (&k1)[E], uint64_t (&k2)[E], int lane)
-{
-    sort_stages<E, 2>(k1, k2, lane);
-}
-
-// Does candidate (ka, na) come before (kb, nb)?  Higher exact score first,
-// then lower flat slot index.
-__device__ __forceinline__ bool before(uint64_t ka, uint32_t na, uint64_t kb, uint32_t nb)
-{
-    return ka > kb || (ka == kb && na < nb);
-}
-
-// Compare-exchange of (k, n) with lane ^ m: this lane keeps the entry of the
-// pair that comes first if keep_first, else the other one.
-__device__ __forceinline__ void ce_lane(uint64_t &k, uint32_t &n, int m, bool keep_first)
-{
-    if (m >= 16) {
-        uint64_t lk, uk;
-        uint32_t ln, un;
-        pair_vals64(k, m, lk, uk);
-        pair_vals(n, m, ln, un);
-        const bool take_lo = before(lk, ln, uk, un) == keep_first;
-        k = take_lo ? lk : uk;
-        n = take_lo ? ln : un;
-        return;
-    }
-    const uint64_t ok = dpp_xor64(k, m);
-    const uint32_t on = dpp_xor(n, m);
-    const bool mine_first = before(k, n, ok, on);
-    if (keep_first != mine_first) {
-        k = ok;
-        n = on;
-    }
-}
-
-// Sort one 64-entry column (one entry per lane) in canonical order.
-template <int KK, int J>
-__device__ __forceinline__ void col_sort_steps(uint64_t &k, uint32_t &n, int lane)
-{
-    ce_lane(k, n, J, ((lane & J) == 0) == ((lane & KK) == 0));
-    if constexpr (J > 1) col_sort_steps<KK, J / 2>(k, n, lane);
-}
-
-template <int KK>
-__device__ __forceinline__ void col_sort_stages(uint64_t &k, uint32_t &n, int lane)
-{
-    col_sort_steps<KK, KK / 2>(k, n, lane);
-    if constexpr (KK < 64) col_sort_stages<2 * KK>(k, n, lane);
-}
-
-// Bitonic clean-up of one 64-entry column: steps 32, 16, ..., 1.
-template <int J>
-__device__ __forceinline__ void col_clean(uint64_t &k, uint32_t &n, int lane)
-{
-    ce_lane(k, n, J, (lane & J) == 0);
-    if constexpr (J > 1) col_clean<J / 2>(k, n, lane);
-}
-
-__device__ __forceinline__ void col_sort(uint64_t &k, uint32_t &n, int lane)
-{
-    col_sort_stages<2>(k, n, lane);
-}
-
-// (ka, na) <- first 64 of two sorted columns, sorted.
-__device__ __forceinline__ void col_merge(uint64_t &ka, uint32_t &na, uint64_t kb, uint32_t nb,
-                                          int lane)
-{
-    const uint64_t rk = shl64(kb, 63 - lane);
-    const uint32_t rn = shl(nb, 63 - lane);
-    if (!before(ka, na, rk, rn)) {
-        ka = rk;
-        na = rn;
-    }
-    col_clean<32>(ka, na, lane);
-}
-
-// Sort one 64-entry bitonic column (falling, then rising) in canonical order.
-__device__ __forceinline__ void col_bitonic(uint64_t &k, uint32_t &n, int lane)
-{
-    col_clean<32>(k, n, lane);
-}
-
-// Pair of per-half ranks (a << 8 | b) held by `lane` in candidate column `col`
-// for a list of K, or kNoPair.  The pruned pairs (a+1)(b+1) <= K split into
-// hooks h = min(a, b): row part (h, b >= h) and column part (a > h, h), each
-// already in canonical order (scores fall along a row and down a column,
-// ties keep the lower index first).  Columns:
-//   0  (0, b), b < K                               sorted
-//   1  (a, 0), 1 <= a < K                          sorted
-//   2  hook 1: row part from lane 0 up, column
-//      part from lane 63 down                      bitonic
-//   3, 4  hooks h >= 2, concatenated               unsorted
-constexpr uint16_t kNoPair = 0xFFFF;
-
-__host__ __device__ inline uint16_t hook_pair(int K, int col, int lane)
-{
-    if (col == 0) return lane < K ? (uint16_t)lane : kNoPair;
-    if (col == 1) return lane + 1 < K ? (uint16_t)((lane + 1) << 8) : kNoPair;
-    if (col == 2) {
-        const int end = K / 2;  // hook 1 spans ranks 1 .. end-1
-        if (lane + 1 < end) return (uint16_t)((1 << 8) | (lane + 1));
-        const int a = 2 + (63 - lane);
-        if (lane > 63 - (end - 2) && a < end) return (uint16_t)((a << 8) | 1);
-        return kNoPair;
-    }
-    int idx = (col - 3) * 64 + lane;
-    for (int h = 2; (h + 1) * (h + 1) <= K; h++) {
-        const int end = K / (h + 1);
-        const int nr = end - h, nc = end - h - 1;
-        if (idx < nr) return (uint16_t)((h << 8) | (h + idx));
-        idx -= nr;
-        if (idx < nc) return (uint16_t)(((h + 1 + idx) << 8) | h);
-        idx -= nc;
-    }
-    return kNoPair;
-}
-
-// Number of pruned pairs with both ranks >= 2 (columns 3 and 4).
-__host__ __device__ inline int hook_rest(int K)
-{
-    int n = 0;
-    for (int h = 2; (h + 1) * (h + 1) <= K; h++) n += 2 * (K / (h + 1) - h) - 1;
-    return n;
-}
 
 struct SelArgs {
     const void *kp, *qp;
@@ -392,20 +104,20 @@ __device__ __forceinline__ void select_body(SelArgs a)
         const float4 m0 = init ? a.M0[jm] : make_float4(0.f, 0.f, 0.f, 0.f);
 
         // ---- stage 1: sort each half, keep the first K ----
-        uint64_t k1[E], k2[E];
+        uint64_t kk[2][E];
 #pragma unroll
         for (int r = 0; r < E; r++) {
             const int e = lane * E + r;
             if (e < S) {
                 const uint32_t inv = ~(uint32_t)e;
-                k1[r] = ((uint64_t)f2ord(load_elem(x, a.bf16, base + e)) << 32) | inv;
-                k2[r] = ((uint64_t)f2ord(load_elem(x, a.bf16, base + S + e)) << 32) | inv;
+                kk[0][r] = ((uint64_t)f2ord(load_elem(x, a.bf16, base + e)) << 32) | inv;
+                kk[1][r] = ((uint64_t)f2ord(load_elem(x, a.bf16, base + S + e)) << 32) | inv;
             } else {
-                k1[r] = 0;  // below every finite score
-                k2[r] = 0;
+                kk[0][r] = 0;  // below every finite score
+                kk[1][r] = 0;
             }
         }
-        sort_halves_desc<E>(k1, k2, lane);
+        sort_desc<2, E>(kk, lane);
         if (init) {  // the piece of M0 has arrived during the sort
             if (a.init_bf16) {
                 const uint2 u = make_uint2(bf16_bits(m0.x) | (bf16_bits(m0.y) << 16),
@@ -419,90 +131,22 @@ __device__ __forceinline__ void select_body(SelArgs a)
         for (int r = 0; r < E; r++) {
             const int e = lane * E + r;
             if (e < K) {
-                sv[wv][0][e] = ord2f((uint32_t)(k1[r] >> 32));
-                si[wv][0][e] = ~(uint32_t)k1[r];
-                sv[wv][1][e] = ord2f((uint32_t)(k2[r] >> 32));
-                si[wv][1][e] = ~(uint32_t)k2[r];
+                sv[wv][0][e] = ord2f((uint32_t)(kk[0][r] >> 32));
+                si[wv][0][e] = ~(uint32_t)kk[0][r];
+                sv[wv][1][e] = ord2f((uint32_t)(kk[1][r] >> 32));
+                si[wv][1][e] = ~(uint32_t)kk[1][r];
             }
         }
         wave_sync();
 
         // ---- stage 2: exact sums of the pruned rank pairs ----
-        uint64_t ck[E2];
-        uint32_t cn[E2];
-#pragma unroll
-        for (int r = 0; r < E2; r++) {
-            ck[r] = 0;  // empty: after every real candidate
-            cn[r] = 0xFFFFFFFFu;
-            const uint32_t ab = tabv[r];
-            if (ab != kNoPair) {
-                const int ra = (int)(ab >> 8), rb = (int)(ab & 0xFF);
-                float hi, lo;
-                two_sum(sv[wv][0][ra], sv[wv][1][rb], hi, lo);
-                ck[r] = ((uint64_t)f2ord(hi) << 32) | f2ord(lo);
-                cn[r] = si[wv][0][ra] * (uint32_t)S + si[wv][1][rb];
-            }
-        }
-        // columns 0, 1 sorted; 2 bitonic; 3, 4 unsorted (K-uniform branches)
-        if (K >= 2) col_merge(ck[0], cn[0], ck[1], cn[1], lane);
-        if (K >= 4) {
-            col_bitonic(ck[2], cn[2], lane);
-            col_merge(ck[0], cn[0], ck[2], cn[2], lane);
-        }
-        if (rest > 0) {
-            // Columns 0-2 now hold the first 64 of hooks 0 and 1, sorted.  A
-            // pair of hooks >= 2 that does not come before its K-th entry has
-            // K pairs before it and cannot be selected; the others (about 20
-            // of 92 for Gaussian scores) are compacted into one column.
-            const uint64_t tk = shl64(ck[0], K - 1);
-            const uint32_t tn = shl(cn[0], K - 1);
-            const bool s3 = before(ck[3], cn[3], tk, tn);
-            const bool s4 = (rest > 64) && before(ck[4], cn[4], tk, tn);
-            const uint64_t m3 = __ballot(s3), m4 = __ballot(s4);
-            const int n3 = __popcll(m3), tot = n3 + __popcll(m4);
-            const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-            const int r3 = __popcll(m3 & below), r4 = n3 + __popcll(m4 & below);
-            uint32_t *xh = reinterpret_cast<uint32_t *>(sv[wv][0]);
-            uint32_t *xl = reinterpret_cast<uint32_t *>(sv[wv][1]);
-            uint32_t *xn = si[wv][0];
-            // 64 survivors at a time (more than 64 is rare)
-            for (int base = 0; base < tot; base += 64) {
-                wave_sync();  // earlier reads of sv/si are done
-                if (s3 & (r3 >= base) & (r3 < base + 64)) {
-                    xh[r3 - base] = (uint32_t)(ck[3] >> 32);
-                    xl[r3 - base] = (uint32_t)ck[3];
-                    xn[r3 - base] = cn[3];
-                }
-                if (s4 & (r4 >= base) & (r4 < base + 64)) {
-                    xh[r4 - base] = (uint32_t)(ck[4] >> 32);
-                    xl[r4 - base] = (uint32_t)ck[4];
-                    xn[r4 - base] = cn[4];
-                }
-                wave_sync();
-                uint64_t sk = 0;
-                uint32_t sn = 0xFFFFFFFFu;
-                if (lane < tot - base) {
-                    sk = ((uint64_t)xh[lane] << 32) | xl[lane];
-                    sn = xn[lane];
-                }
-                col_sort(sk, sn, lane);
-                col_merge(ck[0], cn[0], sk, sn, lane);
-            }
-        }
+        uint64_t key;
+        uint32_t n;
+        select_pairs<E2>(sv[wv][0], sv[wv][1], si[wv][0], si[wv][1], tabv, K, rest, S, lane, key, n);
         wave_sync();  // sv/si are rewritten by the next item
 
         // ---- weights: softmax over the K selected scores ----
-        const uint64_t key = ck[0];
-        const uint32_t n = cn[0];
-        const float hi = ord2f((uint32_t)(key >> 32));
-        const float lo = ord2f((uint32_t)key);
-        const float hi0 = __shfl(hi, 0, 64);
-        const float lo0 = __shfl(lo, 0, 64);
-        const float ex = lane < K ? expf((hi - hi0) + (lo - lo0)) : 0.0f;
-        float z = ex;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o, 64);
-        const float w = ex / z;
+        const float w = select_weight(key, K, lane);
 
         if (a.hist != nullptr) {
             // write-slot utilisation: one count per selected slot of head h
@@ -579,6 +223,17 @@ const HookTable &hook_table(int K)
     }();
     return tables[K];
 }
+
+}  // namespace
+
+const uint16_t *hook_columns(int K, int *rest)
+{
+    const HookTable &t = hook_table(K);
+    *rest = t.rest;
+    return t.pair;
+}
+
+namespace {
 
 template <int E>
 hipError_t launch_e(const SelArgs &args, hipStream_t st)

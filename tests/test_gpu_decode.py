@@ -1,6 +1,7 @@
-"""GPU parity of the one-token step (T = 1, time-parallel variant: a single
-write-then-read kernel) against the float64 oracle run over the whole
-sequence, plus its exact properties."""
+"""GPU parity of the one-token step (T = 1, time-parallel variant: sdm_forward
+runs selection, writes and reads in one launch) against the float64 oracle
+run over the whole sequence, against the two-launch form (sdm_prepare +
+sdm_apply) bit for bit, plus its exact properties."""
 import numpy as np
 import pytest
 import torch
@@ -146,3 +147,48 @@ def test_decode_full_layer_columns():
     ref = oracle.forward(d, wl.sqrtN, wl.W, wl.R, c0=0, c1=64)
     assert_close(y[..., :64].cpu().numpy(), ref["y"], TOL, "y")
     assert_close(M[..., :64].cpu().numpy(), ref["M"], TOL, "M")
+
+
+FUSED = [
+    # (B, H, sqrtN, d_v, W, R, dtype, state, same keys for writing and reading)
+    (3, 2, 8, 20, 3, 5, "f32", "f32", False),       # sqrtN <= 64, ragged slice, W != R
+    (2, 2, 100, 96, 64, 64, "f32", "f32", False),   # 64 < sqrtN <= 128, W = R = 64
+    (1, 3, 150, 40, 17, 33, "bf16", "f32", False),  # 128 < sqrtN <= 256, bf16 inputs
+    (1, 1, 300, 36, 64, 64, "f32", "f32", False),   # 256 < sqrtN <= 512
+    (2, 2, 64, 64, 64, 64, "f32", "f32", True),     # every read's slot written by the token
+    (2, 2, 64, 128, 64, 64, "f32", "bf16", True),   # the same, bfloat16 state
+    (2, 1, 64, 160, 64, 64, "f32", "fp8", True),    # the same, E4M3 state
+    (1, 2, 32, 100, 32, 20, "bf16", "bf16", False),
+    (1, 2, 32, 100, 20, 32, "bf16", "fp8", False),
+    (64, 4, 16, 1000, 8, 8, "f32", "f32", False),   # two slices per wavefront, ragged last slice
+]
+
+
+@pytest.mark.parametrize("shape", FUSED, ids=[str(s) for s in FUSED])
+def test_fused_step_bitwise_equals_two_launches(shape):
+    """sdm_forward's one-launch step (selection inside) gives the bits of
+    sdm_prepare + sdm_apply (selection kernel, records, write/read kernel):
+    from M_0 and continuing a prefilled state."""
+    B, H, S, D, W, R, dt, st, same = shape
+    wl = si.Workload("decode", B=B, T=4, H=H, sqrtN=S, d_v=D, W=W, R=R, dtype=dt, reuse=0.3,
+                     seed=900 + S + D + W)
+    log(f"fused step: B={B} H={H} S={S} d_v={D} W={W} R={R} {dt} state={st} same={same}")
+    d = si.generate(wl)
+    if same:
+        d["qp"] = d["kp"].copy()
+    dd = upload(d)
+    state = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[st]
+    core = make_core(dd, W, R, state)
+    tok = [[dd[n][:, t:t + 1].contiguous().clone() for n in NAMES] for t in range(4)]
+    # first token from M_0 (no continuation)
+    y1, M1 = core.forward(*tok[0], variant=sdm.TIMEPAR)
+    y2, M2 = core.forward(*tok[0], variant=sdm.TIMEPAR, staged=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(M1.view(torch.uint8), M2.view(torch.uint8))
+    # three more tokens continuing the state
+    for t in range(1, 4):
+        y1, _ = core.forward(*tok[t], variant=sdm.TIMEPAR, M=M1, cont=True)
+        y2, _ = core.forward(*tok[t], variant=sdm.TIMEPAR, M=M2, cont=True, staged=True)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2), f"token {t}: y differs"
+        assert torch.equal(M1.view(torch.uint8), M2.view(torch.uint8)), f"token {t}: M differs"
