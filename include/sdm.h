@@ -200,8 +200,11 @@ sdm_status sdm_select(sdm_handle h, int B, int64_t T, const void *kp, const void
  *              M_0 (so a failed call can simply be retried); with the flag it
  *              must hold the state to continue from.
  * Outputs must not alias inputs or each other.
- * Everything runs on `stream`, in order: sdm_prepare(...) then
- * sdm_apply(...) with the same arguments.
+ * Everything runs on `stream`, with the results of sdm_prepare(...) then
+ * sdm_apply(...) with the same arguments, bit for bit.  For one token per
+ * sequence (T = 1) with the time-parallel variant the whole step is one
+ * kernel launch (after the copy of M_0 unless SDM_FLAG_CONTINUE is set) and
+ * the workspace is not touched.
  */
 sdm_status sdm_forward(sdm_handle h, int B, int64_t T, const void *kp, const void *qp,
                        const void *v, const float *alpha, const float *beta,
