@@ -44,11 +44,28 @@ SCHEDULES = {  # schedule -> (kernel source, kernels of the write/read phase)
 }
 
 
+# headers every kernel source includes: a change there changes the kernels too
+KERNEL_HEADERS = ("sdm_internal.h", "tp_device.h")
+
+
+def kernel_source_hash(schedule, root=None):
+    """sha256 over the schedule's kernel source and the headers it includes
+    (a missing file counts as changed content)."""
+    csrc = os.path.join(root or ROOT, "sparse_memory_linear_select_amd", "csrc")
+    h = hashlib.sha256()
+    for name in (SCHEDULES[schedule][0],) + KERNEL_HEADERS:
+        h.update(name.encode() + b"\0")
+        try:
+            h.update(open(os.path.join(csrc, name), "rb").read())
+        except OSError:
+            h.update(b"<missing>")
+    return h.hexdigest()
+
+
 def _traffic(wl, schedule, state="f32"):
     """Counter-measured HBM bytes of the write/read phase per step, if a
     committed summary exists for this workload, schedule and state type and
     the kernel source is unchanged since the counters were taken; else None."""
-    src_name = SCHEDULES[schedule][0]
     tag = schedule.replace("-", "_") + "__" + wl.name.replace(" ", "_")
     if state != "f32":
         tag += f"__{state}_state"
@@ -57,9 +74,7 @@ def _traffic(wl, schedule, state="f32"):
         return None
     try:
         rec = json.load(open(path))
-        src = open(os.path.join(ROOT, "sparse_memory_linear_select_amd", "csrc", src_name),
-                   "rb").read()
-        if rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
+        if rec.get("source_sha256") != kernel_source_hash(schedule):
             return None
         return float(rec["hbm_bytes_per_step"])
     except Exception:
@@ -304,15 +319,13 @@ def counters_summary(args, wl):
         steps = sum(len(vals[(k, "FETCH_SIZE")]) for k in rw)
     fetch = sum(sum(vals[(k, "FETCH_SIZE")]) for k in rw) * 1024 * fscale / steps
     write = sum(sum(vals[(k, "WRITE_SIZE")]) for k in rw) * 1024 * wscale / steps
-    src_name = SCHEDULES[schedule][0]
-    src = open(os.path.join(ROOT, "sparse_memory_linear_select_amd", "csrc", src_name), "rb").read()
     tag = schedule.replace("-", "_") + "__" + wl.name.replace(" ", "_")
     if args.state != "f32":
         tag += f"__{args.state}_state"
     rec = {"schedule": schedule, "workload": wl.name, "kernels": rw,
            "hbm_bytes_per_step": fetch + write, "fetch_bytes": fetch, "write_bytes": write,
            "fetch_scale": fscale, "write_scale": wscale, "steps_in_run": steps,
-           "source_sha256": hashlib.sha256(src).hexdigest()}
+           "source_sha256": kernel_source_hash(schedule)}
     path = os.path.join(ROOT, "profiles", f"traffic_{tag}.json")
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)

@@ -38,7 +38,7 @@
 namespace sdm {
 namespace {
 
-constexpr int kLPR = StateRow<kStateF32>::kLPR;  // 8 lanes x float4 per 128-byte row slice
+constexpr int kLPR = 8;  // dv reduction: 8 lanes x float4 per 128-byte column slice
 constexpr int kRPI = 64 / kLPR;
 constexpr int kDots = 3 * kMaxK;  // per (chain, token): da[64], dc[64], dq[64]
 

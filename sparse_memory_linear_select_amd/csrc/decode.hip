@@ -23,13 +23,14 @@ struct DecArgs {
     int64_t chains;
 };
 
-// Lanes per row slice: the state's 128-byte slice, except for an E4M3 state,
-// whose 128 bytes take 32 lanes; there 16 lanes (64 bytes) keep 4 row groups
-// and at most 16 references per group in registers.
+// Lanes per row slice: 128 bytes for a float32 or bfloat16 state (8 or 16
+// lanes: for one token, more and smaller slices spread the gathers over more
+// compute units); 16 lanes (64 bytes) for an E4M3 state, so that a wave
+// keeps 4 row groups and at most 16 references per group in registers.
 template <int ST>
 constexpr int dec_lpr()
 {
-    return ST == kStateFP8 ? 16 : StateRow<ST>::kLPR;
+    return ST == kStateF32 ? 8 : 16;
 }
 
 template <bool BF16, int ST, int NK>

@@ -336,9 +336,9 @@ __global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int str
 
 // ------------------------------------------------------------------ read
 
-// Float32 state.  One wavefront per (chain, token of the epoch, 128-byte row
+// Float32 state.  One wavefront per (chain, token of the epoch, 256-byte row
 // slice).  With the read plan, y_t = sum_r w_r row_r + sum_j u_j v_(t_j): the
-// 8 row groups take their NR reads at once (epoch-start rows), then the
+// 4 row groups take their NR reads at once (epoch-start rows), then the
 // token's v pairs kPairBatch per group at a time.  Every load depends only on
 // the plan, so all of them can be in flight together; reads that overflowed
 // the plan replay their writes from the sorted events.
@@ -678,8 +678,8 @@ __global__ __launch_bounds__(64 * (WPU > 4 ? WPU : 4)) void tp_read_stored_kerne
 
 // ------------------------------------------------------------------ update
 
-// One wavefront per (chain, block of kRPI*SPG sorted write events, 128-byte
-// row slice); each row group takes SPG consecutive events.  With `rev` the
+// One wavefront per (chain, block of kRPI*SPG sorted write events, row
+// slice); each row group takes SPG consecutive events.  With `rev` the
 // chains are taken last to first: the read kernel before it (or the previous
 // update) ends on the last chains, whose rows may still sit in the
 // memory-side cache (measured: 8.18 -> 8.04 ms write/read per 1.4B-style

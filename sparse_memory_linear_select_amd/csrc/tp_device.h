@@ -38,11 +38,14 @@ __device__ __forceinline__ float4 fma4(float a, float4 x, float c, float4 v)
 }
 
 // Row storage of the state.  Every lane holds 4 columns of a row; a row
-// slice is the 128 bytes that kLPR lanes cover (the fabric's request size).
-//   float32 state: 8 lanes x 16 bytes;
-//   bfloat16 state: 16 lanes x 8 bytes, widened exactly on load, rounded to
-//   nearest-even after every write (the value the state holds);
-//   E4M3 state: 32 lanes x 4 bytes, codes of the values scaled by 2^-s,
+// slice is what the kLPR lanes of a row group cover:
+//   float32 state: 16 lanes x 16 bytes = 256 bytes (against 8 lanes and
+//   128 bytes: write/read 7.12 -> 6.82 ms at the 1.4B-style layer, 29.36 ->
+//   27.56 ms at the 8B-style layer; 32 lanes for the update alone, 6.88);
+//   bfloat16 state: 16 lanes x 8 bytes = 128 bytes (32 lanes: slower, 5.65
+//   -> 5.76 ms), widened exactly on load, rounded to nearest-even after
+//   every write (the value the state holds);
+//   E4M3 state: 32 lanes x 4 bytes = 128 bytes, codes of the values scaled by 2^-s,
 //   decoded exactly and scaled by 2^s on load, encoded (nearest-even,
 //   saturating) after every write.
 // An object carries the scale (sc = 2^s, isc = 2^-s; unused by the other
@@ -52,7 +55,7 @@ struct StateRow;
 
 template <>
 struct StateRow<kStateF32> {
-    static constexpr int kLPR = 8;
+    static constexpr int kLPR = 16;
     static constexpr uint32_t kElem = 4;
     using Raw = float4;
     __device__ StateRow(float, float) {}

@@ -29,11 +29,9 @@ def test_traffic_matches_the_committed_summary():
     rec = json.load(open(os.path.join(ROOT, "profiles",
                                       "traffic_time_parallel__1.4B-style_layer.json")))
     got = bench._traffic(wl, "time-parallel")
-    # null exactly when the kernel source changed since the counters were taken
-    src = open(os.path.join(ROOT, "sparse_memory_linear_select_amd", "csrc", "rw_timepar.hip"),
-               "rb").read()
-    import hashlib
-    if hashlib.sha256(src).hexdigest() == rec["source_sha256"]:
+    # null exactly when the kernel source (or a header it includes) changed
+    # since the counters were taken
+    if bench.kernel_source_hash("time-parallel") == rec["source_sha256"]:
         assert got == pytest.approx(rec["hbm_bytes_per_step"])
         # counted bytes are below the algorithmic bytes (merged writes, L2 hits)
         alg = wl.head_tokens * (2 * wl.W + wl.R) * wl.d_v * 4
@@ -43,6 +41,8 @@ def test_traffic_matches_the_committed_summary():
 
 
 def test_traffic_is_null_for_a_changed_source(tmp_path, monkeypatch):
+    import shutil
+
     wl = si.WORKLOADS[1]
     fake = tmp_path / "repo"
     (fake / "profiles").mkdir(parents=True)
@@ -50,9 +50,20 @@ def test_traffic_is_null_for_a_changed_source(tmp_path, monkeypatch):
     rec = json.load(open(os.path.join(ROOT, "profiles",
                                       "traffic_time_parallel__1.4B-style_layer.json")))
     (fake / "profiles" / "traffic_time_parallel__1.4B-style_layer.json").write_text(json.dumps(rec))
-    (fake / "sparse_memory_linear_select_amd" / "csrc" / "rw_timepar.hip").write_text("changed")
+    csrc = os.path.join(ROOT, "sparse_memory_linear_select_amd", "csrc")
+    for name in ("rw_timepar.hip",) + bench.KERNEL_HEADERS:
+        shutil.copy(os.path.join(csrc, name), fake / "sparse_memory_linear_select_amd" / "csrc")
     monkeypatch.setattr(bench, "ROOT", str(fake))
-    assert bench._traffic(wl, "time-parallel") is None
+    # the committed record holds for a copy of the sources iff it holds here
+    assert (bench._traffic(wl, "time-parallel") is None) == (
+        bench.kernel_source_hash("time-parallel", ROOT) != rec["source_sha256"])
+    # a changed header voids it, as a changed kernel source does
+    for name in ("tp_device.h", "rw_timepar.hip"):
+        p = fake / "sparse_memory_linear_select_amd" / "csrc" / name
+        keep = p.read_bytes()
+        p.write_bytes(keep + b"// changed")
+        assert bench._traffic(wl, "time-parallel") is None
+        p.write_bytes(keep)
     assert bench._traffic(si.WORKLOADS[2], "token-serial") is None  # no summary at all
 
 
@@ -89,8 +100,9 @@ def test_counters_summary_calibrates_with_the_device_copy(tmp_path, monkeypatch,
     fake = tmp_path / "repo"
     (fake / "profiles").mkdir(parents=True)
     (fake / "sparse_memory_linear_select_amd" / "csrc").mkdir(parents=True)
-    shutil.copy(os.path.join(ROOT, "sparse_memory_linear_select_amd", "csrc", "rw_timepar.hip"),
-                fake / "sparse_memory_linear_select_amd" / "csrc" / "rw_timepar.hip")
+    for name in ("rw_timepar.hip",) + bench.KERNEL_HEADERS:
+        shutil.copy(os.path.join(ROOT, "sparse_memory_linear_select_amd", "csrc", name),
+                    fake / "sparse_memory_linear_select_amd" / "csrc" / name)
     monkeypatch.setattr(bench, "ROOT", str(fake))
     wl = si.WORKLOADS[1]  # 16 epochs per step
     rows = []
