@@ -102,13 +102,22 @@ def d2d_copy_gbs(dev, nbytes=1 << 30, reps=5):
 
 
 def _cpu_model() -> str:
+    """The host CPU as /proc/cpuinfo names it, with its family, model and
+    stepping numbers (virtual machines often give only a short name)."""
+    info = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = (x.strip() for x in line.split(":", 1))
+                if k in ("model name", "cpu family", "model", "stepping") and k not in info:
+                    info[k] = v
+            elif info:
+                break  # end of the first processor's block
     except OSError:
         pass
-    return "unknown"
+    name = info.get("model name", "unknown")
+    ids = [f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info]
+    return f"{name} ({', '.join(ids)})" if ids else name
 
 
 def cpu_baseline(d, wl, seqs, T=None, state="f32", threads=None, runs=5):
