@@ -273,7 +273,10 @@ def _short_kernel(name: str) -> str:
         depth += ch == "<"
         depth -= ch == ">"
         out.append(ch)
-    return "".join(out).strip()
+    short = "".join(out).strip()
+    if len(short) > 100:  # a library kernel's long template arguments
+        short = short[:short.index("<")] + "<...>" if "<" in short else short[:100] + "..."
+    return short
 
 
 def counters_summary(args, wl):
