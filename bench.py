@@ -444,6 +444,36 @@ def measure_forward(wl, d, dev, state, variant, steps, warmup):
     rw = [e[1].elapsed_time(e[2]) for e in ev]
     prep = [e[0].elapsed_time(e[1]) for e in ev]
     staged_ms = ev[0][0].elapsed_time(ev[-1][2]) / steps
+
+    # third pass, the preparation split: sdm_prepare continuing the state (no
+    # M <- M0) and sdm_select alone (the same selection, written in the API
+    # layout instead of token records)
+    Kw = torch.empty((B, T, H, wl.W), dtype=torch.float32, device=dev)
+    Kr = torch.empty((B, T, H, wl.R), dtype=torch.float32, device=dev)
+    Iw = torch.empty((B, T, H, wl.W), dtype=torch.int32, device=dev)
+    Ir = torch.empty((B, T, H, wl.R), dtype=torch.int32, device=dev)
+
+    def prepare_cont():
+        sdm._check(L.sdm_prepare(core._h, B, T, P(dd["kp"]), P(dd["qp"]), P(dd["alpha"]),
+                                 P(dd["beta"]), dt_code, variant, sdm.FLAG_CONTINUE, P(ws), ws_n,
+                                 P(M), sp))
+
+    def select():
+        sdm._check(L.sdm_select(core._h, B, T, P(dd["kp"]), P(dd["qp"]), dt_code, P(Iw), P(Kw),
+                                P(Ir), P(Kr), sp))
+
+    ev3 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in ev3:
+        e[0].record(stream)
+        prepare_cont()
+        e[1].record(stream)
+        select()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    prep_cont = sum(e[0].elapsed_time(e[1]) for e in ev3) / steps
+    sel_ms = sum(e[1].elapsed_time(e[2]) for e in ev3) / steps
+    del Kw, Kr, Iw, Ir
     rw_ms = sum(rw) / steps
     ht = wl.head_tokens
     row_bytes = ht * (2 * wl.W + wl.R) * wl.d_v * esz  # algorithmic row traffic per step
@@ -453,6 +483,8 @@ def measure_forward(wl, d, dev, state, variant, steps, warmup):
         "ms_per_step": ms_step, "ms_per_step_median": statistics.median(per_step),
         "head_tokens_per_s": ht / (ms_step * 1e-3),
         "staged_ms_per_step": staged_ms, "prepare_ms": sum(prep) / steps,
+        "init_ms": sum(prep) / steps - prep_cont, "select_ms": sel_ms,
+        "sort_plan_ms": prep_cont - sel_ms,
         "write_read_ms": rw_ms, "write_read_ms_median": statistics.median(rw),
         "schedule": schedule, "row_bytes": row_bytes, "wall_s_timed": wall,
         "effective_gbs": row_bytes / (rw_ms * 1e-3) / 1e9,
@@ -465,6 +497,15 @@ def measure_forward(wl, d, dev, state, variant, steps, warmup):
     return out
 
 
+def _prepare_split(m):
+    """init = prepare - prepare continuing the state (the marginal cost of
+    M <- M0, which the selection carries where it can); select = sdm_select
+    alone; sort + plan = the rest of the continuing prepare."""
+    return {"init": m["init_ms"], "select": m["select_ms"], "sort + plan": m["sort_plan_ms"],
+            "note": "init and sort + plan are differences of timed calls; select writes the "
+                    "API layout rather than token records"}
+
+
 def _workload_record(wl, m, cpu):
     """One workload's figures for the `workloads` object of the JSON line."""
     return {
@@ -473,6 +514,7 @@ def _workload_record(wl, m, cpu):
         "schedule": m["schedule"],
         "head_tokens_per_s": m["head_tokens_per_s"], "ms_per_step": m["ms_per_step"],
         "ms_per_step_median": m["ms_per_step_median"], "prepare_ms": m["prepare_ms"],
+        "prepare_split_ms": _prepare_split(m),
         "write_read_ms": m["write_read_ms"], "algorithmic_row_bytes": m["row_bytes"],
         "effective_gbs": m["effective_gbs"], "frac": m["effective_gbs"] / PEAK_HBM_GBS,
         "traffic": m["traffic"], "hbm_gbs_counted": m["hbm_gbs_counted"],
@@ -603,6 +645,7 @@ def main():
         "row_gbs_whole_step": m["row_gbs_whole_step"],
         "breakdown_ms": {"staged step (prepare + apply, one stream)": m["staged_ms_per_step"],
                          "prepare (init+select+sort+plan)": m["prepare_ms"],
+                         "prepare split": _prepare_split(m),
                          "write+read": m["write_read_ms"],
                          "write+read median": m["write_read_ms_median"]},
         "wall_s_timed": m["wall_s_timed"],
