@@ -142,9 +142,10 @@ hipError_t launch_state(const Shape &s, const DecArgs &a, bool bf16, hipStream_t
 // (list 1); of each list's two wavefronts one merges the pairs of hooks 0
 // and 1 while the other sorts those of hooks >= 2, and the first merges the
 // two and takes the softmax; the write coefficients a = alpha(1 - beta k),
-// c = beta k go to LDS with the slots.  Wavefronts 0 and 1 then take a row
-// slice each, as the two-launch kernel does, but gather the written and the
-// read rows at once; while the gathers are in flight every wavefront looks
+// c = beta k go to LDS with the slots.  Then 1, 2 or 4 of the wavefronts
+// (as many as keep about one workgroup per compute unit) take a row slice
+// each, as the two-launch kernel does, but gather the written and the read
+// rows at once; while the gathers are in flight every wavefront looks
 // for reads whose slot the token also writes, and such a read takes the new
 // row from the LDS copy of the rows its wavefront just wrote (the stored
 // values), so no gather waits on the stores.  Every workgroup of a chain
@@ -159,7 +160,8 @@ struct DecFArgs {
     float ssc, sisc;  // E4M3 state: 2^s, 2^-s
     int64_t N;
     int sqrtN, d_v, W, R, bf16;
-    int nslice, groups, spw;  // row slices per chain; workgroups per chain; slices per wavefront
+    int nslice, groups;  // row slices per chain; workgroups per chain
+    int rw, spw;         // wavefronts per workgroup that take row slices (1, 2 or 4); slices each
     uint16_t tab[2][kTabMax];
     int tabn[2];
 };
@@ -178,7 +180,7 @@ __global__ __launch_bounds__(256) void rw_decode_fused_kernel(DecFArgs a)
     __shared__ uint32_t rsl_s[kMaxK];
     __shared__ float wa_s[kMaxK], wc_s[kMaxK], rq_s[kMaxK];
     __shared__ int rmatch_s[kMaxK];
-    __shared__ Raw wrow[2][kMaxK][kLPR];  // rows wavefronts 0 and 1 wrote, as stored
+    __shared__ Raw wrow[4][kMaxK][kLPR];  // rows each row wavefront wrote, as stored
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int list = wv >> 1, half = wv & 1;
@@ -283,7 +285,7 @@ __global__ __launch_bounds__(256) void rw_decode_fused_kernel(DecFArgs a)
     }
     __syncthreads();
 
-    // ---- writes and reads: wavefronts 0 and 1 take row slices ----
+    // ---- writes and reads: wavefronts 0 .. rw-1 take row slices ----
     const int g = lane / kLPR, q = lane % kLPR;
     const rsrc_t Mr = make_rsrc(static_cast<char *>(a.M) + (int64_t)chain * a.N * a.d_v * S::kElem,
                                 (uint32_t)(a.N * a.d_v * S::kElem));
@@ -306,8 +308,8 @@ __global__ __launch_bounds__(256) void rw_decode_fused_kernel(DecFArgs a)
     // gathers of one slice: the written rows and every read row
     Raw old[NK], row[NK];
     float4 vv = make_float4(0.f, 0.f, 0.f, 0.f);
-    int slice = grp * a.spw * 2 + wv;
-    bool have = wv < 2 && slice < a.nslice;
+    int slice = grp * a.spw * a.rw + wv;
+    bool have = wv < a.rw && slice < a.nslice;
     auto gather = [&](int sl) {
         const int col = sl * 4 * kLPR + q * 4;
         const bool col_ok = col < a.d_v;
@@ -350,7 +352,7 @@ __global__ __launch_bounds__(256) void rw_decode_fused_kernel(DecFArgs a)
         if ((lane & 3) == 0 && i < a.R) rmatch_s[i] = m;
     }
     __syncthreads();
-    if (wv >= 2) return;
+    if (wv >= a.rw) return;
     int rm[NK];
 #pragma unroll
     for (int i = 0; i < NK; i++) {
@@ -392,10 +394,26 @@ __global__ __launch_bounds__(256) void rw_decode_fused_kernel(DecFArgs a)
         if (g == 0 && col_ok)
             *reinterpret_cast<float4 *>(a.y + (int64_t)chain * a.d_v + col) = acc;
         if (++u >= a.spw) break;
-        slice = (grp * a.spw + u) * 2 + wv;
+        slice = (grp * a.spw + u) * a.rw + wv;
         have = slice < a.nslice;
         if (have) gather(slice);
     }
+}
+
+// Compute units of the current device (looked up once per device).
+int compute_units()
+{
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 template <int ST>
@@ -404,12 +422,19 @@ hipError_t launch_fused_state(const Shape &s, DecFArgs &a, hipStream_t st)
     constexpr int kLPR = dec_lpr<ST>();
     a.nslice = (s.d_v + 4 * kLPR - 1) / (4 * kLPR);
     const int64_t chains = (int64_t)s.B * s.H;
-    // two slices per workgroup (one per row wavefront), unless that makes
-    // more than 1024 workgroups (each repeats its chain's selection)
+    // Every workgroup repeats its chain's selection, so a compute unit that
+    // holds two of them takes twice as long over it: about one workgroup per
+    // compute unit, with 1, 2 or 4 of its wavefronts taking row slices (more
+    // workgroups per chain spread the gathers over more compute units), and
+    // more slices per wavefront only beyond that.
+    const int cus = compute_units();
+    const int64_t per = (int64_t)cus;
+    a.rw = chains * a.nslice <= per ? 1 : (chains * ((a.nslice + 1) / 2) <= per ? 2 : 4);
     int spw = 1;
-    while (chains * ((a.nslice + 2 * spw - 1) / (2 * spw)) > 1024 && 2 * spw < a.nslice) spw *= 2;
+    while (chains * ((a.nslice + a.rw * spw - 1) / (a.rw * spw)) > per && a.rw * spw < a.nslice)
+        spw *= 2;
     a.spw = spw;
-    a.groups = (a.nslice + 2 * spw - 1) / (2 * spw);
+    a.groups = (a.nslice + a.rw * spw - 1) / (a.rw * spw);
     const int64_t blocks = chains * a.groups;
     if (blocks >= (int64_t)1 << 31) return hipErrorInvalidValue;
     const dim3 grid((unsigned)blocks);

@@ -160,7 +160,9 @@ FUSED = [
     (2, 1, 64, 160, 64, 64, "f32", "fp8", True),    # the same, E4M3 state
     (1, 2, 32, 100, 32, 20, "bf16", "bf16", False),
     (1, 2, 32, 100, 20, 32, "bf16", "fp8", False),
-    (64, 4, 16, 1000, 8, 8, "f32", "f32", False),   # two slices per wavefront, ragged last slice
+    (64, 4, 16, 1000, 8, 8, "f32", "f32", False),   # four row waves, several slices each, ragged
+    (8, 4, 16, 512, 16, 16, "f32", "f32", False),   # two row waves per workgroup (256 CUs)
+    (8, 4, 16, 2048, 16, 16, "f32", "fp8", True),   # four row waves, E4M3
 ]
 
 
