@@ -9,6 +9,8 @@
 #include "select_device.h"
 #include "tp_device.h"
 
+#include <atomic>
+
 namespace sdm {
 namespace {
 
@@ -400,20 +402,21 @@ __global__ __launch_bounds__(256) void rw_decode_fused_kernel(DecFArgs a)
     }
 }
 
-// Compute units of the current device (looked up once per device).
+// Compute units of the current device (looked up once per device; threads
+// that race here store the same value).
 int compute_units()
 {
-    static int cached[64];
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cached[dev]) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             n <= 0)
             n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 template <int ST>
