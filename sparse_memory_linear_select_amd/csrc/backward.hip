@@ -363,8 +363,11 @@ __global__ __launch_bounds__(256) void bwd_scalar_kernel(BwdArgs a, const float 
                                                          const float *beta, float *dkp, float *dqp,
                                                          float *dalpha, float *dbeta, int64_t n_ht)
 {
-    __shared__ uint32_t sn[4][kMaxK];
-    __shared__ float sd[4][kMaxK];
+    // the halves' indices i, j of each selected slot (~0 past K) and its
+    // score gradient, read back 4 at a time
+    __shared__ __align__(16) uint32_t s1[4][kMaxK];
+    __shared__ __align__(16) uint32_t s2[4][kMaxK];
+    __shared__ __align__(16) float sd[4][kMaxK];
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     const int S2 = 2 * a.sqrtN;
@@ -413,7 +416,11 @@ __global__ __launch_bounds__(256) void bwd_scalar_kernel(BwdArgs a, const float 
 #pragma unroll
         for (int m = 32; m > 0; m >>= 1) sw += __shfl_xor(sw, m, 64);
         const float ds = on ? wgt * (dw - sw) : 0.f;
-        sn[wv][lane] = on ? slot : 0xFFFFFFFFu;
+        // slot n = i*sqrtN + j: one division per selected slot, not one per
+        // (slot, column) pair below
+        const uint32_t si = slot / (uint32_t)a.sqrtN;
+        s1[wv][lane] = on ? si : 0xFFFFFFFFu;
+        s2[wv][lane] = on ? slot - si * (uint32_t)a.sqrtN : 0xFFFFFFFFu;
         sd[wv][lane] = ds;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -422,11 +429,16 @@ __global__ __launch_bounds__(256) void bwd_scalar_kernel(BwdArgs a, const float 
         for (int x = lane; x < S2; x += 64) {  // x < sqrtN: first half index i; else j
             const bool first = x < a.sqrtN;
             const uint32_t want = first ? (uint32_t)x : (uint32_t)(x - a.sqrtN);
+            const uint4 *part = reinterpret_cast<const uint4 *>(first ? s1[wv] : s2[wv]);
+            const float4 *dsv = reinterpret_cast<const float4 *>(sd[wv]);
             float acc = 0.f;
-            for (int k = 0; k < K; k++) {
-                const uint32_t sl = sn[wv][k];
-                const uint32_t part = first ? sl / (uint32_t)a.sqrtN : sl % (uint32_t)a.sqrtN;
-                if (part == want) acc += sd[wv][k];
+            for (int k4 = 0; k4 < (K + 3) / 4; k4++) {  // in slot order: a deterministic sum
+                const uint4 p = part[k4];
+                const float4 g = dsv[k4];
+                if (p.x == want) acc += g.x;
+                if (p.y == want) acc += g.y;
+                if (p.z == want) acc += g.z;
+                if (p.w == want) acc += g.w;
             }
             out[x] = acc;
         }
