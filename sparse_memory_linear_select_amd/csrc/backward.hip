@@ -33,6 +33,7 @@
 // reconstruction without division).  Dot products are reduced over column
 // slices, dv over the W writes of a token, in fixed orders: results are
 // deterministic.
+#include "lane_ops.h"
 #include "tp_device.h"
 
 namespace sdm {
@@ -64,13 +65,6 @@ __device__ __forceinline__ float dot4(float4 a, float4 b)
     return fmaf(a.x, b.x, fmaf(a.y, b.y, fmaf(a.z, b.z, a.w * b.w)));
 }
 
-// Sum over the kLPR lanes of a row group (fixed butterfly order).
-__device__ __forceinline__ float group_sum(float x)
-{
-#pragma unroll
-    for (int m = 1; m < kLPR; m <<= 1) x += __shfl_xor(x, m, 64);
-    return x;
-}
 
 // Segment starts of every (chain, epoch): positions p of the merged sorted
 // list where the slot changes, compacted in order (a block-wide scan), and
@@ -128,7 +122,7 @@ constexpr int kColsPerWave = 256;
 __device__ __forceinline__ float wave_sum(float x)
 {
 #pragma unroll
-    for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
+    for (int m = 1; m < 64; m <<= 1) x = xor_add(x, m);
     return x;
 }
 
@@ -315,10 +309,10 @@ __global__ __launch_bounds__(256) void bwd_dv_kernel(BwdArgs a, int ep, float *d
     }
 #pragma unroll
     for (int m = kLPR; m < 64; m <<= 1) {
-        acc.x += __shfl_xor(acc.x, m, 64);
-        acc.y += __shfl_xor(acc.y, m, 64);
-        acc.z += __shfl_xor(acc.z, m, 64);
-        acc.w += __shfl_xor(acc.w, m, 64);
+        acc.x = xor_add(acc.x, m);
+        acc.y = xor_add(acc.y, m);
+        acc.z = xor_add(acc.z, m);
+        acc.w = xor_add(acc.w, m);
     }
     const int64_t b = (uint32_t)chain / (uint32_t)a.H;  // chains < 2^32 (grid y and z)
     const int h = (int)(chain - b * a.H);
@@ -399,8 +393,8 @@ __global__ __launch_bounds__(256) void bwd_scalar_kernel(BwdArgs a, const float 
             float sb = on ? wgt * (dc - al * da) : 0.f;
 #pragma unroll
             for (int m = 32; m > 0; m >>= 1) {
-                sa += __shfl_xor(sa, m, 64);
-                sb += __shfl_xor(sb, m, 64);
+                sa = xor_add(sa, m);
+                sb = xor_add(sb, m);
             }
             if (lane == 0) {
                 dalpha[ht] = sa;
@@ -414,7 +408,7 @@ __global__ __launch_bounds__(256) void bwd_scalar_kernel(BwdArgs a, const float 
         // softmax backward: ds = w (dw - <w, dw>)
         float sw = wgt * dw;
 #pragma unroll
-        for (int m = 32; m > 0; m >>= 1) sw += __shfl_xor(sw, m, 64);
+        for (int m = 32; m > 0; m >>= 1) sw = xor_add(sw, m);
         const float ds = on ? wgt * (dw - sw) : 0.f;
         // slot n = i*sqrtN + j: one division per selected slot, not one per
         // (slot, column) pair below
