@@ -446,25 +446,46 @@ __global__ __launch_bounds__(256) void bwd_scalar_kernel(BwdArgs a, const float 
 __global__ __launch_bounds__(256) void bwd_dm0_kernel(const float *G, float *dM0, int B,
                                                       int64_t per_b)
 {
+    // per_b = H*N*d_v is a multiple of 4 (d_v % 4 == 0): float4 accesses
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < per_b; i += stride) {
-        float acc = 0.f;
-        for (int b = 0; b < B; b++) acc += G[(int64_t)b * per_b + i];
-        dM0[i] = acc;
+    const int64_t n4 = per_b >> 2;
+    const float4 *G4 = reinterpret_cast<const float4 *>(G);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int b = 0; b < B; b++) {
+            const float4 g = G4[(int64_t)b * n4 + i];
+            acc.x += g.x;
+            acc.y += g.y;
+            acc.z += g.z;
+            acc.w += g.w;
+        }
+        reinterpret_cast<float4 *>(dM0)[i] = acc;
     }
 }
 
 __global__ __launch_bounds__(256) void bwd_fill_kernel(float *x, int64_t n, float value)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    const int64_t n4 = n >> 2;
+    float4 *x4 = reinterpret_cast<float4 *>(x);
+    const float4 v4 = make_float4(value, value, value, value);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+        x4[i] = v4;
+    for (int64_t i = (n4 << 2) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
         x[i] = value;
 }
 
+// dst <- src, n floats; float4 accesses (the callers' buffers are 16-byte
+// aligned), then the tail.
 __global__ __launch_bounds__(256) void bwd_copy_kernel(const float *src, float *dst, int64_t n)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    const int64_t n4 = n >> 2;
+    const float4 *s4 = reinterpret_cast<const float4 *>(src);
+    float4 *d4 = reinterpret_cast<float4 *>(dst);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+        d4[i] = s4[i];
+    for (int64_t i = (n4 << 2) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
         dst[i] = src[i];
 }
 
