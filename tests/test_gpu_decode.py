@@ -134,11 +134,13 @@ def test_decode_leaves_unselected_rows():
     assert not torch.equal(M[~keep], M_before[~keep])
 
 
-def test_decode_full_layer_columns():
-    """The 1.4B-style layer (8 sequences, 4 heads, 16,384 slots of 512
-    columns, W = R = 64): 16 prefill tokens, then 4 one-token steps; y and M
-    of the first 64 columns against the oracle."""
-    wl = si.WORKLOADS[1]
+@pytest.mark.parametrize("cfg", [1, 3, 4], ids=["1.4B-style", "8B-style", "long-context"])
+def test_decode_full_layer_columns(cfg):
+    """A full layer shape (1.4B-style: 8 sequences x 4 heads, 16,384 slots of
+    512 columns; 8B-style: 65,536 slots of 1,024; long-context: one sequence,
+    262,144 slots of 2,048, bf16 inputs; W = R = 64): 16 prefill tokens, then
+    4 one-token steps; y and M of the first 64 columns against the oracle."""
+    wl = si.WORKLOADS[cfg]
     T = 20
     log(f"decode full layer: {wl.name} T={T}")
     d = si.generate(wl, T=T)
