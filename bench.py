@@ -150,16 +150,17 @@ def cpu_baseline(d, wl, seqs, T=None, state="f32", threads=None, runs=5):
                       f"recurrence, median of {runs} runs: {dt:.3f} s"}
 
 
-def decode(args, wl):
-    """Decode: B sequences advance by one token per call (T = 1), continuing
-    from the state left by a 256-token prefill.  Reports the step latency."""
+def measure_decode(wl, steps, warm, variant="auto"):
+    """B sequences advance by one token per call (T = 1), continuing from the
+    state left by a 256-token prefill: the step latency issued eagerly and
+    replayed from a captured HIP graph."""
     import numpy as np
     import torch
 
     import sdm_inputs as si
     import sparse_memory_linear_select_amd as sdm
 
-    prefix, steps, warm = 256, args.steps * 20, args.warmup * 5
+    prefix = 256
     d = si.generate(wl, T=prefix + warm + steps)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -172,7 +173,7 @@ def decode(args, wl):
     core = sdm.SDM(up(d["M0"]), wl.W, wl.R)
     names = ("kp", "qp", "v", "alpha", "beta")
     pre = [up(d[n][:, :prefix]) for n in names]
-    var = {"auto": sdm.AUTO, "serial": sdm.SERIAL, "timepar": sdm.TIMEPAR}[args.variant]
+    var = {"auto": sdm.AUTO, "serial": sdm.SERIAL, "timepar": sdm.TIMEPAR}[variant]
     _, M = core.forward(*pre, variant=var)
     toks = [[up(d[n][:, t:t + 1]) for n in names] for t in range(prefix, prefix + warm + steps)]
     dt_code = sdm.BF16 if wl.dtype == "bf16" else sdm.F32
@@ -201,14 +202,26 @@ def decode(args, wl):
     e1.record()
     torch.cuda.synchronize()
     us_graph = e0.elapsed_time(e1) * 1e3 / steps
+    schedule = sdm.variant_name(core, wl.B, 1, dt_code, var)
+    del g, toks, pre, M, ws, y, core
+    torch.cuda.empty_cache()
+    return {"us_per_step": us, "graph_replay_us_per_step": us_graph, "steps": steps,
+            "warmup": warm, "prefill_tokens": prefix, "schedule": schedule}
+
+
+def decode(args, wl):
+    """Decode: B sequences advance by one token per call (T = 1), continuing
+    from the state left by a 256-token prefill.  Reports the step latency."""
+    r = measure_decode(wl, args.steps * 20, args.warmup * 5, args.variant)
     print(json.dumps({
         "metric": "SDM decode step latency (one token for each of B sequences, state continued)",
-        "value": us, "unit": "us/step", "higher_is_better": False, "n_gpus": 1, "steps": steps,
-        "warmup": warm, "head_tokens_per_s": wl.B * wl.H / (us * 1e-6),
-        "graph_replay_us_per_step": us_graph,
+        "value": r["us_per_step"], "unit": "us/step", "higher_is_better": False, "n_gpus": 1,
+        "steps": r["steps"], "warmup": r["warmup"],
+        "head_tokens_per_s": wl.B * wl.H / (r["us_per_step"] * 1e-6),
+        "graph_replay_us_per_step": r["graph_replay_us_per_step"],
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "sqrtN": wl.sqrtN, "d_v": wl.d_v,
-                   "W": wl.W, "R": wl.R, "prefill_tokens": prefix,
-                   "schedule": sdm.variant_name(core, wl.B, 1, dt_code, var)},
+                   "W": wl.W, "R": wl.R, "prefill_tokens": r["prefill_tokens"],
+                   "schedule": r["schedule"]},
         "data": "synthetic (seeded; recipe in sdm_inputs.py)"}), flush=True)
 
 
@@ -601,6 +614,18 @@ def main():
             cpu1[wl.name] = cpu_baseline(d, wl, 1, min(wl.T, 1024), args.state, threads=1, runs=3)
     del d
 
+    dec = None
+    if not args.no_workloads and args.variant == "auto" and args.state == "f32":
+        _log("decode steps")
+        r = measure_decode(wl, 200, 10)
+        dec = {"workload": wl.name, "B": wl.B, "eager_us_per_step": r["us_per_step"],
+               "graph_replay_us_per_step": r["graph_replay_us_per_step"],
+               "steps": r["steps"], "prefill_tokens": r["prefill_tokens"],
+               "note": "one token for each of B sequences per call, state continued; "
+                       "sdm_forward with T = 1 (one launch)"}
+        _log(f"  {r['graph_replay_us_per_step']:.2f} us/step replayed, "
+             f"{r['us_per_step']:.2f} us/step eager")
+
     workloads = {}
     if not args.no_workloads and args.variant == "auto" and args.state == "f32":
         for c in (1, 2, 3, 4):
@@ -669,6 +694,7 @@ def main():
         "cpu_baseline": cpu,
         "cpu_baseline_1core": cpu1,
         "workloads": workloads or None,
+        "decode": dec,
     }
     print(json.dumps(out), flush=True)
 
