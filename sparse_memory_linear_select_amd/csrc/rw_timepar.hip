@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int str
 // the plan, so all of them can be in flight together; reads that overflowed
 // the plan replay their writes from the sorted events.
 constexpr int kPairBatch = 4;   // v pairs per row group in flight, after the first ones
-constexpr int kFirstPairs = 2;  // v pairs per row group loaded with the plan
+constexpr int kFirstPairs = 1;  // v pairs per row group loaded with the plan (0 - 3: 1 fastest)
 
 template <int NR, bool BF16>
 __global__ __launch_bounds__(256) void tp_read_kernel(TPArgs a, int ep, int nslice)
