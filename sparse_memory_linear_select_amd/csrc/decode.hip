@@ -12,6 +12,24 @@
 #include <atomic>
 
 namespace sdm {
+
+// Compute units of the current device (looked up once per device; threads
+// that race here store the same value).
+int compute_units()
+{
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 namespace {
 
 struct DecArgs {
@@ -402,22 +420,6 @@ __global__ __launch_bounds__(256) void rw_decode_fused_kernel(DecFArgs a)
     }
 }
 
-// Compute units of the current device (looked up once per device; threads
-// that race here store the same value).
-int compute_units()
-{
-    static std::atomic<int> cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int n = cached[dev].load(std::memory_order_relaxed);
-    if (n <= 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            n <= 0)
-            n = 256;
-        cached[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
 
 template <int ST>
 hipError_t launch_fused_state(const Shape &s, DecFArgs &a, hipStream_t st)

@@ -48,8 +48,7 @@ __global__ __launch_bounds__(256) void init_kernel_bf16(const float *__restrict_
     const float4 *src = reinterpret_cast<const float4 *>(M0);
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
         const float4 x = src[i];
-        const uint2 u = make_uint2(bf16_bits(x.x) | (bf16_bits(x.y) << 16),
-                                   bf16_bits(x.z) | (bf16_bits(x.w) << 16));
+        const uint2 u = make_uint2(bf16_pack2(x.x, x.y), bf16_pack2(x.z, x.w));
         for (int b = 0; b < B; b++) M[(int64_t)b * n4 + i] = u;
     }
 }

@@ -29,6 +29,8 @@
 // state y agrees to float32 rounding (its terms are grouped differently).
 #include "tp_device.h"
 
+#include <cstdlib>
+
 namespace sdm {
 namespace {
 
@@ -678,6 +680,80 @@ __global__ __launch_bounds__(64 * (WPU > 4 ? WPU : 4)) void tp_read_stored_kerne
 
 // ------------------------------------------------------------------ update
 
+// A row group's SPG sorted events (event s in lane s of the group; the rows
+// of segments' first events in row[s], the v slices in vv[s]) applied in
+// one pass, in time order: a segment starts from its loaded row at its first
+// event, every event applies row <- round(a*row + c*v) once, and the row is
+// stored after the segment's last event in the group.  The group's leading
+// events may continue a segment of the group before, whose group applies
+// them: they are skipped.  A segment that goes on past the group (bit SPG of
+// `same`) is not stored but left in rt / slt with tail set.  on_head(s, h)
+// sees each event with h = whether it starts a segment.  A narrow state
+// takes one pass (one fma and one rounding per event; applying each segment
+// from its head over the rest of the group cost up to SPG*(SPG+1)/2, and the
+// roundings made that the larger part of a narrow-state write: bfloat16
+// write/read 5.64 -> 4.88 ms at the 1.4B-style layer with the fused kernel);
+// a float32 state keeps the per-head form, whose segments are independent
+// chains (the one pass: 6.74 -> 6.82 ms).
+template <int kLPR, int SPG, class S, class OnHead>
+__device__ __forceinline__ void apply_group(const S &st, const TPEntry &me, uint32_t same, int j0,
+                                            int n, const float4 (&row)[SPG],
+                                            const float4 (&vv)[SPG], rsrc_t Mr, uint32_t rowb,
+                                            int col, bool col_ok, float4 &rt, uint32_t &slt,
+                                            bool &tail, OnHead on_head)
+{
+    if constexpr (S::kElem == 4) {
+        tail = false;
+#pragma unroll
+        for (int s = 0; s < SPG; s++) {
+            const bool head = (j0 + s < n) & !((same >> s) & 1u);
+            on_head(s, head);
+            float4 r = fma4(__uint_as_float(group_bcast<kLPR>(__float_as_uint(me.a), s)), row[s],
+                            __uint_as_float(group_bcast<kLPR>(__float_as_uint(me.c), s)), vv[s]);
+            bool more = true;  // the rest of the segment within the group, in time order
+#pragma unroll
+            for (int s2 = s + 1; s2 < SPG; s2++) {
+                more = more & ((same >> s2) & 1u);
+                if (more)
+                    r = fma4(__uint_as_float(group_bcast<kLPR>(__float_as_uint(me.a), s2)), r,
+                             __uint_as_float(group_bcast<kLPR>(__float_as_uint(me.c), s2)), vv[s2]);
+            }
+            const uint32_t sl = group_bcast<kLPR>(me.slot, s);
+            const bool cont = head & more & ((same >> SPG) & 1u);
+            if (cont) {
+                rt = r;
+                slt = sl;
+            }
+            tail |= cont;
+            st.store(r, Mr, (head & !cont & col_ok) ? sl * rowb + col * S::kElem : kOff);
+        }
+        return;
+    }
+    float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+    bool act = false;  // inside a segment this group applies
+#pragma unroll
+    for (int s = 0; s < SPG; s++) {
+        const bool cont = (same >> s) & 1u;  // set only for events in range
+        const bool head = (j0 + s < n) & !cont;
+        on_head(s, head);
+        act = head | (act & cont);
+        if (head) r = row[s];
+        if (act)
+            r = st.round(fma4(__uint_as_float(group_bcast<kLPR>(__float_as_uint(me.a), s)), r,
+                              __uint_as_float(group_bcast<kLPR>(__float_as_uint(me.c), s)), vv[s]));
+        const uint32_t sl = group_bcast<kLPR>(me.slot, s);
+        const bool nxt = (same >> (s + 1)) & 1u;  // event s + 1 (bit SPG: past the group) continues
+        if (s == SPG - 1) {
+            tail = act & nxt;
+            if (tail) {
+                rt = r;
+                slt = sl;
+            }
+        }
+        st.store(r, Mr, (act & !nxt & col_ok) ? sl * rowb + col * S::kElem : kOff);
+    }
+}
+
 // One wavefront per (chain, block of kRPI*SPG sorted write events, row
 // slice); each row group takes SPG consecutive events.  With `rev` the
 // chains are taken last to first: the read kernel before it (or the previous
@@ -698,9 +774,10 @@ __global__ __launch_bounds__(64 * (WPU > 4 ? WPU : 4)) void tp_read_stored_kerne
 // in the wave's last group or for a segment longer than the next group
 // (write/read 7.50 -> 7.19 ms; doing the tail inside the per-event loop,
 // from memory, forced full waits for every outstanding load).  A bfloat16
-// or E4M3 state is held to six waves per SIMD.
+// or E4M3 state is held to six waves per SIMD, a float32 state (no tape) to
+// five, which the compiler otherwise misses by a few registers.
 template <bool BF16, int SPG, int ST, bool TAPE = false>
-__global__ __launch_bounds__(256, ST != kStateF32 ? 6 : 1) void tp_update_kernel(TPArgs a, int ep,
+__global__ __launch_bounds__(256, ST != kStateF32 ? 6 : (TAPE ? 1 : 5)) void tp_update_kernel(TPArgs a, int ep,
                                                                                  int nslice,
                                                                                  int nblk, bool rev)
 {
@@ -771,34 +848,14 @@ __global__ __launch_bounds__(256, ST != kStateF32 ? 6 : 1) void tp_update_kernel
     float4 rt = make_float4(0.f, 0.f, 0.f, 0.f);
     uint32_t slt = 0u;
     bool tail = false;
-#pragma unroll
-    for (int s = 0; s < SPG; s++) {
-        const bool head = (j0 + s < n) & !((same >> s) & 1u);
-        if (TAPE) {
-            TPEntry ev;
-            ev.tw = group_bcast<kLPR>(me.tw, s);
-            tape_put(ev, row[s], head & col_ok);
-        }
-        float4 r = st.round(fma4(__uint_as_float(group_bcast<kLPR>(__float_as_uint(me.a), s)), row[s],
-                                 __uint_as_float(group_bcast<kLPR>(__float_as_uint(me.c), s)), vv[s]));
-        // the rest of the segment within the group, in time order
-        bool more = true;
-#pragma unroll
-        for (int s2 = s + 1; s2 < SPG; s2++) {
-            more = more & ((same >> s2) & 1u);
-            if (more)
-                r = st.round(fma4(__uint_as_float(group_bcast<kLPR>(__float_as_uint(me.a), s2)), r,
-                                  __uint_as_float(group_bcast<kLPR>(__float_as_uint(me.c), s2)), vv[s2]));
-        }
-        const uint32_t sl = group_bcast<kLPR>(me.slot, s);
-        const bool cont = head & more & ((same >> SPG) & 1u);
-        if (cont) {
-            rt = r;
-            slt = sl;
-        }
-        tail |= cont;
-        st.store(r, Mr, (head & !cont & col_ok) ? sl * rowb + col * S::kElem : kOff);
-    }
+    apply_group<kLPR, SPG>(st, me, same, j0, n, row, vv, Mr, rowb, col, col_ok, rt, slt, tail,
+                           [&](int s, bool head) {
+                               if (TAPE) {
+                                   TPEntry ev;
+                                   ev.tw = group_bcast<kLPR>(me.tw, s);
+                                   tape_put(ev, row[s], head & col_ok);
+                               }
+                           });
     // The events just past the group are the next row group's (same wave,
     // same columns, kLPR lanes up): its lanes hold their fields, v rows and
     // which of them continue the segment (leading bits of its `same`).
@@ -840,6 +897,315 @@ __global__ __launch_bounds__(256, ST != kStateF32 ? 6 : 1) void tp_update_kernel
             rt = st.round(fma4(f1.a, rt, f1.c, v1));
         }
         st.store(rt, Mr, col_ok ? slt * rowb + col * S::kElem : kOff);
+    }
+}
+
+// ------------------------------------------------------------------ fused apply
+
+// Bfloat16 or E4M3 state, epochs of at most kFuseMaxE tokens.  One workgroup
+// of kFuseWaves waves per (chain, 64-column slice) takes every epoch of the
+// call: it stages the epoch's v rows (its columns, float32) in LDS, does the
+// epoch's reads, then its writes, then the next epoch, with a barrier between
+// the phases.  No other workgroup touches its columns of the chain's state,
+// so a barrier orders everything the phases share, and the v slices that the
+// replayed and applied writes need come from LDS rather than from the cache
+// hierarchy.  Each row and each y element is computed with the operations of
+// tp_read_stored_kernel and tp_update_kernel in their order (the same
+// butterfly and wave order for y), so the results are bit-identical to
+// theirs; the per-epoch launches remain for epochs too long to stage and for
+// shapes with fewer units than compute units.
+constexpr int kFuseWaves = 16;
+constexpr int kFuseLPR = 16;     // lanes per row group: 64 columns per slice
+constexpr int kFuseMaxE = 256;   // tokens of v in LDS: kFuseMaxE * 256 bytes
+
+template <bool BF16, int ST>
+__global__ __launch_bounds__(64 * kFuseWaves) void tp_fused_stored_kernel(TPArgs a, int ep0,
+                                                                          int ep1)
+{
+    using S = StateRow<ST>;
+    constexpr int kLPR = kFuseLPR, kRPI = 64 / kLPR, NR = kStoredNR, SPG = 8;
+    // tp_read_stored_kernel's order: a wave there adds its row groups' sums
+    // of NR reads by a butterfly, and its unit adds the waves' sums in order;
+    // here a row group takes kLPR reads, i.e. kOldPerGroup of those waves
+    constexpr int kOldRPI = 64 / S::kLPR;
+    constexpr int kPerOld = NR * kOldRPI;
+    constexpr int kOldPerGroup = kLPR / kPerOld;
+    constexpr int kMaxOld = kRPI * kOldPerGroup;
+    static_assert(kLPR % kPerOld == 0 && kRPI * kLPR >= kMaxK && (kOldRPI == 2 || kOldRPI == 4),
+                  "a row group holds whole waves of the per-epoch read");
+    static_assert(SPG <= kLPR, "one event per lane of a row group");
+    __shared__ float4 vs[kFuseMaxE * kLPR];
+    const S st(a.ssc, a.sisc);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // unit = slice * chains + chain: with chains a multiple of 8, the slices
+    // of a chain share an XCD (workgroups go to XCDs round-robin) and its
+    // plan is fetched into one L2
+    const int64_t chain = (int64_t)(blockIdx.x % (uint32_t)a.chains);
+    const int slice = (int)(blockIdx.x / (uint32_t)a.chains);
+    // Per-lane values are derived from the lane number anew in every
+    // iteration of the loops below: the empty asm hides that the number is
+    // the same each time, so they are recomputed in a few instructions
+    // rather than kept live across the whole kernel (which spilled them).
+    auto lane_ids = [&](int &g, int &q, int &col, bool &col_ok) {
+        int ln = (int)(threadIdx.x & 63);
+        asm volatile("" : "+v"(ln));
+        g = ln / kLPR;
+        q = ln % kLPR;
+        col = slice * 4 * kLPR + q * 4;
+        col_ok = col < a.d_v;
+    };
+    // chains < 2^32, so 32-bit division
+    const int64_t b = (uint32_t)chain / (uint32_t)a.H;
+    const int h = (int)(chain - b * a.H);
+    const int64_t hd = (int64_t)a.H * a.d_v;
+    const int64_t vrow0 = (b * a.T * a.H + h) * a.d_v;  // v of token 0 of the chain, column 0
+    const rsrc_t Mr = make_rsrc(static_cast<char *>(a.M) + chain * a.N * a.d_v * S::kElem,
+                                (uint32_t)(a.N * a.d_v * S::kElem));
+    const uint32_t rowb = (uint32_t)a.d_v * S::kElem;
+    const int wpu_old = stored_waves_per_unit<ST>(a.R);
+
+    for (int ep = ep0; ep < ep1; ep++) {
+        const int64_t t0 = (int64_t)ep * a.E;
+        const int ne = (int)((a.T - t0) < a.E ? (a.T - t0) : a.E);  // <= kFuseMaxE (host check)
+        const int n = ne * a.W;
+        const TPEntry *se = a.sorted + chain * a.T * a.W + t0 * a.W;
+        {  // the epoch's v rows: every load issued, then the LDS stores
+            constexpr int kStage = kFuseMaxE * kLPR / (64 * kFuseWaves);
+            float4 vt[kStage];
+#pragma unroll
+            for (int u = 0; u < kStage; u++) {
+                const int i = (int)threadIdx.x + u * 64 * kFuseWaves;
+                const int c = slice * 4 * kLPR + (i % kLPR) * 4;
+                vt[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (i < ne * kLPR && c < a.d_v) vt[u] = load_v<BF16>(a.v, vrow0 + (t0 + i / kLPR) * hd + c);
+            }
+#pragma unroll
+            for (int u = 0; u < kStage; u++) {
+                const int i = (int)threadIdx.x + u * 64 * kFuseWaves;
+                if (i < ne * kLPR) vs[i] = vt[u];
+            }
+        }
+        __syncthreads();
+
+        // reads: one token per wave at a time; lane q of row group g holds
+        // the plan of read g*kLPR + q
+        // a token's plan, loaded one token ahead (the rows of a token wait
+        // only for its own plan, which arrived during the previous token)
+        struct Plan {
+            uint32_t sl, wr, lk, t12, a1, c1, a2, c2;  // t12: the two writes' tokens (< 2^16)
+        };
+        auto load_plan = [&](int tl) {
+            int g, q, col;
+            bool col_ok;
+            lane_ids(g, q, col, col_ok);
+            const int64_t ct = chain * a.T + t0 + tl;
+            const uint32_t *rc = a.rec + ct * a.rec_dwords;
+            const uint32_t *fw = reinterpret_cast<const uint32_t *>(a.pairs + ct * a.P);
+            const bool mine = g * kLPR + q < a.R;
+            const int rr = mine ? g * kLPR + q : 0;
+            Plan p;
+            p.sl = mine ? rc[3 * a.Wp + rr] : 0u;
+            p.wr = mine ? __float_as_uint(a.rwt[ct * kMaxK + rr]) : 0u;
+            p.lk = mine ? a.rlink[ct * kMaxK + rr] : 0u;
+            p.t12 = (fw[rr] & 0xFFFFu) | (fw[3 * a.R + rr] << 16);
+            p.a1 = fw[a.R + rr];
+            p.c1 = fw[2 * a.R + rr];
+            p.a2 = fw[4 * a.R + rr];
+            p.c2 = fw[5 * a.R + rr];
+            return p;
+        };
+        Plan pnext{};
+        if (wv < ne) pnext = load_plan(wv);
+        for (int tl = wv; tl < ne; tl += kFuseWaves) {
+            int g, q, col;
+            bool col_ok;
+            lane_ids(g, q, col, col_ok);
+            const int64_t t = t0 + tl;
+            const int r0 = g * kLPR;
+            const Plan pl0 = pnext;
+            const uint32_t sl_mine = pl0.sl, lk_mine = pl0.lk;
+            const float wr_mine = __uint_as_float(pl0.wr);
+            const uint32_t t12m = pl0.t12, a1m = pl0.a1, c1m = pl0.c1;
+            const uint32_t a2m = pl0.a2, c2m = pl0.c2;
+            typename S::Raw row[kLPR];
+#pragma unroll
+            for (int i = 0; i < kLPR; i++) {
+                const uint32_t sl = group_bcast<kLPR>(sl_mine, i);
+                const bool ok = col_ok & (r0 + i < a.R);
+                row[i] = st.load_raw(Mr, ok ? (sl & kSlotMask) * rowb + col * S::kElem : kOff);
+            }
+            if (tl + kFuseWaves < ne) pnext = load_plan(tl + kFuseWaves);
+            // sums of NR reads (the per-epoch read's row groups), folded as
+            // soon as they are complete, in its butterfly's order: with 4 row
+            // groups there a wave sum is (p0 + p1) + (p2 + p3), with 2 p0 + p1
+            float4 sw[kOldPerGroup], pl = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int bq = 0; bq < kLPR / NR; bq++) {
+                float4 rv[NR];
+                int cnt[NR], first[NR];
+#pragma unroll
+                for (int i = 0; i < NR; i++) {
+                    const int k = bq * NR + i;
+                    const uint32_t lk = group_bcast<kLPR>(lk_mine, k);
+                    cnt[i] = (int)(lk & ((1u << kCntBits) - 1u));
+                    first[i] = (int)(lk >> kCntBits);
+                    rv[i] = st.widen(row[k]);
+                    if (cnt[i] > 0)
+                        rv[i] = st.round(fma4(__uint_as_float(group_bcast<kLPR>(a1m, k)), rv[i],
+                                              __uint_as_float(group_bcast<kLPR>(c1m, k)),
+                                              vs[(cnt[i] > 0 ? group_bcast<kLPR>(t12m, k) & 0xFFFFu : 0u) * kLPR + q]));
+                    if (cnt[i] > 1)
+                        rv[i] = st.round(fma4(__uint_as_float(group_bcast<kLPR>(a2m, k)), rv[i],
+                                              __uint_as_float(group_bcast<kLPR>(c2m, k)),
+                                              vs[(cnt[i] > 1 ? group_bcast<kLPR>(t12m, k) >> 16 : 0u) * kLPR + q]));
+                }
+                // third and later in-epoch writes (rare): read by read, one
+                // event at a time, which keeps the registers of the common
+                // path free
+#pragma unroll
+                for (int i = 0; i < NR; i++) {
+                    for (int k = 2; k < cnt[i]; k++) {
+                        const TPEntry e = se[first[i] + k];
+                        rv[i] = st.round(fma4(e.a, rv[i], e.c, vs[(e.tw >> 6) * kLPR + q]));
+                    }
+                }
+                float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                for (int i = 0; i < NR; i++) {
+                    // masked references have weight 0 and a zero row
+                    const float wr = __uint_as_float(group_bcast<kLPR>(__float_as_uint(wr_mine), bq * NR + i));
+                    acc.x = fmaf(wr, rv[i].x, acc.x);
+                    acc.y = fmaf(wr, rv[i].y, acc.y);
+                    acc.z = fmaf(wr, rv[i].z, acc.z);
+                    acc.w = fmaf(wr, rv[i].w, acc.w);
+                }
+                if (bq % 2 == 0) {
+                    pl = acc;
+                } else {
+                    const float4 pr = make_float4(pl.x + acc.x, pl.y + acc.y, pl.z + acc.z, pl.w + acc.w);
+                    if constexpr (kOldRPI == 2) {
+                        sw[bq / 2] = pr;
+                    } else if (bq % 4 == 1) {
+                        sw[bq / 4] = pr;
+                    } else {
+                        const float4 x = sw[bq / 4];
+                        sw[bq / 4] = make_float4(x.x + pr.x, x.y + pr.y, x.z + pr.z, x.w + pr.w);
+                    }
+                }
+            }
+            // its unit's sum of the waves, in wave order (wave o of row group g
+            // is wave g*kOldPerGroup + o there)
+            float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int w = 0; w < kMaxOld; w++) {
+                const int src = (w / kOldPerGroup) * kLPR + q;
+                float4 p;
+                p.x = __shfl(sw[w % kOldPerGroup].x, src, 64);
+                p.y = __shfl(sw[w % kOldPerGroup].y, src, 64);
+                p.z = __shfl(sw[w % kOldPerGroup].z, src, 64);
+                p.w = __shfl(sw[w % kOldPerGroup].w, src, 64);
+                if (w == 0) {
+                    y = p;
+                } else if (w < wpu_old) {
+                    y.x += p.x;
+                    y.y += p.y;
+                    y.z += p.z;
+                    y.w += p.w;
+                }
+            }
+            if (g == 0 && col_ok)
+                *reinterpret_cast<float4 *>(a.y + (b * a.T * a.H + t * a.H + h) * a.d_v + col) = y;
+        }
+        __syncthreads();
+
+        // writes: tp_update_kernel's blocks of kRPI*SPG sorted events
+        const int nblk = (n + kRPI * SPG - 1) / (kRPI * SPG);
+        // a block's events, loaded one block ahead
+        struct Block {
+            TPEntry me;
+            uint32_t next, prev0;
+        };
+        auto load_block = [&](int blk) {
+            int g, q, col;
+            bool col_ok;
+            lane_ids(g, q, col, col_ok);
+            const int j0 = (blk * kRPI + g) * SPG;
+            Block k;
+            k.me = se[(q < SPG && j0 + q < n) ? j0 + q : n - 1];
+            k.next = j0 + SPG < n ? se[j0 + SPG].slot : 0xFFFFFFFFu;
+            k.prev0 = j0 > 0 && j0 - 1 < n ? se[j0 - 1].slot : 0xFFFFFFFFu;
+            return k;
+        };
+        Block bnext{};
+        if (wv < nblk) bnext = load_block(wv);
+        for (int blk = wv; blk < nblk; blk += kFuseWaves) {
+            int g, q, col;
+            bool col_ok;
+            lane_ids(g, q, col, col_ok);
+            const int lane = g * kLPR + q;
+            const int j0 = (blk * kRPI + g) * SPG;
+            const Block cur = bnext;
+            const TPEntry me = cur.me;
+            const uint32_t next = cur.next;
+            uint32_t same = 0u, prev = cur.prev0;
+            float4 row[SPG], vv[SPG];
+#pragma unroll
+            for (int s = 0; s < SPG; s++) {
+                const uint32_t sl = group_bcast<kLPR>(me.slot, s);
+                const bool in = j0 + s < n;
+                same |= (uint32_t)(in & (sl == prev)) << s;
+                const bool head = in & (sl != prev);
+                row[s] = st.load(Mr, (head & col_ok) ? sl * rowb + col * S::kElem : kOff);
+                vv[s] = vs[(group_bcast<kLPR>(me.tw, s) >> 6) * kLPR + q];
+                prev = sl;
+            }
+            if (blk + kFuseWaves < nblk) bnext = load_block(blk + kFuseWaves);
+            same |= (uint32_t)((j0 + SPG < n) & (next == prev)) << SPG;
+            float4 rt = make_float4(0.f, 0.f, 0.f, 0.f);
+            uint32_t slt = 0u;
+            bool tail = false;
+            apply_group<kLPR, SPG>(st, me, same, j0, n, row, vv, Mr, rowb, col, col_ok, rt, slt, tail,
+                                   [](int, bool) {});
+            // the segment goes on into the next row group (its lanes hold the
+            // fields and v slices), then from memory
+            int jm = j0 + SPG;
+            if (__builtin_amdgcn_ballot_w64(tail) != 0ull) {
+                const bool inw = g < kRPI - 1;
+                const int up = (lane + kLPR) & 63;
+                const uint32_t same_nx = (uint32_t)__builtin_amdgcn_ds_bpermute(up * 4, (int)same);
+                bool go = tail & inw;
+#pragma unroll
+                for (int s2 = 0; s2 < SPG; s2++) {
+                    go = go & ((same_nx >> s2) & 1u);
+                    if (__builtin_amdgcn_ballot_w64(go) == 0ull) break;
+                    const int src = ((g + 1) * kLPR + s2) & 63;
+                    const float a2 = __int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(me.a)));
+                    const float c2 = __int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(me.c)));
+                    float4 v2;
+                    v2.x = __int_as_float(__builtin_amdgcn_ds_bpermute(up * 4, __float_as_int(vv[s2].x)));
+                    v2.y = __int_as_float(__builtin_amdgcn_ds_bpermute(up * 4, __float_as_int(vv[s2].y)));
+                    v2.z = __int_as_float(__builtin_amdgcn_ds_bpermute(up * 4, __float_as_int(vv[s2].z)));
+                    v2.w = __int_as_float(__builtin_amdgcn_ds_bpermute(up * 4, __float_as_int(vv[s2].w)));
+                    if (go) rt = st.round(fma4(a2, rt, c2, v2));
+                }
+                if (inw) jm = go ? j0 + 2 * SPG : n;
+            }
+            if (tail) {
+                for (int j = jm; j < n; j += 2) {
+                    const TPEntry f0 = se[j];
+                    const TPEntry f1 = se[j + 1 < n ? j + 1 : j];
+                    if (f0.slot != slt) break;
+                    const bool c1 = (j + 1 < n) & (f1.slot == slt);
+                    const float4 v0 = vs[(f0.tw >> 6) * kLPR + q];
+                    const float4 v1 = vs[((c1 ? f1 : f0).tw >> 6) * kLPR + q];
+                    rt = st.round(fma4(f0.a, rt, f0.c, v0));
+                    if (!c1) break;
+                    rt = st.round(fma4(f1.a, rt, f1.c, v1));
+                }
+                st.store(rt, Mr, col_ok ? slt * rowb + col * S::kElem : kOff);
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -966,10 +1332,42 @@ hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipS
     return hipGetLastError();
 }
 
+// Whether a narrow-state apply takes tp_fused_stored_kernel: its epochs must
+// fit the LDS buffer; then the environment variable SDM_TP_FUSED=0 keeps the
+// per-epoch launches and SDM_TP_FUSED=1 takes the fused kernel (the results
+// are bit-identical either way), and otherwise it is taken when the (chain,
+// slice) units give every compute unit one workgroup in every round (one
+// workgroup fits a compute unit at a time): a whole number of rounds, or
+// enough of them that a partial last one costs little.
+static bool use_fused(const TPArgs &a, int d_v)
+{
+    if (a.E > kFuseMaxE) return false;
+    const char *env = getenv("SDM_TP_FUSED");
+    if (env && env[0] == '0') return false;
+    if (env && env[0] == '1') return true;
+    const int64_t units = a.chains * ((d_v + 4 * kFuseLPR - 1) / (4 * kFuseLPR));
+    const int64_t cus = compute_units();
+    return units >= cus && (units % cus == 0 || units >= 8 * cus);
+}
+
 template <int ST>
 static hipError_t tp_apply_state(const Shape &s, TPArgs a, bool bf16, hipStream_t st, int ep0,
                                  int ep1)
 {
+    if constexpr (ST != kStateF32) {
+        if (use_fused(a, s.d_v)) {
+            const int64_t units = a.chains * ((s.d_v + 4 * kFuseLPR - 1) / (4 * kFuseLPR));
+            if (units >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+            if (ep0 >= ep1) return hipSuccess;
+            if (bf16)
+                hipLaunchKernelGGL((tp_fused_stored_kernel<true, ST>), dim3((unsigned)units),
+                                   dim3(64 * kFuseWaves), 0, st, a, ep0, ep1);
+            else
+                hipLaunchKernelGGL((tp_fused_stored_kernel<false, ST>), dim3((unsigned)units),
+                                   dim3(64 * kFuseWaves), 0, st, a, ep0, ep1);
+            return hipGetLastError();
+        }
+    }
     constexpr int kLPR = StateRow<ST>::kLPR, kRPI = 64 / kLPR;
     const int nslice = (s.d_v + 4 * kLPR - 1) / (4 * kLPR);
     const int nr = (s.R + kRPI - 1) / kRPI;

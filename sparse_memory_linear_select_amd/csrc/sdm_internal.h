@@ -57,11 +57,17 @@ struct StateFmt {
     int scale_log2 = 0;  // s (E4M3 state only)
 };
 
-// Nearest bfloat16 (ties to even) of a finite float, as its 16 bits.
-__device__ __forceinline__ uint32_t bf16_bits(float f)
+// Nearest bfloat16 values (ties to even) of two finite floats, packed: a in
+// the low 16 bits, b in the high.  gfx950's v_cvt_pk_bf16_f32 does this in
+// one instruction; it gives the bits (u + 0x7FFF + ((u >> 16) & 1)) >> 16 of
+// the nearest-even rule for every finite float32 u, subnormals included
+// (checked over all of them with denormals enabled, as this library builds).
+typedef __bf16 sdm_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float sdm_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pack2(float a, float b)
 {
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    const sdm_f32x2 x = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, sdm_bf16x2));
 }
 
 // E4M3 codes (OCP FP8: sign, 4 exponent bits with bias 7, 3 mantissa bits;
@@ -174,6 +180,8 @@ bool decode_fused_supported(const Shape &s);
 hipError_t launch_decode_fused(const Shape &s, const void *kp, const void *qp, const void *v,
                                bool bf16, const float *alpha, const float *beta, float *y,
                                void *M, StateFmt fmt, hipStream_t st);
+// Compute units of the current device (queried once per device).
+int compute_units();
 // Candidate columns of stage 2 for lists of K slots (kTabMax entries, pairs
 // a << 8 | b) and the number of pairs with both ranks >= 2.
 const uint16_t *hook_columns(int K, int *rest);

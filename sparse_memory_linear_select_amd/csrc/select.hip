@@ -120,8 +120,7 @@ __device__ __forceinline__ void select_body(SelArgs a)
         sort_desc<2, E>(kk, lane);
         if (init) {  // the piece of M0 has arrived during the sort
             if (a.init_bf16) {
-                const uint2 u = make_uint2(bf16_bits(m0.x) | (bf16_bits(m0.y) << 16),
-                                           bf16_bits(m0.z) | (bf16_bits(m0.w) << 16));
+                const uint2 u = make_uint2(bf16_pack2(m0.x, m0.y), bf16_pack2(m0.z, m0.w));
                 for (int b = 0; b < a.Bseq; b++) reinterpret_cast<uint2 *>(a.M)[b * a.n4 + jm] = u;
             } else {
                 for (int b = 0; b < a.Bseq; b++) reinterpret_cast<float4 *>(a.M)[b * a.n4 + jm] = m0;

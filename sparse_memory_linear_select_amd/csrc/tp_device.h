@@ -90,8 +90,7 @@ struct StateRow<kStateBF16> {
     // the 4 values rounded to bfloat16, packed
     __device__ __forceinline__ Raw pack(float4 v) const
     {
-        return make_uint2(bf16_bits(v.x) | (bf16_bits(v.y) << 16),
-                          bf16_bits(v.z) | (bf16_bits(v.w) << 16));
+        return make_uint2(bf16_pack2(v.x, v.y), bf16_pack2(v.z, v.w));
     }
     __device__ __forceinline__ void store(float4 v, rsrc_t r, uint32_t off) const
     {
@@ -103,8 +102,7 @@ struct StateRow<kStateBF16> {
     }
     __device__ __forceinline__ float4 round(float4 v) const
     {
-        return make_float4(__uint_as_float(bf16_bits(v.x) << 16), __uint_as_float(bf16_bits(v.y) << 16),
-                           __uint_as_float(bf16_bits(v.z) << 16), __uint_as_float(bf16_bits(v.w) << 16));
+        return widen(pack(v));
     }
 };
 
@@ -149,16 +147,30 @@ __device__ __forceinline__ float4 load_v(const void *v, int64_t off)
 }
 
 // Value of x in lane (lane & ~(LPR - 1)) | i, i.e. lane i of this lane's
-// group of LPR lanes (LPR = 8 or 16): ds_swizzle in bit mode acts within 32
-// lanes as lane' = (lane & and_mask) | or_mask.
+// group of LPR lanes.  LPR = 16: the DPP row broadcast row_newbcast:i, a VALU
+// move within each row of 16 lanes (the LDS pipe stays free; every caller
+// runs it where a row's lanes are all active or all inactive, since a DPP
+// read of an inactive lane is undefined).  LPR = 8 or 32: ds_swizzle in bit
+// mode, which acts within 32 lanes as lane' = (lane & and_mask) | or_mask.
 // (i is a constant once the callers' loops are unrolled, so the switch folds
-// to one instruction; the swizzle pattern must be an immediate.)
+// to one instruction; the DPP control and the swizzle pattern are immediates.)
 template <int LPR>
 __device__ __forceinline__ uint32_t group_bcast(uint32_t x, int i)
 {
     static_assert(LPR == 8 || LPR == 16 || LPR == 32, "row groups of 8, 16 or 32 lanes");
-    constexpr int kAnd = 0x1F & ~(LPR - 1);
     const int v = (int)x;
+    if constexpr (LPR == 16) {
+        switch (i) {
+#define SDM_NBC(I) \
+    case I: return (uint32_t)__builtin_amdgcn_mov_dpp(v, 0x150 + (I), 0xF, 0xF, false);
+            SDM_NBC(0) SDM_NBC(1) SDM_NBC(2) SDM_NBC(3) SDM_NBC(4) SDM_NBC(5) SDM_NBC(6) SDM_NBC(7)
+            SDM_NBC(8) SDM_NBC(9) SDM_NBC(10) SDM_NBC(11) SDM_NBC(12) SDM_NBC(13) SDM_NBC(14)
+            SDM_NBC(15)
+#undef SDM_NBC
+        }
+        return 0u;
+    }
+    constexpr int kAnd = 0x1F & ~(LPR - 1);
     switch (i) {
 #define SDM_SWZ(I) \
     case I: return (uint32_t)__builtin_amdgcn_ds_swizzle(v, kAnd | ((I) << 5));
