@@ -42,6 +42,17 @@ SCHEDULES = {  # schedule -> (kernel source, kernels of the write/read phase)
     "token-serial": ("rw_serial.hip", "rw_serial_kernel (one launch)"),
     "time-parallel": ("rw_timepar.hip", "tp_read_kernel + tp_update_kernel (one pair per epoch)"),
 }
+# a bfloat16 or E4M3 state: the library's choice for the shape
+NARROW_KERNELS = ("tp_fused_stored_kernel (one launch: every epoch's reads, then its writes) "
+                  "where the epochs fit its LDS and the (chain, slice) units fill the GPU, else "
+                  "tp_read_stored_kernel + tp_update_kernel (one pair per epoch)")
+
+
+def rw_kernels(schedule, state):
+    """What runs the write/read phase, for the roofline's `kernel` field."""
+    if schedule == "time-parallel" and state != "f32":
+        return NARROW_KERNELS
+    return SCHEDULES[schedule][1]
 
 
 # headers every kernel source includes: a change there changes the kernels too
@@ -335,10 +346,13 @@ def counters_summary(args, wl):
     wscale = 1048576.0 / mean(copy[0], "WRITE_SIZE")
     schedule = "time-parallel" if args.variant in ("auto", "timepar") else "token-serial"
     if schedule == "time-parallel":
-        rw = [k for k in kernels if k.startswith(("tp_read", "tp_update"))]
+        # per-epoch launches (one read launch per epoch) or the fused
+        # narrow-state kernel (one launch per step)
+        rw = [k for k in kernels if k.startswith(("tp_read", "tp_update", "tp_fused"))]
         E = _epoch_len(wl)
-        steps = sum(len(vals[(k, "FETCH_SIZE")]) for k in rw if k.startswith("tp_read")) / (
-            -(-wl.T // E))
+        steps = (sum(len(vals[(k, "FETCH_SIZE")]) for k in rw if k.startswith("tp_read")) /
+                 (-(-wl.T // E)) +
+                 sum(len(vals[(k, "FETCH_SIZE")]) for k in rw if k.startswith("tp_fused")))
     else:
         rw = [k for k in kernels if k.startswith("rw_serial_kernel")]
         steps = sum(len(vals[(k, "FETCH_SIZE")]) for k in rw)
@@ -678,7 +692,7 @@ def main():
                      "unit": "GB/s", "frac": m["effective_gbs"] / PEAK_HBM_GBS,
                      "traffic": m["traffic"],
                      "traffic_unit": "HBM bytes per step (write/read phase, counters)",
-                     "kernel": SCHEDULES[m["schedule"]][1],
+                     "kernel": rw_kernels(m["schedule"], args.state),
                      "timing": "write/read kernels bracketed by HIP events on their stream in "
                                "a second pass of K steps issued as sdm_prepare + sdm_apply",
                      "achieved_is": "effective: algorithmic row bytes ((2W+R) d_v per "

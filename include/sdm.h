@@ -84,6 +84,12 @@ typedef enum { SDM_F32 = 0, SDM_BF16 = 1, SDM_FP8_E4M3 = 2 } sdm_dtype;
  * With one token per sequence (T == 1: a decode step) there is no order
  * across tokens to schedule, and TIMEPAR runs a single kernel instead of the
  * sort and scan: the token's writes, then its reads of the updated rows.
+ * With a bfloat16 or E4M3 state, TIMEPAR applies the chunks either in one
+ * launch (chunks of at most 256 tokens, and enough (sequence, head,
+ * 64-column slice) units to fill the GPU) or as a read and a write launch
+ * per chunk; both give the same bits.  The environment variable
+ * SDM_TP_FUSED=0 or SDM_TP_FUSED=1, read at each call, forces the per-chunk
+ * or the one-launch form where it applies (for tests and measurements).
  */
 typedef enum {
     SDM_VARIANT_AUTO = 0,
