@@ -680,9 +680,9 @@ __global__ __launch_bounds__(64 * (WPU > 4 ? WPU : 4)) void tp_read_stored_kerne
 
 // ------------------------------------------------------------------ update
 
-// A row group's SPG sorted events (event s in lane s of the group; the rows
-// of segments' first events in row[s], the v slices in vv[s]) applied in
-// one pass, in time order: a segment starts from its loaded row at its first
+// A row group's SPG sorted events (event s in lane s of the group; the row
+// of a segment's first event from row_at(s), the v slices from v_at(s))
+// applied in one pass, in time order: a segment starts from its loaded row at its first
 // event, every event applies row <- round(a*row + c*v) once, and the row is
 // stored after the segment's last event in the group.  The group's leading
 // events may continue a segment of the group before, whose group applies
@@ -695,12 +695,11 @@ __global__ __launch_bounds__(64 * (WPU > 4 ? WPU : 4)) void tp_read_stored_kerne
 // write/read 5.64 -> 4.88 ms at the 1.4B-style layer with the fused kernel);
 // a float32 state keeps the per-head form, whose segments are independent
 // chains (the one pass: 6.74 -> 6.82 ms).
-template <int kLPR, int SPG, class S, class OnHead>
+template <int kLPR, int SPG, class S, class RowAt, class VAt, class OnHead>
 __device__ __forceinline__ void apply_group(const S &st, const TPEntry &me, uint32_t same, int j0,
-                                            int n, const float4 (&row)[SPG],
-                                            const float4 (&vv)[SPG], rsrc_t Mr, uint32_t rowb,
-                                            int col, bool col_ok, float4 &rt, uint32_t &slt,
-                                            bool &tail, OnHead on_head)
+                                            int n, RowAt row_at, VAt v_at, rsrc_t Mr,
+                                            uint32_t rowb, int col, bool col_ok, float4 &rt,
+                                            uint32_t &slt, bool &tail, OnHead on_head)
 {
     if constexpr (S::kElem == 4) {
         tail = false;
@@ -708,15 +707,15 @@ __device__ __forceinline__ void apply_group(const S &st, const TPEntry &me, uint
         for (int s = 0; s < SPG; s++) {
             const bool head = (j0 + s < n) & !((same >> s) & 1u);
             on_head(s, head);
-            float4 r = fma4(__uint_as_float(group_bcast<kLPR>(__float_as_uint(me.a), s)), row[s],
-                            __uint_as_float(group_bcast<kLPR>(__float_as_uint(me.c), s)), vv[s]);
+            float4 r = fma4(__uint_as_float(group_bcast<kLPR>(__float_as_uint(me.a), s)), row_at(s),
+                            __uint_as_float(group_bcast<kLPR>(__float_as_uint(me.c), s)), v_at(s));
             bool more = true;  // the rest of the segment within the group, in time order
 #pragma unroll
             for (int s2 = s + 1; s2 < SPG; s2++) {
                 more = more & ((same >> s2) & 1u);
                 if (more)
                     r = fma4(__uint_as_float(group_bcast<kLPR>(__float_as_uint(me.a), s2)), r,
-                             __uint_as_float(group_bcast<kLPR>(__float_as_uint(me.c), s2)), vv[s2]);
+                             __uint_as_float(group_bcast<kLPR>(__float_as_uint(me.c), s2)), v_at(s2));
             }
             const uint32_t sl = group_bcast<kLPR>(me.slot, s);
             const bool cont = head & more & ((same >> SPG) & 1u);
@@ -737,10 +736,10 @@ __device__ __forceinline__ void apply_group(const S &st, const TPEntry &me, uint
         const bool head = (j0 + s < n) & !cont;
         on_head(s, head);
         act = head | (act & cont);
-        if (head) r = row[s];
+        if (head) r = row_at(s);
         if (act)
             r = st.round(fma4(__uint_as_float(group_bcast<kLPR>(__float_as_uint(me.a), s)), r,
-                              __uint_as_float(group_bcast<kLPR>(__float_as_uint(me.c), s)), vv[s]));
+                              __uint_as_float(group_bcast<kLPR>(__float_as_uint(me.c), s)), v_at(s)));
         const uint32_t sl = group_bcast<kLPR>(me.slot, s);
         const bool nxt = (same >> (s + 1)) & 1u;  // event s + 1 (bit SPG: past the group) continues
         if (s == SPG - 1) {
@@ -848,7 +847,8 @@ __global__ __launch_bounds__(256, ST != kStateF32 ? 6 : (TAPE ? 1 : 5)) void tp_
     float4 rt = make_float4(0.f, 0.f, 0.f, 0.f);
     uint32_t slt = 0u;
     bool tail = false;
-    apply_group<kLPR, SPG>(st, me, same, j0, n, row, vv, Mr, rowb, col, col_ok, rt, slt, tail,
+    apply_group<kLPR, SPG>(st, me, same, j0, n, [&](int s) { return row[s]; },
+                           [&](int s) { return vv[s]; }, Mr, rowb, col, col_ok, rt, slt, tail,
                            [&](int s, bool head) {
                                if (TAPE) {
                                    TPEntry ev;
@@ -923,7 +923,7 @@ __global__ __launch_bounds__(64 * kFuseWaves) void tp_fused_stored_kernel(TPArgs
                                                                           int ep1)
 {
     using S = StateRow<ST>;
-    constexpr int kLPR = kFuseLPR, kRPI = 64 / kLPR, NR = kStoredNR, SPG = 8;
+    constexpr int kLPR = kFuseLPR, kRPI = 64 / kLPR, NR = kStoredNR, SPG = 16;
     // tp_read_stored_kernel's order: a wave there adds its row groups' sums
     // of NR reads by a butterfly, and its unit adds the waves' sums in order;
     // here a row group takes kLPR reads, i.e. kOldPerGroup of those waves
@@ -1148,15 +1148,14 @@ __global__ __launch_bounds__(64 * kFuseWaves) void tp_fused_stored_kernel(TPArgs
             const TPEntry me = cur.me;
             const uint32_t next = cur.next;
             uint32_t same = 0u, prev = cur.prev0;
-            float4 row[SPG], vv[SPG];
+            typename S::Raw row[SPG];  // in the state's width until used
 #pragma unroll
             for (int s = 0; s < SPG; s++) {
                 const uint32_t sl = group_bcast<kLPR>(me.slot, s);
                 const bool in = j0 + s < n;
                 same |= (uint32_t)(in & (sl == prev)) << s;
                 const bool head = in & (sl != prev);
-                row[s] = st.load(Mr, (head & col_ok) ? sl * rowb + col * S::kElem : kOff);
-                vv[s] = vs[(group_bcast<kLPR>(me.tw, s) >> 6) * kLPR + q];
+                row[s] = st.load_raw(Mr, (head & col_ok) ? sl * rowb + col * S::kElem : kOff);
                 prev = sl;
             }
             if (blk + kFuseWaves < nblk) bnext = load_block(blk + kFuseWaves);
@@ -1164,8 +1163,10 @@ __global__ __launch_bounds__(64 * kFuseWaves) void tp_fused_stored_kernel(TPArgs
             float4 rt = make_float4(0.f, 0.f, 0.f, 0.f);
             uint32_t slt = 0u;
             bool tail = false;
-            apply_group<kLPR, SPG>(st, me, same, j0, n, row, vv, Mr, rowb, col, col_ok, rt, slt, tail,
-                                   [](int, bool) {});
+            apply_group<kLPR, SPG>(
+                st, me, same, j0, n, [&](int s) { return st.widen(row[s]); },
+                [&](int s) { return vs[(group_bcast<kLPR>(me.tw, s) >> 6) * kLPR + q]; }, Mr, rowb,
+                col, col_ok, rt, slt, tail, [](int, bool) {});
             // the segment goes on into the next row group (its lanes hold the
             // fields and v slices), then from memory
             int jm = j0 + SPG;
@@ -1181,11 +1182,8 @@ __global__ __launch_bounds__(64 * kFuseWaves) void tp_fused_stored_kernel(TPArgs
                     const int src = ((g + 1) * kLPR + s2) & 63;
                     const float a2 = __int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(me.a)));
                     const float c2 = __int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(me.c)));
-                    float4 v2;
-                    v2.x = __int_as_float(__builtin_amdgcn_ds_bpermute(up * 4, __float_as_int(vv[s2].x)));
-                    v2.y = __int_as_float(__builtin_amdgcn_ds_bpermute(up * 4, __float_as_int(vv[s2].y)));
-                    v2.z = __int_as_float(__builtin_amdgcn_ds_bpermute(up * 4, __float_as_int(vv[s2].z)));
-                    v2.w = __int_as_float(__builtin_amdgcn_ds_bpermute(up * 4, __float_as_int(vv[s2].w)));
+                    const uint32_t tw2 = (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)me.tw);
+                    const float4 v2 = vs[(tw2 >> 6) * kLPR + q];
                     if (go) rt = st.round(fma4(a2, rt, c2, v2));
                 }
                 if (inw) jm = go ? j0 + 2 * SPG : n;
