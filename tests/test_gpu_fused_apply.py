@@ -8,7 +8,8 @@ import torch
 import oracle
 import sdm_inputs as si
 import sparse_memory_linear_select_amd as sdm
-from gpu_util import FP8_SCALE_LOG2, TOL_BF16, TOL_FP8, check_bf16_state, gpu_forward, log
+from gpu_util import (FP8_SCALE_LOG2, TOL_BF16, TOL_FP8, check_bf16_state, gpu_forward, log,
+                      make_core, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -78,3 +79,52 @@ def test_fused_continuation_split(monkeypatch):
     torch.cuda.synchronize()
     assert torch.equal(torch.cat([y1, y2], 1), y)
     assert torch.equal(M2.view(torch.uint8), M.view(torch.uint8))
+
+
+@pytest.mark.parametrize("state", ["bf16", "fp8"])
+def test_fused_graph_replays(monkeypatch, state):
+    """The one-launch apply captured in a HIP graph replays bit for bit like
+    the eager call (eager work and a synchronisation between replays)."""
+    wl = _wl((2, 300, 2, 16, 72, 16, 16, "f32", 0.3), 933)
+    monkeypatch.setenv("SDM_TP_FUSED", "1")
+    dd = upload(si.generate(wl))
+    core = make_core(dd, wl.W, wl.R, STATES[state], FP8_SCALE_LOG2)
+    args = [dd[n] for n in ("kp", "qp", "v", "alpha", "beta")]
+    y_e, M_e = core.forward(*args)
+    ws = torch.empty(core.workspace_size(wl.B, wl.T, sdm.F32, sdm.AUTO), dtype=torch.uint8,
+                     device="cuda")
+    y_s, M_s = torch.empty_like(y_e), torch.empty_like(M_e)
+    core.forward(*args, y=y_s, M=M_s, workspace=ws)  # warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        core.forward(*args, y=y_s, M=M_s, workspace=ws)
+    u8 = lambda x: x.view(torch.uint8)
+    for rep in range(3):
+        y_s.fill_(float("nan"))
+        u8(M_s).fill_(0xFF)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_s, y_e) and torch.equal(u8(M_s), u8(M_e)), rep
+        _ = (y_e * 2).sum().item()  # eager work between replays
+
+
+@pytest.mark.parametrize("state", ["bf16", "fp8"])
+def test_fused_noalloc(monkeypatch, state):
+    """sdm_forward_noalloc takes the same one-launch apply: y and M equal
+    sdm_forward's bit for bit, twice (the second call smaller)."""
+    wl = _wl((2, 300, 2, 16, 72, 16, 16, "f32", 0.3), 934)
+    monkeypatch.setenv("SDM_TP_FUSED", "1")
+    dd = upload(si.generate(wl))
+    core = make_core(dd, wl.W, wl.R, STATES[state], FP8_SCALE_LOG2)
+    u8 = lambda x: x.view(torch.uint8)
+    for B, T in ((wl.B, wl.T), (1, 101)):
+        args = [dd[n][:B, :T].contiguous() for n in ("kp", "qp", "v", "alpha", "beta")]
+        y1, M1 = core.forward(*args)
+        y2 = torch.full_like(y1, float("nan"))
+        M2 = torch.empty_like(M1)
+        u8(M2).fill_(0xFF)
+        core.forward_noalloc(*args, y=y2, M=M2)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2) and torch.equal(u8(M1), u8(M2)), (B, T)
