@@ -50,15 +50,22 @@ struct RWArgs {
 // state is branch-free: masked lanes use out-of-range buffer offsets, tokens
 // past the end are clamped for loads and masked for stores, so the compiler
 // can keep the P-token prefetch in flight across iterations.
-template <int LPR, int NW, int NR, int P, bool BF16>
-__global__ __launch_bounds__(256) void rw_serial_kernel(RWArgs a)
+// WPB wavefronts per workgroup: 4 where the units give every SIMD a
+// wavefront in workgroups of four, else 1.  With four, a shape with few
+// units (512 at the 1.4B-style layer) filled only half of the compute
+// units; single-wave workgroups spread the same waves over all of them
+// (write+read 12.19 -> 11.14 ms at the 1.4B-style layer, 43.3 -> 32.8 ms
+// larger state, 1681 -> 1584 ms long-context), but lose where four-wave
+// workgroups already fill the chip (8B-style layer: 41.3 -> 47.8 ms).
+template <int LPR, int NW, int NR, int P, bool BF16, int WPB>
+__global__ __launch_bounds__(64 * WPB) void rw_serial_kernel(RWArgs a)
 {
-    __shared__ float4 ring[4][P][kMaxK][LPR];  // per wave: writes of the last P tokens
+    __shared__ float4 ring[WPB][P][kMaxK][LPR];  // per wave: writes of the last P tokens
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
     // the units of one chain sit on one XCD (workgroups are dealt round-robin)
     const int64_t lwg = (int64_t)(blockIdx.x % 8) * a.per_xcd + blockIdx.x / 8;
-    const int64_t unit = lwg * 4 + wv;
+    const int64_t unit = lwg * WPB + wv;
     if (unit >= a.units) return;
     const int64_t chain = unit / a.nslice;
     const int slice = (int)(unit - chain * a.nslice);
@@ -262,15 +269,13 @@ int rw_serial_depth() { return kDepth; }
 
 namespace {
 
-template <int LPR>
+template <int LPR, int WPB>
 hipError_t launch_lpr(RWArgs &a, const Shape &s, bool bf16, hipStream_t st)
 {
     constexpr int RPI = 64 / LPR;
-    a.nslice = (s.d_v + 4 * LPR - 1) / (4 * LPR);
-    a.units = (int64_t)s.B * s.H * a.nslice;
-    const int64_t wgs = (a.units + 3) / 4;
+    const int64_t wgs = (a.units + WPB - 1) / WPB;
     a.per_xcd = (wgs + 7) / 8;
-    const dim3 grid((unsigned)(a.per_xcd * 8)), block(256);
+    const dim3 grid((unsigned)(a.per_xcd * 8)), block(64 * WPB);
     // references per row group; the shorter list is padded (masked references
     // cost registers only)
     const int nw = (s.W + RPI - 1) / RPI, nr = (s.R + RPI - 1) / RPI;
@@ -278,11 +283,11 @@ hipError_t launch_lpr(RWArgs &a, const Shape &s, bool bf16, hipStream_t st)
 #define SDM_RW_CASE(NM_)                                                                        \
     if (nm <= NM_) {                                                                            \
         if (bf16)                                                                               \
-            hipLaunchKernelGGL((rw_serial_kernel<LPR, NM_, NM_, kDepth, true>), grid, block, 0, \
-                               st, a);                                                          \
+            hipLaunchKernelGGL((rw_serial_kernel<LPR, NM_, NM_, kDepth, true, WPB>), grid,     \
+                               block, 0, st, a);                                                \
         else                                                                                    \
-            hipLaunchKernelGGL((rw_serial_kernel<LPR, NM_, NM_, kDepth, false>), grid, block,   \
-                               0, st, a);                                                       \
+            hipLaunchKernelGGL((rw_serial_kernel<LPR, NM_, NM_, kDepth, false, WPB>), grid,    \
+                               block, 0, st, a);                                                \
         return hipGetLastError();                                                               \
     }
     // W, R <= 64 give nm <= LPR, so RPI * NM <= 64: every group's loads stay
@@ -311,8 +316,12 @@ hipError_t launch_rw_serial(const Shape &s, const uint32_t *rec, const void *v, 
     // fewer than 256 such units the chip is underfilled, and 32-byte slices
     // (four times the units) win.
     const int64_t units8 = (int64_t)s.B * s.H * ((s.d_v + 31) / 32);
-    if (units8 >= 256) return launch_lpr<8>(a, s, bf16, st);
-    return launch_lpr<2>(a, s, bf16, st);
+    const int lpr = units8 >= 256 ? 8 : 2;
+    a.nslice = (s.d_v + 4 * lpr - 1) / (4 * lpr);
+    a.units = (int64_t)s.B * s.H * a.nslice;
+    const bool four = a.units >= 4 * (int64_t)compute_units();
+    if (lpr == 8) return four ? launch_lpr<8, 4>(a, s, bf16, st) : launch_lpr<8, 1>(a, s, bf16, st);
+    return four ? launch_lpr<2, 4>(a, s, bf16, st) : launch_lpr<2, 1>(a, s, bf16, st);
 }
 
 hipError_t launch_rw_simple(const Shape &s, const uint32_t *rec, const void *v, bool bf16,
