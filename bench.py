@@ -39,7 +39,8 @@ def _log(*a):
 
 
 SCHEDULES = {  # schedule -> (kernel source, kernels of the write/read phase)
-    "token-serial": ("rw_serial.hip", "rw_serial_kernel (one launch)"),
+    "token-serial": ("rw_serial.hip", "rw_serial_kernel, or rw_split_kernel where the (chain, "
+                                      "slice) units are fewer than four per compute unit (one launch)"),
     "time-parallel": ("rw_timepar.hip", "tp_read_kernel + tp_update_kernel (one pair per epoch)"),
 }
 # a bfloat16 or E4M3 state: the library's choice for the shape
@@ -354,7 +355,7 @@ def counters_summary(args, wl):
                  (-(-wl.T // E)) +
                  sum(len(vals[(k, "FETCH_SIZE")]) for k in rw if k.startswith("tp_fused")))
     else:
-        rw = [k for k in kernels if k.startswith("rw_serial_kernel")]
+        rw = [k for k in kernels if k.startswith(("rw_serial_kernel", "rw_split_kernel"))]
         steps = sum(len(vals[(k, "FETCH_SIZE")]) for k in rw)
     fetch = sum(sum(vals[(k, "FETCH_SIZE")]) for k in rw) * 1024 * fscale / steps
     write = sum(sum(vals[(k, "WRITE_SIZE")]) for k in rw) * 1024 * wscale / steps

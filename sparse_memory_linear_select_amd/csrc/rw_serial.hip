@@ -19,14 +19,17 @@
 //
 // rw_simple_kernel is the plain version (one column per lane, no prefetch),
 // used when d_v is not a multiple of 4.
+#include "lane_ops.h"
 #include "tp_device.h"
 
 namespace sdm {
 namespace {
 
 // Cross-token prefetch depth: the rows of token t+P are gathered while token
-// t is processed.
+// t is processed (rw_serial_kernel: kDepth; rw_split_kernel, whose waves
+// hold a quarter of the references each: kSplitDepth).
 constexpr int kDepth = 2;
+constexpr int kSplitDepth = 8;
 
 __device__ __forceinline__ void wave_sync()
 {
@@ -41,6 +44,7 @@ struct RWArgs {
     float *y, *M;
     int64_t T, N;
     int H, d_v, W, R, Wp, Rp, rec_dwords;
+    int wk, rk;  // rw_split_kernel: write and read positions per wavefront
     int64_t nslice, units, per_xcd;
 };
 
@@ -187,10 +191,10 @@ __global__ __launch_bounds__(64 * WPB) void rw_serial_kernel(RWArgs a)
             }
 #pragma unroll
             for (int m = LPR; m < 64; m <<= 1) {
-                acc.x += __shfl_xor(acc.x, m, 64);
-                acc.y += __shfl_xor(acc.y, m, 64);
-                acc.z += __shfl_xor(acc.z, m, 64);
-                acc.w += __shfl_xor(acc.w, m, 64);
+                acc.x = xor_add(acc.x, m);
+                acc.y = xor_add(acc.y, m);
+                acc.z = xor_add(acc.z, m);
+                acc.w = xor_add(acc.w, m);
             }
             buf_store4(acc, Yr,
                        ((g == 0) & col_ok & (t0 + u >= 0) & (t0 + u < T)) ? (uint32_t)((u * hd + col) * 4) : kOff);
@@ -204,6 +208,197 @@ __global__ __launch_bounds__(64 * WPB) void rw_serial_kernel(RWArgs a)
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+}
+
+// The same token loop for shapes with few units: KS wavefronts of one
+// workgroup share a unit, wave k taking write positions [k*wk, (k+1)*wk) and
+// read positions [k*rk, (k+1)*rk) of every token (NW and NR per row group).
+// With a single wave per unit, the 256 units of the larger-state layer or of
+// the long-context sequence leave one wave per compute unit, whose token
+// loop is one instruction stream; split four ways, each wave has a quarter
+// of the per-token work and four waves share a compute unit.  The written
+// rows go to a ring in LDS shared by the workgroup, so a forwarded row can
+// come from any wave; the waves' partial sums of y meet in LDS, and wave 0
+// adds them in wave order and stores y one token later.  One workgroup
+// barrier per token, after its writes: the reads take same-token rows from
+// the ring; a row stored before a workgroup barrier is visible to the loads
+// that the other waves of the workgroup issue after it, so a prefetch may
+// read a row that another wave wrote P tokens back; and the waves are never
+// more than one token apart, so a ring of 2P tokens (written P or more
+// tokens after its last forwarded read) and two y buffers need no other
+// barrier.
+template <int LPR, int NW, int NR, int P, bool BF16, int KS>
+__global__ __launch_bounds__(64 * KS) void rw_split_kernel(RWArgs a)
+{
+    static_assert((P & (P - 1)) == 0, "ring slots are taken modulo 2P");
+    __shared__ float4 ring[2 * P][kMaxK][LPR];  // writes of the last 2P tokens, all waves
+    __shared__ float4 ypart[2][KS][LPR];        // partial y of each wave, by token parity
+    const int lane = threadIdx.x & 63;
+    const int k = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
+    const int64_t unit = (int64_t)(blockIdx.x % 8) * a.per_xcd + blockIdx.x / 8;
+    if (unit >= a.units) return;  // the whole workgroup: no barrier is left waiting
+    const int64_t chain = unit / a.nslice;
+    const int slice = (int)(unit - chain * a.nslice);
+    const int g = lane / LPR;  // row group
+    const int q = lane % LPR;  // float4 within the slice
+    const int col = slice * 4 * LPR + q * 4;
+    const bool col_ok = col < a.d_v;
+    const int colc = col_ok ? col : 0;
+    const int64_t b = chain / a.H;
+    const int h = (int)(chain - b * a.H);
+    const int64_t T = a.T;
+    const uint32_t rowb = (uint32_t)a.d_v * 4u;
+    const rsrc_t Mr = make_rsrc(a.M + chain * a.N * a.d_v, (uint32_t)(a.N * a.d_v * 4));
+    const uint32_t *recc = a.rec + chain * T * a.rec_dwords;
+    const int64_t hd = (int64_t)a.H * a.d_v;
+    const int64_t vrow0 = (b * T * a.H + h) * a.d_v + colc;
+    float *ybase = a.y + (b * T * a.H + h) * a.d_v;
+    // positions of this lane's references; groups past the wave's share load
+    // the share's last group (record reads stay inside the 64-entry arrays)
+    const bool gw = g * NW < a.wk, gr = g * NR < a.rk;
+    const int lw = k * a.wk + (gw ? g : a.wk / NW - 1) * NW;
+    const int lr = k * a.rk + (gr ? g : a.rk / NR - 1) * NR;
+    bool pw[NW], okw[NW], okr[NR];
+#pragma unroll
+    for (int i = 0; i < NW; i++) {
+        pw[i] = gw & (lw + i < a.W);  // a position of this wave's share
+        okw[i] = col_ok & pw[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NR; i++) okr[i] = col_ok & gr & (lr + i < a.R);
+
+    uint32_t sw[2 * P][NW], sr[2 * P][NR];
+    float4 rw[P][NW], rr[P][NR];
+    float ma[P][NW], mc[P][NW], mq[P][NR];
+    float4 mv[P];
+
+    auto clampt = [&](int64_t t) { return t < 0 ? 0 : (t < T ? t : T - 1); };
+    auto fwd = [](uint32_t s) {
+        return ((s & kFwdValid) != 0) & (((s >> kFwdDShift) & kFwdDMask) < (uint32_t)P);
+    };
+    auto load_slots = [&](int64_t t, uint32_t (&ow)[NW], uint32_t (&orr)[NR]) {
+        const uint32_t *r = recc + clampt(t) * a.rec_dwords;
+        load_k<NW>(r + lw, ow);
+        load_k<NR>(r + 3 * a.Wp + lr, orr);
+    };
+    auto load_rows = [&](int64_t t, const uint32_t (&iw)[NW], const uint32_t (&ir)[NR],
+                         float4 (&ow)[NW], float4 (&orr)[NR], float (&oa)[NW], float (&oc)[NW],
+                         float (&oq)[NR], float4 &ov) {
+        const int64_t tc = clampt(t);
+#pragma unroll
+        for (int i = 0; i < NW; i++)
+            ow[i] = buf_load4(Mr, (okw[i] & !fwd(iw[i])) ? (iw[i] & kSlotMask) * rowb + col * 4u : kOff);
+#pragma unroll
+        for (int i = 0; i < NR; i++)
+            orr[i] = buf_load4(Mr, (okr[i] & !fwd(ir[i])) ? (ir[i] & kSlotMask) * rowb + col * 4u : kOff);
+        ov = load_v<BF16>(a.v, vrow0 + tc * hd);
+        const float *r = reinterpret_cast<const float *>(recc + tc * a.rec_dwords);
+        load_k<NW>(r + a.Wp + lw, oa);
+        load_k<NW>(r + 2 * a.Wp + lw, oc);
+        load_k<NR>(r + 3 * a.Wp + a.Rp + lr, oq);
+    };
+
+#pragma unroll
+    for (int u = 0; u < 2 * P; u++) {
+#pragma unroll
+        for (int i = 0; i < NW; i++) sw[u][i] = 0;
+#pragma unroll
+        for (int i = 0; i < NR; i++) sr[u][i] = 0;
+    }
+#pragma unroll
+    for (int u = 0; u < P; u++) {
+        mv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int i = 0; i < NW; i++) {
+            rw[u][i] = mv[u];
+            ma[u][i] = 0.f;
+            mc[u][i] = 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < NR; i++) {
+            rr[u][i] = mv[u];
+            mq[u][i] = 0.f;
+        }
+    }
+
+    // wave 0 stores y of the previous token (sum of the waves' partials)
+    auto store_y = [&](const rsrc_t &Yr, int slot, uint32_t off, bool live) {
+        if (k == 0 && g == 0) {
+            float4 ys = ypart[slot][0][q];
+#pragma unroll
+            for (int j = 1; j < KS; j++) {
+                const float4 p = ypart[slot][j][q];
+                ys.x += p.x;
+                ys.y += p.y;
+                ys.z += p.z;
+                ys.w += p.w;
+            }
+            buf_store4(ys, Yr, (col_ok & live) ? off : kOff);
+        }
+    };
+
+    int64_t t0 = -2 * P;
+    for (; t0 < T; t0 += 2 * P) {
+        // y of tokens t0-1 .. t0+2P-2 through a descriptor based at token
+        // t0-1 (only offsets of tokens in [0, T) are ever used)
+        const rsrc_t Yr = make_rsrc(ybase + (t0 - 1) * hd, (uint32_t)(2 * P * hd * 4));
+#pragma unroll
+        for (int u = 0; u < 2 * P; u++) {
+            const int pr = u % P;
+            const bool live = (t0 + u >= 0) & (t0 + u < T);
+            // ---- this wave's writes ----
+#pragma unroll
+            for (int i = 0; i < NW; i++) {
+                const uint32_t s = sw[u][i];
+                const bool f = fwd(s);
+                const int d = f ? (int)((s >> kFwdDShift) & kFwdDMask) : 0;
+                const int wp = f ? (int)((s >> kFwdWShift) & kFwdWMask) : 0;
+                const float4 fv = ring[(u - d) & (2 * P - 1)][wp][q];
+                const float4 old = f ? fv : rw[pr][i];
+                const float4 nv = fma4(ma[pr][i], old, mc[pr][i], mv[pr]);
+                buf_store4(nv, Mr, (okw[i] & live) ? (s & kSlotMask) * rowb + col * 4u : kOff);
+                if (pw[i]) ring[u][lw + i][q] = nv;
+            }
+            __syncthreads();
+            store_y(Yr, (u + 1) & 1, (uint32_t)(u * hd + col) * 4u,
+                    (t0 + u - 1 >= 0) & (t0 + u - 1 < T));
+            // ---- this wave's reads of the post-write state ----
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int i = 0; i < NR; i++) {
+                // a masked reference holds a copy of a live one's slot word:
+                // never forwarded, its (not loaded) row reads as zero
+                const uint32_t s = sr[u][i];
+                const bool f = fwd(s) & okr[i];
+                const int d = f ? (int)((s >> kFwdDShift) & kFwdDMask) : 0;
+                const int wp = f ? (int)((s >> kFwdWShift) & kFwdWMask) : 0;
+                const float4 fv = ring[(u - d) & (2 * P - 1)][wp][q];
+                const float4 val = f ? fv : rr[pr][i];
+                const float qv = mq[pr][i];
+                acc.x = fmaf(qv, val.x, acc.x);
+                acc.y = fmaf(qv, val.y, acc.y);
+                acc.z = fmaf(qv, val.z, acc.z);
+                acc.w = fmaf(qv, val.w, acc.w);
+            }
+#pragma unroll
+            for (int m = LPR; m < 64; m <<= 1) {
+                acc.x = xor_add(acc.x, m);
+                acc.y = xor_add(acc.y, m);
+                acc.z = xor_add(acc.z, m);
+                acc.w = xor_add(acc.w, m);
+            }
+            if (g == 0) ypart[u & 1][k][q] = acc;
+            // ---- prefetch: rows of token t+P, slot words of token t+2P ----
+            load_rows(t0 + u + P, sw[(u + P) % (2 * P)], sr[(u + P) % (2 * P)], rw[pr], rr[pr],
+                      ma[pr], mc[pr], mq[pr], mv[pr]);
+            load_slots(t0 + u + 2 * P, sw[u], sr[u]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // the last trip's last token (t0 - 1 now) has no next token to store its y
+    __syncthreads();
+    const rsrc_t Yr = make_rsrc(ybase + (t0 - 1) * hd, (uint32_t)(hd * 4));
+    store_y(Yr, 1, (uint32_t)col * 4u, t0 - 1 < T);
 }
 
 template <bool BF16>
@@ -265,8 +460,6 @@ RWArgs make_args(const Shape &s, const uint32_t *rec, const void *v, float *y, f
 
 }  // namespace
 
-int rw_serial_depth() { return kDepth; }
-
 namespace {
 
 template <int LPR, int WPB>
@@ -300,7 +493,56 @@ hipError_t launch_lpr(RWArgs &a, const Shape &s, bool bf16, hipStream_t st)
     return hipErrorInvalidValue;
 }
 
+// rw_split_kernel with KS waves per unit: each wave takes ceil(W / KS)
+// write and ceil(R / KS) read positions (rounded up to whole row-group
+// loads), NM per row group
+template <int LPR, int KS>
+hipError_t launch_split(RWArgs &a, const Shape &s, bool bf16, hipStream_t st)
+{
+    constexpr int G = 64 / LPR;
+    const int pw = (s.W + KS - 1) / KS, pr = (s.R + KS - 1) / KS;
+    const int nm = ((pw > pr ? pw : pr) + G - 1) / G;
+    a.per_xcd = (a.units + 7) / 8;
+    const dim3 grid((unsigned)(a.per_xcd * 8)), block(64 * KS);
+#define SDM_SPLIT_CASE(NM_)                                                                     \
+    if (nm <= NM_) {                                                                            \
+        a.wk = (pw + NM_ - 1) / NM_ * NM_;                                                      \
+        a.rk = (pr + NM_ - 1) / NM_ * NM_;                                                      \
+        if (KS * a.wk > kMaxK || KS * a.rk > kMaxK) return hipErrorInvalidValue;               \
+        if (bf16)                                                                               \
+            hipLaunchKernelGGL((rw_split_kernel<LPR, NM_, NM_, kSplitDepth, true, KS>), grid,  \
+                               block, 0, st, a);                                                \
+        else                                                                                    \
+            hipLaunchKernelGGL((rw_split_kernel<LPR, NM_, NM_, kSplitDepth, false, KS>), grid, \
+                               block, 0, st, a);                                                \
+        return hipGetLastError();                                                               \
+    }
+    SDM_SPLIT_CASE(1)
+    SDM_SPLIT_CASE(2)
+#undef SDM_SPLIT_CASE
+    return hipErrorInvalidValue;
+}
+
+// Which kernel runs a shape: 128-byte row slices (8 lanes x float4) give the
+// fullest HBM bursts; where those units give every SIMD a wave in
+// workgroups of four, one wave per unit (rw_serial_kernel); else the split
+// kernel with ks waves per unit, and 32-byte slices (four times the units)
+// where 128-byte ones leave compute units without a unit.
+struct SerialPlan {
+    int lpr, ks;  // lanes per row slice; waves per unit (1: rw_serial_kernel)
+};
+
+SerialPlan serial_plan(const Shape &s)
+{
+    const int64_t units8 = (int64_t)s.B * s.H * ((s.d_v + 31) / 32);
+    const int64_t cus = compute_units();
+    if (units8 >= 4 * cus) return {8, 1};
+    return {units8 >= cus ? 8 : 2, 4};
+}
+
 }  // namespace
+
+int rw_serial_depth(const Shape &s) { return serial_plan(s).ks > 1 ? kSplitDepth : kDepth; }
 
 bool rw_serial_supported(const Shape &s)
 {
@@ -312,16 +554,16 @@ hipError_t launch_rw_serial(const Shape &s, const uint32_t *rec, const void *v, 
                             float *y, float *M, hipStream_t st)
 {
     RWArgs a = make_args(s, rec, v, y, M);
-    // 128-byte row slices (8 lanes x float4) give the fullest HBM bursts; with
-    // fewer than 256 such units the chip is underfilled, and 32-byte slices
-    // (four times the units) win.
-    const int64_t units8 = (int64_t)s.B * s.H * ((s.d_v + 31) / 32);
-    const int lpr = units8 >= 256 ? 8 : 2;
-    a.nslice = (s.d_v + 4 * lpr - 1) / (4 * lpr);
+    const SerialPlan p = serial_plan(s);
+    a.nslice = (s.d_v + 4 * p.lpr - 1) / (4 * p.lpr);
     a.units = (int64_t)s.B * s.H * a.nslice;
-    const bool four = a.units >= 4 * (int64_t)compute_units();
-    if (lpr == 8) return four ? launch_lpr<8, 4>(a, s, bf16, st) : launch_lpr<8, 1>(a, s, bf16, st);
-    return four ? launch_lpr<2, 4>(a, s, bf16, st) : launch_lpr<2, 1>(a, s, bf16, st);
+#define SDM_PLAN_CASE(LPR_, KS_) \
+    if (p.lpr == LPR_ && p.ks == KS_) return launch_split<LPR_, KS_>(a, s, bf16, st);
+    if (p.ks == 1) return launch_lpr<8, 4>(a, s, bf16, st);
+    SDM_PLAN_CASE(8, 4)
+    SDM_PLAN_CASE(2, 4)
+#undef SDM_PLAN_CASE
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_rw_simple(const Shape &s, const uint32_t *rec, const void *v, bool bf16,

@@ -359,7 +359,7 @@ sdm_status sdm_prepare(sdm_handle h, int B, int64_t T, const void *kp, const voi
             if (e != hipSuccess) return hip_fail(e, "time-parallel sort launch");
         }
     } else if (sdm::rw_serial_supported(s)) {
-        e = sdm::launch_plan(s, rec, sdm::rw_serial_depth(), hs);
+        e = sdm::launch_plan(s, rec, sdm::rw_serial_depth(s), hs);
         if (e != hipSuccess) return hip_fail(e, "plan launch");
     }
     return SDM_OK;

@@ -147,7 +147,7 @@ hipError_t launch_plan(const Shape &s, uint32_t *rec, int depth, hipStream_t st)
 bool rw_serial_supported(const Shape &s);
 hipError_t launch_rw_serial(const Shape &s, const uint32_t *rec, const void *v, bool bf16,
                             float *y, float *M, hipStream_t st);
-int rw_serial_depth();  // prefetch depth the serial kernel is compiled for
+int rw_serial_depth(const Shape &s);  // prefetch depth of the serial kernel that runs s
 
 // Token-serial write/read, one column per lane, no prefetch (any d_v).
 hipError_t launch_rw_simple(const Shape &s, const uint32_t *rec, const void *v, bool bf16,

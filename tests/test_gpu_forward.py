@@ -257,8 +257,14 @@ def test_forward_rejects_bad_tensors():
     assert e.value.status == 2
 
 
-@pytest.mark.parametrize("shape", [(2, 300, 2, 32, 64, 32, 32, 0.0), (1, 700, 1, 64, 96, 64, 64, 0.4),
-                                   (4, 129, 2, 16, 32, 16, 8, 0.0)])
+@pytest.mark.parametrize("shape", [
+    (2, 300, 2, 32, 64, 32, 32, 0.0), (1, 700, 1, 64, 96, 64, 64, 0.4),
+    (4, 129, 2, 16, 32, 16, 8, 0.0),
+    # 256 units of 128-byte slices: four waves per unit, two references per row group
+    (2, 300, 4, 64, 1024, 64, 64, 0.2),
+    # 1024 such units: one wave per unit
+    (4, 160, 8, 64, 1024, 64, 48, 0.0),
+])
 def test_schedules_agree_bitwise_on_state(shape):
     """Both schedules apply the same float32 operations to every row in the
     same order, so the final state agrees bit for bit.  y agrees to float32
