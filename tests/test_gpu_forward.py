@@ -264,6 +264,9 @@ def test_forward_rejects_bad_tensors():
     (2, 300, 4, 64, 1024, 64, 64, 0.2),
     # 1024 such units: one wave per unit
     (4, 160, 8, 64, 1024, 64, 48, 0.0),
+    # ragged last slice (28 of 32 columns) in each kernel form
+    (2, 100, 4, 32, 1020, 32, 32, 0.0),
+    (4, 64, 8, 32, 1020, 24, 32, 0.0),
 ])
 def test_schedules_agree_bitwise_on_state(shape):
     """Both schedules apply the same float32 operations to every row in the
