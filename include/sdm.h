@@ -77,7 +77,9 @@ typedef enum { SDM_F32 = 0, SDM_BF16 = 1, SDM_FP8_E4M3 = 2 } sdm_dtype;
  * Write/read schedule used by sdm_forward.  Both produce the same result up
  * to float32 rounding order.
  *   SERIAL   token-serial per (sequence, head, column slice), rows gathered
- *            and scattered in HBM with cross-token prefetch.
+ *            and scattered in HBM with cross-token prefetch; where those
+ *            units are fewer than four per compute unit, the slots of each
+ *            token are split over the four waves of a workgroup.
  *   TIMEPAR  time-parallel: (slot, t) events sorted per chunk of tokens and
  *            a per-slot scan of the affine map M <- a*M + c*v.
  *   AUTO     the library's choice for the shape.
