@@ -38,6 +38,17 @@ __device__ __forceinline__ void wave_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// x of lane (lane ^ m); m is a constant once the callers' loops are unrolled
+__device__ __forceinline__ float xor_get(float x, int m, int lane)
+{
+    if (m >= 16) {
+        uint32_t lo, hi;
+        pair_vals(__float_as_uint(x), m, lo, hi);
+        return __uint_as_float((lane & m) ? lo : hi);
+    }
+    return __uint_as_float(dpp_xor(__float_as_uint(x), m));
+}
+
 struct RWArgs {
     const uint32_t *rec;
     const void *v;
@@ -246,13 +257,16 @@ __global__ __launch_bounds__(64 * KS) void rw_split_kernel(RWArgs a)
     const int colc = col_ok ? col : 0;
     const int64_t b = chain / a.H;
     const int h = (int)(chain - b * a.H);
-    const int64_t T = a.T;
+    // token numbers in 32 bits (B*T*H < 2^31); offsets from them as 32 x 32
+    // -> 64-bit products
+    const int T = (int)a.T;
     const uint32_t rowb = (uint32_t)a.d_v * 4u;
     const rsrc_t Mr = make_rsrc(a.M + chain * a.N * a.d_v, (uint32_t)(a.N * a.d_v * 4));
-    const uint32_t *recc = a.rec + chain * T * a.rec_dwords;
-    const int64_t hd = (int64_t)a.H * a.d_v;
-    const int64_t vrow0 = (b * T * a.H + h) * a.d_v + colc;
-    float *ybase = a.y + (b * T * a.H + h) * a.d_v;
+    const uint32_t *recc = a.rec + chain * a.T * a.rec_dwords;
+    const uint32_t recd = (uint32_t)a.rec_dwords;
+    const uint32_t hd = (uint32_t)a.H * (uint32_t)a.d_v;  // stride of one token in v and y
+    const int64_t vrow0 = (b * a.T * a.H + h) * a.d_v + colc;
+    float *ybase = a.y + (b * a.T * a.H + h) * a.d_v;
     // positions of this lane's references; groups past the wave's share load
     // the share's last group (record reads stay inside the 64-entry arrays)
     const bool gw = g * NW < a.wk, gr = g * NR < a.rk;
@@ -272,27 +286,27 @@ __global__ __launch_bounds__(64 * KS) void rw_split_kernel(RWArgs a)
     float ma[P][NW], mc[P][NW], mq[P][NR];
     float4 mv[P];
 
-    auto clampt = [&](int64_t t) { return t < 0 ? 0 : (t < T ? t : T - 1); };
+    auto clampt = [&](int t) { return (uint32_t)(t < 0 ? 0 : (t < T ? t : T - 1)); };
     auto fwd = [](uint32_t s) {
         return ((s & kFwdValid) != 0) & (((s >> kFwdDShift) & kFwdDMask) < (uint32_t)P);
     };
-    auto load_slots = [&](int64_t t, uint32_t (&ow)[NW], uint32_t (&orr)[NR]) {
-        const uint32_t *r = recc + clampt(t) * a.rec_dwords;
+    auto load_slots = [&](int t, uint32_t (&ow)[NW], uint32_t (&orr)[NR]) {
+        const uint32_t *r = recc + (uint64_t)clampt(t) * recd;
         load_k<NW>(r + lw, ow);
         load_k<NR>(r + 3 * a.Wp + lr, orr);
     };
-    auto load_rows = [&](int64_t t, const uint32_t (&iw)[NW], const uint32_t (&ir)[NR],
+    auto load_rows = [&](int t, const uint32_t (&iw)[NW], const uint32_t (&ir)[NR],
                          float4 (&ow)[NW], float4 (&orr)[NR], float (&oa)[NW], float (&oc)[NW],
                          float (&oq)[NR], float4 &ov) {
-        const int64_t tc = clampt(t);
+        const uint32_t tc = clampt(t);
 #pragma unroll
         for (int i = 0; i < NW; i++)
             ow[i] = buf_load4(Mr, (okw[i] & !fwd(iw[i])) ? (iw[i] & kSlotMask) * rowb + col * 4u : kOff);
 #pragma unroll
         for (int i = 0; i < NR; i++)
             orr[i] = buf_load4(Mr, (okr[i] & !fwd(ir[i])) ? (ir[i] & kSlotMask) * rowb + col * 4u : kOff);
-        ov = load_v<BF16>(a.v, vrow0 + tc * hd);
-        const float *r = reinterpret_cast<const float *>(recc + tc * a.rec_dwords);
+        ov = load_v<BF16>(a.v, vrow0 + (int64_t)((uint64_t)tc * hd));
+        const float *r = reinterpret_cast<const float *>(recc + (uint64_t)tc * recd);
         load_k<NW>(r + a.Wp + lw, oa);
         load_k<NW>(r + 2 * a.Wp + lw, oc);
         load_k<NR>(r + 3 * a.Wp + a.Rp + lr, oq);
@@ -321,7 +335,8 @@ __global__ __launch_bounds__(64 * KS) void rw_split_kernel(RWArgs a)
         }
     }
 
-    // wave 0 stores y of the previous token (sum of the waves' partials)
+    // wave 0 stores y of the previous token (sum of the waves' partials, in
+    // wave order)
     auto store_y = [&](const rsrc_t &Yr, int slot, uint32_t off, bool live) {
         if (k == 0 && g == 0) {
             float4 ys = ypart[slot][0][q];
@@ -337,11 +352,11 @@ __global__ __launch_bounds__(64 * KS) void rw_split_kernel(RWArgs a)
         }
     };
 
-    int64_t t0 = -2 * P;
+    int t0 = -2 * P;
     for (; t0 < T; t0 += 2 * P) {
         // y of tokens t0-1 .. t0+2P-2 through a descriptor based at token
         // t0-1 (only offsets of tokens in [0, T) are ever used)
-        const rsrc_t Yr = make_rsrc(ybase + (t0 - 1) * hd, (uint32_t)(2 * P * hd * 4));
+        const rsrc_t Yr = make_rsrc(ybase + (int64_t)(t0 - 1) * hd, 2 * P * hd * 4);
 #pragma unroll
         for (int u = 0; u < 2 * P; u++) {
             const int pr = u % P;
@@ -360,7 +375,7 @@ __global__ __launch_bounds__(64 * KS) void rw_split_kernel(RWArgs a)
                 if (pw[i]) ring[u][lw + i][q] = nv;
             }
             __syncthreads();
-            store_y(Yr, (u + 1) & 1, (uint32_t)(u * hd + col) * 4u,
+            store_y(Yr, (u + 1) & 1, ((uint32_t)u * hd + (uint32_t)col) * 4u,
                     (t0 + u - 1 >= 0) & (t0 + u - 1 < T));
             // ---- this wave's reads of the post-write state ----
             float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -380,14 +395,19 @@ __global__ __launch_bounds__(64 * KS) void rw_split_kernel(RWArgs a)
                 acc.z = fmaf(qv, val.z, acc.z);
                 acc.w = fmaf(qv, val.w, acc.w);
             }
+            // sum over the row groups, transposed: each step hands the
+            // partner the components it does not keep, so that afterwards
+            // lane (g, q) holds component 2 (g & 1) + ((g >> 1) & 1) of the
+            // wave's sum for float4 q (6 lane moves instead of 4 per step)
+            const bool b0 = (g & 1) != 0, b1 = (g & 2) != 0;
+            float k0 = b0 ? acc.z : acc.x, k1 = b0 ? acc.w : acc.y;
+            k0 += xor_get(b0 ? acc.x : acc.z, LPR, lane);
+            k1 += xor_get(b0 ? acc.y : acc.w, LPR, lane);
+            float kc = b1 ? k1 : k0;
+            kc += xor_get(b1 ? k0 : k1, 2 * LPR, lane);
 #pragma unroll
-            for (int m = LPR; m < 64; m <<= 1) {
-                acc.x = xor_add(acc.x, m);
-                acc.y = xor_add(acc.y, m);
-                acc.z = xor_add(acc.z, m);
-                acc.w = xor_add(acc.w, m);
-            }
-            if (g == 0) ypart[u & 1][k][q] = acc;
+            for (int m = 4 * LPR; m < 64; m <<= 1) kc = xor_add(kc, m);
+            if (g < 4) reinterpret_cast<float *>(&ypart[u & 1][k][q])[2 * (g & 1) + (g >> 1)] = kc;
             // ---- prefetch: rows of token t+P, slot words of token t+2P ----
             load_rows(t0 + u + P, sw[(u + P) % (2 * P)], sr[(u + P) % (2 * P)], rw[pr], rr[pr],
                       ma[pr], mc[pr], mq[pr], mv[pr]);
@@ -397,7 +417,7 @@ __global__ __launch_bounds__(64 * KS) void rw_split_kernel(RWArgs a)
     }
     // the last trip's last token (t0 - 1 now) has no next token to store its y
     __syncthreads();
-    const rsrc_t Yr = make_rsrc(ybase + (t0 - 1) * hd, (uint32_t)(hd * 4));
+    const rsrc_t Yr = make_rsrc(ybase + (int64_t)(t0 - 1) * hd, hd * 4);
     store_y(Yr, 1, (uint32_t)col * 4u, t0 - 1 < T);
 }
 
