@@ -267,6 +267,8 @@ def test_forward_rejects_bad_tensors():
     # ragged last slice (28 of 32 columns) in each kernel form
     (2, 100, 4, 32, 1020, 32, 32, 0.0),
     (4, 64, 8, 32, 1020, 24, 32, 0.0),
+    # odd W != R over four waves: 10 write and 8 read positions per wave
+    (2, 150, 4, 64, 1024, 37, 29, 0.3),
 ])
 def test_schedules_agree_bitwise_on_state(shape):
     """Both schedules apply the same float32 operations to every row in the
