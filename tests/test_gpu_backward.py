@@ -197,6 +197,36 @@ def test_backward_8b_style_shape_in_chunks():
         _compare(g, ref)
 
 
+def test_backward_long_context_epochs_in_chunks():
+    """The long-context slot count (sqrtN = 512, W = R = 64: epochs of 4096
+    tokens) over three epochs, bf16 inputs and key reuse, on 64 columns
+    (columns never interact, so the state's width does not change the
+    schedule).  The backward in three chunks of one epoch and in one chunk
+    gives the same gradients bit for bit, and both match the oracle."""
+    wl = si.Workload("bwd long epochs", B=1, T=9000, H=1, sqrtN=512, d_v=64, W=64, R=64,
+                     dtype="bf16", reuse=0.1, seed=84)
+    log(f"backward: B={wl.B} T={wl.T} H={wl.H} S={wl.sqrtN} d_v={wl.d_v} bf16, 1 and 3 chunks")
+    with Timer("generate"):
+        d = si.generate(wl)
+    dd = upload(d)
+    core = make_core(dd, wl.W, wl.R)
+    # (here E*W = N: one epoch of the tape is the size of one chunk-start
+    # state, so three chunks take as much memory as one)
+    dy, dMT = _dy_dMT(wl, 15)
+    args = [dd[n] for n in ("kp", "qp", "v", "alpha", "beta")]
+    dyg, dMTg = torch.from_numpy(dy).cuda(), torch.from_numpy(dMT).cuda()
+    g3 = core.backward(*args, dyg, dMT=dMTg, chunks=3)
+    g1 = core.backward(*args, dyg, dMT=dMTg, chunks=1)
+    torch.cuda.synchronize()
+    for n in g3:
+        assert torch.equal(g3[n], g1[n]), n
+    with Timer("oracle backward"):
+        ref = oracle.backward(d, wl.sqrtN, wl.W, wl.R, dy.astype(np.float64),
+                              dMT.astype(np.float64))
+    ref["dMinit"] = None
+    _compare(g3, ref)
+
+
 def test_backward_long_context_shape_chained_calls():
     """The long-context head shape (sqrtN = 512, d_v = 2048, W = R = 64, bf16
     inputs, key reuse) run as three calls that continue the state (the
