@@ -350,7 +350,7 @@ def counters_summary(args, wl):
         # per-epoch launches (one read launch per epoch) or the fused
         # narrow-state kernel (one launch per step)
         rw = [k for k in kernels if k.startswith(("tp_read", "tp_update", "tp_fused"))]
-        E = _epoch_len(wl)
+        E = _epoch_len(wl, args.state)
         steps = (sum(len(vals[(k, "FETCH_SIZE")]) for k in rw if k.startswith("tp_read")) /
                  (-(-wl.T // E)) +
                  sum(len(vals[(k, "FETCH_SIZE")]) for k in rw if k.startswith("tp_fused")))
@@ -374,13 +374,18 @@ def counters_summary(args, wl):
           f"{(fetch + write) / 1e9:.2f} GB per step over {steps:g} steps -> {path}")
 
 
-def _epoch_len(wl):
+def _epoch_len(wl, state="f32", cus=256):
     """Tokens per epoch of the time-parallel schedule (the library's rule:
-    the largest power of two <= 4096 with E*W <= N and E*W <= 2^18, and no
+    the largest power of two <= 4096 with E*W <= N and E*W <= 2^18; for a
+    bfloat16 or E4M3 state at most 256 where the one-launch kernel's
+    (chain, 64-column slice) units fill the `cus` compute units; and no
     longer than the next power of two >= T)."""
     e = 4096
     while e > 1 and (e * wl.W > (1 << 18) or e * wl.W > wl.N):
         e //= 2
+    units = wl.B * wl.H * -(-wl.d_v // 64)
+    if state != "f32" and e > 256 and units >= cus and (units % cus == 0 or units >= 8 * cus):
+        e = 256
     if e > wl.T:
         e = 1
         while e < wl.T:

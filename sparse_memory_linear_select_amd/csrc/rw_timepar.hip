@@ -1209,7 +1209,18 @@ __global__ __launch_bounds__(64 * kFuseWaves) void tp_fused_stored_kernel(TPArgs
 
 }  // namespace
 
-int tp_epoch_len(const Shape &s)
+// Whether the (chain, 64-column slice) units of tp_fused_stored_kernel give
+// every compute unit one workgroup in every round (one fits a compute unit
+// at a time): a whole number of rounds, or enough of them that a partial
+// last one costs little.
+static bool fused_units_fill(const Shape &s)
+{
+    const int64_t units = (int64_t)s.B * s.H * ((s.d_v + 4 * kFuseLPR - 1) / (4 * kFuseLPR));
+    const int64_t cus = compute_units();
+    return units >= cus && (units % cus == 0 || units >= 8 * cus);
+}
+
+int tp_epoch_len(const Shape &s, bool stored)
 {
     // E <= kMaxEpoch and E*W <= kMaxEpochEvents (replay links pack an event
     // position and a count into 32 bits), and E*W <= N: longer epochs merge
@@ -1219,6 +1230,13 @@ int tp_epoch_len(const Shape &s)
     const int64_t cap = s.N();
     int64_t e = kMaxEpoch;
     while (e > 1 && (e * s.W > kMaxEpochEvents || e * s.W > cap)) e >>= 1;
+    // A bfloat16 or E4M3 state: every read sees the stored rows, so neither
+    // y nor M depends on where epochs start.  Where the fused kernel's units
+    // fill the GPU, epochs short enough for it to stage their v rows let it
+    // take the whole apply in one launch (8B-style layer, bf16 state:
+    // write/read with 1024-token epochs in per-epoch launches against
+    // 256-token ones in one launch: see the design notes).
+    if (stored && e > kFuseMaxE && fused_units_fill(s)) e = kFuseMaxE;
     if (e > s.T) {
         e = 1;
         while (e < s.T) e <<= 1;
@@ -1237,25 +1255,25 @@ static int tp_pair_cap(const Shape &s, int E)
     return (int)((p + 7) / 8 * 8);
 }
 
-size_t tp_workspace_bytes(const Shape &s)
+size_t tp_workspace_bytes(const Shape &s, bool stored)
 {
     const size_t chains = (size_t)s.B * s.H;
     const size_t ev = chains * (size_t)s.T * s.W;
     const size_t toks = chains * (size_t)s.T;
-    const int P = tp_pair_cap(s, tp_epoch_len(s));
+    const int P = tp_pair_cap(s, tp_epoch_len(s, stored));
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     return up(ev * sizeof(TPEntry)) + 2 * up(ev * 8) + up(ev * 2) + 2 * up(toks * kMaxK * 4) +
            up(toks * 4) + up(toks * (size_t)P * 8);
 }
 
 static TPArgs tp_args(const Shape &s, const uint32_t *rec, void *ws, const void *v, float *y,
-                      void *M)
+                      void *M, bool stored = false)
 {
     const RecLayout L(s.W, s.R);
     TPArgs a{};
     const size_t chains = (size_t)s.B * s.H;
     const size_t ev = chains * (size_t)s.T * s.W;
-    a.E = tp_epoch_len(s);
+    a.E = tp_epoch_len(s, stored);
     a.nepoch = (int)((s.T + a.E - 1) / a.E);
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     char *p = static_cast<char *>(ws);
@@ -1307,7 +1325,7 @@ bool tp_supported(const Shape &s)
 hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipStream_t st,
                              int ep0, int ep1, bool link, bool stored)
 {
-    TPArgs a = tp_args(s, rec, ws, nullptr, nullptr, nullptr);
+    TPArgs a = tp_args(s, rec, ws, nullptr, nullptr, nullptr, stored);
     if (ep1 < 0 || ep1 > a.nepoch) ep1 = a.nepoch;
     if (ep0 >= ep1) return hipSuccess;
     a.ep0 = ep0;
@@ -1333,19 +1351,15 @@ hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipS
 // Whether a narrow-state apply takes tp_fused_stored_kernel: its epochs must
 // fit the LDS buffer; then the environment variable SDM_TP_FUSED=0 keeps the
 // per-epoch launches and SDM_TP_FUSED=1 takes the fused kernel (the results
-// are bit-identical either way), and otherwise it is taken when the (chain,
-// slice) units give every compute unit one workgroup in every round (one
-// workgroup fits a compute unit at a time): a whole number of rounds, or
-// enough of them that a partial last one costs little.
-static bool use_fused(const TPArgs &a, int d_v)
+// are bit-identical either way), and otherwise it is taken when its units
+// fill the GPU (fused_units_fill).
+static bool use_fused(const TPArgs &a, const Shape &s)
 {
     if (a.E > kFuseMaxE) return false;
     const char *env = getenv("SDM_TP_FUSED");
     if (env && env[0] == '0') return false;
     if (env && env[0] == '1') return true;
-    const int64_t units = a.chains * ((d_v + 4 * kFuseLPR - 1) / (4 * kFuseLPR));
-    const int64_t cus = compute_units();
-    return units >= cus && (units % cus == 0 || units >= 8 * cus);
+    return fused_units_fill(s);
 }
 
 template <int ST>
@@ -1353,7 +1367,7 @@ static hipError_t tp_apply_state(const Shape &s, TPArgs a, bool bf16, hipStream_
                                  int ep1)
 {
     if constexpr (ST != kStateF32) {
-        if (use_fused(a, s.d_v)) {
+        if (use_fused(a, s)) {
             const int64_t units = a.chains * ((s.d_v + 4 * kFuseLPR - 1) / (4 * kFuseLPR));
             if (units >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
             if (ep0 >= ep1) return hipSuccess;
@@ -1479,7 +1493,7 @@ hipError_t launch_tp_apply(const Shape &s, const uint32_t *rec, void *ws, const 
                            bool bf16, float *y, void *M, StateFmt fmt, hipStream_t st, int ep0,
                            int ep1)
 {
-    TPArgs a = tp_args(s, rec, ws, v, y, M);
+    TPArgs a = tp_args(s, rec, ws, v, y, M, fmt.type != kStateF32);
     a.ssc = ldexpf(1.0f, fmt.scale_log2);
     a.sisc = ldexpf(1.0f, -fmt.scale_log2);
     if (ep1 < 0 || ep1 > a.nepoch) ep1 = a.nepoch;

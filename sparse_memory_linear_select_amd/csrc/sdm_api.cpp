@@ -98,7 +98,8 @@ sdm_variant resolve_variant(const sdm_ctx *h, int B, int64_t T, sdm_variant v)
 size_t ws_bytes_for(const sdm_ctx *h, int B, int64_t T, sdm_variant var)
 {
     size_t n = records_bytes(h, B, T);
-    if (var == SDM_VARIANT_TIMEPAR) n += round_up(sdm::tp_workspace_bytes(shape_of(h, B, T)));
+    if (var == SDM_VARIANT_TIMEPAR)
+        n += round_up(sdm::tp_workspace_bytes(shape_of(h, B, T), h->state.type != sdm::kStateF32));
     return n;
 }
 

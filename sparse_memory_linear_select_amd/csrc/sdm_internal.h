@@ -155,8 +155,10 @@ hipError_t launch_rw_simple(const Shape &s, const uint32_t *rec, const void *v, 
 
 // Time-parallel schedule (epochs of tokens, slot-sorted write events).
 bool tp_supported(const Shape &s);
-int tp_epoch_len(const Shape &s);
-size_t tp_workspace_bytes(const Shape &s);  // beyond the token records
+// Tokens per epoch and workspace beyond the token records; `stored`: a
+// bfloat16 or E4M3 state (its epochs may be shorter, see tp_epoch_len).
+int tp_epoch_len(const Shape &s, bool stored = false);
+size_t tp_workspace_bytes(const Shape &s, bool stored = false);
 // Epochs [ep0, ep1) (ep1 < 0: through the last epoch).  With `stored` (a
 // bfloat16 or E4M3 state) the read plan is the one of stored-value reads
 // (rows rounded after every write): weights q and each read's in-epoch

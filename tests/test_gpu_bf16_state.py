@@ -36,6 +36,9 @@ SHAPES = [
     (2, 300, 2, 16, 72, 16, 16, "f32", 0.3),   # several epochs, key reuse
     (1, 257, 2, 128, 64, 64, 64, "f32", 0.3),  # the 1.4B-style slot count
     (1, 91, 1, 32, 36, 32, 20, "bf16", 0.5),   # bf16 inputs
+    # 256 (sequence, head, 64-column) units fill the GPU: epochs of 256
+    # tokens (a float32 state would take 512) in one launch
+    (4, 1200, 4, 64, 1024, 8, 8, "f32", 0.2),
 ]
 
 
@@ -47,7 +50,7 @@ def test_bf16_state_shapes(shape):
     _parity(wl)
 
 
-@pytest.mark.parametrize("cfg", [1, 4])
+@pytest.mark.parametrize("cfg", [1, 3, 4])
 def test_bf16_state_full_workload(cfg):
     """Full-size workload on the GPU; the oracle recomputes a 16-column window."""
     wl = si.WORKLOADS[cfg]

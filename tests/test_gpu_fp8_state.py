@@ -42,6 +42,9 @@ SHAPES = [
     (1, 257, 2, 128, 64, 64, 64, "f32", 0.3, -4),  # the 1.4B-style slot count
     (1, 91, 1, 32, 36, 32, 20, "bf16", 0.5, -3),   # bf16 inputs
     (2, 150, 2, 16, 160, 8, 8, "f32", 0.2, 0),     # unscaled codes (subnormal M_0), 2 slices
+    # 256 (sequence, head, 64-column) units fill the GPU: epochs of 256
+    # tokens (a float32 state would take 512) in one launch
+    (4, 1200, 4, 64, 1024, 8, 8, "f32", 0.2, -4),
 ]
 
 
@@ -53,7 +56,7 @@ def test_fp8_state_shapes(shape):
     _parity(wl, s=sc)
 
 
-@pytest.mark.parametrize("cfg", [1, 4])
+@pytest.mark.parametrize("cfg", [1, 3, 4])
 def test_fp8_state_full_workload(cfg):
     """Full-size workload on the GPU; the oracle recomputes a 16-column window."""
     wl = si.WORKLOADS[cfg]
