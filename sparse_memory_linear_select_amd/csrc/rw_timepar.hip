@@ -1220,22 +1220,38 @@ static bool fused_units_fill(const Shape &s)
     return units >= cus && (units % cus == 0 || units >= 8 * cus);
 }
 
-int tp_epoch_len(const Shape &s, bool stored)
+// Tokens per epoch with E*W <= cap: the largest power of two <= kMaxEpoch
+// with E*W <= kMaxEpochEvents (replay links pack an event position and a
+// count into 32 bits) and E*W <= cap.
+static int64_t epoch_for_cap(const Shape &s, int64_t cap)
 {
-    // E <= kMaxEpoch and E*W <= kMaxEpochEvents (replay links pack an event
-    // position and a count into 32 bits), and E*W <= N: longer epochs merge
-    // more repeated writes to a slot, but every read then carries more v
-    // pairs from in-epoch writes (write/read at the 1.4B-style layer with
-    // E*W = N/2, N, 2N: 9.13, 8.25, 8.67 ms).
-    const int64_t cap = s.N();
     int64_t e = kMaxEpoch;
     while (e > 1 && (e * s.W > kMaxEpochEvents || e * s.W > cap)) e >>= 1;
+    return e;
+}
+
+int tp_epoch_len(const Shape &s, bool stored)
+{
+    // Longer epochs merge more repeated writes to a slot and take fewer
+    // launches, but every read then carries more v pairs from in-epoch
+    // writes, and the sort and plan (one workgroup per (chain, epoch)) have
+    // fewer workgroups.  A float32 state takes E*W <= 2N where chains x
+    // epochs still give half the compute units a sort workgroup, else
+    // E*W <= N (1.4B-style layer, write/read and step: E*W = N 6.74 / 7.77
+    // ms, 2N 6.06 / 7.30, 4N 6.63 / 8.52; 8B-style layer 27.52 / 32.53 at
+    // N, 25.45 / 31.66 at 2N; larger state, 8 chains: 13.78 / 16.20 at N,
+    // 12.85 / 16.40 at 2N, its sort and plan on 64 workgroups taking 2.10 ms
+    // instead of 0.96).  A bfloat16 or E4M3 state keeps E*W <= N: each of
+    // its reads replays its in-epoch writes.
+    int64_t e = epoch_for_cap(s, 2 * s.N());
+    const int64_t groups = (int64_t)s.B * s.H * ((s.T + e - 1) / e);
+    if (stored || 2 * groups < compute_units()) e = epoch_for_cap(s, s.N());
     // A bfloat16 or E4M3 state: every read sees the stored rows, so neither
     // y nor M depends on where epochs start.  Where the fused kernel's units
     // fill the GPU, epochs short enough for it to stage their v rows let it
-    // take the whole apply in one launch (8B-style layer, bf16 state:
-    // write/read with 1024-token epochs in per-epoch launches against
-    // 256-token ones in one launch: see the design notes).
+    // take the whole apply in one launch (8B-style layer: bf16 write/read
+    // 21.85 -> 21.42 ms, E4M3 20.10 -> 16.11 ms against 1024-token epochs in
+    // per-epoch launches).
     if (stored && e > kFuseMaxE && fused_units_fill(s)) e = kFuseMaxE;
     if (e > s.T) {
         e = 1;

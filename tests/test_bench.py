@@ -85,8 +85,14 @@ def test_cpu_baseline_token_slice_and_one_core():
 
 
 def test_epoch_length_rule():
-    # tokens per epoch of the time-parallel schedule on the five workloads
-    assert [bench._epoch_len(si.WORKLOADS[c]) for c in range(5)] == [64, 256, 1024, 1024, 4096]
+    # tokens per epoch of the time-parallel schedule on the five workloads:
+    # E*W <= 2N for a float32 state where chains x epochs reach half of 256
+    # compute units (else N: the tiny and larger-state workloads); a narrow
+    # state keeps E*W <= N, and 256 tokens where the one-launch kernel's
+    # units fill 256 compute units
+    assert [bench._epoch_len(si.WORKLOADS[c]) for c in range(5)] == [64, 512, 1024, 2048, 4096]
+    assert [bench._epoch_len(si.WORKLOADS[c], "bf16") for c in range(5)] == \
+        [64, 256, 1024, 256, 4096]
 
 
 def test_counters_summary_calibrates_with_the_device_copy(tmp_path, monkeypatch, capsys):
@@ -104,11 +110,12 @@ def test_counters_summary_calibrates_with_the_device_copy(tmp_path, monkeypatch,
         shutil.copy(os.path.join(ROOT, "sparse_memory_linear_select_amd", "csrc", name),
                     fake / "sparse_memory_linear_select_amd" / "csrc" / name)
     monkeypatch.setattr(bench, "ROOT", str(fake))
-    wl = si.WORKLOADS[1]  # 16 epochs per step
+    wl = si.WORKLOADS[1]
+    nep = -(-wl.T // bench._epoch_len(wl))  # epochs per step
     rows = []
     for cnt, per_read, per_upd, copy in (("FETCH_SIZE", 100.0, 50.0, 524288.0),
                                          ("WRITE_SIZE", 1.0, 80.0, 1048576.0)):
-        for i in range(32):  # two steps
+        for i in range(2 * nep):  # two steps
             rows.append(("void sdm::(anonymous namespace)::tp_read_kernel<8, false>(x)", cnt, per_read))
             rows.append(("void sdm::(anonymous namespace)::tp_update_kernel<false, 8, false, false>(x)",
                          cnt, per_upd))
@@ -128,7 +135,7 @@ def test_counters_summary_calibrates_with_the_device_copy(tmp_path, monkeypatch,
     rec = json.load(open(fake / "profiles" / "traffic_time_parallel__1.4B-style_layer.json"))
     assert rec["steps_in_run"] == 2
     assert rec["fetch_scale"] == pytest.approx(2.0) and rec["write_scale"] == pytest.approx(1.0)
-    assert rec["fetch_bytes"] == pytest.approx(16 * (100 + 50) * 1024 * 2.0)
-    assert rec["write_bytes"] == pytest.approx(16 * (1 + 80) * 1024 * 1.0)
+    assert rec["fetch_bytes"] == pytest.approx(nep * (100 + 50) * 1024 * 2.0)
+    assert rec["write_bytes"] == pytest.approx(nep * (1 + 80) * 1024 * 1.0)
     assert bench._traffic(wl, "time-parallel") == pytest.approx(rec["hbm_bytes_per_step"])
     assert "tp_sort_kernel<false>" in capsys.readouterr().out
