@@ -378,7 +378,7 @@ def _epoch_len(wl, state="f32", cus=256):
     """Tokens per epoch of the time-parallel schedule (the library's rule:
     the largest power of two <= 4096 with E*W <= 2N and E*W <= 2^18, or
     with E*W <= N for a bfloat16 or E4M3 state and where chains x epochs
-    would be fewer than half the `cus` compute units; for a
+    would be fewer than a quarter of the `cus` compute units; for a
     bfloat16 or E4M3 state at most 256 where the one-launch kernel's
     (chain, 64-column slice) units fill the `cus` compute units; and no
     longer than the next power of two >= T)."""
@@ -389,7 +389,7 @@ def _epoch_len(wl, state="f32", cus=256):
         return e
 
     e = for_cap(2 * wl.N)
-    if state != "f32" or 2 * wl.B * wl.H * -(-wl.T // e) < cus:
+    if state != "f32" or 4 * wl.B * wl.H * -(-wl.T // e) < cus:
         e = for_cap(wl.N)
     units = wl.B * wl.H * -(-wl.d_v // 64)
     if state != "f32" and e > 256 and units >= cus and (units % cus == 0 or units >= 8 * cus):

@@ -221,13 +221,17 @@ __global__ __launch_bounds__(kSortThreads) void tp_sort_kernel(TPArgs a, SortIO 
 // first at [r], [R + r], [2R + r], of the second at [3R + r], [4R + r],
 // [5R + r] (6R dwords <= the 2P dwords of the area, as P >= 3R).
 __global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int stride, int exact,
-                                                               int stored)
+                                                               int stored, int parts)
 {
     extern __shared__ uint16_t ck[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int64_t chain = blockIdx.x / a.nrun;
-    const int ep = a.ep0 + (int)(blockIdx.x - chain * a.nrun);
+    // `parts` workgroups per (chain, epoch), each planning a contiguous range
+    // of its tokens
+    const int64_t ce = blockIdx.x / parts;
+    const int part = (int)(blockIdx.x - ce * parts);
+    const int64_t chain = ce / a.nrun;
+    const int ep = a.ep0 + (int)(ce - chain * a.nrun);
     const int64_t t0 = (int64_t)ep * a.E;
     const int ne = (int)((a.T - t0) < a.E ? (a.T - t0) : a.E);
     const int n = ne * a.W;
@@ -243,7 +247,8 @@ __global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int str
         if (exact) tk[k] = (uint16_t)(se[k].tw >> 6);
     }
     __syncthreads();
-    for (int tl = tid >> 6; tl < ne; tl += kSortThreads / 64) {  // wave-uniform token
+    const int tl0 = (int)((int64_t)ne * part / parts), tl1 = (int)((int64_t)ne * (part + 1) / parts);
+    for (int tl = tl0 + (tid >> 6); tl < tl1; tl += kSortThreads / 64) {  // wave-uniform token
         const uint32_t *rc = recc + (int64_t)tl * a.rec_dwords;
         const bool real = lane < a.R;
         int j = 0, cnt = 0;
@@ -1235,18 +1240,19 @@ int tp_epoch_len(const Shape &s, bool stored)
 {
     // Longer epochs merge more repeated writes to a slot and take fewer
     // launches, but every read then carries more v pairs from in-epoch
-    // writes, and the sort and plan (one workgroup per (chain, epoch)) have
-    // fewer workgroups.  A float32 state takes E*W <= 2N where chains x
-    // epochs still give half the compute units a sort workgroup, else
+    // writes, and the sort (one workgroup per (chain, epoch)) has fewer
+    // workgroups.  A float32 state takes E*W <= 2N where chains x epochs
+    // still give a quarter of the compute units a sort workgroup, else
     // E*W <= N (1.4B-style layer, write/read and step: E*W = N 6.74 / 7.77
     // ms, 2N 6.06 / 7.30, 4N 6.63 / 8.52; 8B-style layer 27.52 / 32.53 at
-    // N, 25.45 / 31.66 at 2N; larger state, 8 chains: 13.78 / 16.20 at N,
-    // 12.85 / 16.40 at 2N, its sort and plan on 64 workgroups taking 2.10 ms
-    // instead of 0.96).  A bfloat16 or E4M3 state keeps E*W <= N: each of
-    // its reads replays its in-epoch writes.
+    // N, 25.45 / 31.66 at 2N; larger state, 8 chains and 64 sort
+    // workgroups at 2N: 13.66 / 15.92 at N, 12.62 / 15.38 at 2N with the
+    // plan split over 4 workgroups per (chain, epoch), 12.85 / 16.40 without
+    // that split).  A bfloat16 or E4M3 state keeps E*W <= N: each of its
+    // reads replays its in-epoch writes.
     int64_t e = epoch_for_cap(s, 2 * s.N());
     const int64_t groups = (int64_t)s.B * s.H * ((s.T + e - 1) / e);
-    if (stored || 2 * groups < compute_units()) e = epoch_for_cap(s, s.N());
+    if (stored || 4 * groups < compute_units()) e = epoch_for_cap(s, s.N());
     // A bfloat16 or E4M3 state: every read sees the stored rows, so neither
     // y nor M depends on where epochs start.  Where the fused kernel's units
     // fill the GPU, epochs short enough for it to stage their v rows let it
@@ -1361,8 +1367,14 @@ hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipS
     // epochs; step 7.29 -> 7.21 ms against the sampled search there)
     const int exact = stride == 1 && a.kshift == 0 && nmax <= 32768;
     const size_t lds = (size_t)((nmax + stride - 1) / stride) * sizeof(uint16_t) * (exact ? 2 : 1);
-    hipLaunchKernelGGL(tp_link_kernel, dim3((unsigned)blocks), dim3(kSortThreads), lds, st, a,
-                       stride, exact, stored ? 1 : 0);
+    // fewer (chain, epoch) pairs than compute units: split each one's tokens
+    // over up to 4 workgroups (each loads the epoch's keys itself; 8B-style
+    // layer, 128 pairs in 2 parts: step 31.6 -> 30.8 ms)
+    const int64_t cus = compute_units();
+    int parts = 1;
+    while (parts < 4 && blocks * parts * 2 <= cus) parts *= 2;
+    hipLaunchKernelGGL(tp_link_kernel, dim3((unsigned)(blocks * parts)), dim3(kSortThreads), lds,
+                       st, a, stride, exact, stored ? 1 : 0, parts);
     return hipGetLastError();
 }
 

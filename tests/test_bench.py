@@ -86,11 +86,11 @@ def test_cpu_baseline_token_slice_and_one_core():
 
 def test_epoch_length_rule():
     # tokens per epoch of the time-parallel schedule on the five workloads:
-    # E*W <= 2N for a float32 state where chains x epochs reach half of 256
-    # compute units (else N: the tiny and larger-state workloads); a narrow
-    # state keeps E*W <= N, and 256 tokens where the one-launch kernel's
-    # units fill 256 compute units
-    assert [bench._epoch_len(si.WORKLOADS[c]) for c in range(5)] == [64, 512, 1024, 2048, 4096]
+    # E*W <= 2N for a float32 state where chains x epochs reach a quarter of
+    # 256 compute units (else N: the tiny workload); a narrow state keeps
+    # E*W <= N, and 256 tokens where the one-launch kernel's units fill 256
+    # compute units
+    assert [bench._epoch_len(si.WORKLOADS[c]) for c in range(5)] == [64, 512, 2048, 2048, 4096]
     assert [bench._epoch_len(si.WORKLOADS[c], "bf16") for c in range(5)] == \
         [64, 256, 1024, 256, 4096]
 
