@@ -1216,15 +1216,20 @@ __global__ __launch_bounds__(64 * kFuseWaves) void tp_fused_stored_kernel(TPArgs
 }  // namespace
 
 // Whether the (chain, 64-column slice) units of tp_fused_stored_kernel give
-// every compute unit one workgroup in every round (one fits a compute unit
-// at a time): a whole number of rounds, or enough of them that a partial
-// last one costs little.
-static bool fused_units_fill(const Shape &s)
+// every one of `cus` compute units one workgroup in every round (one fits a
+// compute unit at a time): a whole number of rounds, or enough of them that
+// a partial last one costs little.
+static bool fused_units_fill(const Shape &s, int64_t cus)
 {
     const int64_t units = (int64_t)s.B * s.H * ((s.d_v + 4 * kFuseLPR - 1) / (4 * kFuseLPR));
-    const int64_t cus = compute_units();
     return units >= cus && (units % cus == 0 || units >= 8 * cus);
 }
+
+// The compute units the epoch rule assumes: an MI355X's 256.  A fixed figure
+// keeps the epoch length, and with it every workspace size, a pure function
+// of the shape (any epoch length gives correct results; the launches
+// themselves use the device's own count).
+constexpr int64_t kEpochRuleCUs = 256;
 
 // Tokens per epoch with E*W <= cap: the largest power of two <= kMaxEpoch
 // with E*W <= kMaxEpochEvents (replay links pack an event position and a
@@ -1252,14 +1257,14 @@ int tp_epoch_len(const Shape &s, bool stored)
     // reads replays its in-epoch writes.
     int64_t e = epoch_for_cap(s, 2 * s.N());
     const int64_t groups = (int64_t)s.B * s.H * ((s.T + e - 1) / e);
-    if (stored || 4 * groups < compute_units()) e = epoch_for_cap(s, s.N());
+    if (stored || 4 * groups < kEpochRuleCUs) e = epoch_for_cap(s, s.N());
     // A bfloat16 or E4M3 state: every read sees the stored rows, so neither
     // y nor M depends on where epochs start.  Where the fused kernel's units
     // fill the GPU, epochs short enough for it to stage their v rows let it
     // take the whole apply in one launch (8B-style layer: bf16 write/read
     // 21.85 -> 21.42 ms, E4M3 20.10 -> 16.11 ms against 1024-token epochs in
     // per-epoch launches).
-    if (stored && e > kFuseMaxE && fused_units_fill(s)) e = kFuseMaxE;
+    if (stored && e > kFuseMaxE && fused_units_fill(s, kEpochRuleCUs)) e = kFuseMaxE;
     if (e > s.T) {
         e = 1;
         while (e < s.T) e <<= 1;
@@ -1389,7 +1394,7 @@ static bool use_fused(const TPArgs &a, const Shape &s)
     const char *env = getenv("SDM_TP_FUSED");
     if (env && env[0] == '0') return false;
     if (env && env[0] == '1') return true;
-    return fused_units_fill(s);
+    return fused_units_fill(s, compute_units());
 }
 
 template <int ST>
