@@ -299,6 +299,19 @@ def test_schedules_agree_bitwise_on_state(shape):
     assert torch.allclose(y1, y2, rtol=1e-5, atol=1e-6)
 
 
+def test_schedules_agree_bitwise_with_bf16_inputs():
+    """bfloat16 k', q', v (widened exactly) at a shape whose 256 units of
+    128-byte slices take the four-wave token-serial kernel: the final state
+    agrees bit for bit with the time-parallel schedule."""
+    wl = si.Workload("agree bf16", B=2, T=200, H=4, sqrtN=32, d_v=1024, W=32, R=32,
+                     dtype="bf16", reuse=0.1, seed=48)
+    d = si.generate(wl)
+    _, _, y1, M1 = gpu_forward(d, wl.W, wl.R, sdm.SERIAL)
+    _, _, y2, M2 = gpu_forward(d, wl.W, wl.R, sdm.TIMEPAR)
+    assert torch.equal(M1, M2)
+    assert torch.allclose(y1, y2, rtol=1e-5, atol=1e-6)
+
+
 @pytest.mark.parametrize("variant", VARIANTS, ids=VNAMES)
 def test_decode_token_by_token(variant):
     """Decoding one token per call (continuing from the previous state) gives
