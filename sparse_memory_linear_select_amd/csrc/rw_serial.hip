@@ -283,8 +283,13 @@ __global__ __launch_bounds__(64 * KS) void rw_split_kernel(RWArgs a)
 
     uint32_t sw[2 * P][NW], sr[2 * P][NR];
     float4 rw[P][NW], rr[P][NR];
-    float ma[P][NW], mc[P][NW], mq[P][NR];
-    float4 mv[P];
+    // coefficients and v of the next kQ tokens: their loads need less lead
+    // than the row gathers (and each token's are issued before its rows,
+    // so waiting for them never waits for rows issued later)
+    constexpr int kQ = 2;
+    static_assert((2 * P) % kQ == 0, "coefficient slots are taken modulo kQ");
+    float ma[kQ][NW], mc[kQ][NW], mq[kQ][NR];
+    float4 mv[kQ];
 
     auto clampt = [&](int t) { return (uint32_t)(t < 0 ? 0 : (t < T ? t : T - 1)); };
     auto fwd = [](uint32_t s) {
@@ -295,16 +300,17 @@ __global__ __launch_bounds__(64 * KS) void rw_split_kernel(RWArgs a)
         load_k<NW>(r + lw, ow);
         load_k<NR>(r + 3 * a.Wp + lr, orr);
     };
-    auto load_rows = [&](int t, const uint32_t (&iw)[NW], const uint32_t (&ir)[NR],
-                         float4 (&ow)[NW], float4 (&orr)[NR], float (&oa)[NW], float (&oc)[NW],
-                         float (&oq)[NR], float4 &ov) {
-        const uint32_t tc = clampt(t);
+    auto load_rows = [&](const uint32_t (&iw)[NW], const uint32_t (&ir)[NR], float4 (&ow)[NW],
+                         float4 (&orr)[NR]) {
 #pragma unroll
         for (int i = 0; i < NW; i++)
             ow[i] = buf_load4(Mr, (okw[i] & !fwd(iw[i])) ? (iw[i] & kSlotMask) * rowb + col * 4u : kOff);
 #pragma unroll
         for (int i = 0; i < NR; i++)
             orr[i] = buf_load4(Mr, (okr[i] & !fwd(ir[i])) ? (ir[i] & kSlotMask) * rowb + col * 4u : kOff);
+    };
+    auto load_coef = [&](int t, float (&oa)[NW], float (&oc)[NW], float (&oq)[NR], float4 &ov) {
+        const uint32_t tc = clampt(t);
         ov = load_v<BF16>(a.v, vrow0 + (int64_t)((uint64_t)tc * hd));
         const float *r = reinterpret_cast<const float *>(recc + (uint64_t)tc * recd);
         load_k<NW>(r + a.Wp + lw, oa);
@@ -321,18 +327,21 @@ __global__ __launch_bounds__(64 * KS) void rw_split_kernel(RWArgs a)
     }
 #pragma unroll
     for (int u = 0; u < P; u++) {
+#pragma unroll
+        for (int i = 0; i < NW; i++) rw[u][i] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int i = 0; i < NR; i++) rr[u][i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < kQ; u++) {
         mv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int i = 0; i < NW; i++) {
-            rw[u][i] = mv[u];
             ma[u][i] = 0.f;
             mc[u][i] = 0.f;
         }
 #pragma unroll
-        for (int i = 0; i < NR; i++) {
-            rr[u][i] = mv[u];
-            mq[u][i] = 0.f;
-        }
+        for (int i = 0; i < NR; i++) mq[u][i] = 0.f;
     }
 
     // wave 0 stores y of the previous token (sum of the waves' partials, in
@@ -359,7 +368,7 @@ __global__ __launch_bounds__(64 * KS) void rw_split_kernel(RWArgs a)
         const rsrc_t Yr = make_rsrc(ybase + (int64_t)(t0 - 1) * hd, 2 * P * hd * 4);
 #pragma unroll
         for (int u = 0; u < 2 * P; u++) {
-            const int pr = u % P;
+            const int pr = u % P, cq = u % kQ;
             const bool live = (t0 + u >= 0) & (t0 + u < T);
             // ---- this wave's writes ----
 #pragma unroll
@@ -370,7 +379,7 @@ __global__ __launch_bounds__(64 * KS) void rw_split_kernel(RWArgs a)
                 const int wp = f ? (int)((s >> kFwdWShift) & kFwdWMask) : 0;
                 const float4 fv = ring[(u - d) & (2 * P - 1)][wp][q];
                 const float4 old = f ? fv : rw[pr][i];
-                const float4 nv = fma4(ma[pr][i], old, mc[pr][i], mv[pr]);
+                const float4 nv = fma4(ma[cq][i], old, mc[cq][i], mv[cq]);
                 buf_store4(nv, Mr, (okw[i] & live) ? (s & kSlotMask) * rowb + col * 4u : kOff);
                 if (pw[i]) ring[u][lw + i][q] = nv;
             }
@@ -389,7 +398,7 @@ __global__ __launch_bounds__(64 * KS) void rw_split_kernel(RWArgs a)
                 const int wp = f ? (int)((s >> kFwdWShift) & kFwdWMask) : 0;
                 const float4 fv = ring[(u - d) & (2 * P - 1)][wp][q];
                 const float4 val = f ? fv : rr[pr][i];
-                const float qv = mq[pr][i];
+                const float qv = mq[cq][i];
                 acc.x = fmaf(qv, val.x, acc.x);
                 acc.y = fmaf(qv, val.y, acc.y);
                 acc.z = fmaf(qv, val.z, acc.z);
@@ -408,9 +417,10 @@ __global__ __launch_bounds__(64 * KS) void rw_split_kernel(RWArgs a)
 #pragma unroll
             for (int m = 4 * LPR; m < 64; m <<= 1) kc = xor_add(kc, m);
             if (g < 4) reinterpret_cast<float *>(&ypart[u & 1][k][q])[2 * (g & 1) + (g >> 1)] = kc;
-            // ---- prefetch: rows of token t+P, slot words of token t+2P ----
-            load_rows(t0 + u + P, sw[(u + P) % (2 * P)], sr[(u + P) % (2 * P)], rw[pr], rr[pr],
-                      ma[pr], mc[pr], mq[pr], mv[pr]);
+            // ---- prefetch: coefficients and v of token t+kQ, rows of token
+            // t+P, slot words of token t+2P ----
+            load_coef(t0 + u + kQ, ma[cq], mc[cq], mq[cq], mv[cq]);
+            load_rows(sw[(u + P) % (2 * P)], sr[(u + P) % (2 * P)], rw[pr], rr[pr]);
             load_slots(t0 + u + 2 * P, sw[u], sr[u]);
             __builtin_amdgcn_sched_barrier(0);
         }
