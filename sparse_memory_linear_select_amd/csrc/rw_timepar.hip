@@ -81,14 +81,21 @@ constexpr int kWaves = kSortThreads / 64;
 // Stable LSD radix sort of one epoch's write events by slot (one workgroup per
 // (chain, epoch)).  Events are numbered j = token_in_epoch * W + w, so the
 // input order is time order and stability keeps each slot's writes in time
-// order.  The last pass writes the 16-byte entries and a 16-bit coarse key
-// (slot >> kshift) per entry for the link search.
+// order.  One read of the records gives the digit histograms of every pass.
+// Each scatter tile loads the next tile's items (and, in the last pass, its
+// own events' coefficients) before it ranks, so those loads are in flight
+// across the tile's barriers; the per-wave digit counts alternate between two
+// LDS buffers, the idle one cleared during the scan, so a tile takes two
+// barriers.  The last pass writes the 16-byte entries and a
+// 16-bit coarse key (slot >> kshift) per entry for the link search.
+constexpr int kMaxPasses = (kSlotBits + kDigitBits - 1) / kDigitBits;
+
 template <bool MERGED>
 __global__ __launch_bounds__(kSortThreads) void tp_sort_kernel(TPArgs a, SortIO io)
 {
     const int ept = MERGED ? a.W + a.R : a.W;  // events per token
-    __shared__ uint32_t bins[kBuckets];
-    __shared__ uint32_t wcnt[kWaves][kBuckets];
+    __shared__ uint32_t bins[kMaxPasses][kBuckets];
+    __shared__ uint32_t wcnt[2][kWaves][kBuckets];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = tid >> 6;
@@ -100,32 +107,36 @@ __global__ __launch_bounds__(kSortThreads) void tp_sort_kernel(TPArgs a, SortIO 
     const int64_t base = chain * a.T * ept + t0 * ept;          // epoch region
     const uint32_t *recc = a.rec + (chain * a.T + t0) * a.rec_dwords;
     const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    auto rec_slot = [&](int j) -> uint32_t {  // slot of event j (k >= W: read k - W)
+        const int tl = j / ept, k = j - tl * ept;
+        const int col = (MERGED && k >= a.W) ? 3 * a.Wp + (k - a.W) : k;
+        return recc[(int64_t)tl * a.rec_dwords + col] & kSlotMask;
+    };
 
-    for (int p = 0; p < a.passes; p++) {
-        const int shift = kDigitBits * p;
-        const uint64_t *src = (p & 1) ? io.tmpA + base : io.tmpB + base;  // unused when p == 0
-        uint64_t *dst = (p & 1) ? io.tmpB + base : io.tmpA + base;
-        const bool last = p == a.passes - 1;
-        auto item = [&](int j) -> uint64_t {  // (slot << 32) | event j
-            if (p == 0) {
-                const int tl = j / ept, k = j - tl * ept;  // k >= W: read k - W
-                const int col = (MERGED && k >= a.W) ? 3 * a.Wp + (k - a.W) : k;
-                return ((uint64_t)(recc[(int64_t)tl * a.rec_dwords + col] & kSlotMask) << 32) |
-                       (uint32_t)j;
-            }
-            return src[j];
-        };
-        // histogram of this digit
-        for (int k = tid; k < kBuckets; k += kSortThreads) bins[k] = 0;
-        __syncthreads();
-        for (int j = tid; j < n; j += kSortThreads)
-            atomicAdd(&bins[(uint32_t)(item(j) >> (32 + shift)) & (kBuckets - 1)], 1u);
-        __syncthreads();
-        if (wv == 0) {  // exclusive scan of the buckets, kBuckets/64 per lane
-            constexpr int PER = kBuckets / 64;
+    // histograms of all digits, four events per thread in flight
+    for (int k = tid; k < kMaxPasses * kBuckets; k += kSortThreads) (&bins[0][0])[k] = 0;
+    __syncthreads();
+    for (int j0 = tid; j0 < n; j0 += 4 * kSortThreads) {
+        uint32_t sl[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int j = j0 + u * kSortThreads;
+            sl[u] = j < n ? rec_slot(j) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            if (j0 + u * kSortThreads >= n) break;
+            for (int p = 0; p < a.passes; p++)
+                atomicAdd(&bins[p][(sl[u] >> (kDigitBits * p)) & (kBuckets - 1)], 1u);
+        }
+    }
+    __syncthreads();
+    if (wv == 0) {  // exclusive scan of each pass's buckets, kBuckets/64 per lane
+        constexpr int PER = kBuckets / 64;
+        for (int p = 0; p < a.passes; p++) {
             uint32_t c[PER], sum = 0;
             for (int k = 0; k < PER; k++) {
-                c[k] = bins[lane * PER + k];
+                c[k] = bins[p][lane * PER + k];
                 sum += c[k];
             }
             uint32_t incl = sum;
@@ -135,66 +146,88 @@ __global__ __launch_bounds__(kSortThreads) void tp_sort_kernel(TPArgs a, SortIO 
             }
             uint32_t run = incl - sum;
             for (int k = 0; k < PER; k++) {
-                bins[lane * PER + k] = run;
+                bins[p][lane * PER + k] = run;
                 run += c[k];
             }
         }
+    }
+    __syncthreads();
+
+    for (int p = 0; p < a.passes; p++) {
+        const int shift = kDigitBits * p;
+        const uint64_t *src = (p & 1) ? io.tmpA + base : io.tmpB + base;  // unused when p == 0
+        uint64_t *dst = (p & 1) ? io.tmpB + base : io.tmpA + base;
+        const bool last = p == a.passes - 1;
+        auto item = [&](int j) -> uint64_t {  // (slot << 32) | event j
+            if (p == 0) return ((uint64_t)rec_slot(j) << 32) | (uint32_t)j;
+            return src[j];
+        };
+        uint32_t *pbins = bins[p];
+        for (int k = tid; k < kWaves * kBuckets; k += kSortThreads) (&wcnt[0][0][0])[k] = 0;
         __syncthreads();
         // stable scatter, one tile of kSortThreads events at a time
+        uint64_t nxt = tid < n ? item(tid) : 0;
+        int buf = 0;
         for (int tb = 0; tb < n; tb += kSortThreads) {
             const int j = tb + tid;
             const bool valid = j < n;
-            const uint64_t it = valid ? item(j) : 0;
+            const uint64_t it = nxt;
+            if (j + kSortThreads < n) nxt = item(j + kSortThreads);
+            // last pass: this event's 16-byte entry, its words loaded now
+            TPEntry e;
+            if (last && valid) {
+                const uint32_t ev = (uint32_t)it;
+                const int tl = (int)(ev / (uint32_t)ept), k = (int)(ev - tl * ept);
+                const float *rf = reinterpret_cast<const float *>(recc + (int64_t)tl * a.rec_dwords);
+                e.slot = (uint32_t)(it >> 32);
+                if (!MERGED) {  // write w = k: (token << 6) | w, a, c
+                    e.tw = ((uint32_t)tl << 6) | (uint32_t)k;
+                    e.a = rf[a.Wp + k];
+                    e.c = rf[2 * a.Wp + k];
+                } else if (k < a.W) {  // write: (token << 7) | w, a, c
+                    e.tw = ((uint32_t)tl << 7) | (uint32_t)k;
+                    e.a = rf[a.Wp + k];
+                    e.c = rf[2 * a.Wp + k];
+                } else {  // read r: (token << 7) | 64 | r, q, 0
+                    e.tw = ((uint32_t)tl << 7) | 64u | (uint32_t)(k - a.W);
+                    e.a = rf[3 * a.Wp + a.Rp + (k - a.W)];
+                    e.c = 0.0f;
+                }
+            }
             const uint32_t dg = (uint32_t)(it >> (32 + shift)) & (kBuckets - 1);
-            for (int k = tid; k < kWaves * kBuckets; k += kSortThreads) (&wcnt[0][0])[k] = 0;
             uint64_t peers = __ballot(valid);  // lanes of this wave with the same digit
             for (int bit = 0; bit < kDigitBits; bit++) {
                 const uint64_t m = __ballot((dg >> bit) & 1u);
                 peers &= ((dg >> bit) & 1u) ? m : ~m;
             }
             const uint32_t rank = (uint32_t)__popcll(peers & lanes_below);
-            __syncthreads();
-            if (valid && rank == 0) wcnt[wv][dg] = (uint32_t)__popcll(peers);
+            // wcnt[buf] is zero: cleared before the pass or during the scan two tiles back
+            if (valid && rank == 0) wcnt[buf][wv][dg] = (uint32_t)__popcll(peers);
             __syncthreads();
             for (int d = tid; d < kBuckets; d += kSortThreads) {  // per digit, in wave order
-                uint32_t run = bins[d];
+                uint32_t run = pbins[d];
                 for (int w = 0; w < kWaves; w++) {
-                    const uint32_t c = wcnt[w][d];
-                    wcnt[w][d] = run;
+                    const uint32_t c = wcnt[buf][w][d];
+                    wcnt[buf][w][d] = run;
                     run += c;
                 }
-                bins[d] = run;
+                pbins[d] = run;
             }
+            // the other buffer was last read by the previous tile's scatter, before the barrier above
+            for (int k = tid; k < kWaves * kBuckets; k += kSortThreads) (&wcnt[buf ^ 1][0][0])[k] = 0;
             __syncthreads();
             if (valid) {
-                const uint32_t pos = wcnt[wv][dg] + rank;
+                const uint32_t pos = wcnt[buf][wv][dg] + rank;
                 if (!last) {
                     dst[pos] = it;
-                } else {  // final order: the 16-byte entries and the coarse keys
-                    const uint32_t ev = (uint32_t)it;
-                    const int tl = (int)(ev / (uint32_t)ept), k = (int)(ev - tl * ept);
-                    const float *rf = reinterpret_cast<const float *>(recc + (int64_t)tl * a.rec_dwords);
-                    TPEntry e;
-                    e.slot = (uint32_t)(it >> 32);
-                    if (!MERGED) {  // write w = k: (token << 6) | w, a, c
-                        e.tw = ((uint32_t)tl << 6) | (uint32_t)k;
-                        e.a = rf[a.Wp + k];
-                        e.c = rf[2 * a.Wp + k];
-                    } else if (k < a.W) {  // write: (token << 7) | w, a, c
-                        e.tw = ((uint32_t)tl << 7) | (uint32_t)k;
-                        e.a = rf[a.Wp + k];
-                        e.c = rf[2 * a.Wp + k];
-                    } else {  // read r: (token << 7) | 64 | r, q, 0
-                        e.tw = ((uint32_t)tl << 7) | 64u | (uint32_t)(k - a.W);
-                        e.a = rf[3 * a.Wp + a.Rp + (k - a.W)];
-                        e.c = 0.0f;
-                    }
+                } else {
                     io.out[base + pos] = e;
                     if (!MERGED) io.ckey[base + pos] = (uint16_t)(e.slot >> a.kshift);
                 }
             }
-            __syncthreads();
+            buf ^= 1;
         }
+        __syncthreads();  // this pass's stores and wcnt reads before the next pass
     }
 }
 
