@@ -273,22 +273,55 @@ __global__ __launch_bounds__(kSortThreads) void tp_link_kernel(TPArgs a, int str
     const uint32_t *recc = a.rec + (chain * a.T + t0) * a.rec_dwords;
     const TPEntry *se = a.sorted + base;
     // exact (every write sampled, keys = slots): the token of every sorted
-    // write sits in LDS as well, and the searches never touch memory
-    uint16_t *tk = ck + ns;
-    for (int k = tid; k < ns; k += kSortThreads) {
-        ck[k] = a.ckey[base + (int64_t)k * stride];
-        if (exact) tk[k] = (uint16_t)(se[k].tw >> 6);
+    // write sits in LDS as well, and the searches never touch memory.
+    // exact == 2 (the slot table fits too): st[s] = the first sorted write
+    // whose slot is >= s, for s in [0, N], so a read's writes are
+    // [st[s], st[s + 1]) without a search; otherwise a binary search over the
+    // keys in LDS finds the first.
+    const bool direct = exact == 2;
+    uint16_t *st = ck;
+    uint16_t *tk = direct ? ck + (a.N + 1) : ck + ns;
+    if (direct) {
+        for (int k = tid; k < ns; k += kSortThreads) {
+            const int kj = a.ckey[base + k];
+            const int kp = k > 0 ? (int)a.ckey[base + k - 1] : -1;
+            for (int s2 = kp + 1; s2 <= kj; s2++) st[s2] = (uint16_t)k;
+            tk[k] = (uint16_t)(se[k].tw >> 6);
+        }
+        const int klast = ns > 0 ? (int)a.ckey[base + ns - 1] : -1;
+        for (int s2 = klast + 1 + tid; s2 <= (int)a.N; s2 += kSortThreads) st[s2] = (uint16_t)ns;
+    } else {
+        for (int k = tid; k < ns; k += kSortThreads) {
+            ck[k] = a.ckey[base + (int64_t)k * stride];
+            if (exact) tk[k] = (uint16_t)(se[k].tw >> 6);
+        }
     }
     __syncthreads();
     const int tl0 = (int)((int64_t)ne * part / parts), tl1 = (int)((int64_t)ne * (part + 1) / parts);
-    for (int tl = tl0 + (tid >> 6); tl < tl1; tl += kSortThreads / 64) {  // wave-uniform token
-        const uint32_t *rc = recc + (int64_t)tl * a.rec_dwords;
-        const bool real = lane < a.R;
+    constexpr int kTokStep = kSortThreads / 64;
+    const bool real = lane < a.R;
+    // the slot and weight of this lane's read, loaded one token ahead
+    uint32_t s_nx = 0, q_nx = 0;
+    auto load_read = [&](int t) {
+        if (t < tl1 && real) {
+            const uint32_t *rc = recc + (int64_t)t * a.rec_dwords;
+            s_nx = rc[3 * a.Wp + lane] & kSlotMask;
+            q_nx = rc[3 * a.Wp + a.Rp + lane];
+        }
+    };
+    load_read(tl0 + (tid >> 6));
+    for (int tl = tl0 + (tid >> 6); tl < tl1; tl += kTokStep) {  // wave-uniform token
+        const uint32_t s = s_nx;
+        const float q = real ? __uint_as_float(q_nx) : 0.0f;
+        load_read(tl + kTokStep);
         int j = 0, cnt = 0;
-        float q = 0.0f;
-        if (real) {
-            const uint32_t s = rc[3 * a.Wp + lane] & kSlotMask;
-            q = __uint_as_float(rc[3 * a.Wp + a.Rp + lane]);
+        if (real && direct) {
+            j = st[s];
+            const int je = st[s + 1];
+            int l2 = j;  // past the writes of s at tokens <= tl
+            while (l2 < je && (int)tk[l2] <= tl) l2++;
+            cnt = l2 - j;
+        } else if (real) {
             const uint32_t c = s >> a.kshift;
             int lo = 0, hi = ns;  // first sample with coarse key >= c
             while (lo < hi) {
@@ -1403,8 +1436,14 @@ hipError_t launch_tp_prepare(const Shape &s, const uint32_t *rec, void *ws, hipS
     // with every write sampled and keys equal to slots, also the tokens (at
     // most 128 KiB in all: 32 768 writes, the 1.4B-style layer's 512-token
     // epochs; step 7.29 -> 7.21 ms against the sampled search there)
-    const int exact = stride == 1 && a.kshift == 0 && nmax <= 32768;
-    const size_t lds = (size_t)((nmax + stride - 1) / stride) * sizeof(uint16_t) * (exact ? 2 : 1);
+    int exact = stride == 1 && a.kshift == 0 && nmax <= 32768;
+    size_t lds = (size_t)((nmax + stride - 1) / stride) * sizeof(uint16_t) * (exact ? 2 : 1);
+    // and the table of each slot's first write where it fits with the tokens
+    // (N + 1 + E W 16-bit words: 96 KiB at the 1.4B-style layer)
+    if (exact && (a.N + 1 + nmax) * (int64_t)sizeof(uint16_t) <= 131072) {
+        exact = 2;
+        lds = (size_t)(a.N + 1 + nmax) * sizeof(uint16_t);
+    }
     // fewer (chain, epoch) pairs than compute units: split each one's tokens
     // over up to 4 workgroups (each loads the epoch's keys itself; 8B-style
     // layer, 128 pairs in 2 parts: step 31.6 -> 30.8 ms)
